@@ -1,0 +1,11 @@
+"""CPU oracle for the GKA forward: test infrastructure, not part of the product.
+
+Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s CPU-baseline leg may import it.
+It is plain float64 numpy written from the pages' description of the layer and shares no code,
+header, table or helper with the HIP library in ``test_ridge_regression_amd``.
+"""
+from .gka_oracle import (chebyshev_rates, chebyshev_solve, chebyshev_weights, cholesky_solve,
+                         gka_forward_ref, gka_step_ref, ridge_bruteforce)
+
+__all__ = ["chebyshev_rates", "chebyshev_solve", "chebyshev_weights", "cholesky_solve",
+           "gka_forward_ref", "gka_step_ref", "ridge_bruteforce"]

@@ -1,0 +1,233 @@
+"""Plain float64 CPU oracle of the Gated KalmaNet (GKA) forward pass.
+
+TEST INFRASTRUCTURE ONLY. Only the tests, the package's smoke check and the bench's CPU-baseline
+leg may import this module. The GPU library never calls it and shares no code with it.
+
+What it computes, token by token and head by head (the pages name the pieces; the order below
+is the plainest reading that all of them support):
+
+  ridge objective   S_t = argmin_S  sum_{i<=t} eta_{t,i} ||v_i - S k_i||^2 + lambda_t ||S||_F^2,
+                    o_t = S_t q_t           (ai.info summary, "Main Findings", the KF objective
+                                             "Eq. 3"; pith.science page, appendix fragment
+                                             "No weighting", which sets eta_i = 1 in (3))
+  closed form       (H_t + lambda_t I) x_t = q_t,  o_t = U_t x_t
+                                            (ai.info summary, "Methodology in Plain English")
+  gated weights     eta_{t,i} = prod_{j=i+1}^{t} gamma_j, gamma_j in [0, 1]
+                                            (pith.science page, appendix fragment "Adaptive
+                                             weighting (gating)"), i.e.
+                    H_t = gamma_t H_{t-1} + k_t k_t^T,  U_t = gamma_t U_{t-1} + v_t k_t^T
+  adaptive ridge    lambda_t = a ||H_t||_F, so kappa_t <= (a+1)/a
+                                            (ai.info summary, "Key Contributions" 2 and
+                                             "Main Findings")
+  Frobenius norm    ||H_t||_F^2 = gamma_t^2 ||H_{t-1}||_F^2 + 2 gamma_t k_t^T H_{t-1} k_t
+                                  + ||k_t||^4   (expanding the square of the update above)
+  solver            Chebyshev Iteration on the spectral interval [mu, L] = [lambda_t,
+                    lambda_t + ||H_t||_F] (H_t is PSD, so its largest eigenvalue is at most
+                    ||H_t||_F), with the weight schedule omega_i = 4 / (4 - rho^2 omega_{i-1}),
+                    rho = (L - mu)/(L + mu), omega_0 = 2 (pith.science page, appendix fragments
+                    around Lemma 3 -- omega_i in [1, 2] and non-increasing -- and Lemma 4 with
+                    kappa = L/mu); the three-term Chebyshev semi-iterative form of Golub and
+                    Van Loan, "Matrix Computations" (cited in the pages' reference list)
+  exact mode        Cholesky solve of the same SPD system, for the pins only (the pages'
+                    exact-solver reference, ai.info summary "Key Contributions" 2)
+
+Readings taken where the pages are silent (each also listed in the design notes):
+  * x_0 = 0 and x_1 = c q (one Richardson step); "iters = r" means the iterate x_r is returned,
+    i.e. r - 1 matrix-vector products with A;
+  * gamma_t decays the state before token t writes (the gating fragment's eta_{t,i});
+  * when ||H_t||_F = 0 (only possible when every weighted key so far is zero, hence U_t = 0)
+    the solve is defined as x_t = 0 and o_t = 0;
+  * the initial state is zero unless the caller passes one.
+
+Everything is float64 and vectorised only across independent (batch, head) pairs; the loop
+over tokens is the plain sequential recurrence.
+"""
+from __future__ import annotations
+
+from typing import Optional
+
+import numpy as np
+
+
+# ------------------------------------------------------------------------------------------
+# Chebyshev Iteration
+# ------------------------------------------------------------------------------------------
+
+def chebyshev_weights(rho, iters: int):
+    """Weight schedule omega_0..omega_{iters-1}: omega_0 = 2, omega_i = 4 / (4 - rho^2 omega_{i-1}).
+
+    Follows the weight-schedule update on the pith.science page (Lemma 3 and the map used in
+    the proof of Lemma 4). ``rho`` may be an array (one value per system).
+    """
+    rho = np.asarray(rho, dtype=np.float64)
+    omegas = [np.full(rho.shape, 2.0)]
+    for _ in range(1, iters):
+        omegas.append(4.0 / (4.0 - rho * rho * omegas[-1]))
+    return omegas
+
+
+def chebyshev_rates(kappa: float):
+    """Rates of Lemma 4 (pith.science page): R_a = (sqrt(k)-1)/(sqrt(k)+1), R = (k-1)/(k+1) * R_a."""
+    ra = (np.sqrt(kappa) - 1.0) / (np.sqrt(kappa) + 1.0)
+    rho = (kappa - 1.0) / (kappa + 1.0)
+    return rho * ra, ra
+
+
+def chebyshev_solve(A: np.ndarray, b: np.ndarray, mu: np.ndarray, L: np.ndarray, iters: int,
+                    residuals: Optional[list] = None) -> np.ndarray:
+    """Chebyshev Iteration for A x = b with spectrum(A) in [mu, L]; batched over leading axes.
+
+    A: [..., D, D], b: [..., D], mu, L: [...]. Returns the iterate x_iters.
+    Starts at x_0 = 0; x_1 = x_0 + c (b - A x_0) = c b with c = 2/(L+mu); then for i >= 1
+      x_{i+1} = x_{i-1} + omega_i (x_i - x_{i-1} + c (b - A x_i)).
+    If ``residuals`` is a list, ||b - A x_i|| for i = 0..iters is appended to it.
+    """
+    c = (2.0 / (L + mu))[..., None]
+    rho = (L - mu) / (L + mu)
+    omegas = chebyshev_weights(rho, iters)
+    x_prev = np.zeros_like(b)
+    x = c * b
+    if residuals is not None:
+        residuals.append(np.linalg.norm(b, axis=-1))
+        residuals.append(np.linalg.norm(b - np.einsum("...ij,...j->...i", A, x), axis=-1))
+    for i in range(1, iters):
+        r = b - np.einsum("...ij,...j->...i", A, x)
+        w = omegas[i][..., None]
+        x_next = x_prev + w * (x - x_prev + c * r)
+        x_prev, x = x, x_next
+        if residuals is not None:
+            residuals.append(np.linalg.norm(b - np.einsum("...ij,...j->...i", A, x), axis=-1))
+    return x
+
+
+def cholesky_solve(A: np.ndarray, b: np.ndarray) -> np.ndarray:
+    """Exact solve of the SPD system A x = b through its Cholesky factor (batched)."""
+    Lc = np.linalg.cholesky(A)
+    y = np.linalg.solve(Lc, b[..., None])
+    return np.linalg.solve(np.swapaxes(Lc, -1, -2), y)[..., 0]
+
+
+# ------------------------------------------------------------------------------------------
+# One token of the recurrence
+# ------------------------------------------------------------------------------------------
+
+def _token(H, U, n2, q, k, v, g, a, iters, mode, residuals=None):
+    """Advance (H, U, n2) by one token for every system and return (H, U, n2, x, o).
+
+    H, U: [N, D, D]; n2, g: [N]; q, k, v: [N, D].
+    """
+    kHk = np.einsum("ni,nij,nj->n", k, H, k)
+    kk = np.einsum("ni,ni->n", k, k)
+    n2 = g * g * n2 + 2.0 * g * kHk + kk * kk
+    H = g[:, None, None] * H + k[:, :, None] * k[:, None, :]
+    U = g[:, None, None] * U + v[:, :, None] * k[:, None, :]
+    n = np.sqrt(n2)
+    lam = a * n
+    D = H.shape[-1]
+    zero = n2 == 0.0
+    A = H + lam[:, None, None] * np.eye(D)
+    if zero.any():  # degenerate systems: keep the solver finite, the result is forced to 0
+        A = np.where(zero[:, None, None], np.eye(D), A)
+    if mode == "cheb":
+        mu = np.where(zero, 1.0, lam)
+        L = np.where(zero, 1.0, lam + n)
+        x = chebyshev_solve(A, q, mu, L, iters, residuals)
+    elif mode == "exact":
+        x = cholesky_solve(A, q)
+    else:
+        raise ValueError(f"unknown mode {mode!r}")
+    x = np.where(zero[:, None], 0.0, x)
+    o = np.einsum("nij,nj->ni", U, x)
+    return H, U, n2, x, o
+
+
+# ------------------------------------------------------------------------------------------
+# Public entry points
+# ------------------------------------------------------------------------------------------
+
+def gka_forward_ref(q, k, v, gamma, a: float, iters: int, mode: str = "cheb",
+                    h0=None, u0=None, n2_0=None, return_residuals: bool = False):
+    """Sequential forward over a whole sequence.
+
+    q, k, v: [B, T, H, D]; gamma: [B, T, H]; optional initial state h0, u0 [B, H, D, D]
+    (U indexed [value dim][key dim]) and n2_0 [B, H] (= ||h0||_F^2 as carried by the caller).
+    Returns a dict with o [B,T,H,D], hnorm [B,T,H] (= ||H_t||_F from the recurrence),
+    h, u [B,H,D,D] and n2 [B,H] (final state), and optionally residuals
+    [B, T, H, iters+1] (||q_t - A_t x_i|| for i = 0..iters, Chebyshev mode only).
+    """
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    gamma = np.asarray(gamma, dtype=np.float64)
+    B, T, Hh, D = q.shape
+    N = B * Hh
+
+    def heads(x):  # [B,T,H,...] -> [B*H, T, ...]
+        return np.moveaxis(x, 2, 1).reshape((N, T) + x.shape[3:])
+
+    qh, kh, vh, gh = heads(q), heads(k), heads(v), heads(gamma)
+    H = np.zeros((N, D, D)) if h0 is None else np.asarray(h0, np.float64).reshape(N, D, D).copy()
+    U = np.zeros((N, D, D)) if u0 is None else np.asarray(u0, np.float64).reshape(N, D, D).copy()
+    n2 = np.zeros(N) if n2_0 is None else np.asarray(n2_0, np.float64).reshape(N).copy()
+    o = np.empty((N, T, D))
+    hn = np.empty((N, T))
+    res = np.empty((N, T, iters + 1)) if return_residuals else None
+    for t in range(T):
+        rl = [] if return_residuals else None
+        H, U, n2, _, o[:, t] = _token(H, U, n2, qh[:, t], kh[:, t], vh[:, t], gh[:, t], a, iters,
+                                      mode, rl)
+        hn[:, t] = np.sqrt(n2)
+        if return_residuals:
+            res[:, t] = np.stack(rl, axis=-1)
+
+    def unheads(x):  # [B*H, T, ...] -> [B,T,H,...]
+        return np.moveaxis(x.reshape((B, Hh, T) + x.shape[2:]), 1, 2)
+
+    out = dict(o=unheads(o), hnorm=unheads(hn), h=H.reshape(B, Hh, D, D),
+               u=U.reshape(B, Hh, D, D), n2=n2.reshape(B, Hh))
+    if return_residuals:
+        out["residuals"] = unheads(res)
+    return out
+
+
+def gka_step_ref(q, k, v, gamma, a: float, iters: int, h, u, n2, mode: str = "cheb"):
+    """One recurrent decode step: update the carried state with the token, then solve.
+
+    q, k, v: [B, H, D]; gamma: [B, H]; h, u: [B, H, D, D]; n2: [B, H].
+    Returns (o [B,H,D], h, u, n2) -- new arrays, inputs untouched.
+    """
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    B, Hh, D = q.shape
+    N = B * Hh
+    H2, U2, n22, _, o = _token(np.asarray(h, np.float64).reshape(N, D, D),
+                               np.asarray(u, np.float64).reshape(N, D, D),
+                               np.asarray(n2, np.float64).reshape(N),
+                               q.reshape(N, D), k.reshape(N, D), v.reshape(N, D),
+                               np.asarray(gamma, np.float64).reshape(N), a, iters, mode)
+    return (o.reshape(B, Hh, D), H2.reshape(B, Hh, D, D), U2.reshape(B, Hh, D, D),
+            n22.reshape(B, Hh))
+
+
+def ridge_bruteforce(q, k, v, gamma, a: float):
+    """Solve the weighted ridge objective directly for one head, by least squares.
+
+    q, k, v: [T, D]; gamma: [T]. For every t the weights eta_{t,i} = prod_{j=i+1}^{t} gamma_j
+    are formed as plain products, H_t = sum_i eta_{t,i} k_i k_i^T is summed directly,
+    lambda_t = a ||H_t||_F, and
+        min_S  sum_{i<=t} eta_{t,i} ||v_i - S k_i||^2 + lambda_t ||S||_F^2
+    is solved as the stacked least-squares problem [sqrt(eta_i) k_i^T ; sqrt(lambda_t) I] S^T
+    ~= [sqrt(eta_i) v_i^T ; 0]. Returns o [T, D] with o_t = S_t q_t and hnorm [T].
+    """
+    q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
+    gamma = np.asarray(gamma, dtype=np.float64)
+    T, D = k.shape
+    o = np.zeros((T, D))
+    hn = np.zeros(T)
+    for t in range(T):
+        eta = np.array([np.prod(gamma[i + 1:t + 1]) for i in range(t + 1)])
+        Ht = sum(eta[i] * np.outer(k[i], k[i]) for i in range(t + 1))
+        hn[t] = np.linalg.norm(Ht, "fro")
+        lam = a * hn[t]
+        X = np.vstack([np.sqrt(eta)[:, None] * k[:t + 1], np.sqrt(lam) * np.eye(D)])
+        Y = np.vstack([np.sqrt(eta)[:, None] * v[:t + 1], np.zeros((D, D))])
+        St, *_ = np.linalg.lstsq(X, Y, rcond=None)  # St = S^T, [D_k, D_v]
+        o[t] = St.T @ q[t]
+    return o, hn

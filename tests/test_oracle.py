@@ -1,0 +1,343 @@
+"""Pins of the float64 oracle against what the pages and the mathematics fix (CPU only).
+
+Every check here is independent of the oracle's own code path: brute-force least squares,
+directly summed weighted covariances, closed forms from eigen-decompositions and Chebyshev
+polynomials, special cases with textbook answers, and the numbers printed on the pages.
+"""
+import os
+
+import numpy as np
+import pytest
+
+from oracle import (chebyshev_rates, chebyshev_solve, chebyshev_weights, gka_forward_ref,
+                    gka_step_ref, ridge_bruteforce)
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _rand_inputs(rng, B, T, H, D, gate="sigmoid"):
+    q = rng.standard_normal((B, T, H, D))
+    k = rng.standard_normal((B, T, H, D))
+    v = rng.standard_normal((B, T, H, D))
+    q /= np.linalg.norm(q, axis=-1, keepdims=True)
+    k /= np.linalg.norm(k, axis=-1, keepdims=True)
+    if gate == "sigmoid":
+        g = 1.0 / (1.0 + np.exp(-rng.normal(1.5, 1.0, (B, T, H))))
+    elif gate == "with_zeros":
+        g = 1.0 / (1.0 + np.exp(-rng.normal(1.5, 1.0, (B, T, H))))
+        g[rng.random((B, T, H)) < 0.15] = 0.0
+    elif gate == "ones":
+        g = np.ones((B, T, H))
+    else:
+        raise ValueError(gate)
+    return q, k, v, g
+
+
+def _direct_states(k, v, g, t):
+    """H_t and U_t for one head summed from eta_{t,i} = prod_{j=i+1}^t gamma_j (no recurrence)."""
+    D = k.shape[-1]
+    Ht = np.zeros((D, D))
+    Ut = np.zeros((D, D))
+    for i in range(t + 1):
+        eta = np.prod(g[i + 1:t + 1])
+        Ht += eta * np.outer(k[i], k[i])
+        Ut += eta * np.outer(v[i], k[i])
+    return Ht, Ut
+
+
+def _cheb_T(r, x):
+    return np.polynomial.chebyshev.chebval(x, [0.0] * r + [1.0])
+
+
+def _rel(a, b):
+    return np.linalg.norm(a - b) / max(np.linalg.norm(b), 1e-300)
+
+
+# ------------------------------------------------------------------------------------------
+# 1. the objective: exact mode == brute-force weighted ridge regression
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("gate", ["sigmoid", "with_zeros", "ones"])
+@pytest.mark.parametrize("D", [1, 4, 16])
+def test_exact_mode_matches_bruteforce_ridge(gate, D):
+    rng = np.random.default_rng(100 + D)
+    T, a = 40, 0.1
+    q, k, v, g = _rand_inputs(rng, 1, T, 2, D, gate)
+    ref = gka_forward_ref(q, k, v, g, a, iters=1, mode="exact")
+    for h in range(2):
+        o_bf, hn_bf = ridge_bruteforce(q[0, :, h], k[0, :, h], v[0, :, h], g[0, :, h], a)
+        assert _rel(ref["o"][0, :, h], o_bf) < 1e-10
+        np.testing.assert_allclose(ref["hnorm"][0, :, h], hn_bf, rtol=1e-12, atol=0)
+
+
+def test_bruteforce_is_a_minimiser():
+    """The brute-force S_t satisfies the normal equations of the weighted objective (sanity of the pin)."""
+    rng = np.random.default_rng(7)
+    T, D, a = 12, 5, 0.05
+    q, k, v, g = _rand_inputs(rng, 1, T, 1, D)
+    k0, v0, g0 = k[0, :, 0], v[0, :, 0], g[0, :, 0]
+    t = T - 1
+    Ht, Ut = _direct_states(k0, v0, g0, t)
+    lam = a * np.linalg.norm(Ht)
+    # objective f(S) = sum eta ||v - S k||^2 + lam ||S||^2 ; gradient at S* must vanish
+    S = Ut @ np.linalg.inv(Ht + lam * np.eye(D))
+    grad = -2 * sum(np.prod(g0[i + 1:t + 1]) * np.outer(v0[i] - S @ k0[i], k0[i]) for i in range(t + 1))
+    grad += 2 * lam * S
+    assert np.abs(grad).max() < 1e-10
+    # and the same minimiser gives o_t = S q_t, which the brute force returns
+    o_bf, _ = ridge_bruteforce(q[0, :, 0], k0, v0, g0, a)
+    assert _rel(o_bf[t], S @ q[0, t, 0]) < 1e-10
+
+
+# ------------------------------------------------------------------------------------------
+# 2. the Frobenius-norm recurrence and the condition-number bound
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("gate", ["sigmoid", "with_zeros"])
+def test_norm_recurrence_equals_direct_norm(gate):
+    rng = np.random.default_rng(11)
+    T, D = 48, 8
+    q, k, v, g = _rand_inputs(rng, 2, T, 1, D, gate)
+    # a nonzero initial state: random PSD h0, any u0, carried n2 = ||h0||_F^2
+    Z = rng.standard_normal((2, 1, D, 3 * D))
+    h0 = Z @ np.swapaxes(Z, -1, -2) / D
+    u0 = rng.standard_normal((2, 1, D, D))
+    n20 = np.sum(h0 * h0, axis=(-1, -2))
+    ref = gka_forward_ref(q, k, v, g, 0.1, 4, h0=h0, u0=u0, n2_0=n20)
+    for b in range(2):
+        Hd = h0[b, 0].copy()
+        for t in range(T):
+            Hd = g[b, t, 0] * Hd + np.outer(k[b, t, 0], k[b, t, 0])
+            assert abs(ref["hnorm"][b, t, 0] - np.linalg.norm(Hd)) <= 1e-12 * np.linalg.norm(Hd)
+        np.testing.assert_allclose(ref["h"][b, 0], Hd, rtol=0, atol=1e-12 * np.abs(Hd).max())
+
+
+@pytest.mark.parametrize("a", [0.1, 0.05, 0.02])
+def test_condition_number_bound(a):
+    rng = np.random.default_rng(int(a * 1000))
+    T, D = 32, 6
+    q, k, v, g = _rand_inputs(rng, 1, T, 1, D, "with_zeros")
+    ref = gka_forward_ref(q, k, v, g, a, 2)
+    bound = (a + 1) / a
+    for t in range(T):
+        Ht, _ = _direct_states(k[0, :, 0], v[0, :, 0], g[0, :, 0], t)
+        lam = a * ref["hnorm"][0, t, 0]
+        ev = np.linalg.eigvalsh(Ht + lam * np.eye(D))
+        assert ev.max() / ev.min() <= bound * (1 + 1e-12)
+        # the interval [lam, lam + ||H||_F] used by the solver contains the spectrum
+        assert ev.min() >= lam * (1 - 1e-12) and ev.max() <= (lam + ref["hnorm"][0, t, 0]) * (1 + 1e-12)
+
+
+# ------------------------------------------------------------------------------------------
+# 3. Chebyshev mode: closed form, error bound, weight schedule
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("r", [1, 2, 3, 8, 10, 12])
+def test_chebyshev_mode_matches_polynomial_closed_form(r):
+    """x_r = x* - P_r(A) (x* - x_0), P_r(z) = T_r((L+mu-2z)/(L-mu)) / T_r((L+mu)/(L-mu)), x_0 = 0."""
+    rng = np.random.default_rng(200 + r)
+    T, D, a = 20, 7, 0.05
+    q, k, v, g = _rand_inputs(rng, 1, T, 1, D)
+    ref = gka_forward_ref(q, k, v, g, a, r)
+    k0, v0, g0, q0 = k[0, :, 0], v[0, :, 0], g[0, :, 0], q[0, :, 0]
+    for t in range(T):
+        Ht, Ut = _direct_states(k0, v0, g0, t)
+        n = np.linalg.norm(Ht)
+        mu, L = a * n, a * n + n
+        A = Ht + mu * np.eye(D)
+        w, Q = np.linalg.eigh(A)
+        xs = Q @ ((Q.T @ q0[t]) / w)
+        P = _cheb_T(r, (L + mu - 2 * w) / (L - mu)) / _cheb_T(r, (L + mu) / (L - mu))
+        xr = xs - Q @ (P * (Q.T @ xs))
+        assert _rel(ref["o"][0, t, 0], Ut @ xr) < 1e-10
+
+
+def test_chebyshev_converges_to_exact():
+    rng = np.random.default_rng(5)
+    q, k, v, g = _rand_inputs(rng, 1, 16, 2, 8)
+    ex = gka_forward_ref(q, k, v, g, 0.1, 1, mode="exact")["o"]
+    ch = gka_forward_ref(q, k, v, g, 0.1, 80)["o"]
+    assert _rel(ch, ex) < 1e-12
+
+
+@pytest.mark.parametrize("a,r", [(0.1, 8), (0.05, 10), (0.02, 12), (0.02, 3)])
+def test_chebyshev_error_bound(a, r):
+    """||x_r - x*||_A <= 2 R_a^r / (1 + R_a^{2r}) ||x*||_A for spectrum in [a, 1+a] (kappa=(1+a)/a)."""
+    rng = np.random.default_rng(300 + r)
+    D = 24
+    kappa = (1 + a) / a
+    _, ra = chebyshev_rates(kappa)
+    bound = 2 * ra ** r / (1 + ra ** (2 * r))
+    worst = 0.0
+    for trial in range(20):
+        Qm, _ = np.linalg.qr(rng.standard_normal((D, D)))
+        ev = np.concatenate([[a, 1 + a], rng.uniform(a, 1 + a, D - 2)])
+        A = (Qm * ev) @ Qm.T
+        b = rng.standard_normal(D)
+        xs = np.linalg.solve(A, b)
+        xr = chebyshev_solve(A, b, np.array(a), np.array(1 + a), r)
+        e = xr - xs
+        ratio = np.sqrt(e @ A @ e) / np.sqrt(xs @ A @ xs)
+        worst = max(worst, ratio)
+        assert ratio <= bound * (1 + 1e-9)
+    # the bound is attained in the worst case: equioscillation makes it tight for some rhs
+    assert worst > 0.05 * bound
+
+
+def test_chebyshev_residual_tracking():
+    rng = np.random.default_rng(9)
+    D, r = 10, 6
+    A = np.diag(np.linspace(0.1, 1.1, D))
+    b = rng.standard_normal(D)
+    res = []
+    x = chebyshev_solve(A, b, np.array(0.1), np.array(1.1), r, residuals=res)
+    assert len(res) == r + 1
+    assert abs(res[0] - np.linalg.norm(b)) < 1e-14
+    assert abs(res[-1] - np.linalg.norm(b - A @ x)) < 1e-13
+
+
+@pytest.mark.parametrize("kappa", [1.5, 11.0, 21.0, 51.0, 500.0])
+def test_weight_schedule_lemmas(kappa):
+    """Lemma 3: omega_i in [1, 2], non-increasing, above omega*_1; Lemma 4: rate R = rho R_a."""
+    rho = (kappa - 1) / (kappa + 1)
+    om = np.array([float(w) for w in chebyshev_weights(rho, 40)])
+    ostar = 2.0 / (1.0 + np.sqrt(1.0 - rho * rho))
+    R, _ = chebyshev_rates(kappa)
+    assert om[0] == 2.0
+    assert np.all(om >= 1.0) and np.all(om <= 2.0)
+    assert np.all(np.diff(om) <= 1e-15)
+    assert np.all(om - ostar >= -1e-15)  # strictly above in exact arithmetic; fp64 reaches it
+    assert om[1] > ostar
+    for i in range(40):
+        assert om[i] - ostar <= R ** i * (om[0] - ostar) * (1 + 1e-12)
+    # omega* is the fixed point of the update map
+    assert abs(4.0 / (4.0 - rho * rho * ostar) - ostar) < 1e-14
+
+
+def test_lemma4_printed_rates():
+    """Reproduce every rate the pages print for kappa = 1.02/0.02 = 51, to the printed digits."""
+    rows = []
+    with open(os.path.join(GOLDEN, "lemma4_kappa51.txt")) as f:
+        for line in f:
+            if line.strip() and not line.startswith("#"):
+                name, p, val, sig = line.split()
+                rows.append((name, int(p), float(val), int(sig)))
+    assert len(rows) == 10
+    kappa = 1.02 / 0.02
+    assert abs(kappa - 51.0) < 1e-12
+    R, Ra = chebyshev_rates(kappa)
+    for name, p, val, sig in rows:
+        got = (R if name == "R" else Ra) ** p
+        # the printed value is the computed one cut to `sig` significant digits (the pages round
+        # most values and truncate R^30 = 6.5e-5 to 6e-5): within one unit of the last digit
+        ulp = 10.0 ** (np.floor(np.log10(val)) - sig + 1)
+        assert abs(got - val) < ulp, (name, p, got, val)
+
+
+# ------------------------------------------------------------------------------------------
+# 4. special cases with closed forms
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("r", [1, 2, 5, 8, 10])
+def test_gamma_zero_closed_form(r):
+    """gamma = 0: H_t = k_t k_t^T, lambda = a||k||^2; o_t = (1 - (-1)^r / T_r(1+2a)) v_t k.q / ((1+a)||k||^2)."""
+    rng = np.random.default_rng(400 + r)
+    a = 0.05
+    q, k, v, _ = _rand_inputs(rng, 2, 10, 3, 9)
+    k *= rng.uniform(0.5, 2.0, k.shape[:-1])[..., None]  # non-unit keys too
+    g = np.zeros(k.shape[:-1])
+    ch = gka_forward_ref(q, k, v, g, a, r)["o"]
+    ex = gka_forward_ref(q, k, v, g, a, r, mode="exact")["o"]
+    kk = np.sum(k * k, -1)
+    base = v * (np.sum(k * q, -1) / ((1 + a) * kk))[..., None]
+    fac = 1 - (-1) ** r / _cheb_T(r, 1 + 2 * a)
+    np.testing.assert_allclose(ex, base, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(ch, fac * base, rtol=1e-12, atol=1e-14)
+
+
+@pytest.mark.parametrize("r", [1, 4, 9])
+def test_scalar_d1_closed_form(r):
+    rng = np.random.default_rng(500 + r)
+    a, T = 0.1, 30
+    q = rng.standard_normal((1, T, 1, 1))
+    k = rng.standard_normal((1, T, 1, 1))
+    v = rng.standard_normal((1, T, 1, 1))
+    g = rng.uniform(0, 1, (1, T, 1))
+    out = gka_forward_ref(q, k, v, g, a, r)["o"][0, :, 0, 0]
+    h = u = 0.0
+    fac = 1 - (-1) ** r / _cheb_T(r, 1 + 2 * a)
+    for t in range(T):
+        h = g[0, t, 0] * h + k[0, t, 0, 0] ** 2
+        u = g[0, t, 0] * u + v[0, t, 0, 0] * k[0, t, 0, 0]
+        xs = q[0, t, 0, 0] / (h * (1 + a))
+        assert out[t] == pytest.approx(u * fac * xs, rel=1e-12)
+
+
+def test_zero_keys_give_zero_output():
+    rng = np.random.default_rng(13)
+    q, k, v, g = _rand_inputs(rng, 1, 12, 2, 4)
+    k[:, :5] = 0.0
+    for mode in ("cheb", "exact"):
+        ref = gka_forward_ref(q, k, v, g, 0.1, 6, mode=mode)
+        assert np.all(np.isfinite(ref["o"]))
+        assert np.all(ref["o"][:, :5] == 0.0)
+        assert np.all(ref["hnorm"][:, :5] == 0.0)
+        assert np.all(np.abs(ref["o"][:, 5:]) > 0)
+
+
+# ------------------------------------------------------------------------------------------
+# 5. metamorphic properties
+# ------------------------------------------------------------------------------------------
+
+def test_linear_in_v_and_q():
+    rng = np.random.default_rng(21)
+    q, k, v, g = _rand_inputs(rng, 1, 16, 2, 6)
+    q2, _, v2, _ = _rand_inputs(rng, 1, 16, 2, 6)
+    f = lambda qq, vv: gka_forward_ref(qq, k, vv, g, 0.05, 7)["o"]
+    np.testing.assert_allclose(f(q, 2 * v - 3 * v2), 2 * f(q, v) - 3 * f(q, v2), rtol=1e-11, atol=1e-12)
+    np.testing.assert_allclose(f(0.5 * q + q2, v), 0.5 * f(q, v) + f(q2, v), rtol=1e-11, atol=1e-12)
+
+
+def test_heads_and_batches_are_independent():
+    rng = np.random.default_rng(22)
+    q, k, v, g = _rand_inputs(rng, 2, 10, 3, 5)
+    o = gka_forward_ref(q, k, v, g, 0.1, 5)["o"]
+    perm = [2, 0, 1]
+    op = gka_forward_ref(q[:, :, perm], k[:, :, perm], v[:, :, perm], g[:, :, perm], 0.1, 5)["o"]
+    np.testing.assert_array_equal(op, o[:, :, perm])
+    o1 = gka_forward_ref(q[1:], k[1:], v[1:], g[1:], 0.1, 5)["o"]
+    np.testing.assert_array_equal(o1, o[1:])
+
+
+def test_split_sequence_with_carried_state():
+    rng = np.random.default_rng(23)
+    q, k, v, g = _rand_inputs(rng, 2, 30, 2, 6)
+    full = gka_forward_ref(q, k, v, g, 0.05, 10)
+    p1 = gka_forward_ref(q[:, :13], k[:, :13], v[:, :13], g[:, :13], 0.05, 10)
+    p2 = gka_forward_ref(q[:, 13:], k[:, 13:], v[:, 13:], g[:, 13:], 0.05, 10,
+                         h0=p1["h"], u0=p1["u"], n2_0=p1["n2"])
+    np.testing.assert_allclose(np.concatenate([p1["o"], p2["o"]], 1), full["o"], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(p2["h"], full["h"], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(p2["n2"], full["n2"], rtol=1e-12)
+
+
+def test_step_chain_equals_forward():
+    rng = np.random.default_rng(24)
+    q, k, v, g = _rand_inputs(rng, 2, 9, 3, 5)
+    full = gka_forward_ref(q, k, v, g, 0.1, 8)
+    B, T, H, D = q.shape
+    h, u, n2 = np.zeros((B, H, D, D)), np.zeros((B, H, D, D)), np.zeros((B, H))
+    for t in range(T):
+        o, h, u, n2 = gka_step_ref(q[:, t], k[:, t], v[:, t], g[:, t], 0.1, 8, h, u, n2)
+        np.testing.assert_allclose(o, full["o"][:, t], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(h, full["h"], rtol=1e-12, atol=1e-14)
+
+
+def test_residuals_shape_and_decay():
+    rng = np.random.default_rng(25)
+    q, k, v, g = _rand_inputs(rng, 1, 8, 2, 6)
+    out = gka_forward_ref(q, k, v, g, 0.1, 10, return_residuals=True)
+    res = out["residuals"]
+    assert res.shape == (1, 8, 2, 11)
+    np.testing.assert_allclose(res[..., 0], np.linalg.norm(q, axis=-1), rtol=1e-14)
+    assert np.all(res[..., -1] < 0.05 * res[..., 0])
