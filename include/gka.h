@@ -1,0 +1,127 @@
+/*
+ * gka.h -- C ABI of the MI355X (gfx950) Gated KalmaNet forward library, libgka.so.
+ *
+ * The layer (arXiv 2511.21016, "Gated KalmaNet: A Fading Memory Layer Through Test-Time Ridge
+ * Regression"). For every batch row b, head h and token t it keeps the gated statistics
+ *     H_t = gamma_t H_{t-1} + k_t k_t^T          (D x D, symmetric PSD)
+ *     U_t = gamma_t U_{t-1} + v_t k_t^T          (D x D, indexed [value dim][key dim])
+ * (pith.science page, appendix fragment "Adaptive weighting (gating)": eta_{t,i} is the
+ * product of gamma_j for j = i+1..t), sets the adaptive ridge lambda_t = a ||H_t||_F (ai.info
+ * summary, "Key Contributions" 2: the condition number is then at most (a+1)/a), solves
+ * (H_t + lambda_t I) x_t = q_t with `iters` Chebyshev iterations on the interval
+ * [lambda_t, lambda_t + ||H_t||_F] (ai.info summary, "Methodology in Plain English"; weight
+ * schedule of Lemma 3/4 on the pith.science page) and emits o_t = U_t x_t.
+ *
+ * Conventions shared by both entry points
+ *   - Every data pointer is a DEVICE pointer owned by the caller; the library keeps no global
+ *     state and allocates nothing. `stream` is a hipStream_t (NULL = the default stream); all
+ *     work is enqueued on it and the call returns without synchronising.
+ *   - Tensors are dense, contiguous, row-major: q, k, v, o are [B, T, H, D] (prefill) or
+ *     [B, H, D] (decode) in `dtype`; gamma is float32 [B, T, H] / [B, H] with values in [0, 1];
+ *     h_state and u_state are float32 [B, H, D, D]; hnorm2 is float32 [B, H] holding
+ *     ||H||_F^2 of the carried state.
+ *   - q and k are used as given (the caller l2-normalises them, caption of Figure 2 on the
+ *     pith.science page). gamma = 0 is allowed.
+ *   - Chebyshev convention: x_0 = 0, x_1 = 2 q / (L + mu), three-term recurrence with
+ *     omega_0 = 2; `iters` = r returns x_r (r - 1 products with the system matrix).
+ *     If ||H_t||_F = 0 the output o_t is 0.
+ *   - o is rounded to `dtype` (round to nearest even for bf16). Results are deterministic
+ *     run to run (no atomics in any reduction).
+ *   - Errors: every argument is checked on the host before anything is enqueued; on an error
+ *     the call returns its status and writes nothing. GKA_ERR_HIP reports a failed launch;
+ *     faults inside a kernel surface at the caller's next synchronisation of `stream`.
+ */
+#ifndef GKA_H
+#define GKA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  GKA_OK = 0,
+  GKA_ERR_NULL = 1,      /* a required pointer is NULL, or the state pointers are mixed  */
+  GKA_ERR_SHAPE = 2,     /* B, T, H, D, chunk or segments outside the supported set        */
+  GKA_ERR_VALUE = 3,     /* a <= 0 or not finite, iters outside [1, GKA_MAX_ITERS]           */
+  GKA_ERR_DTYPE = 4,     /* dtype not one of gka_dtype                                       */
+  GKA_ERR_WORKSPACE = 5, /* workspace missing or smaller than gka_fwd_workspace_bytes()      */
+  GKA_ERR_HIP = 6,       /* a kernel launch failed                                           */
+  GKA_ERR_ALIAS = 7      /* o overlaps an input tensor                                       */
+} gka_status;
+
+typedef enum { GKA_BF16 = 0, GKA_FP32 = 1 } gka_dtype;
+
+#define GKA_MAX_ITERS 64
+
+/*
+ * Problem description shared by both entry points.
+ *   B, H     batch rows and heads, >= 1
+ *   T        tokens per sequence (prefill; ignored by gka_step), >= 0; any T is allowed, a
+ *            last partial chunk is handled exactly
+ *   D        head dimension (key dim = value dim): bf16 {32, 64, 128}, fp32 {16, 32, 64}
+ *   chunk    tokens per chunk for the chunk-wise form (prefill; ignored by gka_step):
+ *            bf16 {32, 64}, fp32 {16, 32, 64}. The result does not depend on it beyond
+ *            rounding (N = ceil(T / chunk) chunks).
+ *   iters    Chebyshev iterations r, 1 <= r <= GKA_MAX_ITERS
+ *   a        ridge scale, a > 0 and finite
+ *   dtype    element type of q, k, v, o (gka_dtype)
+ *   segments prefill only: sequence segments scanned in parallel; 0 = chosen by the library,
+ *            otherwise 1 <= segments (clamped to the number of chunks)
+ */
+typedef struct {
+  int32_t B, T, H, D, chunk, iters;
+  float a;
+  int32_t dtype;
+  int32_t segments;
+} gka_params;
+
+/* Bytes of device workspace gka_fwd_chunked needs for *p (0 when none), or 0 for bad *p. */
+size_t gka_fwd_workspace_bytes(const gka_params* p);
+
+/*
+ * Chunk-wise forward over whole sequences (prefill / training forward). The chunk-wise form
+ * follows "Methodology in Plain English" on the ai.info summary: chunks of C tokens, only the
+ * chunk-initial states are carried sequentially, and ||H_t||_F comes from a closed form over the
+ * chunk's key Gram matrix ("Key Contributions" 3).
+ *   q, k, v   [B, T, H, D] dtype, read
+ *   gamma     [B, T, H] float32, read
+ *   o         [B, T, H, D] dtype, written; must not overlap q, k or v
+ *   h_state, u_state, hnorm2
+ *             all NULL: start from the zero state and return no final state; or all non-NULL:
+ *             read as the initial state and overwritten with the final state (in place)
+ *   hnorm_t   optional [B, T, H] float32: ||H_t||_F of every token, written
+ *   workspace device scratch of at least gka_fwd_workspace_bytes(p) bytes (NULL if that is 0)
+ */
+gka_status gka_fwd_chunked(const gka_params* p, const void* q, const void* k, const void* v,
+                           const float* gamma, void* o, float* h_state, float* u_state,
+                           float* hnorm2, float* hnorm_t, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
+ * One recurrent decode step for B x H independent heads (the inference path, ai.info summary
+ * "Key Contributions" 4). The token first updates the carried state, then the system of the
+ * updated state is solved: o uses H_t and U_t including token t, and
+ * ||H_t||_F^2 = gamma^2 ||H_{t-1}||_F^2 + 2 gamma k^T H_{t-1} k + ||k||^4.
+ *   q, k, v   [B, H, D] dtype, read
+ *   gamma     [B, H] float32, read
+ *   o         [B, H, D] dtype, written
+ *   h_state, u_state [B, H, D, D] float32 and hnorm2 [B, H] float32: required, updated in place
+ */
+gka_status gka_step(const gka_params* p, const void* q, const void* k, const void* v,
+                    const float* gamma, void* o, float* h_state, float* u_state, float* hnorm2,
+                    void* stream);
+
+/* Static description of a status code. */
+const char* gka_status_str(int status);
+
+/* ABI version of this header (bumped on any signature change). */
+int gka_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GKA_H */

@@ -121,6 +121,8 @@ def _token(H, U, n2, q, k, v, g, a, iters, mode, residuals=None):
     n2 = g * g * n2 + 2.0 * g * kHk + kk * kk
     H = g[:, None, None] * H + k[:, :, None] * k[:, None, :]
     U = g[:, None, None] * U + v[:, :, None] * k[:, None, :]
+    if mode == "state":  # advance the state only (no solve); o is returned as zeros
+        return H, U, n2, np.zeros_like(q), np.zeros_like(q)
     n = np.sqrt(n2)
     lam = a * n
     D = H.shape[-1]
@@ -148,6 +150,9 @@ def _token(H, U, n2, q, k, v, g, a, iters, mode, residuals=None):
 def gka_forward_ref(q, k, v, gamma, a: float, iters: int, mode: str = "cheb",
                     h0=None, u0=None, n2_0=None, return_residuals: bool = False):
     """Sequential forward over a whole sequence.
+
+    ``mode``: "cheb" (Chebyshev Iteration, as the layer), "exact" (Cholesky solve), or
+    "state" (advance H, U, ||H||^2 only; o is all zeros).
 
     q, k, v: [B, T, H, D]; gamma: [B, T, H]; optional initial state h0, u0 [B, H, D, D]
     (U indexed [value dim][key dim]) and n2_0 [B, H] (= ||h0||_F^2 as carried by the caller).

@@ -1,0 +1,235 @@
+// C ABI of libgka.so: argument checks, segment plan, workspace layout and kernel launches.
+// Every check runs on the host before anything is enqueued, so a rejected call writes nothing.
+#include <algorithm>
+#include <cmath>
+#include <cstdint>
+
+#include "../../include/gka.h"
+#include "gka_internal.hpp"
+
+namespace {
+
+using gka::ChebConsts;
+using gka::FwdPlan;
+
+constexpr int kAbiVersion = 1;
+constexpr int kCUs = 256;  // MI355X compute units: the segment plan aims at >= 2 workgroups per CU
+
+bool dims_supported(int dtype, int D) {
+  if (dtype == GKA_BF16) return D == 32 || D == 64 || D == 128;
+  return D == 16 || D == 32 || D == 64;
+}
+bool chunk_supported(int dtype, int C) {
+  if (dtype == GKA_BF16) return C == 32 || C == 64;
+  return C == 16 || C == 32 || C == 64;
+}
+size_t elem_bytes(int dtype) { return dtype == GKA_BF16 ? 2 : 4; }
+
+gka_status check_common(const gka_params* p) {
+  if (!p) return GKA_ERR_NULL;
+  if (p->dtype != GKA_BF16 && p->dtype != GKA_FP32) return GKA_ERR_DTYPE;
+  if (p->B < 1 || p->H < 1 || !dims_supported(p->dtype, p->D)) return GKA_ERR_SHAPE;
+  if ((long long)p->B * p->H > (1LL << 30)) return GKA_ERR_SHAPE;
+  if (!(p->a > 0.0f) || !std::isfinite(p->a)) return GKA_ERR_VALUE;
+  if (p->iters < 1 || p->iters > GKA_MAX_ITERS) return GKA_ERR_VALUE;
+  return GKA_OK;
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+bool overlap(const void* a, size_t na, const void* b, size_t nb) {
+  const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
+  return x < y + nb && y < x + na;
+}
+
+// Chebyshev constants of the system divided by ||H_t||_F: spectrum in [mu, L] = [a, 1 + a],
+// c = 2 / (L + mu), rho = (L - mu) / (L + mu), omega_0 = 2, omega_i = 4 / (4 - rho^2 omega_{i-1})
+// (weight schedule of Lemma 3 / Lemma 4 on the pith.science page of arXiv 2511.21016).
+ChebConsts cheb_consts(float a, int iters) {
+  ChebConsts cc{};
+  const double ad = a;
+  const double mu = ad, L = 1.0 + ad;
+  const double rho = (L - mu) / (L + mu);
+  cc.a = a;
+  cc.c = (float)(2.0 / (L + mu));
+  cc.iters = iters;
+  double om[GKA_MAX_ITERS];
+  om[0] = 2.0;
+  for (int i = 1; i < iters; ++i) om[i] = 4.0 / (4.0 - rho * rho * om[i - 1]);
+  // x_{i+1} = (1 - omega_i) x_{i-1} + omega_i x_i + omega_i c r_i with x_0 = 0, x_1 = c r_0,
+  // so every iterate is a fixed combination of the residuals: x_i = sum_j b^(i)_j r_j.
+  double prev[GKA_MAX_ITERS] = {0.0}, cur[GKA_MAX_ITERS] = {0.0}, nxt[GKA_MAX_ITERS];
+  cur[0] = 2.0 / (L + mu);
+  for (int i = 1; i < iters; ++i) {
+    for (int j = 0; j < i; ++j) nxt[j] = (1.0 - om[i]) * prev[j] + om[i] * cur[j];
+    nxt[i] = om[i] * 2.0 / (L + mu);
+    for (int j = 0; j <= i; ++j) {
+      prev[j] = cur[j];
+      cur[j] = nxt[j];
+    }
+  }
+  for (int i = 0; i < iters; ++i) {
+    cc.omega[i] = (float)om[i];
+    cc.beta[i] = (float)cur[i];
+  }
+  return cc;
+}
+
+// Segment plan: N chunks per head cut into S segments of J chunks; more segments give more
+// workgroups (B*H*S) at the price of a summary pass over the keys and values.
+bool make_plan(const gka_params* p, FwdPlan& pl) {
+  pl.B = p->B;
+  pl.T = p->T;
+  pl.H = p->H;
+  pl.D = p->D;
+  pl.C = p->chunk;
+  pl.dtype = p->dtype;
+  pl.N = (p->T + p->chunk - 1) / p->chunk;
+  if (pl.N == 0) {
+    pl.S = pl.J = 0;
+    pl.ws_bytes = 0;
+    return true;
+  }
+  int S = p->segments;
+  if (S <= 0) {
+    const long long bh = (long long)p->B * p->H;
+    const long long want = (2LL * kCUs + bh - 1) / bh;  // workgroups >= 2 per CU
+    S = (int)std::min<long long>(want, pl.N);
+    if (pl.N / S < 2 && pl.N >= 2) S = std::max(1, pl.N / 2);  // keep >= 2 chunks per segment
+  }
+  if (S > pl.N) S = pl.N;
+  pl.J = (pl.N + S - 1) / S;
+  pl.S = (pl.N + pl.J - 1) / pl.J;  // no empty segments
+  if (pl.S == 1) {
+    pl.ws_bytes = 0;
+  } else {
+    const size_t bh = (size_t)p->B * p->H;
+    const size_t DD = (size_t)p->D * p->D;
+    pl.ws_bytes = bh * pl.S * 2 * DD * sizeof(float)  // per-segment (dH, dU), then start states
+                  + bh * pl.S * sizeof(float)          // per-segment log2 gate product
+                  + bh * sizeof(float);                // ||H||^2 at the start of segment 0
+    pl.ws_bytes = (pl.ws_bytes + 255) & ~(size_t)255;
+  }
+  return true;
+}
+
+gka_status check_fwd(const gka_params* p) {
+  gka_status st = check_common(p);
+  if (st != GKA_OK) return st;
+  if (p->T < 0 || !chunk_supported(p->dtype, p->chunk)) return GKA_ERR_SHAPE;
+  if (p->segments < 0) return GKA_ERR_SHAPE;
+  if ((long long)p->B * p->T * p->H * p->D > (1LL << 40)) return GKA_ERR_SHAPE;
+  return GKA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int gka_abi_version(void) { return kAbiVersion; }
+
+const char* gka_status_str(int s) {
+  switch (s) {
+    case GKA_OK: return "ok";
+    case GKA_ERR_NULL: return "required pointer is NULL (or state pointers mixed NULL / non-NULL)";
+    case GKA_ERR_SHAPE: return "unsupported shape, chunk, segment count or misaligned pointer";
+    case GKA_ERR_VALUE: return "a must be finite and > 0; iters in [1, GKA_MAX_ITERS]";
+    case GKA_ERR_DTYPE: return "unknown dtype";
+    case GKA_ERR_WORKSPACE: return "workspace missing or too small";
+    case GKA_ERR_HIP: return "HIP launch failed";
+    case GKA_ERR_ALIAS: return "output overlaps an input";
+  }
+  return "unknown status";
+}
+
+size_t gka_fwd_workspace_bytes(const gka_params* p) {
+  if (check_fwd(p) != GKA_OK) return 0;
+  FwdPlan pl;
+  make_plan(p, pl);
+  return pl.ws_bytes;
+}
+
+gka_status gka_fwd_chunked(const gka_params* p, const void* q, const void* k, const void* v,
+                           const float* gamma, void* o, float* h_state, float* u_state,
+                           float* hnorm2, float* hnorm_t, void* workspace,
+                           size_t workspace_bytes, void* stream) {
+  gka_status st = check_fwd(p);
+  if (st != GKA_OK) return st;
+  const bool any_state = h_state || u_state || hnorm2;
+  const bool all_state = h_state && u_state && hnorm2;
+  if (any_state && !all_state) return GKA_ERR_NULL;
+  if (p->T == 0) return GKA_OK;  // nothing to do; the state is unchanged
+  if (!q || !k || !v || !gamma || !o) return GKA_ERR_NULL;
+  if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return GKA_ERR_SHAPE;
+  if (h_state && (!aligned16(h_state) || !aligned16(u_state))) return GKA_ERR_SHAPE;
+  const size_t n_io = (size_t)p->B * p->T * p->H * p->D * elem_bytes(p->dtype);
+  if (overlap(o, n_io, q, n_io) || overlap(o, n_io, k, n_io) || overlap(o, n_io, v, n_io))
+    return GKA_ERR_ALIAS;
+  FwdPlan pl;
+  make_plan(p, pl);
+  if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes || !aligned16(workspace)))
+    return GKA_ERR_WORKSPACE;
+
+  const ChebConsts cc = cheb_consts(p->a, p->iters);
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const long long DD = (long long)p->D * p->D;
+  gka::WalkArgs wa{};
+  wa.q = q;
+  wa.k = k;
+  wa.v = v;
+  wa.gamma = gamma;
+  wa.o = o;
+  wa.hnorm_t = hnorm_t;
+  if (pl.S == 1) {
+    wa.in_h = h_state;
+    wa.in_u = u_state;
+    wa.in_bh = DD;
+    wa.in_seg = 0;
+    wa.n2_in = hnorm2;
+    wa.out_h = h_state;
+    wa.out_u = u_state;
+    wa.n2_out = hnorm2;
+    if (gka::launch_walk(pl, false, wa, cc, s) != hipSuccess) return GKA_ERR_HIP;
+    return GKA_OK;
+  }
+  const size_t bh = (size_t)p->B * p->H;
+  float* ws_states = static_cast<float*>(workspace);
+  float* ws_log2g = ws_states + bh * pl.S * 2 * DD;
+  float* ws_n2 = ws_log2g + bh * pl.S;
+  gka::WalkArgs sa = wa;
+  sa.sum_h = ws_states;
+  sa.sum_u = ws_states + DD;
+  sa.sum_bh = (long long)pl.S * 2 * DD;
+  sa.sum_seg = 2 * DD;
+  sa.log2g_out = ws_log2g;
+  if (gka::launch_walk(pl, true, sa, cc, s) != hipSuccess) return GKA_ERR_HIP;
+  if (gka::launch_scan(pl, ws_states, ws_log2g, h_state, u_state, hnorm2, ws_n2, s) != hipSuccess)
+    return GKA_ERR_HIP;
+  wa.in_h = ws_states;
+  wa.in_u = ws_states + DD;
+  wa.in_bh = (long long)pl.S * 2 * DD;
+  wa.in_seg = 2 * DD;
+  wa.n2_in = ws_n2;
+  wa.n2_out = hnorm2;
+  if (gka::launch_walk(pl, false, wa, cc, s) != hipSuccess) return GKA_ERR_HIP;
+  return GKA_OK;
+}
+
+gka_status gka_step(const gka_params* p, const void* q, const void* k, const void* v,
+                    const float* gamma, void* o, float* h_state, float* u_state, float* hnorm2,
+                    void* stream) {
+  gka_status st = check_common(p);
+  if (st != GKA_OK) return st;
+  if (!q || !k || !v || !gamma || !o || !h_state || !u_state || !hnorm2) return GKA_ERR_NULL;
+  if (!aligned16(h_state) || !aligned16(u_state)) return GKA_ERR_SHAPE;
+  const size_t n_io = (size_t)p->B * p->H * p->D * elem_bytes(p->dtype);
+  if (overlap(o, n_io, q, n_io) || overlap(o, n_io, k, n_io) || overlap(o, n_io, v, n_io))
+    return GKA_ERR_ALIAS;
+  const ChebConsts cc = cheb_consts(p->a, p->iters);
+  if (gka::launch_step(p->dtype, p->D, p->B * p->H, q, k, v, gamma, o, h_state, u_state, hnorm2,
+                       cc, static_cast<hipStream_t>(stream)) != hipSuccess)
+    return GKA_ERR_HIP;
+  return GKA_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,133 @@
+// Device-side building blocks shared by the GKA kernels (gfx950 / CDNA4 only).
+//
+// Matrix-core tiles are 16x16 outputs with float32 accumulation:
+//   bf16 operands: v_mfma_f32_16x16x32_bf16 (K step 32, 8 elements per lane)
+//   fp32 operands: v_mfma_f32_16x16x4_f32   (K step 4, 1 element per lane)
+// Lane l of a wave holds, for an A operand (16 x K, row-major in LDS), row l%16 and the
+// E consecutive columns starting at E*(l/16); for a B operand (K x 16) column l%16 and rows
+// E*(l/16)..+E-1. The 16x16 accumulator of lane l holds rows 4*(l/16)+i (i = 0..3) of
+// column l%16.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace gka {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+template <typename T>
+struct Mma;
+
+template <>
+struct Mma<bf16> {
+  static constexpr int K = 32;  // reduction depth of one instruction
+  static constexpr int E = 8;   // operand elements per lane
+  typedef bf16x8 frag;
+  __device__ static inline f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+  }
+  // operand fragment: E consecutive elements of row `row` starting at column `col`
+  __device__ static inline frag load(const bf16* base, int ld, int row, int col) {
+    return *reinterpret_cast<const bf16x8*>(base + row * ld + col);
+  }
+};
+
+template <>
+struct Mma<float> {
+  static constexpr int K = 4;
+  static constexpr int E = 1;
+  typedef float frag;
+  __device__ static inline f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x4f32(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline frag load(const float* base, int ld, int row, int col) {
+    return base[row * ld + col];
+  }
+};
+
+// ---- element conversions ----------------------------------------------------------------
+__device__ inline float to_f32(bf16 x) { return (float)x; }
+__device__ inline float to_f32(float x) { return x; }
+template <typename T>
+__device__ inline T from_f32(float x);
+template <>
+__device__ inline bf16 from_f32<bf16>(float x) { return (bf16)x; }  // round to nearest even
+template <>
+__device__ inline float from_f32<float>(float x) { return x; }
+
+// four consecutive elements <-> float4
+template <typename T>
+__device__ inline void store4(T* p, f32x4 v);
+template <>
+__device__ inline void store4<bf16>(bf16* p, f32x4 v) {
+  bf16x4 h;
+  h[0] = (bf16)v[0]; h[1] = (bf16)v[1]; h[2] = (bf16)v[2]; h[3] = (bf16)v[3];
+  *reinterpret_cast<bf16x4*>(p) = h;
+}
+template <>
+__device__ inline void store4<float>(float* p, f32x4 v) {
+  *reinterpret_cast<f32x4*>(p) = v;
+}
+// four consecutive elements as hi + lo parts: hi = round(v), lo = round(v - hi); for float the
+// value is exact and only hi is written
+template <typename T>
+__device__ inline void store4_split(T* hi, T* lo, f32x4 v);
+template <>
+__device__ inline void store4_split<bf16>(bf16* hi, bf16* lo, f32x4 v) {
+  bf16x4 h, l;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    h[i] = (bf16)v[i];
+    l[i] = (bf16)(v[i] - (float)h[i]);
+  }
+  *reinterpret_cast<bf16x4*>(hi) = h;
+  *reinterpret_cast<bf16x4*>(lo) = l;
+}
+template <>
+__device__ inline void store4_split<float>(float* hi, float*, f32x4 v) {
+  *reinterpret_cast<f32x4*>(hi) = v;
+}
+
+template <typename T>
+__device__ inline f32x4 load4(const T* p);
+template <>
+__device__ inline f32x4 load4<bf16>(const bf16* p) {
+  bf16x4 h = *reinterpret_cast<const bf16x4*>(p);
+  return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+}
+template <>
+__device__ inline f32x4 load4<float>(const float* p) {
+  return *reinterpret_cast<const f32x4*>(p);
+}
+
+// ---- wave reductions (wave64) -------------------------------------------------------------
+__device__ inline float wave_sum(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x += __shfl_xor(x, m, kWave);
+  return x;
+}
+
+// log2 of a gate with a finite floor for gamma = 0, so that differences of prefix sums stay
+// finite; 2^x for x at or below the floor underflows to exactly 0 in float32.
+constexpr float kLog2GateFloor = -160.0f;
+__device__ inline float log2_gate(float g) { return g > 0.0f ? log2f(g) : kLog2GateFloor; }
+
+// Chebyshev constants of the normalised system  (H_t / ||H_t||_F + a I) xh = q, whose spectrum
+// lies in [a, 1 + a]: step c = 2 / (1 + 2a), weights omega_i (omega_0 = 2), and the weights
+// beta_i of the iterate x_r = sum_i beta_i r_i as a combination of the residuals r_i of the
+// same iteration. Filled on the host.
+struct ChebConsts {
+  float a;
+  float c;
+  int iters;
+  float omega[64];
+  float beta[64];
+};
+
+}  // namespace gka

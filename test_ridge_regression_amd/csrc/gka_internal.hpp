@@ -1,0 +1,57 @@
+// Host-side launchers of the GKA kernels (internal to libgka.so; the public ABI is gka.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gka_common.hpp"
+
+namespace gka {
+
+// Decode step: one workgroup per (batch row, head).
+hipError_t launch_step(int dtype, int D, int BH, const void* q, const void* k, const void* v,
+                       const float* gamma, void* o, float* h, float* u, float* n2,
+                       const ChebConsts& cc, hipStream_t stream);
+
+// Prefill. Segment plan of one call: N chunks split into S segments of J chunks each.
+struct FwdPlan {
+  int B, T, H, D, C, dtype;
+  int N;  // chunks = ceil(T / C)
+  int S;  // segments
+  int J;  // chunks per segment
+  size_t ws_bytes;
+};
+
+// Arguments of the fused chunk walk (one workgroup per (segment, batch row x head)).
+// State matrices are float32 D x D, row-major; head bh, segment sg lives at
+// base + bh * *_bh + sg * *_seg (floats).
+struct WalkArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* gamma;
+  void* o;
+  float* hnorm_t;         // optional per-token ||H_t||_F [B, T, H]
+  const float* in_h;      // segment-start H (NULL: zero state)
+  const float* in_u;      // segment-start U
+  long long in_bh, in_seg;
+  const float* n2_in;     // [BH] ||H||_F^2 at the start of segment 0 (NULL: from in_h / zero)
+  float* out_h;           // optional final state of a single-segment walk, [BH][D][D]
+  float* out_u;
+  float* n2_out;          // optional final ||H||_F^2, written by the last segment
+  float* sum_h;           // summary mode: per-segment (dH, dU) from a zero start
+  float* sum_u;
+  long long sum_bh, sum_seg;
+  float* log2g_out;       // summary mode: per-segment log2 of the gate product [BH][S]
+};
+
+hipError_t launch_walk(const FwdPlan& pl, bool summary, const WalkArgs& a, const ChebConsts& cc,
+                       hipStream_t stream);
+
+// Affine scan over segments: start[s] = G_{s-1} start[s-1] + d_{s-1} (in place over d), final
+// state written to h/u when they are non-NULL; also copies hnorm2 to n2_seg0.
+hipError_t launch_scan(const FwdPlan& pl, float* ws_states, const float* ws_log2g, float* h,
+                       float* u, const float* hnorm2, float* n2_seg0, hipStream_t stream);
+
+}  // namespace gka

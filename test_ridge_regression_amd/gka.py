@@ -1,0 +1,172 @@
+"""Thin Python binding of libgka.so (argument marshalling only; every step runs in the HIP kernels).
+
+The names mirror the C ABI in include/gka.h:
+
+  fwd_chunked(q, k, v, gamma, a, iters, chunk, state=None, ...)   -> gka_fwd_chunked
+  step(q, k, v, gamma, a, iters, state)                             -> gka_step
+
+Tensors are torch device tensors (PyTorch supplies device memory and the current stream).
+If the shared library is missing, loading fails loudly: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libgka.so")
+
+GKA_BF16 = 0
+GKA_FP32 = 1
+GKA_MAX_ITERS = 64
+STATUS = {0: "GKA_OK", 1: "GKA_ERR_NULL", 2: "GKA_ERR_SHAPE", 3: "GKA_ERR_VALUE",
+          4: "GKA_ERR_DTYPE", 5: "GKA_ERR_WORKSPACE", 6: "GKA_ERR_HIP", 7: "GKA_ERR_ALIAS"}
+EXPORTED = ["gka_fwd_workspace_bytes", "gka_fwd_chunked", "gka_step", "gka_status_str",
+            "gka_abi_version"]
+
+
+class GkaParams(ctypes.Structure):
+    _fields_ = [("B", ctypes.c_int32), ("T", ctypes.c_int32), ("H", ctypes.c_int32),
+                ("D", ctypes.c_int32), ("chunk", ctypes.c_int32), ("iters", ctypes.c_int32),
+                ("a", ctypes.c_float), ("dtype", ctypes.c_int32), ("segments", ctypes.c_int32)]
+
+
+class GkaError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"{STATUS.get(status, status)}: {msg}")
+        self.status = status
+
+
+_lib = None
+
+
+def load(path: str = LIB_PATH) -> ctypes.CDLL:
+    """Load libgka.so (once) and declare the C signatures."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(path):
+        raise FileNotFoundError(
+            f"{path} is not built; run `python -m test_ridge_regression_amd.build` "
+            "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(path)
+    P = ctypes.POINTER(GkaParams)
+    vp, fp = ctypes.c_void_p, ctypes.c_void_p
+    lib.gka_fwd_workspace_bytes.argtypes = [P]
+    lib.gka_fwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.gka_fwd_chunked.argtypes = [P, vp, vp, vp, fp, vp, fp, fp, fp, fp, vp, ctypes.c_size_t, vp]
+    lib.gka_fwd_chunked.restype = ctypes.c_int
+    lib.gka_step.argtypes = [P, vp, vp, vp, fp, vp, fp, fp, fp, vp]
+    lib.gka_step.restype = ctypes.c_int
+    lib.gka_status_str.argtypes = [ctypes.c_int]
+    lib.gka_status_str.restype = ctypes.c_char_p
+    lib.gka_abi_version.argtypes = []
+    lib.gka_abi_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise GkaError(status, load().gka_status_str(status).decode())
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    if t.dtype == torch.bfloat16:
+        return GKA_BF16
+    if t.dtype == torch.float32:
+        return GKA_FP32
+    return -1
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _require_io(q, k, v, gamma, o, state):
+    """Marshalling checks the C side cannot make: dense tensors of matching element types."""
+    ts = [q, k, v, gamma, o] + ([state.h, state.u, state.n2] if state is not None else [])
+    for t in ts:
+        if not t.is_contiguous():
+            raise ValueError("libgka takes dense contiguous tensors")
+    if not (q.dtype == k.dtype == v.dtype == o.dtype):
+        raise ValueError("q, k, v and o must share one dtype (bfloat16 or float32)")
+    if gamma.dtype != torch.float32 or (state is not None and not (
+            state.h.dtype == state.u.dtype == state.n2.dtype == torch.float32)):
+        raise ValueError("gamma and the state are float32")
+    if k.shape != q.shape or v.shape != q.shape or o.shape != q.shape:
+        raise ValueError("q, k, v, o must have the same shape")
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+@dataclasses.dataclass
+class GkaState:
+    """Carried state of B x H heads: h, u float32 [B, H, D, D] (u is [value][key]), n2 float32
+    [B, H] = ||H||_F^2. Owned by the caller; updated in place by the library."""
+    h: torch.Tensor
+    u: torch.Tensor
+    n2: torch.Tensor
+
+    @staticmethod
+    def zeros(B: int, H: int, D: int, device="cuda") -> "GkaState":
+        return GkaState(torch.zeros(B, H, D, D, device=device, dtype=torch.float32),
+                        torch.zeros(B, H, D, D, device=device, dtype=torch.float32),
+                        torch.zeros(B, H, device=device, dtype=torch.float32))
+
+
+def make_params(B, T, H, D, chunk, iters, a, dtype_code, segments=0) -> GkaParams:
+    return GkaParams(int(B), int(T), int(H), int(D), int(chunk), int(iters), float(a),
+                     int(dtype_code), int(segments))
+
+
+def workspace_bytes(B, T, H, D, chunk, iters, a, dtype_code, segments=0) -> int:
+    p = make_params(B, T, H, D, chunk, iters, a, dtype_code, segments)
+    return int(load().gka_fwd_workspace_bytes(ctypes.byref(p)))
+
+
+def fwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor, a: float,
+                iters: int, chunk: int = 64, state: Optional[GkaState] = None,
+                return_hnorm: bool = False, segments: int = 0, out: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None, stream=None):
+    """gka_fwd_chunked on [B, T, H, D] tensors; returns o (and per-token ||H_t||_F [B,T,H]).
+
+    ``state`` (optional) is read as the initial state and overwritten with the final one.
+    """
+    lib = load()
+    B, T, H, D = q.shape
+    p = make_params(B, T, H, D, chunk, iters, a, _dtype_code(q), segments)
+    o = torch.empty_like(q) if out is None else out
+    _require_io(q, k, v, gamma, o, state)
+    hn = torch.empty(B, T, H, device=q.device, dtype=torch.float32) if return_hnorm else None
+    need = int(lib.gka_fwd_workspace_bytes(ctypes.byref(p)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    st = lib.gka_fwd_chunked(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(o),
+                             _ptr(state.h if state else None), _ptr(state.u if state else None),
+                             _ptr(state.n2 if state else None), _ptr(hn), _ptr(workspace),
+                             ctypes.c_size_t(workspace.numel() if workspace is not None else 0),
+                             _stream(stream))
+    _check(st)
+    return (o, hn) if return_hnorm else o
+
+
+def step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor, a: float,
+         iters: int, state: GkaState, out: Optional[torch.Tensor] = None, stream=None):
+    """gka_step on [B, H, D] tensors; updates ``state`` in place and returns o [B, H, D]."""
+    lib = load()
+    B, H, D = q.shape
+    p = make_params(B, 1, H, D, 64, iters, a, _dtype_code(q))
+    o = torch.empty_like(q) if out is None else out
+    _require_io(q, k, v, gamma, o, state)
+    st = lib.gka_step(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(o),
+                      _ptr(state.h), _ptr(state.u), _ptr(state.n2), _stream(stream))
+    _check(st)
+    return o

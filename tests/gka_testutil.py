@@ -1,0 +1,62 @@
+"""Helpers shared by the GPU parity tests: device copies of oracle inputs and error measures."""
+from __future__ import annotations
+
+import sys
+
+import numpy as np
+import torch
+
+from test_ridge_regression_amd import gka
+
+TORCH_DTYPE = {"bf16": torch.bfloat16, "fp32": torch.float32}
+# parity bars: relative L2 of o against the oracle's Chebyshev output, and ||H_t||_F per token
+TOL_O = {"bf16": 2e-2, "fp32": 1e-5}
+TOL_HNORM = 1e-3
+
+
+def log(msg: str):
+    """Name the case on stderr before each GPU step (a fault then still says where it was)."""
+    sys.stderr.write(f"[gka-test] {msg}\n")
+    sys.stderr.flush()
+
+
+def dev(x: np.ndarray, dtype: str = "fp32") -> torch.Tensor:
+    """Exact device copy of a float64 array whose values are representable in ``dtype``."""
+    t = torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).to("cuda")
+    return t.to(TORCH_DTYPE[dtype]).contiguous()
+
+
+def host(t: torch.Tensor) -> np.ndarray:
+    return t.detach().to(torch.float32).cpu().numpy().astype(np.float64)
+
+
+def rel_l2(got: np.ndarray, ref: np.ndarray) -> float:
+    den = np.linalg.norm(ref)
+    return float(np.linalg.norm(got - ref) / den) if den > 0 else float(np.linalg.norm(got))
+
+
+def max_rel(got: np.ndarray, ref: np.ndarray, floor: float = 1e-30) -> float:
+    return float(np.max(np.abs(got - ref) / np.maximum(np.abs(ref), floor)))
+
+
+def worst_head_rel_l2(got: np.ndarray, ref: np.ndarray) -> float:
+    """Worst relative L2 over (batch, head) slices of [B, T, H, D] arrays."""
+    B, _, H, _ = ref.shape
+    return max(rel_l2(got[b, :, h], ref[b, :, h]) for b in range(B) for h in range(H))
+
+
+def state_to_dev(h, u, n2) -> gka.GkaState:
+    return gka.GkaState(dev(h), dev(u), dev(n2))
+
+
+def run_prefill(q, k, v, g, a, iters, chunk, dtype, state=None, segments=0, return_hnorm=True):
+    """Run gka_fwd_chunked on device copies of float64 inputs; returns numpy results."""
+    st = None if state is None else state_to_dev(*state)
+    out = gka.fwd_chunked(dev(q, dtype), dev(k, dtype), dev(v, dtype), dev(g), a, iters, chunk,
+                          state=st, return_hnorm=return_hnorm, segments=segments)
+    torch.cuda.synchronize()
+    o, hn = out if return_hnorm else (out, None)
+    res = dict(o=host(o), hnorm=None if hn is None else host(hn))
+    if st is not None:
+        res.update(h=host(st.h), u=host(st.u), n2=host(st.n2))
+    return res

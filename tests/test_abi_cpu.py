@@ -1,0 +1,132 @@
+"""The C ABI without a GPU: the library loads, exports every declared symbol, and rejects bad
+arguments on the host (every rejected call returns before anything is enqueued)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from test_ridge_regression_amd import gka
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gka.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(gka.LIB_PATH):
+        from test_ridge_regression_amd.build import build_library
+        build_library()
+    return gka.load()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gka_\w+)\s*\(", text)))
+
+
+def test_header_declares_the_bound_functions():
+    assert declared_functions() == sorted(gka.EXPORTED)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    assert lib.gka_abi_version() == 1
+
+
+def test_status_strings(lib):
+    for code in range(8):
+        assert lib.gka_status_str(code)
+    assert lib.gka_status_str(99) == b"unknown status"
+
+
+# fake, 256-byte-aligned device addresses: never dereferenced because every case below fails a
+# host-side check before any launch
+ADDR = [0x7F0000000000 + i * (1 << 32) for i in range(12)]
+VP = [ctypes.c_void_p(x) for x in ADDR]
+
+
+def params(**kw):
+    base = dict(B=2, T=128, H=2, D=64, chunk=64, iters=8, a=0.1, dtype_code=gka.GKA_BF16)
+    base.update(kw)
+    seg = base.pop("segments", 0)
+    return gka.make_params(base["B"], base["T"], base["H"], base["D"], base["chunk"],
+                           base["iters"], base["a"], base["dtype_code"], seg)
+
+
+def fwd(lib, p, q=VP[0], k=VP[1], v=VP[2], g=VP[3], o=VP[4], h=None, u=None, n2=None, hn=None,
+        ws=None, wsb=0):
+    return lib.gka_fwd_chunked(ctypes.byref(p) if p is not None else None, q, k, v, g, o, h, u,
+                               n2, hn, ws, ctypes.c_size_t(wsb), None)
+
+
+def step(lib, p, q=VP[0], k=VP[1], v=VP[2], g=VP[3], o=VP[4], h=VP[5], u=VP[6], n2=VP[7]):
+    return lib.gka_step(ctypes.byref(p) if p is not None else None, q, k, v, g, o, h, u, n2, None)
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(dtype_code=7), 4),
+    (dict(D=48), 2), (dict(D=256), 2), (dict(dtype_code=gka.GKA_FP32, D=128), 2),
+    (dict(chunk=48), 2), (dict(chunk=16), 2), (dict(chunk=128), 2),
+    (dict(B=0), 2), (dict(H=0), 2), (dict(T=-1), 2), (dict(segments=-3), 2),
+    (dict(a=0.0), 3), (dict(a=-0.1), 3), (dict(a=float("nan")), 3), (dict(a=float("inf")), 3),
+    (dict(iters=0), 3), (dict(iters=65), 3),
+])
+def test_fwd_rejects_bad_params(lib, kw, code):
+    assert fwd(lib, params(**kw)) == code
+    assert lib.gka_fwd_workspace_bytes(ctypes.byref(params(**kw))) == 0
+
+
+def test_fwd_null_and_mixed_state(lib):
+    assert fwd(lib, None) == 1
+    assert fwd(lib, params(), q=None) == 1
+    assert fwd(lib, params(), g=None) == 1
+    assert fwd(lib, params(), o=None) == 1
+    assert fwd(lib, params(), h=VP[5]) == 1  # state pointers must be all NULL or all set
+    assert fwd(lib, params(), h=VP[5], u=VP[6]) == 1
+
+
+def test_fwd_alignment_alias_and_workspace(lib):
+    assert fwd(lib, params(), q=ctypes.c_void_p(ADDR[0] + 2)) == 2
+    assert fwd(lib, params(), h=ctypes.c_void_p(ADDR[5] + 4), u=VP[6], n2=VP[7]) == 2
+    assert fwd(lib, params(), o=VP[0]) == 7  # o == q
+    assert fwd(lib, params(), o=ctypes.c_void_p(ADDR[1] + 1024)) == 7  # o inside k
+    p = params(B=1, H=1, T=64 * 32, segments=8)
+    need = lib.gka_fwd_workspace_bytes(ctypes.byref(p))
+    assert need > 0
+    assert fwd(lib, p) == 5
+    assert fwd(lib, p, ws=VP[8], wsb=need - 1) == 5
+    assert fwd(lib, p, ws=ctypes.c_void_p(ADDR[8] + 8), wsb=need) == 5
+
+
+def test_fwd_empty_sequence_is_a_noop(lib):
+    # T = 0: valid, nothing is launched, the (absent or present) state is untouched
+    assert fwd(lib, params(T=0), q=None, k=None, v=None, g=None, o=None) == 0
+
+
+def test_workspace_plan(lib):
+    D = 128
+    one = lib.gka_fwd_workspace_bytes(ctypes.byref(params(D=D, B=1, H=1, T=64, segments=0)))
+    assert one == 0  # a single chunk: one segment, no workspace
+    p = params(B=8, H=8, T=2048, D=D)  # 32 chunks per head -> several segments
+    ws = lib.gka_fwd_workspace_bytes(ctypes.byref(p))
+    assert ws >= 64 * 2 * 2 * D * D * 4 and ws % 256 == 0
+    # explicit segment counts are clamped to the number of chunks
+    big = lib.gka_fwd_workspace_bytes(ctypes.byref(params(B=1, H=1, T=128, D=D, segments=50)))
+    two = lib.gka_fwd_workspace_bytes(ctypes.byref(params(B=1, H=1, T=128, D=D, segments=2)))
+    assert big == two > 0
+    assert lib.gka_fwd_workspace_bytes(ctypes.byref(params(B=1, H=1, T=128, D=D, segments=1))) == 0
+
+
+def test_step_rejects_bad_arguments(lib):
+    assert step(lib, None) == 1
+    assert step(lib, params(), h=None) == 1
+    assert step(lib, params(), n2=None) == 1
+    assert step(lib, params(D=96)) == 2
+    assert step(lib, params(iters=0)) == 3
+    assert step(lib, params(a=0.0)) == 3
+    assert step(lib, params(dtype_code=3)) == 4
+    assert step(lib, params(), h=ctypes.c_void_p(ADDR[5] + 8)) == 2
+    assert step(lib, params(), o=VP[2]) == 7

@@ -341,3 +341,14 @@ def test_residuals_shape_and_decay():
     assert res.shape == (1, 8, 2, 11)
     np.testing.assert_allclose(res[..., 0], np.linalg.norm(q, axis=-1), rtol=1e-14)
     assert np.all(res[..., -1] < 0.05 * res[..., 0])
+
+
+def test_state_only_mode_advances_the_same_state():
+    rng = np.random.default_rng(26)
+    q, k, v, g = _rand_inputs(rng, 2, 12, 2, 5)
+    a = gka_forward_ref(q, k, v, g, 0.1, 4)
+    b = gka_forward_ref(q, k, v, g, 0.1, 4, mode="state")
+    np.testing.assert_array_equal(a["h"], b["h"])
+    np.testing.assert_array_equal(a["u"], b["u"])
+    np.testing.assert_array_equal(a["n2"], b["n2"])
+    assert np.all(b["o"] == 0)
