@@ -1,0 +1,312 @@
+"""Benchmark of the GKA forward hot path on one MI355X; prints ONE JSON line on stdout.
+
+Step = one gka_fwd_chunked call over the prefill workload at the pages' figure shape
+(B=8, T=2048, H=8, D=128, chunk 64, a=0.05, 10 Chebyshev iterations, bf16 inputs, float32
+accumulation), inputs resident in HBM. ``value`` is prefill tokens/s (B*T per step time).
+The same line carries the recurrent-decode figures (batch 256 x 8 heads x D 128, 1000 timed
+gka_step calls on a float32 state warmed by 512 tokens), the roofline of the dominant kernel of
+each path (measured with HIP events on the library's stream), and the float64 CPU oracle timed
+on a bounded sample of the prefill workload on this host.
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps S] [--no-cpu]
+"""
+from __future__ import annotations
+
+import argparse
+import ctypes
+import json
+import os
+import platform
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_MFMA = 2.5e15  # MI355X dense bf16 matrix peak, FLOP/s
+PEAK_HBM = 8.0e12  # MI355X HBM3E, bytes/s
+
+
+def log(msg):
+    sys.stderr.write(f"[bench] {msg}\n")
+    sys.stderr.flush()
+
+
+class HipEvents:
+    """Raw HIP events through the runtime's C API (events on the library's stream)."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                 ctypes.c_void_p]
+        self.hip.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventSynchronize.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+
+    def create(self, n):
+        evs = []
+        for _ in range(n):
+            e = ctypes.c_void_p()
+            assert self.hip.hipEventCreate(ctypes.byref(e)) == 0
+            evs.append(e)
+        return evs
+
+    def record(self, ev, stream):
+        assert self.hip.hipEventRecord(ev, ctypes.c_void_p(stream)) == 0
+
+    def elapsed_ms(self, a, b):
+        ms = ctypes.c_float()
+        assert self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) == 0
+        return ms.value
+
+    def sync(self, ev):
+        assert self.hip.hipEventSynchronize(ev) == 0
+
+    def destroy(self, evs):
+        for e in evs:
+            self.hip.hipEventDestroy(e)
+
+
+def prefill_flops_per_token_head(D, C, r):
+    """Algorithmic flops of the chunk-wise forward per (token, head):
+    Chebyshev loop (r-1)(2D^2 + 4CD), output 2D^2 + 4CD, norms 2D^2 + 2CD + 2C^2, carry 4D^2."""
+    return D * D * (2 * r + 6) + C * D * (4 * r + 2) + 2 * C * C
+
+
+def decode_bytes_per_head(D, in_bytes=2):
+    """Algorithmic HBM bytes of one decode step per head: float32 H and U read and written,
+    q, k, v read and o written in the input dtype, gamma read, ||H||^2 read and written."""
+    return 16 * D * D + 4 * D * in_bytes + 4 + 8
+
+
+def bench_prefill(W, steps, warmup, ev):
+    import torch
+    from test_ridge_regression_amd import gka
+    from test_ridge_regression_amd import workloads as Wl
+
+    log(f"prefill inputs {W.name}")
+    q, k, v, g = Wl.make_workload(W)
+    d = lambda x: torch.from_numpy(x.astype(np.float32)).cuda().to(torch.bfloat16).contiguous()
+    qd, kd, vd = d(q), d(k), d(v)
+    gd = torch.from_numpy(g.astype(np.float32)).cuda()
+    del q, k, v
+    o = torch.empty_like(qd)
+    need = gka.workspace_bytes(W.B, W.T, W.H, W.D, W.chunk, W.iters, W.a, gka.GKA_BF16)
+    ws = torch.empty(max(need, 1), device="cuda", dtype=torch.uint8)
+    stream = torch.cuda.current_stream()
+    phase = ev.create(4 * steps)
+    arrs = [(ctypes.c_void_p * 4)(*phase[4 * i:4 * i + 4]) for i in range(steps)]
+    t0, t1 = ev.create(2)
+    log(f"prefill warmup {warmup}")
+    for _ in range(warmup):
+        gka.fwd_chunked(qd, kd, vd, gd, W.a, W.iters, W.chunk, out=o, workspace=ws)
+    torch.cuda.synchronize()
+    log(f"prefill timed {steps}")
+    ev.record(t0, stream.cuda_stream)
+    for i in range(steps):
+        gka.fwd_chunked(qd, kd, vd, gd, W.a, W.iters, W.chunk, out=o, workspace=ws,
+                        phase_events=arrs[i])
+    ev.record(t1, stream.cuda_stream)
+    ev.sync(t1)
+    torch.cuda.synchronize()
+    total_ms = ev.elapsed_ms(t0, t1)
+    walk = [ev.elapsed_ms(phase[4 * i + 2], phase[4 * i + 3]) for i in range(steps)]
+    summ = [ev.elapsed_ms(phase[4 * i + 0], phase[4 * i + 1]) for i in range(steps)]
+    scan = [ev.elapsed_ms(phase[4 * i + 1], phase[4 * i + 2]) for i in range(steps)]
+    ev.destroy(phase + [t0, t1])
+    segs = _segments(W)
+    return dict(total_ms=total_ms, ms_per_step=total_ms / steps, walk_ms=float(np.mean(walk)),
+                summary_ms=float(np.mean(summ)), scan_ms=float(np.mean(scan)), segments=segs,
+                o=o, inputs=(qd, kd, vd, gd))
+
+
+def _segments(W):
+    from test_ridge_regression_amd import gka
+    # the plan's segment count: workspace = B*H*S*(2 D^2 + 1)*4 + B*H*4 (rounded up to 256)
+    need = gka.workspace_bytes(W.B, W.T, W.H, W.D, W.chunk, W.iters, W.a, gka.GKA_BF16)
+    if need == 0:
+        return 1
+    bh = W.B * W.H
+    return int((need - bh * 4) // (bh * (2 * W.D * W.D + 1) * 4))
+
+
+def parity_sample(W, o_dev, heads=((0, 0), (7, 7))):
+    """Sampled heads of the timed prefill against the float64 oracle (full sequence)."""
+    from oracle import gka_forward_ref
+    from test_ridge_regression_amd import workloads as Wl
+
+    q, k, v, g = Wl.make_workload(W)
+    o = o_dev.float().cpu().numpy()
+    errs = []
+    for b, h in heads:
+        sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
+        ref = gka_forward_ref(q[sl], k[sl], v[sl], g[sl], W.a, W.iters)["o"]
+        errs.append(float(np.linalg.norm(o[sl] - ref) / np.linalg.norm(ref)))
+    return max(errs)
+
+
+def bench_decode(Wd, steps, ev):
+    import torch
+    from test_ridge_regression_amd import gka
+    from test_ridge_regression_amd import workloads as Wl
+
+    log(f"decode warm-up state: prefill of {Wd.warmup} tokens, B={Wd.B}")
+    q, k, v, g = Wl.make_decode_warmup(Wd)
+    d = lambda x: torch.from_numpy(x.astype(np.float32)).cuda().to(torch.bfloat16).contiguous()
+    st = gka.GkaState.zeros(Wd.B, Wd.H, Wd.D)
+    gka.fwd_chunked(d(q), d(k), d(v), torch.from_numpy(g.astype(np.float32)).cuda(), Wd.a,
+                    Wd.iters, Wd.chunk, state=st)
+    torch.cuda.synchronize()
+    del q, k, v, g
+    log(f"decode inputs for {steps} steps")
+    qs, ks, vs, gs = [], [], [], []
+    for s in range(steps):
+        q1, k1, v1, g1 = Wl.make_decode_step(Wd, s)
+        qs.append(q1.astype(np.float32))
+        ks.append(k1.astype(np.float32))
+        vs.append(v1.astype(np.float32))
+        gs.append(g1.astype(np.float32))
+    Q = torch.from_numpy(np.stack(qs)).cuda().to(torch.bfloat16)
+    K = torch.from_numpy(np.stack(ks)).cuda().to(torch.bfloat16)
+    V = torch.from_numpy(np.stack(vs)).cuda().to(torch.bfloat16)
+    G = torch.from_numpy(np.stack(gs)).cuda()
+    O = torch.empty_like(Q)
+    stream = torch.cuda.current_stream().cuda_stream
+    evs = ev.create(2 * steps)
+    t0, t1 = ev.create(2)
+    # warm-up launches on a copy of the state (the timed run starts from the warmed state)
+    st_w = gka.GkaState(st.h.clone(), st.u.clone(), st.n2.clone())
+    for s in range(3):
+        gka.step(Q[s], K[s], V[s], G[s], Wd.a, Wd.iters, st_w, out=O[s])
+    del st_w
+    torch.cuda.synchronize()
+    log(f"decode timed {steps}")
+    ev.record(t0, stream)
+    for s in range(steps):
+        ev.record(evs[2 * s], stream)
+        gka.step(Q[s], K[s], V[s], G[s], Wd.a, Wd.iters, st, out=O[s])
+        ev.record(evs[2 * s + 1], stream)
+    ev.record(t1, stream)
+    ev.sync(t1)
+    total_ms = ev.elapsed_ms(t0, t1)
+    per = [ev.elapsed_ms(evs[2 * s], evs[2 * s + 1]) for s in range(steps)]
+    ev.destroy(evs + [t0, t1])
+    return dict(total_ms=total_ms, ms_per_step=total_ms / steps, kernel_ms=float(np.mean(per)))
+
+
+def cpu_baseline(W, budget_s=12.0):
+    """The float64 oracle as it stands, on a prefix of the prefill workload (all B x H heads)."""
+    from oracle import gka_forward_ref
+    from test_ridge_regression_amd import workloads as Wl
+
+    q, k, v, g = Wl.make_workload(W, T=8)
+    t = time.perf_counter()
+    gka_forward_ref(q, k, v, g, W.a, W.iters)
+    per_tok = (time.perf_counter() - t) / 8
+    T = int(max(8, min(W.T, budget_s / max(per_tok, 1e-6))))
+    q, k, v, g = Wl.make_workload(W, T=T)
+    t = time.perf_counter()
+    gka_forward_ref(q, k, v, g, W.a, W.iters)
+    el = time.perf_counter() - t
+    return dict(value=W.B * T / el, unit="tokens/s", cores=1, kind="oracle",
+                sample=f"first {T} of {W.T} tokens of the prefill workload, all {W.B}x{W.H} heads; "
+                       f"{el:.1f} s; numpy float64, einsum single-threaded; "
+                       f"host {platform.processor() or platform.machine()}, "
+                       f"{len(os.sched_getaffinity(0))} cores available")
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="also run a plain 512 MiB device copy (calibrates HBM byte counters)")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU; --gpus {args.gpus} is not supported by this build "
+              "(batch x head sharding needs no communication and is described in the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    from test_ridge_regression_amd import gka
+    from test_ridge_regression_amd import workloads as Wl
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    gka.load()
+    ev = HipEvents()
+    if args.copy_probe:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda").fill_(1)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        log("copy probe: 3 x 512 MiB device-to-device copies")
+        del src, dst
+    W = Wl.WORKLOADS["prefill_b8_t2048_h8_d128"]
+    pre = bench_prefill(W, args.steps, args.warmup, ev)
+    tokens = W.B * W.T
+    value = tokens / (pre["ms_per_step"] * 1e-3)
+    F = prefill_flops_per_token_head(W.D, W.chunk, W.iters) * W.B * W.T * W.H
+    achieved = F / (pre["walk_ms"] * 1e-3)
+    log(f"prefill: {pre['ms_per_step']:.3f} ms/step (summary {pre['summary_ms']:.3f}, scan "
+        f"{pre['scan_ms']:.3f}, walk {pre['walk_ms']:.3f}), {value:.3e} tok/s")
+    err = parity_sample(W, pre["o"])
+    log(f"prefill sampled parity rel_l2 {err:.3e}")
+    rec = {
+        "metric": "GKA forward tokens/s (B8 T2048 H8 D128 bf16) + % MFMA peak; decode tok/s",
+        "value": value,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": pre["ms_per_step"],
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": W.name, "B": W.B, "T": W.T, "H": W.H, "D": W.D, "chunk": W.chunk,
+                   "a": W.a, "iters": W.iters, "segments": pre["segments"]},
+        "roofline": {"bound": "mfma", "kernel": "walk_kernel (fused chunk walk)",
+                     "achieved": achieved / 1e12, "peak": PEAK_BF16_MFMA / 1e12,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_MFMA, "traffic": None,
+                     "flops_per_launch": F, "avg_launch_ms": pre["walk_ms"]},
+        "whole_step_mfma_frac": F / (pre["ms_per_step"] * 1e-3) / PEAK_BF16_MFMA,
+        "phases_ms": {"summary": pre["summary_ms"], "scan": pre["scan_ms"],
+                      "walk": pre["walk_ms"]},
+        "parity_sampled_rel_l2": err,
+    }
+    del pre
+    torch.cuda.empty_cache()
+    if not args.no_decode:
+        Wd = Wl.WORKLOADS["decode_b256_h8_d128"]
+        dec = bench_decode(Wd, args.decode_steps, ev)
+        heads = Wd.B * Wd.H
+        bytes_launch = decode_bytes_per_head(Wd.D) * heads
+        rec["decode"] = {
+            "workload": Wd.name, "tokens_per_s": Wd.B / (dec["ms_per_step"] * 1e-3),
+            "ms_per_step": dec["ms_per_step"], "steps": args.decode_steps,
+            "roofline": {"bound": "hbm", "kernel": "step_kernel",
+                         "achieved": bytes_launch / (dec["kernel_ms"] * 1e-3) / 1e9,
+                         "peak": PEAK_HBM / 1e9, "unit": "GB/s",
+                         "frac": bytes_launch / (dec["kernel_ms"] * 1e-3) / PEAK_HBM,
+                         "traffic": None, "bytes_per_launch": bytes_launch,
+                         "avg_launch_ms": dec["kernel_ms"]},
+        }
+        log(f"decode: {dec['ms_per_step'] * 1e3:.1f} us/step, kernel {dec['kernel_ms'] * 1e3:.1f} us")
+    if not args.no_cpu:
+        log("cpu baseline (oracle)")
+        rec["cpu_baseline"] = cpu_baseline(W)
+    print(json.dumps(rec), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -55,6 +55,7 @@ typedef enum {
 typedef enum { GKA_BF16 = 0, GKA_FP32 = 1 } gka_dtype;
 
 #define GKA_MAX_ITERS 64
+#define GKA_PHASE_EVENTS 4
 
 /*
  * Problem description shared by both entry points.
@@ -94,11 +95,16 @@ size_t gka_fwd_workspace_bytes(const gka_params* p);
  *             read as the initial state and overwritten with the final state (in place)
  *   hnorm_t   optional [B, T, H] float32: ||H_t||_F of every token, written
  *   workspace device scratch of at least gka_fwd_workspace_bytes(p) bytes (NULL if that is 0)
+ *   phase_events
+ *             optional (NULL = none): 4 caller-created hipEvent_t recorded on `stream` at the
+ *             phase boundaries -- [0] before the segment summaries, [1] before the segment
+ *             scan, [2] before the fused chunk walk, [3] after it. With one segment the first
+ *             three are recorded back to back. For per-phase timing only; nothing else changes.
  */
 gka_status gka_fwd_chunked(const gka_params* p, const void* q, const void* k, const void* v,
                            const float* gamma, void* o, float* h_state, float* u_state,
                            float* hnorm2, float* hnorm_t, void* workspace,
-                           size_t workspace_bytes, void* stream);
+                           size_t workspace_bytes, void* stream, void* const* phase_events);
 
 /*
  * One recurrent decode step for B x H independent heads (the inference path, ai.info summary

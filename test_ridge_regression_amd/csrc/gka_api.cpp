@@ -152,7 +152,7 @@ size_t gka_fwd_workspace_bytes(const gka_params* p) {
 gka_status gka_fwd_chunked(const gka_params* p, const void* q, const void* k, const void* v,
                            const float* gamma, void* o, float* h_state, float* u_state,
                            float* hnorm2, float* hnorm_t, void* workspace,
-                           size_t workspace_bytes, void* stream) {
+                           size_t workspace_bytes, void* stream, void* const* phase_events) {
   gka_status st = check_fwd(p);
   if (st != GKA_OK) return st;
   const bool any_state = h_state || u_state || hnorm2;
@@ -172,6 +172,11 @@ gka_status gka_fwd_chunked(const gka_params* p, const void* q, const void* k, co
 
   const ChebConsts cc = cheb_consts(p->a, p->iters);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  auto mark = [&](int i) {
+    if (phase_events && phase_events[i])
+      return hipEventRecord(static_cast<hipEvent_t>(phase_events[i]), s) == hipSuccess;
+    return true;
+  };
   const long long DD = (long long)p->D * p->D;
   gka::WalkArgs wa{};
   wa.q = q;
@@ -189,7 +194,9 @@ gka_status gka_fwd_chunked(const gka_params* p, const void* q, const void* k, co
     wa.out_h = h_state;
     wa.out_u = u_state;
     wa.n2_out = hnorm2;
+    if (!mark(0) || !mark(1) || !mark(2)) return GKA_ERR_HIP;
     if (gka::launch_walk(pl, false, wa, cc, s) != hipSuccess) return GKA_ERR_HIP;
+    if (!mark(3)) return GKA_ERR_HIP;
     return GKA_OK;
   }
   const size_t bh = (size_t)p->B * p->H;
@@ -202,9 +209,12 @@ gka_status gka_fwd_chunked(const gka_params* p, const void* q, const void* k, co
   sa.sum_bh = (long long)pl.S * 2 * DD;
   sa.sum_seg = 2 * DD;
   sa.log2g_out = ws_log2g;
+  if (!mark(0)) return GKA_ERR_HIP;
   if (gka::launch_walk(pl, true, sa, cc, s) != hipSuccess) return GKA_ERR_HIP;
+  if (!mark(1)) return GKA_ERR_HIP;
   if (gka::launch_scan(pl, ws_states, ws_log2g, h_state, u_state, hnorm2, ws_n2, s) != hipSuccess)
     return GKA_ERR_HIP;
+  if (!mark(2)) return GKA_ERR_HIP;
   wa.in_h = ws_states;
   wa.in_u = ws_states + DD;
   wa.in_bh = (long long)pl.S * 2 * DD;
@@ -212,6 +222,7 @@ gka_status gka_fwd_chunked(const gka_params* p, const void* q, const void* k, co
   wa.n2_in = ws_n2;
   wa.n2_out = hnorm2;
   if (gka::launch_walk(pl, false, wa, cc, s) != hipSuccess) return GKA_ERR_HIP;
+  if (!mark(3)) return GKA_ERR_HIP;
   return GKA_OK;
 }
 

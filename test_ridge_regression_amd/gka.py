@@ -58,7 +58,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     vp, fp = ctypes.c_void_p, ctypes.c_void_p
     lib.gka_fwd_workspace_bytes.argtypes = [P]
     lib.gka_fwd_workspace_bytes.restype = ctypes.c_size_t
-    lib.gka_fwd_chunked.argtypes = [P, vp, vp, vp, fp, vp, fp, fp, fp, fp, vp, ctypes.c_size_t, vp]
+    lib.gka_fwd_chunked.argtypes = [P, vp, vp, vp, fp, vp, fp, fp, fp, fp, vp, ctypes.c_size_t, vp,
+                                    ctypes.c_void_p]
     lib.gka_fwd_chunked.restype = ctypes.c_int
     lib.gka_step.argtypes = [P, vp, vp, vp, fp, vp, fp, fp, fp, vp]
     lib.gka_step.restype = ctypes.c_int
@@ -135,10 +136,12 @@ def workspace_bytes(B, T, H, D, chunk, iters, a, dtype_code, segments=0) -> int:
 def fwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor, a: float,
                 iters: int, chunk: int = 64, state: Optional[GkaState] = None,
                 return_hnorm: bool = False, segments: int = 0, out: Optional[torch.Tensor] = None,
-                workspace: Optional[torch.Tensor] = None, stream=None):
+                workspace: Optional[torch.Tensor] = None, stream=None, phase_events=None):
     """gka_fwd_chunked on [B, T, H, D] tensors; returns o (and per-token ||H_t||_F [B,T,H]).
 
     ``state`` (optional) is read as the initial state and overwritten with the final one.
+    ``phase_events`` (optional) is a ctypes array of 4 hipEvent_t handles recorded at the
+    phase boundaries (see include/gka.h).
     """
     lib = load()
     B, T, H, D = q.shape
@@ -153,7 +156,7 @@ def fwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.
                              _ptr(state.h if state else None), _ptr(state.u if state else None),
                              _ptr(state.n2 if state else None), _ptr(hn), _ptr(workspace),
                              ctypes.c_size_t(workspace.numel() if workspace is not None else 0),
-                             _stream(stream))
+                             _stream(stream), phase_events)
     _check(st)
     return (o, hn) if return_hnorm else o
 

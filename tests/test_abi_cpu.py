@@ -59,7 +59,7 @@ def params(**kw):
 def fwd(lib, p, q=VP[0], k=VP[1], v=VP[2], g=VP[3], o=VP[4], h=None, u=None, n2=None, hn=None,
         ws=None, wsb=0):
     return lib.gka_fwd_chunked(ctypes.byref(p) if p is not None else None, q, k, v, g, o, h, u,
-                               n2, hn, ws, ctypes.c_size_t(wsb), None)
+                               n2, hn, ws, ctypes.c_size_t(wsb), None, None)
 
 
 def step(lib, p, q=VP[0], k=VP[1], v=VP[2], g=VP[3], o=VP[4], h=VP[5], u=VP[6], n2=VP[7]):
