@@ -1,6 +1,7 @@
 // Device-side building blocks shared by the GKA kernels (gfx950 / CDNA4 only).
 //
 // Matrix-core tiles are 16x16 outputs with float32 accumulation:
+//   fp16 operands: v_mfma_f32_16x16x32_f16  (K step 32, 8 elements per lane)
 //   bf16 operands: v_mfma_f32_16x16x32_bf16 (K step 32, 8 elements per lane)
 //   fp32 operands: v_mfma_f32_16x16x4_f32   (K step 4, 1 element per lane)
 // Lane l of a wave holds, for an A operand (16 x K, row-major in LDS), row l%16 and the
@@ -35,6 +36,23 @@ struct Mma<bf16> {
   // operand fragment: E consecutive elements of row `row` starting at column `col`
   __device__ static inline frag load(const bf16* base, int ld, int row, int col) {
     return *reinterpret_cast<const bf16x8*>(base + row * ld + col);
+  }
+};
+
+typedef _Float16 f16;
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+
+template <>
+struct Mma<f16> {
+  static constexpr int K = 32;
+  static constexpr int E = 8;
+  typedef f16x8 frag;
+  __device__ static inline f32x4 mma(frag a, frag b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_f16(a, b, c, 0, 0, 0);
+  }
+  __device__ static inline frag load(const f16* base, int ld, int row, int col) {
+    return *reinterpret_cast<const f16x8*>(base + row * ld + col);
   }
 };
 
@@ -74,20 +92,27 @@ template <>
 __device__ inline void store4<float>(float* p, f32x4 v) {
   *reinterpret_cast<f32x4*>(p) = v;
 }
+template <>
+__device__ inline void store4<f16>(f16* p, f32x4 v) {
+  f16x4 h;
+  h[0] = (f16)v[0]; h[1] = (f16)v[1]; h[2] = (f16)v[2]; h[3] = (f16)v[3];
+  *reinterpret_cast<f16x4*>(p) = h;
+}
+
 // four consecutive elements as hi + lo parts: hi = round(v), lo = round(v - hi); for float the
 // value is exact and only hi is written
 template <typename T>
 __device__ inline void store4_split(T* hi, T* lo, f32x4 v);
 template <>
-__device__ inline void store4_split<bf16>(bf16* hi, bf16* lo, f32x4 v) {
-  bf16x4 h, l;
+__device__ inline void store4_split<f16>(f16* hi, f16* lo, f32x4 v) {
+  f16x4 h, l;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    h[i] = (bf16)v[i];
-    l[i] = (bf16)(v[i] - (float)h[i]);
+    h[i] = (f16)v[i];
+    l[i] = (f16)(v[i] - (float)h[i]);
   }
-  *reinterpret_cast<bf16x4*>(hi) = h;
-  *reinterpret_cast<bf16x4*>(lo) = l;
+  *reinterpret_cast<f16x4*>(hi) = h;
+  *reinterpret_cast<f16x4*>(lo) = l;
 }
 template <>
 __device__ inline void store4_split<float>(float* hi, float*, f32x4 v) {
@@ -104,6 +129,33 @@ __device__ inline f32x4 load4<bf16>(const bf16* p) {
 template <>
 __device__ inline f32x4 load4<float>(const float* p) {
   return *reinterpret_cast<const f32x4*>(p);
+}
+template <>
+__device__ inline f32x4 load4<f16>(const f16* p) {
+  f16x4 h = *reinterpret_cast<const f16x4*>(p);
+  return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
+}
+
+// matrix-core operand type for an input element type: bf16 inputs are converted to fp16
+// (exact for every bf16 value in fp16's normal range; 3 more mantissa bits for the rounded
+// operands), fp32 inputs stay fp32
+template <typename T>
+struct OperandOf;
+template <>
+struct OperandOf<bf16> {
+  typedef f16 type;
+};
+template <>
+struct OperandOf<float> {
+  typedef float type;
+};
+template <typename O>
+__device__ inline O to_op(bf16 x) {
+  return (O)(float)x;
+}
+template <typename O>
+__device__ inline O to_op(float x) {
+  return (O)x;
 }
 
 // ---- wave reductions (wave64) -------------------------------------------------------------
