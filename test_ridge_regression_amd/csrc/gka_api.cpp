@@ -4,7 +4,7 @@
 #include <cmath>
 #include <cstdint>
 
-#include "../../include/gka.h"
+#include "gka.h"
 #include "gka_internal.hpp"
 
 namespace {

@@ -168,7 +168,12 @@ __device__ inline float wave_sum(float x) {
 // log2 of a gate with a finite floor for gamma = 0, so that differences of prefix sums stay
 // finite; 2^x for x at or below the floor underflows to exactly 0 in float32.
 constexpr float kLog2GateFloor = -160.0f;
-__device__ inline float log2_gate(float g) { return g > 0.0f ? log2f(g) : kLog2GateFloor; }
+// hardware 2^x and log2(x) (v_exp_f32 / v_log_f32, about 1 ulp); arguments of exp2 here are
+// <= 0 and results below the normal range only ever act as vanishing decay weights
+__device__ inline float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+__device__ inline float log2_gate(float g) {
+  return g >= 1.17549435e-38f ? __builtin_amdgcn_logf(g) : kLog2GateFloor;
+}
 
 // Chebyshev constants of the normalised system  (H_t / ||H_t||_F + a I) xh = q, whose spectrum
 // lies in [a, 1 + a]: step c = 2 / (1 + 2a), weights omega_i (omega_0 = 2), and the weights

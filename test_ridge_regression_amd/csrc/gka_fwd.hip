@@ -75,18 +75,63 @@ struct WalkCfg {
   static constexpr size_t szDC = (size_t)D * LDC * sizeof(O);  // [D][LDC]
   static constexpr size_t szDD = (size_t)D * LDD * sizeof(O);  // [D][LDD]
   static constexpr size_t szVec = (size_t)(8 * C + 2 * NW * C + 32) * sizeof(float);
-  static constexpr size_t oRs = 0;                         // operand (R or X hi), token-major
-  static constexpr size_t oRl = oRs + szRD;                // X lo (output only)
-  static constexpr size_t oPs = oRl + (SPLIT ? szRD : 0);  // masked product (hi), token-major
-  static constexpr size_t oPl = oPs + szRC;                // masked product lo (output only)
-  static constexpr size_t oKs = oPl + (SPLIT ? szRC : 0);  // K, token-major
-  static constexpr size_t oKT = oKs + szRD;                // K^T
-  static constexpr size_t oVT = oKT + szDC;                // V^T
+  static constexpr size_t oRs = 0;            // operand (R or X hi), token-major
+  static constexpr size_t oPs = oRs + szRD;   // masked product (hi), token-major
+  static constexpr size_t oKs = oPs + szRC;   // K, token-major
+  static constexpr size_t oKT = oKs + szRD;   // K^T
+  static constexpr size_t oVT = oKT + szDC;   // V^T
+  // the lo parts of the output operands reuse the K, K^T and V^T buffers: by the time they are
+  // written K lives in registers (resident fragments), the carry (last reader of K^T) has run and
+  // the V^T fragments of the output are loaded
+  static constexpr size_t oRl = oKs;
+  static constexpr size_t oPl = oKT;
+  static_assert(!SPLIT || szRC <= 2 * szDC, "lo masked product must fit the K^T, V^T buffers");
   static constexpr size_t oSt = oVT + szDC;                // H0hat, then U0hat (row-major)
   static constexpr size_t oVec = oSt + szDD;
-  static constexpr size_t bytes = oVec + szVec;
+  // next chunk's raw K, V (16-byte units, [unit column][token]) and gates, filled by
+  // direct global-to-LDS loads while the current chunk computes
+  static constexpr int VEC = 16 / (int)sizeof(T);         // elements per 16-byte unit
+  static constexpr int UPR = D / VEC;                     // units per token row
+  static constexpr int NU = C * UPR;                      // units per matrix
+  static constexpr size_t szPreM = (size_t)NU * 16;
+  static constexpr size_t oPre = oVec + szVec;
+  static constexpr size_t bytes = oPre + 2 * szPreM + (size_t)C * sizeof(float);
+  static_assert(NU % kWave == 0, "prefetch units must fill whole waves");
   static_assert(bytes <= 160 * 1024, "LDS budget of one CU exceeded");
 };
+
+// Direct global-to-LDS loads of chunk chn's K, V and gates into the prefetch buffer (lane l of a
+// wave instruction lands at base + 16 l). Unit u = (column c, token t) with u = c*C + t holds
+// K[t][c*VEC .. c*VEC+VEC-1]; tokens past the end of the sequence are not loaded. (A plain device
+// function, whose body exists in the device compilation pass only.)
+template <typename T, int D, int C, typename V>
+__device__ inline void prefetch_chunk(V* PreK, V* PreV, float* PreG, const T* kg, const T* vg,
+                                      const float* gamma, int b, int h, int Hn, int Tlen, int chn,
+                                      int wave, int lane) {
+#if defined(__HIP_DEVICE_COMPILE__)  // device code only: the host pass has no LDS address space
+  using Cfg = WalkCfg<T, D, C>;
+  typedef __attribute__((address_space(3))) void lds_void;
+  constexpr int NI = Cfg::NU / kWave;  // wave instructions per matrix
+  const long long tok_stride = (long long)Hn * D;
+  const int t0n = chn * C;
+  const int nvn = min(C, Tlen - t0n);
+  for (int q = wave; q < 2 * NI; q += Cfg::NW) {
+    const bool isv = q >= NI;
+    const int qq = isv ? q - NI : q;
+    const int u = qq * kWave + lane;
+    const int t = u % C, c = u / C;
+    if (t < nvn) {
+      const T* src = (isv ? vg : kg) + (b * (long long)Tlen + t0n + t) * tok_stride +
+                     (long long)h * D + c * Cfg::VEC;
+      V* dst = (isv ? PreV : PreK) + qq * kWave;
+      __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst), 16, 0, 0);
+    }
+  }
+  if (wave == Cfg::NW - 1 && lane < nvn)
+    __builtin_amdgcn_global_load_lds(gamma + (b * (long long)Tlen + t0n + lane) * Hn + h,
+                                     (lds_void*)(PreG), 4, 0, 0);
+#endif
+}
 
 template <typename T, int D, int C, bool SUMMARY>
 __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, int Hn, int N,
@@ -122,6 +167,10 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
   float* p_u = v_kk + C;        // [NW][C] partials of k_t^T H0hat k_t
   float* p_v = p_u + NW * C;    // [NW][C] partials of sum_{s<t} M_{t-1,s} G_st^2
   float* v_sc = p_v + NW * C;   // [32] scalars
+  typedef T vecT __attribute__((ext_vector_type(Cfg::VEC)));
+  vecT* PreK = reinterpret_cast<vecT*>(smem + Cfg::oPre);    // [UPR][C] units of K
+  vecT* PreV = PreK + Cfg::NU;                                // [UPR][C] units of V
+  float* PreG = reinterpret_cast<float*>(PreV + Cfg::NU);     // [C] gates
 
   const int seg = blockIdx.x;
   const int bh = blockIdx.y;
@@ -182,25 +231,30 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
   }
   float log2g_seg = 0.0f;  // summary mode: running log2 of the segment's gate product
 
+  if (c_begin < c_end)
+    prefetch_chunk<T, D, C, vecT>(PreK, PreV, PreG, kg, vg, A.gamma, b, h, Hn, Tlen, c_begin, wave,
+                                  lane);
+
   for (int ch = c_begin; ch < c_end; ++ch) {
     const int t0 = ch * C;
     const int nv = min(C, Tlen - t0);  // valid tokens of this chunk
     const float n0 = sqrtf(n0sq);
     const float n0inv = n0 > 0.0f ? 1.0f / n0 : 0.0f;
-    __syncthreads();  // LDS of the previous chunk is free
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads into the prefetch buffer have landed
+    __syncthreads();                // all of them; LDS of the previous chunk is free
 
-    // ---- stage K (token-major), K^T, V^T as operands; tokens past the end are zero ---------
+    // ---- stage K (token-major), K^T, V^T as operands from the prefetch buffer -----------------
+    // The token index runs fastest across lanes: unit reads are consecutive and the transposed
+    // 2-byte writes of a wave cover consecutive addresses of one row of K^T / V^T.
     {
-      constexpr int VEC = 16 / (int)sizeof(T);
-      constexpr int NV = C * D / VEC;
-      typedef T vecT __attribute__((ext_vector_type(VEC)));
-      for (int e = tid; e < NV; e += Cfg::NT) {
-        const int t = e / (D / VEC), d0 = (e % (D / VEC)) * VEC;
+      constexpr int VEC = Cfg::VEC;
+      typedef O vecO __attribute__((ext_vector_type(VEC)));
+      for (int e = tid; e < Cfg::NU; e += Cfg::NT) {
+        const int t = e % C, d0 = (e / C) * VEC;
         vecT kv, vv;
         if (t < nv) {
-          const long long off = (b * (long long)Tlen + t0 + t) * tok_stride + (long long)h * D + d0;
-          kv = *reinterpret_cast<const vecT*>(kg + off);
-          vv = *reinterpret_cast<const vecT*>(vg + off);
+          kv = PreK[e];
+          vv = PreV[e];
         } else {
 #pragma unroll
           for (int i = 0; i < VEC; ++i) {
@@ -208,20 +262,38 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
             vv[i] = (T)0.0f;
           }
         }
+        vecO ko;
 #pragma unroll
         for (int i = 0; i < VEC; ++i) {
-          const O ko = to_op<O>(kv[i]);
-          if (!SUMMARY) Ks[t * LDD + d0 + i] = ko;
-          KT[(d0 + i) * LDC + t] = ko;
+          ko[i] = to_op<O>(kv[i]);
+          KT[(d0 + i) * LDC + t] = ko[i];
           VT[(d0 + i) * LDC + t] = to_op<O>(vv[i]);
         }
+        if (!SUMMARY) *reinterpret_cast<vecO*>(Ks + t * LDD + d0) = ko;
       }
+    }
+    // ---- queries of the own tiles (issued early; zeroed below where ||H_t|| = 0) ---------------
+    typedef T raw4 __attribute__((ext_vector_type(4)));
+    raw4 Qraw[FPW][TPW];
+    if (!SUMMARY) {
+#pragma unroll
+      for (int jt = 0; jt < TPW; ++jt)
+#pragma unroll
+        for (int jf = 0; jf < FPW; ++jf) {
+          const int t = tok_of(jt) + lr;
+          raw4 qv = {(T)0.0f, (T)0.0f, (T)0.0f, (T)0.0f};
+          if (tok_active && t < nv) {
+            const long long off = (b * (long long)Tlen + t0 + t) * tok_stride + (long long)h * D + row_of(jf) + 4 * lg;
+            qv = *reinterpret_cast<const raw4*>(qg + off);
+          }
+          Qraw[jf][jt] = qv;
+        }
     }
     // ---- gate prologue (wave 0) -----------------------------------------------------------------
     if (wave == 0) {
       float g = 1.0f, l2 = 0.0f;  // tokens past the end: gamma = 1 with k = v = q = 0
       if (lane < nv) {
-        g = A.gamma[(b * (long long)Tlen + t0 + lane) * Hn + h];
+        g = PreG[lane];
         l2 = log2_gate(g);
       }
       float cl = l2;
@@ -233,8 +305,8 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
       const float clast = __shfl(cl, C - 1, kWave);
       if (lane < C) {
         v_cl[lane] = cl;
-        v_gam[lane] = exp2f(cl);
-        v_w[lane] = exp2f(fminf(clast - cl, 0.0f));
+        v_gam[lane] = fast_exp2(cl);
+        v_w[lane] = fast_exp2(fminf(clast - cl, 0.0f));
         v_g[lane] = g;
       }
       log2g_seg += clast;
@@ -248,6 +320,15 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
           store4<O>(St + (col_of(jc) + lr) * LDD + row_of(jf) + 4 * lg, Hst[jf][jc] * n0inv);
     }
     __syncthreads();
+    // the prefetch buffer has been consumed. The next chunk's loads are issued once this chunk's
+    // queries are in registers: the memory counter retires in order, so any wait for a load issued
+    // after them (the queries, spill reloads) would also wait for the whole prefetch.
+    auto prefetch_next = [&]() {
+      if (ch + 1 < c_end)
+        prefetch_chunk<T, D, C, vecT>(PreK, PreV, PreG, kg, vg, A.gamma, b, h, Hn, Tlen, ch + 1,
+                                      wave, lane);
+    };
+    if (SUMMARY) prefetch_next();
 
     // ---- operand fragments of the wave's rows, resident for the chunk --------------------------
     Frag fKT[FPW][KC];  // A operand K^T[f][s] (rows = own features)
@@ -300,12 +381,7 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
     };
 
     if (!SUMMARY) {
-      Frag fH[FPW][KD];  // A operand H0hat[f][k], later U0hat[v][k]
       Frag fK[SBW][KD];  // A operand K[s][d] (rows = own s-blocks)
-#pragma unroll
-      for (int jf = 0; jf < FPW; ++jf)
-#pragma unroll
-        for (int kk = 0; kk < KD; ++kk) fH[jf][kk] = M::load(St, LDD, row_of(jf) + lr, kk * K + E * lg);
 #pragma unroll
       for (int js = 0; js < SBW; ++js)
 #pragma unroll
@@ -341,7 +417,7 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
                 const int s = 16 * sb + 4 * lg + i;
-                if (s < t) pv[jt] += exp2f(fminf(clp - v_cl[s], 0.0f)) * (acc[i] * acc[i]);
+                if (s < t) pv[jt] += fast_exp2(fminf(clp - v_cl[s], 0.0f)) * (acc[i] * acc[i]);
                 if (s == t) v_kk[t] = acc[i];
               }
             }
@@ -350,7 +426,8 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
           for (int jf = 0; jf < FPW; ++jf) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < KD; ++kk) acc = M::mma(fH[jf][kk], fb[kk], acc);
+            for (int kk = 0; kk < KD; ++kk)
+              acc = M::mma(M::load(St, LDD, row_of(jf) + lr, kk * K + E * lg), fb[kk], acc);
             const f32x4 kf = load4<O>(Ks + t * LDD + row_of(jf) + 4 * lg);
             pu[jt] += acc[0] * kf[0] + acc[1] * kf[1] + acc[2] * kf[2] + acc[3] * kf[3];
           }
@@ -369,14 +446,6 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
         }
       }
       __syncthreads();
-      // U0hat = U0 / n0 into the staging buffer for the output (H0hat fragments are loaded)
-      if (state_active) {
-#pragma unroll
-        for (int jf = 0; jf < FPW; ++jf)
-#pragma unroll
-          for (int jc = 0; jc < CBW; ++jc)
-            store4<O>(St + (col_of(jc) + lr) * LDD + row_of(jf) + 4 * lg, Ust[jf][jc] * n0inv);
-      }
       // (c) n_t^2 by an affine scan over the chunk (wave 0, lane = token)
       if (wave == 0) {
         const int t = lane;
@@ -430,7 +499,7 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int s = 16 * sb + 4 * lg + i;
-              m4[i] = s <= t ? exp2f(fminf(clt - v_cl[s], 0.0f)) * ninv : 0.0f;
+              m4[i] = s <= t ? fast_exp2(fminf(clt - v_cl[s], 0.0f)) * ninv : 0.0f;
             }
           }
           Mh[js][jt] = m4;
@@ -438,9 +507,9 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
 #pragma unroll
         for (int jf = 0; jf < FPW; ++jf) {
           f32x4 qv = {0.f, 0.f, 0.f, 0.f};
-          if (tok_active && t < nv && v_ninv[t] > 0.0f) {  // ||H_t|| = 0: x_t = 0
-            const long long off = (b * (long long)Tlen + t0 + t) * tok_stride + (long long)h * D + row_of(jf) + 4 * lg;
-            qv = load4<T>(qg + off);
+          if (tok_active && v_ninv[t] > 0.0f) {  // ||H_t|| = 0: x_t = 0
+#pragma unroll
+            for (int i = 0; i < 4; ++i) qv[i] = to_f32(Qraw[jf][jt][i]);
           }
           R[jf][jt] = qv;
           Rp[jf][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -461,43 +530,55 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
             }
         }
       };
-      // Y = Mat V^T (own tiles; Mat fragments fA) and P'^T = (K V^T) o Mhat^T -> Ps (and Pl)
-      auto products_1 = [&](Frag(&fA)[FPW][KD], bool split) {
+      // Y = Mat V^T (own tiles; Mat read from LDS, row-major) and P'^T = (K V^T) o Mhat^T -> Ps
+      // (and Pl); the k-step loop is outermost so independent accumulators interleave
+      auto products_1 = [&](const O* Mat, bool split) {
         if (tok_active) {
+          f32x4 Pa[SBW][TPW];
 #pragma unroll
           for (int jt = 0; jt < TPW; ++jt) {
-            Frag fb[KD], fl[KD];
 #pragma unroll
-            for (int kk = 0; kk < KD; ++kk) {
-              fb[kk] = M::load(Rs, LDD, tok_of(jt) + lr, kk * K + E * lg);
-              if (SPLIT && split) fl[kk] = M::load(Rl, LDD, tok_of(jt) + lr, kk * K + E * lg);
+            for (int jf = 0; jf < FPW; ++jf) Y[jf][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int js = 0; js < SBW; ++js) Pa[js][jt] = f32x4{0.f, 0.f, 0.f, 0.f};
+          }
+#pragma unroll
+          for (int kk = 0; kk < KD; ++kk) {
+            Frag fb[TPW], fl[TPW], fa[FPW];
+#pragma unroll
+            for (int jt = 0; jt < TPW; ++jt) {
+              fb[jt] = M::load(Rs, LDD, tok_of(jt) + lr, kk * K + E * lg);
+              if (SPLIT && split) fl[jt] = M::load(Rl, LDD, tok_of(jt) + lr, kk * K + E * lg);
             }
 #pragma unroll
-            for (int jf = 0; jf < FPW; ++jf) {
-              f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int jf = 0; jf < FPW; ++jf) fa[jf] = M::load(Mat, LDD, row_of(jf) + lr, kk * K + E * lg);
 #pragma unroll
-              for (int kk = 0; kk < KD; ++kk) {
-                acc = M::mma(fA[jf][kk], fb[kk], acc);
-                if (SPLIT && split) acc = M::mma(fA[jf][kk], fl[kk], acc);
+            for (int jt = 0; jt < TPW; ++jt) {
+#pragma unroll
+              for (int jf = 0; jf < FPW; ++jf) {
+                Y[jf][jt] = M::mma(fa[jf], fb[jt], Y[jf][jt]);
+                if (SPLIT && split) Y[jf][jt] = M::mma(fa[jf], fl[jt], Y[jf][jt]);
               }
-              Y[jf][jt] = acc;
+#pragma unroll
+              for (int js = 0; js < SBW; ++js) {
+                if (sblk_of(js) < CT) {
+                  Pa[js][jt] = M::mma(fK[js][kk], fb[jt], Pa[js][jt]);
+                  if (SPLIT && split) Pa[js][jt] = M::mma(fK[js][kk], fl[jt], Pa[js][jt]);
+                }
+              }
             }
+          }
+#pragma unroll
+          for (int jt = 0; jt < TPW; ++jt)
 #pragma unroll
             for (int js = 0; js < SBW; ++js) {
               const int sb = sblk_of(js);
               if (sb < CT) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < KD; ++kk) {
-                  acc = M::mma(fK[js][kk], fb[kk], acc);
-                  if (SPLIT && split) acc = M::mma(fK[js][kk], fl[kk], acc);
-                }
                 const int o = (tok_of(jt) + lr) * LDC + 16 * sb + 4 * lg;
-                if (SPLIT && split) store4_split<O>(Ps + o, Pl + o, acc * Mh[js][jt]);
-                else store4<O>(Ps + o, acc * Mh[js][jt]);
+                if (SPLIT && split) store4_split<O>(Ps + o, Pl + o, Pa[js][jt] * Mh[js][jt]);
+                else store4<O>(Ps + o, Pa[js][jt] * Mh[js][jt]);
               }
             }
-          }
         }
       };
       // Y = diag(s) Y + Mat2 P'^T (Mat2 fragments fB: K^T in the loop, V^T for the output)
@@ -525,10 +606,11 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
         }
       };
 
+      prefetch_next();
       for (int it = 0; it + 1 < cc.iters; ++it) {
         write_operand(R, false);
         __syncthreads();
-        products_1(fH, false);
+        products_1(St, false);
         __syncthreads();
         products_2(fKT, false);
         const float om = cc.omega[it], bn = cc.beta[it + 1];
@@ -545,14 +627,19 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
           }
       }
 
+      // U0hat = U0 / n0 into the staging buffer (every wave is past its last read of H0hat:
+      // the loop ends with a barrier after the products that read it)
+      if (state_active) {
+#pragma unroll
+        for (int jf = 0; jf < FPW; ++jf)
+#pragma unroll
+          for (int jc = 0; jc < CBW; ++jc)
+            store4<O>(St + (col_of(jc) + lr) * LDD + row_of(jf) + 4 * lg, Ust[jf][jc] * n0inv);
+      }
       carry();
 
       // ---- output O^T = diag(s) U0hat X^T + V^T P'^T (X split into hi + lo) --------------------
-      // fragments of U0hat (staged before the loop) and V^T replace those of H0hat and K^T
-#pragma unroll
-      for (int jf = 0; jf < FPW; ++jf)
-#pragma unroll
-        for (int kk = 0; kk < KD; ++kk) fH[jf][kk] = M::load(St, LDD, row_of(jf) + lr, kk * K + E * lg);
+      // V^T fragments replace those of K^T; U0hat was staged into the H0hat buffer after the loop
       Frag fVT[FPW][KC];
 #pragma unroll
       for (int jf = 0; jf < FPW; ++jf)
@@ -560,7 +647,7 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
         for (int kk = 0; kk < KC; ++kk) fVT[jf][kk] = M::load(VT, LDC, row_of(jf) + lr, kk * K + E * lg);
       write_operand(Xa, true);
       __syncthreads();
-      products_1(fH, true);
+      products_1(St, true);
       __syncthreads();
       products_2(fVT, true);
       if (tok_active) {
