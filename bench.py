@@ -14,6 +14,7 @@ from __future__ import annotations
 
 import argparse
 import ctypes
+import hashlib
 import json
 import os
 import platform
@@ -82,6 +83,24 @@ def decode_bytes_per_head(D, in_bytes=2):
     return 16 * D * D + 4 * D * in_bytes + 4 + 8
 
 
+def measured_traffic(kernel):
+    """HBM bytes per launch that rocprofv3 counted for ``kernel`` (profiles/hbm_traffic.json,
+    FETCH_SIZE x 2.0 + WRITE_SIZE x 1.0), or None once the kernel's source differs from the one
+    the counters were taken on."""
+    path = os.path.join(ROOT, "profiles", "hbm_traffic.json")
+    try:
+        rec = json.load(open(path))[kernel]
+    except (OSError, KeyError, ValueError):
+        return None
+    files = {"walk_kernel": ("gka_fwd.hip", "gka_common.hpp"),
+             "step_kernel": ("gka_step.hip", "gka_common.hpp")}[kernel]
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "test_ridge_regression_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return rec["bytes"] if h.hexdigest() == rec.get("source_sha256") else None
+
+
 def bench_prefill(W, steps, warmup, ev):
     import torch
     from test_ridge_regression_amd import gka
@@ -138,13 +157,13 @@ def parity_sample(W, o_dev, heads=((0, 0), (7, 7))):
     from oracle import gka_forward_ref
     from test_ridge_regression_amd import workloads as Wl
 
-    q, k, v, g = Wl.make_workload(W)
-    o = o_dev.float().cpu().numpy()
+    q, k, v, g = Wl.make_workload(W, heads=heads)
+    ref = gka_forward_ref(q, k, v, g, W.a, W.iters)["o"]
     errs = []
-    for b, h in heads:
-        sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
-        ref = gka_forward_ref(q[sl], k[sl], v[sl], g[sl], W.a, W.iters)["o"]
-        errs.append(float(np.linalg.norm(o[sl] - ref) / np.linalg.norm(ref)))
+    for i, (b, h) in enumerate(heads):
+        got = o_dev[b, :, h].float().cpu().numpy()
+        want = ref[0, :, i]
+        errs.append(float(np.linalg.norm(got - want) / np.linalg.norm(want)))
     return max(errs)
 
 
@@ -162,17 +181,12 @@ def bench_decode(Wd, steps, ev):
     torch.cuda.synchronize()
     del q, k, v, g
     log(f"decode inputs for {steps} steps")
-    qs, ks, vs, gs = [], [], [], []
-    for s in range(steps):
-        q1, k1, v1, g1 = Wl.make_decode_step(Wd, s)
-        qs.append(q1.astype(np.float32))
-        ks.append(k1.astype(np.float32))
-        vs.append(v1.astype(np.float32))
-        gs.append(g1.astype(np.float32))
-    Q = torch.from_numpy(np.stack(qs)).cuda().to(torch.bfloat16)
-    K = torch.from_numpy(np.stack(ks)).cuda().to(torch.bfloat16)
-    V = torch.from_numpy(np.stack(vs)).cuda().to(torch.bfloat16)
-    G = torch.from_numpy(np.stack(gs)).cuda()
+    qs, ks, vs, gs = Wl.make_decode_steps(Wd, steps)
+    Q = torch.from_numpy(qs).cuda().to(torch.bfloat16)
+    K = torch.from_numpy(ks).cuda().to(torch.bfloat16)
+    V = torch.from_numpy(vs).cuda().to(torch.bfloat16)
+    G = torch.from_numpy(gs.astype(np.float32)).cuda()
+    del qs, ks, vs, gs
     O = torch.empty_like(Q)
     stream = torch.cuda.current_stream().cuda_stream
     evs = ev.create(2 * steps)
@@ -277,7 +291,8 @@ def main():
                    "a": W.a, "iters": W.iters, "segments": pre["segments"]},
         "roofline": {"bound": "mfma", "kernel": "walk_kernel (fused chunk walk)",
                      "achieved": achieved / 1e12, "peak": PEAK_BF16_MFMA / 1e12,
-                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_MFMA, "traffic": None,
+                     "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_MFMA,
+                     "traffic": measured_traffic("walk_kernel"),
                      "flops_per_launch": F, "avg_launch_ms": pre["walk_ms"]},
         "whole_step_mfma_frac": F / (pre["ms_per_step"] * 1e-3) / PEAK_BF16_MFMA,
         "phases_ms": {"summary": pre["summary_ms"], "scan": pre["scan_ms"],
@@ -298,7 +313,8 @@ def main():
                          "achieved": bytes_launch / (dec["kernel_ms"] * 1e-3) / 1e9,
                          "peak": PEAK_HBM / 1e9, "unit": "GB/s",
                          "frac": bytes_launch / (dec["kernel_ms"] * 1e-3) / PEAK_HBM,
-                         "traffic": None, "bytes_per_launch": bytes_launch,
+                         "traffic": measured_traffic("step_kernel"),
+                         "bytes_per_launch": bytes_launch,
                          "avg_launch_ms": dec["kernel_ms"]},
         }
         log(f"decode: {dec['ms_per_step'] * 1e3:.1f} us/step, kernel {dec['kernel_ms'] * 1e3:.1f} us")

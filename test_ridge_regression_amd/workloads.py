@@ -10,18 +10,25 @@ of the "Main Findings" list of the ai.info summary. The gate values a in {0.1, 0
 among those studied in Fig. 9 (pith.science page, caption of Figure 9). The pages use no dataset
 for the forward itself, so every input is drawn here:
 
-  * q, k, v ~ N(0, 1) with shape [B, T, H, D] (drawn in that order, float64);
-  * z ~ N(mu, sd) with shape [B, T, H], gate gamma = sigmoid(z) stored as float32;
+  * every (batch row b, head h) and every block of 4096 tokens j has its own PCG64 stream,
+    keyed [seed, tag, b, h, j] (tag 0 = prefill, 1 = decode warm-up, 2 = decode steps); from
+    it q, k, v ~ N(0, 1) of shape [tokens, D] are drawn in that order (float64), then the gate
+    pre-activations z ~ N(mu, sd) of shape [tokens]; gate gamma = sigmoid(z) stored as float32;
   * q and k are divided by their L2 norm over D (the block's l2 normalisation, caption of
     Figure 2 on the pith.science page, is the caller's job);
   * bf16 workloads round q, k, v float64 -> float32 -> bfloat16 (round to nearest even).
 
-The arrays returned are float64 copies of exactly the values the device receives.
+The arrays returned are float64 copies of exactly the values the device receives (the decode
+step arrays are float32, which holds every bf16 value exactly). Independent streams per head
+let a test regenerate the heads it samples without drawing the rest, and let the full draws run
+on a thread pool.
 """
 from __future__ import annotations
 
 import dataclasses
-from typing import Dict, Optional
+import os
+from concurrent.futures import ThreadPoolExecutor
+from typing import Dict, List, Optional, Sequence, Tuple
 
 import numpy as np
 
@@ -87,46 +94,104 @@ def _unit(x: np.ndarray) -> np.ndarray:
     return x / np.linalg.norm(x, axis=-1, keepdims=True)
 
 
-def draw(rng: np.random.Generator, shape_btHD, gate_mu: float, gate_sd: float, dtype: str,
-         gamma_override: Optional[float] = None):
-    """Draw (q, k, v, gamma) in the fixed order; q/k unit-norm over the last axis."""
-    q = rng.standard_normal(shape_btHD)
-    k = rng.standard_normal(shape_btHD)
-    v = rng.standard_normal(shape_btHD)
-    z = rng.normal(gate_mu, gate_sd, shape_btHD[:-1])
+TOKEN_BLOCK = 4096  # tokens per independent stream
+TAG_PREFILL, TAG_WARMUP, TAG_STEPS = 0, 1, 2
+
+
+def _workers() -> int:
+    try:
+        n = len(os.sched_getaffinity(0))
+    except AttributeError:
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def draw_block(key: Sequence[int], n: int, D: int, gate_mu: float, gate_sd: float, dtype: str,
+               gamma_override: Optional[float] = None):
+    """One stream's tokens: q, k, v [n, D] (q, k unit-norm, rounded to dtype) and gamma [n]."""
+    rng = np.random.default_rng(list(key))
+    q = rng.standard_normal((n, D))
+    k = rng.standard_normal((n, D))
+    v = rng.standard_normal((n, D))
+    z = rng.normal(gate_mu, gate_sd, n)
     q = round_to(_unit(q), dtype)
     k = round_to(_unit(k), dtype)
     v = round_to(v, dtype)
     if gamma_override is None:
         gamma = (1.0 / (1.0 + np.exp(-z))).astype(np.float32)
     else:
-        gamma = np.full(z.shape, gamma_override, dtype=np.float32)
+        gamma = np.full(n, gamma_override, dtype=np.float32)
     return q, k, v, gamma.astype(np.float64)
 
 
+def _draw_grid(tag: int, cells: List[Tuple[int, int, int, int]], R: int, C: int, T: int, D: int,
+               gate_mu: float, gate_sd: float, dtype: str, seed: int,
+               gamma_override: Optional[float] = None, out_dtype=np.float64,
+               time_major: bool = False):
+    """Draw the streams of the cells (r, c, b, h) -- output slot (r, c), stream of head (b, h) --
+    into q, k, v [R, T, C, D] and gamma [R, T, C] ([T, R, C, ...] if ``time_major``)."""
+    lead = (T, R, C) if time_major else (R, T, C)
+    q, k, v = (np.empty(lead + (D,), dtype=out_dtype) for _ in range(3))
+    g = np.empty(lead, dtype=np.float64)
+    jobs = [(cell, t0) for cell in cells for t0 in range(0, T, TOKEN_BLOCK)]
+
+    def run(job):
+        (r, c, b, h), t0 = job
+        n = min(TOKEN_BLOCK, T - t0)
+        blk = draw_block((seed, tag, b, h, t0 // TOKEN_BLOCK), n, D, gate_mu, gate_sd, dtype,
+                         gamma_override)
+        idx = (slice(t0, t0 + n), r, c) if time_major else (r, slice(t0, t0 + n), c)
+        for dst, src in zip((q, k, v, g), blk):
+            dst[idx] = src
+
+    if len(jobs) == 1:
+        run(jobs[0])
+    else:
+        with ThreadPoolExecutor(_workers()) as ex:
+            list(ex.map(run, jobs))
+    return q, k, v, g
+
+
 def make_prefill(B: int, T: int, H: int, D: int, gate_mu: float, gate_sd: float, dtype: str,
-                 seed: int, gamma_override: Optional[float] = None):
-    """Inputs for one prefill call: q, k, v [B,T,H,D] and gamma [B,T,H], as float64 arrays."""
-    rng = np.random.default_rng(seed)
-    return draw(rng, (B, T, H, D), gate_mu, gate_sd, dtype, gamma_override)
+                 seed: int, gamma_override: Optional[float] = None,
+                 heads: Optional[Sequence[Tuple[int, int]]] = None):
+    """Inputs for one prefill call: q, k, v [B,T,H,D] and gamma [B,T,H], as float64 arrays.
 
-
-def make_workload(w: Workload, T: Optional[int] = None, B: Optional[int] = None):
-    """Prefill inputs for a named workload (optionally a T or B prefix-shaped variant)."""
-    return make_prefill(B or w.B, T or w.T, w.H, w.D, w.gate_mu, w.gate_sd, w.dtype, w.seed)
-
-
-def make_decode_warmup(w: Workload, B: Optional[int] = None):
-    """Warm-up tokens [B, warmup, H, D] that build the carried state before decoding."""
-    rng = np.random.default_rng([w.seed, 0])
-    return draw(rng, (B or w.B, w.warmup, w.H, w.D), w.gate_mu, w.gate_sd, w.dtype)
-
-
-def make_decode_step(w: Workload, step: int, B: Optional[int] = None):
-    """Inputs of recurrent step ``step`` (0-based): q, k, v [B,H,D], gamma [B,H].
-
-    Each step has its own stream (seed, step+1), so any step can be drawn on its own.
+    With ``heads`` (a list of (b, h) pairs) only those heads are drawn and the arrays are
+    [1, T, P, D] / [1, T, P], holding exactly the values of those heads in the full draw.
     """
-    rng = np.random.default_rng([w.seed, step + 1])
-    q, k, v, g = draw(rng, (B or w.B, 1, w.H, w.D), w.gate_mu, w.gate_sd, w.dtype)
-    return q[:, 0], k[:, 0], v[:, 0], g[:, 0]
+    if heads is None:
+        cells = [(b, h, b, h) for b in range(B) for h in range(H)]
+        return _draw_grid(TAG_PREFILL, cells, B, H, T, D, gate_mu, gate_sd, dtype, seed,
+                          gamma_override)
+    cells = [(0, i, b, h) for i, (b, h) in enumerate(heads)]
+    return _draw_grid(TAG_PREFILL, cells, 1, len(cells), T, D, gate_mu, gate_sd, dtype, seed,
+                      gamma_override)
+
+
+def make_workload(w: Workload, T: Optional[int] = None, B: Optional[int] = None,
+                  heads: Optional[Sequence[Tuple[int, int]]] = None):
+    """Prefill inputs for a named workload (optionally fewer tokens or rows, or sampled heads)."""
+    return make_prefill(B or w.B, T or w.T, w.H, w.D, w.gate_mu, w.gate_sd, w.dtype, w.seed,
+                        heads=heads)
+
+
+def make_decode_warmup(w: Workload, rows: Optional[Sequence[int]] = None):
+    """Warm-up tokens [R, warmup, H, D] (R = len(rows), default all rows) that build the
+    carried state before decoding."""
+    rows = list(range(w.B)) if rows is None else list(rows)
+    cells = [(i, h, b, h) for i, b in enumerate(rows) for h in range(w.H)]
+    return _draw_grid(TAG_WARMUP, cells, len(rows), w.H, w.warmup, w.D, w.gate_mu, w.gate_sd,
+                      w.dtype, w.seed)
+
+
+def make_decode_steps(w: Workload, steps: Optional[int] = None,
+                      rows: Optional[Sequence[int]] = None):
+    """Inputs of ``steps`` recurrent steps: q, k, v [steps, R, H, D] float32 and gamma
+    [steps, R, H] float64, for rows ``rows`` (default all rows). Step s of row b is the
+    token s of that row's own stream, so any subset of rows is drawn on its own."""
+    steps = w.steps if steps is None else steps
+    rows = list(range(w.B)) if rows is None else list(rows)
+    cells = [(i, h, b, h) for i, b in enumerate(rows) for h in range(w.H)]
+    return _draw_grid(TAG_STEPS, cells, len(rows), w.H, steps, w.D, w.gate_mu, w.gate_sd,
+                      w.dtype, w.seed, out_dtype=np.float32, time_major=True)

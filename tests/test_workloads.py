@@ -34,11 +34,36 @@ def test_workload_inputs(name):
     np.testing.assert_array_equal(g, g2)
 
 
-def test_decode_steps_are_independent_streams():
+def test_decode_streams_are_per_row():
     w = W.WORKLOADS["decode_b256_h8_d128"]
-    a = W.make_decode_step(w, 3, B=4)
-    b = W.make_decode_step(w, 3, B=4)
-    c = W.make_decode_step(w, 4, B=4)
-    np.testing.assert_array_equal(a[0], b[0])
-    assert not np.array_equal(a[0], c[0])
-    assert a[0].shape == (4, 8, 128) and a[3].shape == (4, 8)
+    a = W.make_decode_steps(w, steps=5, rows=[3, 9])
+    b = W.make_decode_steps(w, steps=5, rows=[9])
+    c = W.make_decode_steps(w, steps=7, rows=[9])
+    np.testing.assert_array_equal(a[0][:, 1], b[0][:, 0])
+    np.testing.assert_array_equal(c[0][:5], b[0])  # q of more steps extends the same stream
+    assert not np.array_equal(a[0][:, 0], a[0][:, 1])
+    assert a[0].shape == (5, 2, 8, 128) and a[3].shape == (5, 2, 8)
+    np.testing.assert_array_equal(W.round_bf16(a[2]), a[2])
+    wq = W.make_decode_warmup(w, rows=[9])
+    assert wq[0].shape == (1, w.warmup, 8, 128)
+    assert not np.array_equal(wq[0][0, :5], b[0][:, 0])  # warm-up and steps differ
+
+
+def test_sampled_heads_equal_the_full_draw():
+    w = W.WORKLOADS["prefill_b8_t2048_h8_d128"]
+    T = 300
+    q, k, v, g = W.make_workload(w, T=T, B=3)
+    pairs = [(2, 5), (0, 0), (1, 7)]
+    qs, ks, vs, gs = W.make_workload(w, T=T, heads=pairs)
+    for i, (b, h) in enumerate(pairs):
+        for full, samp in ((q, qs), (k, ks), (v, vs), (g, gs)):
+            np.testing.assert_array_equal(full[b, :, h], samp[0, :, i])
+
+
+def test_token_blocks_continue_across_streams():
+    # sequences longer than one stream block: the block boundary changes nothing visible
+    q, k, v, g = W.make_prefill(1, W.TOKEN_BLOCK + 10, 2, 16, 3.0, 1.0, "bf16", 11)
+    assert q.shape == (1, W.TOKEN_BLOCK + 10, 2, 16)
+    np.testing.assert_allclose(np.linalg.norm(q, axis=-1), 1.0, atol=1e-2)
+    q2, *_ = W.make_prefill(1, W.TOKEN_BLOCK, 2, 16, 3.0, 1.0, "bf16", 11)
+    np.testing.assert_array_equal(q[:, :W.TOKEN_BLOCK], q2)
