@@ -158,6 +158,17 @@ __device__ inline O to_op(float x) {
   return (O)x;
 }
 
+// ---- workgroup barrier for LDS exchange --------------------------------------------------
+// Completes this wave's LDS instructions (lgkmcnt) and meets the other waves; global loads,
+// stores and direct global-to-LDS loads stay in flight. __syncthreads() (and an LDS-scoped
+// fence, which counts direct loads as LDS writes) would wait for all of them, stalling the
+// barrier behind a prefetch issued for later use. Direct loads are never covered by this
+// barrier: they are waited for explicitly (vmcnt) before their buffer is read. The memory
+// clobber keeps the compiler from moving memory accesses across it.
+__device__ inline void lds_barrier() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // ---- wave reductions (wave64) -------------------------------------------------------------
 __device__ inline float wave_sum(float x) {
 #pragma unroll

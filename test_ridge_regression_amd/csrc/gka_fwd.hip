@@ -93,17 +93,45 @@ struct WalkCfg {
   static constexpr int VEC = 16 / (int)sizeof(T);         // elements per 16-byte unit
   static constexpr int UPR = D / VEC;                     // units per token row
   static constexpr int NU = C * UPR;                      // units per matrix
+  // It is a static LDS object of its own, apart from the dynamic buffer above, so that the
+  // compiler can tell reads of the other buffers from the in-flight direct loads and does not
+  // make them wait for the whole prefetch.
   static constexpr size_t szPreM = (size_t)NU * 16;
-  static constexpr size_t oPre = oVec + szVec;
-  static constexpr size_t bytes = oPre + 2 * szPreM + (size_t)C * sizeof(float);
+  static constexpr size_t szPre = 2 * szPreM + (size_t)C * sizeof(float);
+  static constexpr size_t bytes = oVec + szVec;  // dynamic part
   static_assert(NU % kWave == 0, "prefetch units must fill whole waves");
-  static_assert(bytes <= 160 * 1024, "LDS budget of one CU exceeded");
+  static_assert(bytes + szPre <= 160 * 1024, "LDS budget of one CU exceeded");
 };
 
-// Direct global-to-LDS loads of chunk chn's K, V and gates into the prefetch buffer (lane l of a
-// wave instruction lands at base + 16 l). Unit u = (column c, token t) with u = c*C + t holds
-// K[t][c*VEC .. c*VEC+VEC-1]; tokens past the end of the sequence are not loaded. (A plain device
-// function, whose body exists in the device compilation pass only.)
+// One direct global-to-LDS load per active lane: lane l copies 16 (or 4) bytes from src to
+// LDS address lds_base + 16 l (+ 4 l); lds_base is wave-uniform. Issued from inline assembly so
+// that the compiler does not track these loads as pending LDS writes: it would otherwise make
+// every later LDS read wait for them (it cannot tell the prefetch buffer from the others). Their
+// one consumer, the staging of the next chunk, waits for them explicitly (vmcnt(0) followed by
+// a workgroup barrier). They have no register results.
+__device__ inline void dma_load16(const void* src, uint32_t lds_base) {
+  uint32_t m0_saved;  // m0 is reserved by the compiler: restore it
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(m0_saved)
+      : "v"(src), "s"(lds_base)
+      : "memory");
+}
+__device__ inline void dma_load4(const void* src, uint32_t lds_base) {
+  uint32_t m0_saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+      "global_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(m0_saved)
+      : "v"(src), "s"(lds_base)
+      : "memory");
+}
+
+// Direct global-to-LDS loads of chunk chn's K, V and gates into the prefetch buffer. Unit
+// u = (column c, token t) with u = c*C + t holds K[t][c*VEC .. c*VEC+VEC-1]; tokens past the end
+// of the sequence are not loaded. (A plain device function, whose body exists in the device
+// compilation pass only.)
 template <typename T, int D, int C, typename V>
 __device__ inline void prefetch_chunk(V* PreK, V* PreV, float* PreG, const T* kg, const T* vg,
                                       const float* gamma, int b, int h, int Hn, int Tlen, int chn,
@@ -120,16 +148,18 @@ __device__ inline void prefetch_chunk(V* PreK, V* PreV, float* PreG, const T* kg
     const int qq = isv ? q - NI : q;
     const int u = qq * kWave + lane;
     const int t = u % C, c = u / C;
+    const uint32_t base = __builtin_amdgcn_readfirstlane(
+        (uint32_t)(uintptr_t)(lds_void*)((isv ? PreV : PreK) + qq * kWave));
     if (t < nvn) {
       const T* src = (isv ? vg : kg) + (b * (long long)Tlen + t0n + t) * tok_stride +
                      (long long)h * D + c * Cfg::VEC;
-      V* dst = (isv ? PreV : PreK) + qq * kWave;
-      __builtin_amdgcn_global_load_lds(src, (lds_void*)(dst), 16, 0, 0);
+      dma_load16(src, base);
     }
   }
-  if (wave == Cfg::NW - 1 && lane < nvn)
-    __builtin_amdgcn_global_load_lds(gamma + (b * (long long)Tlen + t0n + lane) * Hn + h,
-                                     (lds_void*)(PreG), 4, 0, 0);
+  if (wave == Cfg::NW - 1) {
+    const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)PreG);
+    if (lane < nvn) dma_load4(gamma + (b * (long long)Tlen + t0n + lane) * Hn + h, base);
+  }
 #endif
 }
 
@@ -168,16 +198,24 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
   float* p_v = p_u + NW * C;    // [NW][C] partials of sum_{s<t} M_{t-1,s} G_st^2
   float* v_sc = p_v + NW * C;   // [32] scalars
   typedef T vecT __attribute__((ext_vector_type(Cfg::VEC)));
-  vecT* PreK = reinterpret_cast<vecT*>(smem + Cfg::oPre);    // [UPR][C] units of K
+  __shared__ __attribute__((aligned(16))) unsigned char pre_buf[Cfg::szPre];
+  vecT* PreK = reinterpret_cast<vecT*>(pre_buf);              // [UPR][C] units of K
   vecT* PreV = PreK + Cfg::NU;                                // [UPR][C] units of V
   float* PreG = reinterpret_cast<float*>(PreV + Cfg::NU);     // [C] gates
 
   const int seg = blockIdx.x;
   const int bh = blockIdx.y;
   const int b = bh / Hn, h = bh % Hn;
-  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
-  const int lr = lane % 16;  // row (operand A) / column (operand B, accumulator) inside a tile
-  const int lg = lane / 16;  // lane group: operand K offset E*lg, accumulator rows 4*lg..
+  const int wave = threadIdx.x / kWave;
+  // Per-lane indices. They are passed through refresh() at the start of every phase of the chunk
+  // walk, so that the many addresses derived from them are recomputed where they are used instead
+  // of being computed once for the whole walk and kept live (which would spill them).
+  int tid = threadIdx.x, lane = tid % kWave;
+  int lr = lane % 16;  // row (operand A) / column (operand B, accumulator) inside a tile
+  int lg = lane / 16;  // lane group: operand K offset E*lg, accumulator rows 4*lg..
+  auto refresh = [&]() {
+    asm volatile("" : "+v"(tid), "+v"(lane), "+v"(lr), "+v"(lg));
+  };
   const int fg = wave % FG, tg = wave / FG;
   const bool tok_active = tg < TG;    // this wave owns feature x token tiles
   const bool state_active = tg < SG;  // this wave owns state tiles
@@ -236,6 +274,7 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
                                   lane);
 
   for (int ch = c_begin; ch < c_end; ++ch) {
+    refresh();
     const int t0 = ch * C;
     const int nv = min(C, Tlen - t0);  // valid tokens of this chunk
     const float n0 = sqrtf(n0sq);
@@ -319,7 +358,7 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
         for (int jc = 0; jc < CBW; ++jc)
           store4<O>(St + (col_of(jc) + lr) * LDD + row_of(jf) + 4 * lg, Hst[jf][jc] * n0inv);
     }
-    __syncthreads();
+    lds_barrier();
     // the prefetch buffer has been consumed. The next chunk's loads are issued once this chunk's
     // queries are in registers: the memory counter retires in order, so any wait for a load issued
     // after them (the queries, spill reloads) would also wait for the whole prefetch.
@@ -389,6 +428,7 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
           fK[js][kk] = sblk_of(js) < CT ? M::load(Ks, LDD, 16 * sblk_of(js) + lr, kk * K + E * lg)
                                         : Frag{};
 
+      refresh();
       // ---- norm phase ----------------------------------------------------------------------------
       // (a) G tiles (own s-blocks x own token tiles): partial sum_{s<t} 2^(cl_{t-1}-cl_s) G_st^2
       //     and ||k_t||^2 from the diagonal; (b) Y = H0hat K^T (own features x own tokens):
@@ -445,7 +485,7 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
           }
         }
       }
-      __syncthreads();
+      lds_barrier();
       // (c) n_t^2 by an affine scan over the chunk (wave 0, lane = token)
       if (wave == 0) {
         const int t = lane;
@@ -480,8 +520,9 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
           if (A.hnorm_t && t < nv) A.hnorm_t[(b * (long long)Tlen + t0 + t) * Hn + h] = sqrtf(n2);
         }
       }
-      __syncthreads();
+      lds_barrier();
 
+      refresh();
       // ---- Chebyshev loop on the residuals -------------------------------------------------------
       f32x4 R[FPW][TPW], Rp[FPW][TPW], Xa[FPW][TPW], Y[FPW][TPW];
       float sv[TPW];
@@ -606,13 +647,10 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
         }
       };
 
-      prefetch_next();
-      for (int it = 0; it + 1 < cc.iters; ++it) {
-        write_operand(R, false);
-        __syncthreads();
-        products_1(St, false);
-        __syncthreads();
-        products_2(fKT, false);
+      // residual update after the products of iteration it (Y = A R_i - a R_i):
+      // R_{i+1} = R_{i-1} + omega_i (R_i - R_{i-1} - c A R_i) (R_1 = R_0 - c A R_0), and
+      // X += beta_{i+1} R_{i+1}
+      auto update = [&](int it) {
         const float om = cc.omega[it], bn = cc.beta[it + 1];
 #pragma unroll
         for (int jf = 0; jf < FPW; ++jf)
@@ -625,8 +663,19 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
             R[jf][jt] = rn;
             Xa[jf][jt] += bn * rn;
           }
+      };
+
+      prefetch_next();
+      for (int it = 0; it + 1 < cc.iters; ++it) {
+        write_operand(R, false);
+        lds_barrier();
+        products_1(St, false);
+        lds_barrier();
+        products_2(fKT, false);
+        update(it);
       }
 
+      refresh();
       // U0hat = U0 / n0 into the staging buffer (every wave is past its last read of H0hat:
       // the loop ends with a barrier after the products that read it)
       if (state_active) {
@@ -646,9 +695,9 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
 #pragma unroll
         for (int kk = 0; kk < KC; ++kk) fVT[jf][kk] = M::load(VT, LDC, row_of(jf) + lr, kk * K + E * lg);
       write_operand(Xa, true);
-      __syncthreads();
+      lds_barrier();
       products_1(St, true);
-      __syncthreads();
+      lds_barrier();
       products_2(fVT, true);
       if (tok_active) {
 #pragma unroll
