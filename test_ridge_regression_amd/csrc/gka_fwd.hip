@@ -45,10 +45,13 @@
 
 namespace gka {
 
-template <typename T, int D, int C>
+// Tiling of one workgroup of NWaves waves: 8 for the fused walk (two waves per SIMD, each with
+// the register room for its share of the state, the iterate and the resident fragments); 16 for
+// the summary walk, which holds only the state and so spreads it over four waves per SIMD.
+template <typename T, int D, int C, int NWaves = 8>
 struct WalkCfg {
   typedef typename OperandOf<T>::type O;  // matrix-core operand type
-  static constexpr int NW = 8;
+  static constexpr int NW = NWaves;
   static constexpr int NT = NW * kWave;
   static constexpr int FT = D / 16;  // feature tiles
   static constexpr int CT = C / 16;  // token tiles
@@ -67,7 +70,7 @@ struct WalkCfg {
   static constexpr int E = Mma<O>::E;
   static constexpr bool SPLIT = sizeof(O) == 2;  // hi/lo operands for the output products
   static_assert(D % K == 0 && C % K == 0 && C <= kWave, "unsupported D / C");
-  static_assert(NT == 512, "walk_kernel is declared with __launch_bounds__(512)");
+  static_assert(NT <= 1024, "workgroup size");
 
   // LDS layout (bytes)
   static constexpr size_t szRD = (size_t)C * LDD * sizeof(O);  // [C][LDD]
@@ -99,6 +102,11 @@ struct WalkCfg {
   static constexpr size_t szPreM = (size_t)NU * 16;
   static constexpr size_t szPre = 2 * szPreM + (size_t)C * sizeof(float);
   static constexpr size_t bytes = oVec + szVec;  // dynamic part
+  // the summary walk (carry only) uses K^T, V^T and the per-token vectors alone
+  static constexpr size_t oKT_sum = 0;
+  static constexpr size_t oVT_sum = szDC;
+  static constexpr size_t oVec_sum = 2 * szDC;
+  static constexpr size_t bytes_sum = oVec_sum + szVec;
   static_assert(NU % kWave == 0, "prefetch units must fill whole waves");
   static_assert(bytes + szPre <= 160 * 1024, "LDS budget of one CU exceeded");
 };
@@ -132,12 +140,12 @@ __device__ inline void dma_load4(const void* src, uint32_t lds_base) {
 // u = (column c, token t) with u = c*C + t holds K[t][c*VEC .. c*VEC+VEC-1]; tokens past the end
 // of the sequence are not loaded. (A plain device function, whose body exists in the device
 // compilation pass only.)
-template <typename T, int D, int C, typename V>
+template <typename T, int D, int C, int NWaves, typename V>
 __device__ inline void prefetch_chunk(V* PreK, V* PreV, float* PreG, const T* kg, const T* vg,
                                       const float* gamma, int b, int h, int Hn, int Tlen, int chn,
                                       int wave, int lane) {
 #if defined(__HIP_DEVICE_COMPILE__)  // device code only: the host pass has no LDS address space
-  using Cfg = WalkCfg<T, D, C>;
+  using Cfg = WalkCfg<T, D, C, NWaves>;
   typedef __attribute__((address_space(3))) void lds_void;
   constexpr int NI = Cfg::NU / kWave;  // wave instructions per matrix
   const long long tok_stride = (long long)Hn * D;
@@ -164,9 +172,10 @@ __device__ inline void prefetch_chunk(V* PreK, V* PreV, float* PreG, const T* kg
 }
 
 template <typename T, int D, int C, bool SUMMARY>
-__global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, int Hn, int N,
+__global__ __launch_bounds__(SUMMARY ? 1024 : 512) void walk_kernel(WalkArgs A, int B, int Tlen,
+                                                                    int Hn, int N,
                                                    int S, int J, ChebConsts cc) {
-  using Cfg = WalkCfg<T, D, C>;
+  using Cfg = WalkCfg<T, D, C, SUMMARY ? 16 : 8>;
   using O = typename Cfg::O;
   using M = Mma<O>;
   using Frag = typename M::frag;
@@ -182,10 +191,10 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
   O* Ps = reinterpret_cast<O*>(smem + Cfg::oPs);
   O* Pl = reinterpret_cast<O*>(smem + Cfg::oPl);
   O* Ks = reinterpret_cast<O*>(smem + Cfg::oKs);
-  O* KT = reinterpret_cast<O*>(smem + Cfg::oKT);
-  O* VT = reinterpret_cast<O*>(smem + Cfg::oVT);
+  O* KT = reinterpret_cast<O*>(smem + (SUMMARY ? Cfg::oKT_sum : Cfg::oKT));
+  O* VT = reinterpret_cast<O*>(smem + (SUMMARY ? Cfg::oVT_sum : Cfg::oVT));
   O* St = reinterpret_cast<O*>(smem + Cfg::oSt);
-  float* vec = reinterpret_cast<float*>(smem + Cfg::oVec);
+  float* vec = reinterpret_cast<float*>(smem + (SUMMARY ? Cfg::oVec_sum : Cfg::oVec));
   float* v_cl = vec;            // [C] in-chunk log2 gate prefix
   float* v_gam = v_cl + C;      // [C] 2^cl
   float* v_w = v_gam + C;       // [C] carry weights 2^(cl_C - cl_s)
@@ -270,7 +279,7 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
   float log2g_seg = 0.0f;  // summary mode: running log2 of the segment's gate product
 
   if (c_begin < c_end)
-    prefetch_chunk<T, D, C, vecT>(PreK, PreV, PreG, kg, vg, A.gamma, b, h, Hn, Tlen, c_begin, wave,
+    prefetch_chunk<T, D, C, NW, vecT>(PreK, PreV, PreG, kg, vg, A.gamma, b, h, Hn, Tlen, c_begin, wave,
                                   lane);
 
   for (int ch = c_begin; ch < c_end; ++ch) {
@@ -364,17 +373,20 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
     // after them (the queries, spill reloads) would also wait for the whole prefetch.
     auto prefetch_next = [&]() {
       if (ch + 1 < c_end)
-        prefetch_chunk<T, D, C, vecT>(PreK, PreV, PreG, kg, vg, A.gamma, b, h, Hn, Tlen, ch + 1,
+        prefetch_chunk<T, D, C, NW, vecT>(PreK, PreV, PreG, kg, vg, A.gamma, b, h, Hn, Tlen, ch + 1,
                                       wave, lane);
     };
     if (SUMMARY) prefetch_next();
 
     // ---- operand fragments of the wave's rows, resident for the chunk --------------------------
+    // (the summary walk, which holds no other operands, loads them where the carry needs them)
     Frag fKT[FPW][KC];  // A operand K^T[f][s] (rows = own features)
+    if (!SUMMARY) {
 #pragma unroll
-    for (int jf = 0; jf < FPW; ++jf)
+      for (int jf = 0; jf < FPW; ++jf)
 #pragma unroll
-      for (int kk = 0; kk < KC; ++kk) fKT[jf][kk] = M::load(KT, LDC, row_of(jf) + lr, kk * K + E * lg);
+        for (int kk = 0; kk < KC; ++kk) fKT[jf][kk] = M::load(KT, LDC, row_of(jf) + lr, kk * K + E * lg);
+    }
 
     // ---- state carry: H <- Gam_C H + K^T diag(w) K, U^T <- Gam_C U^T + K^T diag(w) V ----------
     // (runs before the output products: the U0 copy for the output is staged already)
@@ -388,12 +400,13 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
         Frag aw[KC], awl[KC];
 #pragma unroll
         for (int kk = 0; kk < KC; ++kk) {
+          const Frag kf = SUMMARY ? M::load(KT, LDC, row_of(jf) + lr, kk * K + E * lg) : fKT[jf][kk];
           if constexpr (E == 1) {
-            aw[kk] = fKT[jf][kk] * v_w[kk * K + lg];
+            aw[kk] = kf * v_w[kk * K + lg];
           } else {
 #pragma unroll
             for (int e = 0; e < E; ++e) {
-              const float x = (float)fKT[jf][kk][e] * v_w[kk * K + E * lg + e];
+              const float x = (float)kf[e] * v_w[kk * K + E * lg + e];
               aw[kk][e] = (O)x;
               awl[kk][e] = (O)(x - (float)aw[kk][e]);
             }
@@ -783,13 +796,16 @@ __global__ __launch_bounds__(256) void scan_kernel(float* __restrict__ st,
 template <typename T, int D, int C>
 static hipError_t launch_walk_t(const FwdPlan& pl, bool summary, const WalkArgs& a,
                                 const ChebConsts& cc, hipStream_t stream) {
-  using Cfg = WalkCfg<T, D, C>;
+  using Cfg = WalkCfg<T, D, C, 8>;
+  using CfgS = WalkCfg<T, D, C, 16>;
   const dim3 grid(pl.S, pl.B * pl.H);
   auto kern = summary ? walk_kernel<T, D, C, true> : walk_kernel<T, D, C, false>;
+  const size_t bytes = summary ? CfgS::bytes_sum : Cfg::bytes;
+  const int threads = summary ? CfgS::NT : Cfg::NT;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::bytes);
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, grid, dim3(Cfg::NT), Cfg::bytes, stream, a, pl.B, pl.T, pl.H, pl.N,
+  hipLaunchKernelGGL(kern, grid, dim3(threads), bytes, stream, a, pl.B, pl.T, pl.H, pl.N,
                      pl.S, pl.J, cc);
   return hipGetLastError();
 }
