@@ -13,7 +13,7 @@ using gka::ChebConsts;
 using gka::FwdPlan;
 
 constexpr int kAbiVersion = 1;
-constexpr int kCUs = 256;  // MI355X compute units: the segment plan aims at >= 2 workgroups per CU
+constexpr int kCUs = 256;  // MI355X compute units: the segment plan aims at one workgroup per CU
 
 bool dims_supported(int dtype, int D) {
   if (dtype == GKA_BF16) return D == 32 || D == 64 || D == 128;
@@ -93,7 +93,9 @@ bool make_plan(const gka_params* p, FwdPlan& pl) {
   int S = p->segments;
   if (S <= 0) {
     const long long bh = (long long)p->B * p->H;
-    const long long want = (2LL * kCUs + bh - 1) / bh;  // workgroups >= 2 per CU
+    // one fused-walk workgroup fits a compute unit (its LDS): aim at one workgroup per CU;
+    // more segments only lengthen the segment scan
+    const long long want = (kCUs + bh - 1) / bh;
     S = (int)std::min<long long>(want, pl.N);
     if (pl.N / S < 2 && pl.N >= 2) S = std::max(1, pl.N / 2);  // keep >= 2 chunks per segment
   }

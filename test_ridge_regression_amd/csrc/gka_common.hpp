@@ -69,6 +69,38 @@ struct Mma<float> {
   }
 };
 
+// ---- operand fragments of a transposed matrix ---------------------------------------------
+// Fragment of M^T (rows r0 + lr of a 16-row tile, k-slots k0 + E lg .. + E - 1) for a matrix
+// stored row-major as M[k][r] with ld elements per row, i.e. the rows of M are the k index.
+// fp16: two transposing 8-byte LDS reads (ds_read_b64_tr_b16). Within each group of 16 lanes,
+// lane i of such a read receives element i % 4 of the 8-byte chunks addressed by lanes
+// i / 4 + 4 m (m = 0..3) of its group; lane j therefore addresses row k0 + 8 lg + 4 h + j / 4,
+// columns r0 + 4 (j % 4) .. + 3 (read h = 0, 1), and lane i receives M[k0 + 8 lg + 4 h + m][r0 + i].
+// Requires r0 and ld to be multiples of 4 (8-byte aligned chunks).
+template <typename O>
+__device__ inline typename Mma<O>::frag load_trans(const O* base, int ld, int r0, int k0, int lr,
+                                                  int lg);
+typedef __fp16 fp16x4_t __attribute__((__vector_size__(4 * sizeof(__fp16))));
+template <>
+__device__ inline f16x8 load_trans<f16>(const f16* base, int ld, int r0, int k0, int lr, int lg) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(3))) fp16x4_t lds_fp16x4;
+  const int s = k0 + 8 * lg + (lr >> 2), c = r0 + 4 * (lr & 3);
+  const fp16x4_t a = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)(base + s * ld + c));
+  const fp16x4_t b = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)(base + (s + 4) * ld + c));
+  return f16x8{(f16)a[0], (f16)a[1], (f16)a[2], (f16)a[3], (f16)b[0], (f16)b[1], (f16)b[2],
+               (f16)b[3]};
+#else
+  return f16x8{};
+#endif
+}
+// fp32 operands hold one k-slot per lane: a plain read of M[k0 + lg][r0 + lr]
+template <>
+__device__ inline float load_trans<float>(const float* base, int ld, int r0, int k0, int lr,
+                                          int lg) {
+  return base[(k0 + lg) * ld + r0 + lr];
+}
+
 // ---- element conversions ----------------------------------------------------------------
 __device__ inline float to_f32(bf16 x) { return (float)x; }
 __device__ inline float to_f32(float x) { return x; }
@@ -167,6 +199,51 @@ __device__ inline O to_op(float x) {
 // clobber keeps the compiler from moving memory accesses across it.
 __device__ inline void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// ---- wave scans (DPP: register-to-register lane moves, no LDS round trip) -----------------
+// dpp_ctrl encodings: row_shr:n = 0x110 + n (within rows of 16 lanes), row_bcast:15 = 0x142
+// (lane 15 of a row to the whole next row), row_bcast:31 = 0x143 (lane 31 to rows 2 and 3).
+// A lane whose source is outside its row, or whose row is masked off, keeps `old`.
+template <int CTRL, int ROW_MASK>
+__device__ inline float dpp_move(float old, float x) {
+  return __builtin_bit_cast(
+      float, __builtin_amdgcn_update_dpp(__builtin_bit_cast(int, old), __builtin_bit_cast(int, x),
+                                         CTRL, ROW_MASK, 0xf, false));
+}
+// inclusive prefix sum over groups of W lanes (W = 16, 32 or 64)
+template <int W>
+__device__ inline float scan_add(float x) {
+  static_assert(W == 16 || W == 32 || W == 64, "segment width");
+  x += dpp_move<0x111, 0xf>(0.0f, x);
+  x += dpp_move<0x112, 0xf>(0.0f, x);
+  x += dpp_move<0x114, 0xf>(0.0f, x);
+  x += dpp_move<0x118, 0xf>(0.0f, x);
+  if constexpr (W >= 32) x += dpp_move<0x142, 0xa>(0.0f, x);
+  if constexpr (W == 64) x += dpp_move<0x143, 0xc>(0.0f, x);
+  return x;
+}
+// inclusive scan of affine maps y -> a y + b over the wave (lane order = application order):
+// (a, b) of lane l becomes the composition of the maps of lanes 0..l
+__device__ inline void scan_affine(float& a, float& b) {
+  float ta, tb;
+#define GKA_AFFINE_STEP(CTRL, MASK)        \
+  ta = dpp_move<CTRL, MASK>(1.0f, a);      \
+  tb = dpp_move<CTRL, MASK>(0.0f, b);      \
+  b = a * tb + b;                          \
+  a = a * ta;
+  GKA_AFFINE_STEP(0x111, 0xf)
+  GKA_AFFINE_STEP(0x112, 0xf)
+  GKA_AFFINE_STEP(0x114, 0xf)
+  GKA_AFFINE_STEP(0x118, 0xf)
+  GKA_AFFINE_STEP(0x142, 0xa)
+  GKA_AFFINE_STEP(0x143, 0xc)
+#undef GKA_AFFINE_STEP
+}
+
+// value of x in lane l (wave-uniform l), read through a scalar register
+__device__ inline float lane_value(float x, int l) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
 }
 
 // ---- wave reductions (wave64) -------------------------------------------------------------

@@ -41,6 +41,8 @@
 //      state over the segment's chunks, and the segment's total gate (log2);
 //   2. segment scan: elementwise affine scan over segments -> segment-start states, final state;
 //   3. fused walk: per (segment, head), from the segment-start state, chunk by chunk.
+#include <type_traits>
+
 #include "gka_internal.hpp"
 
 namespace gka {
@@ -83,12 +85,9 @@ struct WalkCfg {
   static constexpr size_t oKs = oPs + szRC;   // K, token-major
   static constexpr size_t oKT = oKs + szRD;   // K^T
   static constexpr size_t oVT = oKT + szDC;   // V^T
-  // the lo parts of the output operands reuse the K, K^T and V^T buffers: by the time they are
-  // written K lives in registers (resident fragments), the carry (last reader of K^T) has run and
-  // the V^T fragments of the output are loaded
+  // the lo part of the output's iterate reuses the K buffer: by the time it is written K lives in
+  // registers (resident fragments)
   static constexpr size_t oRl = oKs;
-  static constexpr size_t oPl = oKT;
-  static_assert(!SPLIT || szRC <= 2 * szDC, "lo masked product must fit the K^T, V^T buffers");
   static constexpr size_t oSt = oVT + szDC;                // H0hat, then U0hat (row-major)
   static constexpr size_t oVec = oSt + szDD;
   // next chunk's raw K, V (16-byte units, [unit column][token]) and gates, filled by
@@ -102,11 +101,6 @@ struct WalkCfg {
   static constexpr size_t szPreM = (size_t)NU * 16;
   static constexpr size_t szPre = 2 * szPreM + (size_t)C * sizeof(float);
   static constexpr size_t bytes = oVec + szVec;  // dynamic part
-  // the summary walk (carry only) uses K^T, V^T and the per-token vectors alone
-  static constexpr size_t oKT_sum = 0;
-  static constexpr size_t oVT_sum = szDC;
-  static constexpr size_t oVec_sum = 2 * szDC;
-  static constexpr size_t bytes_sum = oVec_sum + szVec;
   static_assert(NU % kWave == 0, "prefetch units must fill whole waves");
   static_assert(bytes + szPre <= 160 * 1024, "LDS budget of one CU exceeded");
 };
@@ -171,11 +165,10 @@ __device__ inline void prefetch_chunk(V* PreK, V* PreV, float* PreG, const T* kg
 #endif
 }
 
-template <typename T, int D, int C, bool SUMMARY>
-__global__ __launch_bounds__(SUMMARY ? 1024 : 512) void walk_kernel(WalkArgs A, int B, int Tlen,
-                                                                    int Hn, int N,
+template <typename T, int D, int C>
+__global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, int Hn, int N,
                                                    int S, int J, ChebConsts cc) {
-  using Cfg = WalkCfg<T, D, C, SUMMARY ? 16 : 8>;
+  using Cfg = WalkCfg<T, D, C, 8>;
   using O = typename Cfg::O;
   using M = Mma<O>;
   using Frag = typename M::frag;
@@ -189,12 +182,11 @@ __global__ __launch_bounds__(SUMMARY ? 1024 : 512) void walk_kernel(WalkArgs A, 
   O* Rs = reinterpret_cast<O*>(smem + Cfg::oRs);
   O* Rl = reinterpret_cast<O*>(smem + Cfg::oRl);
   O* Ps = reinterpret_cast<O*>(smem + Cfg::oPs);
-  O* Pl = reinterpret_cast<O*>(smem + Cfg::oPl);
   O* Ks = reinterpret_cast<O*>(smem + Cfg::oKs);
-  O* KT = reinterpret_cast<O*>(smem + (SUMMARY ? Cfg::oKT_sum : Cfg::oKT));
-  O* VT = reinterpret_cast<O*>(smem + (SUMMARY ? Cfg::oVT_sum : Cfg::oVT));
+  O* KT = reinterpret_cast<O*>(smem + Cfg::oKT);
+  O* VT = reinterpret_cast<O*>(smem + Cfg::oVT);
   O* St = reinterpret_cast<O*>(smem + Cfg::oSt);
-  float* vec = reinterpret_cast<float*>(smem + (SUMMARY ? Cfg::oVec_sum : Cfg::oVec));
+  float* vec = reinterpret_cast<float*>(smem + Cfg::oVec);
   float* v_cl = vec;            // [C] in-chunk log2 gate prefix
   float* v_gam = v_cl + C;      // [C] 2^cl
   float* v_w = v_gam + C;       // [C] carry weights 2^(cl_C - cl_s)
@@ -207,10 +199,12 @@ __global__ __launch_bounds__(SUMMARY ? 1024 : 512) void walk_kernel(WalkArgs A, 
   float* p_v = p_u + NW * C;    // [NW][C] partials of sum_{s<t} M_{t-1,s} G_st^2
   float* v_sc = p_v + NW * C;   // [32] scalars
   typedef T vecT __attribute__((ext_vector_type(Cfg::VEC)));
+  // the next chunk is loaded straight into this LDS buffer ([UPR][C] units of K, then of V,
+  // then [C] gates) while the current one computes
   __shared__ __attribute__((aligned(16))) unsigned char pre_buf[Cfg::szPre];
-  vecT* PreK = reinterpret_cast<vecT*>(pre_buf);              // [UPR][C] units of K
-  vecT* PreV = PreK + Cfg::NU;                                // [UPR][C] units of V
-  float* PreG = reinterpret_cast<float*>(PreV + Cfg::NU);     // [C] gates
+  vecT* PreK = reinterpret_cast<vecT*>(pre_buf);
+  vecT* PreV = PreK + Cfg::NU;
+  float* PreG = reinterpret_cast<float*>(PreV + Cfg::NU);
 
   const int seg = blockIdx.x;
   const int bh = blockIdx.y;
@@ -250,7 +244,7 @@ __global__ __launch_bounds__(SUMMARY ? 1024 : 512) void walk_kernel(WalkArgs A, 
       Ust[jf][jc] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   float n0sq = 0.0f;
-  if (!SUMMARY) {
+  {
     float sq = 0.0f;
     if (A.in_h && state_active) {
       const float* ih = A.in_h + bh * A.in_bh + seg * A.in_seg;
@@ -276,11 +270,13 @@ __global__ __launch_bounds__(SUMMARY ? 1024 : 512) void walk_kernel(WalkArgs A, 
       for (int w = 0; w < NW; ++w) n0sq += v_sc[w];
     }
   }
-  float log2g_seg = 0.0f;  // summary mode: running log2 of the segment's gate product
 
-  if (c_begin < c_end)
-    prefetch_chunk<T, D, C, NW, vecT>(PreK, PreV, PreG, kg, vg, A.gamma, b, h, Hn, Tlen, c_begin, wave,
-                                  lane);
+  auto prefetch = [&](int chn) {
+    if (chn < c_end)
+      prefetch_chunk<T, D, C, NW, vecT>(PreK, PreV, PreG, kg, vg, A.gamma, b, h, Hn, Tlen, chn,
+                                        wave, lane);
+  };
+  prefetch(c_begin);
 
   for (int ch = c_begin; ch < c_end; ++ch) {
     refresh();
@@ -288,8 +284,8 @@ __global__ __launch_bounds__(SUMMARY ? 1024 : 512) void walk_kernel(WalkArgs A, 
     const int nv = min(C, Tlen - t0);  // valid tokens of this chunk
     const float n0 = sqrtf(n0sq);
     const float n0inv = n0 > 0.0f ? 1.0f / n0 : 0.0f;
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads into the prefetch buffer have landed
-    __syncthreads();                // all of them; LDS of the previous chunk is free
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads of this chunk have landed
+    __syncthreads();                // all waves' loads have landed; LDS of the previous chunk is free
 
     // ---- stage K (token-major), K^T, V^T as operands from the prefetch buffer -----------------
     // The token index runs fastest across lanes: unit reads are consecutive and the transposed
@@ -317,13 +313,13 @@ __global__ __launch_bounds__(SUMMARY ? 1024 : 512) void walk_kernel(WalkArgs A, 
           KT[(d0 + i) * LDC + t] = ko[i];
           VT[(d0 + i) * LDC + t] = to_op<O>(vv[i]);
         }
-        if (!SUMMARY) *reinterpret_cast<vecO*>(Ks + t * LDD + d0) = ko;
+        *reinterpret_cast<vecO*>(Ks + t * LDD + d0) = ko;
       }
     }
     // ---- queries of the own tiles (issued early; zeroed below where ||H_t|| = 0) ---------------
     typedef T raw4 __attribute__((ext_vector_type(4)));
     raw4 Qraw[FPW][TPW];
-    if (!SUMMARY) {
+    {
 #pragma unroll
       for (int jt = 0; jt < TPW; ++jt)
 #pragma unroll
@@ -344,23 +340,17 @@ __global__ __launch_bounds__(SUMMARY ? 1024 : 512) void walk_kernel(WalkArgs A, 
         g = PreG[lane];
         l2 = log2_gate(g);
       }
-      float cl = l2;
-#pragma unroll
-      for (int m = 1; m < kWave; m <<= 1) {
-        const float o = __shfl_up(cl, m, kWave);
-        if (lane >= m) cl += o;
-      }
-      const float clast = __shfl(cl, C - 1, kWave);
+      const float cl = scan_add<kWave>(l2);
+      const float clast = lane_value(cl, C - 1);
       if (lane < C) {
         v_cl[lane] = cl;
         v_gam[lane] = fast_exp2(cl);
         v_w[lane] = fast_exp2(fminf(clast - cl, 0.0f));
         v_g[lane] = g;
       }
-      log2g_seg += clast;
     }
     // ---- H0hat = H0 / n0 into the staging buffer (row-major; H symmetric) ----------------------
-    if (!SUMMARY && state_active) {
+    if (state_active) {
 #pragma unroll
       for (int jf = 0; jf < FPW; ++jf)
 #pragma unroll
@@ -371,22 +361,13 @@ __global__ __launch_bounds__(SUMMARY ? 1024 : 512) void walk_kernel(WalkArgs A, 
     // the prefetch buffer has been consumed. The next chunk's loads are issued once this chunk's
     // queries are in registers: the memory counter retires in order, so any wait for a load issued
     // after them (the queries, spill reloads) would also wait for the whole prefetch.
-    auto prefetch_next = [&]() {
-      if (ch + 1 < c_end)
-        prefetch_chunk<T, D, C, NW, vecT>(PreK, PreV, PreG, kg, vg, A.gamma, b, h, Hn, Tlen, ch + 1,
-                                      wave, lane);
-    };
-    if (SUMMARY) prefetch_next();
 
     // ---- operand fragments of the wave's rows, resident for the chunk --------------------------
-    // (the summary walk, which holds no other operands, loads them where the carry needs them)
     Frag fKT[FPW][KC];  // A operand K^T[f][s] (rows = own features)
-    if (!SUMMARY) {
 #pragma unroll
-      for (int jf = 0; jf < FPW; ++jf)
+    for (int jf = 0; jf < FPW; ++jf)
 #pragma unroll
-        for (int kk = 0; kk < KC; ++kk) fKT[jf][kk] = M::load(KT, LDC, row_of(jf) + lr, kk * K + E * lg);
-    }
+      for (int kk = 0; kk < KC; ++kk) fKT[jf][kk] = M::load(KT, LDC, row_of(jf) + lr, kk * K + E * lg);
 
     // ---- state carry: H <- Gam_C H + K^T diag(w) K, U^T <- Gam_C U^T + K^T diag(w) V ----------
     // (runs before the output products: the U0 copy for the output is staged already)
@@ -400,7 +381,7 @@ __global__ __launch_bounds__(SUMMARY ? 1024 : 512) void walk_kernel(WalkArgs A, 
         Frag aw[KC], awl[KC];
 #pragma unroll
         for (int kk = 0; kk < KC; ++kk) {
-          const Frag kf = SUMMARY ? M::load(KT, LDC, row_of(jf) + lr, kk * K + E * lg) : fKT[jf][kk];
+          const Frag kf = fKT[jf][kk];
           if constexpr (E == 1) {
             aw[kk] = kf * v_w[kk * K + lg];
           } else {
@@ -432,7 +413,7 @@ __global__ __launch_bounds__(SUMMARY ? 1024 : 512) void walk_kernel(WalkArgs A, 
       }
     };
 
-    if (!SUMMARY) {
+    {
       Frag fK[SBW][KD];  // A operand K[s][d] (rows = own s-blocks)
 #pragma unroll
       for (int js = 0; js < SBW; ++js)
@@ -515,14 +496,7 @@ __global__ __launch_bounds__(SUMMARY ? 1024 : 512) void walk_kernel(WalkArgs A, 
           a = g * g;
           bb = 2.0f * g * (gprev * n0 * u + vv) + kk * kk;
         }
-#pragma unroll
-        for (int m = 1; m < kWave; m <<= 1) {
-          const float ao = __shfl_up(a, m, kWave), bo = __shfl_up(bb, m, kWave);
-          if (lane >= m) {
-            bb = a * bo + bb;
-            a = a * ao;
-          }
-        }
+        scan_affine(a, bb);
         if (t < C) {
           const float n2 = a * n0sq + bb;
           const bool zero = !(n2 > 0.0f);
@@ -584,8 +558,10 @@ __global__ __launch_bounds__(SUMMARY ? 1024 : 512) void walk_kernel(WalkArgs A, 
             }
         }
       };
-      // Y = Mat V^T (own tiles; Mat read from LDS, row-major) and P'^T = (K V^T) o Mhat^T -> Ps
-      // (and Pl); the k-step loop is outermost so independent accumulators interleave
+      // Y = Mat V^T (own tiles; Mat read from LDS, row-major) and P'^T = (K V^T) o Mhat^T -> Ps;
+      // with split, V is taken as its hi + lo parts (P' itself is rounded once: its entries are
+      // the key-direction components, which carry no cancellation); the k-step loop is outermost
+      // so independent accumulators interleave
       auto products_1 = [&](const O* Mat, bool split) {
         if (tok_active) {
           f32x4 Pa[SBW][TPW];
@@ -629,31 +605,24 @@ __global__ __launch_bounds__(SUMMARY ? 1024 : 512) void walk_kernel(WalkArgs A, 
               const int sb = sblk_of(js);
               if (sb < CT) {
                 const int o = (tok_of(jt) + lr) * LDC + 16 * sb + 4 * lg;
-                if (SPLIT && split) store4_split<O>(Ps + o, Pl + o, Pa[js][jt] * Mh[js][jt]);
-                else store4<O>(Ps + o, Pa[js][jt] * Mh[js][jt]);
+                store4<O>(Ps + o, Pa[js][jt] * Mh[js][jt]);
               }
             }
         }
       };
       // Y = diag(s) Y + Mat2 P'^T (Mat2 fragments fB: K^T in the loop, V^T for the output)
-      auto products_2 = [&](Frag(&fB)[FPW][KC], bool split) {
+      auto products_2 = [&](Frag(&fB)[FPW][KC]) {
         if (tok_active) {
 #pragma unroll
           for (int jt = 0; jt < TPW; ++jt) {
-            Frag pb[KC], pl[KC];
+            Frag pb[KC];
 #pragma unroll
-            for (int kk = 0; kk < KC; ++kk) {
-              pb[kk] = M::load(Ps, LDC, tok_of(jt) + lr, kk * K + E * lg);
-              if (SPLIT && split) pl[kk] = M::load(Pl, LDC, tok_of(jt) + lr, kk * K + E * lg);
-            }
+            for (int kk = 0; kk < KC; ++kk) pb[kk] = M::load(Ps, LDC, tok_of(jt) + lr, kk * K + E * lg);
 #pragma unroll
             for (int jf = 0; jf < FPW; ++jf) {
               f32x4 acc = Y[jf][jt] * sv[jt];
 #pragma unroll
-              for (int kk = 0; kk < KC; ++kk) {
-                acc = M::mma(fB[jf][kk], pb[kk], acc);
-                if (SPLIT && split) acc = M::mma(fB[jf][kk], pl[kk], acc);
-              }
+              for (int kk = 0; kk < KC; ++kk) acc = M::mma(fB[jf][kk], pb[kk], acc);
               Y[jf][jt] = acc;
             }
           }
@@ -678,13 +647,13 @@ __global__ __launch_bounds__(SUMMARY ? 1024 : 512) void walk_kernel(WalkArgs A, 
           }
       };
 
-      prefetch_next();
+      prefetch(ch + 1);
       for (int it = 0; it + 1 < cc.iters; ++it) {
         write_operand(R, false);
         lds_barrier();
         products_1(St, false);
         lds_barrier();
-        products_2(fKT, false);
+        products_2(fKT);
         update(it);
       }
 
@@ -711,7 +680,7 @@ __global__ __launch_bounds__(SUMMARY ? 1024 : 512) void walk_kernel(WalkArgs A, 
       lds_barrier();
       products_1(St, true);
       lds_barrier();
-      products_2(fVT, true);
+      products_2(fVT);
       if (tok_active) {
 #pragma unroll
         for (int jf = 0; jf < FPW; ++jf)
@@ -726,40 +695,189 @@ __global__ __launch_bounds__(SUMMARY ? 1024 : 512) void walk_kernel(WalkArgs A, 
       }
     }
 
-    if (SUMMARY) carry();
-    if (!SUMMARY) n0sq = v_n2[C - 1];
+    n0sq = v_n2[C - 1];
   }
 
   // ---- results of the walk ------------------------------------------------------------------
-  if (SUMMARY) {
-    if (state_active) {
-      float* oh = A.sum_h + bh * A.sum_bh + seg * A.sum_seg;
-      float* ou = A.sum_u + bh * A.sum_bh + seg * A.sum_seg;
+  if (A.out_h && state_active) {
+    float* oh = A.out_h + (size_t)bh * D * D;
+    float* ou = A.out_u + (size_t)bh * D * D;
 #pragma unroll
-      for (int jf = 0; jf < FPW; ++jf)
+    for (int jf = 0; jf < FPW; ++jf)
 #pragma unroll
-        for (int jc = 0; jc < CBW; ++jc) {
-          const int r = row_of(jf) + 4 * lg, c = col_of(jc) + lr;
-          *reinterpret_cast<f32x4*>(oh + (size_t)c * D + r) = Hst[jf][jc];
-          *reinterpret_cast<f32x4*>(ou + (size_t)c * D + r) = Ust[jf][jc];
-        }
-    }
-    if (tid == 0) A.log2g_out[(long long)bh * S + seg] = log2g_seg;
-  } else {
-    if (A.out_h && state_active) {
-      float* oh = A.out_h + (size_t)bh * D * D;
-      float* ou = A.out_u + (size_t)bh * D * D;
-#pragma unroll
-      for (int jf = 0; jf < FPW; ++jf)
-#pragma unroll
-        for (int jc = 0; jc < CBW; ++jc) {
-          const int r = row_of(jf) + 4 * lg, c = col_of(jc) + lr;
-          *reinterpret_cast<f32x4*>(oh + (size_t)c * D + r) = Hst[jf][jc];
-          *reinterpret_cast<f32x4*>(ou + (size_t)c * D + r) = Ust[jf][jc];
-        }
-    }
-    if (A.n2_out && seg == S - 1 && tid == 0) A.n2_out[bh] = n0sq;
+      for (int jc = 0; jc < CBW; ++jc) {
+        const int r = row_of(jf) + 4 * lg, c = col_of(jc) + lr;
+        *reinterpret_cast<f32x4*>(oh + (size_t)c * D + r) = Hst[jf][jc];
+        *reinterpret_cast<f32x4*>(ou + (size_t)c * D + r) = Ust[jf][jc];
+      }
   }
+  if (A.n2_out && seg == S - 1 && tid == 0) A.n2_out[bh] = n0sq;
+}
+
+// Segment summaries (carry only): for each (segment, head), the state reached from a zero state
+// over the segment's chunks,
+//   H <- Gam_C H + K^T diag(w) K,  U^T <- Gam_C U^T + K^T diag(w) V  per chunk,
+// and the segment's total log2 gate. One workgroup of 16 waves per (segment, head), four waves
+// per SIMD, each holding its tiles of the float32 state. Per chunk every wave computes the gate
+// prefix of the chunk itself (lane = token, a scan over groups of C lanes). Each thread loads one
+// 16-byte unit of K and of V for the next chunk into registers (consecutive threads cover a
+// token's row: whole cache lines); they are staged token-major into LDS together with the
+// gate-weighted keys w K (split into hi + lo fp16 parts), one 16-byte write each, and the
+// carry reads its operands K^T, V^T and (w K)^T with transposing LDS reads.
+template <typename T, int D, int C>
+__global__ __launch_bounds__(1024) void summary_kernel(WalkArgs A, int B, int Tlen, int Hn, int N,
+                                                       int S, int J) {
+  using Cfg = WalkCfg<T, D, C, 16>;
+  using O = typename Cfg::O;
+  using M = Mma<O>;
+  using Frag = typename M::frag;
+  constexpr int LDD = Cfg::LDD, FG = Cfg::FG, SG = Cfg::SG, FPW = Cfg::FPW, CBW = Cfg::CBW;
+  constexpr int K = Cfg::K, E = Cfg::E, KC = C / K, VEC = Cfg::VEC, UPR = Cfg::UPR;
+  constexpr bool SPLIT = Cfg::SPLIT;
+  static_assert(Cfg::NU <= Cfg::NT, "one unit of K and V per thread");
+  static_assert(kWave % C == 0, "a chunk's tokens fit a wave");
+
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  O* Kt = reinterpret_cast<O*>(smem);  // [C][LDD] K, token-major
+  O* Vt = Kt + C * LDD;                // [C][LDD] V
+  O* Wh = Vt + C * LDD;                // [C][LDD] w K, hi part
+  O* Wl = Wh + C * LDD;                // [C][LDD] w K, lo part (fp16 operands only)
+  typedef T vecT __attribute__((ext_vector_type(VEC)));
+  typedef O vecO __attribute__((ext_vector_type(VEC)));
+
+  const int seg = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int b = bh / Hn, h = bh % Hn;
+  const int wave = threadIdx.x / kWave;
+  int tid = threadIdx.x, lane = tid % kWave;
+  int lr = lane % 16, lg = lane / 16;
+  auto refresh = [&]() { asm volatile("" : "+v"(tid), "+v"(lane), "+v"(lr), "+v"(lg)); };
+  const int fg = wave % FG, tg = wave / FG;
+  const bool state_active = tg < SG;
+  const int c_begin = seg * J;
+  const int c_end = min(N, c_begin + J);
+  const long long tok_stride = (long long)Hn * D;
+  const T* kg = static_cast<const T*>(A.k);
+  const T* vg = static_cast<const T*>(A.v);
+  auto row_of = [&](int jf) { return 16 * (fg * FPW + jf); };
+  auto col_of = [&](int jc) { return 16 * (tg * CBW + jc); };
+
+  f32x4 Hst[FPW][CBW], Ust[FPW][CBW];
+#pragma unroll
+  for (int jf = 0; jf < FPW; ++jf)
+#pragma unroll
+    for (int jc = 0; jc < CBW; ++jc) {
+      Hst[jf][jc] = f32x4{0.f, 0.f, 0.f, 0.f};
+      Ust[jf][jc] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  float log2g_seg = 0.0f;
+
+  // registers of the next two chunks (slot 0: the next one, slot 1: the one after): unit
+  // (token tid / UPR, column tid % UPR) of K and V, and the gate of token lane % C. Two chunks
+  // in flight keep enough bytes outstanding per compute unit to cover the memory latency.
+  vecT kreg[2] = {}, vreg[2] = {};
+  float greg[2] = {1.0f, 1.0f};
+  auto prefetch = [&](int chn, int slot) {
+    if (chn >= c_end) return;
+    const int t0n = chn * C, nvn = min(C, Tlen - t0n);
+    const int t = tid / UPR, c = tid % UPR;
+    if (tid < Cfg::NU && t < nvn) {
+      const long long off =
+          (b * (long long)Tlen + t0n + t) * tok_stride + (long long)h * D + c * VEC;
+      kreg[slot] = *reinterpret_cast<const vecT*>(kg + off);
+      vreg[slot] = *reinterpret_cast<const vecT*>(vg + off);
+    }
+    if (lane % C < nvn) greg[slot] = A.gamma[(b * (long long)Tlen + t0n + lane % C) * Hn + h];
+  };
+  prefetch(c_begin, 0);
+  prefetch(c_begin + 1, 1);
+
+  // one chunk; its data are in register slot SLOT (chunks alternate between the two slots, so
+  // that no register of a load in flight is ever copied)
+  auto chunk = [&](int ch, auto slot_tag) {
+    constexpr int SLOT = decltype(slot_tag)::value;
+    refresh();
+    const int nv = min(C, Tlen - ch * C);
+    const int tl = lane % C;  // this lane's token for the gate prefix
+    // in-chunk log2 gate prefix over the lane's group of C lanes; tokens past the end of the
+    // sequence have gamma = 1 (and zero keys and values)
+    const float gcur = greg[SLOT];
+    const float cl = scan_add<C>(tl < nv ? log2_gate(gcur) : 0.0f);
+    float clast;  // prefix at the last token of the lane's group
+    if constexpr (C == kWave) clast = lane_value(cl, C - 1);
+    else clast = __shfl(cl, C - 1, C);
+    const float wl = fast_exp2(fminf(clast - cl, 0.0f));  // carry weight of token tl
+    const float gC = fast_exp2(clast);
+    log2g_seg += clast;
+    const int t = tid / UPR, c = tid % UPR;  // this thread's unit
+    const float w = __shfl(wl, t % kWave);   // carry weight of its token (lane t holds it)
+    const vecT kv = kreg[SLOT], vv = vreg[SLOT];
+    lds_barrier();           // every wave is past the previous chunk's carry
+    prefetch(ch + 2, SLOT);  // in flight during this chunk and the next
+    if (tid < Cfg::NU) {
+      vecO ko, vo, xh, xl;
+#pragma unroll
+      for (int i = 0; i < VEC; ++i) {
+        ko[i] = t < nv ? to_op<O>(kv[i]) : (O)0.0f;
+        vo[i] = t < nv ? to_op<O>(vv[i]) : (O)0.0f;
+        const float x = (float)ko[i] * w;
+        xh[i] = (O)x;
+        xl[i] = (O)(x - (float)xh[i]);
+      }
+      const int o = t * LDD + c * VEC;
+      *reinterpret_cast<vecO*>(Kt + o) = ko;
+      *reinterpret_cast<vecO*>(Vt + o) = vo;
+      *reinterpret_cast<vecO*>(Wh + o) = xh;
+      if (SPLIT) *reinterpret_cast<vecO*>(Wl + o) = xl;
+    }
+    lds_barrier();  // the operands of this chunk are staged
+    if (state_active) {
+#pragma unroll
+      for (int jf = 0; jf < FPW; ++jf) {
+        Frag aw[KC], awl[KC];
+#pragma unroll
+        for (int kk = 0; kk < KC; ++kk) {
+          aw[kk] = load_trans<O>(Wh, LDD, row_of(jf), kk * K, lr, lg);
+          if (SPLIT) awl[kk] = load_trans<O>(Wl, LDD, row_of(jf), kk * K, lr, lg);
+        }
+#pragma unroll
+        for (int jc = 0; jc < CBW; ++jc) {
+          f32x4 hacc = Hst[jf][jc] * gC, uacc = Ust[jf][jc] * gC;
+#pragma unroll
+          for (int kk = 0; kk < KC; ++kk) {
+            const Frag bk = load_trans<O>(Kt, LDD, col_of(jc), kk * K, lr, lg);
+            const Frag bv = load_trans<O>(Vt, LDD, col_of(jc), kk * K, lr, lg);
+            hacc = M::mma(aw[kk], bk, hacc);
+            uacc = M::mma(aw[kk], bv, uacc);
+            if (SPLIT) {
+              hacc = M::mma(awl[kk], bk, hacc);
+              uacc = M::mma(awl[kk], bv, uacc);
+            }
+          }
+          Hst[jf][jc] = hacc;
+          Ust[jf][jc] = uacc;
+        }
+      }
+    }
+  };
+  for (int ch = c_begin; ch < c_end; ch += 2) {
+    chunk(ch, std::integral_constant<int, 0>());
+    if (ch + 1 < c_end) chunk(ch + 1, std::integral_constant<int, 1>());
+  }
+
+  if (state_active) {
+    float* oh = A.sum_h + bh * A.sum_bh + seg * A.sum_seg;
+    float* ou = A.sum_u + bh * A.sum_bh + seg * A.sum_seg;
+#pragma unroll
+    for (int jf = 0; jf < FPW; ++jf)
+#pragma unroll
+      for (int jc = 0; jc < CBW; ++jc) {
+        const int r = row_of(jf) + 4 * lg, c = col_of(jc) + lr;
+        *reinterpret_cast<f32x4*>(oh + (size_t)c * D + r) = Hst[jf][jc];
+        *reinterpret_cast<f32x4*>(ou + (size_t)c * D + r) = Ust[jf][jc];
+      }
+  }
+  if (tid == 0) A.log2g_out[(long long)bh * S + seg] = log2g_seg;
 }
 
 // Affine scan over segments, elementwise over the D x D entries of H and U.
@@ -799,9 +917,19 @@ static hipError_t launch_walk_t(const FwdPlan& pl, bool summary, const WalkArgs&
   using Cfg = WalkCfg<T, D, C, 8>;
   using CfgS = WalkCfg<T, D, C, 16>;
   const dim3 grid(pl.S, pl.B * pl.H);
-  auto kern = summary ? walk_kernel<T, D, C, true> : walk_kernel<T, D, C, false>;
-  const size_t bytes = summary ? CfgS::bytes_sum : Cfg::bytes;
-  const int threads = summary ? CfgS::NT : Cfg::NT;
+  if (summary) {
+    const size_t bytes = 4 * CfgS::szRD;  // K, V, w K hi and lo (token-major)
+    auto kern = summary_kernel<T, D, C>;
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(kern, grid, dim3(CfgS::NT), bytes, stream, a, pl.B, pl.T, pl.H, pl.N,
+                       pl.S, pl.J);
+    return hipGetLastError();
+  }
+  auto kern = walk_kernel<T, D, C>;
+  const size_t bytes = Cfg::bytes;
+  const int threads = Cfg::NT;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
   if (e != hipSuccess) return e;

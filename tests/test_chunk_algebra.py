@@ -137,8 +137,8 @@ def test_fp16_operand_rounding_budget(regime, mu, a, r):
 
     Rounded to fp16 (round to nearest even): the keys and values (exact for bf16 inputs in
     fp16's normal range), the copies H0/n0 and U0/n0 of the chunk-start state, the residual
-    operand of every product in the loop and the masked product P' that it feeds. Split into
-    hi + lo fp16 parts: the iterate X and its masked product in both output products, and the
+    operand of every product in the loop and the masked products P' (in the loop and in the
+    output). Split into hi + lo fp16 parts: the iterate X in both output products, and the
     gate-weighted keys of the carry (so the float32 state is accurate to float32). Rounding the
     plain iterate instead of the residual costs up to (1+a)/a times the unit error.
     """
@@ -184,7 +184,7 @@ def test_fp16_operand_rounding_budget(regime, mu, a, r):
 
         X = _residual_chebyshev(Q, apply, cst, om, r)
         Xs = split(X)
-        out[c0:c0 + C] = s[:, None] * (Xs @ Uh.T) + split((Xs @ K.T) * Mh) @ V
+        out[c0:c0 + C] = s[:, None] * (Xs @ Uh.T) + rh((Xs @ K.T) * Mh) @ V
         hn[c0:c0 + C] = n
         wK = split(K * (2.0 ** (cl[-1] - cl))[:, None])
         H0 = Gam[-1] * H0 + wK.T @ K
