@@ -72,6 +72,15 @@ ChebConsts cheb_consts(float a, int iters) {
     cc.omega[i] = (float)om[i];
     cc.beta[i] = (float)cur[i];
   }
+  // R_{i+1} = R_{i-1} + omega_i (R_i - R_{i-1} - c (Y + a R_i)) = kp R_{i-1} + kr R_i + ky Y,
+  // and the first step R_1 = R_0 - c (Y + a R_0)
+  const double c = 2.0 / (L + mu);
+  for (int i = 0; i < iters; ++i) {
+    const double w = i == 0 ? 1.0 : om[i];
+    cc.kp[i] = (float)(i == 0 ? 0.0 : 1.0 - w);
+    cc.kr[i] = (float)(w * (1.0 - c * ad));
+    cc.ky[i] = (float)(-w * c);
+  }
   return cc;
 }
 

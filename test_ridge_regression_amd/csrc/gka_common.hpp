@@ -267,12 +267,16 @@ __device__ inline float log2_gate(float g) {
 // lies in [a, 1 + a]: step c = 2 / (1 + 2a), weights omega_i (omega_0 = 2), and the weights
 // beta_i of the iterate x_r = sum_i beta_i r_i as a combination of the residuals r_i of the
 // same iteration. Filled on the host.
+// The residual recurrence is applied as R_{i+1} = kp_i R_{i-1} + kr_i R_i + ky_i (A - a I) R_i.
 struct ChebConsts {
   float a;
   float c;
   int iters;
   float omega[64];
   float beta[64];
+  float kp[64];
+  float kr[64];
+  float ky[64];
 };
 
 }  // namespace gka

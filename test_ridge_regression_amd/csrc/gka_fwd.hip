@@ -630,17 +630,16 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
       };
 
       // residual update after the products of iteration it (Y = A R_i - a R_i):
-      // R_{i+1} = R_{i-1} + omega_i (R_i - R_{i-1} - c A R_i) (R_1 = R_0 - c A R_0), and
+      // R_{i+1} = R_{i-1} + omega_i (R_i - R_{i-1} - c A R_i) (R_1 = R_0 - c A R_0), applied as
+      // kp_i R_{i-1} + kr_i R_i + ky_i Y with the coefficients expanded on the host; and
       // X += beta_{i+1} R_{i+1}
       auto update = [&](int it) {
-        const float om = cc.omega[it], bn = cc.beta[it + 1];
+        const float kp = cc.kp[it], kr = cc.kr[it], ky = cc.ky[it], bn = cc.beta[it + 1];
 #pragma unroll
         for (int jf = 0; jf < FPW; ++jf)
 #pragma unroll
           for (int jt = 0; jt < TPW; ++jt) {
-            const f32x4 ar = Y[jf][jt] + cc.a * R[jf][jt];  // A R_i
-            const f32x4 rn = it == 0 ? R[jf][jt] - cc.c * ar
-                                     : Rp[jf][jt] + om * (R[jf][jt] - Rp[jf][jt] - cc.c * ar);
+            const f32x4 rn = kp * Rp[jf][jt] + kr * R[jf][jt] + ky * Y[jf][jt];
             Rp[jf][jt] = R[jf][jt];
             R[jf][jt] = rn;
             Xa[jf][jt] += bn * rn;
