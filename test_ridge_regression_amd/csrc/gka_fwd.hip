@@ -374,37 +374,48 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
     auto carry = [&]() {
       if (!state_active) return;
       const float gC = v_gam[C - 1];
+      // A operand K^T[f][s] w_s of the own rows; for fp16 operands split into hi + lo parts so
+      // the float32 state gets the weighted keys to float32 accuracy
+      Frag aw[FPW][KC], awl[FPW][KC];
 #pragma unroll
-      for (int jf = 0; jf < FPW; ++jf) {
-        // A operand K^T[f][s] w_s of the own rows; for fp16 operands split into hi + lo parts so
-        // the float32 state gets the weighted keys to float32 accuracy
-        Frag aw[KC], awl[KC];
+      for (int kk = 0; kk < KC; ++kk) {
+        float wv[E];  // weights of this lane's k-slots
 #pragma unroll
-        for (int kk = 0; kk < KC; ++kk) {
+        for (int e = 0; e < E; ++e) wv[e] = v_w[kk * K + E * lg + e];
+#pragma unroll
+        for (int jf = 0; jf < FPW; ++jf) {
           const Frag kf = fKT[jf][kk];
           if constexpr (E == 1) {
-            aw[kk] = kf * v_w[kk * K + lg];
+            aw[jf][kk] = kf * wv[0];
           } else {
 #pragma unroll
             for (int e = 0; e < E; ++e) {
-              const float x = (float)kf[e] * v_w[kk * K + E * lg + e];
-              aw[kk][e] = (O)x;
-              awl[kk][e] = (O)(x - (float)aw[kk][e]);
+              const float x = (float)kf[e] * wv[e];
+              aw[jf][kk][e] = (O)x;
+              awl[jf][kk][e] = (O)(x - (float)aw[jf][kk][e]);
             }
           }
         }
+      }
+      // each B operand (columns of K^T and V^T) is loaded once and used for all own rows
 #pragma unroll
-        for (int jc = 0; jc < CBW; ++jc) {
+      for (int jc = 0; jc < CBW; ++jc) {
+        Frag bk[KC], bv[KC];
+#pragma unroll
+        for (int kk = 0; kk < KC; ++kk) {
+          bk[kk] = M::load(KT, LDC, col_of(jc) + lr, kk * K + E * lg);
+          bv[kk] = M::load(VT, LDC, col_of(jc) + lr, kk * K + E * lg);
+        }
+#pragma unroll
+        for (int jf = 0; jf < FPW; ++jf) {
           f32x4 hacc = Hst[jf][jc] * gC, uacc = Ust[jf][jc] * gC;
 #pragma unroll
           for (int kk = 0; kk < KC; ++kk) {
-            const Frag bk = M::load(KT, LDC, col_of(jc) + lr, kk * K + E * lg);
-            const Frag bv = M::load(VT, LDC, col_of(jc) + lr, kk * K + E * lg);
-            hacc = M::mma(aw[kk], bk, hacc);
-            uacc = M::mma(aw[kk], bv, uacc);
+            hacc = M::mma(aw[jf][kk], bk[kk], hacc);
+            uacc = M::mma(aw[jf][kk], bv[kk], uacc);
             if constexpr (E != 1) {
-              hacc = M::mma(awl[kk], bk, hacc);
-              uacc = M::mma(awl[kk], bv, uacc);
+              hacc = M::mma(awl[jf][kk], bk[kk], hacc);
+              uacc = M::mma(awl[jf][kk], bv[kk], uacc);
             }
           }
           Hst[jf][jc] = hacc;
@@ -428,40 +439,49 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
       //     and ||k_t||^2 from the diagonal; (b) Y = H0hat K^T (own features x own tokens):
       //     partial k_t^T H0hat k_t over the own features.
       if (tok_active) {
+        // all operand fragments first (one round of loads): K rows of the own tokens (B operand)
+        // and H0hat rows of the own features (A operand)
+        Frag fbt[TPW][KD], fh[FPW][KD];
+#pragma unroll
+        for (int jt = 0; jt < TPW; ++jt)
+#pragma unroll
+          for (int kk = 0; kk < KD; ++kk) fbt[jt][kk] = M::load(Ks, LDD, tok_of(jt) + lr, kk * K + E * lg);
+#pragma unroll
+        for (int jf = 0; jf < FPW; ++jf)
+#pragma unroll
+          for (int kk = 0; kk < KD; ++kk) fh[jf][kk] = M::load(St, LDD, row_of(jf) + lr, kk * K + E * lg);
         float pv[TPW], pu[TPW];
 #pragma unroll
         for (int jt = 0; jt < TPW; ++jt) {
+          const int t = tok_of(jt) + lr;
           pv[jt] = 0.0f;
           pu[jt] = 0.0f;
-        }
-#pragma unroll
-        for (int jt = 0; jt < TPW; ++jt) {
-          const int t = tok_of(jt) + lr;
-          Frag fb[KD];
-#pragma unroll
-          for (int kk = 0; kk < KD; ++kk) fb[kk] = M::load(Ks, LDD, tok_of(jt) + lr, kk * K + E * lg);
+          const float clp = t > 0 ? v_cl[t - 1] : 0.0f;
 #pragma unroll
           for (int js = 0; js < SBW; ++js) {
             const int sb = sblk_of(js);
             if (sb < CT) {
               f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-              for (int kk = 0; kk < KD; ++kk) acc = M::mma(fK[js][kk], fb[kk], acc);
-              const float clp = t > 0 ? v_cl[t - 1] : 0.0f;
+              for (int kk = 0; kk < KD; ++kk) acc = M::mma(fK[js][kk], fbt[jt][kk], acc);
+              // accumulator rows s = 16 sb + 4 lg + i of column t
+              const f32x4 cls = *reinterpret_cast<const f32x4*>(v_cl + 16 * sb + 4 * lg);
+              float kd = 0.0f;
 #pragma unroll
               for (int i = 0; i < 4; ++i) {
                 const int s = 16 * sb + 4 * lg + i;
-                if (s < t) pv[jt] += fast_exp2(fminf(clp - v_cl[s], 0.0f)) * (acc[i] * acc[i]);
-                if (s == t) v_kk[t] = acc[i];
+                const float e = fast_exp2(fminf(clp - cls[i], 0.0f)) * (acc[i] * acc[i]);
+                pv[jt] += s < t ? e : 0.0f;
+                kd = s == t ? acc[i] : kd;
               }
+              if (sb == (t >> 4) && lg == ((t & 15) >> 2)) v_kk[t] = kd;  // the lane with G_tt
             }
           }
 #pragma unroll
           for (int jf = 0; jf < FPW; ++jf) {
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < KD; ++kk)
-              acc = M::mma(M::load(St, LDD, row_of(jf) + lr, kk * K + E * lg), fb[kk], acc);
+            for (int kk = 0; kk < KD; ++kk) acc = M::mma(fh[jf][kk], fbt[jt][kk], acc);
             const f32x4 kf = load4<O>(Ks + t * LDD + row_of(jf) + 4 * lg);
             pu[jt] += acc[0] * kf[0] + acc[1] * kf[1] + acc[2] * kf[2] + acc[3] * kf[3];
           }
@@ -524,10 +544,12 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
           const int sb = sblk_of(js);
           if (tok_active && sb < CT) {
             const float ninv = v_ninv[t], clt = v_cl[t];
+            const f32x4 cls = *reinterpret_cast<const f32x4*>(v_cl + 16 * sb + 4 * lg);
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
               const int s = 16 * sb + 4 * lg + i;
-              m4[i] = s <= t ? fast_exp2(fminf(clt - v_cl[s], 0.0f)) * ninv : 0.0f;
+              const float m = fast_exp2(fminf(clt - cls[i], 0.0f)) * ninv;
+              m4[i] = s <= t ? m : 0.0f;
             }
           }
           Mh[js][jt] = m4;
