@@ -276,6 +276,24 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
       prefetch_chunk<T, D, C, NW, vecT>(PreK, PreV, PreG, kg, vg, A.gamma, b, h, Hn, Tlen, chn,
                                         wave, lane);
   };
+  // The output tile of a chunk is staged token-major (in the operand buffer, idle by then) and
+  // written out after the next workgroup barrier in 16-byte units, consecutive threads covering
+  // a token's row (whole cache lines instead of 8-byte pieces spread over 16 rows)
+  T* Ob = reinterpret_cast<T*>(smem + Cfg::oRs);  // [C][LDD] elements of T
+  int pend_t0 = 0, pend_nv = 0;                   // the staged tile: first token, tokens
+  auto flush_o = [&]() {
+    if (pend_nv > 0) {
+      for (int e = tid; e < Cfg::NU; e += Cfg::NT) {
+        const int t = e / Cfg::UPR, c = e % Cfg::UPR;
+        if (t < pend_nv) {
+          const vecT v = *reinterpret_cast<const vecT*>(Ob + t * LDD + c * Cfg::VEC);
+          *reinterpret_cast<vecT*>(og + (b * (long long)Tlen + pend_t0 + t) * tok_stride +
+                                   (long long)h * D + c * Cfg::VEC) = v;
+        }
+      }
+      pend_nv = 0;
+    }
+  };
   prefetch(c_begin);
 
   for (int ch = c_begin; ch < c_end; ++ch) {
@@ -286,6 +304,7 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
     const float n0inv = n0 > 0.0f ? 1.0f / n0 : 0.0f;
     __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads of this chunk have landed
     __syncthreads();                // all waves' loads have landed; LDS of the previous chunk is free
+    flush_o();                      // the previous chunk's output
 
     // ---- stage K (token-major), K^T, V^T as operands from the prefetch buffer -----------------
     // The token index runs fastest across lanes: unit reads are consecutive and the transposed
@@ -702,23 +721,23 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
       products_1(St, true);
       lds_barrier();
       products_2(fVT);
+      // every wave is past its reads of the operand buffer (the barrier before products_2)
       if (tok_active) {
 #pragma unroll
         for (int jf = 0; jf < FPW; ++jf)
 #pragma unroll
-          for (int jt = 0; jt < TPW; ++jt) {
-            const int t = tok_of(jt) + lr;
-            if (t < nv) {
-              const long long off = (b * (long long)Tlen + t0 + t) * tok_stride + (long long)h * D + row_of(jf) + 4 * lg;
-              store4<T>(og + off, Y[jf][jt]);
-            }
-          }
+          for (int jt = 0; jt < TPW; ++jt)
+            store4<T>(Ob + (tok_of(jt) + lr) * LDD + row_of(jf) + 4 * lg, Y[jf][jt]);
       }
+      pend_t0 = t0;
+      pend_nv = nv;
     }
 
     n0sq = v_n2[C - 1];
   }
 
+  lds_barrier();  // the last chunk's output tile is staged
+  flush_o();
   // ---- results of the walk ------------------------------------------------------------------
   if (A.out_h && state_active) {
     float* oh = A.out_h + (size_t)bh * D * D;
