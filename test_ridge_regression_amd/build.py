@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgka.so")
-SOURCES = ["gka_api.cpp", "gka_step.hip", "gka_fwd.hip"]
+SOURCES = ["gka_api.cpp", "gka_step.hip", "gka_fwd.hip", "gka_walk_tok.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -27,9 +27,15 @@ FLAGS = [
 ]
 
 
+# Per-source flags. The token-owning walk keeps matrix-core results in vector registers (its
+# products feed vector arithmetic directly); its resident operands are placed in the accumulator
+# registers by the kernel itself.
+EXTRA = {"gka_walk_tok.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+
+
 def _compile(src: str, verbose: bool) -> str:
     obj = os.path.join(BUILD, os.path.basename(src) + ".o")
-    cmd = [HIPCC, "-x", "hip", *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    cmd = [HIPCC, "-x", "hip", *FLAGS, *EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj]
     if verbose:
         cmd.insert(1, "-Rpass-analysis=kernel-resource-usage")
     r = subprocess.run(cmd, capture_output=True, text=True)

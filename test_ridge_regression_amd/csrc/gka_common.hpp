@@ -201,6 +201,31 @@ __device__ inline void lds_barrier() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
+// One direct global-to-LDS load per active lane: lane l copies 16 (or 4) bytes from src to
+// LDS address lds_base + 16 l (+ 4 l); lds_base is wave-uniform. Issued from inline assembly so
+// that the compiler does not track these loads as pending LDS writes: it would otherwise make
+// every later LDS read wait for them (it cannot tell the prefetch buffer from the others). Their
+// one consumer, the staging of the next chunk, waits for them explicitly (vmcnt(0) followed by
+// a workgroup barrier). They have no register results.
+__device__ inline void dma_load16(const void* src, uint32_t lds_base) {
+  uint32_t m0_saved;  // m0 is reserved by the compiler: restore it
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(m0_saved)
+      : "v"(src), "s"(lds_base)
+      : "memory");
+}
+__device__ inline void dma_load4(const void* src, uint32_t lds_base) {
+  uint32_t m0_saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
+      "global_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
+      : "=&s"(m0_saved)
+      : "v"(src), "s"(lds_base)
+      : "memory");
+}
+
 // ---- wave scans (DPP: register-to-register lane moves, no LDS round trip) -----------------
 // dpp_ctrl encodings: row_shr:n = 0x110 + n (within rows of 16 lanes), row_bcast:15 = 0x142
 // (lane 15 of a row to the whole next row), row_bcast:31 = 0x143 (lane 31 to rows 2 and 3).

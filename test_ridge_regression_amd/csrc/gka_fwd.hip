@@ -105,31 +105,6 @@ struct WalkCfg {
   static_assert(bytes + szPre <= 160 * 1024, "LDS budget of one CU exceeded");
 };
 
-// One direct global-to-LDS load per active lane: lane l copies 16 (or 4) bytes from src to
-// LDS address lds_base + 16 l (+ 4 l); lds_base is wave-uniform. Issued from inline assembly so
-// that the compiler does not track these loads as pending LDS writes: it would otherwise make
-// every later LDS read wait for them (it cannot tell the prefetch buffer from the others). Their
-// one consumer, the staging of the next chunk, waits for them explicitly (vmcnt(0) followed by
-// a workgroup barrier). They have no register results.
-__device__ inline void dma_load16(const void* src, uint32_t lds_base) {
-  uint32_t m0_saved;  // m0 is reserved by the compiler: restore it
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
-      "global_load_lds_dwordx4 %1, off\n\ts_mov_b32 m0, %0"
-      : "=&s"(m0_saved)
-      : "v"(src), "s"(lds_base)
-      : "memory");
-}
-__device__ inline void dma_load4(const void* src, uint32_t lds_base) {
-  uint32_t m0_saved;
-  asm volatile(
-      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %2\n\ts_nop 0\n\t"
-      "global_load_lds_dword %1, off\n\ts_mov_b32 m0, %0"
-      : "=&s"(m0_saved)
-      : "v"(src), "s"(lds_base)
-      : "memory");
-}
-
 // Direct global-to-LDS loads of chunk chn's K, V and gates into the prefetch buffer. Unit
 // u = (column c, token t) with u = c*C + t holds K[t][c*VEC .. c*VEC+VEC-1]; tokens past the end
 // of the sequence are not loaded. (A plain device function, whose body exists in the device
@@ -980,6 +955,7 @@ static hipError_t launch_walk_t(const FwdPlan& pl, bool summary, const WalkArgs&
 
 hipError_t launch_walk(const FwdPlan& pl, bool summary, const WalkArgs& a, const ChebConsts& cc,
                        hipStream_t stream) {
+  if (!summary && walk_tok_supported(pl)) return launch_walk_tok(pl, a, cc, stream);
   if (pl.dtype == 0) {
     if (pl.C == 64) {
       switch (pl.D) {

@@ -49,6 +49,12 @@ struct WalkArgs {
 hipError_t launch_walk(const FwdPlan& pl, bool summary, const WalkArgs& a, const ChebConsts& cc,
                        hipStream_t stream);
 
+// The chunk walk with token-owning waves (bf16 inputs, chunks of 64 tokens, D = 32, 64, 128):
+// same arguments and results as the feature-split walk of launch_walk.
+bool walk_tok_supported(const FwdPlan& pl);
+hipError_t launch_walk_tok(const FwdPlan& pl, const WalkArgs& a, const ChebConsts& cc,
+                           hipStream_t stream);
+
 // Affine scan over segments: start[s] = G_{s-1} start[s-1] + d_{s-1} (in place over d), final
 // state written to h/u when they are non-NULL; also copies hnorm2 to n2_seg0.
 hipError_t launch_scan(const FwdPlan& pl, float* ws_states, const float* ws_log2g, float* h,

@@ -1,0 +1,663 @@
+// Chunk walk of gka_fwd_chunked with token-owning waves (bf16 inputs, chunks of 64 tokens).
+//
+// The chunk algebra is the one of the feature-split walk in gka_fwd.hip ("Methodology in Plain
+// English" and "Key Contributions" 3 on the ai.info summary of arXiv 2511.21016): per chunk,
+//   Y_t   = s_t H0hat R_t + sum_{s<=t} Mhat_ts (k_s . R_t) k_s    (the system minus a I, on R_t)
+//   n_t^2 = gamma_t^2 n_{t-1}^2 + 2 gamma_t k_t^T H_{t-1} k_t + ||k_t||^4   (affine scan over t)
+//   o_t   = s_t U0hat X_t + sum_{s<=t} Mhat_ts (k_s . X_t) v_s
+//   carry H <- Gam_C H + K^T diag(w) K,  U^T <- Gam_C U^T + K^T diag(w) V
+// with H0hat = H0 / n0, U0hat = U0 / n0, s_t = Gam_t n0 / n_t, Mhat_ts = 2^(cl_t - cl_s) / n_t.
+//
+// Every token's Chebyshev iteration is a system of its own: Y_t needs R_t and the chunk's
+// shared matrices (H0hat, K), nothing of the other tokens' iterates. Wave w (one per SIMD)
+// therefore owns the 16 tokens 16w..16w+15 and all D features of them, and runs the whole
+// Chebyshev loop without exchanging anything with the other waves: the iterate stays in
+// matrix-core accumulators and is fed back as the B operand of the next products directly.
+//
+// For that the reduction index of a product over features (or tokens) is taken in a permuted
+// order within each block of 32: k-slot j of lane group g (slots 8g..8g+7 of the block) stands
+// for index 16 (j / 4) + 4 g + j % 4. The accumulator of a 16x16 output tile holds, in lane
+// (column c, group g), rows 4g..4g+3; with this order the B fragment of block kk of a
+// feature x token matrix is the accumulator rows of tiles 2kk and 2kk+1 of the same lane.
+// The A operands are laid out to match: K and H0hat (U0hat) are staged in LDS with their
+// feature columns permuted the same way (a fragment is one 16-byte read), and K^T / V^T
+// fragments in the permuted token order come from transposing LDS reads.
+//
+// Per chunk: stage K, V (fp16), gates and H0hat; the norm phase (k_t^T H0hat k_t from the
+// resident H0hat fragments, the Gram tiles of the own tokens) and a scan over the 64 tokens;
+// U0hat is staged; the carry advances the float32 state (held as accumulator tiles, a quarter
+// per wave); the Chebyshev loop; the output products. The next chunk's K, V and gates are
+// loaded straight into LDS during the loop.
+#include "gka_internal.hpp"
+
+namespace gka {
+namespace {
+
+template <int D>
+struct TokCfg {
+  static constexpr int C = 64;               // tokens per chunk
+  static constexpr int NW = 4;               // waves: one per SIMD
+  static constexpr int NT = NW * kWave;
+  static constexpr int FT = D / 16;          // feature tiles
+  static constexpr int KD = D / 32;          // 32-deep blocks over the features
+  static constexpr int KC = C / 32;          // 32-deep blocks over the tokens
+  static constexpr int ST = C / 16;          // token (s) tiles
+  static constexpr int NST = FT * FT / NW;   // state tiles per wave
+  static constexpr int NRT = NST >= FT ? NST / FT : 1;  // state row tiles per wave
+  static constexpr int NCT = NST >= FT ? FT : NST;      // state column tiles per wave
+  static constexpr int LDD = D + 8;          // row stride of the [*][D] fp16 / bf16 tiles
+  static constexpr bool PIN = D >= 128;      // resident fragments and state in AGPRs
+  static constexpr int VEC = 8;              // bf16 elements per 16-byte unit
+  static constexpr int UPR = D / VEC;        // units per token row
+  static constexpr int NU = C * UPR;         // units per matrix
+  static constexpr size_t szTok = (size_t)C * LDD * 2;
+  static constexpr size_t szHs = (size_t)D * LDD * 2;
+  static constexpr size_t oKp = 0;               // K, token-major, permuted features (fp16)
+  static constexpr size_t oVp = oKp + szTok;     // V, token-major (fp16)
+  static constexpr size_t oHs = oVp + szTok;     // H0hat, then U0hat: row-major, permuted columns
+  static constexpr size_t oOb = oHs + szHs;      // output tile, token-major (bf16)
+  static constexpr size_t oVec = oOb + szTok;
+  static constexpr size_t szVec = (size_t)(4 * C + 16 + 4 * 64) * sizeof(float);
+  static constexpr size_t bytes = oVec + szVec;  // dynamic LDS
+  static constexpr size_t szPre = 2 * (size_t)NU * 16 + C * sizeof(float);  // static LDS
+  static_assert(D % 32 == 0 && NST >= 1, "unsupported D");
+  static_assert(NU % NT == 0, "staging units must fill whole workgroups");
+  static_assert(bytes + szPre <= 160 * 1024, "LDS budget of one CU exceeded");
+};
+
+// column of logical feature d in a permuted row: within each block of 32, the four-element
+// group 4g + 16h (g = 0..3, h = 0, 1) sits at 8g + 4h
+__device__ constexpr int pcol(int d) {
+  return (d & ~31) + 8 * ((d >> 2) & 3) + 4 * ((d >> 4) & 1) + (d & 3);
+}
+
+// Operand fragment of M^T for a token-major matrix M[s][*] in LDS (row stride LDD): rows
+// (output index) col0 + lr, where the four columns col0 + 4q .. + 3 of a row start at element
+// off(q) of that row; the eight k-slots of lane group lg are tokens s0 + m (first read) and
+// s1 + m (second read), m = 0..3. Two transposing 8-byte reads (ds_read_b64_tr_b16): within a
+// group of 16 lanes, lane i receives element i % 4 of the chunks addressed by lanes i / 4 + 4m,
+// so lane q addresses row s + q / 4 at the four columns of lane group q % 4.
+template <int LDD>
+__device__ inline f16x8 frag_trans(const f16* base, int s0, int s1, int coff, int lr) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(3))) fp16x4_t lds_fp16x4;
+  const int r = lr >> 2;
+  const fp16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)(base + (s0 + r) * LDD + coff));
+  const fp16x4_t y = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)(base + (s1 + r) * LDD + coff));
+  return f16x8{(f16)x[0], (f16)x[1], (f16)x[2], (f16)x[3],
+               (f16)y[0], (f16)y[1], (f16)y[2], (f16)y[3]};
+#else
+  return f16x8{};
+#endif
+}
+
+// Register-class hints for values that only matrix-core instructions read between chunk
+// boundaries: the resident operand fragments and the float32 state live in the accumulator
+// registers (AGPRs), leaving the vector registers to the iterate and the products. An empty
+// asm statement with an AGPR operand makes the allocator keep the value there.
+template <typename V>
+__device__ inline void keep_in_agpr(V& x) {
+  asm volatile("" : "+a"(x));
+}
+
+__device__ inline f16x8 pack8(f32x4 a, f32x4 b) {
+  return f16x8{(f16)a[0], (f16)a[1], (f16)a[2], (f16)a[3], (f16)b[0], (f16)b[1], (f16)b[2],
+               (f16)b[3]};
+}
+
+template <int D>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, ChebConsts cc) {
+  using Cfg = TokCfg<D>;
+  using M = Mma<f16>;
+  typedef f16x8 Frag;
+  constexpr int C = Cfg::C, NW = Cfg::NW, NT = Cfg::NT, FT = Cfg::FT, KD = Cfg::KD;
+  constexpr int KC = Cfg::KC, ST = Cfg::ST, LDD = Cfg::LDD, UPR = Cfg::UPR, NU = Cfg::NU;
+  constexpr int NST = Cfg::NST, NRT = Cfg::NRT, NCT = Cfg::NCT;
+
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  f16* Kp = reinterpret_cast<f16*>(smem + Cfg::oKp);
+  f16* Vp = reinterpret_cast<f16*>(smem + Cfg::oVp);
+  f16* Hs = reinterpret_cast<f16*>(smem + Cfg::oHs);
+  bf16* Ob = reinterpret_cast<bf16*>(smem + Cfg::oOb);
+  float* v_cl = reinterpret_cast<float*>(smem + Cfg::oVec);  // [C] in-chunk log2 gate prefix
+  float* v_w = v_cl + C;    // [C] carry weights 2^(cl_C - cl_s)
+  float* v_a = v_w + C;     // [C] n^2 scan: a_t = gamma_t^2
+  float* v_b = v_a + C;     // [C] n^2 scan: b_t
+  float* v_sc = v_b + C;    // [16] scratch
+  float* v_coef = v_sc + 16;  // [iters][4] kp, kr, ky, beta of each iteration
+  // the next chunk's K and V ([token][unit], 16-byte units) and gates, loaded straight from
+  // global memory while the current chunk computes
+  __shared__ __attribute__((aligned(16))) unsigned char pre_buf[Cfg::szPre];
+  bf16x8* PreK = reinterpret_cast<bf16x8*>(pre_buf);
+  bf16x8* PreV = PreK + NU;
+  float* PreG = reinterpret_cast<float*>(PreV + NU);
+
+  const int seg = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int b = bh / Hn, h = bh % Hn;
+  const int wave = threadIdx.x / kWave;
+  // Per-lane indices, passed through refresh() at the start of every phase so that the
+  // addresses derived from them are recomputed where they are used instead of being hoisted
+  // out of the chunk loop and kept live for the whole walk (which would spill them)
+  int tid = threadIdx.x, lane = tid % kWave;
+  int lr = lane % 16, lg = lane / 16;
+  int t = 16 * wave + lr;  // own token (column of the wave's accumulator tiles)
+  auto refresh = [&]() { asm volatile("" : "+v"(tid), "+v"(lane), "+v"(lr), "+v"(lg), "+v"(t)); };
+  const int c_begin = seg * J;
+  const int c_end = min(N, c_begin + J);
+  const long long tok_stride = (long long)Hn * D;
+  const bf16* qg = static_cast<const bf16*>(A.q);
+  const bf16* kg = static_cast<const bf16*>(A.k);
+  const bf16* vg = static_cast<const bf16*>(A.v);
+  bf16* og = static_cast<bf16*>(A.o);
+
+  // ---- float32 state: tiles (a0 + jr, b0 + jc) of H and of U^T (rows = key features) -------
+  const int a0 = (wave * NST) / FT, b0 = (wave * NST) % FT;
+  f32x4 Hst[NRT][NCT], Ust[NRT][NCT];
+#pragma unroll
+  for (int jr = 0; jr < NRT; ++jr)
+#pragma unroll
+    for (int jc = 0; jc < NCT; ++jc) {
+      Hst[jr][jc] = f32x4{0.f, 0.f, 0.f, 0.f};
+      Ust[jr][jc] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  float n0sq = 0.0f;
+  {
+    float sq = 0.0f;
+    if (A.in_h) {
+      const float* ih = A.in_h + bh * A.in_bh + seg * A.in_seg;
+      const float* iu = A.in_u + bh * A.in_bh + seg * A.in_seg;
+#pragma unroll
+      for (int jr = 0; jr < NRT; ++jr)
+#pragma unroll
+        for (int jc = 0; jc < NCT; ++jc) {
+          // H[r..r+3][c] is read as H[c][r..r+3] (symmetric); U^T[r..r+3][c] = U[c][r..r+3]
+          const size_t o = (size_t)(16 * (b0 + jc) + lr) * D + 16 * (a0 + jr) + 4 * lg;
+          Hst[jr][jc] = *reinterpret_cast<const f32x4*>(ih + o);
+          Ust[jr][jc] = *reinterpret_cast<const f32x4*>(iu + o);
+          const f32x4 x = Hst[jr][jc];
+          sq += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
+        }
+    }
+    sq = wave_sum(sq);
+    if (lane == 0) v_sc[wave] = sq;
+    // Chebyshev coefficients, read from LDS in the loop (scalar loads in flight would make
+    // every wait for an LDS fragment a wait for all of them)
+    if (tid < cc.iters) {
+      v_coef[4 * tid] = cc.kp[tid];
+      v_coef[4 * tid + 1] = cc.kr[tid];
+      v_coef[4 * tid + 2] = cc.ky[tid];
+      v_coef[4 * tid + 3] = cc.beta[tid];
+    }
+    __syncthreads();
+    if (seg == 0 && A.n2_in) {
+      n0sq = A.n2_in[bh];
+    } else if (A.in_h) {
+      for (int w = 0; w < NW; ++w) n0sq += v_sc[w];
+    }
+  }
+
+  auto prefetch = [&](int chn) {
+#if defined(__HIP_DEVICE_COMPILE__)
+    if (chn >= c_end) return;
+    refresh();  // keeps the per-lane source addresses from being hoisted out of the chunk loop
+    typedef __attribute__((address_space(3))) void lds_void;
+    constexpr int NI = NU / kWave;  // wave instructions per matrix
+    static_assert(NI % NW == 0, "prefetch instructions must split evenly over the waves");
+    const int t0n = chn * C;
+    const int nvn = min(C, Tlen - t0n);
+    const long long row0 = (b * (long long)Tlen + t0n) * tok_stride + (long long)h * D;
+    const bf16* ks = kg + row0;
+    const bf16* vs = vg + row0;
+#pragma unroll
+    for (int k = 0; k < NI / NW; ++k) {
+      const int qq = wave + k * NW;
+      const int u = qq * kWave + lane;
+      const int tt = u / UPR, cu = u % UPR;
+      const uint32_t kb = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)(PreK + qq * kWave));
+      const uint32_t vb = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)(PreV + qq * kWave));
+      if (tt < nvn) {
+        const long long off = (long long)tt * tok_stride + cu * Cfg::VEC;
+        dma_load16(ks + off, kb);
+        dma_load16(vs + off, vb);
+      }
+    }
+    if (wave == NW - 1) {
+      const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)PreG);
+      if (lane < nvn) dma_load4(A.gamma + (b * (long long)Tlen + t0n + lane) * Hn + h, base);
+    }
+#endif
+  };
+  // the output tile of a chunk is written out after the next workgroup barrier, in 16-byte
+  // units with consecutive threads along a token's row
+  int pend_t0 = 0, pend_nv = 0;
+  auto flush_o = [&]() {
+    if (pend_nv > 0) {
+#pragma unroll
+      for (int k = 0; k < NU / NT; ++k) {
+        const int u = tid + k * NT;
+        const int tt = u / UPR, cu = u % UPR;
+        if (tt < pend_nv)
+          *reinterpret_cast<bf16x8*>(og + (b * (long long)Tlen + pend_t0 + tt) * tok_stride +
+                                     (long long)h * D + cu * Cfg::VEC) =
+              *reinterpret_cast<const bf16x8*>(Ob + tt * LDD + cu * Cfg::VEC);
+      }
+      pend_nv = 0;
+    }
+  };
+  // state tiles (times sc) -> Hs as fp16 rows e = column index of the tile, permuted columns
+  auto stage_state = [&](f32x4(&St)[NRT][NCT], float sc) {
+#pragma unroll
+    for (int jr = 0; jr < NRT; ++jr)
+#pragma unroll
+      for (int jc = 0; jc < NCT; ++jc) {
+        const f32x4 x = St[jr][jc] * sc;
+        f16x4 y = {(f16)x[0], (f16)x[1], (f16)x[2], (f16)x[3]};
+        *reinterpret_cast<f16x4*>(Hs + (16 * (b0 + jc) + lr) * LDD + pcol(16 * (a0 + jr) + 4 * lg)) = y;
+      }
+  };
+  // A fragment of K (rows = tokens 16 sb + lr) over feature block kk
+  auto frag_k = [&](int sb, int kk) {
+    return *reinterpret_cast<const Frag*>(Kp + (16 * sb + lr) * LDD + 32 * kk + 8 * lg);
+  };
+
+  prefetch(c_begin);
+
+  for (int ch = c_begin; ch < c_end; ++ch) {
+    refresh();
+    const int t0 = ch * C;
+    const int nv = min(C, Tlen - t0);
+    const float n0 = sqrtf(n0sq);
+    const float n0inv = n0 > 0.0f ? 1.0f / n0 : 0.0f;
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads of this chunk have landed
+    __syncthreads();                // every wave's loads have landed; the last chunk's LDS reads are done
+    flush_o();
+
+    // ---- queries of the own token, accumulator layout: Q[t][16 ft + 4 lg .. + 3] ------------
+    bf16x4 Qraw[FT];
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft) {
+      bf16x4 qv = {(bf16)0.0f, (bf16)0.0f, (bf16)0.0f, (bf16)0.0f};
+      if (t < nv)
+        qv = *reinterpret_cast<const bf16x4*>(qg + (b * (long long)Tlen + t0 + t) * tok_stride +
+                                               (long long)h * D + 16 * ft + 4 * lg);
+      Qraw[ft] = qv;
+    }
+    // ---- gate prefix (every wave; lane = token) ---------------------------------------------
+    float g_l = 1.0f, l2 = 0.0f;  // tokens past the end: gamma = 1 with k = v = q = 0
+    if (lane < nv) {
+      g_l = PreG[lane];
+      l2 = log2_gate(g_l);
+    }
+    const float cl = scan_add<kWave>(l2);
+    const float clast = lane_value(cl, C - 1);
+    const float gam = fast_exp2(cl);
+    const float gC = lane_value(gam, C - 1);
+    if (wave == 0) {
+      v_cl[lane] = cl;
+      v_w[lane] = fast_exp2(fminf(clast - cl, 0.0f));
+    }
+    // ---- stage K (fp16, permuted features) and V (fp16) ------------------------------------
+#pragma unroll
+    for (int k = 0; k < NU / NT; ++k) {
+      const int u = tid + k * NT;
+      const int tt = u / UPR, cu = u % UPR;
+      bf16x8 kv = PreK[u], vv = PreV[u];
+      f16x8 ko, vo;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        ko[i] = tt < nv ? (f16)(float)kv[i] : (f16)0.0f;
+        vo[i] = tt < nv ? (f16)(float)vv[i] : (f16)0.0f;
+      }
+      *reinterpret_cast<f16x8*>(Vp + tt * LDD + 8 * cu) = vo;
+      *reinterpret_cast<f16x4*>(Kp + tt * LDD + pcol(8 * cu)) = f16x4{ko[0], ko[1], ko[2], ko[3]};
+      *reinterpret_cast<f16x4*>(Kp + tt * LDD + pcol(8 * cu + 4)) = f16x4{ko[4], ko[5], ko[6], ko[7]};
+    }
+    stage_state(Hst, n0inv);  // H0hat
+    lds_barrier();
+
+    // the queries are consumed before the next chunk's loads are issued: loads retire in order,
+    // so a wait for the queries issued after the prefetch would also wait for the prefetch
+    f32x4 Ra[FT], Rb[FT], X[FT];
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft) {
+      Ra[ft] = f32x4{(float)Qraw[ft][0], (float)Qraw[ft][1], (float)Qraw[ft][2], (float)Qraw[ft][3]};
+      asm volatile("" : "+v"(Ra[ft]));
+    }
+    prefetch(ch + 1);
+    refresh();
+
+    // ---- resident H0hat fragments ------------------------------------------------------------
+    Frag Hres[FT][KD];
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+      for (int kk = 0; kk < KD; ++kk)
+        Hres[ft][kk] = *reinterpret_cast<const Frag*>(Hs + (16 * ft + lr) * LDD + 32 * kk + 8 * lg);
+    if constexpr (Cfg::PIN) {
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk) keep_in_agpr(Hres[ft][kk]);
+    }
+
+    // ---- norm phase: k_t^T H0hat k_t and sum_{s<t} 2^(cl_{t-1} - cl_s) G_st^2 ---------------
+    {
+      Frag kb[KD];  // B fragments of the own token's key
+#pragma unroll
+      for (int kk = 0; kk < KD; ++kk)
+        kb[kk] = *reinterpret_cast<const Frag*>(Kp + t * LDD + 32 * kk + 8 * lg);
+      float pu = 0.0f;
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft) {
+        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk) z = M::mma(Hres[ft][kk], kb[kk], z);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pu += z[i] * (float)kb[ft / 2][4 * (ft % 2) + i];
+      }
+      const float clp = t > 0 ? v_cl[t - 1] : 0.0f;
+      float pv = 0.0f, kd = 0.0f;
+#pragma unroll
+      for (int sb = 0; sb < ST; ++sb) {
+        f32x4 gacc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk) gacc = M::mma(frag_k(sb, kk), kb[kk], gacc);
+        const f32x4 cls = *reinterpret_cast<const f32x4*>(v_cl + 16 * sb + 4 * lg);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int s = 16 * sb + 4 * lg + i;
+          const float e = fast_exp2(fminf(clp - cls[i], 0.0f)) * (gacc[i] * gacc[i]);
+          pv += s < t ? e : 0.0f;
+          kd = s == t ? gacc[i] : kd;
+        }
+      }
+      pu += __shfl_xor(pu, 16, kWave);
+      pu += __shfl_xor(pu, 32, kWave);
+      pv += __shfl_xor(pv, 16, kWave);
+      pv += __shfl_xor(pv, 32, kWave);
+      kd += __shfl_xor(kd, 16, kWave);
+      kd += __shfl_xor(kd, 32, kWave);
+      const float gt = __shfl(g_l, t, kWave);
+      const float gprev = __shfl(gam, t > 0 ? t - 1 : 0, kWave);
+      if (lg == 0) {
+        v_a[t] = gt * gt;
+        v_b[t] = 2.0f * gt * ((t > 0 ? gprev : 1.0f) * n0 * pu + pv) + kd * kd;
+      }
+    }
+    lds_barrier();
+
+    // ---- n_t^2 by an affine scan over the chunk (every wave; lane = token) -------------------
+    refresh();
+    float sa = v_a[lane], sb_ = v_b[lane];
+    scan_affine(sa, sb_);
+    const float n2 = sa * n0sq + sb_;
+    const float ninv = n2 > 0.0f ? 1.0f / sqrtf(n2) : 0.0f;
+    if (wave == 0 && A.hnorm_t && lane < nv)
+      A.hnorm_t[(b * (long long)Tlen + t0 + lane) * Hn + h] = sqrtf(n2);
+    const float n2last = lane_value(n2, C - 1);
+    const float ninv_t = __shfl(ninv, t, kWave);
+    const float s_t = __shfl(gam, t, kWave) * n0 * ninv_t;
+    const float cl_t = __shfl(cl, t, kWave);
+    // Mhat^T tiles of the own token: Mh[sb][i] = Mhat_{t, 16 sb + 4 lg + i}
+    f32x4 Mh[ST];
+#pragma unroll
+    for (int sb = 0; sb < ST; ++sb) {
+      const f32x4 cls = *reinterpret_cast<const f32x4*>(v_cl + 16 * sb + 4 * lg);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int s = 16 * sb + 4 * lg + i;
+        Mh[sb][i] = s <= t ? fast_exp2(fminf(cl_t - cls[i], 0.0f)) * ninv_t : 0.0f;
+      }
+    }
+    stage_state(Ust, n0inv);  // U0hat (every wave has read its H0hat fragments)
+
+    // ---- state carry: H <- Gam_C H + K^T diag(w) K, U^T <- Gam_C U^T + K^T diag(w) V --------
+    {
+      // A operands (w K)^T of the own row tiles, tokens in natural order, split hi + lo
+      Frag awh[NRT][KC], awl[NRT][KC];
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const int s0 = 32 * kc + 8 * lg;
+        const f32x4 w0 = *reinterpret_cast<const f32x4*>(v_w + s0);
+        const f32x4 w1 = *reinterpret_cast<const f32x4*>(v_w + s0 + 4);
+#pragma unroll
+        for (int jr = 0; jr < NRT; ++jr) {
+          const int a = a0 + jr;
+          const Frag kf = frag_trans<LDD>(Kp, s0, s0 + 4, 32 * (a >> 1) + 8 * (lr & 3) + 4 * (a & 1), lr);
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float x = (float)kf[j] * (j < 4 ? w0[j] : w1[j - 4]);
+            awh[jr][kc][j] = (f16)x;
+            awl[jr][kc][j] = (f16)(x - (float)awh[jr][kc][j]);
+          }
+        }
+      }
+#pragma unroll
+      for (int jc = 0; jc < NCT; ++jc) {
+        const int bc = b0 + jc;
+        Frag bk[KC], bv[KC];
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) {
+          const int s0 = 32 * kc + 8 * lg;
+          bk[kc] = frag_trans<LDD>(Kp, s0, s0 + 4, 32 * (bc >> 1) + 8 * (lr & 3) + 4 * (bc & 1), lr);
+          bv[kc] = frag_trans<LDD>(Vp, s0, s0 + 4, 16 * bc + 4 * (lr & 3), lr);
+        }
+#pragma unroll
+        for (int jr = 0; jr < NRT; ++jr) {
+          f32x4 hacc = Hst[jr][jc] * gC, uacc = Ust[jr][jc] * gC;
+#pragma unroll
+          for (int kc = 0; kc < KC; ++kc) {
+            hacc = M::mma(awh[jr][kc], bk[kc], hacc);
+            hacc = M::mma(awl[jr][kc], bk[kc], hacc);
+            uacc = M::mma(awh[jr][kc], bv[kc], uacc);
+            uacc = M::mma(awl[jr][kc], bv[kc], uacc);
+          }
+          Hst[jr][jc] = hacc;
+          Ust[jr][jc] = uacc;
+          if constexpr (Cfg::PIN) {
+            keep_in_agpr(Hst[jr][jc]);
+            keep_in_agpr(Ust[jr][jc]);
+          }
+        }
+      }
+    }
+
+    // ---- Chebyshev loop on the residuals of the own token ----------------------------------
+    refresh();
+    // A fragment of K^T (rows = features 16 ft + lr) over token block kc, permuted token order
+    auto frag_kt = [&](int ft, int kc) {
+      return frag_trans<LDD>(Kp, 32 * kc + 4 * lg, 32 * kc + 16 + 4 * lg,
+                             32 * (ft >> 1) + 8 * (lr & 3) + 4 * (ft & 1), lr);
+    };
+    const bool live = ninv_t > 0.0f;  // ||H_t|| = 0: x_t = 0
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft) {
+      Ra[ft] = live ? Ra[ft] : f32x4{0.f, 0.f, 0.f, 0.f};
+      Rb[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+      X[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+    // One iteration it on the current residual Rc = R_it:
+    //   Ro <- kp Ro + kr Rc + H0hat (ky s_t Rc) + K^T ((K Rc) o ky Mhat)
+    // (Ro held R_{it-1} and now holds R_{it+1}), and X += beta_it R_it.
+    // The products form a pipeline of instruction groups (sched_barrier boundaries): K fragments
+    // are read two feature blocks ahead of their products, K^T fragments during the last
+    // blocks, and the vector work (operand packing, the recurrence, the X update) sits between
+    // independent matrix-core instructions. With one wave per SIMD nothing else hides latency.
+    auto step = [&](f32x4(&Ro)[FT], f32x4(&Rc)[FT], int it) {
+      // K and K^T fragments are read from LDS in every iteration: without this the compiler
+      // hoists them out of the loop as invariant loads and runs out of registers
+      asm volatile("" ::: "memory");
+      const f32x4 cf = *reinterpret_cast<const f32x4*>(v_coef + 4 * it);  // kp, kr, ky, beta
+      Frag rf[KD], rs[KD], kq[KD][ST], kt[KC][FT], pf[KC];
+      f32x4 pa[ST];
+#pragma unroll
+      for (int kk = 0; kk < KD; ++kk) rf[kk] = pack8(Rc[2 * kk], Rc[2 * kk + 1]);
+#pragma unroll
+      for (int kk = 0; kk < (KD < 2 ? KD : 2); ++kk)
+#pragma unroll
+        for (int sb = 0; sb < ST; ++sb) kq[kk][sb] = frag_k(sb, kk);
+      __builtin_amdgcn_sched_barrier(0);
+      const float kys = cf[2] * s_t;
+#pragma unroll
+      for (int sb = 0; sb < ST; ++sb) pa[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk <= KD; ++kk) {
+        if (kk < KD) {
+#pragma unroll
+          for (int sb = 0; sb < ST; ++sb) pa[sb] = M::mma(kq[kk][sb], rf[kk], pa[sb]);
+          if (kk + 2 < KD) {
+#pragma unroll
+            for (int sb = 0; sb < ST; ++sb) kq[kk + 2][sb] = frag_k(sb, kk + 2);
+          }
+          if (kk + 1 == KD) {
+#pragma unroll
+            for (int ft = 0; ft < FT; ++ft) kt[0][ft] = frag_kt(ft, 0);
+          }
+          rs[kk] = pack8(Rc[2 * kk] * kys, Rc[2 * kk + 1] * kys);
+          if (kk == 0) {
+#pragma unroll
+            for (int ft = 0; ft < FT; ++ft) Ro[ft] = cf[0] * Ro[ft] + cf[1] * Rc[ft];
+          }
+#pragma unroll
+          for (int ft = kk * FT / KD; ft < (kk + 1) * FT / KD; ++ft) X[ft] += cf[3] * Rc[ft];
+        } else {
+#pragma unroll
+          for (int ft = 0; ft < FT; ++ft) kt[1][ft] = frag_kt(ft, 1);
+#pragma unroll
+          for (int kc = 0; kc < KC; ++kc)
+            pf[kc] = pack8(pa[2 * kc] * Mh[2 * kc] * cf[2], pa[2 * kc + 1] * Mh[2 * kc + 1] * cf[2]);
+        }
+        if (kk >= 1) {
+#pragma unroll
+          for (int ft = 0; ft < FT; ++ft) Ro[ft] = M::mma(Hres[ft][kk - 1], rs[kk - 1], Ro[ft]);
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft) Ro[ft] = M::mma(kt[kc][ft], pf[kc], Ro[ft]);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    {
+      int it = 0;
+      for (; it + 2 < cc.iters; it += 2) {
+        step(Rb, Ra, it);
+        step(Ra, Rb, it + 1);
+      }
+      const float bl = v_coef[4 * (cc.iters - 1) + 3];  // X += beta_{r-1} R_{r-1}
+      if (it + 1 < cc.iters) {
+        step(Rb, Ra, it);
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft) X[ft] += bl * Rb[ft];
+      } else {
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft) X[ft] += bl * Ra[ft];
+      }
+    }
+
+    // ---- output O^T = diag(s) U0hat X^T + V^T ((K X^T) o Mhat), X split into hi + lo -------
+    lds_barrier();  // U0hat is staged
+    refresh();
+#pragma unroll
+    for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+      for (int kk = 0; kk < KD; ++kk)
+        Hres[ft][kk] = *reinterpret_cast<const Frag*>(Hs + (16 * ft + lr) * LDD + 32 * kk + 8 * lg);
+    {
+      Frag xh[KD], xl[KD];
+#pragma unroll
+      for (int kk = 0; kk < KD; ++kk) {
+        xh[kk] = pack8(X[2 * kk], X[2 * kk + 1]);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float x = j < 4 ? X[2 * kk][j] : X[2 * kk + 1][j - 4];
+          xl[kk][j] = (f16)(x - (float)xh[kk][j]);
+        }
+      }
+      f32x4 pa[ST];
+#pragma unroll
+      for (int sb = 0; sb < ST; ++sb) {
+        pa[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk) {
+          const Frag kf = frag_k(sb, kk);
+          pa[sb] = M::mma(kf, xh[kk], pa[sb]);
+          pa[sb] = M::mma(kf, xl[kk], pa[sb]);
+        }
+      }
+      Frag pf[KC];
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) pf[kc] = pack8(pa[2 * kc] * Mh[2 * kc], pa[2 * kc + 1] * Mh[2 * kc + 1]);
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft) {
+        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk) {
+          y = M::mma(Hres[ft][kk], xh[kk], y);
+          y = M::mma(Hres[ft][kk], xl[kk], y);
+        }
+        y = y * s_t;
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc)
+          y = M::mma(frag_trans<LDD>(Vp, 32 * kc + 4 * lg, 32 * kc + 16 + 4 * lg, 16 * ft + 4 * (lr & 3), lr),
+                     pf[kc], y);
+        bf16x4 ov = {(bf16)y[0], (bf16)y[1], (bf16)y[2], (bf16)y[3]};
+        *reinterpret_cast<bf16x4*>(Ob + t * LDD + 16 * ft + 4 * lg) = ov;
+      }
+    }
+    pend_t0 = t0;
+    pend_nv = nv;
+    n0sq = n2last;
+  }
+
+  lds_barrier();  // the last chunk's output tile is staged
+  flush_o();
+  if (A.out_h) {
+    float* oh = A.out_h + (size_t)bh * D * D;
+    float* ou = A.out_u + (size_t)bh * D * D;
+#pragma unroll
+    for (int jr = 0; jr < NRT; ++jr)
+#pragma unroll
+      for (int jc = 0; jc < NCT; ++jc) {
+        const size_t o = (size_t)(16 * (b0 + jc) + lr) * D + 16 * (a0 + jr) + 4 * lg;
+        *reinterpret_cast<f32x4*>(oh + o) = Hst[jr][jc];
+        *reinterpret_cast<f32x4*>(ou + o) = Ust[jr][jc];
+      }
+  }
+  if (A.n2_out && seg == S - 1 && tid == 0) A.n2_out[bh] = n0sq;
+}
+
+template <int D>
+hipError_t launch_tok(const FwdPlan& pl, const WalkArgs& a, const ChebConsts& cc,
+                      hipStream_t stream) {
+  using Cfg = TokCfg<D>;
+  auto kern = walk_tok_kernel<D>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::bytes);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(pl.S, pl.B * pl.H), dim3(Cfg::NT), Cfg::bytes, stream, a, pl.B,
+                     pl.T, pl.H, pl.N, pl.S, pl.J, cc);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+bool walk_tok_supported(const FwdPlan& pl) {
+  return pl.dtype == 0 && pl.C == 64 && (pl.D == 32 || pl.D == 64 || pl.D == 128);
+}
+
+hipError_t launch_walk_tok(const FwdPlan& pl, const WalkArgs& a, const ChebConsts& cc,
+                           hipStream_t stream) {
+  switch (pl.D) {
+    case 32: return launch_tok<32>(pl, a, cc, stream);
+    case 64: return launch_tok<64>(pl, a, cc, stream);
+    case 128: return launch_tok<128>(pl, a, cc, stream);
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gka

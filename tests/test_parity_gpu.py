@@ -92,7 +92,7 @@ def test_fp32_chunk_and_head_sizes(D, C):
     check_prefill(got, ref, "fp32", f"fp32 D={D} C={C}")
 
 
-@pytest.mark.parametrize("D,C", [(32, 32), (64, 32), (64, 64), (128, 32), (128, 64)])
+@pytest.mark.parametrize("D,C", [(32, 32), (32, 64), (64, 32), (64, 64), (128, 32), (128, 64)])
 def test_bf16_chunk_and_head_sizes(D, C):
     T = 448
     q, k, v, g = inputs(2, T, 3, D, "bf16", seed=30 + D + C)
@@ -137,6 +137,51 @@ def test_empty_sequence_leaves_state():
 
 
 # ------------------------------------------------------------------------------------------
+# bf16 with chunks of 64 (the token-owning walk): ragged lengths, iteration counts, states
+# ------------------------------------------------------------------------------------------
+
+@pytest.mark.parametrize("D", [32, 64, 128])
+@pytest.mark.parametrize("T", [1, 5, 63, 65, 130])
+def test_bf16_chunk64_ragged(D, T):
+    q, k, v, g = inputs(2, T, 2, D, "bf16", seed=300 + T + D)
+    ref = gka_forward_ref(q, k, v, g, 0.05, 10)
+    log(f"bf16 C=64 ragged D={D} T={T}")
+    got = run_prefill(q, k, v, g, 0.05, 10, 64, "bf16", state=zero_state(2, 2, D))
+    check_prefill(got, ref, "bf16", f"bf16 C=64 D={D} T={T}")
+    assert rel_l2(got["h"], ref["h"]) < 1e-4
+    assert rel_l2(got["u"], ref["u"]) < 1e-4
+    assert max_rel(got["n2"], ref["n2"]) < 1e-4
+
+
+@pytest.mark.parametrize("iters", [1, 2, 3, 4, 11])
+def test_bf16_chunk64_iteration_counts(iters):
+    q, k, v, g = inputs(1, 200, 2, 64, "bf16", seed=320 + iters)
+    ref = gka_forward_ref(q, k, v, g, 0.1, iters)
+    log(f"bf16 C=64 iters={iters}")
+    got = run_prefill(q, k, v, g, 0.1, iters, 64, "bf16")
+    check_prefill(got, ref, "bf16", f"bf16 C=64 iters={iters}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_bf16_chunk64_nonzero_initial_state(D):
+    T = 300
+    rng = np.random.default_rng(330 + D)
+    Z = rng.standard_normal((1, 2, D, 2 * D))
+    h0 = (Z @ np.swapaxes(Z, -1, -2) / D).astype(np.float32).astype(np.float64)
+    u0 = rng.standard_normal((1, 2, D, D)).astype(np.float32).astype(np.float64)
+    n20 = np.sum(h0 * h0, axis=(-1, -2))
+    q, k, v, g = inputs(1, T, 2, D, "bf16", seed=331 + D)
+    ref = gka_forward_ref(q, k, v, g, 0.05, 10, h0=h0, u0=u0, n2_0=n20)
+    for seg in (1, 3):
+        log(f"bf16 C=64 nonzero initial state D={D} segments={seg}")
+        got = run_prefill(q, k, v, g, 0.05, 10, 64, "bf16", state=(h0, u0, n20), segments=seg)
+        check_prefill(got, ref, "bf16", f"bf16 initial state D={D} S={seg}")
+        assert rel_l2(got["h"], ref["h"]) < 1e-4
+        assert rel_l2(got["u"], ref["u"]) < 1e-4
+        assert max_rel(got["n2"], ref["n2"]) < 1e-4
+
+
+# ------------------------------------------------------------------------------------------
 # carried state: split calls, initial states, prefill -> decode hand-off
 # ------------------------------------------------------------------------------------------
 
@@ -175,15 +220,15 @@ def test_nonzero_initial_state_fp32():
         assert rel_l2(got["u"], ref["u"]) < 1e-6
 
 
-@pytest.mark.parametrize("dtype,D", [("fp32", 64), ("bf16", 128)])
-def test_prefill_then_step_equals_longer_prefill(dtype, D):
+@pytest.mark.parametrize("dtype,D,C", [("fp32", 64, 16), ("bf16", 128, 32), ("bf16", 128, 64)])
+def test_prefill_then_step_equals_longer_prefill(dtype, D, C):
     T = 160
     q, k, v, g = inputs(2, T + 3, 2, D, dtype, seed=80 + D)
     ref = gka_forward_ref(q, k, v, g, 0.05, 10)
     log(f"prefill -> step {dtype} D={D}")
     st = gka.GkaState.zeros(2, 2, D)
     gka.fwd_chunked(dev(q[:, :T], dtype), dev(k[:, :T], dtype), dev(v[:, :T], dtype),
-                    dev(g[:, :T]), 0.05, 10, 32 if dtype == "bf16" else 16, state=st)
+                    dev(g[:, :T]), 0.05, 10, C, state=st)
     outs = []
     for t in range(T, T + 3):
         outs.append(host(gka.step(dev(q[:, t], dtype), dev(k[:, t], dtype), dev(v[:, t], dtype),
@@ -198,7 +243,7 @@ def test_prefill_then_step_equals_longer_prefill(dtype, D):
 # degenerate cases
 # ------------------------------------------------------------------------------------------
 
-@pytest.mark.parametrize("dtype,D,C", [("fp32", 16, 16), ("bf16", 64, 32)])
+@pytest.mark.parametrize("dtype,D,C", [("fp32", 16, 16), ("bf16", 64, 32), ("bf16", 128, 64)])
 def test_gamma_zero_closed_form(dtype, D, C):
     """gamma = 0 and unit keys: o_t = (1 - (-1)^r / T_r(1+2a)) v_t (k_t . q_t) / (1 + a)."""
     a, r = 0.05, 7
@@ -217,13 +262,13 @@ def test_gamma_zero_closed_form(dtype, D, C):
     assert rel_l2(o, expect[:, 0]) <= TOL_O[dtype]
 
 
-@pytest.mark.parametrize("dtype,D", [("fp32", 32), ("bf16", 64)])
-def test_zero_keys_give_zero_output(dtype, D):
+@pytest.mark.parametrize("dtype,D,C", [("fp32", 32, 32), ("bf16", 64, 32), ("bf16", 64, 64)])
+def test_zero_keys_give_zero_output(dtype, D, C):
     q, k, v, g = inputs(1, 96, 2, D, dtype, seed=95)
     k[:, :40] = 0.0  # ||H_t|| = 0 for the first 40 tokens
     ref = gka_forward_ref(q, k, v, g, 0.1, 8)
     log(f"zero keys {dtype}")
-    got = run_prefill(q, k, v, g, 0.1, 8, 32, dtype)
+    got = run_prefill(q, k, v, g, 0.1, 8, C, dtype)
     assert np.all(np.isfinite(got["o"]))
     assert np.all(got["o"][:, :40] == 0.0)
     assert np.all(got["hnorm"][:, :40] == 0.0)
