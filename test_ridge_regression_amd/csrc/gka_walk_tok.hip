@@ -56,7 +56,9 @@ struct TokCfg {
   static constexpr size_t oVp = oKp + szTok;     // V, token-major (fp16)
   static constexpr size_t oHs = oVp + szTok;     // H0hat, then U0hat: row-major, permuted columns
   static constexpr size_t oOb = oHs + szHs;      // output tile, token-major (bf16)
-  static constexpr size_t oVec = oOb + szTok;
+  static constexpr int LDC = C + 8;              // row stride of the [D][C] fp16 tile
+  static constexpr size_t oKT = oOb + szTok;     // K^T: row-major, tokens permuted (fp16)
+  static constexpr size_t oVec = oKT + (size_t)D * LDC * 2;
   static constexpr size_t szVec = (size_t)(4 * C + 16 + 4 * 64) * sizeof(float);
   static constexpr size_t bytes = oVec + szVec;  // dynamic LDS
   static constexpr size_t szPre = 2 * (size_t)NU * 16 + C * sizeof(float);  // static LDS
@@ -113,6 +115,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
   typedef f16x8 Frag;
   constexpr int C = Cfg::C, NW = Cfg::NW, NT = Cfg::NT, FT = Cfg::FT, KD = Cfg::KD;
   constexpr int KC = Cfg::KC, ST = Cfg::ST, LDD = Cfg::LDD, UPR = Cfg::UPR, NU = Cfg::NU;
+  constexpr int LDC = Cfg::LDC;
   constexpr int NST = Cfg::NST, NRT = Cfg::NRT, NCT = Cfg::NCT;
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -120,6 +123,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
   f16* Vp = reinterpret_cast<f16*>(smem + Cfg::oVp);
   f16* Hs = reinterpret_cast<f16*>(smem + Cfg::oHs);
   bf16* Ob = reinterpret_cast<bf16*>(smem + Cfg::oOb);
+  f16* KT = reinterpret_cast<f16*>(smem + Cfg::oKT);
   float* v_cl = reinterpret_cast<float*>(smem + Cfg::oVec);  // [C] in-chunk log2 gate prefix
   float* v_w = v_cl + C;    // [C] carry weights 2^(cl_C - cl_s)
   float* v_a = v_w + C;     // [C] n^2 scan: a_t = gamma_t^2
@@ -136,14 +140,16 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
   const int seg = blockIdx.x;
   const int bh = blockIdx.y;
   const int b = bh / Hn, h = bh % Hn;
-  const int wave = threadIdx.x / kWave;
+  int wave = threadIdx.x / kWave;
   // Per-lane indices, passed through refresh() at the start of every phase so that the
   // addresses derived from them are recomputed where they are used instead of being hoisted
   // out of the chunk loop and kept live for the whole walk (which would spill them)
   int tid = threadIdx.x, lane = tid % kWave;
   int lr = lane % 16, lg = lane / 16;
   int t = 16 * wave + lr;  // own token (column of the wave's accumulator tiles)
-  auto refresh = [&]() { asm volatile("" : "+v"(tid), "+v"(lane), "+v"(lr), "+v"(lg), "+v"(t)); };
+  auto refresh = [&]() {
+    asm volatile("" : "+v"(tid), "+v"(lane), "+v"(lr), "+v"(lg), "+v"(t), "+v"(wave));
+  };
   const int c_begin = seg * J;
   const int c_end = min(N, c_begin + J);
   const long long tok_stride = (long long)Hn * D;
@@ -261,6 +267,10 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
   auto frag_k = [&](int sb, int kk) {
     return *reinterpret_cast<const Frag*>(Kp + (16 * sb + lr) * LDD + 32 * kk + 8 * lg);
   };
+  // A fragment of K^T (rows = features 16 ft + lr) over token block kc, permuted token order
+  auto frag_kt = [&](int ft, int kc) {
+    return *reinterpret_cast<const Frag*>(KT + (16 * ft + lr) * LDC + 32 * kc + 8 * lg);
+  };
 
   prefetch(c_begin);
 
@@ -342,6 +352,20 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
         for (int kk = 0; kk < KD; ++kk) keep_in_agpr(Hres[ft][kk]);
     }
 
+    // ---- K^T with the tokens in the permuted order (fragments from transposing reads of K,
+    // written back as rows): every later K^T operand is then one 16-byte read ---------------
+    refresh();
+#pragma unroll
+    for (int k = 0; k < (FT * KC + NW - 1) / NW; ++k) {
+      const int phi = wave + k * NW;
+      if (FT * KC % NW == 0 || phi < FT * KC) {
+        const int ft = phi / KC, kc = phi % KC;
+        const Frag f = frag_trans<LDD>(Kp, 32 * kc + 4 * lg, 32 * kc + 16 + 4 * lg,
+                                       pcol(16 * ft + 4 * (lr & 3)), lr);
+        *reinterpret_cast<Frag*>(KT + (16 * ft + lr) * LDC + 32 * kc + 8 * lg) = f;
+      }
+    }
+
     // ---- norm phase: k_t^T H0hat k_t and sum_{s<t} 2^(cl_{t-1} - cl_s) G_st^2 ---------------
     {
       Frag kb[KD];  // B fragments of the own token's key
@@ -415,17 +439,16 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
 
     // ---- state carry: H <- Gam_C H + K^T diag(w) K, U^T <- Gam_C U^T + K^T diag(w) V --------
     {
-      // A operands (w K)^T of the own row tiles, tokens in natural order, split hi + lo
+      // A operands (w K)^T of the own row tiles, split hi + lo; tokens in the permuted order
+      // of the K^T tile (k-slot j of lane group lg: token 32 kc + 16 (j / 4) + 4 lg + j % 4)
       Frag awh[NRT][KC], awl[NRT][KC];
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
-        const int s0 = 32 * kc + 8 * lg;
-        const f32x4 w0 = *reinterpret_cast<const f32x4*>(v_w + s0);
-        const f32x4 w1 = *reinterpret_cast<const f32x4*>(v_w + s0 + 4);
+        const f32x4 w0 = *reinterpret_cast<const f32x4*>(v_w + 32 * kc + 4 * lg);
+        const f32x4 w1 = *reinterpret_cast<const f32x4*>(v_w + 32 * kc + 16 + 4 * lg);
 #pragma unroll
         for (int jr = 0; jr < NRT; ++jr) {
-          const int a = a0 + jr;
-          const Frag kf = frag_trans<LDD>(Kp, s0, s0 + 4, 32 * (a >> 1) + 8 * (lr & 3) + 4 * (a & 1), lr);
+          const Frag kf = frag_kt(a0 + jr, kc);
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const float x = (float)kf[j] * (j < 4 ? w0[j] : w1[j - 4]);
@@ -440,9 +463,8 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
         Frag bk[KC], bv[KC];
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
-          const int s0 = 32 * kc + 8 * lg;
-          bk[kc] = frag_trans<LDD>(Kp, s0, s0 + 4, 32 * (bc >> 1) + 8 * (lr & 3) + 4 * (bc & 1), lr);
-          bv[kc] = frag_trans<LDD>(Vp, s0, s0 + 4, 16 * bc + 4 * (lr & 3), lr);
+          bk[kc] = frag_kt(bc, kc);  // K[s][16 bc + lr] over the same token slots
+          bv[kc] = frag_trans<LDD>(Vp, 32 * kc + 4 * lg, 32 * kc + 16 + 4 * lg, 16 * bc + 4 * (lr & 3), lr);
         }
 #pragma unroll
         for (int jr = 0; jr < NRT; ++jr) {
@@ -466,11 +488,6 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
 
     // ---- Chebyshev loop on the residuals of the own token ----------------------------------
     refresh();
-    // A fragment of K^T (rows = features 16 ft + lr) over token block kc, permuted token order
-    auto frag_kt = [&](int ft, int kc) {
-      return frag_trans<LDD>(Kp, 32 * kc + 4 * lg, 32 * kc + 16 + 4 * lg,
-                             32 * (ft >> 1) + 8 * (lr & 3) + 4 * (ft & 1), lr);
-    };
     const bool live = ninv_t > 0.0f;  // ||H_t|| = 0: x_t = 0
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) {
@@ -480,69 +497,82 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
     }
     // One iteration it on the current residual Rc = R_it:
     //   Ro <- kp Ro + kr Rc + H0hat (ky s_t Rc) + K^T ((K Rc) o ky Mhat)
-    // (Ro held R_{it-1} and now holds R_{it+1}), and X += beta_it R_it.
-    // The products form a pipeline of instruction groups (sched_barrier boundaries): K fragments
-    // are read two feature blocks ahead of their products, K^T fragments during the last
-    // blocks, and the vector work (operand packing, the recurrence, the X update) sits between
-    // independent matrix-core instructions. With one wave per SIMD nothing else hides latency.
+    // (Ro held R_{it-1} and now holds R_{it+1}), and X += beta_it R_it. The kp Ro term is
+    // applied one step early: once Rc has served this step, it is scaled by the next step's kp.
+    // The work forms three instruction groups (sched_barrier boundaries), each pairing
+    // matrix-core products with independent vector work and with the LDS reads of a later
+    // group: (A) the K products P = K Rc^T and the recurrence start; (B) the H0hat products on
+    // the scaled operands and the P' operands; (C) the K^T products, the X update, the
+    // pre-scaling and the next step's first K fragments. With one wave per SIMD nothing else
+    // hides latency.
+    constexpr int KN = KD < 2 ? KD : 2;  // K fragment blocks read ahead of a step
+    Frag kn[KN][ST];
+    auto load_kn = [&]() {
+#pragma unroll
+      for (int kk = 0; kk < KN; ++kk)
+#pragma unroll
+        for (int sb = 0; sb < ST; ++sb) kn[kk][sb] = frag_k(sb, kk);
+    };
     auto step = [&](f32x4(&Ro)[FT], f32x4(&Rc)[FT], int it) {
       // K and K^T fragments are read from LDS in every iteration: without this the compiler
       // hoists them out of the loop as invariant loads and runs out of registers
       asm volatile("" ::: "memory");
       const f32x4 cf = *reinterpret_cast<const f32x4*>(v_coef + 4 * it);  // kp, kr, ky, beta
+      const float kp_next = v_coef[4 * (it + 1)];
       Frag rf[KD], rs[KD], kq[KD][ST], kt[KC][FT], pf[KC];
       f32x4 pa[ST];
+      // (A)
+#pragma unroll
+      for (int kk = KN; kk < KD; ++kk)
+#pragma unroll
+        for (int sb = 0; sb < ST; ++sb) kq[kk][sb] = frag_k(sb, kk);
+#pragma unroll
+      for (int kk = 0; kk < KN; ++kk)
+#pragma unroll
+        for (int sb = 0; sb < ST; ++sb) kq[kk][sb] = kn[kk][sb];
 #pragma unroll
       for (int kk = 0; kk < KD; ++kk) rf[kk] = pack8(Rc[2 * kk], Rc[2 * kk + 1]);
 #pragma unroll
-      for (int kk = 0; kk < (KD < 2 ? KD : 2); ++kk)
-#pragma unroll
-        for (int sb = 0; sb < ST; ++sb) kq[kk][sb] = frag_k(sb, kk);
-      __builtin_amdgcn_sched_barrier(0);
-      const float kys = cf[2] * s_t;
-#pragma unroll
       for (int sb = 0; sb < ST; ++sb) pa[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk <= KD; ++kk) {
-        if (kk < KD) {
+      for (int kk = 0; kk < KD; ++kk)
 #pragma unroll
-          for (int sb = 0; sb < ST; ++sb) pa[sb] = M::mma(kq[kk][sb], rf[kk], pa[sb]);
-          if (kk + 2 < KD) {
+        for (int sb = 0; sb < ST; ++sb) pa[sb] = M::mma(kq[kk][sb], rf[kk], pa[sb]);
+      const float kys = cf[2] * s_t;
+      rs[0] = pack8(Rc[0] * kys, Rc[1] * kys);
 #pragma unroll
-            for (int sb = 0; sb < ST; ++sb) kq[kk + 2][sb] = frag_k(sb, kk + 2);
-          }
-          if (kk + 1 == KD) {
+      for (int ft = 0; ft < FT; ++ft) Ro[ft] = Ro[ft] + cf[1] * Rc[ft];
+      __builtin_amdgcn_sched_barrier(0);
+      // (B)
 #pragma unroll
-            for (int ft = 0; ft < FT; ++ft) kt[0][ft] = frag_kt(ft, 0);
-          }
-          rs[kk] = pack8(Rc[2 * kk] * kys, Rc[2 * kk + 1] * kys);
-          if (kk == 0) {
+      for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
-            for (int ft = 0; ft < FT; ++ft) Ro[ft] = cf[0] * Ro[ft] + cf[1] * Rc[ft];
-          }
+        for (int ft = 0; ft < FT; ++ft) kt[kc][ft] = frag_kt(ft, kc);
 #pragma unroll
-          for (int ft = kk * FT / KD; ft < (kk + 1) * FT / KD; ++ft) X[ft] += cf[3] * Rc[ft];
-        } else {
+      for (int kk = 1; kk < KD; ++kk) rs[kk] = pack8(Rc[2 * kk] * kys, Rc[2 * kk + 1] * kys);
 #pragma unroll
-          for (int ft = 0; ft < FT; ++ft) kt[1][ft] = frag_kt(ft, 1);
+      for (int kk = 0; kk < KD; ++kk)
 #pragma unroll
-          for (int kc = 0; kc < KC; ++kc)
-            pf[kc] = pack8(pa[2 * kc] * Mh[2 * kc] * cf[2], pa[2 * kc + 1] * Mh[2 * kc + 1] * cf[2]);
-        }
-        if (kk >= 1) {
+        for (int ft = 0; ft < FT; ++ft) Ro[ft] = M::mma(Hres[ft][kk], rs[kk], Ro[ft]);
 #pragma unroll
-          for (int ft = 0; ft < FT; ++ft) Ro[ft] = M::mma(Hres[ft][kk - 1], rs[kk - 1], Ro[ft]);
-        }
-        __builtin_amdgcn_sched_barrier(0);
-      }
+      for (int kc = 0; kc < KC; ++kc)
+        pf[kc] = pack8(pa[2 * kc] * Mh[2 * kc] * cf[2], pa[2 * kc + 1] * Mh[2 * kc + 1] * cf[2]);
+      __builtin_amdgcn_sched_barrier(0);
+      // (C)
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
+      for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
         for (int ft = 0; ft < FT; ++ft) Ro[ft] = M::mma(kt[kc][ft], pf[kc], Ro[ft]);
-        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft) {
+        X[ft] += cf[3] * Rc[ft];
+        Rc[ft] = Rc[ft] * kp_next;
       }
+      load_kn();
+      __builtin_amdgcn_sched_barrier(0);
     };
     {
+      load_kn();
       int it = 0;
       for (; it + 2 < cc.iters; it += 2) {
         step(Rb, Ra, it);
