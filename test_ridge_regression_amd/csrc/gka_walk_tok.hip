@@ -58,7 +58,8 @@ struct TokCfg {
   static constexpr size_t oOb = oHs + szHs;      // output tile, token-major (bf16)
   static constexpr int LDC = C + 8;              // row stride of the [D][C] fp16 tile
   static constexpr size_t oKT = oOb + szTok;     // K^T: row-major, tokens permuted (fp16)
-  static constexpr size_t oVec = oKT + (size_t)D * LDC * 2;
+  static constexpr size_t oVT = oKT + (size_t)D * LDC * 2;  // V^T, likewise
+  static constexpr size_t oVec = oVT + (size_t)D * LDC * 2;
   static constexpr size_t szVec = (size_t)(4 * C + 16 + 4 * 64) * sizeof(float);
   static constexpr size_t bytes = oVec + szVec;  // dynamic LDS
   static constexpr size_t szPre = 2 * (size_t)NU * 16 + C * sizeof(float);  // static LDS
@@ -124,6 +125,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
   f16* Hs = reinterpret_cast<f16*>(smem + Cfg::oHs);
   bf16* Ob = reinterpret_cast<bf16*>(smem + Cfg::oOb);
   f16* KT = reinterpret_cast<f16*>(smem + Cfg::oKT);
+  f16* VT = reinterpret_cast<f16*>(smem + Cfg::oVT);
   float* v_cl = reinterpret_cast<float*>(smem + Cfg::oVec);  // [C] in-chunk log2 gate prefix
   float* v_w = v_cl + C;    // [C] carry weights 2^(cl_C - cl_s)
   float* v_a = v_w + C;     // [C] n^2 scan: a_t = gamma_t^2
@@ -240,14 +242,19 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
   int pend_t0 = 0, pend_nv = 0;
   auto flush_o = [&]() {
     if (pend_nv > 0) {
+      bf16x8 ov[NU / NT];
+#pragma unroll
+      for (int k = 0; k < NU / NT; ++k) {
+        const int u = tid + k * NT;
+        ov[k] = *reinterpret_cast<const bf16x8*>(Ob + (u / UPR) * LDD + (u % UPR) * Cfg::VEC);
+      }
 #pragma unroll
       for (int k = 0; k < NU / NT; ++k) {
         const int u = tid + k * NT;
         const int tt = u / UPR, cu = u % UPR;
         if (tt < pend_nv)
           *reinterpret_cast<bf16x8*>(og + (b * (long long)Tlen + pend_t0 + tt) * tok_stride +
-                                     (long long)h * D + cu * Cfg::VEC) =
-              *reinterpret_cast<const bf16x8*>(Ob + tt * LDD + cu * Cfg::VEC);
+                                     (long long)h * D + cu * Cfg::VEC) = ov[k];
       }
       pend_nv = 0;
     }
@@ -267,9 +274,13 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
   auto frag_k = [&](int sb, int kk) {
     return *reinterpret_cast<const Frag*>(Kp + (16 * sb + lr) * LDD + 32 * kk + 8 * lg);
   };
-  // A fragment of K^T (rows = features 16 ft + lr) over token block kc, permuted token order
+  // A fragment of K^T (V^T) (rows = features 16 ft + lr) over token block kc, permuted token
+  // order (k-slot j of lane group lg: token 32 kc + 16 (j / 4) + 4 lg + j % 4)
   auto frag_kt = [&](int ft, int kc) {
     return *reinterpret_cast<const Frag*>(KT + (16 * ft + lr) * LDC + 32 * kc + 8 * lg);
+  };
+  auto frag_vt = [&](int ft, int kc) {
+    return *reinterpret_cast<const Frag*>(VT + (16 * ft + lr) * LDC + 32 * kc + 8 * lg);
   };
 
   prefetch(c_begin);
@@ -309,11 +320,18 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
       v_w[lane] = fast_exp2(fminf(clast - cl, 0.0f));
     }
     // ---- stage K (fp16, permuted features) and V (fp16) ------------------------------------
+    {
+      bf16x8 kin[NU / NT], vin[NU / NT];  // all reads first: one wait covers them
+#pragma unroll
+      for (int k = 0; k < NU / NT; ++k) {
+        kin[k] = PreK[tid + k * NT];
+        vin[k] = PreV[tid + k * NT];
+      }
 #pragma unroll
     for (int k = 0; k < NU / NT; ++k) {
       const int u = tid + k * NT;
       const int tt = u / UPR, cu = u % UPR;
-      bf16x8 kv = PreK[u], vv = PreV[u];
+      const bf16x8 kv = kin[k], vv = vin[k];
       f16x8 ko, vo;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -324,17 +342,14 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
       *reinterpret_cast<f16x4*>(Kp + tt * LDD + pcol(8 * cu)) = f16x4{ko[0], ko[1], ko[2], ko[3]};
       *reinterpret_cast<f16x4*>(Kp + tt * LDD + pcol(8 * cu + 4)) = f16x4{ko[4], ko[5], ko[6], ko[7]};
     }
+    }
     stage_state(Hst, n0inv);  // H0hat
     lds_barrier();
 
     // the queries are consumed before the next chunk's loads are issued: loads retire in order,
     // so a wait for the queries issued after the prefetch would also wait for the prefetch
-    f32x4 Ra[FT], Rb[FT], X[FT];
 #pragma unroll
-    for (int ft = 0; ft < FT; ++ft) {
-      Ra[ft] = f32x4{(float)Qraw[ft][0], (float)Qraw[ft][1], (float)Qraw[ft][2], (float)Qraw[ft][3]};
-      asm volatile("" : "+v"(Ra[ft]));
-    }
+    for (int ft = 0; ft < FT; ++ft) asm volatile("" : "+v"(Qraw[ft]));
     prefetch(ch + 1);
     refresh();
 
@@ -352,8 +367,8 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
         for (int kk = 0; kk < KD; ++kk) keep_in_agpr(Hres[ft][kk]);
     }
 
-    // ---- K^T with the tokens in the permuted order (fragments from transposing reads of K,
-    // written back as rows): every later K^T operand is then one 16-byte read ---------------
+    // ---- K^T and V^T with the tokens in the permuted order (fragments from transposing reads
+    // of K and V, written back as rows): every later operand of them is one 16-byte read -----
     refresh();
 #pragma unroll
     for (int k = 0; k < (FT * KC + NW - 1) / NW; ++k) {
@@ -362,7 +377,10 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
         const int ft = phi / KC, kc = phi % KC;
         const Frag f = frag_trans<LDD>(Kp, 32 * kc + 4 * lg, 32 * kc + 16 + 4 * lg,
                                        pcol(16 * ft + 4 * (lr & 3)), lr);
+        const Frag g = frag_trans<LDD>(Vp, 32 * kc + 4 * lg, 32 * kc + 16 + 4 * lg,
+                                       16 * ft + 4 * (lr & 3), lr);
         *reinterpret_cast<Frag*>(KT + (16 * ft + lr) * LDC + 32 * kc + 8 * lg) = f;
+        *reinterpret_cast<Frag*>(VT + (16 * ft + lr) * LDC + 32 * kc + 8 * lg) = g;
       }
     }
 
@@ -457,41 +475,56 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
           }
         }
       }
+      // column operands in groups of two column tiles, double-buffered: the next group's
+      // reads are in flight during the current group's products
+      constexpr int CG = NCT >= 2 ? 2 : 1, NG = NCT / CG;
+      Frag bk[2][CG][KC], bv[2][CG][KC];
+      auto load_group = [&](int g, int buf) {
 #pragma unroll
-      for (int jc = 0; jc < NCT; ++jc) {
-        const int bc = b0 + jc;
-        Frag bk[KC], bv[KC];
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc) {
-          bk[kc] = frag_kt(bc, kc);  // K[s][16 bc + lr] over the same token slots
-          bv[kc] = frag_trans<LDD>(Vp, 32 * kc + 4 * lg, 32 * kc + 16 + 4 * lg, 16 * bc + 4 * (lr & 3), lr);
-        }
-#pragma unroll
-        for (int jr = 0; jr < NRT; ++jr) {
-          f32x4 hacc = Hst[jr][jc] * gC, uacc = Ust[jr][jc] * gC;
+        for (int j = 0; j < CG; ++j)
 #pragma unroll
           for (int kc = 0; kc < KC; ++kc) {
-            hacc = M::mma(awh[jr][kc], bk[kc], hacc);
-            hacc = M::mma(awl[jr][kc], bk[kc], hacc);
-            uacc = M::mma(awh[jr][kc], bv[kc], uacc);
-            uacc = M::mma(awl[jr][kc], bv[kc], uacc);
+            bk[buf][j][kc] = frag_kt(b0 + g * CG + j, kc);  // K[s][16 bc + lr], same token slots
+            bv[buf][j][kc] = frag_vt(b0 + g * CG + j, kc);
           }
-          Hst[jr][jc] = hacc;
-          Ust[jr][jc] = uacc;
-          if constexpr (Cfg::PIN) {
-            keep_in_agpr(Hst[jr][jc]);
-            keep_in_agpr(Ust[jr][jc]);
+      };
+      load_group(0, 0);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int g = 0; g < NG; ++g) {
+        if (g + 1 < NG) load_group(g + 1, (g + 1) % 2);
+#pragma unroll
+        for (int j = 0; j < CG; ++j)
+#pragma unroll
+          for (int jr = 0; jr < NRT; ++jr) {
+            const int jc = g * CG + j;
+            f32x4 hacc = Hst[jr][jc] * gC, uacc = Ust[jr][jc] * gC;
+#pragma unroll
+            for (int kc = 0; kc < KC; ++kc) {
+              hacc = M::mma(awh[jr][kc], bk[g % 2][j][kc], hacc);
+              hacc = M::mma(awl[jr][kc], bk[g % 2][j][kc], hacc);
+              uacc = M::mma(awh[jr][kc], bv[g % 2][j][kc], uacc);
+              uacc = M::mma(awl[jr][kc], bv[g % 2][j][kc], uacc);
+            }
+            Hst[jr][jc] = hacc;
+            Ust[jr][jc] = uacc;
+            if constexpr (Cfg::PIN) {
+              keep_in_agpr(Hst[jr][jc]);
+              keep_in_agpr(Ust[jr][jc]);
+            }
           }
-        }
+        __builtin_amdgcn_sched_barrier(0);
       }
     }
 
     // ---- Chebyshev loop on the residuals of the own token ----------------------------------
     refresh();
     const bool live = ninv_t > 0.0f;  // ||H_t|| = 0: x_t = 0
+    f32x4 Ra[FT], Rb[FT], X[FT];
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) {
-      Ra[ft] = live ? Ra[ft] : f32x4{0.f, 0.f, 0.f, 0.f};
+      Ra[ft] = live ? f32x4{(float)Qraw[ft][0], (float)Qraw[ft][1], (float)Qraw[ft][2], (float)Qraw[ft][3]}
+                    : f32x4{0.f, 0.f, 0.f, 0.f};
       Rb[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
       X[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
@@ -590,15 +623,23 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
     }
 
     // ---- output O^T = diag(s) U0hat X^T + V^T ((K X^T) o Mhat), X split into hi + lo -------
+    // Instruction groups: (1) U0hat and K fragment reads, the split of X; (2) the K products
+    // and the V^T fragment reads; (3) the U0hat products; (4) the V^T products and the stores.
     lds_barrier();  // U0hat is staged
     refresh();
+    {
 #pragma unroll
-    for (int ft = 0; ft < FT; ++ft)
+      for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk) {
+          Hres[ft][kk] = *reinterpret_cast<const Frag*>(Hs + (16 * ft + lr) * LDD + 32 * kk + 8 * lg);
+          if constexpr (Cfg::PIN) keep_in_agpr(Hres[ft][kk]);
+        }
+      Frag kq[KD][ST], vq[KC][FT], xh[KD], xl[KD], pf[KC];
 #pragma unroll
       for (int kk = 0; kk < KD; ++kk)
-        Hres[ft][kk] = *reinterpret_cast<const Frag*>(Hs + (16 * ft + lr) * LDD + 32 * kk + 8 * lg);
-    {
-      Frag xh[KD], xl[KD];
+#pragma unroll
+        for (int sb = 0; sb < ST; ++sb) kq[kk][sb] = frag_k(sb, kk);
 #pragma unroll
       for (int kk = 0; kk < KD; ++kk) {
         xh[kk] = pack8(X[2 * kk], X[2 * kk + 1]);
@@ -608,34 +649,44 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
           xl[kk][j] = (f16)(x - (float)xh[kk][j]);
         }
       }
+      __builtin_amdgcn_sched_barrier(0);
       f32x4 pa[ST];
 #pragma unroll
-      for (int sb = 0; sb < ST; ++sb) {
-        pa[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int sb = 0; sb < ST; ++sb) pa[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < KD; ++kk) {
-          const Frag kf = frag_k(sb, kk);
-          pa[sb] = M::mma(kf, xh[kk], pa[sb]);
-          pa[sb] = M::mma(kf, xl[kk], pa[sb]);
+      for (int kk = 0; kk < KD; ++kk)
+#pragma unroll
+        for (int sb = 0; sb < ST; ++sb) {
+          pa[sb] = M::mma(kq[kk][sb], xh[kk], pa[sb]);
+          pa[sb] = M::mma(kq[kk][sb], xl[kk], pa[sb]);
         }
-      }
-      Frag pf[KC];
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft) vq[kc][ft] = frag_vt(ft, kc);
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 y[FT];
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft) y[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KD; ++kk)
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft) {
+          y[ft] = M::mma(Hres[ft][kk], xh[kk], y[ft]);
+          y[ft] = M::mma(Hres[ft][kk], xl[kk], y[ft]);
+        }
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) pf[kc] = pack8(pa[2 * kc] * Mh[2 * kc], pa[2 * kc + 1] * Mh[2 * kc + 1]);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft) y[ft] = y[ft] * s_t;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft) y[ft] = M::mma(vq[kc][ft], pf[kc], y[ft]);
 #pragma unroll
       for (int ft = 0; ft < FT; ++ft) {
-        f32x4 y = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KD; ++kk) {
-          y = M::mma(Hres[ft][kk], xh[kk], y);
-          y = M::mma(Hres[ft][kk], xl[kk], y);
-        }
-        y = y * s_t;
-#pragma unroll
-        for (int kc = 0; kc < KC; ++kc)
-          y = M::mma(frag_trans<LDD>(Vp, 32 * kc + 4 * lg, 32 * kc + 16 + 4 * lg, 16 * ft + 4 * (lr & 3), lr),
-                     pf[kc], y);
-        bf16x4 ov = {(bf16)y[0], (bf16)y[1], (bf16)y[2], (bf16)y[3]};
+        bf16x4 ov = {(bf16)y[ft][0], (bf16)y[ft][1], (bf16)y[ft][2], (bf16)y[ft][3]};
         *reinterpret_cast<bf16x4*>(Ob + t * LDD + 16 * ft + 4 * lg) = ov;
       }
     }
