@@ -231,6 +231,8 @@ gka_status gka_fwd_chunked(const gka_params* p, const void* q, const void* k, co
   wa.in_bh = (long long)pl.S * 2 * DD;
   wa.in_seg = 2 * DD;
   wa.n2_in = ws_n2;
+  wa.out_h = h_state;
+  wa.out_u = u_state;
   wa.n2_out = hnorm2;
   if (gka::launch_walk(pl, false, wa, cc, s) != hipSuccess) return GKA_ERR_HIP;
   if (!mark(3)) return GKA_ERR_HIP;

@@ -216,6 +216,22 @@ __device__ inline void dma_load16(const void* src, uint32_t lds_base) {
       : "v"(src), "s"(lds_base)
       : "memory");
 }
+// The same with a wave-uniform 64-bit base in scalar registers and a 32-bit byte offset per
+// lane (no 64-bit address arithmetic per lane). The base is read from the first lane.
+__device__ inline void dma_load16_so(const void* base, uint32_t voff, uint32_t lds_base) {
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  // (readfirstlane returns a signed int: widen through uint32_t, never by sign extension)
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  const uint64_t sbase = lo | (hi << 32);
+  uint32_t m0_saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+      "global_load_lds_dwordx4 %1, %2\n\ts_mov_b32 m0, %0"
+      : "=&s"(m0_saved)
+      : "v"(voff), "s"(sbase), "s"(lds_base)
+      : "memory");
+}
 __device__ inline void dma_load4(const void* src, uint32_t lds_base) {
   uint32_t m0_saved;
   asm volatile(

@@ -714,7 +714,7 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
   lds_barrier();  // the last chunk's output tile is staged
   flush_o();
   // ---- results of the walk ------------------------------------------------------------------
-  if (A.out_h && state_active) {
+  if (A.out_h && state_active && seg == S - 1) {
     float* oh = A.out_h + (size_t)bh * D * D;
     float* ou = A.out_u + (size_t)bh * D * D;
 #pragma unroll
@@ -913,16 +913,18 @@ __global__ __launch_bounds__(256) void scan_kernel(float* __restrict__ st,
   for (int s = 0; s < S; ++s) {
     f32x4* ph = reinterpret_cast<f32x4*>(st + ((size_t)bh * S + s) * 2 * DD) + e4;
     f32x4* pu = reinterpret_cast<f32x4*>(st + ((size_t)bh * S + s) * 2 * DD + DD) + e4;
-    const f32x4 dh = *ph, du = *pu;
+    f32x4 dh = {0.f, 0.f, 0.f, 0.f}, du = {0.f, 0.f, 0.f, 0.f};
+    if (s + 1 < S) {  // the last segment has no summary
+      dh = *ph;
+      du = *pu;
+    }
     *ph = sh;
     *pu = su;
-    const float g = exp2f(log2g[(size_t)bh * S + s]);
-    sh = g * sh + dh;
-    su = g * su + du;
-  }
-  if (h) {
-    reinterpret_cast<f32x4*>(h + (size_t)bh * DD)[e4] = sh;
-    reinterpret_cast<f32x4*>(u + (size_t)bh * DD)[e4] = su;
+    if (s + 1 < S) {
+      const float g = exp2f(log2g[(size_t)bh * S + s]);
+      sh = g * sh + dh;
+      su = g * su + du;
+    }
   }
 }
 
@@ -933,12 +935,14 @@ static hipError_t launch_walk_t(const FwdPlan& pl, bool summary, const WalkArgs&
   using CfgS = WalkCfg<T, D, C, 16>;
   const dim3 grid(pl.S, pl.B * pl.H);
   if (summary) {
+    // segments 0 .. S-2: the last segment's walk produces the final state itself
+    const dim3 sgrid(pl.S - 1, pl.B * pl.H);
     const size_t bytes = 4 * CfgS::szRD;  // K, V, w K hi and lo (token-major)
     auto kern = summary_kernel<T, D, C>;
     hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(kern, grid, dim3(CfgS::NT), bytes, stream, a, pl.B, pl.T, pl.H, pl.N,
+    hipLaunchKernelGGL(kern, sgrid, dim3(CfgS::NT), bytes, stream, a, pl.B, pl.T, pl.H, pl.N,
                        pl.S, pl.J);
     return hipGetLastError();
   }
@@ -956,6 +960,7 @@ static hipError_t launch_walk_t(const FwdPlan& pl, bool summary, const WalkArgs&
 hipError_t launch_walk(const FwdPlan& pl, bool summary, const WalkArgs& a, const ChebConsts& cc,
                        hipStream_t stream) {
   if (!summary && walk_tok_supported(pl)) return launch_walk_tok(pl, a, cc, stream);
+  if (summary && summary_tok_supported(pl)) return launch_summary_tok(pl, a, stream);
   if (pl.dtype == 0) {
     if (pl.C == 64) {
       switch (pl.D) {

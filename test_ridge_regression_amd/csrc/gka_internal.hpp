@@ -37,7 +37,7 @@ struct WalkArgs {
   const float* in_u;      // segment-start U
   long long in_bh, in_seg;
   const float* n2_in;     // [BH] ||H||_F^2 at the start of segment 0 (NULL: from in_h / zero)
-  float* out_h;           // optional final state of a single-segment walk, [BH][D][D]
+  float* out_h;           // optional final state, [BH][D][D], written by the last segment
   float* out_u;
   float* n2_out;          // optional final ||H||_F^2, written by the last segment
   float* sum_h;           // summary mode: per-segment (dH, dU) from a zero start
@@ -55,8 +55,14 @@ bool walk_tok_supported(const FwdPlan& pl);
 hipError_t launch_walk_tok(const FwdPlan& pl, const WalkArgs& a, const ChebConsts& cc,
                            hipStream_t stream);
 
-// Affine scan over segments: start[s] = G_{s-1} start[s-1] + d_{s-1} (in place over d), final
-// state written to h/u when they are non-NULL; also copies hnorm2 to n2_seg0.
+// Segment summaries of the token-owning walk's configurations (bf16, chunks of 64, D = 64, 128),
+// for segments 0 .. S-2; same arguments and results as launch_walk with summary = true.
+bool summary_tok_supported(const FwdPlan& pl);
+hipError_t launch_summary_tok(const FwdPlan& pl, const WalkArgs& a, hipStream_t stream);
+
+// Affine scan over segments: start[0] = (h, u) (zero when NULL), start[s] = G_{s-1} start[s-1] +
+// d_{s-1} for s >= 1, written in place over the summaries d_0 .. d_{S-2} (slot S-1 receives
+// start[S-1]); also copies hnorm2 to n2_seg0. The final state comes from the last segment's walk.
 hipError_t launch_scan(const FwdPlan& pl, float* ws_states, const float* ws_log2g, float* h,
                        float* u, const float* hnorm2, float* n2_seg0, hipStream_t stream);
 

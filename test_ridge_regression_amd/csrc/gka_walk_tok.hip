@@ -697,7 +697,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
 
   lds_barrier();  // the last chunk's output tile is staged
   flush_o();
-  if (A.out_h) {
+  if (A.out_h && seg == S - 1) {
     float* oh = A.out_h + (size_t)bh * D * D;
     float* ou = A.out_u + (size_t)bh * D * D;
 #pragma unroll
@@ -710,6 +710,269 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
       }
   }
   if (A.n2_out && seg == S - 1 && tid == 0) A.n2_out[bh] = n0sq;
+}
+
+// ---- segment summaries -------------------------------------------------------------------
+// For each (segment, head): the state reached from a zero state over the segment's tokens and
+// the segment's total log2 gate. Unrolling the carry H <- Gam_C H + K^T diag(w) K over the
+// segment gives one weighted sum over its tokens,
+//   dH = sum_s w_s k_s k_s^T,  dU^T = sum_s w_s k_s v_s^T,  w_s = 2^(log2 of the gates after s),
+// so the tokens are taken in blocks of 32 from the last block to the first, with the gate sum
+// of the blocks already taken as the suffix of every weight, and no rescaling of the state.
+// Matrix-core operands are bf16: K and V exactly, the weighted keys w k as a hi + lo pair
+// (about 2^-17 relative). Sixteen waves in two roles, two waves of each per SIMD:
+//  * waves 0..7 hold the float32 state (wave w: row tiles RT*(w % 4).., column tiles
+//    CT*(w / 4).. of dH and dU^T) and only accumulate;
+//  * waves 8..15 load the blocks straight into LDS three ahead, compute the weights and build
+//    the operand tiles K^T, V^T, (w K)^T hi and lo of the next block, as [feature][token] tiles
+//    in the walk's permuted token order (one 16-byte read per fragment).
+// The tiles are double-buffered: each phase builds block p + 1 while block p is accumulated,
+// so the vector work of one role overlaps the matrix-core work of the other, behind one
+// barrier per phase. The roles run separate loops with the same barriers.
+template <int D>
+struct SumCfg {
+  static constexpr int CB = 32;                // tokens per block
+  static constexpr int NA = 8;                 // accumulating waves
+  static constexpr int NBW = 8;                // building waves
+  static constexpr int NT = (NA + NBW) * kWave;
+  static constexpr int FT = D / 16;
+  static constexpr int RT = FT / 4;            // state row tiles per accumulating wave
+  static constexpr int CT = FT / 2;            // state column tiles per accumulating wave
+  static constexpr int LDC = CB + 8;
+  static constexpr int VEC = 8, UPR = D / VEC, NU = CB * UPR;
+  static constexpr int NI = NU / kWave;        // direct-load instructions per matrix and block
+  static constexpr int NPW = 2 * NI / NBW;     // K and V direct loads per building wave per block
+  static constexpr int NBUF = 4;               // block buffers of direct loads
+  static constexpr size_t szT = (size_t)D * LDC * 2;
+  static constexpr size_t szSet = 4 * szT;     // K^T, V^T, (w K)^T hi, lo of one block
+  static constexpr size_t bytes = 2 * szSet + (size_t)NBW * CB * sizeof(float);  // + weights
+  static constexpr size_t szBuf = 2 * (size_t)NU * 16 + CB * sizeof(float);
+  static constexpr int FPB = (FT + NBW - 1) / NBW;  // operand fragments per building wave
+  static_assert(D == 64 || D == 128, "summary tiling");
+  static_assert((2 * NI) % NBW == 0 && NPW >= 1 && 2 * NPW <= 15, "direct loads per wave");
+  static_assert(bytes + NBUF * szBuf <= 160 * 1024, "LDS budget of one CU exceeded");
+  static_assert(NBUF == 4, "the waits below count the blocks in flight for four buffers");
+};
+
+template <int D>
+__global__ __launch_bounds__(1024) void summary_tok_kernel(WalkArgs A, int B, int Tlen, int Hn,
+                                                           int N, int S, int J) {
+  using Cfg = SumCfg<D>;
+  using M = Mma<bf16>;
+  typedef bf16x8 Frag;
+  constexpr int CB = Cfg::CB, NA = Cfg::NA, NBW = Cfg::NBW, FT = Cfg::FT, RT = Cfg::RT;
+  constexpr int CT = Cfg::CT, LDC = Cfg::LDC, UPR = Cfg::UPR, NU = Cfg::NU, NI = Cfg::NI;
+  constexpr int NBUF = Cfg::NBUF;
+  extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+  auto tile = [&](int set, int which) {  // which: 0 K^T, 1 V^T, 2 (w K)^T hi, 3 lo
+    return reinterpret_cast<bf16*>(smem + set * Cfg::szSet + which * Cfg::szT);
+  };
+  __shared__ __attribute__((aligned(16))) unsigned char pre_buf[NBUF * Cfg::szBuf];
+
+  const int seg = blockIdx.x;
+  const int bh = blockIdx.y;
+  const int b = bh / Hn, h = bh % Hn;
+  // the role is uniform per wave (a scalar branch)
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  int lane = threadIdx.x % kWave;
+  int lr = lane % 16, lg = lane / 16;
+  auto refresh = [&]() { asm volatile("" : "+v"(lane), "+v"(lr), "+v"(lg)); };
+  // the segment's tokens [t_begin, t_end) in blocks of CB, block 0 being the last one
+  const int t_begin = seg * J * (2 * CB);
+  const int t_end = min(Tlen, t_begin + J * 2 * CB);
+  const int NB = (t_end - t_begin + CB - 1) / CB;
+
+  if (wave >= NA) {
+    // ================================ building waves ================================
+    const int bw = wave - NA;
+    const long long tok_stride = (long long)Hn * D;
+    auto block_t0 = [&](int p) { return t_begin + (NB - 1 - p) * CB; };
+    auto buf_k = [&](int slot) { return reinterpret_cast<bf16*>(pre_buf + slot * Cfg::szBuf); };
+    auto buf_v = [&](int slot) { return buf_k(slot) + NU * Cfg::VEC; };
+    auto buf_g = [&](int slot) {
+      return reinterpret_cast<float*>(pre_buf + slot * Cfg::szBuf + 2 * (size_t)NU * 16);
+    };
+    // direct loads of block p into buffer p % NBUF: the gates first (the first building wave),
+    // then this wave's share of the units of K and V (jobs j = bw + NBW k: K units, then V)
+    auto prefetch = [&](int p) {
+#if defined(__HIP_DEVICE_COMPILE__)
+      if (p >= NB) return;
+      refresh();
+      typedef __attribute__((address_space(3))) void lds_void;
+      const int slot = p % NBUF;
+      const int t0n = block_t0(p);
+      const int nvn = min(CB, t_end - t0n);
+      if (bw == 0) {
+        const uint32_t gb = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)buf_g(slot));
+        if (lane < nvn) dma_load4(A.gamma + (b * (long long)Tlen + t0n + lane) * Hn + h, gb);
+      }
+      const long long row0 = (b * (long long)Tlen + t0n) * tok_stride + (long long)h * D;
+      const bf16* kb0 = static_cast<const bf16*>(A.k) + row0;
+      const bf16* vb0 = static_cast<const bf16*>(A.v) + row0;
+#pragma unroll
+      for (int k = 0; k < Cfg::NPW; ++k) {
+        const int j = bw + k * NBW;
+        const bool isv = j >= NI;
+        const int qq = isv ? j - NI : j;
+        const int u = qq * kWave + lane;
+        const int tt = u / UPR, cu = u % UPR;
+        const uint32_t lb = __builtin_amdgcn_readfirstlane(
+            (uint32_t)(uintptr_t)(lds_void*)((isv ? buf_v(slot) : buf_k(slot)) + qq * kWave * Cfg::VEC));
+        const uint32_t off = (uint32_t)(tt * (int)tok_stride + cu * Cfg::VEC) * 2u;  // bytes
+        if (tt < nvn) dma_load16_so(isv ? vb0 : kb0, off, lb);
+      }
+#endif
+    };
+    // wait until block p's direct loads of this wave have landed, while the loads of blocks
+    // p + 1 .. p + issued (at most) were issued after them: loads retire in order, so those may
+    // stay outstanding (the first building wave issues one more per block, its gates, which this
+    // over-waits)
+    auto wait_block = [&](int p, int issued) {
+      const int ahead = min(NB - 1 - p, issued);
+      if (ahead >= 2) {
+        constexpr int n = 2 * Cfg::NPW;
+        __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+      } else if (ahead == 1) {
+        constexpr int n = Cfg::NPW;
+        __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
+      } else {
+        __builtin_amdgcn_s_waitcnt(0);
+      }
+    };
+    // operand tiles of block p into tile set p % 2: fragments ft = bw + NBW i (feature tiles),
+    // k-slot j of lane group lg = token 16 (j / 4) + 4 lg + j % 4 of the block; tokens past the
+    // end give zeros. The weights come from a scan over the block (lane = token).
+    float suffix = 0.0f;  // log2 gate sum of the blocks already taken (the later ones)
+    float* v_wl = reinterpret_cast<float*>(smem + 2 * Cfg::szSet) + bw * CB;
+    auto build = [&](int p) {
+      const int slot = p % NBUF, set = p & 1;
+      const int nv = min(CB, t_end - block_t0(p));
+      const float l2 = lane < nv ? log2_gate(buf_g(slot)[lane % CB]) : 0.0f;
+      const float cl = scan_add<CB>(lane < CB ? l2 : 0.0f);
+      const float clast = lane_value(cl, CB - 1);
+      if (lane < CB) v_wl[lane] = fast_exp2(fminf(clast - cl + suffix, 0.0f));
+      suffix += clast;
+#pragma unroll
+      for (int i = 0; i < Cfg::FPB; ++i) {
+        const int ft = bw + NBW * i;
+        if (FT % NBW != 0 && ft >= FT) break;
+        const int s0 = 4 * lg, s1 = s0 + 16;
+        const int r = lr >> 2, coff = 16 * ft + 4 * (lr & 3);
+        bf16x4 k0, k1, u0, u1;
+#if defined(__HIP_DEVICE_COMPILE__)
+        typedef __attribute__((address_space(3))) fp16x4_t lds_fp16x4;
+        const bf16* bk_ = buf_k(slot);
+        const bf16* bv_ = buf_v(slot);
+        k0 = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)(bk_ + (s0 + r) * D + coff)));
+        k1 = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)(bk_ + (s1 + r) * D + coff)));
+        u0 = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)(bv_ + (s0 + r) * D + coff)));
+        u1 = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)(bv_ + (s1 + r) * D + coff)));
+#else
+        k0 = k1 = u0 = u1 = bf16x4{};
+#endif
+        const f32x4 w0 = *reinterpret_cast<const f32x4*>(v_wl + s0);
+        const f32x4 w1 = *reinterpret_cast<const f32x4*>(v_wl + s1);
+        Frag f, g, wh, wlo;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const bool ok = (j < 4 ? s0 : s1) + (j & 3) < nv;
+          const bf16 zero = (bf16)0.0f;
+          f[j] = ok ? (j < 4 ? k0[j] : k1[j - 4]) : zero;
+          g[j] = ok ? (j < 4 ? u0[j] : u1[j - 4]) : zero;
+          const float xw = (float)f[j] * (j < 4 ? w0[j] : w1[j - 4]);
+          wh[j] = (bf16)xw;
+          wlo[j] = (bf16)(xw - (float)wh[j]);
+        }
+        const int o = (16 * ft + lr) * LDC + 8 * lg;
+        *reinterpret_cast<Frag*>(tile(set, 0) + o) = f;
+        *reinterpret_cast<Frag*>(tile(set, 1) + o) = g;
+        *reinterpret_cast<Frag*>(tile(set, 2) + o) = wh;
+        *reinterpret_cast<Frag*>(tile(set, 3) + o) = wlo;
+      }
+    };
+
+    // phase p builds block p + 1 while block p is accumulated; block p + NBUF - 1 is loaded
+    // during phase p into the buffer that block p - 1 has left
+#pragma unroll
+    for (int p = 0; p < NBUF - 1; ++p) prefetch(p);
+    wait_block(0, NBUF - 2);  // blocks 1 .. NBUF - 2 were issued after block 0
+    lds_barrier();
+    build(0);
+    for (int p = 0; p < NB; ++p) {
+      refresh();
+      if (p + 1 < NB) wait_block(p + 1, NBUF - 3);  // block p + 2 was issued after it
+      // block p's tiles are built and block p + 1's loads have landed (every wave); block
+      // p - 1's tiles have been read. This barrier leaves later direct loads in flight.
+      lds_barrier();
+      prefetch(p + NBUF - 1);
+      if (p + 1 < NB) build(p + 1);
+    }
+    if (bw == 0 && lane == 0) A.log2g_out[(long long)bh * S + seg] = suffix;
+  } else {
+    // =============================== accumulating waves ===============================
+    const int a0 = RT * (wave % 4), b0 = CT * (wave / 4);
+    f32x4 Hst[RT][CT], Ust[RT][CT];
+#pragma unroll
+    for (int jr = 0; jr < RT; ++jr)
+#pragma unroll
+      for (int jc = 0; jc < CT; ++jc) {
+        Hst[jr][jc] = f32x4{0.f, 0.f, 0.f, 0.f};
+        Ust[jr][jc] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    lds_barrier();  // (the building waves' first barrier)
+    for (int p = 0; p < NB; ++p) {
+      refresh();
+      lds_barrier();  // block p's tiles are built
+      const int set = p & 1;
+      auto frag = [&](int which, int ft) {
+        return *reinterpret_cast<const Frag*>(tile(set, which) + (16 * ft + lr) * LDC + 8 * lg);
+      };
+      Frag aw[RT], al[RT], bk[CT], bv[CT];
+#pragma unroll
+      for (int jr = 0; jr < RT; ++jr) {
+        aw[jr] = frag(2, a0 + jr);
+        al[jr] = frag(3, a0 + jr);
+      }
+#pragma unroll
+      for (int jc = 0; jc < CT; ++jc) {
+        bk[jc] = frag(0, b0 + jc);
+        bv[jc] = frag(1, b0 + jc);
+      }
+#pragma unroll
+      for (int jc = 0; jc < CT; ++jc)
+#pragma unroll
+        for (int jr = 0; jr < RT; ++jr) {
+          Hst[jr][jc] = M::mma(aw[jr], bk[jc], Hst[jr][jc]);
+          Ust[jr][jc] = M::mma(aw[jr], bv[jc], Ust[jr][jc]);
+          Hst[jr][jc] = M::mma(al[jr], bk[jc], Hst[jr][jc]);
+          Ust[jr][jc] = M::mma(al[jr], bv[jc], Ust[jr][jc]);
+        }
+    }
+    float* oh = A.sum_h + bh * A.sum_bh + seg * A.sum_seg;
+    float* ou = A.sum_u + bh * A.sum_bh + seg * A.sum_seg;
+#pragma unroll
+    for (int jr = 0; jr < RT; ++jr)
+#pragma unroll
+      for (int jc = 0; jc < CT; ++jc) {
+        // H[r..r+3][c] is written as H[c][r..r+3] (symmetric); U^T[r..r+3][c] = U[c][r..r+3]
+        const size_t o = (size_t)(16 * (b0 + jc) + lr) * D + 16 * (a0 + jr) + 4 * lg;
+        *reinterpret_cast<f32x4*>(oh + o) = Hst[jr][jc];
+        *reinterpret_cast<f32x4*>(ou + o) = Ust[jr][jc];
+      }
+  }
+}
+
+template <int D>
+hipError_t launch_sum(const FwdPlan& pl, const WalkArgs& a, hipStream_t stream) {
+  using Cfg = SumCfg<D>;
+  auto kern = summary_tok_kernel<D>;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::bytes);
+  if (e != hipSuccess) return e;
+  // the last segment needs no summary: the walk of that segment produces the final state
+  hipLaunchKernelGGL(kern, dim3(pl.S - 1, pl.B * pl.H), dim3(Cfg::NT), Cfg::bytes, stream, a,
+                     pl.B, pl.T, pl.H, pl.N, pl.S, pl.J);
+  return hipGetLastError();
 }
 
 template <int D>
@@ -729,6 +992,20 @@ hipError_t launch_tok(const FwdPlan& pl, const WalkArgs& a, const ChebConsts& cc
 
 bool walk_tok_supported(const FwdPlan& pl) {
   return pl.dtype == 0 && pl.C == 64 && (pl.D == 32 || pl.D == 64 || pl.D == 128);
+}
+
+bool summary_tok_supported(const FwdPlan& pl) {
+  // the direct loads address a block of 32 tokens with 32-bit byte offsets per lane
+  const long long block_bytes = 32LL * pl.H * pl.D * 2;
+  return pl.dtype == 0 && pl.C == 64 && (pl.D == 64 || pl.D == 128) && block_bytes < (1LL << 31);
+}
+
+hipError_t launch_summary_tok(const FwdPlan& pl, const WalkArgs& a, hipStream_t stream) {
+  switch (pl.D) {
+    case 64: return launch_sum<64>(pl, a, stream);
+    case 128: return launch_sum<128>(pl, a, stream);
+  }
+  return hipErrorInvalidValue;
 }
 
 hipError_t launch_walk_tok(const FwdPlan& pl, const WalkArgs& a, const ChebConsts& cc,
