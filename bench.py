@@ -92,7 +92,7 @@ def measured_traffic(kernel):
         rec = json.load(open(path))[kernel]
     except (OSError, KeyError, ValueError):
         return None
-    files = {"walk_kernel": ("gka_fwd.hip", "gka_common.hpp"),
+    files = {"walk_tok_kernel": ("gka_walk_tok.hip", "gka_common.hpp"),
              "step_kernel": ("gka_step.hip", "gka_common.hpp")}[kernel]
     h = hashlib.sha256()
     for f in files:
@@ -126,12 +126,18 @@ def bench_prefill(W, steps, warmup, ev):
     log(f"prefill timed {steps}")
     ev.record(t0, stream.cuda_stream)
     for i in range(steps):
-        gka.fwd_chunked(qd, kd, vd, gd, W.a, W.iters, W.chunk, out=o, workspace=ws,
-                        phase_events=arrs[i])
+        gka.fwd_chunked(qd, kd, vd, gd, W.a, W.iters, W.chunk, out=o, workspace=ws)
     ev.record(t1, stream.cuda_stream)
     ev.sync(t1)
     torch.cuda.synchronize()
     total_ms = ev.elapsed_ms(t0, t1)
+    # per-kernel times in a second pass of the same steps: events between the launches of one
+    # call (on the launch stream) would add their own gaps to the timed steps
+    log(f"prefill phases {steps}")
+    for i in range(steps):
+        gka.fwd_chunked(qd, kd, vd, gd, W.a, W.iters, W.chunk, out=o, workspace=ws,
+                        phase_events=arrs[i])
+    torch.cuda.synchronize()
     walk = [ev.elapsed_ms(phase[4 * i + 2], phase[4 * i + 3]) for i in range(steps)]
     summ = [ev.elapsed_ms(phase[4 * i + 0], phase[4 * i + 1]) for i in range(steps)]
     scan = [ev.elapsed_ms(phase[4 * i + 1], phase[4 * i + 2]) for i in range(steps)]
@@ -289,10 +295,10 @@ def main():
         "data": "synthetic",
         "config": {"workload": W.name, "B": W.B, "T": W.T, "H": W.H, "D": W.D, "chunk": W.chunk,
                    "a": W.a, "iters": W.iters, "segments": pre["segments"]},
-        "roofline": {"bound": "mfma", "kernel": "walk_kernel (fused chunk walk)",
+        "roofline": {"bound": "mfma", "kernel": "walk_tok_kernel (token-owning chunk walk)",
                      "achieved": achieved / 1e12, "peak": PEAK_BF16_MFMA / 1e12,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_MFMA,
-                     "traffic": measured_traffic("walk_kernel"),
+                     "traffic": measured_traffic("walk_tok_kernel"),
                      "flops_per_launch": F, "avg_launch_ms": pre["walk_ms"]},
         "whole_step_mfma_frac": F / (pre["ms_per_step"] * 1e-3) / PEAK_BF16_MFMA,
         "phases_ms": {"summary": pre["summary_ms"], "scan": pre["scan_ms"],

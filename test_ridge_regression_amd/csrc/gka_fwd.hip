@@ -939,8 +939,8 @@ static hipError_t launch_walk_t(const FwdPlan& pl, bool summary, const WalkArgs&
     const dim3 sgrid(pl.S - 1, pl.B * pl.H);
     const size_t bytes = 4 * CfgS::szRD;  // K, V, w K hi and lo (token-major)
     auto kern = summary_kernel<T, D, C>;
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    static std::atomic<uint64_t> lds_set{0};
+    hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), (int)bytes, lds_set);
     if (e != hipSuccess) return e;
     hipLaunchKernelGGL(kern, sgrid, dim3(CfgS::NT), bytes, stream, a, pl.B, pl.T, pl.H, pl.N,
                        pl.S, pl.J);
@@ -949,8 +949,8 @@ static hipError_t launch_walk_t(const FwdPlan& pl, bool summary, const WalkArgs&
   auto kern = walk_kernel<T, D, C>;
   const size_t bytes = Cfg::bytes;
   const int threads = Cfg::NT;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), (int)bytes, lds_set);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, grid, dim3(threads), bytes, stream, a, pl.B, pl.T, pl.H, pl.N,
                      pl.S, pl.J, cc);

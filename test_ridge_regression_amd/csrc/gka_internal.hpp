@@ -5,9 +5,25 @@
 #include <stddef.h>
 #include <stdint.h>
 
+#include <atomic>
+
 #include "gka_common.hpp"
 
 namespace gka {
+
+// Raises a kernel's dynamic LDS limit, once per device: the attribute persists, and setting it on
+// every launch costs host time between the launches of one call. `done` holds one bit per
+// device (devices >= 64 are set every time).
+inline hipError_t ensure_dynamic_lds(const void* kern, int bytes, std::atomic<uint64_t>& done) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const uint64_t bit = dev >= 0 && dev < 64 ? (uint64_t)1 << dev : 0;
+  if (bit && (done.load(std::memory_order_acquire) & bit)) return hipSuccess;
+  e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e == hipSuccess && bit) done.fetch_or(bit, std::memory_order_release);
+  return e;
+}
 
 // Decode step: one workgroup per (batch row, head).
 hipError_t launch_step(int dtype, int D, int BH, const void* q, const void* k, const void* v,

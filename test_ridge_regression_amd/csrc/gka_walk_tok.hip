@@ -966,8 +966,8 @@ template <int D>
 hipError_t launch_sum(const FwdPlan& pl, const WalkArgs& a, hipStream_t stream) {
   using Cfg = SumCfg<D>;
   auto kern = summary_tok_kernel<D>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::bytes);
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), (int)Cfg::bytes, lds_set);
   if (e != hipSuccess) return e;
   // the last segment needs no summary: the walk of that segment produces the final state
   hipLaunchKernelGGL(kern, dim3(pl.S - 1, pl.B * pl.H), dim3(Cfg::NT), Cfg::bytes, stream, a,
@@ -980,8 +980,8 @@ hipError_t launch_tok(const FwdPlan& pl, const WalkArgs& a, const ChebConsts& cc
                       hipStream_t stream) {
   using Cfg = TokCfg<D>;
   auto kern = walk_tok_kernel<D>;
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)Cfg::bytes);
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), (int)Cfg::bytes, lds_set);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(kern, dim3(pl.S, pl.B * pl.H), dim3(Cfg::NT), Cfg::bytes, stream, a, pl.B,
                      pl.T, pl.H, pl.N, pl.S, pl.J, cc);
