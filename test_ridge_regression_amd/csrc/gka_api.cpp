@@ -45,6 +45,8 @@ bool overlap(const void* a, size_t na, const void* b, size_t nb) {
 // Chebyshev constants of the system divided by ||H_t||_F: spectrum in [mu, L] = [a, 1 + a],
 // c = 2 / (L + mu), rho = (L - mu) / (L + mu), omega_0 = 2, omega_i = 4 / (4 - rho^2 omega_{i-1})
 // (weight schedule of Lemma 3 / Lemma 4 on the pith.science page of arXiv 2511.21016).
+double w_of(int i, const double* om) { return i == 0 ? 1.0 : om[i]; }
+
 ChebConsts cheb_consts(float a, int iters) {
   ChebConsts cc{};
   const double ad = a;
@@ -80,6 +82,26 @@ ChebConsts cheb_consts(float a, int iters) {
     cc.kp[i] = (float)(i == 0 ? 0.0 : 1.0 - w);
     cc.kr[i] = (float)(w * (1.0 - c * ad));
     cc.ky[i] = (float)(-w * c);
+  }
+  // Rescaled form: ratio r = s_i / s_{i-1} of consecutive scales, s_i itself only for bts
+  // (where underflow to 0 only drops terms far below the rounding of the rest)
+  constexpr double kS0 = 0.7390851332151607;  // the fixed point of cos
+  cc.iters_rs = iters;
+  cc.inv_s0 = (float)(1.0 / kS0);
+  double r = 1.0, s = kS0;
+  for (int i = 0; i < iters; ++i) {
+    cc.bts[i] = (float)(cur[i] * s);
+    if (i + 1 == iters) break;
+    const double kp = i == 0 ? 0.0 : 1.0 - om[i];
+    if (i >= 1 && std::fabs(kp) < 0x1p-64) {
+      cc.iters_rs = i + 1;
+      break;
+    }
+    const double rn = i == 0 ? 1.0 : kp / r;  // s_{i+1} / s_i
+    cc.krs[i] = (float)(w_of(i, om) * (1.0 - c * ad) / rn);
+    cc.kys[i] = (float)(-w_of(i, om) * c / rn);
+    s *= rn;
+    r = rn;
   }
   return cc;
 }

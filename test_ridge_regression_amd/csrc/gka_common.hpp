@@ -232,6 +232,54 @@ __device__ inline void dma_load16_so(const void* base, uint32_t voff, uint32_t l
       : "v"(voff), "s"(sbase), "s"(lds_base)
       : "memory");
 }
+// Buffer resource over `bytes` bytes from `base` (wave-uniform): raw buffer loads at byte
+// offsets at or past the end return 0 and stores there are dropped, so ragged tails need no
+// branches. Descriptor word 3 = 0x00020000 is the raw 32-bit-element layout of the gfx9 family.
+// The base and size are read from the first lane: the compiler then keeps the descriptor in
+// scalar registers even where it cannot prove the arguments uniform (otherwise every access
+// becomes a loop over the distinct descriptors of the wave).
+__device__ inline __amdgpu_buffer_rsrc_t buffer_rsrc(const void* base, uint32_t bytes) {
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  const int n = __builtin_amdgcn_readfirstlane((int)bytes);
+  return __builtin_amdgcn_make_buffer_rsrc(reinterpret_cast<void*>((uintptr_t)(lo | (hi << 32))),
+                                           (short)0, n, 0x00020000);
+}
+template <typename V>
+__device__ inline V buffer_load16(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  static_assert(sizeof(V) == 16, "16-byte element");
+  return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+template <typename V>
+__device__ inline V buffer_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  static_assert(sizeof(V) == 8, "8-byte element");
+  return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
+}
+__device__ inline float buffer_load4f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+template <typename V>
+__device__ inline void buffer_store8(V x, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  static_assert(sizeof(V) == 8, "8-byte element");
+  typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+  __builtin_amdgcn_raw_buffer_store_b64(__builtin_bit_cast(u32x2, x), r, off, 0, 0);
+}
+
+// 4-byte form of dma_load16_so
+__device__ inline void dma_load4_so(const void* base, uint32_t voff, uint32_t lds_base) {
+  const uint64_t p = (uint64_t)(uintptr_t)base;
+  const uint64_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)p);
+  const uint64_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(p >> 32));
+  const uint64_t sbase = lo | (hi << 32);
+  uint32_t m0_saved;
+  asm volatile(
+      "s_mov_b32 %0, m0\n\ts_mov_b32 m0, %3\n\ts_nop 0\n\t"
+      "global_load_lds_dword %1, %2\n\ts_mov_b32 m0, %0"
+      : "=&s"(m0_saved)
+      : "v"(voff), "s"(sbase), "s"(lds_base)
+      : "memory");
+}
 __device__ inline void dma_load4(const void* src, uint32_t lds_base) {
   uint32_t m0_saved;
   asm volatile(
@@ -287,6 +335,11 @@ __device__ inline float lane_value(float x, int l) {
   return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, x), l));
 }
 
+// value of x in lane src (0 <= src < 64, per lane), through the LDS crossbar (ds_bpermute)
+__device__ inline float lane_read(float x, int src) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, x)));
+}
+
 // ---- wave reductions (wave64) -------------------------------------------------------------
 __device__ inline float wave_sum(float x) {
 #pragma unroll
@@ -309,15 +362,30 @@ __device__ inline float log2_gate(float g) {
 // beta_i of the iterate x_r = sum_i beta_i r_i as a combination of the residuals r_i of the
 // same iteration. Filled on the host.
 // The residual recurrence is applied as R_{i+1} = kp_i R_{i-1} + kr_i R_i + ky_i (A - a I) R_i.
+// Rescaled form (no multiply by kp): with scalars s_0 = s_1 = s0 and s_{i+1} = kp_i s_{i-1},
+// the residuals Rt_i = R_i / s_i obey Rt_{i+1} = Rt_{i-1} + krs_i Rt_i + kys_i (A - a I) Rt_i
+// and x_r = sum_i bts_i Rt_i, with krs_i = kr_i s_i / s_{i+1}, kys_i = ky_i s_i / s_{i+1} and
+// bts_i = beta_i s_i; Rt_0 = q * inv_s0. iters_rs <= iters is the count for that form: it stops
+// before the first step whose |kp_i| is below 2^-64, where every later residual is below 2^-64
+// of the first. s0 is a constant far from short binary fractions: with s0 = 1, the rescaled
+// residuals of a system whose spectrum sits at both interval ends reproduce q exactly every
+// second step, and the fp16 rounding of those (q on the bf16 grid plus a multiple of k) adds up
+// along k; in a float64 model of the rounding that costs about 1.5x the error of the plain form
+// when gates are 0, against about 1.15x with this s0.
 struct ChebConsts {
   float a;
   float c;
   int iters;
+  int iters_rs;
+  float inv_s0;
   float omega[64];
   float beta[64];
   float kp[64];
   float kr[64];
   float ky[64];
+  float krs[64];
+  float kys[64];
+  float bts[64];
 };
 
 }  // namespace gka

@@ -27,7 +27,7 @@
 // resident H0hat fragments, the Gram tiles of the own tokens) and a scan over the 64 tokens;
 // U0hat is staged; the carry advances the float32 state (held as accumulator tiles, a quarter
 // per wave); the Chebyshev loop; the output products. The next chunk's K, V and gates are
-// loaded straight into LDS during the loop.
+// loaded into registers during the output phase and staged at the top of the next chunk.
 #include "gka_internal.hpp"
 
 namespace gka {
@@ -55,17 +55,15 @@ struct TokCfg {
   static constexpr size_t oKp = 0;               // K, token-major, permuted features (fp16)
   static constexpr size_t oVp = oKp + szTok;     // V, token-major (fp16)
   static constexpr size_t oHs = oVp + szTok;     // H0hat, then U0hat: row-major, permuted columns
-  static constexpr size_t oOb = oHs + szHs;      // output tile, token-major (bf16)
   static constexpr int LDC = C + 8;              // row stride of the [D][C] fp16 tile
-  static constexpr size_t oKT = oOb + szTok;     // K^T: row-major, tokens permuted (fp16)
+  static constexpr size_t oKT = oHs + szHs;      // K^T: row-major, tokens permuted (fp16)
   static constexpr size_t oVT = oKT + (size_t)D * LDC * 2;  // V^T, likewise
   static constexpr size_t oVec = oVT + (size_t)D * LDC * 2;
   static constexpr size_t szVec = (size_t)(4 * C + 16 + 4 * 64) * sizeof(float);
   static constexpr size_t bytes = oVec + szVec;  // dynamic LDS
-  static constexpr size_t szPre = 2 * (size_t)NU * 16 + C * sizeof(float);  // static LDS
   static_assert(D % 32 == 0 && NST >= 1, "unsupported D");
   static_assert(NU % NT == 0, "staging units must fill whole workgroups");
-  static_assert(bytes + szPre <= 160 * 1024, "LDS budget of one CU exceeded");
+  static_assert(bytes <= 160 * 1024, "LDS budget of one CU exceeded");
 };
 
 // column of logical feature d in a permuted row: within each block of 32, the four-element
@@ -123,7 +121,6 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
   f16* Kp = reinterpret_cast<f16*>(smem + Cfg::oKp);
   f16* Vp = reinterpret_cast<f16*>(smem + Cfg::oVp);
   f16* Hs = reinterpret_cast<f16*>(smem + Cfg::oHs);
-  bf16* Ob = reinterpret_cast<bf16*>(smem + Cfg::oOb);
   f16* KT = reinterpret_cast<f16*>(smem + Cfg::oKT);
   f16* VT = reinterpret_cast<f16*>(smem + Cfg::oVT);
   float* v_cl = reinterpret_cast<float*>(smem + Cfg::oVec);  // [C] in-chunk log2 gate prefix
@@ -131,13 +128,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
   float* v_a = v_w + C;     // [C] n^2 scan: a_t = gamma_t^2
   float* v_b = v_a + C;     // [C] n^2 scan: b_t
   float* v_sc = v_b + C;    // [16] scratch
-  float* v_coef = v_sc + 16;  // [iters][4] kp, kr, ky, beta of each iteration
-  // the next chunk's K and V ([token][unit], 16-byte units) and gates, loaded straight from
-  // global memory while the current chunk computes
-  __shared__ __attribute__((aligned(16))) unsigned char pre_buf[Cfg::szPre];
-  bf16x8* PreK = reinterpret_cast<bf16x8*>(pre_buf);
-  bf16x8* PreV = PreK + NU;
-  float* PreG = reinterpret_cast<float*>(PreV + NU);
+  float* v_coef = v_sc + 16;  // [iters][4] krs, kys, bts of each iteration (rescaled form)
 
   const int seg = blockIdx.x;
   const int bh = blockIdx.y;
@@ -149,19 +140,22 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
   int tid = threadIdx.x, lane = tid % kWave;
   int lr = lane % 16, lg = lane / 16;
   int t = 16 * wave + lr;  // own token (column of the wave's accumulator tiles)
+  // (the wave's state tiles a0, b0 likewise)
+  int a0 = (wave * Cfg::NST) / FT, b0 = (wave * Cfg::NST) % FT;
   auto refresh = [&]() {
     asm volatile("" : "+v"(tid), "+v"(lane), "+v"(lr), "+v"(lg), "+v"(t), "+v"(wave));
+    asm volatile("" : "+v"(a0), "+v"(b0));
   };
   const int c_begin = seg * J;
   const int c_end = min(N, c_begin + J);
   const long long tok_stride = (long long)Hn * D;
+  const uint32_t tok_bytes = (uint32_t)Hn * D * 2u;  // < 2^25: 64 rows fit a 32-bit offset
   const bf16* qg = static_cast<const bf16*>(A.q);
   const bf16* kg = static_cast<const bf16*>(A.k);
   const bf16* vg = static_cast<const bf16*>(A.v);
   bf16* og = static_cast<bf16*>(A.o);
 
   // ---- float32 state: tiles (a0 + jr, b0 + jc) of H and of U^T (rows = key features) -------
-  const int a0 = (wave * NST) / FT, b0 = (wave * NST) % FT;
   f32x4 Hst[NRT][NCT], Ust[NRT][NCT];
 #pragma unroll
   for (int jr = 0; jr < NRT; ++jr)
@@ -192,11 +186,11 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
     if (lane == 0) v_sc[wave] = sq;
     // Chebyshev coefficients, read from LDS in the loop (scalar loads in flight would make
     // every wait for an LDS fragment a wait for all of them)
-    if (tid < cc.iters) {
-      v_coef[4 * tid] = cc.kp[tid];
-      v_coef[4 * tid + 1] = cc.kr[tid];
-      v_coef[4 * tid + 2] = cc.ky[tid];
-      v_coef[4 * tid + 3] = cc.beta[tid];
+    if (tid < cc.iters_rs) {
+      v_coef[4 * tid] = cc.krs[tid];
+      v_coef[4 * tid + 1] = cc.kys[tid];
+      v_coef[4 * tid + 2] = cc.bts[tid];
+      v_coef[4 * tid + 3] = 0.0f;
     }
     __syncthreads();
     if (seg == 0 && A.n2_in) {
@@ -206,58 +200,35 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
     }
   }
 
-  auto prefetch = [&](int chn) {
-#if defined(__HIP_DEVICE_COMPILE__)
-    if (chn >= c_end) return;
-    refresh();  // keeps the per-lane source addresses from being hoisted out of the chunk loop
-    typedef __attribute__((address_space(3))) void lds_void;
-    constexpr int NI = NU / kWave;  // wave instructions per matrix
-    static_assert(NI % NW == 0, "prefetch instructions must split evenly over the waves");
-    const int t0n = chn * C;
-    const int nvn = min(C, Tlen - t0n);
+  // The next chunk's K and V (16-byte units, consecutive threads along a token row) and gates
+  // (lane = token) are loaded into registers at the start of the output phase, where few
+  // registers are live, and staged at the top of the next chunk. Rows past the end of the
+  // sequence are zero, with gate 1.
+  bf16x8 kin[NU / NT], vin[NU / NT];
+  float gin = 1.0f;
+  auto load_kv = [&](int chn) {
+    refresh();  // keeps the per-lane addresses from being hoisted out of the chunk loop
+    // Bounds-checked buffer loads: rows past the end of the sequence (or of the segment) read
+    // as 0, with no branch, so the compiler counts these loads and waits for exactly them
+    // where they are used. The values are defined on every path.
+    const int chv = chn < c_end ? chn : c_end - 1;
+    const int t0n = chv * C;
+    const int nvn = chn < c_end ? min(C, Tlen - t0n) : 0;
     const long long row0 = (b * (long long)Tlen + t0n) * tok_stride + (long long)h * D;
-    const bf16* ks = kg + row0;
-    const bf16* vs = vg + row0;
+    const uint32_t valid = nvn > 0 ? (uint32_t)(nvn - 1) * tok_bytes + D * 2u : 0u;
+    const auto rk = buffer_rsrc(kg + row0, valid);
+    const auto rv = buffer_rsrc(vg + row0, valid);
 #pragma unroll
-    for (int k = 0; k < NI / NW; ++k) {
-      const int qq = wave + k * NW;
-      const int u = qq * kWave + lane;
-      const int tt = u / UPR, cu = u % UPR;
-      const uint32_t kb = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)(PreK + qq * kWave));
-      const uint32_t vb = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)(PreV + qq * kWave));
-      if (tt < nvn) {
-        const long long off = (long long)tt * tok_stride + cu * Cfg::VEC;
-        dma_load16(ks + off, kb);
-        dma_load16(vs + off, vb);
-      }
+    for (int k = 0; k < NU / NT; ++k) {
+      const int u = tid + k * NT;
+      const int tt = (uint32_t)u / UPR, cu = (uint32_t)u % UPR;  // u >= 0
+      const uint32_t off = (uint32_t)tt * tok_bytes + (uint32_t)cu * 16u;
+      kin[k] = buffer_load16<bf16x8>(rk, off);
+      vin[k] = buffer_load16<bf16x8>(rv, off);
     }
-    if (wave == NW - 1) {
-      const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)PreG);
-      if (lane < nvn) dma_load4(A.gamma + (b * (long long)Tlen + t0n + lane) * Hn + h, base);
-    }
-#endif
-  };
-  // the output tile of a chunk is written out after the next workgroup barrier, in 16-byte
-  // units with consecutive threads along a token's row
-  int pend_t0 = 0, pend_nv = 0;
-  auto flush_o = [&]() {
-    if (pend_nv > 0) {
-      bf16x8 ov[NU / NT];
-#pragma unroll
-      for (int k = 0; k < NU / NT; ++k) {
-        const int u = tid + k * NT;
-        ov[k] = *reinterpret_cast<const bf16x8*>(Ob + (u / UPR) * LDD + (u % UPR) * Cfg::VEC);
-      }
-#pragma unroll
-      for (int k = 0; k < NU / NT; ++k) {
-        const int u = tid + k * NT;
-        const int tt = u / UPR, cu = u % UPR;
-        if (tt < pend_nv)
-          *reinterpret_cast<bf16x8*>(og + (b * (long long)Tlen + pend_t0 + tt) * tok_stride +
-                                     (long long)h * D + cu * Cfg::VEC) = ov[k];
-      }
-      pend_nv = 0;
-    }
+    const auto rg = buffer_rsrc(A.gamma + (b * (long long)Tlen + t0n) * Hn + h,
+                                nvn > 0 ? (uint32_t)(nvn - 1) * Hn * 4u + 4u : 0u);
+    gin = buffer_load4f(rg, (uint32_t)lane * Hn * 4u);
   };
   // state tiles (times sc) -> Hs as fp16 rows e = column index of the tile, permuted columns
   auto stage_state = [&](f32x4(&St)[NRT][NCT], float sc) {
@@ -283,7 +254,10 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
     return *reinterpret_cast<const Frag*>(VT + (16 * ft + lr) * LDC + 32 * kc + 8 * lg);
   };
 
-  prefetch(c_begin);
+  load_kv(c_begin);
+  // nothing in flight on entry to the chunk loop, so that the compiler's wait at its top counts
+  // only the loads issued in the output phase of the previous chunk (and not its stores)
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
 
   for (int ch = c_begin; ch < c_end; ++ch) {
     refresh();
@@ -291,24 +265,12 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
     const int nv = min(C, Tlen - t0);
     const float n0 = sqrtf(n0sq);
     const float n0inv = n0 > 0.0f ? 1.0f / n0 : 0.0f;
-    __builtin_amdgcn_s_waitcnt(0);  // this wave's direct loads of this chunk have landed
-    __syncthreads();                // every wave's loads have landed; the last chunk's LDS reads are done
-    flush_o();
+    lds_barrier();  // the last chunk's LDS reads are done
 
-    // ---- queries of the own token, accumulator layout: Q[t][16 ft + 4 lg .. + 3] ------------
-    bf16x4 Qraw[FT];
-#pragma unroll
-    for (int ft = 0; ft < FT; ++ft) {
-      bf16x4 qv = {(bf16)0.0f, (bf16)0.0f, (bf16)0.0f, (bf16)0.0f};
-      if (t < nv)
-        qv = *reinterpret_cast<const bf16x4*>(qg + (b * (long long)Tlen + t0 + t) * tok_stride +
-                                               (long long)h * D + 16 * ft + 4 * lg);
-      Qraw[ft] = qv;
-    }
     // ---- gate prefix (every wave; lane = token) ---------------------------------------------
     float g_l = 1.0f, l2 = 0.0f;  // tokens past the end: gamma = 1 with k = v = q = 0
     if (lane < nv) {
-      g_l = PreG[lane];
+      g_l = gin;
       l2 = log2_gate(g_l);
     }
     const float cl = scan_add<kWave>(l2);
@@ -321,22 +283,16 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
     }
     // ---- stage K (fp16, permuted features) and V (fp16) ------------------------------------
     {
-      bf16x8 kin[NU / NT], vin[NU / NT];  // all reads first: one wait covers them
-#pragma unroll
-      for (int k = 0; k < NU / NT; ++k) {
-        kin[k] = PreK[tid + k * NT];
-        vin[k] = PreV[tid + k * NT];
-      }
 #pragma unroll
     for (int k = 0; k < NU / NT; ++k) {
       const int u = tid + k * NT;
-      const int tt = u / UPR, cu = u % UPR;
-      const bf16x8 kv = kin[k], vv = vin[k];
+      const int tt = (uint32_t)u / UPR, cu = (uint32_t)u % UPR;  // u >= 0
+      const bf16x8 kv = kin[k], vv = vin[k];  // rows past the end were read as 0
       f16x8 ko, vo;
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        ko[i] = tt < nv ? (f16)(float)kv[i] : (f16)0.0f;
-        vo[i] = tt < nv ? (f16)(float)vv[i] : (f16)0.0f;
+        ko[i] = (f16)(float)kv[i];
+        vo[i] = (f16)(float)vv[i];
       }
       *reinterpret_cast<f16x8*>(Vp + tt * LDD + 8 * cu) = vo;
       *reinterpret_cast<f16x4*>(Kp + tt * LDD + pcol(8 * cu)) = f16x4{ko[0], ko[1], ko[2], ko[3]};
@@ -346,11 +302,6 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
     stage_state(Hst, n0inv);  // H0hat
     lds_barrier();
 
-    // the queries are consumed before the next chunk's loads are issued: loads retire in order,
-    // so a wait for the queries issued after the prefetch would also wait for the prefetch
-#pragma unroll
-    for (int ft = 0; ft < FT; ++ft) asm volatile("" : "+v"(Qraw[ft]));
-    prefetch(ch + 1);
     refresh();
 
     // ---- resident H0hat fragments ------------------------------------------------------------
@@ -415,14 +366,14 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
           kd = s == t ? gacc[i] : kd;
         }
       }
-      pu += __shfl_xor(pu, 16, kWave);
-      pu += __shfl_xor(pu, 32, kWave);
-      pv += __shfl_xor(pv, 16, kWave);
-      pv += __shfl_xor(pv, 32, kWave);
-      kd += __shfl_xor(kd, 16, kWave);
-      kd += __shfl_xor(kd, 32, kWave);
-      const float gt = __shfl(g_l, t, kWave);
-      const float gprev = __shfl(gam, t > 0 ? t - 1 : 0, kWave);
+      pu += lane_read(pu, lane ^ 16);
+      pu += lane_read(pu, lane ^ 32);
+      pv += lane_read(pv, lane ^ 16);
+      pv += lane_read(pv, lane ^ 32);
+      kd += lane_read(kd, lane ^ 16);
+      kd += lane_read(kd, lane ^ 32);
+      const float gt = lane_read(g_l, t);
+      const float gprev = lane_read(gam, t > 0 ? t - 1 : 0);
       if (lg == 0) {
         v_a[t] = gt * gt;
         v_b[t] = 2.0f * gt * ((t > 0 ? gprev : 1.0f) * n0 * pu + pv) + kd * kd;
@@ -439,9 +390,9 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
     if (wave == 0 && A.hnorm_t && lane < nv)
       A.hnorm_t[(b * (long long)Tlen + t0 + lane) * Hn + h] = sqrtf(n2);
     const float n2last = lane_value(n2, C - 1);
-    const float ninv_t = __shfl(ninv, t, kWave);
-    const float s_t = __shfl(gam, t, kWave) * n0 * ninv_t;
-    const float cl_t = __shfl(cl, t, kWave);
+    const float ninv_t = lane_read(ninv, t);
+    const float s_t = lane_read(gam, t) * n0 * ninv_t;
+    const float cl_t = lane_read(cl, t);
     // Mhat^T tiles of the own token: Mh[sb][i] = Mhat_{t, 16 sb + 4 lg + i}
     f32x4 Mh[ST];
 #pragma unroll
@@ -455,6 +406,17 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
     }
     stage_state(Ust, n0inv);  // U0hat (every wave has read its H0hat fragments)
 
+    // ---- queries of the own token, accumulator layout: Q[t][16 ft + 4 lg .. + 3], loaded
+    // during the carry's products and consumed at the start of the loop ----------------------
+    bf16x4 Qraw[FT];
+    {
+      // bounds-checked: tokens past the end read as 0
+      const auto rq = buffer_rsrc(qg + (b * (long long)Tlen + t0) * tok_stride + (long long)h * D,
+                                  (uint32_t)(nv - 1) * tok_bytes + D * 2u);
+      const uint32_t qoff = (uint32_t)t * tok_bytes + (uint32_t)lg * 8u;
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft) Qraw[ft] = buffer_load8<bf16x4>(rq, qoff + 32u * ft);
+    }
     // ---- state carry: H <- Gam_C H + K^T diag(w) K, U^T <- Gam_C U^T + K^T diag(w) V --------
     {
       // A operands (w K)^T of the own row tiles, split hi + lo; tokens in the permuted order
@@ -523,21 +485,20 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
     f32x4 Ra[FT], Rb[FT], X[FT];
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) {
-      Ra[ft] = live ? f32x4{(float)Qraw[ft][0], (float)Qraw[ft][1], (float)Qraw[ft][2], (float)Qraw[ft][3]}
+      Ra[ft] = live ? f32x4{(float)Qraw[ft][0], (float)Qraw[ft][1], (float)Qraw[ft][2], (float)Qraw[ft][3]} * cc.inv_s0
                     : f32x4{0.f, 0.f, 0.f, 0.f};
       Rb[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
       X[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
-    // One iteration it on the current residual Rc = R_it:
-    //   Ro <- kp Ro + kr Rc + H0hat (ky s_t Rc) + K^T ((K Rc) o ky Mhat)
-    // (Ro held R_{it-1} and now holds R_{it+1}), and X += beta_it R_it. The kp Ro term is
-    // applied one step early: once Rc has served this step, it is scaled by the next step's kp.
+    // One iteration it on the current rescaled residual Rc = Rt_it (the residuals divided by
+    // host scalars that absorb the R_{it-1} coefficient of the recurrence):
+    //   Ro <- Ro + krs Rc + H0hat (kys s_t Rc) + K^T ((K Rc) o kys Mhat)
+    // (Ro held Rt_{it-1} and now holds Rt_{it+1}), and X += bts_it Rt_it.
     // The work forms three instruction groups (sched_barrier boundaries), each pairing
     // matrix-core products with independent vector work and with the LDS reads of a later
     // group: (A) the K products P = K Rc^T and the recurrence start; (B) the H0hat products on
-    // the scaled operands and the P' operands; (C) the K^T products, the X update, the
-    // pre-scaling and the next step's first K fragments. With one wave per SIMD nothing else
-    // hides latency.
+    // the scaled operands and the P' operands; (C) the K^T products, the X update and the
+    // next step's first K fragments. With one wave per SIMD nothing else hides latency.
     constexpr int KN = KD < 2 ? KD : 2;  // K fragment blocks read ahead of a step
     Frag kn[KN][ST];
     auto load_kn = [&]() {
@@ -550,8 +511,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
       // K and K^T fragments are read from LDS in every iteration: without this the compiler
       // hoists them out of the loop as invariant loads and runs out of registers
       asm volatile("" ::: "memory");
-      const f32x4 cf = *reinterpret_cast<const f32x4*>(v_coef + 4 * it);  // kp, kr, ky, beta
-      const float kp_next = v_coef[4 * (it + 1)];
+      const f32x4 cf = *reinterpret_cast<const f32x4*>(v_coef + 4 * it);  // krs, kys, bts
       Frag rf[KD], rs[KD], kq[KD][ST], kt[KC][FT], pf[KC];
       f32x4 pa[ST];
       // (A)
@@ -571,10 +531,10 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
       for (int kk = 0; kk < KD; ++kk)
 #pragma unroll
         for (int sb = 0; sb < ST; ++sb) pa[sb] = M::mma(kq[kk][sb], rf[kk], pa[sb]);
-      const float kys = cf[2] * s_t;
+      const float kys = cf[1] * s_t;
       rs[0] = pack8(Rc[0] * kys, Rc[1] * kys);
 #pragma unroll
-      for (int ft = 0; ft < FT; ++ft) Ro[ft] = Ro[ft] + cf[1] * Rc[ft];
+      for (int ft = 0; ft < FT; ++ft) Ro[ft] = Ro[ft] + cf[0] * Rc[ft];
       __builtin_amdgcn_sched_barrier(0);
       // (B)
 #pragma unroll
@@ -589,7 +549,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
         for (int ft = 0; ft < FT; ++ft) Ro[ft] = M::mma(Hres[ft][kk], rs[kk], Ro[ft]);
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc)
-        pf[kc] = pack8(pa[2 * kc] * Mh[2 * kc] * cf[2], pa[2 * kc + 1] * Mh[2 * kc + 1] * cf[2]);
+        pf[kc] = pack8(pa[2 * kc] * Mh[2 * kc] * cf[1], pa[2 * kc + 1] * Mh[2 * kc + 1] * cf[1]);
       __builtin_amdgcn_sched_barrier(0);
       // (C)
 #pragma unroll
@@ -597,22 +557,20 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
 #pragma unroll
         for (int ft = 0; ft < FT; ++ft) Ro[ft] = M::mma(kt[kc][ft], pf[kc], Ro[ft]);
 #pragma unroll
-      for (int ft = 0; ft < FT; ++ft) {
-        X[ft] += cf[3] * Rc[ft];
-        Rc[ft] = Rc[ft] * kp_next;
-      }
+      for (int ft = 0; ft < FT; ++ft) X[ft] += cf[2] * Rc[ft];
       load_kn();
       __builtin_amdgcn_sched_barrier(0);
     };
     {
       load_kn();
       int it = 0;
-      for (; it + 2 < cc.iters; it += 2) {
+      const int iters = cc.iters_rs;
+      for (; it + 2 < iters; it += 2) {
         step(Rb, Ra, it);
         step(Ra, Rb, it + 1);
       }
-      const float bl = v_coef[4 * (cc.iters - 1) + 3];  // X += beta_{r-1} R_{r-1}
-      if (it + 1 < cc.iters) {
+      const float bl = v_coef[4 * (iters - 1) + 2];  // X += bts_{r-1} Rt_{r-1}
+      if (it + 1 < iters) {
         step(Rb, Ra, it);
 #pragma unroll
         for (int ft = 0; ft < FT; ++ft) X[ft] += bl * Rb[ft];
@@ -626,6 +584,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
     // Instruction groups: (1) U0hat and K fragment reads, the split of X; (2) the K products
     // and the V^T fragment reads; (3) the U0hat products; (4) the V^T products and the stores.
     lds_barrier();  // U0hat is staged
+    load_kv(ch + 1);
     refresh();
     {
 #pragma unroll
@@ -684,19 +643,20 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
       for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
         for (int ft = 0; ft < FT; ++ft) y[ft] = M::mma(vq[kc][ft], pf[kc], y[ft]);
+      // o of the own token straight from the accumulators: 8 bytes per lane, 32 per token row
+      // and tile
+      // (bounds-checked: the stores of tokens past the end are dropped)
+      const auto ro = buffer_rsrc(og + (b * (long long)Tlen + t0) * tok_stride + (long long)h * D,
+                                  (uint32_t)(nv - 1) * tok_bytes + D * 2u);
+      const uint32_t ooff = (uint32_t)t * tok_bytes + (uint32_t)lg * 8u;
 #pragma unroll
       for (int ft = 0; ft < FT; ++ft) {
-        bf16x4 ov = {(bf16)y[ft][0], (bf16)y[ft][1], (bf16)y[ft][2], (bf16)y[ft][3]};
-        *reinterpret_cast<bf16x4*>(Ob + t * LDD + 16 * ft + 4 * lg) = ov;
+        const bf16x4 ov = {(bf16)y[ft][0], (bf16)y[ft][1], (bf16)y[ft][2], (bf16)y[ft][3]};
+        buffer_store8(ov, ro, ooff + 32u * ft);
       }
     }
-    pend_t0 = t0;
-    pend_nv = nv;
     n0sq = n2last;
   }
-
-  lds_barrier();  // the last chunk's output tile is staged
-  flush_o();
   if (A.out_h && seg == S - 1) {
     float* oh = A.out_h + (size_t)bh * D * D;
     float* ou = A.out_u + (size_t)bh * D * D;
@@ -815,7 +775,7 @@ __global__ __launch_bounds__(1024) void summary_tok_kernel(WalkArgs A, int B, in
         const bool isv = j >= NI;
         const int qq = isv ? j - NI : j;
         const int u = qq * kWave + lane;
-        const int tt = u / UPR, cu = u % UPR;
+        const int tt = (uint32_t)u / UPR, cu = (uint32_t)u % UPR;  // u >= 0
         const uint32_t lb = __builtin_amdgcn_readfirstlane(
             (uint32_t)(uintptr_t)(lds_void*)((isv ? buf_v(slot) : buf_k(slot)) + qq * kWave * Cfg::VEC));
         const uint32_t off = (uint32_t)(tt * (int)tok_stride + cu * Cfg::VEC) * 2u;  // bytes
@@ -991,7 +951,10 @@ hipError_t launch_tok(const FwdPlan& pl, const WalkArgs& a, const ChebConsts& cc
 }  // namespace
 
 bool walk_tok_supported(const FwdPlan& pl) {
-  return pl.dtype == 0 && pl.C == 64 && (pl.D == 32 || pl.D == 64 || pl.D == 128);
+  // per-lane byte offsets within a chunk of 64 token rows are 32-bit
+  const long long chunk_bytes = 64LL * pl.H * pl.D * 2;
+  return pl.dtype == 0 && pl.C == 64 && (pl.D == 32 || pl.D == 64 || pl.D == 128) &&
+         chunk_bytes < (1LL << 31);
 }
 
 bool summary_tok_supported(const FwdPlan& pl) {
