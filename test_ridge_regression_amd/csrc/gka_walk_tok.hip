@@ -56,9 +56,9 @@ struct TokCfg {
   static constexpr size_t oVp = oKp + szTok;     // V, token-major (fp16)
   static constexpr size_t oHs = oVp + szTok;     // H0hat, then U0hat: row-major, permuted columns
   static constexpr int LDC = C + 8;              // row stride of the [D][C] fp16 tile
-  static constexpr size_t oKT = oHs + szHs;      // K^T: row-major, tokens permuted (fp16)
-  static constexpr size_t oVT = oKT + (size_t)D * LDC * 2;  // V^T, likewise
-  static constexpr size_t oVec = oVT + (size_t)D * LDC * 2;
+  static constexpr size_t oVT = oHs + szHs;      // V^T: row-major, tokens permuted (fp16)
+  static constexpr size_t oUs = oVT + (size_t)D * LDC * 2;  // float32 U^T state, tile-major
+  static constexpr size_t oVec = oUs + (size_t)D * D * sizeof(float);
   static constexpr size_t szVec = (size_t)(4 * C + 16 + 4 * 64) * sizeof(float);
   static constexpr size_t bytes = oVec + szVec;  // dynamic LDS
   static_assert(D % 32 == 0 && NST >= 1, "unsupported D");
@@ -121,8 +121,8 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
   f16* Kp = reinterpret_cast<f16*>(smem + Cfg::oKp);
   f16* Vp = reinterpret_cast<f16*>(smem + Cfg::oVp);
   f16* Hs = reinterpret_cast<f16*>(smem + Cfg::oHs);
-  f16* KT = reinterpret_cast<f16*>(smem + Cfg::oKT);
   f16* VT = reinterpret_cast<f16*>(smem + Cfg::oVT);
+  float* Us = reinterpret_cast<float*>(smem + Cfg::oUs);
   float* v_cl = reinterpret_cast<float*>(smem + Cfg::oVec);  // [C] in-chunk log2 gate prefix
   float* v_w = v_cl + C;    // [C] carry weights 2^(cl_C - cl_s)
   float* v_a = v_w + C;     // [C] n^2 scan: a_t = gamma_t^2
@@ -155,14 +155,19 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
   const bf16* vg = static_cast<const bf16*>(A.v);
   bf16* og = static_cast<bf16*>(A.o);
 
-  // ---- float32 state: tiles (a0 + jr, b0 + jc) of H and of U^T (rows = key features) -------
-  f32x4 Hst[NRT][NCT], Ust[NRT][NCT];
+  // ---- float32 state: tiles (a0 + jr, b0 + jc) of H and of U^T (rows = key features). H is
+  // held in registers; U^T in LDS, where each wave only ever touches its own tiles (one f32x4
+  // per lane and tile, tile-major), which frees the registers for resident K^T fragments ------
+  auto us_tile = [&](int jr, int jc) {
+    return reinterpret_cast<f32x4*>(Us) + ((jr * NCT + jc) * NW + wave) * kWave + lane;
+  };
+  f32x4 Hst[NRT][NCT];
 #pragma unroll
   for (int jr = 0; jr < NRT; ++jr)
 #pragma unroll
     for (int jc = 0; jc < NCT; ++jc) {
       Hst[jr][jc] = f32x4{0.f, 0.f, 0.f, 0.f};
-      Ust[jr][jc] = f32x4{0.f, 0.f, 0.f, 0.f};
+      *us_tile(jr, jc) = f32x4{0.f, 0.f, 0.f, 0.f};
     }
   float n0sq = 0.0f;
   {
@@ -177,7 +182,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
           // H[r..r+3][c] is read as H[c][r..r+3] (symmetric); U^T[r..r+3][c] = U[c][r..r+3]
           const size_t o = (size_t)(16 * (b0 + jc) + lr) * D + 16 * (a0 + jr) + 4 * lg;
           Hst[jr][jc] = *reinterpret_cast<const f32x4*>(ih + o);
-          Ust[jr][jc] = *reinterpret_cast<const f32x4*>(iu + o);
+          *us_tile(jr, jc) = *reinterpret_cast<const f32x4*>(iu + o);
           const f32x4 x = Hst[jr][jc];
           sq += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
         }
@@ -231,24 +236,36 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
     gin = buffer_load4f(rg, (uint32_t)lane * Hn * 4u);
   };
   // state tiles (times sc) -> Hs as fp16 rows e = column index of the tile, permuted columns
-  auto stage_state = [&](f32x4(&St)[NRT][NCT], float sc) {
+  auto stage_tile = [&](int jr, int jc, f32x4 x) {
+    f16x4 y = {(f16)x[0], (f16)x[1], (f16)x[2], (f16)x[3]};
+    *reinterpret_cast<f16x4*>(Hs + (16 * (b0 + jc) + lr) * LDD + pcol(16 * (a0 + jr) + 4 * lg)) = y;
+  };
+  auto stage_h = [&](float sc) {
 #pragma unroll
     for (int jr = 0; jr < NRT; ++jr)
 #pragma unroll
-      for (int jc = 0; jc < NCT; ++jc) {
-        const f32x4 x = St[jr][jc] * sc;
-        f16x4 y = {(f16)x[0], (f16)x[1], (f16)x[2], (f16)x[3]};
-        *reinterpret_cast<f16x4*>(Hs + (16 * (b0 + jc) + lr) * LDD + pcol(16 * (a0 + jr) + 4 * lg)) = y;
-      }
+      for (int jc = 0; jc < NCT; ++jc) stage_tile(jr, jc, Hst[jr][jc] * sc);
+  };
+  auto stage_u = [&](float sc) {
+    f32x4 x[NRT][NCT];  // all reads first: one wait covers them
+#pragma unroll
+    for (int jr = 0; jr < NRT; ++jr)
+#pragma unroll
+      for (int jc = 0; jc < NCT; ++jc) x[jr][jc] = *us_tile(jr, jc);
+#pragma unroll
+    for (int jr = 0; jr < NRT; ++jr)
+#pragma unroll
+      for (int jc = 0; jc < NCT; ++jc) stage_tile(jr, jc, x[jr][jc] * sc);
   };
   // A fragment of K (rows = tokens 16 sb + lr) over feature block kk
   auto frag_k = [&](int sb, int kk) {
     return *reinterpret_cast<const Frag*>(Kp + (16 * sb + lr) * LDD + 32 * kk + 8 * lg);
   };
   // A fragment of K^T (V^T) (rows = features 16 ft + lr) over token block kc, permuted token
-  // order (k-slot j of lane group lg: token 32 kc + 16 (j / 4) + 4 lg + j % 4)
+  // order (k-slot j of lane group lg: token 32 kc + 16 (j / 4) + 4 lg + j % 4); K^T by two
+  // transposing reads of K, V^T from its tile
   auto frag_kt = [&](int ft, int kc) {
-    return *reinterpret_cast<const Frag*>(KT + (16 * ft + lr) * LDC + 32 * kc + 8 * lg);
+    return frag_trans<LDD>(Kp, 32 * kc + 4 * lg, 32 * kc + 16 + 4 * lg, pcol(16 * ft + 4 * (lr & 3)), lr);
   };
   auto frag_vt = [&](int ft, int kc) {
     return *reinterpret_cast<const Frag*>(VT + (16 * ft + lr) * LDC + 32 * kc + 8 * lg);
@@ -299,7 +316,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
       *reinterpret_cast<f16x4*>(Kp + tt * LDD + pcol(8 * cu + 4)) = f16x4{ko[4], ko[5], ko[6], ko[7]};
     }
     }
-    stage_state(Hst, n0inv);  // H0hat
+    stage_h(n0inv);  // H0hat
     lds_barrier();
 
     refresh();
@@ -318,22 +335,34 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
         for (int kk = 0; kk < KD; ++kk) keep_in_agpr(Hres[ft][kk]);
     }
 
-    // ---- K^T and V^T with the tokens in the permuted order (fragments from transposing reads
-    // of K and V, written back as rows): every later operand of them is one 16-byte read -----
+    // ---- V^T with the tokens in the permuted order (fragments from transposing reads of V,
+    // written back as rows: every later operand of it is one 16-byte read), and every K^T
+    // fragment of the chunk, resident in registers until the loop ends ----------------------
     refresh();
 #pragma unroll
     for (int k = 0; k < (FT * KC + NW - 1) / NW; ++k) {
       const int phi = wave + k * NW;
       if (FT * KC % NW == 0 || phi < FT * KC) {
         const int ft = phi / KC, kc = phi % KC;
-        const Frag f = frag_trans<LDD>(Kp, 32 * kc + 4 * lg, 32 * kc + 16 + 4 * lg,
-                                       pcol(16 * ft + 4 * (lr & 3)), lr);
         const Frag g = frag_trans<LDD>(Vp, 32 * kc + 4 * lg, 32 * kc + 16 + 4 * lg,
                                        16 * ft + 4 * (lr & 3), lr);
-        *reinterpret_cast<Frag*>(KT + (16 * ft + lr) * LDC + 32 * kc + 8 * lg) = f;
         *reinterpret_cast<Frag*>(VT + (16 * ft + lr) * LDC + 32 * kc + 8 * lg) = g;
       }
     }
+    Frag ktr[KC][FT];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft) {
+        ktr[kc][ft] = frag_kt(ft, kc);
+        if constexpr (Cfg::PIN) keep_in_agpr(ktr[kc][ft]);
+      }
+    // and every K fragment (rows = tokens), resident in vector registers until the output
+    Frag kres[KD][ST];
+#pragma unroll
+    for (int kk = 0; kk < KD; ++kk)
+#pragma unroll
+      for (int sb = 0; sb < ST; ++sb) kres[kk][sb] = frag_k(sb, kk);
 
     // ---- norm phase: k_t^T H0hat k_t and sum_{s<t} 2^(cl_{t-1} - cl_s) G_st^2 ---------------
     {
@@ -356,7 +385,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
       for (int sb = 0; sb < ST; ++sb) {
         f32x4 gacc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < KD; ++kk) gacc = M::mma(frag_k(sb, kk), kb[kk], gacc);
+        for (int kk = 0; kk < KD; ++kk) gacc = M::mma(kres[kk][sb], kb[kk], gacc);
         const f32x4 cls = *reinterpret_cast<const f32x4*>(v_cl + 16 * sb + 4 * lg);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -404,7 +433,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
         Mh[sb][i] = s <= t ? fast_exp2(fminf(cl_t - cls[i], 0.0f)) * ninv_t : 0.0f;
       }
     }
-    stage_state(Ust, n0inv);  // U0hat (every wave has read its H0hat fragments)
+    stage_u(n0inv);  // U0hat (every wave has read its H0hat fragments)
 
     // ---- queries of the own token, accumulator layout: Q[t][16 ft + 4 lg .. + 3], loaded
     // during the carry's products and consumed at the start of the loop ----------------------
@@ -438,7 +467,9 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
         }
       }
       // column operands in groups of two column tiles, double-buffered: the next group's
-      // reads are in flight during the current group's products
+      // reads are in flight during the current group's products. The K operands of column
+      // tile bc are the resident K^T fragments of feature tile bc (K[s][16 bc + lr], the same
+      // token slots) when the wave's column tiles are all of them (b0 = 0), else read again.
       constexpr int CG = NCT >= 2 ? 2 : 1, NG = NCT / CG;
       Frag bk[2][CG][KC], bv[2][CG][KC];
       auto load_group = [&](int g, int buf) {
@@ -446,7 +477,11 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
         for (int j = 0; j < CG; ++j)
 #pragma unroll
           for (int kc = 0; kc < KC; ++kc) {
-            bk[buf][j][kc] = frag_kt(b0 + g * CG + j, kc);  // K[s][16 bc + lr], same token slots
+            if constexpr (NCT == FT) {
+              bk[buf][j][kc] = ktr[kc][g * CG + j];
+            } else {
+              bk[buf][j][kc] = frag_kt(b0 + g * CG + j, kc);
+            }
             bv[buf][j][kc] = frag_vt(b0 + g * CG + j, kc);
           }
       };
@@ -460,7 +495,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
 #pragma unroll
           for (int jr = 0; jr < NRT; ++jr) {
             const int jc = g * CG + j;
-            f32x4 hacc = Hst[jr][jc] * gC, uacc = Ust[jr][jc] * gC;
+            f32x4 hacc = Hst[jr][jc] * gC, uacc = *us_tile(jr, jc) * gC;
 #pragma unroll
             for (int kc = 0; kc < KC; ++kc) {
               hacc = M::mma(awh[jr][kc], bk[g % 2][j][kc], hacc);
@@ -469,11 +504,8 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
               uacc = M::mma(awl[jr][kc], bv[g % 2][j][kc], uacc);
             }
             Hst[jr][jc] = hacc;
-            Ust[jr][jc] = uacc;
-            if constexpr (Cfg::PIN) {
-              keep_in_agpr(Hst[jr][jc]);
-              keep_in_agpr(Ust[jr][jc]);
-            }
+            *us_tile(jr, jc) = uacc;
+            if constexpr (Cfg::PIN) keep_in_agpr(Hst[jr][jc]);
           }
         __builtin_amdgcn_sched_barrier(0);
       }
@@ -499,30 +531,11 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
     // group: (A) the K products P = K Rc^T and the recurrence start; (B) the H0hat products on
     // the scaled operands and the P' operands; (C) the K^T products, the X update and the
     // next step's first K fragments. With one wave per SIMD nothing else hides latency.
-    constexpr int KN = KD < 2 ? KD : 2;  // K fragment blocks read ahead of a step
-    Frag kn[KN][ST];
-    auto load_kn = [&]() {
-#pragma unroll
-      for (int kk = 0; kk < KN; ++kk)
-#pragma unroll
-        for (int sb = 0; sb < ST; ++sb) kn[kk][sb] = frag_k(sb, kk);
-    };
     auto step = [&](f32x4(&Ro)[FT], f32x4(&Rc)[FT], int it) {
-      // K and K^T fragments are read from LDS in every iteration: without this the compiler
-      // hoists them out of the loop as invariant loads and runs out of registers
-      asm volatile("" ::: "memory");
       const f32x4 cf = *reinterpret_cast<const f32x4*>(v_coef + 4 * it);  // krs, kys, bts
-      Frag rf[KD], rs[KD], kq[KD][ST], kt[KC][FT], pf[KC];
+      Frag rf[KD], rs[KD], pf[KC];
       f32x4 pa[ST];
       // (A)
-#pragma unroll
-      for (int kk = KN; kk < KD; ++kk)
-#pragma unroll
-        for (int sb = 0; sb < ST; ++sb) kq[kk][sb] = frag_k(sb, kk);
-#pragma unroll
-      for (int kk = 0; kk < KN; ++kk)
-#pragma unroll
-        for (int sb = 0; sb < ST; ++sb) kq[kk][sb] = kn[kk][sb];
 #pragma unroll
       for (int kk = 0; kk < KD; ++kk) rf[kk] = pack8(Rc[2 * kk], Rc[2 * kk + 1]);
 #pragma unroll
@@ -530,17 +543,13 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
 #pragma unroll
       for (int kk = 0; kk < KD; ++kk)
 #pragma unroll
-        for (int sb = 0; sb < ST; ++sb) pa[sb] = M::mma(kq[kk][sb], rf[kk], pa[sb]);
+        for (int sb = 0; sb < ST; ++sb) pa[sb] = M::mma(kres[kk][sb], rf[kk], pa[sb]);
       const float kys = cf[1] * s_t;
       rs[0] = pack8(Rc[0] * kys, Rc[1] * kys);
 #pragma unroll
       for (int ft = 0; ft < FT; ++ft) Ro[ft] = Ro[ft] + cf[0] * Rc[ft];
       __builtin_amdgcn_sched_barrier(0);
       // (B)
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc)
-#pragma unroll
-        for (int ft = 0; ft < FT; ++ft) kt[kc][ft] = frag_kt(ft, kc);
 #pragma unroll
       for (int kk = 1; kk < KD; ++kk) rs[kk] = pack8(Rc[2 * kk] * kys, Rc[2 * kk + 1] * kys);
 #pragma unroll
@@ -555,14 +564,12 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
-        for (int ft = 0; ft < FT; ++ft) Ro[ft] = M::mma(kt[kc][ft], pf[kc], Ro[ft]);
+        for (int ft = 0; ft < FT; ++ft) Ro[ft] = M::mma(ktr[kc][ft], pf[kc], Ro[ft]);
 #pragma unroll
       for (int ft = 0; ft < FT; ++ft) X[ft] += cf[2] * Rc[ft];
-      load_kn();
       __builtin_amdgcn_sched_barrier(0);
     };
     {
-      load_kn();
       int it = 0;
       const int iters = cc.iters_rs;
       for (; it + 2 < iters; it += 2) {
@@ -594,11 +601,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
           Hres[ft][kk] = *reinterpret_cast<const Frag*>(Hs + (16 * ft + lr) * LDD + 32 * kk + 8 * lg);
           if constexpr (Cfg::PIN) keep_in_agpr(Hres[ft][kk]);
         }
-      Frag kq[KD][ST], vq[KC][FT], xh[KD], xl[KD], pf[KC];
-#pragma unroll
-      for (int kk = 0; kk < KD; ++kk)
-#pragma unroll
-        for (int sb = 0; sb < ST; ++sb) kq[kk][sb] = frag_k(sb, kk);
+      Frag vq[KC][FT], xh[KD], xl[KD], pf[KC];
 #pragma unroll
       for (int kk = 0; kk < KD; ++kk) {
         xh[kk] = pack8(X[2 * kk], X[2 * kk + 1]);
@@ -616,8 +619,8 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
       for (int kk = 0; kk < KD; ++kk)
 #pragma unroll
         for (int sb = 0; sb < ST; ++sb) {
-          pa[sb] = M::mma(kq[kk][sb], xh[kk], pa[sb]);
-          pa[sb] = M::mma(kq[kk][sb], xl[kk], pa[sb]);
+          pa[sb] = M::mma(kres[kk][sb], xh[kk], pa[sb]);
+          pa[sb] = M::mma(kres[kk][sb], xl[kk], pa[sb]);
         }
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc)
@@ -666,7 +669,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
       for (int jc = 0; jc < NCT; ++jc) {
         const size_t o = (size_t)(16 * (b0 + jc) + lr) * D + 16 * (a0 + jr) + 4 * lg;
         *reinterpret_cast<f32x4*>(oh + o) = Hst[jr][jc];
-        *reinterpret_cast<f32x4*>(ou + o) = Ust[jr][jc];
+        *reinterpret_cast<f32x4*>(ou + o) = *us_tile(jr, jc);
       }
   }
   if (A.n2_out && seg == S - 1 && tid == 0) A.n2_out[bh] = n0sq;
