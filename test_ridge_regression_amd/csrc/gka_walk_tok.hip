@@ -679,250 +679,220 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
 // For each (segment, head): the state reached from a zero state over the segment's tokens and
 // the segment's total log2 gate. Unrolling the carry H <- Gam_C H + K^T diag(w) K over the
 // segment gives one weighted sum over its tokens,
-//   dH = sum_s w_s k_s k_s^T,  dU^T = sum_s w_s k_s v_s^T,  w_s = 2^(log2 of the gates after s),
-// so the tokens are taken in blocks of 32 from the last block to the first, with the gate sum
+//   dH = sum_s w_s k_s k_s^T,  dU = sum_s w_s v_s k_s^T,  w_s = 2^(log2 of the gates after s),
+// so the tokens are taken in blocks of 64 from the last block to the first, with the gate sum
 // of the blocks already taken as the suffix of every weight, and no rescaling of the state.
 // Matrix-core operands are bf16: K and V exactly, the weighted keys w k as a hi + lo pair
-// (about 2^-17 relative). Sixteen waves in two roles, two waves of each per SIMD:
-//  * waves 0..7 hold the float32 state (wave w: row tiles RT*(w % 4).., column tiles
-//    CT*(w / 4).. of dH and dU^T) and only accumulate;
-//  * waves 8..15 load the blocks straight into LDS three ahead, compute the weights and build
-//    the operand tiles K^T, V^T, (w K)^T hi and lo of the next block, as [feature][token] tiles
-//    in the walk's permuted token order (one 16-byte read per fragment).
-// The tiles are double-buffered: each phase builds block p + 1 while block p is accumulated,
-// so the vector work of one role overlaps the matrix-core work of the other, behind one
-// barrier per phase. The roles run separate loops with the same barriers.
+// (about 2^-17 relative). Eight waves, two per SIMD; wave w holds the float32 tiles (row tiles
+// RT*(w % 2).., column tiles CT*(w / 2)..) of dH and of dU (rows = value features), computed as
+// dH = K^T diag(w) K and dU = V^T diag(w) K, so that both take the weighted keys of the wave's
+// column tiles as their second operand (weighted by the two waves that share those tiles).
+// Per block every wave reads its own operand fragments with transposing reads of the block's
+// K and V rows in LDS (bf16, padded rows), in the walk's permuted token order; the block's
+// weights were computed one block earlier, from its gates in registers. The rows of
+// the next block go to the other of two LDS slots, from registers loaded two blocks ahead with
+// bounds-checked buffer loads (rows past the end read as 0): one barrier per block.
 template <int D>
 struct SumCfg {
-  static constexpr int CB = 32;                // tokens per block
-  static constexpr int NA = 8;                 // accumulating waves
-  static constexpr int NBW = 8;                // building waves
-  static constexpr int NT = (NA + NBW) * kWave;
+  static constexpr int CB = 64;                // tokens per block (a chunk)
+  static constexpr int KB = CB / 32;           // 32-deep token blocks per block
+  static constexpr int NW = 8;                 // waves, two per SIMD
+  static constexpr int NT = NW * kWave;
   static constexpr int FT = D / 16;
-  static constexpr int RT = FT / 4;            // state row tiles per accumulating wave
-  static constexpr int CT = FT / 2;            // state column tiles per accumulating wave
-  static constexpr int LDC = CB + 8;
+  static constexpr int RT = FT / 2;            // state row tiles per wave (more rows than
+  static constexpr int CT = FT / 4;            // columns: fewer operand fragments per product)
+  static constexpr int LDR = D + 8;            // row stride of a block's K or V rows (bf16)
   static constexpr int VEC = 8, UPR = D / VEC, NU = CB * UPR;
-  static constexpr int NI = NU / kWave;        // direct-load instructions per matrix and block
-  static constexpr int NPW = 2 * NI / NBW;     // K and V direct loads per building wave per block
-  static constexpr int NBUF = 4;               // block buffers of direct loads
-  static constexpr size_t szT = (size_t)D * LDC * 2;
-  static constexpr size_t szSet = 4 * szT;     // K^T, V^T, (w K)^T hi, lo of one block
-  static constexpr size_t bytes = 2 * szSet + (size_t)NBW * CB * sizeof(float);  // + weights
-  static constexpr size_t szBuf = 2 * (size_t)NU * 16 + CB * sizeof(float);
-  static constexpr int FPB = (FT + NBW - 1) / NBW;  // operand fragments per building wave
+  static constexpr int NUT = (NU + NT - 1) / NT;  // 16-byte units per thread and matrix
+  static constexpr size_t szRows = (size_t)CB * LDR * 2;
+  static constexpr size_t szSlot = 2 * szRows;  // K rows, V rows
+  static constexpr size_t bytes = 2 * szSlot + 2 * (size_t)NW * CB * sizeof(float);  // + weights
   static_assert(D == 64 || D == 128, "summary tiling");
-  static_assert((2 * NI) % NBW == 0 && NPW >= 1 && 2 * NPW <= 15, "direct loads per wave");
-  static_assert(bytes + NBUF * szBuf <= 160 * 1024, "LDS budget of one CU exceeded");
-  static_assert(NBUF == 4, "the waits below count the blocks in flight for four buffers");
+  static_assert(bytes <= 160 * 1024, "LDS budget of one CU exceeded");
 };
 
+// fragment of M^T for rows M[s][*] (bf16, row stride LDR) in the permuted token order: two
+// transposing 8-byte reads (lane layout as in frag_trans)
+template <int LDR>
+__device__ inline bf16x8 frag_trans_bf16(const bf16* base, int s0, int s1, int coff, int lr) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(3))) fp16x4_t lds_fp16x4;
+  const int r = lr >> 2;
+  const fp16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)(base + (s0 + r) * LDR + coff));
+  const fp16x4_t y = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)(base + (s1 + r) * LDR + coff));
+  const bf16x4 bx = __builtin_bit_cast(bf16x4, x), by = __builtin_bit_cast(bf16x4, y);
+  return bf16x8{bx[0], bx[1], bx[2], bx[3], by[0], by[1], by[2], by[3]};
+#else
+  return bf16x8{};
+#endif
+}
+
 template <int D>
-__global__ __launch_bounds__(1024) void summary_tok_kernel(WalkArgs A, int B, int Tlen, int Hn,
-                                                           int N, int S, int J) {
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void summary_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J) {
   using Cfg = SumCfg<D>;
   using M = Mma<bf16>;
   typedef bf16x8 Frag;
-  constexpr int CB = Cfg::CB, NA = Cfg::NA, NBW = Cfg::NBW, FT = Cfg::FT, RT = Cfg::RT;
-  constexpr int CT = Cfg::CT, LDC = Cfg::LDC, UPR = Cfg::UPR, NU = Cfg::NU, NI = Cfg::NI;
-  constexpr int NBUF = Cfg::NBUF;
+  constexpr int CB = Cfg::CB, NT = Cfg::NT, RT = Cfg::RT, CT = Cfg::CT, LDR = Cfg::LDR;
+  constexpr int UPR = Cfg::UPR, NU = Cfg::NU, NUT = Cfg::NUT;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
-  auto tile = [&](int set, int which) {  // which: 0 K^T, 1 V^T, 2 (w K)^T hi, 3 lo
-    return reinterpret_cast<bf16*>(smem + set * Cfg::szSet + which * Cfg::szT);
-  };
-  __shared__ __attribute__((aligned(16))) unsigned char pre_buf[NBUF * Cfg::szBuf];
+  auto krows = [&](int slot) { return reinterpret_cast<bf16*>(smem + slot * Cfg::szSlot); };
+  auto vrows = [&](int slot) { return krows(slot) + CB * LDR; };
 
   const int seg = blockIdx.x;
   const int bh = blockIdx.y;
   const int b = bh / Hn, h = bh % Hn;
-  // the role is uniform per wave (a scalar branch)
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
-  int lane = threadIdx.x % kWave;
+  int tid = threadIdx.x, lane = tid % kWave;
   int lr = lane % 16, lg = lane / 16;
-  auto refresh = [&]() { asm volatile("" : "+v"(lane), "+v"(lr), "+v"(lg)); };
-  // the segment's tokens [t_begin, t_end) in blocks of CB, block 0 being the last one
-  const int t_begin = seg * J * (2 * CB);
-  const int t_end = min(Tlen, t_begin + J * 2 * CB);
+  auto refresh = [&]() { asm volatile("" : "+v"(tid), "+v"(lane), "+v"(lr), "+v"(lg)); };
+  // the wave's weights of two blocks (block p in half p % 2)
+  float* v_wl = reinterpret_cast<float*>(smem + 2 * Cfg::szSlot) + wave * 2 * CB;
+  const int a0 = RT * (wave % 2), b0 = CT * (wave / 2);
+  // the segment's tokens [t_begin, t_end) in blocks of CB (= the chunk), block 0 the last one
+  const int t_begin = seg * J * CB;
+  const int t_end = min(Tlen, t_begin + J * CB);
   const int NB = (t_end - t_begin + CB - 1) / CB;
+  const long long tok_stride = (long long)Hn * D;
+  const uint32_t tok_bytes = (uint32_t)Hn * D * 2u;
+  auto block_t0 = [&](int p) { return t_begin + (NB - 1 - p) * CB; };
 
-  if (wave >= NA) {
-    // ================================ building waves ================================
-    const int bw = wave - NA;
-    const long long tok_stride = (long long)Hn * D;
-    auto block_t0 = [&](int p) { return t_begin + (NB - 1 - p) * CB; };
-    auto buf_k = [&](int slot) { return reinterpret_cast<bf16*>(pre_buf + slot * Cfg::szBuf); };
-    auto buf_v = [&](int slot) { return buf_k(slot) + NU * Cfg::VEC; };
-    auto buf_g = [&](int slot) {
-      return reinterpret_cast<float*>(pre_buf + slot * Cfg::szBuf + 2 * (size_t)NU * 16);
-    };
-    // direct loads of block p into buffer p % NBUF: the gates first (the first building wave),
-    // then this wave's share of the units of K and V (jobs j = bw + NBW k: K units, then V)
-    auto prefetch = [&](int p) {
-#if defined(__HIP_DEVICE_COMPILE__)
-      if (p >= NB) return;
-      refresh();
-      typedef __attribute__((address_space(3))) void lds_void;
-      const int slot = p % NBUF;
-      const int t0n = block_t0(p);
-      const int nvn = min(CB, t_end - t0n);
-      if (bw == 0) {
-        const uint32_t gb = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)buf_g(slot));
-        if (lane < nvn) dma_load4(A.gamma + (b * (long long)Tlen + t0n + lane) * Hn + h, gb);
-      }
-      const long long row0 = (b * (long long)Tlen + t0n) * tok_stride + (long long)h * D;
-      const bf16* kb0 = static_cast<const bf16*>(A.k) + row0;
-      const bf16* vb0 = static_cast<const bf16*>(A.v) + row0;
+  // rows of two blocks in registers (register set q holds block p with p % 2 == q)
+  bf16x8 kr[2][NUT], vr[2][NUT];
+  float gr[2];
+  auto load_block = [&](int p, int q) {
+    refresh();
+    const int pv = p < NB ? p : NB - 1;
+    const int t0n = block_t0(pv);
+    const int nvn = p < NB ? min(CB, t_end - t0n) : 0;
+    const long long row0 = (b * (long long)Tlen + t0n) * tok_stride + (long long)h * D;
+    const uint32_t valid = nvn > 0 ? (uint32_t)(nvn - 1) * tok_bytes + D * 2u : 0u;
+    const auto rk = buffer_rsrc(static_cast<const bf16*>(A.k) + row0, valid);
+    const auto rv = buffer_rsrc(static_cast<const bf16*>(A.v) + row0, valid);
 #pragma unroll
-      for (int k = 0; k < Cfg::NPW; ++k) {
-        const int j = bw + k * NBW;
-        const bool isv = j >= NI;
-        const int qq = isv ? j - NI : j;
-        const int u = qq * kWave + lane;
-        const int tt = (uint32_t)u / UPR, cu = (uint32_t)u % UPR;  // u >= 0
-        const uint32_t lb = __builtin_amdgcn_readfirstlane(
-            (uint32_t)(uintptr_t)(lds_void*)((isv ? buf_v(slot) : buf_k(slot)) + qq * kWave * Cfg::VEC));
-        const uint32_t off = (uint32_t)(tt * (int)tok_stride + cu * Cfg::VEC) * 2u;  // bytes
-        if (tt < nvn) dma_load16_so(isv ? vb0 : kb0, off, lb);
-      }
-#endif
-    };
-    // wait until block p's direct loads of this wave have landed, while the loads of blocks
-    // p + 1 .. p + issued (at most) were issued after them: loads retire in order, so those may
-    // stay outstanding (the first building wave issues one more per block, its gates, which this
-    // over-waits)
-    auto wait_block = [&](int p, int issued) {
-      const int ahead = min(NB - 1 - p, issued);
-      if (ahead >= 2) {
-        constexpr int n = 2 * Cfg::NPW;
-        __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
-      } else if (ahead == 1) {
-        constexpr int n = Cfg::NPW;
-        __builtin_amdgcn_s_waitcnt((n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8));
-      } else {
-        __builtin_amdgcn_s_waitcnt(0);
-      }
-    };
-    // operand tiles of block p into tile set p % 2: fragments ft = bw + NBW i (feature tiles),
-    // k-slot j of lane group lg = token 16 (j / 4) + 4 lg + j % 4 of the block; tokens past the
-    // end give zeros. The weights come from a scan over the block (lane = token).
-    float suffix = 0.0f;  // log2 gate sum of the blocks already taken (the later ones)
-    float* v_wl = reinterpret_cast<float*>(smem + 2 * Cfg::szSet) + bw * CB;
-    auto build = [&](int p) {
-      const int slot = p % NBUF, set = p & 1;
-      const int nv = min(CB, t_end - block_t0(p));
-      const float l2 = lane < nv ? log2_gate(buf_g(slot)[lane % CB]) : 0.0f;
-      const float cl = scan_add<CB>(lane < CB ? l2 : 0.0f);
-      const float clast = lane_value(cl, CB - 1);
-      if (lane < CB) v_wl[lane] = fast_exp2(fminf(clast - cl + suffix, 0.0f));
-      suffix += clast;
-#pragma unroll
-      for (int i = 0; i < Cfg::FPB; ++i) {
-        const int ft = bw + NBW * i;
-        if (FT % NBW != 0 && ft >= FT) break;
-        const int s0 = 4 * lg, s1 = s0 + 16;
-        const int r = lr >> 2, coff = 16 * ft + 4 * (lr & 3);
-        bf16x4 k0, k1, u0, u1;
-#if defined(__HIP_DEVICE_COMPILE__)
-        typedef __attribute__((address_space(3))) fp16x4_t lds_fp16x4;
-        const bf16* bk_ = buf_k(slot);
-        const bf16* bv_ = buf_v(slot);
-        k0 = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)(bk_ + (s0 + r) * D + coff)));
-        k1 = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)(bk_ + (s1 + r) * D + coff)));
-        u0 = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)(bv_ + (s0 + r) * D + coff)));
-        u1 = __builtin_bit_cast(bf16x4, __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)(bv_ + (s1 + r) * D + coff)));
-#else
-        k0 = k1 = u0 = u1 = bf16x4{};
-#endif
-        const f32x4 w0 = *reinterpret_cast<const f32x4*>(v_wl + s0);
-        const f32x4 w1 = *reinterpret_cast<const f32x4*>(v_wl + s1);
-        Frag f, g, wh, wlo;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const bool ok = (j < 4 ? s0 : s1) + (j & 3) < nv;
-          const bf16 zero = (bf16)0.0f;
-          f[j] = ok ? (j < 4 ? k0[j] : k1[j - 4]) : zero;
-          g[j] = ok ? (j < 4 ? u0[j] : u1[j - 4]) : zero;
-          const float xw = (float)f[j] * (j < 4 ? w0[j] : w1[j - 4]);
-          wh[j] = (bf16)xw;
-          wlo[j] = (bf16)(xw - (float)wh[j]);
-        }
-        const int o = (16 * ft + lr) * LDC + 8 * lg;
-        *reinterpret_cast<Frag*>(tile(set, 0) + o) = f;
-        *reinterpret_cast<Frag*>(tile(set, 1) + o) = g;
-        *reinterpret_cast<Frag*>(tile(set, 2) + o) = wh;
-        *reinterpret_cast<Frag*>(tile(set, 3) + o) = wlo;
-      }
-    };
-
-    // phase p builds block p + 1 while block p is accumulated; block p + NBUF - 1 is loaded
-    // during phase p into the buffer that block p - 1 has left
-#pragma unroll
-    for (int p = 0; p < NBUF - 1; ++p) prefetch(p);
-    wait_block(0, NBUF - 2);  // blocks 1 .. NBUF - 2 were issued after block 0
-    lds_barrier();
-    build(0);
-    for (int p = 0; p < NB; ++p) {
-      refresh();
-      if (p + 1 < NB) wait_block(p + 1, NBUF - 3);  // block p + 2 was issued after it
-      // block p's tiles are built and block p + 1's loads have landed (every wave); block
-      // p - 1's tiles have been read. This barrier leaves later direct loads in flight.
-      lds_barrier();
-      prefetch(p + NBUF - 1);
-      if (p + 1 < NB) build(p + 1);
+    for (int k = 0; k < NUT; ++k) {
+      const int u = (tid + k * NT) % NU;  // (threads past NU repeat a unit; never written)
+      const int tt = (uint32_t)u / UPR, cu = (uint32_t)u % UPR;  // u >= 0
+      const uint32_t off = (uint32_t)tt * tok_bytes + (uint32_t)cu * 16u;
+      kr[q][k] = buffer_load16<bf16x8>(rk, off);
+      vr[q][k] = buffer_load16<bf16x8>(rv, off);
     }
-    if (bw == 0 && lane == 0) A.log2g_out[(long long)bh * S + seg] = suffix;
-  } else {
-    // =============================== accumulating waves ===============================
-    const int a0 = RT * (wave % 4), b0 = CT * (wave / 4);
-    f32x4 Hst[RT][CT], Ust[RT][CT];
+    const auto rg = buffer_rsrc(A.gamma + (b * (long long)Tlen + t0n) * Hn + h,
+                                nvn > 0 ? (uint32_t)(nvn - 1) * Hn * 4u + 4u : 0u);
+    gr[q] = buffer_load4f(rg, (uint32_t)lane * Hn * 4u);
+  };
+  auto write_block = [&](int slot, int q) {
+    refresh();
 #pragma unroll
-    for (int jr = 0; jr < RT; ++jr)
-#pragma unroll
-      for (int jc = 0; jc < CT; ++jc) {
-        Hst[jr][jc] = f32x4{0.f, 0.f, 0.f, 0.f};
-        Ust[jr][jc] = f32x4{0.f, 0.f, 0.f, 0.f};
+    for (int k = 0; k < NUT; ++k) {
+      const int u = tid + k * NT;
+      if (NU % NT == 0 || u < NU) {
+        const int tt = (uint32_t)u / UPR, cu = (uint32_t)u % UPR;  // u >= 0
+        *reinterpret_cast<bf16x8*>(krows(slot) + tt * LDR + cu * 8) = kr[q][k];
+        *reinterpret_cast<bf16x8*>(vrows(slot) + tt * LDR + cu * 8) = vr[q][k];
       }
-    lds_barrier();  // (the building waves' first barrier)
-    for (int p = 0; p < NB; ++p) {
-      refresh();
-      lds_barrier();  // block p's tiles are built
-      const int set = p & 1;
-      auto frag = [&](int which, int ft) {
-        return *reinterpret_cast<const Frag*>(tile(set, which) + (16 * ft + lr) * LDC + 8 * lg);
-      };
-      Frag aw[RT], al[RT], bk[CT], bv[CT];
+    }
+  };
+
+  f32x4 Hst[RT][CT], Ust[RT][CT];
+#pragma unroll
+  for (int jr = 0; jr < RT; ++jr)
+#pragma unroll
+    for (int jc = 0; jc < CT; ++jc) {
+      Hst[jr][jc] = f32x4{0.f, 0.f, 0.f, 0.f};
+      Ust[jr][jc] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+  float suffix = 0.0f;  // log2 gate sum of the blocks already weighted (the later ones)
+
+  // weights of block p (lane = token), from its gates in register set q, one phase before
+  // its products: 2^(log2 of the gates after the token)
+  auto weigh = [&](int p, int q) {
+    const int nv = p < NB ? min(CB, t_end - block_t0(p)) : 0;
+    const float l2 = lane < nv ? log2_gate(gr[q]) : 0.0f;
+    const float cl = scan_add<kWave>(l2);
+    const float clast = lane_value(cl, CB - 1);
+    v_wl[(p & 1) * CB + lane] = fast_exp2(fminf(clast - cl + suffix, 0.0f));
+    suffix += clast;
+  };
+  // block p from slot p % 2 into the state
+  auto accumulate = [&](int p) {
+    refresh();
+    const int slot = p & 1;
+    const float* wl = v_wl + (p & 1) * CB;
+    const bf16* kb = krows(slot);
+    const bf16* vb = vrows(slot);
+    const int cq = 4 * (lr & 3);
+#pragma unroll
+    for (int kc = 0; kc < Cfg::KB; ++kc) {
+      const int s0 = 32 * kc + 4 * lg, s1 = s0 + 16;
+      // A operands: K^T and V^T row fragments; B operands: the weighted keys of the column
+      // tiles, hi + lo (shared by the two products: dH = K^T diag(w) K, dU = V^T diag(w) K)
+      Frag ak[RT], av[RT], bh[CT], bl[CT];
 #pragma unroll
       for (int jr = 0; jr < RT; ++jr) {
-        aw[jr] = frag(2, a0 + jr);
-        al[jr] = frag(3, a0 + jr);
+        ak[jr] = frag_trans_bf16<LDR>(kb, s0, s1, 16 * (a0 + jr) + cq, lr);
+        av[jr] = frag_trans_bf16<LDR>(vb, s0, s1, 16 * (a0 + jr) + cq, lr);
       }
+      const f32x4 w0 = *reinterpret_cast<const f32x4*>(wl + s0);
+      const f32x4 w1 = *reinterpret_cast<const f32x4*>(wl + s1);
 #pragma unroll
       for (int jc = 0; jc < CT; ++jc) {
-        bk[jc] = frag(0, b0 + jc);
-        bv[jc] = frag(1, b0 + jc);
+        const Frag f = frag_trans_bf16<LDR>(kb, s0, s1, 16 * (b0 + jc) + cq, lr);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float x = (float)f[j] * (j < 4 ? w0[j] : w1[j - 4]);
+          bh[jc][j] = (bf16)x;
+          bl[jc][j] = (bf16)(x - (float)bh[jc][j]);
+        }
       }
 #pragma unroll
       for (int jc = 0; jc < CT; ++jc)
 #pragma unroll
         for (int jr = 0; jr < RT; ++jr) {
-          Hst[jr][jc] = M::mma(aw[jr], bk[jc], Hst[jr][jc]);
-          Ust[jr][jc] = M::mma(aw[jr], bv[jc], Ust[jr][jc]);
-          Hst[jr][jc] = M::mma(al[jr], bk[jc], Hst[jr][jc]);
-          Ust[jr][jc] = M::mma(al[jr], bv[jc], Ust[jr][jc]);
+          Hst[jr][jc] = M::mma(ak[jr], bh[jc], Hst[jr][jc]);
+          Ust[jr][jc] = M::mma(av[jr], bh[jc], Ust[jr][jc]);
+          Hst[jr][jc] = M::mma(ak[jr], bl[jc], Hst[jr][jc]);
+          Ust[jr][jc] = M::mma(av[jr], bl[jc], Ust[jr][jc]);
         }
     }
-    float* oh = A.sum_h + bh * A.sum_bh + seg * A.sum_seg;
-    float* ou = A.sum_u + bh * A.sum_bh + seg * A.sum_seg;
-#pragma unroll
-    for (int jr = 0; jr < RT; ++jr)
-#pragma unroll
-      for (int jc = 0; jc < CT; ++jc) {
-        // H[r..r+3][c] is written as H[c][r..r+3] (symmetric); U^T[r..r+3][c] = U[c][r..r+3]
-        const size_t o = (size_t)(16 * (b0 + jc) + lr) * D + 16 * (a0 + jr) + 4 * lg;
-        *reinterpret_cast<f32x4*>(oh + o) = Hst[jr][jc];
-        *reinterpret_cast<f32x4*>(ou + o) = Ust[jr][jc];
-      }
+  };
+  // phase p: the rows of block p + 1 (register set (p + 1) % 2) go to slot (p + 1) % 2, that set
+  // is reloaded with block p + 3, and block p is accumulated from slot p % 2
+  auto phase = [&](int p, int q) {
+    if (p + 1 < NB) {
+      write_block(q, q);
+      weigh(p + 1, q);
+      load_block(p + 3, q);
+    }
+    accumulate(p);
+    lds_barrier();  // slot (p + 1) % 2 is written; slot p % 2 is read
+  };
+  load_block(0, 0);
+  load_block(1, 1);
+  write_block(0, 0);
+  weigh(0, 0);
+  load_block(2, 0);
+  lds_barrier();
+  for (int p = 0; p < NB; p += 2) {
+    phase(p, 1);
+    if (p + 1 < NB) phase(p + 1, 0);
   }
+
+  if (wave == 0 && lane == 0) A.log2g_out[(long long)bh * S + seg] = suffix;
+  float* oh = A.sum_h + bh * A.sum_bh + seg * A.sum_seg;
+  float* ou = A.sum_u + bh * A.sum_bh + seg * A.sum_seg;
+#pragma unroll
+  for (int jr = 0; jr < RT; ++jr)
+#pragma unroll
+    for (int jc = 0; jc < CT; ++jc) {
+      // H[r..r+3][c] is written as H[c][r..r+3] (symmetric); the tile of U holds
+      // U[r..r+3][c] (rows = value features), four scattered stores
+      const size_t o = (size_t)(16 * (b0 + jc) + lr) * D + 16 * (a0 + jr) + 4 * lg;
+      *reinterpret_cast<f32x4*>(oh + o) = Hst[jr][jc];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        ou[(size_t)(16 * (a0 + jr) + 4 * lg + i) * D + 16 * (b0 + jc) + lr] = Ust[jr][jc][i];
+    }
 }
 
 template <int D>
@@ -961,8 +931,8 @@ bool walk_tok_supported(const FwdPlan& pl) {
 }
 
 bool summary_tok_supported(const FwdPlan& pl) {
-  // the direct loads address a block of 32 tokens with 32-bit byte offsets per lane
-  const long long block_bytes = 32LL * pl.H * pl.D * 2;
+  // the buffer loads address a block of 64 tokens with 32-bit byte offsets per lane
+  const long long block_bytes = 64LL * pl.H * pl.D * 2;
   return pl.dtype == 0 && pl.C == 64 && (pl.D == 64 || pl.D == 128) && block_bytes < (1LL << 31);
 }
 
