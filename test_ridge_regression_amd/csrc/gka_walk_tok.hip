@@ -30,6 +30,8 @@
 // loaded into registers during the output phase and staged at the top of the next chunk.
 #include "gka_internal.hpp"
 
+#include <type_traits>
+
 namespace gka {
 namespace {
 
@@ -335,29 +337,9 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
         for (int kk = 0; kk < KD; ++kk) keep_in_agpr(Hres[ft][kk]);
     }
 
-    // ---- V^T with the tokens in the permuted order (fragments from transposing reads of V,
-    // written back as rows: every later operand of it is one 16-byte read), and every K^T
-    // fragment of the chunk, resident in registers until the loop ends ----------------------
+    // ---- every K fragment of the chunk (rows = tokens), resident in vector registers until
+    // the output ---------------------------------------------------------------------------------
     refresh();
-#pragma unroll
-    for (int k = 0; k < (FT * KC + NW - 1) / NW; ++k) {
-      const int phi = wave + k * NW;
-      if (FT * KC % NW == 0 || phi < FT * KC) {
-        const int ft = phi / KC, kc = phi % KC;
-        const Frag g = frag_trans<LDD>(Vp, 32 * kc + 4 * lg, 32 * kc + 16 + 4 * lg,
-                                       16 * ft + 4 * (lr & 3), lr);
-        *reinterpret_cast<Frag*>(VT + (16 * ft + lr) * LDC + 32 * kc + 8 * lg) = g;
-      }
-    }
-    Frag ktr[KC][FT];
-#pragma unroll
-    for (int kc = 0; kc < KC; ++kc)
-#pragma unroll
-      for (int ft = 0; ft < FT; ++ft) {
-        ktr[kc][ft] = frag_kt(ft, kc);
-        if constexpr (Cfg::PIN) keep_in_agpr(ktr[kc][ft]);
-      }
-    // and every K fragment (rows = tokens), resident in vector registers until the output
     Frag kres[KD][ST];
 #pragma unroll
     for (int kk = 0; kk < KD; ++kk)
@@ -408,6 +390,29 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
         v_b[t] = 2.0f * gt * ((t > 0 ? gprev : 1.0f) * n0 * pu + pv) + kd * kd;
       }
     }
+    // ---- V^T with the tokens in the permuted order (fragments from transposing reads of V,
+    // written back as rows: every later operand of it is one 16-byte read), and every K^T
+    // fragment of the chunk, resident in registers until the loop ends (after the norm
+    // phase's products, which do not need them) ----------------------------------------------
+    refresh();
+#pragma unroll
+    for (int k = 0; k < (FT * KC + NW - 1) / NW; ++k) {
+      const int phi = wave + k * NW;
+      if (FT * KC % NW == 0 || phi < FT * KC) {
+        const int ft = phi / KC, kc = phi % KC;
+        const Frag g = frag_trans<LDD>(Vp, 32 * kc + 4 * lg, 32 * kc + 16 + 4 * lg,
+                                       16 * ft + 4 * (lr & 3), lr);
+        *reinterpret_cast<Frag*>(VT + (16 * ft + lr) * LDC + 32 * kc + 8 * lg) = g;
+      }
+    }
+    Frag ktr[KC][FT];
+#pragma unroll
+    for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft) {
+        ktr[kc][ft] = frag_kt(ft, kc);
+        if constexpr (Cfg::PIN) keep_in_agpr(ktr[kc][ft]);
+      }
     lds_barrier();
 
     // ---- n_t^2 by an affine scan over the chunk (every wave; lane = token) -------------------
@@ -514,14 +519,11 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
     // ---- Chebyshev loop on the residuals of the own token ----------------------------------
     refresh();
     const bool live = ninv_t > 0.0f;  // ||H_t|| = 0: x_t = 0
-    f32x4 Ra[FT], Rb[FT], X[FT];
+    f32x4 Ra[FT], Rb[FT], X[FT];  // (Rb and X are first written by the first step)
 #pragma unroll
-    for (int ft = 0; ft < FT; ++ft) {
+    for (int ft = 0; ft < FT; ++ft)
       Ra[ft] = live ? f32x4{(float)Qraw[ft][0], (float)Qraw[ft][1], (float)Qraw[ft][2], (float)Qraw[ft][3]} * cc.inv_s0
                     : f32x4{0.f, 0.f, 0.f, 0.f};
-      Rb[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
-      X[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
     // One iteration it on the current rescaled residual Rc = Rt_it (the residuals divided by
     // host scalars that absorb the R_{it-1} coefficient of the recurrence):
     //   Ro <- Ro + krs Rc + H0hat (kys s_t Rc) + K^T ((K Rc) o kys Mhat)
@@ -531,7 +533,9 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
     // group: (A) the K products P = K Rc^T and the recurrence start; (B) the H0hat products on
     // the scaled operands and the P' operands; (C) the K^T products, the X update and the
     // next step's first K fragments. With one wave per SIMD nothing else hides latency.
-    auto step = [&](f32x4(&Ro)[FT], f32x4(&Rc)[FT], int it) {
+    // (the first step, FIRST = true, has Rt_{-1} = 0 and X = 0: it writes Ro and X outright)
+    auto step = [&](auto first, f32x4(&Ro)[FT], f32x4(&Rc)[FT], int it) {
+      constexpr bool FIRST = decltype(first)::value;
       const f32x4 cf = *reinterpret_cast<const f32x4*>(v_coef + 4 * it);  // krs, kys, bts
       Frag rf[KD], rs[KD], pf[KC];
       f32x4 pa[ST];
@@ -547,7 +551,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
       const float kys = cf[1] * s_t;
       rs[0] = pack8(Rc[0] * kys, Rc[1] * kys);
 #pragma unroll
-      for (int ft = 0; ft < FT; ++ft) Ro[ft] = Ro[ft] + cf[0] * Rc[ft];
+      for (int ft = 0; ft < FT; ++ft) Ro[ft] = FIRST ? cf[0] * Rc[ft] : Ro[ft] + cf[0] * Rc[ft];
       __builtin_amdgcn_sched_barrier(0);
       // (B)
 #pragma unroll
@@ -566,24 +570,32 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
 #pragma unroll
         for (int ft = 0; ft < FT; ++ft) Ro[ft] = M::mma(ktr[kc][ft], pf[kc], Ro[ft]);
 #pragma unroll
-      for (int ft = 0; ft < FT; ++ft) X[ft] += cf[2] * Rc[ft];
+      for (int ft = 0; ft < FT; ++ft) X[ft] = FIRST ? cf[2] * Rc[ft] : X[ft] + cf[2] * Rc[ft];
       __builtin_amdgcn_sched_barrier(0);
     };
     {
-      int it = 0;
+      using T1 = std::integral_constant<bool, true>;
+      using T0 = std::integral_constant<bool, false>;
       const int iters = cc.iters_rs;
-      for (; it + 2 < iters; it += 2) {
-        step(Rb, Ra, it);
-        step(Ra, Rb, it + 1);
-      }
       const float bl = v_coef[4 * (iters - 1) + 2];  // X += bts_{r-1} Rt_{r-1}
-      if (it + 1 < iters) {
-        step(Rb, Ra, it);
+      if (iters == 1) {
 #pragma unroll
-        for (int ft = 0; ft < FT; ++ft) X[ft] += bl * Rb[ft];
+        for (int ft = 0; ft < FT; ++ft) X[ft] = bl * Ra[ft];
       } else {
+        step(T1{}, Rb, Ra, 0);  // Rb = Rt_1
+        int it = 1;
+        for (; it + 2 < iters; it += 2) {
+          step(T0{}, Ra, Rb, it);      // Ra = Rt_{it+1}
+          step(T0{}, Rb, Ra, it + 1);  // Rb = Rt_{it+2}
+        }
+        if (it + 1 < iters) {
+          step(T0{}, Ra, Rb, it);
 #pragma unroll
-        for (int ft = 0; ft < FT; ++ft) X[ft] += bl * Ra[ft];
+          for (int ft = 0; ft < FT; ++ft) X[ft] += bl * Ra[ft];
+        } else {
+#pragma unroll
+          for (int ft = 0; ft < FT; ++ft) X[ft] += bl * Rb[ft];
+        }
       }
     }
 
