@@ -477,9 +477,10 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
       // token slots) when the wave's column tiles are all of them (b0 = 0), else read again.
       constexpr int CG = NCT >= 2 ? 2 : 1, NG = NCT / CG;
       Frag bk[2][CG][KC], bv[2][CG][KC];
+      f32x4 ub[CG][NRT];  // the group's U^T tiles, read as the group starts
       auto load_group = [&](int g, int buf) {
 #pragma unroll
-        for (int j = 0; j < CG; ++j)
+        for (int j = 0; j < CG; ++j) {
 #pragma unroll
           for (int kc = 0; kc < KC; ++kc) {
             if constexpr (NCT == FT) {
@@ -489,28 +490,46 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
             }
             bv[buf][j][kc] = frag_vt(b0 + g * CG + j, kc);
           }
+        }
       };
       load_group(0, 0);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
       for (int g = 0; g < NG; ++g) {
+#pragma unroll
+        for (int j = 0; j < CG; ++j)
+#pragma unroll
+          for (int jr = 0; jr < NRT; ++jr) ub[j][jr] = *us_tile(jr, g * CG + j);
         if (g + 1 < NG) load_group(g + 1, (g + 1) % 2);
+        // the group's 2 CG NRT accumulators take turns, so that no product waits for the one
+        // before it
+        f32x4 hacc[CG][NRT], uacc[CG][NRT];
 #pragma unroll
         for (int j = 0; j < CG; ++j)
 #pragma unroll
           for (int jr = 0; jr < NRT; ++jr) {
-            const int jc = g * CG + j;
-            f32x4 hacc = Hst[jr][jc] * gC, uacc = *us_tile(jr, jc) * gC;
+            hacc[j][jr] = Hst[jr][g * CG + j] * gC;
+            uacc[j][jr] = ub[j][jr] * gC;
+          }
 #pragma unroll
-            for (int kc = 0; kc < KC; ++kc) {
-              hacc = M::mma(awh[jr][kc], bk[g % 2][j][kc], hacc);
-              hacc = M::mma(awl[jr][kc], bk[g % 2][j][kc], hacc);
-              uacc = M::mma(awh[jr][kc], bv[g % 2][j][kc], uacc);
-              uacc = M::mma(awl[jr][kc], bv[g % 2][j][kc], uacc);
-            }
-            Hst[jr][jc] = hacc;
-            *us_tile(jr, jc) = uacc;
-            if constexpr (Cfg::PIN) keep_in_agpr(Hst[jr][jc]);
+        for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+          for (int hl = 0; hl < 2; ++hl)
+#pragma unroll
+            for (int j = 0; j < CG; ++j)
+#pragma unroll
+              for (int jr = 0; jr < NRT; ++jr) {
+                const Frag& aw = hl == 0 ? awh[jr][kc] : awl[jr][kc];
+                hacc[j][jr] = M::mma(aw, bk[g % 2][j][kc], hacc[j][jr]);
+                uacc[j][jr] = M::mma(aw, bv[g % 2][j][kc], uacc[j][jr]);
+              }
+#pragma unroll
+        for (int j = 0; j < CG; ++j)
+#pragma unroll
+          for (int jr = 0; jr < NRT; ++jr) {
+            Hst[jr][g * CG + j] = hacc[j][jr];
+            *us_tile(jr, g * CG + j) = uacc[j][jr];
+            if constexpr (Cfg::PIN) keep_in_agpr(Hst[jr][g * CG + j]);
           }
         __builtin_amdgcn_sched_barrier(0);
       }
