@@ -353,21 +353,29 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
       for (int kk = 0; kk < KD; ++kk)
         kb[kk] = *reinterpret_cast<const Frag*>(Kp + t * LDD + 32 * kk + 8 * lg);
       float pu = 0.0f;
+      f32x4 z[FT];  // H0hat k of the own token, the FT accumulators taking turns
 #pragma unroll
-      for (int ft = 0; ft < FT; ++ft) {
-        f32x4 z = {0.f, 0.f, 0.f, 0.f};
+      for (int ft = 0; ft < FT; ++ft) z[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < KD; ++kk) z = M::mma(Hres[ft][kk], kb[kk], z);
+      for (int kk = 0; kk < KD; ++kk)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) pu += z[i] * (float)kb[ft / 2][4 * (ft % 2) + i];
-      }
+        for (int ft = 0; ft < FT; ++ft) z[ft] = M::mma(Hres[ft][kk], kb[kk], z[ft]);
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) pu += z[ft][i] * (float)kb[ft / 2][4 * (ft % 2) + i];
       const float clp = t > 0 ? v_cl[t - 1] : 0.0f;
       float pv = 0.0f, kd = 0.0f;
+      f32x4 gram[ST];  // Gram tiles G[s][t] of the own token, accumulators taking turns
+#pragma unroll
+      for (int sb = 0; sb < ST; ++sb) gram[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KD; ++kk)
+#pragma unroll
+        for (int sb = 0; sb < ST; ++sb) gram[sb] = M::mma(kres[kk][sb], kb[kk], gram[sb]);
 #pragma unroll
       for (int sb = 0; sb < ST; ++sb) {
-        f32x4 gacc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < KD; ++kk) gacc = M::mma(kres[kk][sb], kb[kk], gacc);
+        const f32x4 gacc = gram[sb];
         const f32x4 cls = *reinterpret_cast<const f32x4*>(v_cl + 16 * sb + 4 * lg);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -647,12 +655,12 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
 #pragma unroll
       for (int sb = 0; sb < ST; ++sb) pa[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < KD; ++kk)
+      for (int kk = 0; kk < KD; ++kk) {  // (hi and lo products not back to back)
 #pragma unroll
-        for (int sb = 0; sb < ST; ++sb) {
-          pa[sb] = M::mma(kres[kk][sb], xh[kk], pa[sb]);
-          pa[sb] = M::mma(kres[kk][sb], xl[kk], pa[sb]);
-        }
+        for (int sb = 0; sb < ST; ++sb) pa[sb] = M::mma(kres[kk][sb], xh[kk], pa[sb]);
+#pragma unroll
+        for (int sb = 0; sb < ST; ++sb) pa[sb] = M::mma(kres[kk][sb], xl[kk], pa[sb]);
+      }
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
@@ -662,12 +670,12 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
 #pragma unroll
       for (int ft = 0; ft < FT; ++ft) y[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < KD; ++kk)
+      for (int kk = 0; kk < KD; ++kk) {
 #pragma unroll
-        for (int ft = 0; ft < FT; ++ft) {
-          y[ft] = M::mma(Hres[ft][kk], xh[kk], y[ft]);
-          y[ft] = M::mma(Hres[ft][kk], xl[kk], y[ft]);
-        }
+        for (int ft = 0; ft < FT; ++ft) y[ft] = M::mma(Hres[ft][kk], xh[kk], y[ft]);
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft) y[ft] = M::mma(Hres[ft][kk], xl[kk], y[ft]);
+      }
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) pf[kc] = pack8(pa[2 * kc] * Mh[2 * kc], pa[2 * kc + 1] * Mh[2 * kc + 1]);
       __builtin_amdgcn_sched_barrier(0);
