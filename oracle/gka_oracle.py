@@ -31,6 +31,12 @@ is the plainest reading that all of them support):
   exact mode        Cholesky solve of the same SPD system, for the pins only (the pages'
                     exact-solver reference, ai.info summary "Key Contributions" 2)
 
+  write gate        optional beta_t in [0, 1] scaling the token's write (ai.info summary, "Main
+                    Findings", the beta_t-augmented variant; its "Future Directions" call it the
+                    released default): H_t = gamma_t H_{t-1} + beta_t k_t k_t^T and
+                    U_t = gamma_t U_{t-1} + beta_t v_t k_t^T, i.e. weights eta_{t,i} beta_i in
+                    the ridge objective; beta = None means beta_t = 1 (the paper's experiments)
+
 Readings taken where the pages are silent (each also listed in the design notes):
   * x_0 = 0 and x_1 = c q (one Richardson step); "iters = r" means the iterate x_r is returned,
     i.e. r - 1 matrix-vector products with A;
@@ -111,16 +117,20 @@ def cholesky_solve(A: np.ndarray, b: np.ndarray) -> np.ndarray:
 # One token of the recurrence
 # ------------------------------------------------------------------------------------------
 
-def _token(H, U, n2, q, k, v, g, a, iters, mode, residuals=None):
+def _token(H, U, n2, q, k, v, g, a, iters, mode, residuals=None, b=None):
     """Advance (H, U, n2) by one token for every system and return (H, U, n2, x, o).
 
-    H, U: [N, D, D]; n2, g: [N]; q, k, v: [N, D].
+    H, U: [N, D, D]; n2, g: [N]; q, k, v: [N, D]; b: [N] write gate or None (= 1).
+    With the write gate the update is H <- g H + b k k^T, U <- g U + b v k^T, so that
+    ||H||^2 <- g^2 ||H||^2 + 2 g b k^T H k + b^2 ||k||^4 (the square of the update, expanded).
     """
+    if b is None:
+        b = np.ones_like(g)
     kHk = np.einsum("ni,nij,nj->n", k, H, k)
     kk = np.einsum("ni,ni->n", k, k)
-    n2 = g * g * n2 + 2.0 * g * kHk + kk * kk
-    H = g[:, None, None] * H + k[:, :, None] * k[:, None, :]
-    U = g[:, None, None] * U + v[:, :, None] * k[:, None, :]
+    n2 = g * g * n2 + 2.0 * g * b * kHk + (b * kk) ** 2
+    H = g[:, None, None] * H + b[:, None, None] * (k[:, :, None] * k[:, None, :])
+    U = g[:, None, None] * U + b[:, None, None] * (v[:, :, None] * k[:, None, :])
     if mode == "state":  # advance the state only (no solve); o is returned as zeros
         return H, U, n2, np.zeros_like(q), np.zeros_like(q)
     n = np.sqrt(n2)
@@ -148,13 +158,14 @@ def _token(H, U, n2, q, k, v, g, a, iters, mode, residuals=None):
 # ------------------------------------------------------------------------------------------
 
 def gka_forward_ref(q, k, v, gamma, a: float, iters: int, mode: str = "cheb",
-                    h0=None, u0=None, n2_0=None, return_residuals: bool = False):
+                    h0=None, u0=None, n2_0=None, return_residuals: bool = False, beta=None):
     """Sequential forward over a whole sequence.
 
     ``mode``: "cheb" (Chebyshev Iteration, as the layer), "exact" (Cholesky solve), or
     "state" (advance H, U, ||H||^2 only; o is all zeros).
 
-    q, k, v: [B, T, H, D]; gamma: [B, T, H]; optional initial state h0, u0 [B, H, D, D]
+    q, k, v: [B, T, H, D]; gamma and the optional write gate beta: [B, T, H] (beta None: all
+    ones); optional initial state h0, u0 [B, H, D, D]
     (U indexed [value dim][key dim]) and n2_0 [B, H] (= ||h0||_F^2 as carried by the caller).
     Returns a dict with o [B,T,H,D], hnorm [B,T,H] (= ||H_t||_F from the recurrence),
     h, u [B,H,D,D] and n2 [B,H] (final state), and optionally residuals
@@ -169,6 +180,7 @@ def gka_forward_ref(q, k, v, gamma, a: float, iters: int, mode: str = "cheb",
         return np.moveaxis(x, 2, 1).reshape((N, T) + x.shape[3:])
 
     qh, kh, vh, gh = heads(q), heads(k), heads(v), heads(gamma)
+    bh = None if beta is None else heads(np.asarray(beta, dtype=np.float64))
     H = np.zeros((N, D, D)) if h0 is None else np.asarray(h0, np.float64).reshape(N, D, D).copy()
     U = np.zeros((N, D, D)) if u0 is None else np.asarray(u0, np.float64).reshape(N, D, D).copy()
     n2 = np.zeros(N) if n2_0 is None else np.asarray(n2_0, np.float64).reshape(N).copy()
@@ -178,7 +190,7 @@ def gka_forward_ref(q, k, v, gamma, a: float, iters: int, mode: str = "cheb",
     for t in range(T):
         rl = [] if return_residuals else None
         H, U, n2, _, o[:, t] = _token(H, U, n2, qh[:, t], kh[:, t], vh[:, t], gh[:, t], a, iters,
-                                      mode, rl)
+                                      mode, rl, None if bh is None else bh[:, t])
         hn[:, t] = np.sqrt(n2)
         if return_residuals:
             res[:, t] = np.stack(rl, axis=-1)
@@ -193,10 +205,12 @@ def gka_forward_ref(q, k, v, gamma, a: float, iters: int, mode: str = "cheb",
     return out
 
 
-def gka_step_ref(q, k, v, gamma, a: float, iters: int, h, u, n2, mode: str = "cheb"):
+def gka_step_ref(q, k, v, gamma, a: float, iters: int, h, u, n2, mode: str = "cheb",
+                 beta=None):
     """One recurrent decode step: update the carried state with the token, then solve.
 
-    q, k, v: [B, H, D]; gamma: [B, H]; h, u: [B, H, D, D]; n2: [B, H].
+    q, k, v: [B, H, D]; gamma and the optional write gate beta: [B, H]; h, u: [B, H, D, D];
+    n2: [B, H].
     Returns (o [B,H,D], h, u, n2) -- new arrays, inputs untouched.
     """
     q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
@@ -206,16 +220,18 @@ def gka_step_ref(q, k, v, gamma, a: float, iters: int, h, u, n2, mode: str = "ch
                                np.asarray(u, np.float64).reshape(N, D, D),
                                np.asarray(n2, np.float64).reshape(N),
                                q.reshape(N, D), k.reshape(N, D), v.reshape(N, D),
-                               np.asarray(gamma, np.float64).reshape(N), a, iters, mode)
+                               np.asarray(gamma, np.float64).reshape(N), a, iters, mode, None,
+                               None if beta is None else np.asarray(beta, np.float64).reshape(N))
     return (o.reshape(B, Hh, D), H2.reshape(B, Hh, D, D), U2.reshape(B, Hh, D, D),
             n22.reshape(B, Hh))
 
 
-def ridge_bruteforce(q, k, v, gamma, a: float):
+def ridge_bruteforce(q, k, v, gamma, a: float, beta=None):
     """Solve the weighted ridge objective directly for one head, by least squares.
 
-    q, k, v: [T, D]; gamma: [T]. For every t the weights eta_{t,i} = prod_{j=i+1}^{t} gamma_j
-    are formed as plain products, H_t = sum_i eta_{t,i} k_i k_i^T is summed directly,
+    q, k, v: [T, D]; gamma (and the optional write gate beta): [T]. For every t the weights
+    eta_{t,i} = beta_i prod_{j=i+1}^{t} gamma_j are formed as plain products,
+    H_t = sum_i eta_{t,i} k_i k_i^T is summed directly,
     lambda_t = a ||H_t||_F, and
         min_S  sum_{i<=t} eta_{t,i} ||v_i - S k_i||^2 + lambda_t ||S||_F^2
     is solved as the stacked least-squares problem [sqrt(eta_i) k_i^T ; sqrt(lambda_t) I] S^T
@@ -224,10 +240,11 @@ def ridge_bruteforce(q, k, v, gamma, a: float):
     q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
     gamma = np.asarray(gamma, dtype=np.float64)
     T, D = k.shape
+    beta = np.ones(T) if beta is None else np.asarray(beta, dtype=np.float64)
     o = np.zeros((T, D))
     hn = np.zeros(T)
     for t in range(T):
-        eta = np.array([np.prod(gamma[i + 1:t + 1]) for i in range(t + 1)])
+        eta = np.array([beta[i] * np.prod(gamma[i + 1:t + 1]) for i in range(t + 1)])
         Ht = sum(eta[i] * np.outer(k[i], k[i]) for i in range(t + 1))
         hn[t] = np.linalg.norm(Ht, "fro")
         lam = a * hn[t]

@@ -352,3 +352,90 @@ def test_state_only_mode_advances_the_same_state():
     np.testing.assert_array_equal(a["u"], b["u"])
     np.testing.assert_array_equal(a["n2"], b["n2"])
     assert np.all(b["o"] == 0)
+
+
+# ------------------------------------------------------------------------------------------
+# write gate beta_t (the beta-augmented recurrence, ai.info summary "Main Findings")
+# ------------------------------------------------------------------------------------------
+
+def _rand_beta(rng, shape, zeros=False):
+    b = 1.0 / (1.0 + np.exp(-rng.normal(0.5, 1.5, shape)))
+    if zeros:
+        b[rng.random(shape) < 0.2] = 0.0
+    return b
+
+
+@pytest.mark.parametrize("gate", ["sigmoid", "with_zeros"])
+@pytest.mark.parametrize("D", [1, 4, 12])
+def test_beta_exact_mode_matches_bruteforce_ridge(gate, D):
+    """With beta the objective weighs pair i by beta_i prod_{j>i} gamma_j (brute force)."""
+    rng = np.random.default_rng(300 + D)
+    T, a = 30, 0.1
+    q, k, v, g = _rand_inputs(rng, 1, T, 2, D, gate)
+    beta = _rand_beta(rng, (1, T, 2), zeros=True)
+    ref = gka_forward_ref(q, k, v, g, a, iters=1, mode="exact", beta=beta)
+    for h in range(2):
+        o_bf, hn_bf = ridge_bruteforce(q[0, :, h], k[0, :, h], v[0, :, h], g[0, :, h], a,
+                                       beta=beta[0, :, h])
+        assert _rel(ref["o"][0, :, h], o_bf) < 1e-10
+        np.testing.assert_allclose(ref["hnorm"][0, :, h], hn_bf, rtol=1e-12, atol=1e-300)
+
+
+def test_beta_states_equal_direct_sums():
+    rng = np.random.default_rng(310)
+    T, D = 17, 6
+    q, k, v, g = _rand_inputs(rng, 1, T, 1, D, "with_zeros")
+    beta = _rand_beta(rng, (1, T, 1), zeros=True)
+    out = gka_forward_ref(q, k, v, g, 0.1, 6, beta=beta)
+    Ht = sum(beta[0, i, 0] * np.prod(g[0, i + 1:, 0]) * np.outer(k[0, i, 0], k[0, i, 0]) for i in range(T))
+    Ut = sum(beta[0, i, 0] * np.prod(g[0, i + 1:, 0]) * np.outer(v[0, i, 0], k[0, i, 0]) for i in range(T))
+    np.testing.assert_allclose(out["h"][0, 0], Ht, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(out["u"][0, 0], Ut, rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(out["n2"][0, 0], np.sum(Ht * Ht), rtol=1e-12)
+
+
+def test_beta_equals_scaled_keys_and_values():
+    """beta_t k k^T = (sqrt(beta_t) k)(sqrt(beta_t) k)^T and beta_t v k^T likewise: the gated
+    forward equals the plain forward fed sqrt(beta) k and sqrt(beta) v (q unchanged)."""
+    rng = np.random.default_rng(311)
+    q, k, v, g = _rand_inputs(rng, 2, 20, 3, 8, "with_zeros")
+    beta = _rand_beta(rng, (2, 20, 3), zeros=True)
+    sb = np.sqrt(beta)[..., None]
+    a = gka_forward_ref(q, k, v, g, 0.05, 10, beta=beta)
+    b = gka_forward_ref(q, k * sb, v * sb, g, 0.05, 10)
+    for key in ("o", "hnorm", "h", "u", "n2"):
+        np.testing.assert_allclose(a[key], b[key], rtol=1e-10, atol=1e-13)
+
+
+def test_beta_ones_is_the_plain_layer():
+    rng = np.random.default_rng(312)
+    q, k, v, g = _rand_inputs(rng, 1, 15, 2, 6)
+    a = gka_forward_ref(q, k, v, g, 0.1, 8)
+    b = gka_forward_ref(q, k, v, g, 0.1, 8, beta=np.ones(g.shape))
+    for key in ("o", "hnorm", "h", "u", "n2"):
+        np.testing.assert_array_equal(a[key], b[key])
+
+
+def test_beta_zero_token_writes_nothing():
+    rng = np.random.default_rng(313)
+    q, k, v, g = _rand_inputs(rng, 1, 6, 1, 5)
+    beta = np.ones(g.shape)
+    beta[0, 3, 0] = 0.0
+    before = gka_forward_ref(q[:, :3], k[:, :3], v[:, :3], g[:, :3], 0.1, 8, beta=beta[:, :3])
+    after = gka_forward_ref(q[:, :4], k[:, :4], v[:, :4], g[:, :4], 0.1, 8, beta=beta[:, :4])
+    np.testing.assert_allclose(after["h"], g[0, 3, 0] * before["h"], rtol=1e-14)
+    np.testing.assert_allclose(after["u"], g[0, 3, 0] * before["u"], rtol=1e-14)
+
+
+def test_beta_step_chain_equals_forward():
+    rng = np.random.default_rng(314)
+    q, k, v, g = _rand_inputs(rng, 2, 9, 3, 5)
+    beta = _rand_beta(rng, g.shape)
+    full = gka_forward_ref(q, k, v, g, 0.1, 8, beta=beta)
+    B, T, H, D = q.shape
+    h, u, n2 = np.zeros((B, H, D, D)), np.zeros((B, H, D, D)), np.zeros((B, H))
+    for t in range(T):
+        o, h, u, n2 = gka_step_ref(q[:, t], k[:, t], v[:, t], g[:, t], 0.1, 8, h, u, n2,
+                                   beta=beta[:, t])
+        np.testing.assert_allclose(o, full["o"][:, t], rtol=1e-12, atol=1e-14)
+    np.testing.assert_allclose(h, full["h"], rtol=1e-12, atol=1e-14)
