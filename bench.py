@@ -8,7 +8,12 @@ gka_step calls on a float32 state warmed by 512 tokens), the roofline of the dom
 each path (measured with HIP events on the library's stream), and the float64 CPU oracle timed
 on a bounded sample of the prefill workload on this host.
 
+The write-gated prefill (gka_fwd_chunked_beta, same workload plus per-token write gates) is
+timed the same way and reported under "write_gate". The oracle leg also compares its outputs of
+the prefix with the timed device run's.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps S] [--no-cpu]
+                       [--no-decode] [--no-beta]
 """
 from __future__ import annotations
 
@@ -101,17 +106,24 @@ def measured_traffic(kernel):
     return rec["bytes"] if h.hexdigest() == rec.get("source_sha256") else None
 
 
-def bench_prefill(W, steps, warmup, ev):
+def prefill_inputs(W):
+    """Device copies of the prefill workload's inputs (bf16 q, k, v; float32 gates)."""
     import torch
-    from test_ridge_regression_amd import gka
     from test_ridge_regression_amd import workloads as Wl
 
     log(f"prefill inputs {W.name}")
     q, k, v, g = Wl.make_workload(W)
     d = lambda x: torch.from_numpy(x.astype(np.float32)).cuda().to(torch.bfloat16).contiguous()
-    qd, kd, vd = d(q), d(k), d(v)
-    gd = torch.from_numpy(g.astype(np.float32)).cuda()
-    del q, k, v
+    return d(q), d(k), d(v), torch.from_numpy(g.astype(np.float32)).cuda()
+
+
+def bench_prefill(W, inputs, steps, warmup, ev, beta=None, what="prefill"):
+    """Times `steps` gka_fwd_chunked calls (gka_fwd_chunked_beta with ``beta``) on resident
+    inputs, then the per-phase kernel times in a second pass of the same calls."""
+    import torch
+    from test_ridge_regression_amd import gka
+
+    qd, kd, vd, gd = inputs
     o = torch.empty_like(qd)
     need = gka.workspace_bytes(W.B, W.T, W.H, W.D, W.chunk, W.iters, W.a, gka.GKA_BF16)
     ws = torch.empty(max(need, 1), device="cuda", dtype=torch.uint8)
@@ -119,24 +131,25 @@ def bench_prefill(W, steps, warmup, ev):
     phase = ev.create(4 * steps)
     arrs = [(ctypes.c_void_p * 4)(*phase[4 * i:4 * i + 4]) for i in range(steps)]
     t0, t1 = ev.create(2)
-    log(f"prefill warmup {warmup}")
+    call = lambda **kw: gka.fwd_chunked(qd, kd, vd, gd, W.a, W.iters, W.chunk, out=o,
+                                        workspace=ws, beta=beta, **kw)
+    log(f"{what} warmup {warmup}")
     for _ in range(warmup):
-        gka.fwd_chunked(qd, kd, vd, gd, W.a, W.iters, W.chunk, out=o, workspace=ws)
+        call()
     torch.cuda.synchronize()
-    log(f"prefill timed {steps}")
+    log(f"{what} timed {steps}")
     ev.record(t0, stream.cuda_stream)
     for i in range(steps):
-        gka.fwd_chunked(qd, kd, vd, gd, W.a, W.iters, W.chunk, out=o, workspace=ws)
+        call()
     ev.record(t1, stream.cuda_stream)
     ev.sync(t1)
     torch.cuda.synchronize()
     total_ms = ev.elapsed_ms(t0, t1)
     # per-kernel times in a second pass of the same steps: events between the launches of one
     # call (on the launch stream) would add their own gaps to the timed steps
-    log(f"prefill phases {steps}")
+    log(f"{what} phases {steps}")
     for i in range(steps):
-        gka.fwd_chunked(qd, kd, vd, gd, W.a, W.iters, W.chunk, out=o, workspace=ws,
-                        phase_events=arrs[i])
+        call(phase_events=arrs[i])
     torch.cuda.synchronize()
     walk = [ev.elapsed_ms(phase[4 * i + 2], phase[4 * i + 3]) for i in range(steps)]
     summ = [ev.elapsed_ms(phase[4 * i + 0], phase[4 * i + 1]) for i in range(steps)]
@@ -144,8 +157,7 @@ def bench_prefill(W, steps, warmup, ev):
     ev.destroy(phase + [t0, t1])
     segs = _segments(W)
     return dict(total_ms=total_ms, ms_per_step=total_ms / steps, walk_ms=float(np.mean(walk)),
-                summary_ms=float(np.mean(summ)), scan_ms=float(np.mean(scan)), segments=segs,
-                o=o, inputs=(qd, kd, vd, gd))
+                summary_ms=float(np.mean(summ)), scan_ms=float(np.mean(scan)), segments=segs, o=o)
 
 
 def _segments(W):
@@ -156,21 +168,6 @@ def _segments(W):
         return 1
     bh = W.B * W.H
     return int((need - bh * 4) // (bh * (2 * W.D * W.D + 1) * 4))
-
-
-def parity_sample(W, o_dev, heads=((0, 0), (7, 7))):
-    """Sampled heads of the timed prefill against the float64 oracle (full sequence)."""
-    from oracle import gka_forward_ref
-    from test_ridge_regression_amd import workloads as Wl
-
-    q, k, v, g = Wl.make_workload(W, heads=heads)
-    ref = gka_forward_ref(q, k, v, g, W.a, W.iters)["o"]
-    errs = []
-    for i, (b, h) in enumerate(heads):
-        got = o_dev[b, :, h].float().cpu().numpy()
-        want = ref[0, :, i]
-        errs.append(float(np.linalg.norm(got - want) / np.linalg.norm(want)))
-    return max(errs)
 
 
 def bench_decode(Wd, steps, ev):
@@ -217,25 +214,36 @@ def bench_decode(Wd, steps, ev):
     return dict(total_ms=total_ms, ms_per_step=total_ms / steps, kernel_ms=float(np.mean(per)))
 
 
-def cpu_baseline(W, budget_s=12.0):
-    """The float64 oracle as it stands, on a prefix of the prefill workload (all B x H heads)."""
+def cpu_baseline(W, o_dev=None, budget_s=12.0):
+    """The float64 oracle as it stands, on a prefix of the prefill workload (all B x H heads).
+    Outputs are causal, so the oracle's outputs of the prefix are also those of the timed
+    device run there: with ``o_dev`` their relative L2 distance is reported alongside."""
     from oracle import gka_forward_ref
     from test_ridge_regression_amd import workloads as Wl
 
-    q, k, v, g = Wl.make_workload(W, T=8)
+    # the full draw, sliced: a shorter draw would not hold the same values (each stream draws
+    # q, k, v, gamma of a whole block in turn)
+    qa, ka, va, ga = Wl.make_workload(W)
+    pre = lambda T: (qa[:, :T], ka[:, :T], va[:, :T], ga[:, :T])
     t = time.perf_counter()
-    gka_forward_ref(q, k, v, g, W.a, W.iters)
+    gka_forward_ref(*pre(8), W.a, W.iters)
     per_tok = (time.perf_counter() - t) / 8
     T = int(max(8, min(W.T, budget_s / max(per_tok, 1e-6))))
-    q, k, v, g = Wl.make_workload(W, T=T)
     t = time.perf_counter()
-    gka_forward_ref(q, k, v, g, W.a, W.iters)
+    ref = gka_forward_ref(*pre(T), W.a, W.iters)
     el = time.perf_counter() - t
-    return dict(value=W.B * T / el, unit="tokens/s", cores=1, kind="oracle",
-                sample=f"first {T} of {W.T} tokens of the prefill workload, all {W.B}x{W.H} heads; "
-                       f"{el:.1f} s; numpy float64, einsum single-threaded; "
-                       f"host {platform.processor() or platform.machine()}, "
-                       f"{len(os.sched_getaffinity(0))} cores available")
+    rec = dict(value=W.B * T / el, unit="tokens/s", cores=1, kind="oracle",
+               sample=f"first {T} of {W.T} tokens of the prefill workload, all {W.B}x{W.H} heads; "
+                      f"{el:.1f} s; numpy float64, einsum single-threaded; "
+                      f"host {platform.processor() or platform.machine()}, "
+                      f"{len(os.sched_getaffinity(0))} cores available")
+    if o_dev is not None:
+        got = o_dev[:, :T].float().cpu().numpy().astype(np.float64)
+        want = ref["o"]
+        per_head = [float(np.linalg.norm(got[b, :, h] - want[b, :, h]) /
+                          np.linalg.norm(want[b, :, h])) for b in range(W.B) for h in range(W.H)]
+        rec["sample_parity_worst_head_rel_l2"] = max(per_head)
+    return rec
 
 
 def main():
@@ -246,6 +254,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-beta", action="store_true", help="skip the write-gated prefill")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 512 MiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -271,15 +280,14 @@ def main():
         log("copy probe: 3 x 512 MiB device-to-device copies")
         del src, dst
     W = Wl.WORKLOADS["prefill_b8_t2048_h8_d128"]
-    pre = bench_prefill(W, args.steps, args.warmup, ev)
+    inputs = prefill_inputs(W)
+    pre = bench_prefill(W, inputs, args.steps, args.warmup, ev)
     tokens = W.B * W.T
     value = tokens / (pre["ms_per_step"] * 1e-3)
     F = prefill_flops_per_token_head(W.D, W.chunk, W.iters) * W.B * W.T * W.H
     achieved = F / (pre["walk_ms"] * 1e-3)
     log(f"prefill: {pre['ms_per_step']:.3f} ms/step (summary {pre['summary_ms']:.3f}, scan "
         f"{pre['scan_ms']:.3f}, walk {pre['walk_ms']:.3f}), {value:.3e} tok/s")
-    err = parity_sample(W, pre["o"])
-    log(f"prefill sampled parity rel_l2 {err:.3e}")
     rec = {
         "metric": "GKA forward tokens/s (B8 T2048 H8 D128 bf16) + % MFMA peak; decode tok/s",
         "value": value,
@@ -303,9 +311,23 @@ def main():
         "whole_step_mfma_frac": F / (pre["ms_per_step"] * 1e-3) / PEAK_BF16_MFMA,
         "phases_ms": {"summary": pre["summary_ms"], "scan": pre["scan_ms"],
                       "walk": pre["walk_ms"]},
-        "parity_sampled_rel_l2": err,
     }
-    del pre
+    o_base = pre.pop("o")
+    if not args.no_beta:
+        # the write-gated recurrence (gka_fwd_chunked_beta) on the same inputs, with gates
+        # beta_t = sigmoid(N(0, 2)) drawn per token
+        bd = torch.from_numpy(Wl.make_beta(W.B, W.T, W.H, W.seed).astype(np.float32)).cuda()
+        pb = bench_prefill(W, inputs, args.steps, args.warmup, ev, beta=bd, what="beta prefill")
+        rec["write_gate"] = {
+            "entry_point": "gka_fwd_chunked_beta", "workload": W.name,
+            "tokens_per_s": tokens / (pb["ms_per_step"] * 1e-3), "ms_per_step": pb["ms_per_step"],
+            "phases_ms": {"summary": pb["summary_ms"], "scan": pb["scan_ms"],
+                          "walk": pb["walk_ms"]},
+            "walk_mfma_frac": F / (pb["walk_ms"] * 1e-3) / PEAK_BF16_MFMA,
+        }
+        log(f"beta prefill: {pb['ms_per_step']:.3f} ms/step (walk {pb['walk_ms']:.3f})")
+        del pb, bd
+    del pre, inputs
     torch.cuda.empty_cache()
     if not args.no_decode:
         Wd = Wl.WORKLOADS["decode_b256_h8_d128"]
@@ -326,7 +348,7 @@ def main():
         log(f"decode: {dec['ms_per_step'] * 1e3:.1f} us/step, kernel {dec['kernel_ms'] * 1e3:.1f} us")
     if not args.no_cpu:
         log("cpu baseline (oracle)")
-        rec["cpu_baseline"] = cpu_baseline(W)
+        rec["cpu_baseline"] = cpu_baseline(W, o_base)
     print(json.dumps(rec), flush=True)
 
 

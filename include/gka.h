@@ -120,6 +120,32 @@ gka_status gka_step(const gka_params* p, const void* q, const void* k, const voi
                     const float* gamma, void* o, float* h_state, float* u_state, float* hnorm2,
                     void* stream);
 
+/*
+ * Write-gated variants (ai.info summary, "Main Findings": the variant whose recurrence carries a
+ * per-token write strength beta_t next to the forget gate gamma_t). Every token's write into the
+ * statistics is scaled by beta_t:
+ *     H_t = gamma_t H_{t-1} + beta_t k_t k_t^T,   U_t = gamma_t U_{t-1} + beta_t v_t k_t^T
+ * and, for the decode step, ||H_t||_F^2 = gamma^2 ||H_{t-1}||_F^2 + 2 gamma beta k^T H_{t-1} k
+ * + beta^2 ||k||^4. Everything else (ridge, solver, output) is as in gka_fwd_chunked / gka_step.
+ *   beta      float32 [B, T, H] (prefill) or [B, H] (decode), values in [0, 1], read; NULL means
+ *             beta = 1 for every token, which gives results identical to the base entry points
+ *             (they are these calls with beta = NULL)
+ * Other arguments, layouts, ownership and errors are those of the base entry point; in addition
+ * a beta that is not 4-byte aligned gives GKA_ERR_SHAPE and one that overlaps o GKA_ERR_ALIAS.
+ * Internally
+ * the prefill applies beta as sqrt(beta_t) on the token's key and value rows where they are
+ * converted to the 16-bit matrix operands, and as a factor of the token's weight in the
+ * per-segment summaries; in exact arithmetic both give the recurrence above.
+ */
+gka_status gka_fwd_chunked_beta(const gka_params* p, const void* q, const void* k, const void* v,
+                                const float* gamma, const float* beta, void* o, float* h_state,
+                                float* u_state, float* hnorm2, float* hnorm_t, void* workspace,
+                                size_t workspace_bytes, void* stream, void* const* phase_events);
+
+gka_status gka_step_beta(const gka_params* p, const void* q, const void* k, const void* v,
+                         const float* gamma, const float* beta, void* o, float* h_state,
+                         float* u_state, float* hnorm2, void* stream);
+
 /* Static description of a status code. */
 const char* gka_status_str(int status);
 

@@ -12,7 +12,7 @@ namespace {
 using gka::ChebConsts;
 using gka::FwdPlan;
 
-constexpr int kAbiVersion = 1;
+constexpr int kAbiVersion = 2;
 constexpr int kCUs = 256;  // MI355X compute units: the segment plan aims at one workgroup per CU
 
 bool dims_supported(int dtype, int D) {
@@ -186,6 +186,14 @@ gka_status gka_fwd_chunked(const gka_params* p, const void* q, const void* k, co
                            const float* gamma, void* o, float* h_state, float* u_state,
                            float* hnorm2, float* hnorm_t, void* workspace,
                            size_t workspace_bytes, void* stream, void* const* phase_events) {
+  return gka_fwd_chunked_beta(p, q, k, v, gamma, nullptr, o, h_state, u_state, hnorm2, hnorm_t,
+                              workspace, workspace_bytes, stream, phase_events);
+}
+
+gka_status gka_fwd_chunked_beta(const gka_params* p, const void* q, const void* k, const void* v,
+                                const float* gamma, const float* beta, void* o, float* h_state,
+                                float* u_state, float* hnorm2, float* hnorm_t, void* workspace,
+                                size_t workspace_bytes, void* stream, void* const* phase_events) {
   gka_status st = check_fwd(p);
   if (st != GKA_OK) return st;
   const bool any_state = h_state || u_state || hnorm2;
@@ -197,6 +205,9 @@ gka_status gka_fwd_chunked(const gka_params* p, const void* q, const void* k, co
   if (h_state && (!aligned16(h_state) || !aligned16(u_state))) return GKA_ERR_SHAPE;
   const size_t n_io = (size_t)p->B * p->T * p->H * p->D * elem_bytes(p->dtype);
   if (overlap(o, n_io, q, n_io) || overlap(o, n_io, k, n_io) || overlap(o, n_io, v, n_io))
+    return GKA_ERR_ALIAS;
+  if (beta && (reinterpret_cast<uintptr_t>(beta) & 3u)) return GKA_ERR_SHAPE;
+  if (beta && overlap(o, n_io, beta, (size_t)p->B * p->T * p->H * sizeof(float)))
     return GKA_ERR_ALIAS;
   FwdPlan pl;
   make_plan(p, pl);
@@ -216,6 +227,7 @@ gka_status gka_fwd_chunked(const gka_params* p, const void* q, const void* k, co
   wa.k = k;
   wa.v = v;
   wa.gamma = gamma;
+  wa.beta = beta;
   wa.o = o;
   wa.hnorm_t = hnorm_t;
   if (pl.S == 1) {
@@ -264,6 +276,12 @@ gka_status gka_fwd_chunked(const gka_params* p, const void* q, const void* k, co
 gka_status gka_step(const gka_params* p, const void* q, const void* k, const void* v,
                     const float* gamma, void* o, float* h_state, float* u_state, float* hnorm2,
                     void* stream) {
+  return gka_step_beta(p, q, k, v, gamma, nullptr, o, h_state, u_state, hnorm2, stream);
+}
+
+gka_status gka_step_beta(const gka_params* p, const void* q, const void* k, const void* v,
+                         const float* gamma, const float* beta, void* o, float* h_state,
+                         float* u_state, float* hnorm2, void* stream) {
   gka_status st = check_common(p);
   if (st != GKA_OK) return st;
   if (!q || !k || !v || !gamma || !o || !h_state || !u_state || !hnorm2) return GKA_ERR_NULL;
@@ -271,9 +289,11 @@ gka_status gka_step(const gka_params* p, const void* q, const void* k, const voi
   const size_t n_io = (size_t)p->B * p->H * p->D * elem_bytes(p->dtype);
   if (overlap(o, n_io, q, n_io) || overlap(o, n_io, k, n_io) || overlap(o, n_io, v, n_io))
     return GKA_ERR_ALIAS;
+  if (beta && (reinterpret_cast<uintptr_t>(beta) & 3u)) return GKA_ERR_SHAPE;
+  if (beta && overlap(o, n_io, beta, (size_t)p->B * p->H * sizeof(float))) return GKA_ERR_ALIAS;
   const ChebConsts cc = cheb_consts(p->a, p->iters);
-  if (gka::launch_step(p->dtype, p->D, p->B * p->H, q, k, v, gamma, o, h_state, u_state, hnorm2,
-                       cc, static_cast<hipStream_t>(stream)) != hipSuccess)
+  if (gka::launch_step(p->dtype, p->D, p->B * p->H, q, k, v, gamma, beta, o, h_state, u_state,
+                       hnorm2, cc, static_cast<hipStream_t>(stream)) != hipSuccess)
     return GKA_ERR_HIP;
   return GKA_OK;
 }

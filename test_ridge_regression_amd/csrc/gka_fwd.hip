@@ -14,6 +14,11 @@
 //             (the Frobenius-norm recurrence with H_{t-1} in chunk form; an affine scan over t)
 //   carry     H0 <- Gam_C H0 + K^T diag(w) K,  U0 <- Gam_C U0 + V^T diag(w) K,  w_s = 2^(cl_C - cl_s)
 //
+// With the optional write gate beta_t (the variant of "Main Findings" on the ai.info summary,
+// H_t = gamma_t H_{t-1} + beta_t k_t k_t^T and likewise U_t) all of the above holds with k_s and
+// v_s replaced by sqrt(beta_s) k_s and sqrt(beta_s) v_s: the walk scales the rows where they are
+// converted to operands, the segment summary multiplies beta_s into the weight w_s.
+//
 // The Chebyshev iteration runs on the system divided by ||H_t||_F (spectrum in [a, 1 + a]), so
 // its step and weights are launch constants, and on the residuals R_i = Q - A X_i:
 //   R_0 = Q, R_1 = R_0 - c A R_0, R_{i+1} = R_{i-1} + omega_i (R_i - R_{i-1} - c A R_i),
@@ -290,9 +295,11 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
       for (int e = tid; e < Cfg::NU; e += Cfg::NT) {
         const int t = e % C, d0 = (e / C) * VEC;
         vecT kv, vv;
+        float sb = 1.0f;  // sqrt(beta_t): the write gate on the token's key and value
         if (t < nv) {
           kv = PreK[e];
           vv = PreV[e];
+          if (A.beta) sb = sqrtf(A.beta[(b * (long long)Tlen + t0 + t) * Hn + h]);
         } else {
 #pragma unroll
           for (int i = 0; i < VEC; ++i) {
@@ -303,9 +310,9 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
         vecO ko;
 #pragma unroll
         for (int i = 0; i < VEC; ++i) {
-          ko[i] = to_op<O>(kv[i]);
+          ko[i] = to_op<O>((float)kv[i] * sb);
           KT[(d0 + i) * LDC + t] = ko[i];
-          VT[(d0 + i) * LDC + t] = to_op<O>(vv[i]);
+          VT[(d0 + i) * LDC + t] = to_op<O>((float)vv[i] * sb);
         }
         *reinterpret_cast<vecO*>(Ks + t * LDD + d0) = ko;
       }
@@ -791,7 +798,7 @@ __global__ __launch_bounds__(1024) void summary_kernel(WalkArgs A, int B, int Tl
   // (token tid / UPR, column tid % UPR) of K and V, and the gate of token lane % C. Two chunks
   // in flight keep enough bytes outstanding per compute unit to cover the memory latency.
   vecT kreg[2] = {}, vreg[2] = {};
-  float greg[2] = {1.0f, 1.0f};
+  float greg[2] = {1.0f, 1.0f}, breg[2] = {1.0f, 1.0f};  // gates and write gates
   auto prefetch = [&](int chn, int slot) {
     if (chn >= c_end) return;
     const int t0n = chn * C, nvn = min(C, Tlen - t0n);
@@ -802,7 +809,11 @@ __global__ __launch_bounds__(1024) void summary_kernel(WalkArgs A, int B, int Tl
       kreg[slot] = *reinterpret_cast<const vecT*>(kg + off);
       vreg[slot] = *reinterpret_cast<const vecT*>(vg + off);
     }
-    if (lane % C < nvn) greg[slot] = A.gamma[(b * (long long)Tlen + t0n + lane % C) * Hn + h];
+    if (lane % C < nvn) {
+      const long long gi = (b * (long long)Tlen + t0n + lane % C) * Hn + h;
+      greg[slot] = A.gamma[gi];
+      if (A.beta) breg[slot] = A.beta[gi];
+    }
   };
   prefetch(c_begin, 0);
   prefetch(c_begin + 1, 1);
@@ -821,7 +832,8 @@ __global__ __launch_bounds__(1024) void summary_kernel(WalkArgs A, int B, int Tl
     float clast;  // prefix at the last token of the lane's group
     if constexpr (C == kWave) clast = lane_value(cl, C - 1);
     else clast = __shfl(cl, C - 1, C);
-    const float wl = fast_exp2(fminf(clast - cl, 0.0f));  // carry weight of token tl
+    // carry weight of token tl, times its write gate
+    const float wl = fast_exp2(fminf(clast - cl, 0.0f)) * breg[SLOT];
     const float gC = fast_exp2(clast);
     log2g_seg += clast;
     const int t = tid / UPR, c = tid % UPR;  // this thread's unit

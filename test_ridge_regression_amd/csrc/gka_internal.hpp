@@ -27,7 +27,8 @@ inline hipError_t ensure_dynamic_lds(const void* kern, int bytes, std::atomic<ui
 
 // Decode step: one workgroup per (batch row, head).
 hipError_t launch_step(int dtype, int D, int BH, const void* q, const void* k, const void* v,
-                       const float* gamma, void* o, float* h, float* u, float* n2,
+                       const float* gamma, const float* beta, void* o, float* h, float* u,
+                       float* n2,
                        const ChebConsts& cc, hipStream_t stream);
 
 // Prefill. Segment plan of one call: N chunks split into S segments of J chunks each.
@@ -47,6 +48,7 @@ struct WalkArgs {
   const void* k;
   const void* v;
   const float* gamma;
+  const float* beta;      // optional per-token write gate [B, T, H] (NULL: 1)
   void* o;
   float* hnorm_t;         // optional per-token ||H_t||_F [B, T, H]
   const float* in_h;      // segment-start H (NULL: zero state)

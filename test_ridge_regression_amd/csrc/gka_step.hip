@@ -2,8 +2,10 @@
 //
 // Per head (arXiv 2511.21016; recurrences from the gating fragment and the adaptive ridge of
 // "Key Contributions" 2 on the ai.info summary; solver of Lemma 3/4 on the pith.science page):
-//   n2  <- gamma^2 n2 + 2 gamma k^T H k + ||k||^4       (uses H before the update)
-//   H   <- gamma H + k k^T,   U <- gamma U + v k^T
+//   n2  <- gamma^2 n2 + 2 gamma beta k^T H k + beta^2 ||k||^4   (uses H before the update)
+//   H   <- gamma H + beta k k^T,   U <- gamma U + beta v k^T
+// with the optional write gate beta of the variant in "Main Findings" on the ai.info summary
+// (beta = 1 without it)
 //   Chebyshev on (H / ||H||_F + a I) xh = q (spectrum in [a, 1+a]), x = xh / ||H||_F
 //   o   =  U x
 //
@@ -23,6 +25,7 @@ template <typename T, int D, int NT>
 __global__ __launch_bounds__(NT) void step_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                   const T* __restrict__ v,
                                                   const float* __restrict__ gamma,
+                                                  const float* __restrict__ beta,
                                                   T* __restrict__ o, float* __restrict__ hs,
                                                   float* __restrict__ us,
                                                   float* __restrict__ n2s, ChebConsts cc) {
@@ -52,6 +55,7 @@ __global__ __launch_bounds__(NT) void step_kernel(const T* __restrict__ q, const
     Ur[j] = *reinterpret_cast<const f32x4*>(us + mat + (size_t)(r0 + j * RS) * D + 4 * c4);
 
   const float g = gamma[head];
+  const float bt = beta ? beta[head] : 1.0f;
   const float n2_old = n2s[head];
   float q_own = 0.0f;
   if (tid < D) {
@@ -67,9 +71,10 @@ __global__ __launch_bounds__(NT) void step_kernel(const T* __restrict__ q, const
   for (int j = 0; j < F; ++j) {
     const float kr = ks[r0 + j * RS];
     const float vr = vs[r0 + j * RS];
+    const float bkr = bt * kr, bvr = bt * vr;
     kHk += kr * (Hr[j][0] * kc[0] + Hr[j][1] * kc[1] + Hr[j][2] * kc[2] + Hr[j][3] * kc[3]);
-    Hr[j] = g * Hr[j] + kr * kc;
-    Ur[j] = g * Ur[j] + vr * kc;
+    Hr[j] = g * Hr[j] + bkr * kc;
+    Ur[j] = g * Ur[j] + bvr * kc;
   }
 #pragma unroll
   for (int j = 0; j < F; ++j) {
@@ -92,7 +97,8 @@ __global__ __launch_bounds__(NT) void step_kernel(const T* __restrict__ q, const
     kHk += red[0][w];
     kk += red[1][w];
   }
-  const float n2 = g * g * n2_old + 2.0f * g * kHk + kk * kk;
+  const float bkk = bt * kk;
+  const float n2 = g * g * n2_old + 2.0f * g * bt * kHk + bkk * bkk;
   if (tid == 0) n2s[head] = n2;
 
   // Chebyshev iteration on the normalised system; thread c < D owns element c of the iterates
@@ -141,28 +147,28 @@ __global__ __launch_bounds__(NT) void step_kernel(const T* __restrict__ q, const
 
 template <typename T, int D, int NT>
 static hipError_t launch_step_t(int BH, const void* q, const void* k, const void* v,
-                                const float* gamma, void* o, float* h, float* u, float* n2,
+                                const float* gamma, const float* beta, void* o, float* h, float* u, float* n2,
                                 const ChebConsts& cc, hipStream_t stream) {
   hipLaunchKernelGGL((step_kernel<T, D, NT>), dim3(BH), dim3(NT), 0, stream,
                      static_cast<const T*>(q), static_cast<const T*>(k),
-                     static_cast<const T*>(v), gamma, static_cast<T*>(o), h, u, n2, cc);
+                     static_cast<const T*>(v), gamma, beta, static_cast<T*>(o), h, u, n2, cc);
   return hipGetLastError();
 }
 
 hipError_t launch_step(int dtype, int D, int BH, const void* q, const void* k, const void* v,
-                       const float* gamma, void* o, float* h, float* u, float* n2,
+                       const float* gamma, const float* beta, void* o, float* h, float* u, float* n2,
                        const ChebConsts& cc, hipStream_t stream) {
   if (dtype == 0) {
     switch (D) {
-      case 32: return launch_step_t<bf16, 32, 128>(BH, q, k, v, gamma, o, h, u, n2, cc, stream);
-      case 64: return launch_step_t<bf16, 64, 256>(BH, q, k, v, gamma, o, h, u, n2, cc, stream);
-      case 128: return launch_step_t<bf16, 128, 512>(BH, q, k, v, gamma, o, h, u, n2, cc, stream);
+      case 32: return launch_step_t<bf16, 32, 128>(BH, q, k, v, gamma, beta, o, h, u, n2, cc, stream);
+      case 64: return launch_step_t<bf16, 64, 256>(BH, q, k, v, gamma, beta, o, h, u, n2, cc, stream);
+      case 128: return launch_step_t<bf16, 128, 512>(BH, q, k, v, gamma, beta, o, h, u, n2, cc, stream);
     }
   } else {
     switch (D) {
-      case 16: return launch_step_t<float, 16, 64>(BH, q, k, v, gamma, o, h, u, n2, cc, stream);
-      case 32: return launch_step_t<float, 32, 128>(BH, q, k, v, gamma, o, h, u, n2, cc, stream);
-      case 64: return launch_step_t<float, 64, 256>(BH, q, k, v, gamma, o, h, u, n2, cc, stream);
+      case 16: return launch_step_t<float, 16, 64>(BH, q, k, v, gamma, beta, o, h, u, n2, cc, stream);
+      case 32: return launch_step_t<float, 32, 128>(BH, q, k, v, gamma, beta, o, h, u, n2, cc, stream);
+      case 64: return launch_step_t<float, 64, 256>(BH, q, k, v, gamma, beta, o, h, u, n2, cc, stream);
     }
   }
   return hipErrorInvalidValue;

@@ -23,6 +23,10 @@
 // feature columns permuted the same way (a fragment is one 16-byte read), and K^T / V^T
 // fragments in the permuted token order come from transposing LDS reads.
 //
+// With the optional write gate beta_t ("Main Findings" on the ai.info summary: H_t = gamma_t
+// H_{t-1} + beta_t k_t k_t^T, likewise U_t) everything above holds for the rows sqrt(beta_t) k_t
+// and sqrt(beta_t) v_t, which is what the staging writes.
+//
 // Per chunk: stage K, V (fp16), gates and H0hat; the norm phase (k_t^T H0hat k_t from the
 // resident H0hat fragments, the Gram tiles of the own tokens) and a scan over the 64 tokens;
 // U0hat is staged; the carry advances the float32 state (held as accumulator tiles, a quarter
@@ -212,7 +216,9 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
   // registers are live, and staged at the top of the next chunk. Rows past the end of the
   // sequence are zero, with gate 1.
   bf16x8 kin[NU / NT], vin[NU / NT];
-  float gin = 1.0f;
+  float gin = 1.0f, bin = 1.0f;  // gate and write gate of token `lane`
+  // the write gates are read from the gates when there are none (and then not used)
+  const float* bsrc = A.beta ? A.beta : A.gamma;
   auto load_kv = [&](int chn) {
     refresh();  // keeps the per-lane addresses from being hoisted out of the chunk loop
     // Bounds-checked buffer loads: rows past the end of the sequence (or of the segment) read
@@ -233,9 +239,11 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
       kin[k] = buffer_load16<bf16x8>(rk, off);
       vin[k] = buffer_load16<bf16x8>(rv, off);
     }
-    const auto rg = buffer_rsrc(A.gamma + (b * (long long)Tlen + t0n) * Hn + h,
-                                nvn > 0 ? (uint32_t)(nvn - 1) * Hn * 4u + 4u : 0u);
+    const uint32_t gvalid = nvn > 0 ? (uint32_t)(nvn - 1) * Hn * 4u + 4u : 0u;
+    const auto rg = buffer_rsrc(A.gamma + (b * (long long)Tlen + t0n) * Hn + h, gvalid);
+    const auto rb = buffer_rsrc(bsrc + (b * (long long)Tlen + t0n) * Hn + h, gvalid);
     gin = buffer_load4f(rg, (uint32_t)lane * Hn * 4u);
+    bin = buffer_load4f(rb, (uint32_t)lane * Hn * 4u);
   };
   // state tiles (times sc) -> Hs as fp16 rows e = column index of the tile, permuted columns
   auto stage_tile = [&](int jr, int jc, f32x4 x) {
@@ -301,23 +309,36 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
       v_w[lane] = fast_exp2(fminf(clast - cl, 0.0f));
     }
     // ---- stage K (fp16, permuted features) and V (fp16) ------------------------------------
-    {
+    // With the write gate, the rows of token t are scaled by sqrt(beta_t) (lane t holds beta_t):
+    // the base recurrence on the scaled rows is the write-gated one.
+    auto stage_kv = [&](auto gated) {
 #pragma unroll
-    for (int k = 0; k < NU / NT; ++k) {
-      const int u = tid + k * NT;
-      const int tt = (uint32_t)u / UPR, cu = (uint32_t)u % UPR;  // u >= 0
-      const bf16x8 kv = kin[k], vv = vin[k];  // rows past the end were read as 0
-      f16x8 ko, vo;
+      for (int k = 0; k < NU / NT; ++k) {
+        const int u = tid + k * NT;
+        const int tt = (uint32_t)u / UPR, cu = (uint32_t)u % UPR;  // u >= 0
+        const bf16x8 kv = kin[k], vv = vin[k];  // rows past the end were read as 0
+        f16x8 ko, vo;
+        if constexpr (decltype(gated)::value) {
+          const float sb = sqrtf(lane_read(bin, tt));
 #pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        ko[i] = (f16)(float)kv[i];
-        vo[i] = (f16)(float)vv[i];
+          for (int i = 0; i < 8; ++i) {
+            ko[i] = (f16)((float)kv[i] * sb);
+            vo[i] = (f16)((float)vv[i] * sb);
+          }
+        } else {
+#pragma unroll
+          for (int i = 0; i < 8; ++i) {
+            ko[i] = (f16)(float)kv[i];
+            vo[i] = (f16)(float)vv[i];
+          }
+        }
+        *reinterpret_cast<f16x8*>(Vp + tt * LDD + 8 * cu) = vo;
+        *reinterpret_cast<f16x4*>(Kp + tt * LDD + pcol(8 * cu)) = f16x4{ko[0], ko[1], ko[2], ko[3]};
+        *reinterpret_cast<f16x4*>(Kp + tt * LDD + pcol(8 * cu + 4)) = f16x4{ko[4], ko[5], ko[6], ko[7]};
       }
-      *reinterpret_cast<f16x8*>(Vp + tt * LDD + 8 * cu) = vo;
-      *reinterpret_cast<f16x4*>(Kp + tt * LDD + pcol(8 * cu)) = f16x4{ko[0], ko[1], ko[2], ko[3]};
-      *reinterpret_cast<f16x4*>(Kp + tt * LDD + pcol(8 * cu + 4)) = f16x4{ko[4], ko[5], ko[6], ko[7]};
-    }
-    }
+    };
+    if (A.beta) stage_kv(std::true_type());
+    else stage_kv(std::false_type());
     stage_h(n0inv);  // H0hat
     lds_barrier();
 
@@ -718,7 +739,8 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
 // For each (segment, head): the state reached from a zero state over the segment's tokens and
 // the segment's total log2 gate. Unrolling the carry H <- Gam_C H + K^T diag(w) K over the
 // segment gives one weighted sum over its tokens,
-//   dH = sum_s w_s k_s k_s^T,  dU = sum_s w_s v_s k_s^T,  w_s = 2^(log2 of the gates after s),
+//   dH = sum_s w_s k_s k_s^T,  dU = sum_s w_s v_s k_s^T,  w_s = 2^(log2 of the gates after s)
+// (times beta_s with the write gate),
 // so the tokens are taken in blocks of 64 from the last block to the first, with the gate sum
 // of the blocks already taken as the suffix of every weight, and no rescaling of the state.
 // Matrix-core operands are bf16: K and V exactly, the weighted keys w k as a hi + lo pair
@@ -798,7 +820,9 @@ void summary_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J
 
   // rows of two blocks in registers (register set q holds block p with p % 2 == q)
   bf16x8 kr[2][NUT], vr[2][NUT];
-  float gr[2];
+  float gr[2], br[2];  // gates and write gates (lane = token)
+  // the write gates are read from the gates when there are none (and then not used)
+  const float* bsrc = A.beta ? A.beta : A.gamma;
   auto load_block = [&](int p, int q) {
     refresh();
     const int pv = p < NB ? p : NB - 1;
@@ -816,9 +840,11 @@ void summary_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J
       kr[q][k] = buffer_load16<bf16x8>(rk, off);
       vr[q][k] = buffer_load16<bf16x8>(rv, off);
     }
-    const auto rg = buffer_rsrc(A.gamma + (b * (long long)Tlen + t0n) * Hn + h,
-                                nvn > 0 ? (uint32_t)(nvn - 1) * Hn * 4u + 4u : 0u);
+    const uint32_t gvalid = nvn > 0 ? (uint32_t)(nvn - 1) * Hn * 4u + 4u : 0u;
+    const auto rg = buffer_rsrc(A.gamma + (b * (long long)Tlen + t0n) * Hn + h, gvalid);
+    const auto rb = buffer_rsrc(bsrc + (b * (long long)Tlen + t0n) * Hn + h, gvalid);
     gr[q] = buffer_load4f(rg, (uint32_t)lane * Hn * 4u);
+    br[q] = buffer_load4f(rb, (uint32_t)lane * Hn * 4u);
   };
   auto write_block = [&](int slot, int q) {
     refresh();
@@ -844,13 +870,14 @@ void summary_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J
   float suffix = 0.0f;  // log2 gate sum of the blocks already weighted (the later ones)
 
   // weights of block p (lane = token), from its gates in register set q, one phase before
-  // its products: 2^(log2 of the gates after the token)
+  // its products: 2^(log2 of the gates after the token), times the token's write gate
   auto weigh = [&](int p, int q) {
     const int nv = p < NB ? min(CB, t_end - block_t0(p)) : 0;
     const float l2 = lane < nv ? log2_gate(gr[q]) : 0.0f;
     const float cl = scan_add<kWave>(l2);
     const float clast = lane_value(cl, CB - 1);
-    v_wl[(p & 1) * CB + lane] = fast_exp2(fminf(clast - cl + suffix, 0.0f));
+    const float bw = A.beta ? br[q] : 1.0f;
+    v_wl[(p & 1) * CB + lane] = fast_exp2(fminf(clast - cl + suffix, 0.0f)) * bw;
     suffix += clast;
   };
   // block p from slot p % 2 into the state

@@ -25,8 +25,8 @@ GKA_FP32 = 1
 GKA_MAX_ITERS = 64
 STATUS = {0: "GKA_OK", 1: "GKA_ERR_NULL", 2: "GKA_ERR_SHAPE", 3: "GKA_ERR_VALUE",
           4: "GKA_ERR_DTYPE", 5: "GKA_ERR_WORKSPACE", 6: "GKA_ERR_HIP", 7: "GKA_ERR_ALIAS"}
-EXPORTED = ["gka_fwd_workspace_bytes", "gka_fwd_chunked", "gka_step", "gka_status_str",
-            "gka_abi_version"]
+EXPORTED = ["gka_fwd_workspace_bytes", "gka_fwd_chunked", "gka_step", "gka_fwd_chunked_beta",
+            "gka_step_beta", "gka_status_str", "gka_abi_version"]
 
 
 class GkaParams(ctypes.Structure):
@@ -63,6 +63,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gka_fwd_chunked.restype = ctypes.c_int
     lib.gka_step.argtypes = [P, vp, vp, vp, fp, vp, fp, fp, fp, vp]
     lib.gka_step.restype = ctypes.c_int
+    lib.gka_fwd_chunked_beta.argtypes = [P, vp, vp, vp, fp, fp, vp, fp, fp, fp, fp, vp,
+                                         ctypes.c_size_t, vp, ctypes.c_void_p]
+    lib.gka_fwd_chunked_beta.restype = ctypes.c_int
+    lib.gka_step_beta.argtypes = [P, vp, vp, vp, fp, fp, vp, fp, fp, fp, vp]
+    lib.gka_step_beta.restype = ctypes.c_int
     lib.gka_status_str.argtypes = [ctypes.c_int]
     lib.gka_status_str.restype = ctypes.c_char_p
     lib.gka_abi_version.argtypes = []
@@ -103,6 +108,14 @@ def _require_io(q, k, v, gamma, o, state):
         raise ValueError("q, k, v, o must have the same shape")
 
 
+def _require_beta(beta, shape):
+    """The write gate: None, or a dense float32 tensor of the gates' shape."""
+    if beta is None:
+        return
+    if beta.dtype != torch.float32 or not beta.is_contiguous() or tuple(beta.shape) != tuple(shape):
+        raise ValueError(f"beta must be a dense float32 tensor of shape {tuple(shape)}")
+
+
 def _stream(stream) -> ctypes.c_void_p:
     s = torch.cuda.current_stream() if stream is None else stream
     return ctypes.c_void_p(s.cuda_stream)
@@ -136,40 +149,65 @@ def workspace_bytes(B, T, H, D, chunk, iters, a, dtype_code, segments=0) -> int:
 def fwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor, a: float,
                 iters: int, chunk: int = 64, state: Optional[GkaState] = None,
                 return_hnorm: bool = False, segments: int = 0, out: Optional[torch.Tensor] = None,
-                workspace: Optional[torch.Tensor] = None, stream=None, phase_events=None):
+                workspace: Optional[torch.Tensor] = None, stream=None, phase_events=None,
+                beta: Optional[torch.Tensor] = None):
     """gka_fwd_chunked on [B, T, H, D] tensors; returns o (and per-token ||H_t||_F [B,T,H]).
 
     ``state`` (optional) is read as the initial state and overwritten with the final one.
     ``phase_events`` (optional) is a ctypes array of 4 hipEvent_t handles recorded at the
-    phase boundaries (see include/gka.h).
+    phase boundaries (see include/gka.h). ``beta`` (optional, float32 [B, T, H]) is the
+    per-token write gate; with it the call goes to gka_fwd_chunked_beta.
     """
     lib = load()
     B, T, H, D = q.shape
     p = make_params(B, T, H, D, chunk, iters, a, _dtype_code(q), segments)
     o = torch.empty_like(q) if out is None else out
     _require_io(q, k, v, gamma, o, state)
+    _require_beta(beta, (B, T, H))
     hn = torch.empty(B, T, H, device=q.device, dtype=torch.float32) if return_hnorm else None
     need = int(lib.gka_fwd_workspace_bytes(ctypes.byref(p)))
     if workspace is None and need > 0:
         workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
-    st = lib.gka_fwd_chunked(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(o),
-                             _ptr(state.h if state else None), _ptr(state.u if state else None),
-                             _ptr(state.n2 if state else None), _ptr(hn), _ptr(workspace),
-                             ctypes.c_size_t(workspace.numel() if workspace is not None else 0),
-                             _stream(stream), phase_events)
+    rest = (_ptr(o), _ptr(state.h if state else None), _ptr(state.u if state else None),
+            _ptr(state.n2 if state else None), _ptr(hn), _ptr(workspace),
+            ctypes.c_size_t(workspace.numel() if workspace is not None else 0),
+            _stream(stream), phase_events)
+    if beta is None:
+        st = lib.gka_fwd_chunked(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), *rest)
+    else:
+        st = lib.gka_fwd_chunked_beta(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma),
+                                      _ptr(beta), *rest)
     _check(st)
     return (o, hn) if return_hnorm else o
 
 
+def fwd_chunked_beta(q, k, v, gamma, beta, a, iters, **kw):
+    """gka_fwd_chunked_beta: fwd_chunked with the per-token write gate beta [B, T, H]."""
+    return fwd_chunked(q, k, v, gamma, a, iters, beta=beta, **kw)
+
+
 def step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor, a: float,
-         iters: int, state: GkaState, out: Optional[torch.Tensor] = None, stream=None):
-    """gka_step on [B, H, D] tensors; updates ``state`` in place and returns o [B, H, D]."""
+         iters: int, state: GkaState, out: Optional[torch.Tensor] = None, stream=None,
+         beta: Optional[torch.Tensor] = None):
+    """gka_step on [B, H, D] tensors; updates ``state`` in place and returns o [B, H, D].
+    ``beta`` (optional, float32 [B, H]) is the write gate; with it the call goes to
+    gka_step_beta."""
     lib = load()
     B, H, D = q.shape
     p = make_params(B, 1, H, D, 64, iters, a, _dtype_code(q))
     o = torch.empty_like(q) if out is None else out
     _require_io(q, k, v, gamma, o, state)
-    st = lib.gka_step(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(o),
-                      _ptr(state.h), _ptr(state.u), _ptr(state.n2), _stream(stream))
+    _require_beta(beta, (B, H))
+    rest = (_ptr(o), _ptr(state.h), _ptr(state.u), _ptr(state.n2), _stream(stream))
+    if beta is None:
+        st = lib.gka_step(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), *rest)
+    else:
+        st = lib.gka_step_beta(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma),
+                               _ptr(beta), *rest)
     _check(st)
     return o
+
+
+def step_beta(q, k, v, gamma, beta, a, iters, state, **kw):
+    """gka_step_beta: step with the write gate beta [B, H]."""
+    return step(q, k, v, gamma, a, iters, state, beta=beta, **kw)

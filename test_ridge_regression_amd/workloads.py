@@ -16,7 +16,9 @@ for the forward itself, so every input is drawn here:
     pre-activations z ~ N(mu, sd) of shape [tokens]; gate gamma = sigmoid(z) stored as float32;
   * q and k are divided by their L2 norm over D (the block's l2 normalisation, caption of
     Figure 2 on the pith.science page, is the caller's job);
-  * bf16 workloads round q, k, v float64 -> float32 -> bfloat16 (round to nearest even).
+  * bf16 workloads round q, k, v float64 -> float32 -> bfloat16 (round to nearest even);
+  * the optional write gates beta_t (the beta-augmented recurrence) come from streams of their
+    own: beta = sigmoid(z), z ~ N(0, 2), stored as float32, which spreads them over (0, 1).
 
 The arrays returned are float64 copies of exactly the values the device receives (the decode
 step arrays are float32, which holds every bf16 value exactly). Independent streams per head
@@ -95,7 +97,7 @@ def _unit(x: np.ndarray) -> np.ndarray:
 
 
 TOKEN_BLOCK = 4096  # tokens per independent stream
-TAG_PREFILL, TAG_WARMUP, TAG_STEPS = 0, 1, 2
+TAG_PREFILL, TAG_WARMUP, TAG_STEPS, TAG_BETA = 0, 1, 2, 3
 
 
 def _workers() -> int:
@@ -167,6 +169,25 @@ def make_prefill(B: int, T: int, H: int, D: int, gate_mu: float, gate_sd: float,
     cells = [(0, i, b, h) for i, (b, h) in enumerate(heads)]
     return _draw_grid(TAG_PREFILL, cells, 1, len(cells), T, D, gate_mu, gate_sd, dtype, seed,
                       gamma_override)
+
+
+def make_beta(B: int, T: int, H: int, seed: int, beta_mu: float = 0.0, beta_sd: float = 2.0,
+              heads: Optional[Sequence[Tuple[int, int]]] = None) -> np.ndarray:
+    """Write gates beta_t = sigmoid(z), z ~ N(beta_mu, beta_sd), stored as float32 (returned as
+    float64 copies): [B, T, H], or [1, T, P] for the sampled ``heads``. Each head and block of
+    TOKEN_BLOCK tokens has its own stream keyed [seed, TAG_BETA, b, h, j], so the gates of a
+    head do not depend on which other heads are drawn, and q, k, v, gamma are unchanged."""
+    pairs = [(b, h) for b in range(B) for h in range(H)] if heads is None else list(heads)
+    out = np.empty((len(pairs), T), dtype=np.float64)
+    for i, (b, h) in enumerate(pairs):
+        for t0 in range(0, T, TOKEN_BLOCK):
+            n = min(TOKEN_BLOCK, T - t0)
+            z = np.random.default_rng([seed, TAG_BETA, b, h, t0 // TOKEN_BLOCK]).normal(
+                beta_mu, beta_sd, n)
+            out[i, t0:t0 + n] = (1.0 / (1.0 + np.exp(-z))).astype(np.float32)
+    if heads is None:
+        return np.ascontiguousarray(out.reshape(B, H, T).transpose(0, 2, 1))
+    return np.ascontiguousarray(out.T[None])
 
 
 def make_workload(w: Workload, T: Optional[int] = None, B: Optional[int] = None,

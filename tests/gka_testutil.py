@@ -49,11 +49,14 @@ def state_to_dev(h, u, n2) -> gka.GkaState:
     return gka.GkaState(dev(h), dev(u), dev(n2))
 
 
-def run_prefill(q, k, v, g, a, iters, chunk, dtype, state=None, segments=0, return_hnorm=True):
-    """Run gka_fwd_chunked on device copies of float64 inputs; returns numpy results."""
+def run_prefill(q, k, v, g, a, iters, chunk, dtype, state=None, segments=0, return_hnorm=True,
+                beta=None):
+    """Run gka_fwd_chunked (gka_fwd_chunked_beta with ``beta``) on device copies of float64
+    inputs; returns numpy results."""
     st = None if state is None else state_to_dev(*state)
     out = gka.fwd_chunked(dev(q, dtype), dev(k, dtype), dev(v, dtype), dev(g), a, iters, chunk,
-                          state=st, return_hnorm=return_hnorm, segments=segments)
+                          state=st, return_hnorm=return_hnorm, segments=segments,
+                          beta=None if beta is None else dev(beta))
     torch.cuda.synchronize()
     o, hn = out if return_hnorm else (out, None)
     res = dict(o=host(o), hnorm=None if hn is None else host(hn))

@@ -33,7 +33,7 @@ def test_header_declares_the_bound_functions():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.gka_abi_version() == 1
+    assert lib.gka_abi_version() == 2
 
 
 def test_status_strings(lib):
@@ -130,3 +130,46 @@ def test_step_rejects_bad_arguments(lib):
     assert step(lib, params(dtype_code=3)) == 4
     assert step(lib, params(), h=ctypes.c_void_p(ADDR[5] + 8)) == 2
     assert step(lib, params(), o=VP[2]) == 7
+
+
+def fwd_beta(lib, p, beta, o=VP[4], q=VP[0], g=VP[3]):
+    return lib.gka_fwd_chunked_beta(ctypes.byref(p) if p is not None else None, q, VP[1], VP[2],
+                                    g, beta, o, None, None, None, None, None, ctypes.c_size_t(0),
+                                    None, None)
+
+
+def step_beta(lib, p, beta, o=VP[4]):
+    return lib.gka_step_beta(ctypes.byref(p) if p is not None else None, VP[0], VP[1], VP[2],
+                             VP[3], beta, o, VP[5], VP[6], VP[7], None)
+
+
+def test_beta_entry_points_check_like_the_base_ones(lib):
+    one = dict(B=1, H=1, T=64, segments=1)  # a single segment: no workspace needed
+    # the base checks come first, in the same order
+    assert fwd_beta(lib, None, VP[9]) == 1
+    assert fwd_beta(lib, params(D=48, **one), VP[9]) == 2
+    assert fwd_beta(lib, params(iters=0, **one), VP[9]) == 3
+    assert fwd_beta(lib, params(**one), VP[9], q=None) == 1
+    assert fwd_beta(lib, params(**one), VP[9], o=VP[0]) == 7
+    assert step_beta(lib, params(dtype_code=3), VP[9]) == 4
+    # the write gate itself: 4-byte aligned, not overlapping o
+    assert fwd_beta(lib, params(**one), ctypes.c_void_p(ADDR[9] + 2)) == 2
+    assert fwd_beta(lib, params(**one), ctypes.c_void_p(ADDR[4] + 64)) == 7  # beta inside o
+    assert step_beta(lib, params(), ctypes.c_void_p(ADDR[9] + 1)) == 2
+    assert step_beta(lib, params(), VP[4]) == 7  # beta == o
+    # an empty sequence is a no-op with or without the gate
+    assert fwd_beta(lib, params(T=0), None, q=None, g=None, o=None) == 0
+    assert fwd_beta(lib, params(T=0), VP[9], q=None, g=None, o=None) == 0
+
+
+def test_binding_checks_the_write_gate():
+    import torch
+    q = torch.zeros(1, 64, 1, 32, dtype=torch.bfloat16)
+    g = torch.ones(1, 64, 1)
+    for bad in (torch.ones(1, 64, 1, dtype=torch.float64), torch.ones(1, 64, 2),
+                torch.ones(1, 64, 2)[:, :, :1]):
+        with pytest.raises(ValueError):
+            gka._require_beta(bad, (1, 64, 1))
+    gka._require_beta(None, (1, 64, 1))
+    gka._require_beta(g, (1, 64, 1))
+    assert q.shape[:3] == g.shape
