@@ -4,8 +4,10 @@ Only ``tests/``, ``__graft_entry__.smoke()`` and ``bench.py``'s CPU-baseline leg
 It is plain float64 numpy written from the pages' description of the layer and shares no code,
 header, table or helper with the HIP library in ``test_ridge_regression_amd``.
 """
-from .gka_oracle import (chebyshev_rates, chebyshev_solve, chebyshev_weights, cholesky_solve,
-                         gka_forward_ref, gka_step_ref, ridge_bruteforce)
+from .gka_oracle import (SOLVERS, agd_solve, cg_solve, chebyshev_rates, chebyshev_solve,
+                         chebyshev_weights, cholesky_solve, gd_solve, gka_forward_ref,
+                         gka_step_ref, ridge_bruteforce, solver_residuals)
 
-__all__ = ["chebyshev_rates", "chebyshev_solve", "chebyshev_weights", "cholesky_solve",
-           "gka_forward_ref", "gka_step_ref", "ridge_bruteforce"]
+__all__ = ["SOLVERS", "agd_solve", "cg_solve", "chebyshev_rates", "chebyshev_solve",
+           "chebyshev_weights", "cholesky_solve", "gd_solve", "gka_forward_ref", "gka_step_ref",
+           "ridge_bruteforce", "solver_residuals"]

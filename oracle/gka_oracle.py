@@ -30,6 +30,12 @@ is the plainest reading that all of them support):
                     Van Loan, "Matrix Computations" (cited in the pages' reference list)
   exact mode        Cholesky solve of the same SPD system, for the pins only (the pages'
                     exact-solver reference, ai.info summary "Key Contributions" 2)
+  residuals         optionally ||q_t - A_t x_i|| for i = 0..iters, the quantity of the pages'
+                    convergence plot (pith.science page, caption of Figure 1 (a); ai.info
+                    summary, "Main Findings", the bullet comparing CH with CG)
+  comparators       conjugate gradient, gradient descent and accelerated gradient descent on
+                    the same systems (the solvers CH is compared with in those two passages),
+                    for the convergence comparison only; the layer itself uses CH
 
   write gate        optional beta_t in [0, 1] scaling the token's write (ai.info summary, "Main
                     Findings", the beta_t-augmented variant; its "Future Directions" call it the
@@ -42,7 +48,8 @@ Readings taken where the pages are silent (each also listed in the design notes)
     i.e. r - 1 matrix-vector products with A;
   * gamma_t decays the state before token t writes (the gating fragment's eta_{t,i});
   * when ||H_t||_F = 0 (only possible when every weighted key so far is zero, hence U_t = 0)
-    the solve is defined as x_t = 0 and o_t = 0;
+    the solve is defined as x_t = 0 and o_t = 0; every iterate is then 0, so every residual
+    q_t - A_t x_i is q_t;
   * the initial state is zero unless the caller passes one.
 
 Everything is float64 and vectorised only across independent (batch, head) pairs; the loop
@@ -106,6 +113,102 @@ def chebyshev_solve(A: np.ndarray, b: np.ndarray, mu: np.ndarray, L: np.ndarray,
     return x
 
 
+# ------------------------------------------------------------------------------------------
+# Comparator solvers (convergence comparison only; x_0 = 0 and residuals[i] = ||b - A x_i||)
+# ------------------------------------------------------------------------------------------
+
+def _matvec(A, x):
+    return np.einsum("...ij,...j->...i", A, x)
+
+
+def cg_solve(A: np.ndarray, b: np.ndarray, iters: int, residuals: Optional[list] = None):
+    """Conjugate gradient (Hestenes-Stiefel) for SPD A; iterate x_i after i steps (i products
+    with A). A system whose residual is exactly 0 stays where it is."""
+    x = np.zeros_like(b)
+    r = b.copy()
+    p = r.copy()
+    rr = np.einsum("...i,...i->...", r, r)
+    if residuals is not None:
+        residuals.append(np.sqrt(rr))
+    for _ in range(iters):
+        Ap = _matvec(A, p)
+        pAp = np.einsum("...i,...i->...", p, Ap)
+        alpha = np.where(rr > 0.0, rr / np.where(pAp > 0.0, pAp, 1.0), 0.0)[..., None]
+        x = x + alpha * p
+        r = r - alpha * Ap
+        rr_new = np.einsum("...i,...i->...", r, r)
+        beta = np.where(rr > 0.0, rr_new / np.where(rr > 0.0, rr, 1.0), 0.0)[..., None]
+        p = r + beta * p
+        rr = rr_new
+        if residuals is not None:
+            residuals.append(np.linalg.norm(b - _matvec(A, x), axis=-1))
+    return x
+
+
+def gd_solve(A: np.ndarray, b: np.ndarray, mu, L, iters: int,
+             residuals: Optional[list] = None):
+    """Gradient descent on 1/2 x^T A x - b^T x with the fixed step c = 2 / (L + mu) (the
+    optimal constant step for spectrum in [mu, L]): x_{i+1} = x_i + c (b - A x_i). Its first
+    iterate equals CH's x_1."""
+    c = (2.0 / (np.asarray(L, np.float64) + np.asarray(mu, np.float64)))[..., None]
+    x = np.zeros_like(b)
+    if residuals is not None:
+        residuals.append(np.linalg.norm(b, axis=-1))
+    for _ in range(iters):
+        x = x + c * (b - _matvec(A, x))
+        if residuals is not None:
+            residuals.append(np.linalg.norm(b - _matvec(A, x), axis=-1))
+    return x
+
+
+def agd_solve(A: np.ndarray, b: np.ndarray, mu, L, iters: int,
+              residuals: Optional[list] = None):
+    """Accelerated gradient descent (Nesterov's constant-momentum scheme for an L-smooth,
+    mu-strongly convex objective, here 1/2 x^T A x - b^T x): y_i = x_i + m (x_i - x_{i-1}),
+    x_{i+1} = y_i + (b - A y_i) / L, m = (sqrt(kappa) - 1) / (sqrt(kappa) + 1), kappa = L / mu,
+    x_{-1} = x_0 = 0."""
+    L = np.asarray(L, np.float64)
+    kappa = L / np.asarray(mu, np.float64)
+    m = ((np.sqrt(kappa) - 1.0) / (np.sqrt(kappa) + 1.0))[..., None]
+    step = (1.0 / L)[..., None]
+    x_prev = np.zeros_like(b)
+    x = np.zeros_like(b)
+    if residuals is not None:
+        residuals.append(np.linalg.norm(b, axis=-1))
+    for _ in range(iters):
+        y = x + m * (x - x_prev)
+        x_prev, x = x, y + step * (b - _matvec(A, y))
+        if residuals is not None:
+            residuals.append(np.linalg.norm(b - _matvec(A, x), axis=-1))
+    return x
+
+
+SOLVERS = ("cheb", "cg", "gd", "agd")
+
+
+def solver_residuals(H: np.ndarray, q: np.ndarray, a: float, iters: int, solver: str):
+    """Residual norms ||q - A x_i||, i = 0..iters, of one solver on the layer's systems
+    A = H + a ||H||_F I with the layer's interval [mu, L] = [a ||H||_F, (1 + a) ||H||_F].
+    H: [..., D, D] PSD with ||H||_F > 0, q: [..., D]. Returns [..., iters + 1]."""
+    H = np.asarray(H, np.float64)
+    q = np.asarray(q, np.float64)
+    n = np.linalg.norm(H, axis=(-2, -1))
+    A = H + (a * n)[..., None, None] * np.eye(H.shape[-1])
+    mu, L = a * n, (1.0 + a) * n
+    res: list = []
+    if solver == "cheb":
+        chebyshev_solve(A, q, mu, L, iters, res)
+    elif solver == "cg":
+        cg_solve(A, q, iters, res)
+    elif solver == "gd":
+        gd_solve(A, q, mu, L, iters, res)
+    elif solver == "agd":
+        agd_solve(A, q, mu, L, iters, res)
+    else:
+        raise ValueError(f"unknown solver {solver!r}")
+    return np.stack(res, axis=-1)
+
+
 def cholesky_solve(A: np.ndarray, b: np.ndarray) -> np.ndarray:
     """Exact solve of the SPD system A x = b through its Cholesky factor (batched)."""
     Lc = np.linalg.cholesky(A)
@@ -143,7 +246,11 @@ def _token(H, U, n2, q, k, v, g, a, iters, mode, residuals=None, b=None):
     if mode == "cheb":
         mu = np.where(zero, 1.0, lam)
         L = np.where(zero, 1.0, lam + n)
-        x = chebyshev_solve(A, q, mu, L, iters, residuals)
+        rl = [] if residuals is not None else None
+        x = chebyshev_solve(A, q, mu, L, iters, rl)
+        if residuals is not None:  # x_t = 0 for ||H_t|| = 0: every residual is q_t
+            qn = np.linalg.norm(q, axis=-1)
+            residuals.extend(np.where(zero, qn, r) for r in rl)
     elif mode == "exact":
         x = cholesky_solve(A, q)
     else:
@@ -206,24 +313,29 @@ def gka_forward_ref(q, k, v, gamma, a: float, iters: int, mode: str = "cheb",
 
 
 def gka_step_ref(q, k, v, gamma, a: float, iters: int, h, u, n2, mode: str = "cheb",
-                 beta=None):
+                 beta=None, return_residuals: bool = False):
     """One recurrent decode step: update the carried state with the token, then solve.
 
     q, k, v: [B, H, D]; gamma and the optional write gate beta: [B, H]; h, u: [B, H, D, D];
     n2: [B, H].
-    Returns (o [B,H,D], h, u, n2) -- new arrays, inputs untouched.
+    Returns (o [B,H,D], h, u, n2) -- new arrays, inputs untouched -- and, with
+    ``return_residuals``, a fifth entry [B, H, iters+1]: ||q - A x_i|| for i = 0..iters.
     """
     q, k, v = (np.asarray(x, dtype=np.float64) for x in (q, k, v))
     B, Hh, D = q.shape
     N = B * Hh
+    rl = [] if return_residuals else None
     H2, U2, n22, _, o = _token(np.asarray(h, np.float64).reshape(N, D, D),
                                np.asarray(u, np.float64).reshape(N, D, D),
                                np.asarray(n2, np.float64).reshape(N),
                                q.reshape(N, D), k.reshape(N, D), v.reshape(N, D),
-                               np.asarray(gamma, np.float64).reshape(N), a, iters, mode, None,
+                               np.asarray(gamma, np.float64).reshape(N), a, iters, mode, rl,
                                None if beta is None else np.asarray(beta, np.float64).reshape(N))
-    return (o.reshape(B, Hh, D), H2.reshape(B, Hh, D, D), U2.reshape(B, Hh, D, D),
-            n22.reshape(B, Hh))
+    out = (o.reshape(B, Hh, D), H2.reshape(B, Hh, D, D), U2.reshape(B, Hh, D, D),
+           n22.reshape(B, Hh))
+    if return_residuals:
+        out = out + (np.stack(rl, axis=-1).reshape(B, Hh, iters + 1),)
+    return out
 
 
 def ridge_bruteforce(q, k, v, gamma, a: float, beta=None):

@@ -9,8 +9,8 @@ import os
 import numpy as np
 import pytest
 
-from oracle import (chebyshev_rates, chebyshev_solve, chebyshev_weights, gka_forward_ref,
-                    gka_step_ref, ridge_bruteforce)
+from oracle import (agd_solve, cg_solve, chebyshev_rates, chebyshev_solve, chebyshev_weights,
+                    gd_solve, gka_forward_ref, gka_step_ref, ridge_bruteforce, solver_residuals)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -439,3 +439,131 @@ def test_beta_step_chain_equals_forward():
                                    beta=beta[:, t])
         np.testing.assert_allclose(o, full["o"][:, t], rtol=1e-12, atol=1e-14)
     np.testing.assert_allclose(h, full["h"], rtol=1e-12, atol=1e-14)
+
+
+# ------------------------------------------------------------------------------------------
+# residual norms and the comparator solvers of the convergence plot (pith.science page,
+# caption of Figure 1 (a); ai.info summary, "Main Findings", the CH-versus-CG bullet)
+# ------------------------------------------------------------------------------------------
+
+def _spd(rng, D, lo=0.2, hi=1.0):
+    Q, _ = np.linalg.qr(rng.standard_normal((D, D)))
+    lam = np.linspace(lo, hi, D)
+    return Q @ np.diag(lam) @ Q.T, Q, lam
+
+
+def test_cg_first_step_is_exact_line_search():
+    # x_1 of CG is the steepest-descent step with exact line search: (b.b / b.Ab) b
+    rng = np.random.default_rng(40)
+    A, _, _ = _spd(rng, 9)
+    b = rng.standard_normal(9)
+    x1 = cg_solve(A, b, 1)
+    np.testing.assert_allclose(x1, (b @ b) / (b @ A @ b) * b, rtol=1e-13)
+
+
+def test_cg_second_iterate_is_the_krylov_galerkin_solution():
+    # x_2 minimises the A-norm error over span{b, A b}: x = V (V^T A V)^-1 V^T b
+    rng = np.random.default_rng(41)
+    A, _, _ = _spd(rng, 11)
+    b = rng.standard_normal(11)
+    V = np.stack([b, A @ b], axis=1)
+    x_ref = V @ np.linalg.solve(V.T @ A @ V, V.T @ b)
+    np.testing.assert_allclose(cg_solve(A, b, 2), x_ref, rtol=1e-10, atol=1e-12)
+
+
+def test_cg_terminates_after_as_many_steps_as_distinct_eigenvalues():
+    rng = np.random.default_rng(42)
+    D = 12
+    Q, _ = np.linalg.qr(rng.standard_normal((D, D)))
+    lam = np.array([0.3] * 4 + [0.7] * 5 + [1.1] * 3)  # three distinct eigenvalues
+    A = Q @ np.diag(lam) @ Q.T
+    b = rng.standard_normal(D)
+    res = []
+    cg_solve(A, b, 4, res)
+    assert res[2] > 1e-3 * res[0]
+    assert res[3] < 1e-12 * res[0]
+    assert res[4] < 1e-12 * res[0]  # a converged system stays converged (no 0/0)
+
+
+def test_gd_residuals_match_the_eigen_closed_form():
+    # r_i = (I - c A)^i b with c = 2 / (L + mu)
+    rng = np.random.default_rng(43)
+    A, Q, lam = _spd(rng, 10, 0.25, 1.25)
+    b = rng.standard_normal(10)
+    mu, L = 0.25, 1.25
+    c = 2.0 / (L + mu)
+    res = []
+    gd_solve(A, b, mu, L, 7, res)
+    for i, r in enumerate(res):
+        want = np.linalg.norm(Q @ ((1.0 - c * lam) ** i * (Q.T @ b)))
+        assert abs(r - want) <= 1e-12 * np.linalg.norm(b)
+
+
+def test_agd_residuals_match_the_characteristic_roots():
+    # per eigen-mode lambda the error e_i = x* - x_i obeys
+    # e_{i+1} = s ((1 + m) e_i - m e_{i-1}),  s = 1 - lambda / L,  e_{-1} = e_0 = x*,
+    # so e_i = c1 z1^i + c2 z2^i with z1, z2 the roots of z^2 - (1 + m) s z + m s
+    rng = np.random.default_rng(44)
+    D = 8
+    lam = np.linspace(0.3, 1.0, D)  # strictly inside (mu, L): distinct roots
+    A = np.diag(lam)
+    b = rng.standard_normal(D)
+    mu, L = 0.2, 1.1
+    kap = L / mu
+    m = (np.sqrt(kap) - 1.0) / (np.sqrt(kap) + 1.0)
+    res = []
+    agd_solve(A, b, mu, L, 9, res)
+    xs = b / lam
+    sv = 1.0 - lam / L
+    disc = ((1.0 + m) * sv) ** 2 - 4.0 * m * sv + 0j
+    z1 = ((1.0 + m) * sv + np.sqrt(disc)) / 2.0
+    z2 = ((1.0 + m) * sv - np.sqrt(disc)) / 2.0
+    # c1 + c2 = x*, c1 / z1 + c2 / z2 = x*
+    c1 = xs * (1.0 - 1.0 / z2) / (1.0 / z1 - 1.0 / z2)
+    c2 = xs - c1
+    for i, r in enumerate(res):
+        e = (c1 * z1 ** i + c2 * z2 ** i).real
+        assert abs(r - np.linalg.norm(lam * e)) <= 1e-12 * np.linalg.norm(b)
+
+
+def test_solver_residuals_use_the_layer_systems():
+    # the systems are A = H + a ||H||_F I: CG reaches their solution in D steps, and the
+    # Chebyshev residuals are those the layer records for the same token
+    rng = np.random.default_rng(45)
+    q, k, v, g = _rand_inputs(rng, 1, 9, 1, 6)
+    out = gka_forward_ref(q, k, v, g, 0.1, 5, return_residuals=True)
+    H = out["h"][0, 0]
+    qt = q[0, -1, 0]
+    ch = solver_residuals(H, qt, 0.1, 5, "cheb")
+    np.testing.assert_allclose(ch, out["residuals"][0, -1, 0], rtol=1e-12)
+    cg = solver_residuals(H, qt, 0.1, 6, "cg")
+    assert cg[-1] < 1e-10 * cg[0]
+    A = H + 0.1 * np.linalg.norm(H) * np.eye(6)
+    np.testing.assert_allclose(np.linalg.solve(A, qt), cg_solve(A, qt, 6), rtol=1e-8)
+    for s in ("gd", "agd"):
+        r = solver_residuals(H, qt, 0.1, 5, s)
+        assert r.shape == (6,) and abs(r[0] - np.linalg.norm(qt)) < 1e-14
+
+
+def test_residuals_of_a_token_with_zero_state_are_q():
+    # ||H_t|| = 0 (no key written yet): x_t = 0 is every iterate, so every residual is ||q_t||
+    rng = np.random.default_rng(46)
+    q, k, v, g = _rand_inputs(rng, 1, 6, 2, 5)
+    k[0, :2, 0] = 0.0  # head 0: the first two tokens write nothing
+    out = gka_forward_ref(q, k, v, g, 0.1, 6, return_residuals=True)
+    res = out["residuals"]
+    for t in range(2):
+        np.testing.assert_array_equal(res[0, t, 0], np.full(7, np.linalg.norm(q[0, t, 0])))
+    assert res[0, 2, 0, -1] < 0.1 * res[0, 2, 0, 0]
+    assert np.all(res[0, :, 1, -1] < 0.1 * res[0, :, 1, 0])
+
+
+def test_step_residuals_match_the_sequence_residuals():
+    rng = np.random.default_rng(47)
+    q, k, v, g = _rand_inputs(rng, 2, 5, 2, 4)
+    full = gka_forward_ref(q, k, v, g, 0.05, 7, return_residuals=True)
+    h, u, n2 = np.zeros((2, 2, 4, 4)), np.zeros((2, 2, 4, 4)), np.zeros((2, 2))
+    for t in range(5):
+        o, h, u, n2, r = gka_step_ref(q[:, t], k[:, t], v[:, t], g[:, t], 0.05, 7, h, u, n2,
+                                      return_residuals=True)
+        np.testing.assert_allclose(r, full["residuals"][:, t], rtol=1e-12, atol=1e-15)
