@@ -9,11 +9,12 @@ each path (measured with HIP events on the library's stream), and the float64 CP
 on a bounded sample of the prefill workload on this host.
 
 The write-gated prefill (gka_fwd_chunked_beta, same workload plus per-token write gates) is
-timed the same way and reported under "write_gate". The oracle leg also compares its outputs of
+timed the same way and reported under "write_gate"; the solver-convergence mode
+(gka_fwd_chunked_residuals) under "solver_convergence", with its residual curve. The oracle leg also compares its outputs of
 the prefix with the timed device run's.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps S] [--no-cpu]
-                       [--no-decode] [--no-beta]
+                       [--no-decode] [--no-beta] [--no-resid]
 """
 from __future__ import annotations
 
@@ -160,6 +161,51 @@ def bench_prefill(W, inputs, steps, warmup, ev, beta=None, what="prefill"):
                 summary_ms=float(np.mean(summ)), scan_ms=float(np.mean(scan)), segments=segs, o=o)
 
 
+def bench_residuals(W, inputs, steps, warmup, ev, sweep=(0.1, 0.05, 0.02)):
+    """The solver-convergence mode (gka_fwd_chunked_residuals) on the prefill workload: time
+    per call, and the geometric mean over all B*T*H tokens of ||q_t - A_t x_i|| / ||q_t|| for
+    i = 0..iters (the quantity of the pages' convergence plot), at the workload's a and over a
+    sweep of a (the pages' plot of convergence against regularisation strength)."""
+    import torch
+    from test_ridge_regression_amd import gka
+
+    qd, kd, vd, gd = inputs
+    need = gka.workspace_bytes(W.B, W.T, W.H, W.D, W.chunk, W.iters, W.a, gka.GKA_BF16)
+    ws = torch.empty(max(need, 1), device="cuda", dtype=torch.uint8)
+    o = torch.empty_like(qd)
+    res = torch.empty(W.B, W.T, W.H, W.iters + 1, device="cuda", dtype=torch.float32)
+    qn = qd.float().norm(dim=-1, keepdim=True)
+    call = lambda a: gka.fwd_chunked_residuals(qd, kd, vd, gd, a, W.iters, W.chunk, out=o,
+                                               resid=res, workspace=ws)
+    log(f"residual mode warmup {warmup}")
+    for _ in range(warmup):
+        call(W.a)
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0, t1 = ev.create(2)
+    log(f"residual mode timed {steps}")
+    ev.record(t0, stream.cuda_stream)
+    for _ in range(steps):
+        call(W.a)
+    ev.record(t1, stream.cuda_stream)
+    ev.sync(t1)
+    ms = ev.elapsed_ms(t0, t1) / steps
+    ev.destroy([t0, t1])
+
+    def curve():
+        r = (res / qn).clamp_min(1e-30).log().mean(dim=(0, 1, 2)).exp()
+        return [float(x) for x in r.cpu()]
+
+    out = {"entry_point": "gka_fwd_chunked_residuals", "workload": W.name, "ms_per_step": ms,
+           "a": W.a, "geomean_rel_residual": curve(), "sweep": {}}
+    for a in sweep:
+        call(a)
+        torch.cuda.synchronize()
+        out["sweep"][str(a)] = curve()
+    log("residual mode: " + " ".join(f"{x:.2e}" for x in out["geomean_rel_residual"]))
+    return out
+
+
 def _segments(W):
     from test_ridge_regression_amd import gka
     # the plan's segment count: workspace = B*H*S*(2 D^2 + 1)*4 + B*H*4 (rounded up to 256)
@@ -255,6 +301,7 @@ def main():
     ap.add_argument("--no-cpu", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-beta", action="store_true", help="skip the write-gated prefill")
+    ap.add_argument("--no-resid", action="store_true", help="skip the solver-convergence mode")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 512 MiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -327,6 +374,9 @@ def main():
         }
         log(f"beta prefill: {pb['ms_per_step']:.3f} ms/step (walk {pb['walk_ms']:.3f})")
         del pb, bd
+    if not args.no_resid:
+        rec["solver_convergence"] = bench_residuals(W, inputs, max(1, args.steps // 2),
+                                                    args.warmup, ev)
     del pre, inputs
     torch.cuda.empty_cache()
     if not args.no_decode:

@@ -146,6 +146,37 @@ gka_status gka_step_beta(const gka_params* p, const void* q, const void* k, cons
                          const float* gamma, const float* beta, void* o, float* h_state,
                          float* u_state, float* hnorm2, void* stream);
 
+/*
+ * Solver-convergence mode: the calls above (with the optional write gate beta, NULL = 1), which
+ * also record how the Chebyshev iteration converges on every token's system. The pages compare
+ * solvers by the residual norm per iteration (pith.science page, caption of Figure 1 (a);
+ * ai.info summary, "Main Findings", the bullet comparing CH with CG); this is that quantity
+ * for the layer's own solver, at the layer's own precision.
+ *   resid     required, float32 [B, T, H, iters + 1] (prefill) or [B, H, iters + 1] (decode),
+ *             written: resid[..., i] = ||q_t - A_t x_i||_2 for i = 0..iters, A_t = H_t + a
+ *             ||H_t||_F I and x_i the i-th Chebyshev iterate (x_0 = 0, so resid[..., 0] =
+ *             ||q_t||). The prefill reports the residual that its iteration carries (equal to
+ *             q_t - A_t x_i in exact arithmetic, computed with the same matrix-core operands as
+ *             the solve; R_iters takes one extra product), the decode step recomputes it from
+ *             x_i. Tokens with ||H_t||_F = 0 have x_i = 0 for every i and report ||q_t||
+ *             throughout; residuals past the point where the iteration's own coefficients
+ *             vanish (|1 - omega_i| < 2^-64, only for a of order 1e9 and more) are below 2^-64
+ *             ||q_t|| and are reported as 0.
+ * Everything else, o, the state and hnorm_t included, is exactly what the base call computes
+ * (the same kernels plus the residual output), so a call here replaces the base call. resid
+ * must be 4-byte aligned (GKA_ERR_SHAPE) and must not overlap o (GKA_ERR_ALIAS); NULL resid is
+ * GKA_ERR_NULL (for T > 0). The residual mode runs slower than the base call.
+ */
+gka_status gka_fwd_chunked_residuals(const gka_params* p, const void* q, const void* k,
+                                     const void* v, const float* gamma, const float* beta,
+                                     void* o, float* h_state, float* u_state, float* hnorm2,
+                                     float* hnorm_t, float* resid, void* workspace,
+                                     size_t workspace_bytes, void* stream);
+
+gka_status gka_step_residuals(const gka_params* p, const void* q, const void* k, const void* v,
+                              const float* gamma, const float* beta, void* o, float* h_state,
+                              float* u_state, float* hnorm2, float* resid, void* stream);
+
 /* Static description of a status code. */
 const char* gka_status_str(int status);
 

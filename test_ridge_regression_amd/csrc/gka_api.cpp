@@ -12,7 +12,7 @@ namespace {
 using gka::ChebConsts;
 using gka::FwdPlan;
 
-constexpr int kAbiVersion = 2;
+constexpr int kAbiVersion = 3;
 constexpr int kCUs = 256;  // MI355X compute units: the segment plan aims at one workgroup per CU
 
 bool dims_supported(int dtype, int D) {
@@ -88,13 +88,14 @@ ChebConsts cheb_consts(float a, int iters) {
   constexpr double kS0 = 0.7390851332151607;  // the fixed point of cos
   cc.iters_rs = iters;
   cc.inv_s0 = (float)(1.0 / kS0);
+  // The coefficients of step iters - 1 (which gives R_iters) are used by the residual mode only.
   double r = 1.0, s = kS0;
   for (int i = 0; i < iters; ++i) {
     cc.bts[i] = (float)(cur[i] * s);
-    if (i + 1 == iters) break;
+    cc.sres[i] = (float)s;
     const double kp = i == 0 ? 0.0 : 1.0 - om[i];
     if (i >= 1 && std::fabs(kp) < 0x1p-64) {
-      cc.iters_rs = i + 1;
+      if (i + 1 < iters) cc.iters_rs = i + 1;
       break;
     }
     const double rn = i == 0 ? 1.0 : kp / r;  // s_{i+1} / s_i
@@ -102,6 +103,10 @@ ChebConsts cheb_consts(float a, int iters) {
     cc.kys[i] = (float)(-w_of(i, om) * c / rn);
     s *= rn;
     r = rn;
+    if (i + 1 == iters) {
+      cc.sres[iters] = (float)s;
+      cc.res_extra = 1;
+    }
   }
   return cc;
 }
@@ -155,6 +160,11 @@ gka_status check_fwd(const gka_params* p) {
   return GKA_OK;
 }
 
+gka_status fwd_impl(const gka_params* p, const void* q, const void* k, const void* v,
+                    const float* gamma, const float* beta, void* o, float* h_state,
+                    float* u_state, float* hnorm2, float* hnorm_t, float* resid, void* workspace,
+                    size_t workspace_bytes, void* stream, void* const* phase_events);
+
 }  // namespace
 
 extern "C" {
@@ -194,6 +204,30 @@ gka_status gka_fwd_chunked_beta(const gka_params* p, const void* q, const void* 
                                 const float* gamma, const float* beta, void* o, float* h_state,
                                 float* u_state, float* hnorm2, float* hnorm_t, void* workspace,
                                 size_t workspace_bytes, void* stream, void* const* phase_events) {
+  return fwd_impl(p, q, k, v, gamma, beta, o, h_state, u_state, hnorm2, hnorm_t, nullptr,
+                  workspace, workspace_bytes, stream, phase_events);
+}
+
+gka_status gka_fwd_chunked_residuals(const gka_params* p, const void* q, const void* k,
+                                     const void* v, const float* gamma, const float* beta,
+                                     void* o, float* h_state, float* u_state, float* hnorm2,
+                                     float* hnorm_t, float* resid, void* workspace,
+                                     size_t workspace_bytes, void* stream) {
+  gka_status st = check_fwd(p);
+  if (st != GKA_OK) return st;
+  if (p->T > 0 && !resid) return GKA_ERR_NULL;
+  return fwd_impl(p, q, k, v, gamma, beta, o, h_state, u_state, hnorm2, hnorm_t, resid,
+                  workspace, workspace_bytes, stream, nullptr);
+}
+
+}  // extern "C"
+
+namespace {
+
+gka_status fwd_impl(const gka_params* p, const void* q, const void* k, const void* v,
+                    const float* gamma, const float* beta, void* o, float* h_state,
+                    float* u_state, float* hnorm2, float* hnorm_t, float* resid, void* workspace,
+                    size_t workspace_bytes, void* stream, void* const* phase_events) {
   gka_status st = check_fwd(p);
   if (st != GKA_OK) return st;
   const bool any_state = h_state || u_state || hnorm2;
@@ -208,6 +242,10 @@ gka_status gka_fwd_chunked_beta(const gka_params* p, const void* q, const void* 
     return GKA_ERR_ALIAS;
   if (beta && (reinterpret_cast<uintptr_t>(beta) & 3u)) return GKA_ERR_SHAPE;
   if (beta && overlap(o, n_io, beta, (size_t)p->B * p->T * p->H * sizeof(float)))
+    return GKA_ERR_ALIAS;
+  if (resid && (reinterpret_cast<uintptr_t>(resid) & 3u)) return GKA_ERR_SHAPE;
+  if (resid && overlap(o, n_io, resid,
+                       (size_t)p->B * p->T * p->H * (p->iters + 1) * sizeof(float)))
     return GKA_ERR_ALIAS;
   FwdPlan pl;
   make_plan(p, pl);
@@ -228,6 +266,7 @@ gka_status gka_fwd_chunked_beta(const gka_params* p, const void* q, const void* 
   wa.v = v;
   wa.gamma = gamma;
   wa.beta = beta;
+  wa.resid = resid;
   wa.o = o;
   wa.hnorm_t = hnorm_t;
   if (pl.S == 1) {
@@ -273,15 +312,9 @@ gka_status gka_fwd_chunked_beta(const gka_params* p, const void* q, const void* 
   return GKA_OK;
 }
 
-gka_status gka_step(const gka_params* p, const void* q, const void* k, const void* v,
-                    const float* gamma, void* o, float* h_state, float* u_state, float* hnorm2,
-                    void* stream) {
-  return gka_step_beta(p, q, k, v, gamma, nullptr, o, h_state, u_state, hnorm2, stream);
-}
-
-gka_status gka_step_beta(const gka_params* p, const void* q, const void* k, const void* v,
-                         const float* gamma, const float* beta, void* o, float* h_state,
-                         float* u_state, float* hnorm2, void* stream) {
+gka_status step_impl(const gka_params* p, const void* q, const void* k, const void* v,
+                     const float* gamma, const float* beta, void* o, float* h_state,
+                     float* u_state, float* hnorm2, float* resid, void* stream) {
   gka_status st = check_common(p);
   if (st != GKA_OK) return st;
   if (!q || !k || !v || !gamma || !o || !h_state || !u_state || !hnorm2) return GKA_ERR_NULL;
@@ -291,11 +324,40 @@ gka_status gka_step_beta(const gka_params* p, const void* q, const void* k, cons
     return GKA_ERR_ALIAS;
   if (beta && (reinterpret_cast<uintptr_t>(beta) & 3u)) return GKA_ERR_SHAPE;
   if (beta && overlap(o, n_io, beta, (size_t)p->B * p->H * sizeof(float))) return GKA_ERR_ALIAS;
+  if (resid && (reinterpret_cast<uintptr_t>(resid) & 3u)) return GKA_ERR_SHAPE;
+  if (resid && overlap(o, n_io, resid, (size_t)p->B * p->H * (p->iters + 1) * sizeof(float)))
+    return GKA_ERR_ALIAS;
   const ChebConsts cc = cheb_consts(p->a, p->iters);
   if (gka::launch_step(p->dtype, p->D, p->B * p->H, q, k, v, gamma, beta, o, h_state, u_state,
-                       hnorm2, cc, static_cast<hipStream_t>(stream)) != hipSuccess)
+                       hnorm2, resid, cc, static_cast<hipStream_t>(stream)) != hipSuccess)
     return GKA_ERR_HIP;
   return GKA_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+gka_status gka_step(const gka_params* p, const void* q, const void* k, const void* v,
+                    const float* gamma, void* o, float* h_state, float* u_state, float* hnorm2,
+                    void* stream) {
+  return step_impl(p, q, k, v, gamma, nullptr, o, h_state, u_state, hnorm2, nullptr, stream);
+}
+
+gka_status gka_step_beta(const gka_params* p, const void* q, const void* k, const void* v,
+                         const float* gamma, const float* beta, void* o, float* h_state,
+                         float* u_state, float* hnorm2, void* stream) {
+  return step_impl(p, q, k, v, gamma, beta, o, h_state, u_state, hnorm2, nullptr, stream);
+}
+
+gka_status gka_step_residuals(const gka_params* p, const void* q, const void* k, const void* v,
+                              const float* gamma, const float* beta, void* o, float* h_state,
+                              float* u_state, float* hnorm2, float* resid, void* stream) {
+  if (!resid && p) {
+    const gka_status st = check_common(p);
+    return st != GKA_OK ? st : GKA_ERR_NULL;
+  }
+  return step_impl(p, q, k, v, gamma, beta, o, h_state, u_state, hnorm2, resid, stream);
 }
 
 }  // extern "C"

@@ -256,6 +256,9 @@ __device__ inline V buffer_load8(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   static_assert(sizeof(V) == 8, "8-byte element");
   return __builtin_bit_cast(V, __builtin_amdgcn_raw_buffer_load_b64(r, off, 0, 0));
 }
+__device__ inline void buffer_store4f(float x, __amdgpu_buffer_rsrc_t r, uint32_t off) {
+  __builtin_amdgcn_raw_buffer_store_b32(__builtin_bit_cast(unsigned int, x), r, off, 0, 0);
+}
 __device__ inline float buffer_load4f(__amdgpu_buffer_rsrc_t r, uint32_t off) {
   return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
 }
@@ -386,6 +389,10 @@ struct ChebConsts {
   float krs[64];
   float kys[64];
   float bts[64];
+  // residual mode: s_i of the rescaled residuals (R_i = s_i Rt_i) for i = 0..iters, and whether
+  // the coefficients of one more step (it = iters - 1, giving R_iters) are set
+  float sres[65];
+  int res_extra;
 };
 
 }  // namespace gka

@@ -145,7 +145,8 @@ __device__ inline void prefetch_chunk(V* PreK, V* PreV, float* PreG, const T* kg
 #endif
 }
 
-template <typename T, int D, int C>
+// RES: residual mode, which also writes ||q_t - A_t x_i|| for i = 0..iters to A.resid
+template <typename T, int D, int C, bool RES>
 __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, int Hn, int N,
                                                    int S, int J, ChebConsts cc) {
   using Cfg = WalkCfg<T, D, C, 8>;
@@ -655,9 +656,10 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
       // residual update after the products of iteration it (Y = A R_i - a R_i):
       // R_{i+1} = R_{i-1} + omega_i (R_i - R_{i-1} - c A R_i) (R_1 = R_0 - c A R_0), applied as
       // kp_i R_{i-1} + kr_i R_i + ky_i Y with the coefficients expanded on the host; and
-      // X += beta_{i+1} R_{i+1}
-      auto update = [&](int it) {
-        const float kp = cc.kp[it], kr = cc.kr[it], ky = cc.ky[it], bn = cc.beta[it + 1];
+      // X += beta_{i+1} R_{i+1} (not for the residual mode's extra step, which gives R_iters)
+      auto update = [&](int it, bool updx) {
+        const float kp = cc.kp[it], kr = cc.kr[it], ky = cc.ky[it];
+        const float bn = updx ? cc.beta[it + 1] : 0.0f;
 #pragma unroll
         for (int jf = 0; jf < FPW; ++jf)
 #pragma unroll
@@ -665,9 +667,80 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
             const f32x4 rn = kp * Rp[jf][jt] + kr * R[jf][jt] + ky * Y[jf][jt];
             Rp[jf][jt] = R[jf][jt];
             R[jf][jt] = rn;
-            Xa[jf][jt] += bn * rn;
+            if (updx) Xa[jf][jt] += bn * rn;
           }
       };
+      // Residual mode: ||R_i|| per token, summed over the wave's features and lane groups, then
+      // over the feature groups through LDS (p_u is free after the norm phase); every wave
+      // takes part in the barriers, waves of feature group 0 write. A token with ||H_t|| = 0
+      // has x_i = 0 for every i: its residuals are all ||q_t||.
+      float res_q[TPW] = {};
+      auto res_reduce = [&](float(&part)[TPW], float(&out)[TPW]) {
+        if (tok_active) {
+#pragma unroll
+          for (int jt = 0; jt < TPW; ++jt) {
+            float x = part[jt];
+            x += __shfl_xor(x, 16, kWave);
+            x += __shfl_xor(x, 32, kWave);
+            if (lg == 0) p_u[fg * C + tok_of(jt) + lr] = x;
+          }
+        }
+        lds_barrier();
+        if (tok_active && fg == 0) {
+#pragma unroll
+          for (int jt = 0; jt < TPW; ++jt) {
+            float x = 0.0f;
+            for (int f = 0; f < FG; ++f) x += p_u[f * C + tok_of(jt) + lr];
+            out[jt] = x;
+          }
+        }
+        lds_barrier();
+      };
+      auto res_write = [&](int i, const float(&val)[TPW]) {
+        if (tok_active && fg == 0 && lg == 0) {
+#pragma unroll
+          for (int jt = 0; jt < TPW; ++jt) {
+            const int t = tok_of(jt) + lr;
+            if (t < nv) {
+              const float x = v_ninv[t] > 0.0f ? val[jt] : res_q[jt];
+              A.resid[((b * (long long)Tlen + t0 + t) * Hn + h) * (cc.iters + 1) + i] = x;
+            }
+          }
+        }
+      };
+      auto res_emit = [&](int i) {
+        float part[TPW], out[TPW] = {};
+#pragma unroll
+        for (int jt = 0; jt < TPW; ++jt) {
+          float x = 0.0f;
+#pragma unroll
+          for (int jf = 0; jf < FPW; ++jf) {
+            const f32x4 r = R[jf][jt];
+            x += r[0] * r[0] + r[1] * r[1] + r[2] * r[2] + r[3] * r[3];
+          }
+          part[jt] = x;
+        }
+        res_reduce(part, out);
+#pragma unroll
+        for (int jt = 0; jt < TPW; ++jt) out[jt] = sqrtf(out[jt]);
+        res_write(i, out);
+      };
+      if constexpr (RES) {
+        float part[TPW];
+#pragma unroll
+        for (int jt = 0; jt < TPW; ++jt) {
+          float x = 0.0f;
+#pragma unroll
+          for (int jf = 0; jf < FPW; ++jf)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x += to_f32(Qraw[jf][jt][i]) * to_f32(Qraw[jf][jt][i]);
+          part[jt] = x;
+        }
+        res_reduce(part, res_q);
+#pragma unroll
+        for (int jt = 0; jt < TPW; ++jt) res_q[jt] = sqrtf(res_q[jt]);
+        res_write(0, res_q);  // x_0 = 0
+      }
 
       prefetch(ch + 1);
       for (int it = 0; it + 1 < cc.iters; ++it) {
@@ -676,7 +749,17 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
         products_1(St, false);
         lds_barrier();
         products_2(fKT);
-        update(it);
+        update(it, true);
+        if constexpr (RES) res_emit(it + 1);
+      }
+      if constexpr (RES) {  // one more step on R_{r-1} gives R_r
+        write_operand(R, false);
+        lds_barrier();
+        products_1(St, false);
+        lds_barrier();
+        products_2(fKT);
+        update(cc.iters - 1, false);
+        res_emit(cc.iters);
       }
 
       refresh();
@@ -940,12 +1023,24 @@ __global__ __launch_bounds__(256) void scan_kernel(float* __restrict__ st,
   }
 }
 
+template <typename T, int D, int C, bool RES>
+static hipError_t launch_walk_rt(const FwdPlan& pl, const WalkArgs& a, const ChebConsts& cc,
+                                 hipStream_t stream) {
+  using Cfg = WalkCfg<T, D, C, 8>;
+  auto kern = walk_kernel<T, D, C, RES>;
+  static std::atomic<uint64_t> lds_set{0};
+  hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), (int)Cfg::bytes, lds_set);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(kern, dim3(pl.S, pl.B * pl.H), dim3(Cfg::NT), Cfg::bytes, stream, a, pl.B,
+                     pl.T, pl.H, pl.N, pl.S, pl.J, cc);
+  return hipGetLastError();
+}
+
 template <typename T, int D, int C>
 static hipError_t launch_walk_t(const FwdPlan& pl, bool summary, const WalkArgs& a,
                                 const ChebConsts& cc, hipStream_t stream) {
   using Cfg = WalkCfg<T, D, C, 8>;
   using CfgS = WalkCfg<T, D, C, 16>;
-  const dim3 grid(pl.S, pl.B * pl.H);
   if (summary) {
     // segments 0 .. S-2: the last segment's walk produces the final state itself
     const dim3 sgrid(pl.S - 1, pl.B * pl.H);
@@ -958,15 +1053,8 @@ static hipError_t launch_walk_t(const FwdPlan& pl, bool summary, const WalkArgs&
                        pl.S, pl.J);
     return hipGetLastError();
   }
-  auto kern = walk_kernel<T, D, C>;
-  const size_t bytes = Cfg::bytes;
-  const int threads = Cfg::NT;
-  static std::atomic<uint64_t> lds_set{0};
-  hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), (int)bytes, lds_set);
-  if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(kern, grid, dim3(threads), bytes, stream, a, pl.B, pl.T, pl.H, pl.N,
-                     pl.S, pl.J, cc);
-  return hipGetLastError();
+  if (a.resid) return launch_walk_rt<T, D, C, true>(pl, a, cc, stream);
+  return launch_walk_rt<T, D, C, false>(pl, a, cc, stream);
 }
 
 hipError_t launch_walk(const FwdPlan& pl, bool summary, const WalkArgs& a, const ChebConsts& cc,

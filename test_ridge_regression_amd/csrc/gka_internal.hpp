@@ -26,10 +26,10 @@ inline hipError_t ensure_dynamic_lds(const void* kern, int bytes, std::atomic<ui
 }
 
 // Decode step: one workgroup per (batch row, head).
+// resid (optional, [BH][iters + 1]): the residual mode's ||q - A x_i|| for i = 0..iters.
 hipError_t launch_step(int dtype, int D, int BH, const void* q, const void* k, const void* v,
                        const float* gamma, const float* beta, void* o, float* h, float* u,
-                       float* n2,
-                       const ChebConsts& cc, hipStream_t stream);
+                       float* n2, float* resid, const ChebConsts& cc, hipStream_t stream);
 
 // Prefill. Segment plan of one call: N chunks split into S segments of J chunks each.
 struct FwdPlan {
@@ -62,6 +62,7 @@ struct WalkArgs {
   float* sum_u;
   long long sum_bh, sum_seg;
   float* log2g_out;       // summary mode: per-segment log2 of the gate product [BH][S]
+  float* resid;           // optional residual norms ||q_t - A_t x_i||, [B, T, H, iters + 1]
 };
 
 hipError_t launch_walk(const FwdPlan& pl, bool summary, const WalkArgs& a, const ChebConsts& cc,

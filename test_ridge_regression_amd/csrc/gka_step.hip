@@ -21,14 +21,16 @@
 
 namespace gka {
 
-template <typename T, int D, int NT>
+// RES: residual mode, which also writes ||q - A x_i|| for i = 0..iters to resid[head][i]
+template <typename T, int D, int NT, bool RES>
 __global__ __launch_bounds__(NT) void step_kernel(const T* __restrict__ q, const T* __restrict__ k,
                                                   const T* __restrict__ v,
                                                   const float* __restrict__ gamma,
                                                   const float* __restrict__ beta,
                                                   T* __restrict__ o, float* __restrict__ hs,
                                                   float* __restrict__ us,
-                                                  float* __restrict__ n2s, ChebConsts cc) {
+                                                  float* __restrict__ n2s,
+                                                  float* __restrict__ resid, ChebConsts cc) {
   constexpr int C4 = D / 4;    // float4 groups per row
   constexpr int RS = NT / C4;  // rows covered by one pass of the workgroup
   constexpr int F = D / RS;    // rows per thread
@@ -104,10 +106,27 @@ __global__ __launch_bounds__(NT) void step_kernel(const T* __restrict__ q, const
   // Chebyshev iteration on the normalised system; thread c < D owns element c of the iterates
   const bool degenerate = !(n2 > 0.0f);
   const float inv_n = degenerate ? 0.0f : 1.0f / sqrtf(n2);
+  // residual mode: sqrt of the sum over the D threads of r^2 (every thread takes part)
+  auto block_norm = [&](float r) {
+    float s2 = wave_sum(r * r);
+    __syncthreads();  // the previous readers of red are done
+    if (lane == 0) red[0][wave] = s2;
+    __syncthreads();
+    s2 = 0.0f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) s2 += red[0][w];
+    return sqrtf(s2);
+  };
+  // ||H_t|| = 0: x_i = 0 for every i, so every residual is ||q||
+  float qn = 0.0f;
+  if constexpr (RES) {
+    qn = block_norm(q_own);
+    if (tid == 0) resid[(size_t)head * (cc.iters + 1)] = qn;  // x_0 = 0
+  }
   if (degenerate) q_own = 0.0f;  // ||H_t|| = 0: x = 0 and o = 0
-  float x = cc.c * q_own, xp = 0.0f;
-  for (int i = 1; i < cc.iters; ++i) {
-    if (tid < D) xs[tid] = x;
+  // A x_i of the normalised system (threads c < D; y = H x as column sums, H symmetric)
+  auto apply = [&](float xv) {
+    if (tid < D) xs[tid] = xv;
     __syncthreads();
     f32x4 y = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
@@ -121,16 +140,30 @@ __global__ __launch_bounds__(NT) void step_kernel(const T* __restrict__ q, const
     }
     if (lane < C4) *reinterpret_cast<f32x4*>(&part[wave][4 * c4]) = y;
     __syncthreads();
+    float ax = 0.0f;
     if (tid < D) {
       float yc = 0.0f;
 #pragma unroll
       for (int w = 0; w < NW; ++w) yc += part[w][tid];
-      const float ax = yc * inv_n + cc.a * x;
+      ax = yc * inv_n + cc.a * xv;
+    }
+    return ax;
+  };
+  auto put_res = [&](int i, float r) {
+    const float nr = block_norm(tid < D ? r : 0.0f);
+    if (tid == 0) resid[(size_t)head * (cc.iters + 1) + i] = degenerate ? qn : nr;
+  };
+  float x = cc.c * q_own, xp = 0.0f;
+  for (int i = 1; i < cc.iters; ++i) {
+    const float ax = apply(x);
+    if constexpr (RES) put_res(i, q_own - ax);  // every thread: it holds barriers
+    if (tid < D) {
       const float xn = xp + cc.omega[i] * (x - xp + cc.c * (q_own - ax));
       xp = x;
       x = xn;
     }
   }
+  if constexpr (RES) put_res(cc.iters, q_own - apply(x));
 
   // o = U x = (U xh) / ||H||_F
   if (tid < D) xs[tid] = x;
@@ -147,28 +180,36 @@ __global__ __launch_bounds__(NT) void step_kernel(const T* __restrict__ q, const
 
 template <typename T, int D, int NT>
 static hipError_t launch_step_t(int BH, const void* q, const void* k, const void* v,
-                                const float* gamma, const float* beta, void* o, float* h, float* u, float* n2,
-                                const ChebConsts& cc, hipStream_t stream) {
-  hipLaunchKernelGGL((step_kernel<T, D, NT>), dim3(BH), dim3(NT), 0, stream,
-                     static_cast<const T*>(q), static_cast<const T*>(k),
-                     static_cast<const T*>(v), gamma, beta, static_cast<T*>(o), h, u, n2, cc);
+                                const float* gamma, const float* beta, void* o, float* h,
+                                float* u, float* n2, float* resid, const ChebConsts& cc,
+                                hipStream_t stream) {
+  if (resid)
+    hipLaunchKernelGGL((step_kernel<T, D, NT, true>), dim3(BH), dim3(NT), 0, stream,
+                       static_cast<const T*>(q), static_cast<const T*>(k),
+                       static_cast<const T*>(v), gamma, beta, static_cast<T*>(o), h, u, n2, resid,
+                       cc);
+  else
+    hipLaunchKernelGGL((step_kernel<T, D, NT, false>), dim3(BH), dim3(NT), 0, stream,
+                       static_cast<const T*>(q), static_cast<const T*>(k),
+                       static_cast<const T*>(v), gamma, beta, static_cast<T*>(o), h, u, n2,
+                       nullptr, cc);
   return hipGetLastError();
 }
 
 hipError_t launch_step(int dtype, int D, int BH, const void* q, const void* k, const void* v,
-                       const float* gamma, const float* beta, void* o, float* h, float* u, float* n2,
-                       const ChebConsts& cc, hipStream_t stream) {
+                       const float* gamma, const float* beta, void* o, float* h, float* u,
+                       float* n2, float* resid, const ChebConsts& cc, hipStream_t stream) {
   if (dtype == 0) {
     switch (D) {
-      case 32: return launch_step_t<bf16, 32, 128>(BH, q, k, v, gamma, beta, o, h, u, n2, cc, stream);
-      case 64: return launch_step_t<bf16, 64, 256>(BH, q, k, v, gamma, beta, o, h, u, n2, cc, stream);
-      case 128: return launch_step_t<bf16, 128, 512>(BH, q, k, v, gamma, beta, o, h, u, n2, cc, stream);
+      case 32: return launch_step_t<bf16, 32, 128>(BH, q, k, v, gamma, beta, o, h, u, n2, resid, cc, stream);
+      case 64: return launch_step_t<bf16, 64, 256>(BH, q, k, v, gamma, beta, o, h, u, n2, resid, cc, stream);
+      case 128: return launch_step_t<bf16, 128, 512>(BH, q, k, v, gamma, beta, o, h, u, n2, resid, cc, stream);
     }
   } else {
     switch (D) {
-      case 16: return launch_step_t<float, 16, 64>(BH, q, k, v, gamma, beta, o, h, u, n2, cc, stream);
-      case 32: return launch_step_t<float, 32, 128>(BH, q, k, v, gamma, beta, o, h, u, n2, cc, stream);
-      case 64: return launch_step_t<float, 64, 256>(BH, q, k, v, gamma, beta, o, h, u, n2, cc, stream);
+      case 16: return launch_step_t<float, 16, 64>(BH, q, k, v, gamma, beta, o, h, u, n2, resid, cc, stream);
+      case 32: return launch_step_t<float, 32, 128>(BH, q, k, v, gamma, beta, o, h, u, n2, resid, cc, stream);
+      case 64: return launch_step_t<float, 64, 256>(BH, q, k, v, gamma, beta, o, h, u, n2, resid, cc, stream);
     }
   }
   return hipErrorInvalidValue;

@@ -112,7 +112,8 @@ __device__ inline f16x8 pack8(f32x4 a, f32x4 b) {
                (f16)b[3]};
 }
 
-template <int D>
+// RES: residual mode, which also writes ||q_t - A_t x_i|| for i = 0..iters to A.resid
+template <int D, bool RES>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
 void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, ChebConsts cc) {
   using Cfg = TokCfg<D>;
@@ -582,8 +583,9 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
     // the scaled operands and the P' operands; (C) the K^T products, the X update and the
     // next step's first K fragments. With one wave per SIMD nothing else hides latency.
     // (the first step, FIRST = true, has Rt_{-1} = 0 and X = 0: it writes Ro and X outright)
-    auto step = [&](auto first, f32x4(&Ro)[FT], f32x4(&Rc)[FT], int it) {
+    auto step = [&](auto first, f32x4(&Ro)[FT], f32x4(&Rc)[FT], int it, auto... no_x) {
       constexpr bool FIRST = decltype(first)::value;
+      constexpr bool UPDX = sizeof...(no_x) == 0;  // the residual mode's last step leaves X
       const f32x4 cf = *reinterpret_cast<const f32x4*>(v_coef + 4 * it);  // krs, kys, bts
       Frag rf[KD], rs[KD], pf[KC];
       f32x4 pa[ST];
@@ -617,33 +619,95 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
       for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
         for (int ft = 0; ft < FT; ++ft) Ro[ft] = M::mma(ktr[kc][ft], pf[kc], Ro[ft]);
+      if constexpr (UPDX) {
 #pragma unroll
-      for (int ft = 0; ft < FT; ++ft) X[ft] = FIRST ? cf[2] * Rc[ft] : X[ft] + cf[2] * Rc[ft];
+        for (int ft = 0; ft < FT; ++ft) X[ft] = FIRST ? cf[2] * Rc[ft] : X[ft] + cf[2] * Rc[ft];
+      }
       __builtin_amdgcn_sched_barrier(0);
     };
+    // Residual mode: ||R_i|| = |s_i| ||Rt_i|| of the own token (a sum over the lane's features,
+    // then over the four lane groups), written by lane group 0; a token with ||H_t|| = 0 has
+    // x_i = 0 for every i, so its residuals are all ||q_t||. Rows past the end of the sequence
+    // (and the other lane groups) store out of the buffer's range, which drops the store.
+    float res_qn = 0.0f;
+    const int res_i1 = cc.iters + 1;
+    const uint32_t res_row = (uint32_t)Hn * (uint32_t)res_i1 * 4u;  // bytes per token
+    const auto res_rsrc =
+        buffer_rsrc(RES ? A.resid + ((b * (long long)Tlen + t0) * Hn + h) * res_i1 : nullptr,
+                    RES ? (uint32_t)(nv - 1) * res_row + (uint32_t)res_i1 * 4u : 0u);
+    const uint32_t res_off = lg == 0 ? (uint32_t)t * res_row : 0x80000000u;
+    auto lane_sum = [&](float x) {
+      x += lane_read(x, lane ^ 16);
+      return x + lane_read(x, lane ^ 32);
+    };
+    auto res_put = [&](int i, float val) { buffer_store4f(val, res_rsrc, res_off + 4u * (uint32_t)i); };
+    auto res_step = [&](int i, const f32x4(&R)[FT]) {
+      float x = 0.0f;
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft) x += R[ft][0] * R[ft][0] + R[ft][1] * R[ft][1] + R[ft][2] * R[ft][2] + R[ft][3] * R[ft][3];
+      x = lane_sum(x);
+      res_put(i, live ? fabsf(cc.sres[i]) * sqrtf(x) : res_qn);
+    };
+    if constexpr (RES) {
+      float x = 0.0f;
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) x += (float)Qraw[ft][j] * (float)Qraw[ft][j];
+      res_qn = sqrtf(lane_sum(x));
+      res_put(0, res_qn);  // x_0 = 0
+    }
     {
       using T1 = std::integral_constant<bool, true>;
       using T0 = std::integral_constant<bool, false>;
       const int iters = cc.iters_rs;
       const float bl = v_coef[4 * (iters - 1) + 2];  // X += bts_{r-1} Rt_{r-1}
+      // residual mode: one more step on Rt_{r-1} without the X update gives Rt_r
+      const bool extra = RES && cc.res_extra;
       if (iters == 1) {
 #pragma unroll
         for (int ft = 0; ft < FT; ++ft) X[ft] = bl * Ra[ft];
+        if constexpr (RES) {
+          if (extra) {
+            step(T1{}, Rb, Ra, 0, 0);
+            res_step(1, Rb);
+          }
+        }
       } else {
         step(T1{}, Rb, Ra, 0);  // Rb = Rt_1
+        if constexpr (RES) res_step(1, Rb);
         int it = 1;
         for (; it + 2 < iters; it += 2) {
           step(T0{}, Ra, Rb, it);      // Ra = Rt_{it+1}
+          if constexpr (RES) res_step(it + 1, Ra);
           step(T0{}, Rb, Ra, it + 1);  // Rb = Rt_{it+2}
+          if constexpr (RES) res_step(it + 2, Rb);
         }
         if (it + 1 < iters) {
           step(T0{}, Ra, Rb, it);
+          if constexpr (RES) res_step(it + 1, Ra);
 #pragma unroll
           for (int ft = 0; ft < FT; ++ft) X[ft] += bl * Ra[ft];
+          if constexpr (RES) {
+            if (extra) {
+              step(T0{}, Rb, Ra, iters - 1, 0);
+              res_step(iters, Rb);
+            }
+          }
         } else {
 #pragma unroll
           for (int ft = 0; ft < FT; ++ft) X[ft] += bl * Rb[ft];
+          if constexpr (RES) {
+            if (extra) {
+              step(T0{}, Ra, Rb, iters - 1, 0);
+              res_step(iters, Ra);
+            }
+          }
         }
+      }
+      // residuals past a truncated recurrence are below 2^-64 of ||q_t||: written as 0
+      if constexpr (RES) {
+        for (int i = extra ? cc.iters + 1 : iters; i <= cc.iters; ++i) res_put(i, live ? 0.0f : res_qn);
       }
     }
 
@@ -974,11 +1038,11 @@ hipError_t launch_sum(const FwdPlan& pl, const WalkArgs& a, hipStream_t stream) 
   return hipGetLastError();
 }
 
-template <int D>
+template <int D, bool RES>
 hipError_t launch_tok(const FwdPlan& pl, const WalkArgs& a, const ChebConsts& cc,
                       hipStream_t stream) {
   using Cfg = TokCfg<D>;
-  auto kern = walk_tok_kernel<D>;
+  auto kern = walk_tok_kernel<D, RES>;
   static std::atomic<uint64_t> lds_set{0};
   hipError_t e = ensure_dynamic_lds(reinterpret_cast<const void*>(kern), (int)Cfg::bytes, lds_set);
   if (e != hipSuccess) return e;
@@ -1012,10 +1076,20 @@ hipError_t launch_summary_tok(const FwdPlan& pl, const WalkArgs& a, hipStream_t 
 
 hipError_t launch_walk_tok(const FwdPlan& pl, const WalkArgs& a, const ChebConsts& cc,
                            hipStream_t stream) {
+  if (a.resid) {
+    // 32-bit byte offsets of a chunk's residual rows
+    if (64LL * pl.H * (cc.iters + 1) * 4 >= (1LL << 31)) return hipErrorInvalidValue;
+    switch (pl.D) {
+      case 32: return launch_tok<32, true>(pl, a, cc, stream);
+      case 64: return launch_tok<64, true>(pl, a, cc, stream);
+      case 128: return launch_tok<128, true>(pl, a, cc, stream);
+    }
+    return hipErrorInvalidValue;
+  }
   switch (pl.D) {
-    case 32: return launch_tok<32>(pl, a, cc, stream);
-    case 64: return launch_tok<64>(pl, a, cc, stream);
-    case 128: return launch_tok<128>(pl, a, cc, stream);
+    case 32: return launch_tok<32, false>(pl, a, cc, stream);
+    case 64: return launch_tok<64, false>(pl, a, cc, stream);
+    case 128: return launch_tok<128, false>(pl, a, cc, stream);
   }
   return hipErrorInvalidValue;
 }

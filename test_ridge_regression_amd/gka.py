@@ -26,7 +26,8 @@ GKA_MAX_ITERS = 64
 STATUS = {0: "GKA_OK", 1: "GKA_ERR_NULL", 2: "GKA_ERR_SHAPE", 3: "GKA_ERR_VALUE",
           4: "GKA_ERR_DTYPE", 5: "GKA_ERR_WORKSPACE", 6: "GKA_ERR_HIP", 7: "GKA_ERR_ALIAS"}
 EXPORTED = ["gka_fwd_workspace_bytes", "gka_fwd_chunked", "gka_step", "gka_fwd_chunked_beta",
-            "gka_step_beta", "gka_status_str", "gka_abi_version"]
+            "gka_step_beta", "gka_fwd_chunked_residuals", "gka_step_residuals",
+            "gka_status_str", "gka_abi_version"]
 
 
 class GkaParams(ctypes.Structure):
@@ -68,6 +69,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gka_fwd_chunked_beta.restype = ctypes.c_int
     lib.gka_step_beta.argtypes = [P, vp, vp, vp, fp, fp, vp, fp, fp, fp, vp]
     lib.gka_step_beta.restype = ctypes.c_int
+    lib.gka_fwd_chunked_residuals.argtypes = [P, vp, vp, vp, fp, fp, vp, fp, fp, fp, fp, fp, vp,
+                                              ctypes.c_size_t, vp]
+    lib.gka_fwd_chunked_residuals.restype = ctypes.c_int
+    lib.gka_step_residuals.argtypes = [P, vp, vp, vp, fp, fp, vp, fp, fp, fp, fp, vp]
+    lib.gka_step_residuals.restype = ctypes.c_int
     lib.gka_status_str.argtypes = [ctypes.c_int]
     lib.gka_status_str.restype = ctypes.c_char_p
     lib.gka_abi_version.argtypes = []
@@ -211,3 +217,56 @@ def step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor,
 def step_beta(q, k, v, gamma, beta, a, iters, state, **kw):
     """gka_step_beta: step with the write gate beta [B, H]."""
     return step(q, k, v, gamma, a, iters, state, beta=beta, **kw)
+
+
+def fwd_chunked_residuals(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
+                          gamma: torch.Tensor, a: float, iters: int, chunk: int = 64,
+                          state: Optional[GkaState] = None, beta: Optional[torch.Tensor] = None,
+                          return_hnorm: bool = False, segments: int = 0,
+                          out: Optional[torch.Tensor] = None,
+                          resid: Optional[torch.Tensor] = None,
+                          workspace: Optional[torch.Tensor] = None, stream=None):
+    """gka_fwd_chunked_residuals: the forward plus ||q_t - A_t x_i|| for i = 0..iters.
+
+    Returns (o, resid) -- resid float32 [B, T, H, iters + 1] -- or (o, resid, hnorm)."""
+    lib = load()
+    B, T, H, D = q.shape
+    p = make_params(B, T, H, D, chunk, iters, a, _dtype_code(q), segments)
+    o = torch.empty_like(q) if out is None else out
+    _require_io(q, k, v, gamma, o, state)
+    _require_beta(beta, (B, T, H))
+    if resid is None:
+        resid = torch.empty(B, T, H, iters + 1, device=q.device, dtype=torch.float32)
+    elif (resid.dtype != torch.float32 or not resid.is_contiguous()
+          or tuple(resid.shape) != (B, T, H, iters + 1)):
+        raise ValueError("resid must be a dense float32 [B, T, H, iters + 1] tensor")
+    hn = torch.empty(B, T, H, device=q.device, dtype=torch.float32) if return_hnorm else None
+    need = int(lib.gka_fwd_workspace_bytes(ctypes.byref(p)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    st = lib.gka_fwd_chunked_residuals(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(beta), _ptr(o),
+        _ptr(state.h if state else None), _ptr(state.u if state else None),
+        _ptr(state.n2 if state else None), _ptr(hn), _ptr(resid), _ptr(workspace),
+        ctypes.c_size_t(workspace.numel() if workspace is not None else 0), _stream(stream))
+    _check(st)
+    return (o, resid, hn) if return_hnorm else (o, resid)
+
+
+def step_residuals(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor,
+                   a: float, iters: int, state: GkaState, beta: Optional[torch.Tensor] = None,
+                   out: Optional[torch.Tensor] = None, stream=None):
+    """gka_step_residuals: one decode step plus ||q - A x_i||, i = 0..iters; returns
+    (o [B, H, D], resid float32 [B, H, iters + 1])."""
+    lib = load()
+    B, H, D = q.shape
+    p = make_params(B, 1, H, D, 64, iters, a, _dtype_code(q))
+    o = torch.empty_like(q) if out is None else out
+    _require_io(q, k, v, gamma, o, state)
+    _require_beta(beta, (B, H))
+    resid = torch.empty(B, H, iters + 1, device=q.device, dtype=torch.float32)
+    st = lib.gka_step_residuals(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma),
+                                _ptr(beta), _ptr(o), _ptr(state.h), _ptr(state.u),
+                                _ptr(state.n2), _ptr(resid), _stream(stream))
+    _check(st)
+    return o, resid

@@ -33,7 +33,7 @@ def test_header_declares_the_bound_functions():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.gka_abi_version() == 2
+    assert lib.gka_abi_version() == 3
 
 
 def test_status_strings(lib):
@@ -173,3 +173,25 @@ def test_binding_checks_the_write_gate():
     gka._require_beta(None, (1, 64, 1))
     gka._require_beta(g, (1, 64, 1))
     assert q.shape[:3] == g.shape
+
+
+def test_residual_entry_points_check_their_output(lib):
+    P = ctypes.byref
+    one = params(B=1, H=1, T=64, segments=1)
+    fwd_res = lambda p, r, o=VP[4]: lib.gka_fwd_chunked_residuals(
+        P(p) if p is not None else None, VP[0], VP[1], VP[2], VP[3], None, o, None, None, None,
+        None, r, None, ctypes.c_size_t(0), None)
+    step_res = lambda p, r, o=VP[4]: lib.gka_step_residuals(
+        P(p) if p is not None else None, VP[0], VP[1], VP[2], VP[3], None, o, VP[5], VP[6],
+        VP[7], r, None)
+    assert fwd_res(None, VP[10]) == 1
+    assert fwd_res(params(D=48, B=1, H=1, T=64), VP[10]) == 2
+    assert fwd_res(one, None) == 1  # the residual output is required
+    assert fwd_res(one, ctypes.c_void_p(ADDR[10] + 2)) == 2
+    assert fwd_res(one, ctypes.c_void_p(ADDR[4] + 4)) == 7  # overlaps o
+    assert fwd_res(params(T=0), None) == 0  # an empty sequence writes nothing
+    assert step_res(None, VP[10]) == 1
+    assert step_res(params(iters=0), VP[10]) == 3
+    assert step_res(params(), None) == 1
+    assert step_res(params(), ctypes.c_void_p(ADDR[10] + 1)) == 2
+    assert step_res(params(), VP[4]) == 7
