@@ -10,11 +10,12 @@ on a bounded sample of the prefill workload on this host.
 
 The write-gated prefill (gka_fwd_chunked_beta, same workload plus per-token write gates) is
 timed the same way and reported under "write_gate"; the solver-convergence mode
-(gka_fwd_chunked_residuals) under "solver_convergence", with its residual curve. The oracle leg also compares its outputs of
+(gka_fwd_chunked_residuals) under "solver_convergence", with its residual curve; a serving
+step on a packed batch of prompts and decode rows (gka_fwd_varlen) under "varlen". The oracle leg also compares its outputs of
 the prefix with the timed device run's.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps S] [--no-cpu]
-                       [--no-decode] [--no-beta] [--no-resid]
+                       [--no-decode] [--no-beta] [--no-resid] [--no-varlen]
 """
 from __future__ import annotations
 
@@ -206,6 +207,52 @@ def bench_residuals(W, inputs, steps, warmup, ev, sweep=(0.1, 0.05, 0.02)):
     return out
 
 
+def bench_varlen(Wv, steps, warmup, ev):
+    """A serving step on the packed batch (gka_fwd_varlen): 8 prompts and 56 decode rows that
+    continue carried states (built untimed by a packed prefill of their warm-up tokens).
+    Reports step tokens per second."""
+    import torch
+    from test_ridge_regression_amd import gka
+    from test_ridge_regression_amd import workloads as Wl
+
+    pre, step = Wl.varlen_lengths(Wv)
+    q, k, v, g, cu = Wl.make_varlen([a + b for a, b in zip(pre, step)], Wv.H, Wv.D, Wv.gate_mu,
+                                    Wv.gate_sd, Wv.dtype, Wv.seed)
+    idx1 = np.concatenate([np.arange(cu[b], cu[b] + pre[b]) for b in range(Wv.B)])
+    idx2 = np.concatenate([np.arange(cu[b] + pre[b], cu[b + 1]) for b in range(Wv.B)])
+    d = lambda x: torch.from_numpy(x.astype(np.float32)).cuda().to(torch.bfloat16).contiguous()
+    f = lambda x: torch.from_numpy(x.astype(np.float32)).cuda().contiguous()
+    offs = lambda L: torch.from_numpy(np.concatenate([[0], np.cumsum(L)]).astype(np.int32)).cuda()
+    st = gka.GkaState.zeros(Wv.B, Wv.H, Wv.D)
+    log(f"varlen warm-up prefill: {len(idx1)} tokens")
+    gka.fwd_varlen(d(q[idx1]), d(k[idx1]), d(v[idx1]), f(g[idx1]), offs(pre), max(pre), Wv.a,
+                   Wv.iters, Wv.chunk, state=st)
+    qs, ks, vs, gs, cs = d(q[idx2]), d(k[idx2]), d(v[idx2]), f(g[idx2]), offs(step)
+    o = torch.empty_like(qs)
+    need = gka.workspace_bytes(Wv.B, max(step), Wv.H, Wv.D, Wv.chunk, Wv.iters, Wv.a,
+                               gka.GKA_BF16)
+    ws = torch.empty(max(need, 1), device="cuda", dtype=torch.uint8)
+    call = lambda: gka.fwd_varlen(qs, ks, vs, gs, cs, max(step), Wv.a, Wv.iters, Wv.chunk,
+                                  state=st, out=o, workspace=ws)
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0, t1 = ev.create(2)
+    log(f"varlen timed {steps}")
+    ev.record(t0, stream.cuda_stream)
+    for _ in range(steps):
+        call()
+    ev.record(t1, stream.cuda_stream)
+    ev.sync(t1)
+    ms = ev.elapsed_ms(t0, t1) / steps
+    ev.destroy([t0, t1])
+    n = int(sum(step))
+    return {"entry_point": "gka_fwd_varlen", "workload": Wv.name, "sequences": Wv.B,
+            "step_tokens": n, "prompts": int(sum(1 for x in pre if x == 0)),
+            "longest": int(max(step)), "ms_per_step": ms, "tokens_per_s": n / (ms * 1e-3)}
+
+
 def _segments(W):
     from test_ridge_regression_amd import gka
     # the plan's segment count: workspace = B*H*S*(2 D^2 + 1)*4 + B*H*4 (rounded up to 256)
@@ -302,6 +349,7 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-beta", action="store_true", help="skip the write-gated prefill")
     ap.add_argument("--no-resid", action="store_true", help="skip the solver-convergence mode")
+    ap.add_argument("--no-varlen", action="store_true", help="skip the packed serving step")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 512 MiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -379,6 +427,12 @@ def main():
                                                     args.warmup, ev)
     del pre, inputs
     torch.cuda.empty_cache()
+    if not args.no_varlen:
+        rec["varlen"] = bench_varlen(Wl.WORKLOADS["varlen_b64_h8_d128"], args.steps, args.warmup,
+                                     ev)
+        log(f"varlen: {rec['varlen']['ms_per_step']:.3f} ms/step, "
+            f"{rec['varlen']['tokens_per_s']:.3e} tok/s")
+        torch.cuda.empty_cache()
     if not args.no_decode:
         Wd = Wl.WORKLOADS["decode_b256_h8_d128"]
         dec = bench_decode(Wd, args.decode_steps, ev)

@@ -177,6 +177,34 @@ gka_status gka_step_residuals(const gka_params* p, const void* q, const void* k,
                               const float* gamma, const float* beta, void* o, float* h_state,
                               float* u_state, float* hnorm2, float* resid, void* stream);
 
+/*
+ * Packed variable-length batches (serving): B sequences of different lengths concatenated on
+ * the token axis, each with its own carried state. Every sequence is the recurrence of
+ * gka_fwd_chunked_beta on its own rows. A decode row is a sequence of length 1 continuing its
+ * carried state, so one call can serve a batch that mixes prompts being prefilled and
+ * sequences being decoded (the chunked-prefill / decode hand-off inside one call).
+ *   p          B = number of sequences, T = an upper bound on every sequence length (it sizes
+ *              the segment plan and the workspace: gka_fwd_workspace_bytes(p) as for a dense
+ *              [B, T] call); other fields as for gka_fwd_chunked
+ *   cu_seqlens DEVICE int32 [B + 1], 4-byte aligned: sequence b is rows [cu[b], cu[b+1]) of
+ *              the token axis, cu[0] = 0, non-decreasing, cu[B] = total. A length above T counts
+ *              as T (the rows past it are not read, written or carried); an empty sequence
+ *              leaves its state unchanged.
+ *   total      number of rows (host copy of cu[B]), 0 <= total <= B T; it sizes the alias
+ *              checks only
+ *   q, k, v, o [total, H, D] dtype; gamma, optional beta (NULL = 1) and optional hnorm_t
+ *              [total, H] float32
+ *   h_state, u_state [B, H, D, D], hnorm2 [B, H]: per sequence, as for gka_fwd_chunked (all
+ *              NULL: every sequence starts from the zero state and no final state is returned)
+ * Errors as for gka_fwd_chunked_beta; NULL cu_seqlens is GKA_ERR_NULL, a misaligned one or a
+ * total outside [0, B T] GKA_ERR_SHAPE. total = 0 (or T = 0) is a no-op.
+ */
+gka_status gka_fwd_varlen(const gka_params* p, const int32_t* cu_seqlens, int64_t total,
+                          const void* q, const void* k, const void* v, const float* gamma,
+                          const float* beta, void* o, float* h_state, float* u_state,
+                          float* hnorm2, float* hnorm_t, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
 /* Static description of a status code. */
 const char* gka_status_str(int status);
 

@@ -12,7 +12,7 @@ namespace {
 using gka::ChebConsts;
 using gka::FwdPlan;
 
-constexpr int kAbiVersion = 3;
+constexpr int kAbiVersion = 4;
 constexpr int kCUs = 256;  // MI355X compute units: the segment plan aims at one workgroup per CU
 
 bool dims_supported(int dtype, int D) {
@@ -160,10 +160,11 @@ gka_status check_fwd(const gka_params* p) {
   return GKA_OK;
 }
 
-gka_status fwd_impl(const gka_params* p, const void* q, const void* k, const void* v,
-                    const float* gamma, const float* beta, void* o, float* h_state,
-                    float* u_state, float* hnorm2, float* hnorm_t, float* resid, void* workspace,
-                    size_t workspace_bytes, void* stream, void* const* phase_events);
+gka_status fwd_impl(const gka_params* p, const int32_t* cu, int64_t total, const void* q,
+                    const void* k, const void* v, const float* gamma, const float* beta, void* o,
+                    float* h_state, float* u_state, float* hnorm2, float* hnorm_t, float* resid,
+                    void* workspace, size_t workspace_bytes, void* stream,
+                    void* const* phase_events);
 
 }  // namespace
 
@@ -204,8 +205,8 @@ gka_status gka_fwd_chunked_beta(const gka_params* p, const void* q, const void* 
                                 const float* gamma, const float* beta, void* o, float* h_state,
                                 float* u_state, float* hnorm2, float* hnorm_t, void* workspace,
                                 size_t workspace_bytes, void* stream, void* const* phase_events) {
-  return fwd_impl(p, q, k, v, gamma, beta, o, h_state, u_state, hnorm2, hnorm_t, nullptr,
-                  workspace, workspace_bytes, stream, phase_events);
+  return fwd_impl(p, nullptr, -1, q, k, v, gamma, beta, o, h_state, u_state, hnorm2, hnorm_t,
+                  nullptr, workspace, workspace_bytes, stream, phase_events);
 }
 
 gka_status gka_fwd_chunked_residuals(const gka_params* p, const void* q, const void* k,
@@ -216,36 +217,51 @@ gka_status gka_fwd_chunked_residuals(const gka_params* p, const void* q, const v
   gka_status st = check_fwd(p);
   if (st != GKA_OK) return st;
   if (p->T > 0 && !resid) return GKA_ERR_NULL;
-  return fwd_impl(p, q, k, v, gamma, beta, o, h_state, u_state, hnorm2, hnorm_t, resid,
-                  workspace, workspace_bytes, stream, nullptr);
+  return fwd_impl(p, nullptr, -1, q, k, v, gamma, beta, o, h_state, u_state, hnorm2, hnorm_t,
+                  resid, workspace, workspace_bytes, stream, nullptr);
+}
+
+gka_status gka_fwd_varlen(const gka_params* p, const int32_t* cu_seqlens, int64_t total,
+                          const void* q, const void* k, const void* v, const float* gamma,
+                          const float* beta, void* o, float* h_state, float* u_state,
+                          float* hnorm2, float* hnorm_t, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  gka_status st = check_fwd(p);
+  if (st != GKA_OK) return st;
+  if (!cu_seqlens) return GKA_ERR_NULL;
+  if (reinterpret_cast<uintptr_t>(cu_seqlens) & 3u) return GKA_ERR_SHAPE;
+  if (total < 0 || total > (int64_t)p->B * p->T) return GKA_ERR_SHAPE;
+  return fwd_impl(p, cu_seqlens, total, q, k, v, gamma, beta, o, h_state, u_state, hnorm2,
+                  hnorm_t, nullptr, workspace, workspace_bytes, stream, nullptr);
 }
 
 }  // extern "C"
 
 namespace {
 
-gka_status fwd_impl(const gka_params* p, const void* q, const void* k, const void* v,
-                    const float* gamma, const float* beta, void* o, float* h_state,
-                    float* u_state, float* hnorm2, float* hnorm_t, float* resid, void* workspace,
-                    size_t workspace_bytes, void* stream, void* const* phase_events) {
+gka_status fwd_impl(const gka_params* p, const int32_t* cu, int64_t total, const void* q,
+                    const void* k, const void* v, const float* gamma, const float* beta, void* o,
+                    float* h_state, float* u_state, float* hnorm2, float* hnorm_t, float* resid,
+                    void* workspace, size_t workspace_bytes, void* stream,
+                    void* const* phase_events) {
   gka_status st = check_fwd(p);
   if (st != GKA_OK) return st;
   const bool any_state = h_state || u_state || hnorm2;
   const bool all_state = h_state && u_state && hnorm2;
   if (any_state && !all_state) return GKA_ERR_NULL;
-  if (p->T == 0) return GKA_OK;  // nothing to do; the state is unchanged
+  // rows of the token axis: B T (dense) or the packed total
+  const int64_t rows = cu ? total : (int64_t)p->B * p->T;
+  if (p->T == 0 || rows == 0) return GKA_OK;  // nothing to do; the state is unchanged
   if (!q || !k || !v || !gamma || !o) return GKA_ERR_NULL;
   if (!aligned16(q) || !aligned16(k) || !aligned16(v) || !aligned16(o)) return GKA_ERR_SHAPE;
   if (h_state && (!aligned16(h_state) || !aligned16(u_state))) return GKA_ERR_SHAPE;
-  const size_t n_io = (size_t)p->B * p->T * p->H * p->D * elem_bytes(p->dtype);
+  const size_t n_io = (size_t)rows * p->H * p->D * elem_bytes(p->dtype);
   if (overlap(o, n_io, q, n_io) || overlap(o, n_io, k, n_io) || overlap(o, n_io, v, n_io))
     return GKA_ERR_ALIAS;
   if (beta && (reinterpret_cast<uintptr_t>(beta) & 3u)) return GKA_ERR_SHAPE;
-  if (beta && overlap(o, n_io, beta, (size_t)p->B * p->T * p->H * sizeof(float)))
-    return GKA_ERR_ALIAS;
+  if (beta && overlap(o, n_io, beta, (size_t)rows * p->H * sizeof(float))) return GKA_ERR_ALIAS;
   if (resid && (reinterpret_cast<uintptr_t>(resid) & 3u)) return GKA_ERR_SHAPE;
-  if (resid && overlap(o, n_io, resid,
-                       (size_t)p->B * p->T * p->H * (p->iters + 1) * sizeof(float)))
+  if (resid && overlap(o, n_io, resid, (size_t)rows * p->H * (p->iters + 1) * sizeof(float)))
     return GKA_ERR_ALIAS;
   FwdPlan pl;
   make_plan(p, pl);
@@ -267,6 +283,7 @@ gka_status fwd_impl(const gka_params* p, const void* q, const void* k, const voi
   wa.gamma = gamma;
   wa.beta = beta;
   wa.resid = resid;
+  wa.cu = cu;
   wa.o = o;
   wa.hnorm_t = hnorm_t;
   if (pl.S == 1) {

@@ -116,7 +116,7 @@ struct WalkCfg {
 // compilation pass only.)
 template <typename T, int D, int C, int NWaves, typename V>
 __device__ inline void prefetch_chunk(V* PreK, V* PreV, float* PreG, const T* kg, const T* vg,
-                                      const float* gamma, int b, int h, int Hn, int Tlen, int chn,
+                                      const float* gamma, long long seq0, int h, int Hn, int Tlen, int chn,
                                       int wave, int lane) {
 #if defined(__HIP_DEVICE_COMPILE__)  // device code only: the host pass has no LDS address space
   using Cfg = WalkCfg<T, D, C, NWaves>;
@@ -133,21 +133,21 @@ __device__ inline void prefetch_chunk(V* PreK, V* PreV, float* PreG, const T* kg
     const uint32_t base = __builtin_amdgcn_readfirstlane(
         (uint32_t)(uintptr_t)(lds_void*)((isv ? PreV : PreK) + qq * kWave));
     if (t < nvn) {
-      const T* src = (isv ? vg : kg) + (b * (long long)Tlen + t0n + t) * tok_stride +
+      const T* src = (isv ? vg : kg) + (seq0 + t0n + t) * tok_stride +
                      (long long)h * D + c * Cfg::VEC;
       dma_load16(src, base);
     }
   }
   if (wave == Cfg::NW - 1) {
     const uint32_t base = __builtin_amdgcn_readfirstlane((uint32_t)(uintptr_t)(lds_void*)PreG);
-    if (lane < nvn) dma_load4(gamma + (b * (long long)Tlen + t0n + lane) * Hn + h, base);
+    if (lane < nvn) dma_load4(gamma + (seq0 + t0n + lane) * Hn + h, base);
   }
 #endif
 }
 
 // RES: residual mode, which also writes ||q_t - A_t x_i|| for i = 0..iters to A.resid
 template <typename T, int D, int C, bool RES>
-__global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, int Hn, int N,
+__global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tmax, int Hn, int N,
                                                    int S, int J, ChebConsts cc) {
   using Cfg = WalkCfg<T, D, C, 8>;
   using O = typename Cfg::O;
@@ -203,8 +203,11 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
   const int fg = wave % FG, tg = wave / FG;
   const bool tok_active = tg < TG;    // this wave owns feature x token tiles
   const bool state_active = tg < SG;  // this wave owns state tiles
+  long long seq0;  // first row of sequence b
+  int Tlen;        // its length
+  seq_range(A, b, Tmax, seq0, Tlen);
   const int c_begin = seg * J;
-  const int c_end = min(N, c_begin + J);
+  const int c_end = min(min(N, c_begin + J), (Tlen + C - 1) / C);  // may be empty
   const long long tok_stride = (long long)Hn * D;
   const T* qg = static_cast<const T*>(A.q);
   const T* kg = static_cast<const T*>(A.k);
@@ -254,7 +257,7 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
 
   auto prefetch = [&](int chn) {
     if (chn < c_end)
-      prefetch_chunk<T, D, C, NW, vecT>(PreK, PreV, PreG, kg, vg, A.gamma, b, h, Hn, Tlen, chn,
+      prefetch_chunk<T, D, C, NW, vecT>(PreK, PreV, PreG, kg, vg, A.gamma, seq0, h, Hn, Tlen, chn,
                                         wave, lane);
   };
   // The output tile of a chunk is staged token-major (in the operand buffer, idle by then) and
@@ -268,7 +271,7 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
         const int t = e / Cfg::UPR, c = e % Cfg::UPR;
         if (t < pend_nv) {
           const vecT v = *reinterpret_cast<const vecT*>(Ob + t * LDD + c * Cfg::VEC);
-          *reinterpret_cast<vecT*>(og + (b * (long long)Tlen + pend_t0 + t) * tok_stride +
+          *reinterpret_cast<vecT*>(og + (seq0 + pend_t0 + t) * tok_stride +
                                    (long long)h * D + c * Cfg::VEC) = v;
         }
       }
@@ -300,7 +303,7 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
         if (t < nv) {
           kv = PreK[e];
           vv = PreV[e];
-          if (A.beta) sb = sqrtf(A.beta[(b * (long long)Tlen + t0 + t) * Hn + h]);
+          if (A.beta) sb = sqrtf(A.beta[(seq0 + t0 + t) * Hn + h]);
         } else {
 #pragma unroll
           for (int i = 0; i < VEC; ++i) {
@@ -329,7 +332,7 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
           const int t = tok_of(jt) + lr;
           raw4 qv = {(T)0.0f, (T)0.0f, (T)0.0f, (T)0.0f};
           if (tok_active && t < nv) {
-            const long long off = (b * (long long)Tlen + t0 + t) * tok_stride + (long long)h * D + row_of(jf) + 4 * lg;
+            const long long off = (seq0 + t0 + t) * tok_stride + (long long)h * D + row_of(jf) + 4 * lg;
             qv = *reinterpret_cast<const raw4*>(qg + off);
           }
           Qraw[jf][jt] = qv;
@@ -526,7 +529,7 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
           v_n2[t] = n2;
           v_ninv[t] = ninv;
           v_s[t] = v_gam[t] * n0 * ninv;
-          if (A.hnorm_t && t < nv) A.hnorm_t[(b * (long long)Tlen + t0 + t) * Hn + h] = sqrtf(n2);
+          if (A.hnorm_t && t < nv) A.hnorm_t[(seq0 + t0 + t) * Hn + h] = sqrtf(n2);
         }
       }
       lds_barrier();
@@ -703,7 +706,7 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
             const int t = tok_of(jt) + lr;
             if (t < nv) {
               const float x = v_ninv[t] > 0.0f ? val[jt] : res_q[jt];
-              A.resid[((b * (long long)Tlen + t0 + t) * Hn + h) * (cc.iters + 1) + i] = x;
+              A.resid[((seq0 + t0 + t) * Hn + h) * (cc.iters + 1) + i] = x;
             }
           }
         }
@@ -816,7 +819,9 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
         *reinterpret_cast<f32x4*>(ou + (size_t)c * D + r) = Ust[jf][jc];
       }
   }
-  if (A.n2_out && seg == S - 1 && tid == 0) A.n2_out[bh] = n0sq;
+  // (a sequence without tokens keeps the carried ||H||^2 as it was, not its recomputed value)
+  if (A.n2_out && seg == S - 1 && tid == 0)
+    A.n2_out[bh] = Tlen == 0 && A.n2_in ? A.n2_in[bh] : n0sq;
 }
 
 // Segment summaries (carry only): for each (segment, head), the state reached from a zero state
@@ -830,7 +835,7 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tlen, 
 // gate-weighted keys w K (split into hi + lo fp16 parts), one 16-byte write each, and the
 // carry reads its operands K^T, V^T and (w K)^T with transposing LDS reads.
 template <typename T, int D, int C>
-__global__ __launch_bounds__(1024) void summary_kernel(WalkArgs A, int B, int Tlen, int Hn, int N,
+__global__ __launch_bounds__(1024) void summary_kernel(WalkArgs A, int B, int Tmax, int Hn, int N,
                                                        int S, int J) {
   using Cfg = WalkCfg<T, D, C, 16>;
   using O = typename Cfg::O;
@@ -859,8 +864,11 @@ __global__ __launch_bounds__(1024) void summary_kernel(WalkArgs A, int B, int Tl
   auto refresh = [&]() { asm volatile("" : "+v"(tid), "+v"(lane), "+v"(lr), "+v"(lg)); };
   const int fg = wave % FG, tg = wave / FG;
   const bool state_active = tg < SG;
+  long long seq0;  // first row of sequence b
+  int Tlen;        // its length
+  seq_range(A, b, Tmax, seq0, Tlen);
   const int c_begin = seg * J;
-  const int c_end = min(N, c_begin + J);
+  const int c_end = min(min(N, c_begin + J), (Tlen + C - 1) / C);  // may be empty
   const long long tok_stride = (long long)Hn * D;
   const T* kg = static_cast<const T*>(A.k);
   const T* vg = static_cast<const T*>(A.v);
@@ -888,12 +896,12 @@ __global__ __launch_bounds__(1024) void summary_kernel(WalkArgs A, int B, int Tl
     const int t = tid / UPR, c = tid % UPR;
     if (tid < Cfg::NU && t < nvn) {
       const long long off =
-          (b * (long long)Tlen + t0n + t) * tok_stride + (long long)h * D + c * VEC;
+          (seq0 + t0n + t) * tok_stride + (long long)h * D + c * VEC;
       kreg[slot] = *reinterpret_cast<const vecT*>(kg + off);
       vreg[slot] = *reinterpret_cast<const vecT*>(vg + off);
     }
     if (lane % C < nvn) {
-      const long long gi = (b * (long long)Tlen + t0n + lane % C) * Hn + h;
+      const long long gi = (seq0 + t0n + lane % C) * Hn + h;
       greg[slot] = A.gamma[gi];
       if (A.beta) breg[slot] = A.beta[gi];
     }

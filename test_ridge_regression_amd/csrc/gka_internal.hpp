@@ -63,7 +63,22 @@ struct WalkArgs {
   long long sum_bh, sum_seg;
   float* log2g_out;       // summary mode: per-segment log2 of the gate product [BH][S]
   float* resid;           // optional residual norms ||q_t - A_t x_i||, [B, T, H, iters + 1]
+  const int* cu;          // packed batches: sequence b is rows [cu[b], cu[b+1]) (NULL: dense)
 };
+
+// Rows of sequence b on the token axis: [s0, s0 + len). Dense batches: s0 = b Tmax, len = Tmax;
+// packed batches: from the offsets, the length clamped to [0, Tmax] (rows past Tmax are not
+// part of the call).
+__device__ inline void seq_range(const WalkArgs& A, int b, int Tmax, long long& s0, int& len) {
+  if (A.cu) {
+    const int a0 = A.cu[b], a1 = A.cu[b + 1];
+    s0 = a0;
+    len = min(max(a1 - a0, 0), Tmax);
+  } else {
+    s0 = (long long)b * Tmax;
+    len = Tmax;
+  }
+}
 
 hipError_t launch_walk(const FwdPlan& pl, bool summary, const WalkArgs& a, const ChebConsts& cc,
                        hipStream_t stream);

@@ -115,7 +115,7 @@ __device__ inline f16x8 pack8(f32x4 a, f32x4 b) {
 // RES: residual mode, which also writes ||q_t - A_t x_i|| for i = 0..iters to A.resid
 template <int D, bool RES>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
-void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, ChebConsts cc) {
+void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, ChebConsts cc) {
   using Cfg = TokCfg<D>;
   using M = Mma<f16>;
   typedef f16x8 Frag;
@@ -153,8 +153,11 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
     asm volatile("" : "+v"(tid), "+v"(lane), "+v"(lr), "+v"(lg), "+v"(t), "+v"(wave));
     asm volatile("" : "+v"(a0), "+v"(b0));
   };
+  long long seq0;  // first row of sequence b
+  int Tlen;        // its length
+  seq_range(A, b, Tmax, seq0, Tlen);
   const int c_begin = seg * J;
-  const int c_end = min(N, c_begin + J);
+  const int c_end = min(min(N, c_begin + J), (Tlen + C - 1) / C);  // may be empty
   const long long tok_stride = (long long)Hn * D;
   const uint32_t tok_bytes = (uint32_t)Hn * D * 2u;  // < 2^25: 64 rows fit a 32-bit offset
   const bf16* qg = static_cast<const bf16*>(A.q);
@@ -228,7 +231,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
     const int chv = chn < c_end ? chn : c_end - 1;
     const int t0n = chv * C;
     const int nvn = chn < c_end ? min(C, Tlen - t0n) : 0;
-    const long long row0 = (b * (long long)Tlen + t0n) * tok_stride + (long long)h * D;
+    const long long row0 = (seq0 + t0n) * tok_stride + (long long)h * D;
     const uint32_t valid = nvn > 0 ? (uint32_t)(nvn - 1) * tok_bytes + D * 2u : 0u;
     const auto rk = buffer_rsrc(kg + row0, valid);
     const auto rv = buffer_rsrc(vg + row0, valid);
@@ -241,8 +244,8 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
       vin[k] = buffer_load16<bf16x8>(rv, off);
     }
     const uint32_t gvalid = nvn > 0 ? (uint32_t)(nvn - 1) * Hn * 4u + 4u : 0u;
-    const auto rg = buffer_rsrc(A.gamma + (b * (long long)Tlen + t0n) * Hn + h, gvalid);
-    const auto rb = buffer_rsrc(bsrc + (b * (long long)Tlen + t0n) * Hn + h, gvalid);
+    const auto rg = buffer_rsrc(A.gamma + (seq0 + t0n) * Hn + h, gvalid);
+    const auto rb = buffer_rsrc(bsrc + (seq0 + t0n) * Hn + h, gvalid);
     gin = buffer_load4f(rg, (uint32_t)lane * Hn * 4u);
     bin = buffer_load4f(rb, (uint32_t)lane * Hn * 4u);
   };
@@ -452,7 +455,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
     const float n2 = sa * n0sq + sb_;
     const float ninv = n2 > 0.0f ? 1.0f / sqrtf(n2) : 0.0f;
     if (wave == 0 && A.hnorm_t && lane < nv)
-      A.hnorm_t[(b * (long long)Tlen + t0 + lane) * Hn + h] = sqrtf(n2);
+      A.hnorm_t[(seq0 + t0 + lane) * Hn + h] = sqrtf(n2);
     const float n2last = lane_value(n2, C - 1);
     const float ninv_t = lane_read(ninv, t);
     const float s_t = lane_read(gam, t) * n0 * ninv_t;
@@ -475,7 +478,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
     bf16x4 Qraw[FT];
     {
       // bounds-checked: tokens past the end read as 0
-      const auto rq = buffer_rsrc(qg + (b * (long long)Tlen + t0) * tok_stride + (long long)h * D,
+      const auto rq = buffer_rsrc(qg + (seq0 + t0) * tok_stride + (long long)h * D,
                                   (uint32_t)(nv - 1) * tok_bytes + D * 2u);
       const uint32_t qoff = (uint32_t)t * tok_bytes + (uint32_t)lg * 8u;
 #pragma unroll
@@ -633,7 +636,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
     const int res_i1 = cc.iters + 1;
     const uint32_t res_row = (uint32_t)Hn * (uint32_t)res_i1 * 4u;  // bytes per token
     const auto res_rsrc =
-        buffer_rsrc(RES ? A.resid + ((b * (long long)Tlen + t0) * Hn + h) * res_i1 : nullptr,
+        buffer_rsrc(RES ? A.resid + ((seq0 + t0) * Hn + h) * res_i1 : nullptr,
                     RES ? (uint32_t)(nv - 1) * res_row + (uint32_t)res_i1 * 4u : 0u);
     const uint32_t res_off = lg == 0 ? (uint32_t)t * res_row : 0x80000000u;
     auto lane_sum = [&](float x) {
@@ -773,7 +776,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
       // o of the own token straight from the accumulators: 8 bytes per lane, 32 per token row
       // and tile
       // (bounds-checked: the stores of tokens past the end are dropped)
-      const auto ro = buffer_rsrc(og + (b * (long long)Tlen + t0) * tok_stride + (long long)h * D,
+      const auto ro = buffer_rsrc(og + (seq0 + t0) * tok_stride + (long long)h * D,
                                   (uint32_t)(nv - 1) * tok_bytes + D * 2u);
       const uint32_t ooff = (uint32_t)t * tok_bytes + (uint32_t)lg * 8u;
 #pragma unroll
@@ -796,7 +799,9 @@ void walk_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J, C
         *reinterpret_cast<f32x4*>(ou + o) = *us_tile(jr, jc);
       }
   }
-  if (A.n2_out && seg == S - 1 && tid == 0) A.n2_out[bh] = n0sq;
+  // (a sequence without tokens keeps the carried ||H||^2 as it was, not its recomputed value)
+  if (A.n2_out && seg == S - 1 && tid == 0)
+    A.n2_out[bh] = Tlen == 0 && A.n2_in ? A.n2_in[bh] : n0sq;
 }
 
 // ---- segment summaries -------------------------------------------------------------------
@@ -854,7 +859,7 @@ __device__ inline bf16x8 frag_trans_bf16(const bf16* base, int s0, int s1, int c
 
 template <int D>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void summary_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J) {
+void summary_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J) {
   using Cfg = SumCfg<D>;
   using M = Mma<bf16>;
   typedef bf16x8 Frag;
@@ -876,8 +881,11 @@ void summary_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J
   const int a0 = RT * (wave % 2), b0 = CT * (wave / 2);
   // the segment's tokens [t_begin, t_end) in blocks of CB (= the chunk), block 0 the last one
   const int t_begin = seg * J * CB;
+  long long seq0;  // first row of sequence b
+  int Tlen;        // its length
+  seq_range(A, b, Tmax, seq0, Tlen);
   const int t_end = min(Tlen, t_begin + J * CB);
-  const int NB = (t_end - t_begin + CB - 1) / CB;
+  const int NB = max(0, (t_end - t_begin + CB - 1) / CB);  // 0: an empty segment
   const long long tok_stride = (long long)Hn * D;
   const uint32_t tok_bytes = (uint32_t)Hn * D * 2u;
   auto block_t0 = [&](int p) { return t_begin + (NB - 1 - p) * CB; };
@@ -892,7 +900,7 @@ void summary_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J
     const int pv = p < NB ? p : NB - 1;
     const int t0n = block_t0(pv);
     const int nvn = p < NB ? min(CB, t_end - t0n) : 0;
-    const long long row0 = (b * (long long)Tlen + t0n) * tok_stride + (long long)h * D;
+    const long long row0 = (seq0 + t0n) * tok_stride + (long long)h * D;
     const uint32_t valid = nvn > 0 ? (uint32_t)(nvn - 1) * tok_bytes + D * 2u : 0u;
     const auto rk = buffer_rsrc(static_cast<const bf16*>(A.k) + row0, valid);
     const auto rv = buffer_rsrc(static_cast<const bf16*>(A.v) + row0, valid);
@@ -905,8 +913,8 @@ void summary_tok_kernel(WalkArgs A, int B, int Tlen, int Hn, int N, int S, int J
       vr[q][k] = buffer_load16<bf16x8>(rv, off);
     }
     const uint32_t gvalid = nvn > 0 ? (uint32_t)(nvn - 1) * Hn * 4u + 4u : 0u;
-    const auto rg = buffer_rsrc(A.gamma + (b * (long long)Tlen + t0n) * Hn + h, gvalid);
-    const auto rb = buffer_rsrc(bsrc + (b * (long long)Tlen + t0n) * Hn + h, gvalid);
+    const auto rg = buffer_rsrc(A.gamma + (seq0 + t0n) * Hn + h, gvalid);
+    const auto rb = buffer_rsrc(bsrc + (seq0 + t0n) * Hn + h, gvalid);
     gr[q] = buffer_load4f(rg, (uint32_t)lane * Hn * 4u);
     br[q] = buffer_load4f(rb, (uint32_t)lane * Hn * 4u);
   };

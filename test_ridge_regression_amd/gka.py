@@ -27,7 +27,7 @@ STATUS = {0: "GKA_OK", 1: "GKA_ERR_NULL", 2: "GKA_ERR_SHAPE", 3: "GKA_ERR_VALUE"
           4: "GKA_ERR_DTYPE", 5: "GKA_ERR_WORKSPACE", 6: "GKA_ERR_HIP", 7: "GKA_ERR_ALIAS"}
 EXPORTED = ["gka_fwd_workspace_bytes", "gka_fwd_chunked", "gka_step", "gka_fwd_chunked_beta",
             "gka_step_beta", "gka_fwd_chunked_residuals", "gka_step_residuals",
-            "gka_status_str", "gka_abi_version"]
+            "gka_fwd_varlen", "gka_status_str", "gka_abi_version"]
 
 
 class GkaParams(ctypes.Structure):
@@ -74,6 +74,9 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gka_fwd_chunked_residuals.restype = ctypes.c_int
     lib.gka_step_residuals.argtypes = [P, vp, vp, vp, fp, fp, vp, fp, fp, fp, fp, vp]
     lib.gka_step_residuals.restype = ctypes.c_int
+    lib.gka_fwd_varlen.argtypes = [P, vp, ctypes.c_int64, vp, vp, vp, fp, fp, vp, fp, fp, fp, fp,
+                                   vp, ctypes.c_size_t, vp]
+    lib.gka_fwd_varlen.restype = ctypes.c_int
     lib.gka_status_str.argtypes = [ctypes.c_int]
     lib.gka_status_str.restype = ctypes.c_char_p
     lib.gka_abi_version.argtypes = []
@@ -270,3 +273,38 @@ def step_residuals(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: tor
                                 _ptr(state.n2), _ptr(resid), _stream(stream))
     _check(st)
     return o, resid
+
+
+def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor,
+               cu_seqlens: torch.Tensor, max_seqlen: int, a: float, iters: int, chunk: int = 64,
+               state: Optional[GkaState] = None, beta: Optional[torch.Tensor] = None,
+               return_hnorm: bool = False, segments: int = 0, out: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None, stream=None, total: Optional[int] = None):
+    """gka_fwd_varlen on a packed batch: q, k, v [total, H, D]; gamma (and beta) [total, H];
+    cu_seqlens int32 [B + 1] on the device; every length <= max_seqlen. ``state`` (optional)
+    holds one carried state per sequence ([B, H, D, D], [B, H]). ``total`` defaults to the
+    number of rows of q. Returns o (and per-row ||H_t||_F [total, H])."""
+    lib = load()
+    rows, H, D = q.shape
+    B = cu_seqlens.numel() - 1
+    if cu_seqlens.dtype != torch.int32 or not cu_seqlens.is_contiguous() or B < 1:
+        raise ValueError("cu_seqlens must be a dense int32 tensor of B + 1 offsets")
+    total = rows if total is None else int(total)
+    p = make_params(B, max_seqlen, H, D, chunk, iters, a, _dtype_code(q), segments)
+    o = torch.empty_like(q) if out is None else out
+    _require_io(q, k, v, gamma, o, state)
+    _require_beta(beta, (rows, H))
+    if tuple(gamma.shape) != (rows, H):
+        raise ValueError("gamma must be [total, H]")
+    hn = torch.empty(rows, H, device=q.device, dtype=torch.float32) if return_hnorm else None
+    need = int(lib.gka_fwd_workspace_bytes(ctypes.byref(p)))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    st = lib.gka_fwd_varlen(
+        ctypes.byref(p), _ptr(cu_seqlens), ctypes.c_int64(total), _ptr(q), _ptr(k), _ptr(v),
+        _ptr(gamma), _ptr(beta), _ptr(o), _ptr(state.h if state else None),
+        _ptr(state.u if state else None), _ptr(state.n2 if state else None), _ptr(hn),
+        _ptr(workspace), ctypes.c_size_t(workspace.numel() if workspace is not None else 0),
+        _stream(stream))
+    _check(st)
+    return (o, hn) if return_hnorm else o

@@ -73,7 +73,28 @@ WORKLOADS: Dict[str, Workload] = {
     "decode_b256_h8_d128": Workload("decode_b256_h8_d128", B=256, T=1, H=8, D=128, chunk=64,
                                     gate_mu=3.0, gate_sd=1.0, a=0.05, iters=10, dtype="bf16",
                                     seed=5, warmup=512, steps=1000),
+    # a serving step on a packed batch: 8 prompts of 256..2048 tokens and 56 decode rows, each
+    # continuing a state built from `warmup` tokens (lengths from varlen_lengths)
+    "varlen_b64_h8_d128": Workload("varlen_b64_h8_d128", B=64, T=2048, H=8, D=128, chunk=64,
+                                   gate_mu=3.0, gate_sd=1.0, a=0.05, iters=10, dtype="bf16",
+                                   seed=6, warmup=64, steps=1),
 }
+
+
+def varlen_lengths(w: Workload):
+    """Token counts of the packed serving workload, per sequence: (warm-up tokens, tokens of the
+    step). Every eighth sequence is a prompt (no warm-up; length uniform in 256..T from a stream
+    keyed [seed, 5]); the others decode one token after w.warmup warm-up tokens."""
+    rng = np.random.default_rng([w.seed, 5])
+    pre, step = [], []
+    for b in range(w.B):
+        if b % 8 == 0:
+            pre.append(0)
+            step.append(int(rng.integers(256, w.T + 1)))
+        else:
+            pre.append(w.warmup)
+            step.append(1)
+    return pre, step
 
 
 def round_bf16(x: np.ndarray) -> np.ndarray:
@@ -188,6 +209,26 @@ def make_beta(B: int, T: int, H: int, seed: int, beta_mu: float = 0.0, beta_sd: 
     if heads is None:
         return np.ascontiguousarray(out.reshape(B, H, T).transpose(0, 2, 1))
     return np.ascontiguousarray(out.T[None])
+
+
+def make_varlen(lengths: Sequence[int], H: int, D: int, gate_mu: float, gate_sd: float,
+                dtype: str, seed: int):
+    """A packed batch of sequences with the given lengths: q, k, v [total, H, D], gamma
+    [total, H] (float64 copies of the device values, as make_prefill) and the offsets cu
+    (int32 [B + 1], sequence b = rows cu[b]..cu[b+1]). Sequence b is make_prefill's single row
+    with seed = 1000 seed + b, so any one sequence can be redrawn on its own."""
+    cu = np.zeros(len(lengths) + 1, dtype=np.int32)
+    cu[1:] = np.cumsum(np.asarray(lengths, dtype=np.int64))
+    total = int(cu[-1])
+    q, k, v = (np.zeros((total, H, D)) for _ in range(3))
+    g = np.zeros((total, H))
+    for b, L in enumerate(lengths):
+        if L == 0:
+            continue
+        qb, kb, vb, gb = make_prefill(1, L, H, D, gate_mu, gate_sd, dtype, 1000 * seed + b)
+        sl = slice(int(cu[b]), int(cu[b + 1]))
+        q[sl], k[sl], v[sl], g[sl] = qb[0], kb[0], vb[0], gb[0]
+    return q, k, v, g, cu
 
 
 def make_workload(w: Workload, T: Optional[int] = None, B: Optional[int] = None,

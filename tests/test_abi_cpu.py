@@ -33,7 +33,7 @@ def test_header_declares_the_bound_functions():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.gka_abi_version() == 3
+    assert lib.gka_abi_version() == 4
 
 
 def test_status_strings(lib):
@@ -195,3 +195,24 @@ def test_residual_entry_points_check_their_output(lib):
     assert step_res(params(), None) == 1
     assert step_res(params(), ctypes.c_void_p(ADDR[10] + 1)) == 2
     assert step_res(params(), VP[4]) == 7
+
+
+def test_varlen_entry_point_checks(lib):
+    P = ctypes.byref
+    vl = lambda p, cu, total, q=VP[0], o=VP[4]: lib.gka_fwd_varlen(
+        P(p) if p is not None else None, cu, ctypes.c_int64(total), q, VP[1], VP[2], VP[3], None,
+        o, None, None, None, None, None, ctypes.c_size_t(0), None)
+    one = params(B=4, H=1, T=64, segments=1)
+    assert vl(None, VP[11], 10) == 1
+    assert vl(params(D=48, B=4, T=64), VP[11], 10) == 2
+    assert vl(one, None, 10) == 1  # the offsets are required
+    assert vl(one, ctypes.c_void_p(ADDR[11] + 2), 10) == 2
+    assert vl(one, VP[11], -1) == 2
+    assert vl(one, VP[11], 4 * 64 + 1) == 2  # more rows than B sequences of T
+    assert vl(one, VP[11], 0, q=None, o=None) == 0  # no rows: nothing to do
+    assert vl(params(T=0, B=4), VP[11], 0, q=None, o=None) == 0
+    assert vl(one, VP[11], 100, q=None) == 1
+    assert vl(one, VP[11], 100, o=VP[0]) == 7
+    # the alias check covers the packed rows: o starting inside the 100 rows of q is rejected
+    p2 = params(B=4, H=1, T=64, D=64, segments=1)
+    assert vl(p2, VP[11], 100, o=ctypes.c_void_p(ADDR[0] + 99 * 64 * 2)) == 7
