@@ -229,8 +229,8 @@ def bench_varlen(Wv, steps, warmup, ev):
                    Wv.iters, Wv.chunk, state=st)
     qs, ks, vs, gs, cs = d(q[idx2]), d(k[idx2]), d(v[idx2]), f(g[idx2]), offs(step)
     o = torch.empty_like(qs)
-    need = gka.workspace_bytes(Wv.B, max(step), Wv.H, Wv.D, Wv.chunk, Wv.iters, Wv.a,
-                               gka.GKA_BF16)
+    need = gka.varlen_workspace_bytes(Wv.B, max(step), Wv.H, Wv.D, Wv.chunk, Wv.iters, Wv.a,
+                                      gka.GKA_BF16)
     ws = torch.empty(max(need, 1), device="cuda", dtype=torch.uint8)
     call = lambda: gka.fwd_varlen(qs, ks, vs, gs, cs, max(step), Wv.a, Wv.iters, Wv.chunk,
                                   state=st, out=o, workspace=ws)

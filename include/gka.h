@@ -184,8 +184,10 @@ gka_status gka_step_residuals(const gka_params* p, const void* q, const void* k,
  * carried state, so one call can serve a batch that mixes prompts being prefilled and
  * sequences being decoded (the chunked-prefill / decode hand-off inside one call).
  *   p          B = number of sequences, T = an upper bound on every sequence length (it sizes
- *              the segment plan and the workspace: gka_fwd_workspace_bytes(p) as for a dense
- *              [B, T] call); other fields as for gka_fwd_chunked
+ *              the segment plan); other fields as for gka_fwd_chunked. segments = 0 chooses
+ *              about 12 chunks of T per segment.
+ *   workspace  at least gka_fwd_varlen_workspace_bytes(p) bytes (it also holds the dispatch
+ *              order: the workgroups of the longest sequences are started first, for B <= 4096)
  *   cu_seqlens DEVICE int32 [B + 1], 4-byte aligned: sequence b is rows [cu[b], cu[b+1]) of
  *              the token axis, cu[0] = 0, non-decreasing, cu[B] = total. A length above T counts
  *              as T (the rows past it are not read, written or carried); an empty sequence
@@ -199,6 +201,8 @@ gka_status gka_step_residuals(const gka_params* p, const void* q, const void* k,
  * Errors as for gka_fwd_chunked_beta; NULL cu_seqlens is GKA_ERR_NULL, a misaligned one or a
  * total outside [0, B T] GKA_ERR_SHAPE. total = 0 (or T = 0) is a no-op.
  */
+size_t gka_fwd_varlen_workspace_bytes(const gka_params* p);
+
 gka_status gka_fwd_varlen(const gka_params* p, const int32_t* cu_seqlens, int64_t total,
                           const void* q, const void* k, const void* v, const float* gamma,
                           const float* beta, void* o, float* h_state, float* u_state,

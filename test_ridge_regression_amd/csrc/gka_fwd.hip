@@ -188,8 +188,9 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tmax, 
   float* PreG = reinterpret_cast<float*>(PreV + Cfg::NU);
 
   const int seg = blockIdx.x;
-  const int bh = blockIdx.y;
-  const int b = bh / Hn, h = bh % Hn;
+  int b, h;
+  head_of(A, blockIdx.y, Hn, b, h);
+  const int bh = b * Hn + h;
   const int wave = threadIdx.x / kWave;
   // Per-lane indices. They are passed through refresh() at the start of every phase of the chunk
   // walk, so that the many addresses derived from them are recomputed where they are used instead
@@ -206,8 +207,12 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tmax, 
   long long seq0;  // first row of sequence b
   int Tlen;        // its length
   seq_range(A, b, Tmax, seq0, Tlen);
+  // segments past the sequence's last one have nothing to do (packed batches); the last one
+  // writes the final state
+  const int last = last_segment(Tlen, J, C);
+  if (seg > last) return;
   const int c_begin = seg * J;
-  const int c_end = min(min(N, c_begin + J), (Tlen + C - 1) / C);  // may be empty
+  const int c_end = min(min(N, c_begin + J), (Tlen + C - 1) / C);
   const long long tok_stride = (long long)Hn * D;
   const T* qg = static_cast<const T*>(A.q);
   const T* kg = static_cast<const T*>(A.k);
@@ -807,7 +812,7 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tmax, 
   lds_barrier();  // the last chunk's output tile is staged
   flush_o();
   // ---- results of the walk ------------------------------------------------------------------
-  if (A.out_h && state_active && seg == S - 1) {
+  if (A.out_h && state_active && seg == last) {
     float* oh = A.out_h + (size_t)bh * D * D;
     float* ou = A.out_u + (size_t)bh * D * D;
 #pragma unroll
@@ -819,9 +824,7 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tmax, 
         *reinterpret_cast<f32x4*>(ou + (size_t)c * D + r) = Ust[jf][jc];
       }
   }
-  // (a sequence without tokens keeps the carried ||H||^2 as it was, not its recomputed value)
-  if (A.n2_out && seg == S - 1 && tid == 0)
-    A.n2_out[bh] = Tlen == 0 && A.n2_in ? A.n2_in[bh] : n0sq;
+  if (A.n2_out && seg == last && tid == 0) A.n2_out[bh] = n0sq;
 }
 
 // Segment summaries (carry only): for each (segment, head), the state reached from a zero state
@@ -856,8 +859,9 @@ __global__ __launch_bounds__(1024) void summary_kernel(WalkArgs A, int B, int Tm
   typedef O vecO __attribute__((ext_vector_type(VEC)));
 
   const int seg = blockIdx.x;
-  const int bh = blockIdx.y;
-  const int b = bh / Hn, h = bh % Hn;
+  int b, h;
+  head_of(A, blockIdx.y, Hn, b, h);
+  const int bh = b * Hn + h;
   const int wave = threadIdx.x / kWave;
   int tid = threadIdx.x, lane = tid % kWave;
   int lr = lane % 16, lg = lane / 16;
@@ -867,8 +871,11 @@ __global__ __launch_bounds__(1024) void summary_kernel(WalkArgs A, int B, int Tm
   long long seq0;  // first row of sequence b
   int Tlen;        // its length
   seq_range(A, b, Tmax, seq0, Tlen);
+  // the last segment of the sequence needs no summary (its walk writes the final state), nor
+  // do the segments past it
+  if (seg >= last_segment(Tlen, J, C)) return;
   const int c_begin = seg * J;
-  const int c_end = min(min(N, c_begin + J), (Tlen + C - 1) / C);  // may be empty
+  const int c_end = min(N, c_begin + J);
   const long long tok_stride = (long long)Hn * D;
   const T* kg = static_cast<const T*>(A.k);
   const T* vg = static_cast<const T*>(A.v);
@@ -998,32 +1005,70 @@ __global__ __launch_bounds__(1024) void summary_kernel(WalkArgs A, int B, int Tm
   if (tid == 0) A.log2g_out[(long long)bh * S + seg] = log2g_seg;
 }
 
+// Dispatch order of a packed batch: thread b counts the sequences that come before it (longer,
+// or as long with a smaller index) over tiles of the lengths staged in LDS; that count is its
+// rank. One thread per sequence, B <= kMaxOrdered.
+__global__ __launch_bounds__(256) void order_kernel(const int* __restrict__ cu, int B, int Tmax,
+                                                    int* __restrict__ order) {
+  __shared__ int len_s[256];
+  const int b = blockIdx.x * 256 + threadIdx.x;
+  auto len_of = [&](int j) { return min(max(cu[j + 1] - cu[j], 0), Tmax); };
+  const int mine = b < B ? len_of(b) : 0;
+  int rank = 0;
+  for (int j0 = 0; j0 < B; j0 += 256) {
+    __syncthreads();  // the previous tile is read
+    if (j0 + (int)threadIdx.x < B) len_s[threadIdx.x] = len_of(j0 + threadIdx.x);
+    __syncthreads();
+    const int n = min(256, B - j0);
+    for (int i = 0; i < n; ++i) {
+      const int l = len_s[i], j = j0 + i;
+      rank += (l > mine) || (l == mine && j < b);
+    }
+  }
+  if (b < B) order[rank] = b;
+}
+
+hipError_t launch_order(const int* cu, int B, int Tmax, int* order, hipStream_t stream) {
+  hipLaunchKernelGGL(order_kernel, dim3((B + 255) / 256), dim3(256), 0, stream, cu, B, Tmax,
+                     order);
+  return hipGetLastError();
+}
+
 // Affine scan over segments, elementwise over the D x D entries of H and U.
 __global__ __launch_bounds__(256) void scan_kernel(float* __restrict__ st,
                                                    const float* __restrict__ log2g,
                                                    float* __restrict__ h, float* __restrict__ u,
                                                    const float* __restrict__ hnorm2,
-                                                   float* __restrict__ n2_seg0, int S, int DD) {
+                                                   float* __restrict__ n2_seg0, int S, int DD,
+                                                   const int* __restrict__ cu, int Tmax, int Hn,
+                                                   int J, int C) {
   const int bh = blockIdx.y;
   const int e4 = blockIdx.x * blockDim.x + threadIdx.x;  // float4 index inside one matrix
   if (blockIdx.x == 0 && threadIdx.x == 0) n2_seg0[bh] = hnorm2 ? hnorm2[bh] : 0.0f;
   if (e4 * 4 >= DD) return;
+  // packed batches: start states up to the sequence's last segment only (summaries exist
+  // below it); a dense batch has last = S - 1
+  int last = S - 1;
+  if (cu) {
+    const int b = bh / Hn;
+    last = last_segment(min(max(cu[b + 1] - cu[b], 0), Tmax), J, C);
+  }
   f32x4 sh = {0.f, 0.f, 0.f, 0.f}, su = {0.f, 0.f, 0.f, 0.f};
   if (h) {
     sh = reinterpret_cast<const f32x4*>(h + (size_t)bh * DD)[e4];
     su = reinterpret_cast<const f32x4*>(u + (size_t)bh * DD)[e4];
   }
-  for (int s = 0; s < S; ++s) {
+  for (int s = 0; s <= last; ++s) {
     f32x4* ph = reinterpret_cast<f32x4*>(st + ((size_t)bh * S + s) * 2 * DD) + e4;
     f32x4* pu = reinterpret_cast<f32x4*>(st + ((size_t)bh * S + s) * 2 * DD + DD) + e4;
     f32x4 dh = {0.f, 0.f, 0.f, 0.f}, du = {0.f, 0.f, 0.f, 0.f};
-    if (s + 1 < S) {  // the last segment has no summary
+    if (s < last) {  // the last segment has no summary
       dh = *ph;
       du = *pu;
     }
     *ph = sh;
     *pu = su;
-    if (s + 1 < S) {
+    if (s < last) {
       const float g = exp2f(log2g[(size_t)bh * S + s]);
       sh = g * sh + dh;
       su = g * su + du;
@@ -1108,11 +1153,12 @@ hipError_t launch_walk(const FwdPlan& pl, bool summary, const WalkArgs& a, const
 }
 
 hipError_t launch_scan(const FwdPlan& pl, float* ws_states, const float* ws_log2g, float* h,
-                       float* u, const float* hnorm2, float* n2_seg0, hipStream_t stream) {
+                       float* u, const float* hnorm2, float* n2_seg0, const int* cu,
+                       hipStream_t stream) {
   const int DD = pl.D * pl.D;
   const dim3 grid((DD / 4 + 255) / 256, pl.B * pl.H);
   hipLaunchKernelGGL(scan_kernel, grid, dim3(256), 0, stream, ws_states, ws_log2g, h, u, hnorm2,
-                     n2_seg0, pl.S, DD);
+                     n2_seg0, pl.S, DD, cu, pl.T, pl.H, pl.J, pl.C);
   return hipGetLastError();
 }
 

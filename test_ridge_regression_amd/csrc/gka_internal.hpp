@@ -38,6 +38,7 @@ struct FwdPlan {
   int S;  // segments
   int J;  // chunks per segment
   size_t ws_bytes;
+  size_t order_off;  // packed batches: byte offset of the dispatch order in the workspace
 };
 
 // Arguments of the fused chunk walk (one workgroup per (segment, batch row x head)).
@@ -64,7 +65,23 @@ struct WalkArgs {
   float* log2g_out;       // summary mode: per-segment log2 of the gate product [BH][S]
   float* resid;           // optional residual norms ||q_t - A_t x_i||, [B, T, H, iters + 1]
   const int* cu;          // packed batches: sequence b is rows [cu[b], cu[b+1]) (NULL: dense)
+  const int* order;       // packed batches: sequences by decreasing length (NULL: in order)
 };
+
+// The last segment holding tokens of a sequence of len tokens (segments of J chunks of C): -1
+// for an empty sequence. Segments past it have nothing to do; it writes the final state. For a
+// dense batch it is S - 1.
+__host__ __device__ inline int last_segment(int len, int J, int C) {
+  return (len + J * C - 1) / (J * C) - 1;
+}
+
+// Sequence b and head h of grid row y: with an order, rows go to the longest sequences first,
+// so that their workgroups are dispatched first.
+__device__ inline void head_of(const WalkArgs& A, int y, int Hn, int& b, int& h) {
+  const int slot = y / Hn;
+  b = A.order ? A.order[slot] : slot;
+  h = y % Hn;
+}
 
 // Rows of sequence b on the token axis: [s0, s0 + len). Dense batches: s0 = b Tmax, len = Tmax;
 // packed batches: from the offsets, the length clamped to [0, Tmax] (rows past Tmax are not
@@ -83,6 +100,11 @@ __device__ inline void seq_range(const WalkArgs& A, int b, int Tmax, long long& 
 hipError_t launch_walk(const FwdPlan& pl, bool summary, const WalkArgs& a, const ChebConsts& cc,
                        hipStream_t stream);
 
+// Packed batches: order[rank] = b, the sequences by decreasing length (ties by index), from
+// the offsets cu [B + 1] with lengths clamped to [0, Tmax]. B <= kMaxOrdered.
+constexpr int kMaxOrdered = 4096;
+hipError_t launch_order(const int* cu, int B, int Tmax, int* order, hipStream_t stream);
+
 // The chunk walk with token-owning waves (bf16 inputs, chunks of 64 tokens, D = 32, 64, 128):
 // same arguments and results as the feature-split walk of launch_walk.
 bool walk_tok_supported(const FwdPlan& pl);
@@ -98,6 +120,7 @@ hipError_t launch_summary_tok(const FwdPlan& pl, const WalkArgs& a, hipStream_t 
 // d_{s-1} for s >= 1, written in place over the summaries d_0 .. d_{S-2} (slot S-1 receives
 // start[S-1]); also copies hnorm2 to n2_seg0. The final state comes from the last segment's walk.
 hipError_t launch_scan(const FwdPlan& pl, float* ws_states, const float* ws_log2g, float* h,
-                       float* u, const float* hnorm2, float* n2_seg0, hipStream_t stream);
+                       float* u, const float* hnorm2, float* n2_seg0, const int* cu,
+                       hipStream_t stream);
 
 }  // namespace gka

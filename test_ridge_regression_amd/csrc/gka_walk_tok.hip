@@ -138,8 +138,9 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
   float* v_coef = v_sc + 16;  // [iters][4] krs, kys, bts of each iteration (rescaled form)
 
   const int seg = blockIdx.x;
-  const int bh = blockIdx.y;
-  const int b = bh / Hn, h = bh % Hn;
+  int b, h;
+  head_of(A, blockIdx.y, Hn, b, h);
+  const int bh = b * Hn + h;
   int wave = threadIdx.x / kWave;
   // Per-lane indices, passed through refresh() at the start of every phase so that the
   // addresses derived from them are recomputed where they are used instead of being hoisted
@@ -156,8 +157,12 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
   long long seq0;  // first row of sequence b
   int Tlen;        // its length
   seq_range(A, b, Tmax, seq0, Tlen);
+  // segments past the sequence's last one have nothing to do (packed batches); the last one
+  // writes the final state
+  const int last = last_segment(Tlen, J, C);
+  if (seg > last) return;
   const int c_begin = seg * J;
-  const int c_end = min(min(N, c_begin + J), (Tlen + C - 1) / C);  // may be empty
+  const int c_end = min(min(N, c_begin + J), (Tlen + C - 1) / C);
   const long long tok_stride = (long long)Hn * D;
   const uint32_t tok_bytes = (uint32_t)Hn * D * 2u;  // < 2^25: 64 rows fit a 32-bit offset
   const bf16* qg = static_cast<const bf16*>(A.q);
@@ -787,7 +792,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
     }
     n0sq = n2last;
   }
-  if (A.out_h && seg == S - 1) {
+  if (A.out_h && seg == last) {
     float* oh = A.out_h + (size_t)bh * D * D;
     float* ou = A.out_u + (size_t)bh * D * D;
 #pragma unroll
@@ -799,9 +804,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
         *reinterpret_cast<f32x4*>(ou + o) = *us_tile(jr, jc);
       }
   }
-  // (a sequence without tokens keeps the carried ||H||^2 as it was, not its recomputed value)
-  if (A.n2_out && seg == S - 1 && tid == 0)
-    A.n2_out[bh] = Tlen == 0 && A.n2_in ? A.n2_in[bh] : n0sq;
+  if (A.n2_out && seg == last && tid == 0) A.n2_out[bh] = n0sq;
 }
 
 // ---- segment summaries -------------------------------------------------------------------
@@ -870,8 +873,9 @@ void summary_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J
   auto vrows = [&](int slot) { return krows(slot) + CB * LDR; };
 
   const int seg = blockIdx.x;
-  const int bh = blockIdx.y;
-  const int b = bh / Hn, h = bh % Hn;
+  int b, h;
+  head_of(A, blockIdx.y, Hn, b, h);
+  const int bh = b * Hn + h;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
   int tid = threadIdx.x, lane = tid % kWave;
   int lr = lane % 16, lg = lane / 16;
@@ -884,8 +888,11 @@ void summary_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J
   long long seq0;  // first row of sequence b
   int Tlen;        // its length
   seq_range(A, b, Tmax, seq0, Tlen);
+  // the last segment of the sequence needs no summary (its walk writes the final state), nor
+  // do the segments past it
+  if (seg >= last_segment(Tlen, J, CB)) return;
   const int t_end = min(Tlen, t_begin + J * CB);
-  const int NB = max(0, (t_end - t_begin + CB - 1) / CB);  // 0: an empty segment
+  const int NB = (t_end - t_begin + CB - 1) / CB;
   const long long tok_stride = (long long)Hn * D;
   const uint32_t tok_bytes = (uint32_t)Hn * D * 2u;
   auto block_t0 = [&](int p) { return t_begin + (NB - 1 - p) * CB; };

@@ -27,7 +27,8 @@ STATUS = {0: "GKA_OK", 1: "GKA_ERR_NULL", 2: "GKA_ERR_SHAPE", 3: "GKA_ERR_VALUE"
           4: "GKA_ERR_DTYPE", 5: "GKA_ERR_WORKSPACE", 6: "GKA_ERR_HIP", 7: "GKA_ERR_ALIAS"}
 EXPORTED = ["gka_fwd_workspace_bytes", "gka_fwd_chunked", "gka_step", "gka_fwd_chunked_beta",
             "gka_step_beta", "gka_fwd_chunked_residuals", "gka_step_residuals",
-            "gka_fwd_varlen", "gka_status_str", "gka_abi_version"]
+            "gka_fwd_varlen", "gka_fwd_varlen_workspace_bytes", "gka_status_str",
+            "gka_abi_version"]
 
 
 class GkaParams(ctypes.Structure):
@@ -77,6 +78,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gka_fwd_varlen.argtypes = [P, vp, ctypes.c_int64, vp, vp, vp, fp, fp, vp, fp, fp, fp, fp,
                                    vp, ctypes.c_size_t, vp]
     lib.gka_fwd_varlen.restype = ctypes.c_int
+    lib.gka_fwd_varlen_workspace_bytes.argtypes = [P]
+    lib.gka_fwd_varlen_workspace_bytes.restype = ctypes.c_size_t
     lib.gka_status_str.argtypes = [ctypes.c_int]
     lib.gka_status_str.restype = ctypes.c_char_p
     lib.gka_abi_version.argtypes = []
@@ -153,6 +156,12 @@ def make_params(B, T, H, D, chunk, iters, a, dtype_code, segments=0) -> GkaParam
 def workspace_bytes(B, T, H, D, chunk, iters, a, dtype_code, segments=0) -> int:
     p = make_params(B, T, H, D, chunk, iters, a, dtype_code, segments)
     return int(load().gka_fwd_workspace_bytes(ctypes.byref(p)))
+
+
+def varlen_workspace_bytes(B, T, H, D, chunk, iters, a, dtype_code, segments=0) -> int:
+    """gka_fwd_varlen_workspace_bytes: B sequences, every length <= T."""
+    p = make_params(B, T, H, D, chunk, iters, a, dtype_code, segments)
+    return int(load().gka_fwd_varlen_workspace_bytes(ctypes.byref(p)))
 
 
 def fwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor, a: float,
@@ -297,7 +306,7 @@ def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.T
     if tuple(gamma.shape) != (rows, H):
         raise ValueError("gamma must be [total, H]")
     hn = torch.empty(rows, H, device=q.device, dtype=torch.float32) if return_hnorm else None
-    need = int(lib.gka_fwd_workspace_bytes(ctypes.byref(p)))
+    need = int(lib.gka_fwd_varlen_workspace_bytes(ctypes.byref(p)))
     if workspace is None and need > 0:
         workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
     st = lib.gka_fwd_varlen(

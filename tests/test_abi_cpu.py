@@ -33,7 +33,7 @@ def test_header_declares_the_bound_functions():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.gka_abi_version() == 4
+    assert lib.gka_abi_version() == 5
 
 
 def test_status_strings(lib):
@@ -203,6 +203,12 @@ def test_varlen_entry_point_checks(lib):
         P(p) if p is not None else None, cu, ctypes.c_int64(total), q, VP[1], VP[2], VP[3], None,
         o, None, None, None, None, None, ctypes.c_size_t(0), None)
     one = params(B=4, H=1, T=64, segments=1)
+    assert vl(one, VP[11], 10) == 5  # the dispatch order needs a workspace even for one segment
+    ws = lib.gka_fwd_varlen_workspace_bytes(P(one))
+    assert ws >= 4 * 4 and ws % 256 == 0
+    vl = lambda p, cu, total, q=VP[0], o=VP[4], w=ctypes.c_void_p(ADDR[11] + (1 << 31)), wsb=1 << 30: lib.gka_fwd_varlen(
+        P(p) if p is not None else None, cu, ctypes.c_int64(total), q, VP[1], VP[2], VP[3], None,
+        o, None, None, None, None, w, ctypes.c_size_t(wsb), None)
     assert vl(None, VP[11], 10) == 1
     assert vl(params(D=48, B=4, T=64), VP[11], 10) == 2
     assert vl(one, None, 10) == 1  # the offsets are required
@@ -216,3 +222,19 @@ def test_varlen_entry_point_checks(lib):
     # the alias check covers the packed rows: o starting inside the 100 rows of q is rejected
     p2 = params(B=4, H=1, T=64, D=64, segments=1)
     assert vl(p2, VP[11], 100, o=ctypes.c_void_p(ADDR[0] + 99 * 64 * 2)) == 7
+
+
+def test_varlen_plan_and_workspace(lib):
+    P = ctypes.byref
+    # dense plans are unchanged by the packed-batch plan
+    p = params(B=8, H=8, T=2048, D=128)
+    assert lib.gka_fwd_workspace_bytes(P(p)) == lib.gka_fwd_workspace_bytes(P(params(B=8, H=8, T=2048, D=128)))
+    # packed: about 12 chunks of T per segment by default, plus the order of the B sequences
+    D, B, H = 128, 64, 8
+    for T, S in ((64, 1), (768, 1), (832, 2), (2048, 3)):
+        ws = lib.gka_fwd_varlen_workspace_bytes(P(params(B=B, H=H, T=T, D=D)))
+        seg = 0 if S == 1 else ((B * H * S * (2 * D * D + 1) + B * H) * 4 + 255) // 256 * 256
+        assert ws == seg + 256, (T, S, ws)
+    # more sequences than the order kernel takes: no order, no extra bytes
+    big = params(B=5000, H=1, T=64, D=32)
+    assert lib.gka_fwd_varlen_workspace_bytes(P(big)) == lib.gka_fwd_workspace_bytes(P(big))

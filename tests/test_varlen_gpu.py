@@ -177,3 +177,18 @@ def test_serving_batch_at_scale():
         eh = max_rel(hn2[cu2[b]:cu2[b + 1]], ref["hnorm"][0, lens_pre[b]:])
         log(f"  sequence {b} ({lens_pre[b]} + {lens[b]} tokens): rel_l2(o)={e:.3e} hnorm={eh:.3e}")
         assert e <= TOL_O["bf16"] and eh <= TOL_HNORM
+
+
+def test_many_sequences_without_a_dispatch_order():
+    # more than 4096 sequences: the launch keeps the plain order; equal lengths must still give
+    # the dense call's results bit for bit
+    B, T, H, D = 4100, 3, 1, 32
+    q, k, v, g = W.make_prefill(B, T, H, D, 3.0, 1.0, "fp32", seed=860)
+    cu = (np.arange(B + 1) * T).astype(np.int32)
+    log("varlen B=4100 (no dispatch order) == dense")
+    o_d = gka.fwd_chunked(dev(q), dev(k), dev(v), dev(g), 0.05, 6, 16, segments=1)
+    o_v = gka.fwd_varlen(dev(q.reshape(B * T, H, D)), dev(k.reshape(B * T, H, D)),
+                         dev(v.reshape(B * T, H, D)), dev(g.reshape(B * T, H)),
+                         torch.from_numpy(cu).to("cuda"), T, 0.05, 6, 16, segments=1)
+    torch.cuda.synchronize()
+    assert torch.equal(o_d.reshape(B * T, H, D), o_v)
