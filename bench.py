@@ -99,8 +99,8 @@ def measured_traffic(kernel):
         rec = json.load(open(path))[kernel]
     except (OSError, KeyError, ValueError):
         return None
-    files = {"walk_tok_kernel": ("gka_walk_tok.hip", "gka_common.hpp"),
-             "step_kernel": ("gka_step.hip", "gka_common.hpp")}[kernel]
+    files = {"walk_tok_kernel": ("gka_walk_tok.hip", "gka_common.hpp", "gka_internal.hpp"),
+             "step_kernel": ("gka_step.hip", "gka_common.hpp", "gka_internal.hpp")}[kernel]
     h = hashlib.sha256()
     for f in files:
         with open(os.path.join(ROOT, "test_ridge_regression_amd", "csrc", f), "rb") as fh:
