@@ -83,6 +83,12 @@ ChebConsts cheb_consts(float a, int iters) {
     cc.kr[i] = (float)(w * (1.0 - c * ad));
     cc.ky[i] = (float)(-w * c);
   }
+  // The iterate's coefficients (beta, bts) carry the power of two xsc (exact scaling): for
+  // large a the iterate is about |q| / a, below the normal range of fp16 operands
+  double xsc = 1.0;
+  while (xsc * 2.0 <= ad) xsc *= 2.0;
+  cc.inv_xsc = (float)(1.0 / xsc);
+  for (int i = 0; i < iters; ++i) cc.beta[i] = (float)(cur[i] * xsc);
   // Rescaled form: ratio r = s_i / s_{i-1} of consecutive scales, s_i itself only for bts
   // (where underflow to 0 only drops terms far below the rounding of the rest)
   constexpr double kS0 = 0.7390851332151607;  // the fixed point of cos
@@ -91,7 +97,7 @@ ChebConsts cheb_consts(float a, int iters) {
   // The coefficients of step iters - 1 (which gives R_iters) are used by the residual mode only.
   double r = 1.0, s = kS0;
   for (int i = 0; i < iters; ++i) {
-    cc.bts[i] = (float)(cur[i] * s);
+    cc.bts[i] = (float)(cur[i] * s * xsc);
     cc.sres[i] = (float)s;
     const double kp = i == 0 ? 0.0 : 1.0 - om[i];
     if (i >= 1 && std::fabs(kp) < 0x1p-64) {

@@ -393,6 +393,10 @@ struct ChebConsts {
   // the coefficients of one more step (it = iters - 1, giving R_iters) are set
   float sres[65];
   int res_extra;
+  // the iterate is formed times xsc = 2^floor(log2 a) (1 for a < 2), a power of two that keeps
+  // it (about |q| / a) in the normal range of the 16-bit operands of the output products; the
+  // output accumulators are multiplied by inv_xsc = 1 / xsc before they are stored
+  float inv_xsc;
 };
 
 }  // namespace gka

@@ -800,7 +800,8 @@ __global__ __launch_bounds__(512) void walk_kernel(WalkArgs A, int B, int Tmax, 
         for (int jf = 0; jf < FPW; ++jf)
 #pragma unroll
           for (int jt = 0; jt < TPW; ++jt)
-            store4<T>(Ob + (tok_of(jt) + lr) * LDD + row_of(jf) + 4 * lg, Y[jf][jt]);
+            // (the iterate was formed times a power of two)
+            store4<T>(Ob + (tok_of(jt) + lr) * LDD + row_of(jf) + 4 * lg, Y[jf][jt] * cc.inv_xsc);
       }
       pend_t0 = t0;
       pend_nv = nv;

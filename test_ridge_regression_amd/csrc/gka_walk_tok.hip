@@ -786,7 +786,8 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
       const uint32_t ooff = (uint32_t)t * tok_bytes + (uint32_t)lg * 8u;
 #pragma unroll
       for (int ft = 0; ft < FT; ++ft) {
-        const bf16x4 ov = {(bf16)y[ft][0], (bf16)y[ft][1], (bf16)y[ft][2], (bf16)y[ft][3]};
+        const f32x4 yo = y[ft] * cc.inv_xsc;  // the iterate was formed times a power of two
+        const bf16x4 ov = {(bf16)yo[0], (bf16)yo[1], (bf16)yo[2], (bf16)yo[3]};
         buffer_store8(ov, ro, ooff + 32u * ft);
       }
     }

@@ -295,3 +295,15 @@ def test_bitwise_deterministic():
     o2 = gka.fwd_chunked(*args, 0.05, 10, 64, segments=4)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2)
+
+
+@pytest.mark.parametrize("a", [3.0, 1e2, 1e4, 1e6])
+@pytest.mark.parametrize("dtype,D,C", [("bf16", 128, 64), ("bf16", 64, 32), ("fp32", 32, 16)])
+def test_large_ridge_scale(dtype, D, C, a):
+    # the iterate is about |q| / a: for large a it would fall below the normal range of the fp16
+    # operands of the output products, so it is formed times a power of two near a
+    q, k, v, g = inputs(2, 150, 2, D, dtype, seed=900 + D)
+    ref = gka_forward_ref(q, k, v, g, a, 8)
+    log(f"large a={a:g} {dtype} D={D} C={C}")
+    got = run_prefill(q, k, v, g, a, 8, C, dtype, segments=2)
+    check_prefill(got, ref, dtype, f"a={a:g} {dtype} D={D} C={C}")

@@ -78,6 +78,23 @@ def test_prefill_residuals_iteration_counts(dtype, D, C, iters):
     check_resid(host(res), ref["residuals"], q, dtype, iters, f"{dtype} D={D} iters={iters}")
 
 
+@pytest.mark.parametrize("a", [1e6, 1e10])
+def test_prefill_residuals_huge_ridge(a):
+    # a = 1e10: |1 - omega_1| < 2^-64, the rescaled recurrence stops after R_1 and the kernels
+    # report the later residuals (below 2^-64 ||q_t||) as 0; a = 1e6 runs all steps
+    q, k, v, g = W.make_prefill(1, 70, 2, 128, 3.0, 1.0, "bf16", seed=730)
+    ref = gka_forward_ref(q, k, v, g, a, 6, return_residuals=True)
+    log(f"residuals bf16 D=128 a={a:g}")
+    o, res = gka.fwd_chunked_residuals(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), dev(g), a,
+                                       6, 64)
+    o0 = gka.fwd_chunked(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), dev(g), a, 6, 64)
+    torch.cuda.synchronize()
+    check_resid(host(res), ref["residuals"], q, "bf16", 6, f"bf16 a={a:g}")
+    assert torch.equal(o, o0)
+    if a > 1e9:
+        assert np.all(host(res)[..., 2:] == 0.0)
+
+
 def test_prefill_residuals_with_write_gate_and_state():
     D, T = 128, 200
     q, k, v, g = W.make_prefill(1, T, 2, D, 3.0, 1.0, "bf16", seed=740)
