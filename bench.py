@@ -304,7 +304,26 @@ def bench_decode(Wd, steps, ev):
     total_ms = ev.elapsed_ms(t0, t1)
     per = [ev.elapsed_ms(evs[2 * s], evs[2 * s + 1]) for s in range(steps)]
     ev.destroy(evs + [t0, t1])
-    return dict(total_ms=total_ms, ms_per_step=total_ms / steps, kernel_ms=float(np.mean(per)))
+    # the same steps captured in one HIP graph (a serving loop's form: no host launch per step)
+    log(f"decode graph: capture and replay {steps} steps")
+    st_g = gka.GkaState(st.h.clone(), st.u.clone(), st.n2.clone())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        for s in range(steps):
+            gka.step(Q[s], K[s], V[s], G[s], Wd.a, Wd.iters, st_g, out=O[s])
+    graph.replay()  # warm-up replay
+    torch.cuda.synchronize()
+    t0, t1 = ev.create(2)
+    stream = torch.cuda.current_stream().cuda_stream
+    ev.record(t0, stream)
+    graph.replay()
+    ev.record(t1, stream)
+    ev.sync(t1)
+    graph_ms = ev.elapsed_ms(t0, t1)
+    ev.destroy([t0, t1])
+    del graph, st_g
+    return dict(total_ms=total_ms, ms_per_step=total_ms / steps, kernel_ms=float(np.mean(per)),
+                graph_ms_per_step=graph_ms / steps)
 
 
 def cpu_baseline(W, o_dev=None, budget_s=12.0):
@@ -441,6 +460,8 @@ def main():
         rec["decode"] = {
             "workload": Wd.name, "tokens_per_s": Wd.B / (dec["ms_per_step"] * 1e-3),
             "ms_per_step": dec["ms_per_step"], "steps": args.decode_steps,
+            "graph_ms_per_step": dec["graph_ms_per_step"],
+            "graph_tokens_per_s": Wd.B / (dec["graph_ms_per_step"] * 1e-3),
             "roofline": {"bound": "hbm", "kernel": "step_kernel",
                          "achieved": bytes_launch / (dec["kernel_ms"] * 1e-3) / 1e9,
                          "peak": PEAK_HBM / 1e9, "unit": "GB/s",
@@ -449,7 +470,8 @@ def main():
                          "bytes_per_launch": bytes_launch,
                          "avg_launch_ms": dec["kernel_ms"]},
         }
-        log(f"decode: {dec['ms_per_step'] * 1e3:.1f} us/step, kernel {dec['kernel_ms'] * 1e3:.1f} us")
+        log(f"decode: {dec['ms_per_step'] * 1e3:.1f} us/step, kernel {dec['kernel_ms'] * 1e3:.1f} us, "
+            f"graph {dec['graph_ms_per_step'] * 1e3:.1f} us/step")
     if not args.no_cpu:
         log("cpu baseline (oracle)")
         rec["cpu_baseline"] = cpu_baseline(W, o_base)
