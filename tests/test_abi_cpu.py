@@ -238,3 +238,14 @@ def test_varlen_plan_and_workspace(lib):
     # more sequences than the order kernel takes: no order, no extra bytes
     big = params(B=5000, H=1, T=64, D=32)
     assert lib.gka_fwd_varlen_workspace_bytes(P(big)) == lib.gka_fwd_workspace_bytes(P(big))
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    # no fallback path: without the built library the binding raises
+    saved = gka._lib
+    try:
+        gka._lib = None
+        with pytest.raises(FileNotFoundError):
+            gka.load(str(tmp_path / "libgka.so"))
+    finally:
+        gka._lib = saved
