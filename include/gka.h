@@ -62,10 +62,10 @@ typedef enum { GKA_BF16 = 0, GKA_FP32 = 1 } gka_dtype;
  *   B, H     batch rows and heads, >= 1
  *   T        tokens per sequence (prefill; ignored by gka_step), >= 0; any T is allowed, a
  *            last partial chunk is handled exactly
- *   D        head dimension (key dim = value dim): bf16 {32, 64, 128}, fp32 {16, 32, 64}
+ *   D        head dimension (key dim = value dim): {16, 32, 64, 128}
  *   chunk    tokens per chunk for the chunk-wise form (prefill; ignored by gka_step):
- *            bf16 {32, 64}, fp32 {16, 32, 64}. The result does not depend on it beyond
- *            rounding (N = ceil(T / chunk) chunks).
+ *            bf16 {32, 64}; fp32 {16, 32, 64} for D <= 64 and {16} for D = 128. The result
+ *            does not depend on it beyond rounding (N = ceil(T / chunk) chunks).
  *   iters    Chebyshev iterations r, 1 <= r <= GKA_MAX_ITERS
  *   a        ridge scale, a > 0 and finite
  *   dtype    element type of q, k, v, o (gka_dtype)

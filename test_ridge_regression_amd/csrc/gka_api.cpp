@@ -16,11 +16,12 @@ constexpr int kAbiVersion = 5;
 constexpr int kCUs = 256;  // MI355X compute units: the segment plan aims at one workgroup per CU
 
 bool dims_supported(int dtype, int D) {
-  if (dtype == GKA_BF16) return D == 32 || D == 64 || D == 128;
-  return D == 16 || D == 32 || D == 64;
+  (void)dtype;
+  return D == 16 || D == 32 || D == 64 || D == 128;
 }
-bool chunk_supported(int dtype, int C) {
+bool chunk_supported(int dtype, int D, int C) {
   if (dtype == GKA_BF16) return C == 32 || C == 64;
+  if (D == 128) return C == 16;  // float32 operands of D = 128 fit the LDS of a CU at C = 16
   return C == 16 || C == 32 || C == 64;
 }
 size_t elem_bytes(int dtype) { return dtype == GKA_BF16 ? 2 : 4; }
@@ -171,7 +172,7 @@ bool make_plan(const gka_params* p, FwdPlan& pl, bool packed = false) {
 gka_status check_fwd(const gka_params* p) {
   gka_status st = check_common(p);
   if (st != GKA_OK) return st;
-  if (p->T < 0 || !chunk_supported(p->dtype, p->chunk)) return GKA_ERR_SHAPE;
+  if (p->T < 0 || !chunk_supported(p->dtype, p->D, p->chunk)) return GKA_ERR_SHAPE;
   if (p->segments < 0) return GKA_ERR_SHAPE;
   if ((long long)p->B * p->T * p->H * p->D > (1LL << 40)) return GKA_ERR_SHAPE;
   return GKA_OK;

@@ -57,7 +57,9 @@ namespace gka {
 // the summary walk, which holds only the state and so spreads it over four waves per SIMD.
 template <typename T, int D, int C, int NWaves = 8>
 struct WalkCfg {
-  typedef typename OperandOf<T>::type O;  // matrix-core operand type
+  // matrix-core operand type: fp16 for bf16 inputs, whose products take blocks of 32 features;
+  // float32 for float32 inputs and for bf16 inputs with D = 16 (exact for bf16 values)
+  typedef typename std::conditional<(D < 32), float, typename OperandOf<T>::type>::type O;
   static constexpr int NW = NWaves;
   static constexpr int NT = NW * kWave;
   static constexpr int FT = D / 16;  // feature tiles
@@ -1118,12 +1120,14 @@ hipError_t launch_walk(const FwdPlan& pl, bool summary, const WalkArgs& a, const
   if (pl.dtype == 0) {
     if (pl.C == 64) {
       switch (pl.D) {
+        case 16: return launch_walk_t<bf16, 16, 64>(pl, summary, a, cc, stream);
         case 32: return launch_walk_t<bf16, 32, 64>(pl, summary, a, cc, stream);
         case 64: return launch_walk_t<bf16, 64, 64>(pl, summary, a, cc, stream);
         case 128: return launch_walk_t<bf16, 128, 64>(pl, summary, a, cc, stream);
       }
     } else if (pl.C == 32) {
       switch (pl.D) {
+        case 16: return launch_walk_t<bf16, 16, 32>(pl, summary, a, cc, stream);
         case 32: return launch_walk_t<bf16, 32, 32>(pl, summary, a, cc, stream);
         case 64: return launch_walk_t<bf16, 64, 32>(pl, summary, a, cc, stream);
         case 128: return launch_walk_t<bf16, 128, 32>(pl, summary, a, cc, stream);
@@ -1135,6 +1139,7 @@ hipError_t launch_walk(const FwdPlan& pl, bool summary, const WalkArgs& a, const
         case 16: return launch_walk_t<float, 16, 16>(pl, summary, a, cc, stream);
         case 32: return launch_walk_t<float, 32, 16>(pl, summary, a, cc, stream);
         case 64: return launch_walk_t<float, 64, 16>(pl, summary, a, cc, stream);
+        case 128: return launch_walk_t<float, 128, 16>(pl, summary, a, cc, stream);
       }
     } else if (pl.C == 32) {
       switch (pl.D) {

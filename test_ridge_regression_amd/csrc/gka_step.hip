@@ -201,6 +201,7 @@ hipError_t launch_step(int dtype, int D, int BH, const void* q, const void* k, c
                        float* n2, float* resid, const ChebConsts& cc, hipStream_t stream) {
   if (dtype == 0) {
     switch (D) {
+      case 16: return launch_step_t<bf16, 16, 64>(BH, q, k, v, gamma, beta, o, h, u, n2, resid, cc, stream);
       case 32: return launch_step_t<bf16, 32, 128>(BH, q, k, v, gamma, beta, o, h, u, n2, resid, cc, stream);
       case 64: return launch_step_t<bf16, 64, 256>(BH, q, k, v, gamma, beta, o, h, u, n2, resid, cc, stream);
       case 128: return launch_step_t<bf16, 128, 512>(BH, q, k, v, gamma, beta, o, h, u, n2, resid, cc, stream);
@@ -210,6 +211,7 @@ hipError_t launch_step(int dtype, int D, int BH, const void* q, const void* k, c
       case 16: return launch_step_t<float, 16, 64>(BH, q, k, v, gamma, beta, o, h, u, n2, resid, cc, stream);
       case 32: return launch_step_t<float, 32, 128>(BH, q, k, v, gamma, beta, o, h, u, n2, resid, cc, stream);
       case 64: return launch_step_t<float, 64, 256>(BH, q, k, v, gamma, beta, o, h, u, n2, resid, cc, stream);
+      case 128: return launch_step_t<float, 128, 512>(BH, q, k, v, gamma, beta, o, h, u, n2, resid, cc, stream);
     }
   }
   return hipErrorInvalidValue;

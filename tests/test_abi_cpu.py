@@ -249,3 +249,13 @@ def test_missing_library_fails_loudly(tmp_path):
             gka.load(str(tmp_path / "libgka.so"))
     finally:
         gka._lib = saved
+
+
+def test_all_head_sizes_are_accepted(lib):
+    P = ctypes.byref
+    # multi-segment plans need a workspace: a nonzero size means the shape passed the checks
+    for dt, D, C in ((gka.GKA_BF16, 16, 32), (gka.GKA_BF16, 16, 64), (gka.GKA_FP32, 128, 16)):
+        assert lib.gka_fwd_workspace_bytes(P(params(dtype_code=dt, D=D, chunk=C, T=4096))) > 0
+    for C in (32, 64):  # float32 D = 128 only with chunks of 16
+        assert lib.gka_fwd_workspace_bytes(P(params(dtype_code=gka.GKA_FP32, D=128, chunk=C,
+                                                    T=4096))) == 0

@@ -307,3 +307,29 @@ def test_large_ridge_scale(dtype, D, C, a):
     log(f"large a={a:g} {dtype} D={D} C={C}")
     got = run_prefill(q, k, v, g, a, 8, C, dtype, segments=2)
     check_prefill(got, ref, dtype, f"a={a:g} {dtype} D={D} C={C}")
+
+
+@pytest.mark.parametrize("dtype,D,C", [("bf16", 16, 32), ("bf16", 16, 64), ("fp32", 128, 16)])
+@pytest.mark.parametrize("T", [37, 200])
+def test_head_sizes_16_and_128_with_state(dtype, D, C, T):
+    # bf16 with D = 16 (float32 operands) and float32 with D = 128 (chunks of 16)
+    rng = np.random.default_rng(950 + D + T)
+    Z = rng.standard_normal((2, 2, D, 2 * D))
+    h0 = (Z @ np.swapaxes(Z, -1, -2) / D).astype(np.float32).astype(np.float64)
+    u0 = rng.standard_normal((2, 2, D, D)).astype(np.float32).astype(np.float64)
+    n20 = np.sum(h0 * h0, axis=(-1, -2))
+    q, k, v, g = inputs(2, T, 2, D, dtype, seed=951 + D + T)
+    ref = gka_forward_ref(q, k, v, g, 0.05, 10, h0=h0, u0=u0, n2_0=n20)
+    for seg in (1, 3):
+        log(f"{dtype} D={D} C={C} T={T} segments={seg}")
+        got = run_prefill(q, k, v, g, 0.05, 10, C, dtype, state=(h0, u0, n20), segments=seg)
+        check_prefill(got, ref, dtype, f"{dtype} D={D} C={C} T={T} S={seg}")
+        tol = 1e-6 if dtype == "fp32" else 1e-5
+        assert rel_l2(got["h"], ref["h"]) < tol and rel_l2(got["u"], ref["u"]) < tol
+    # and a decode step continuing the state
+    st = gka.GkaState(dev(ref["h"]), dev(ref["u"]), dev(ref["n2"]))
+    q1, k1, v1, g1 = (x[:, 0] for x in inputs(2, 1, 2, D, dtype, seed=952 + D))
+    o1 = host(gka.step(dev(q1, dtype), dev(k1, dtype), dev(v1, dtype), dev(g1), 0.05, 10, st))
+    o1r, *_ = gka_step_ref(q1, k1, v1, g1, 0.05, 10, ref["h"].astype(np.float32),
+                           ref["u"].astype(np.float32), ref["n2"].astype(np.float32))
+    assert rel_l2(o1, o1r) <= TOL_O[dtype]
