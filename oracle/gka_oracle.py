@@ -33,6 +33,11 @@ is the plainest reading that all of them support):
   residuals         optionally ||q_t - A_t x_i|| for i = 0..iters, the quantity of the pages'
                     convergence plot (pith.science page, caption of Figure 1 (a); ai.info
                     summary, "Main Findings", the bullet comparing CH with CG)
+  backward          gradients of L = sum_t <do_t, o_t> by implicit differentiation of the solve
+                    (ai.info summary, "Methodology in Plain English" and "Main Findings": the
+                    backward re-runs the solver on the upstream gradient; Lemma 2: the query
+                    gradient is that solve), through the adaptive ridge lambda_t = a ||H_t||_F
+                    and back through the gated recurrences (derivation in gka_backward_ref)
   comparators       conjugate gradient, gradient descent and accelerated gradient descent on
                     the same systems (the solvers CH is compared with in those two passages),
                     for the convergence comparison only; the layer itself uses CH
@@ -365,3 +370,93 @@ def ridge_bruteforce(q, k, v, gamma, a: float, beta=None):
         St, *_ = np.linalg.lstsq(X, Y, rcond=None)  # St = S^T, [D_k, D_v]
         o[t] = St.T @ q[t]
     return o, hn
+
+
+# ------------------------------------------------------------------------------------------
+# Backward pass by implicit differentiation
+# ------------------------------------------------------------------------------------------
+
+def gka_backward_ref(q, k, v, gamma, do, a: float, iters: int, mode: str = "cheb", beta=None):
+    """Gradients of L = sum_t <do_t, o_t> with respect to q, k, v, gamma (and beta).
+
+    The solve x_t = A_t^-1 q_t, A_t = H_t + a ||H_t||_F I (symmetric), is differentiated
+    implicitly: with g_t = U_t^T do_t (= dL/dx_t) and y_t = A_t^-1 g_t (the same solver on the
+    upstream gradient, ``mode`` "cheb" or "exact"),
+        dq_t = y_t,
+        dL/dA_t = -y_t x_t^T, and A_t depends on H_t directly and through lambda_t, whose
+        derivative is a H_t / ||H_t||_F; so the local gradients of the statistics are
+        G_t = -y_t x_t^T + c_t H_t,  c_t = -a (y_t . x_t) / ||H_t||_F,   W_t = do_t x_t^T.
+    Back through H_t = gamma_t H_{t-1} + beta_t k_t k_t^T (and U_t likewise) the total
+    gradients obey Gb_t = G_t + gamma_{t+1} Gb_{t+1}, Wb_t = W_t + gamma_{t+1} Wb_{t+1}, and
+        dk_t = beta_t ((Gb_t + Gb_t^T) k_t + Wb_t^T v_t),   dv_t = beta_t Wb_t k_t,
+        dbeta_t = k_t^T Gb_t k_t + v_t^T Wb_t k_t,
+        dgamma_t = <Gb_t, H_{t-1}> + <Wb_t, U_{t-1}>.
+    A token with ||H_t||_F = 0 has x_t = 0 by definition: it contributes nothing and dq_t = 0.
+    Shapes as gka_forward_ref (zero initial state); do: [B, T, H, D]. Returns a dict with dq,
+    dk, dv [B, T, H, D], dgamma and dbeta [B, T, H].
+    """
+    q, k, v, do = (np.asarray(x, dtype=np.float64) for x in (q, k, v, do))
+    gamma = np.asarray(gamma, dtype=np.float64)
+    B, T, Hh, D = q.shape
+    N = B * Hh
+
+    def heads(x):
+        return np.moveaxis(x, 2, 1).reshape((N, T) + x.shape[3:])
+
+    qh, kh, vh, gh, dh = heads(q), heads(k), heads(v), heads(gamma), heads(do)
+    bh = np.ones((N, T)) if beta is None else heads(np.asarray(beta, dtype=np.float64))
+    # forward, keeping every state
+    Hs = np.zeros((N, T + 1, D, D))  # Hs[:, t + 1] = H_t, Hs[:, 0] = the zero initial state
+    Us = np.zeros((N, T + 1, D, D))
+    for t in range(T):
+        kk = kh[:, t, :, None] * kh[:, t, None, :]
+        vk = vh[:, t, :, None] * kh[:, t, None, :]
+        Hs[:, t + 1] = gh[:, t, None, None] * Hs[:, t] + bh[:, t, None, None] * kk
+        Us[:, t + 1] = gh[:, t, None, None] * Us[:, t] + bh[:, t, None, None] * vk
+    dq = np.zeros((N, T, D))
+    G = np.zeros((N, T, D, D))
+    W = np.zeros((N, T, D, D))
+    eye = np.eye(D)
+    for t in range(T):
+        H, U = Hs[:, t + 1], Us[:, t + 1]
+        n = np.linalg.norm(H, axis=(-2, -1))
+        live = n > 0.0
+        ns = np.where(live, n, 1.0)
+        A = np.where(live[:, None, None], H + (a * ns)[:, None, None] * eye, eye)
+        g = np.einsum("nij,ni->nj", U, dh[:, t])  # U^T do
+        if mode == "cheb":
+            mu, L = np.where(live, a * ns, 1.0), np.where(live, (1.0 + a) * ns, 1.0)
+            x = chebyshev_solve(A, qh[:, t], mu, L, iters)
+            y = chebyshev_solve(A, g, mu, L, iters)
+        elif mode == "exact":
+            x, y = cholesky_solve(A, qh[:, t]), cholesky_solve(A, g)
+        else:
+            raise ValueError(f"unknown mode {mode!r}")
+        x = np.where(live[:, None], x, 0.0)
+        y = np.where(live[:, None], y, 0.0)
+        c = -a * np.einsum("ni,ni->n", y, x) / ns
+        dq[:, t] = y
+        G[:, t] = -y[:, :, None] * x[:, None, :] + c[:, None, None] * H
+        W[:, t] = dh[:, t, :, None] * x[:, None, :]
+    dk = np.zeros((N, T, D))
+    dv = np.zeros((N, T, D))
+    dgam = np.zeros((N, T))
+    dbet = np.zeros((N, T))
+    Gb = np.zeros((N, D, D))
+    Wb = np.zeros((N, D, D))
+    for t in range(T - 1, -1, -1):
+        gn = gh[:, t + 1, None, None] if t + 1 < T else 0.0
+        Gb = G[:, t] + gn * Gb
+        Wb = W[:, t] + gn * Wb
+        kt, vt = kh[:, t], vh[:, t]
+        Gs = Gb + np.swapaxes(Gb, -1, -2)
+        dk[:, t] = bh[:, t, None] * (np.einsum("nij,nj->ni", Gs, kt) + np.einsum("nij,ni->nj", Wb, vt))
+        dv[:, t] = bh[:, t, None] * np.einsum("nij,nj->ni", Wb, kt)
+        dbet[:, t] = np.einsum("ni,nij,nj->n", kt, Gb, kt) + np.einsum("ni,nij,nj->n", vt, Wb, kt)
+        dgam[:, t] = np.einsum("nij,nij->n", Gb, Hs[:, t]) + np.einsum("nij,nij->n", Wb, Us[:, t])
+
+    def unheads(x):
+        return np.moveaxis(x.reshape((B, Hh, T) + x.shape[2:]), 1, 2)
+
+    return dict(dq=unheads(dq), dk=unheads(dk), dv=unheads(dv), dgamma=unheads(dgam),
+                dbeta=unheads(dbet))

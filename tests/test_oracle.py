@@ -9,7 +9,7 @@ import os
 import numpy as np
 import pytest
 
-from oracle import (agd_solve, cg_solve, chebyshev_rates, chebyshev_solve, chebyshev_weights,
+from oracle import (agd_solve, cg_solve, gka_backward_ref, chebyshev_rates, chebyshev_solve, chebyshev_weights,
                     gd_solve, gka_forward_ref, gka_step_ref, ridge_bruteforce, solver_residuals)
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
@@ -567,3 +567,78 @@ def test_step_residuals_match_the_sequence_residuals():
         o, h, u, n2, r = gka_step_ref(q[:, t], k[:, t], v[:, t], g[:, t], 0.05, 7, h, u, n2,
                                       return_residuals=True)
         np.testing.assert_allclose(r, full["residuals"][:, t], rtol=1e-12, atol=1e-15)
+
+
+# ------------------------------------------------------------------------------------------
+# backward by implicit differentiation, pinned by finite differences of the forward
+# ------------------------------------------------------------------------------------------
+
+def _loss(q, k, v, g, do, a, iters, mode, beta):
+    return float(np.sum(gka_forward_ref(q, k, v, g, a, iters, mode=mode, beta=beta)["o"] * do))
+
+
+def _fd(f, x, idx, h=1e-6):
+    xp, xm = x.copy(), x.copy()
+    xp[idx] += h
+    xm[idx] -= h
+    return (f(xp) - f(xm)) / (2 * h)
+
+
+@pytest.mark.parametrize("gated", [False, True])
+def test_backward_matches_finite_differences_of_the_exact_solve(gated):
+    # with the exact solve, implicit differentiation is the exact gradient of the forward:
+    # central differences of L = sum <do, o> agree for every input
+    rng = np.random.default_rng(60)
+    B, T, H, D, a = 1, 5, 2, 4, 0.3
+    q, k, v, g = _rand_inputs(rng, B, T, H, D)
+    do = rng.standard_normal((B, T, H, D))
+    beta = rng.uniform(0.2, 1.0, (B, T, H)) if gated else None
+    grads = gka_backward_ref(q, k, v, g, do, a, 0, mode="exact", beta=beta)
+    L = lambda **kw: _loss(kw.get("q", q), kw.get("k", k), kw.get("v", v), kw.get("g", g), do,
+                           a, 0, "exact", kw.get("beta", beta))
+    for t in range(T):
+        for h in range(H):
+            for i in (0, 3):
+                idx = (0, t, h, i)
+                assert abs(_fd(lambda x: L(q=x), q, idx) - grads["dq"][idx]) < 1e-6
+                assert abs(_fd(lambda x: L(k=x), k, idx) - grads["dk"][idx]) < 1e-6
+                assert abs(_fd(lambda x: L(v=x), v, idx) - grads["dv"][idx]) < 1e-6
+            assert abs(_fd(lambda x: L(g=x), g, (0, t, h)) - grads["dgamma"][0, t, h]) < 1e-6
+            if gated:
+                assert abs(_fd(lambda x: L(beta=x), beta, (0, t, h)) - grads["dbeta"][0, t, h]) < 1e-6
+
+
+def test_query_gradient_of_the_chebyshev_forward_is_the_solve():
+    # Lemma 2: x_t is a fixed polynomial of A_t applied to q_t, so the gradient of the
+    # Chebyshev forward with respect to q_t is that polynomial applied to U_t^T do_t --
+    # the implicit gradient with the same solver -- exactly, not only in the limit
+    rng = np.random.default_rng(61)
+    B, T, H, D, a, r = 1, 6, 2, 5, 0.05, 6
+    q, k, v, g = _rand_inputs(rng, B, T, H, D)
+    do = rng.standard_normal((B, T, H, D))
+    grads = gka_backward_ref(q, k, v, g, do, a, r, mode="cheb")
+    for t in range(T):
+        for i in range(D):
+            idx = (0, t, 1, i)
+            fd = _fd(lambda x: _loss(x, k, v, g, do, a, r, "cheb", None), q, idx)
+            assert abs(fd - grads["dq"][idx]) < 1e-7
+
+
+def test_backward_special_cases():
+    rng = np.random.default_rng(62)
+    B, T, H, D = 1, 6, 2, 4
+    q, k, v, g = _rand_inputs(rng, B, T, H, D)
+    do = rng.standard_normal((B, T, H, D))
+    # zero upstream gradient: all gradients vanish
+    z = gka_backward_ref(q, k, v, g, np.zeros_like(do), 0.1, 5)
+    assert all(np.all(z[n] == 0) for n in z)
+    # beta = 1 gives the ungated gradients, bit for bit in dq, dk, dv, dgamma
+    a1 = gka_backward_ref(q, k, v, g, do, 0.1, 5)
+    b1 = gka_backward_ref(q, k, v, g, do, 0.1, 5, beta=np.ones((B, T, H)))
+    for n in ("dq", "dk", "dv", "dgamma", "dbeta"):
+        np.testing.assert_array_equal(a1[n], b1[n])
+    # a token before any key is written (||H_t|| = 0) has dq_t = 0
+    k2 = k.copy()
+    k2[0, :2, 0] = 0.0
+    c = gka_backward_ref(q, k2, v, g, do, 0.1, 5)
+    assert np.all(c["dq"][0, :2, 0] == 0.0)
