@@ -11,11 +11,12 @@ on a bounded sample of the prefill workload on this host.
 The write-gated prefill (gka_fwd_chunked_beta, same workload plus per-token write gates) is
 timed the same way and reported under "write_gate"; the solver-convergence mode
 (gka_fwd_chunked_residuals) under "solver_convergence", with its residual curve; a serving
-step on a packed batch of prompts and decode rows (gka_fwd_varlen) under "varlen". The oracle leg also compares its outputs of
+step on a packed batch of prompts and decode rows (gka_fwd_varlen) under "varlen"; the backward
+pass (gka_bwd) on the prefill workload under "backward". The oracle leg also compares its outputs of
 the prefix with the timed device run's.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps S] [--no-cpu]
-                       [--no-decode] [--no-beta] [--no-resid] [--no-varlen]
+                       [--no-decode] [--no-beta] [--no-resid] [--no-varlen] [--no-bwd]
 """
 from __future__ import annotations
 
@@ -35,6 +36,7 @@ sys.path.insert(0, ROOT)
 
 PEAK_BF16_MFMA = 2.5e15  # MI355X dense bf16 matrix peak, FLOP/s
 PEAK_HBM = 8.0e12  # MI355X HBM3E, bytes/s
+PEAK_FP32_VALU = 157.3e12  # MI355X fp32 vector peak, FLOP/s
 
 
 def log(msg):
@@ -253,6 +255,49 @@ def bench_varlen(Wv, steps, warmup, ev):
             "longest": int(max(step)), "ms_per_step": ms, "tokens_per_s": n / (ms * 1e-3)}
 
 
+def backward_flops_per_token_head(D, r):
+    """Algorithmic flops of one token-head of the backward (gka_bwd), multiply-add = 2: forward
+    sweep -- H and U updates 6 D^2, ||H||^2 2 D^2, two Chebyshev solves 2 (r - 1) 2 D^2,
+    U^T do 2 D^2; reverse sweep -- the two gradient recurrences 8 D^2, dgamma 4 D^2, dk and dv
+    products 8 D^2."""
+    return (6 + 2 + 4 * (r - 1) + 2 + 8 + 4 + 8) * D * D
+
+
+def bench_backward(W, inputs, steps, warmup, ev):
+    """gka_bwd on the prefill workload with an upstream gradient do ~ N(0, 1) (bf16)."""
+    import torch
+    from test_ridge_regression_amd import gka
+
+    qd, kd, vd, gd = inputs
+    do = torch.randn(qd.shape, device="cuda", generator=torch.Generator("cuda").manual_seed(7)
+                     ).to(torch.bfloat16)
+    need = gka.lib_bwd_workspace(W)
+    ws = torch.empty(need, device="cuda", dtype=torch.uint8)
+    call = lambda: gka.bwd(qd, kd, vd, gd, do, W.a, W.iters, workspace=ws)
+    log(f"backward warmup {warmup} (workspace {need / 2**30:.1f} GiB)")
+    for _ in range(warmup):
+        call()
+    torch.cuda.synchronize()
+    stream = torch.cuda.current_stream()
+    t0, t1 = ev.create(2)
+    log(f"backward timed {steps}")
+    ev.record(t0, stream.cuda_stream)
+    for _ in range(steps):
+        call()
+    ev.record(t1, stream.cuda_stream)
+    ev.sync(t1)
+    ms = ev.elapsed_ms(t0, t1) / steps
+    ev.destroy([t0, t1])
+    F = backward_flops_per_token_head(W.D, W.iters) * W.B * W.T * W.H
+    return {"entry_point": "gka_bwd", "workload": W.name, "ms_per_step": ms,
+            "tokens_per_s": W.B * W.T / (ms * 1e-3),
+            "roofline": {"bound": "alu", "kernel": "bwd_forward_kernel + bwd_reverse_kernel",
+                         "achieved": F / (ms * 1e-3) / 1e12, "peak": PEAK_FP32_VALU / 1e12,
+                         "unit": "TFLOP/s", "frac": F / (ms * 1e-3) / PEAK_FP32_VALU,
+                         "traffic": None, "flops_per_launch": F, "avg_launch_ms": ms},
+            "workspace_bytes": need}
+
+
 def _segments(W):
     from test_ridge_regression_amd import gka
     # the plan's segment count: workspace = B*H*S*(2 D^2 + 1)*4 + B*H*4 (rounded up to 256)
@@ -369,6 +414,7 @@ def main():
     ap.add_argument("--no-beta", action="store_true", help="skip the write-gated prefill")
     ap.add_argument("--no-resid", action="store_true", help="skip the solver-convergence mode")
     ap.add_argument("--no-varlen", action="store_true", help="skip the packed serving step")
+    ap.add_argument("--no-bwd", action="store_true", help="skip the backward pass")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 512 MiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -441,6 +487,10 @@ def main():
         }
         log(f"beta prefill: {pb['ms_per_step']:.3f} ms/step (walk {pb['walk_ms']:.3f})")
         del pb, bd
+    if not args.no_bwd:
+        rec["backward"] = bench_backward(W, inputs, max(1, args.steps // 10), 1, ev)
+        log(f"backward: {rec['backward']['ms_per_step']:.2f} ms/step")
+        torch.cuda.empty_cache()
     if not args.no_resid:
         rec["solver_convergence"] = bench_residuals(W, inputs, max(1, args.steps // 2),
                                                     args.warmup, ev)

@@ -209,6 +209,34 @@ gka_status gka_fwd_varlen(const gka_params* p, const int32_t* cu_seqlens, int64_
                           float* hnorm2, float* hnorm_t, void* workspace, size_t workspace_bytes,
                           void* stream);
 
+/*
+ * Backward pass: the gradients of L = sum_t <do_t, o_t> for the forward of gka_fwd_chunked_beta
+ * from the zero initial state, by implicit differentiation of the solve (ai.info summary,
+ * "Methodology in Plain English" and "Main Findings": the backward re-runs the solver on the
+ * upstream gradient; Lemma 2: the query gradient is that solve). With x_t the Chebyshev iterate
+ * of the forward, y_t = A_t^-1 U_t^T do_t (the same Chebyshev iteration) and
+ * c_t = -a (y_t . x_t) / ||H_t||_F:
+ *   dq_t = y_t; the statistics' local gradients G_t = -y_t x_t^T + c_t H_t, W_t = do_t x_t^T
+ *   run back through the gated recurrences (Gb_t = G_t + gamma_{t+1} Gb_{t+1}, Wb likewise);
+ *   dk_t = beta_t ((Gb_t + Gb_t^T) k_t + Wb_t^T v_t), dv_t = beta_t Wb_t k_t,
+ *   dgamma_t = <Gb_t, H_{t-1}> + <Wb_t, U_{t-1}>, dbeta_t = k_t^T Gb_t k_t + v_t^T Wb_t k_t.
+ * A token with ||H_t||_F = 0 has x_t = 0 by definition and contributes nothing (dq_t = 0).
+ *   q, k, v, dout  [B, T, H, D] dtype, read; gamma, optional beta (NULL = 1) [B, T, H] float32
+ *   dq, dk, dv     [B, T, H, D] dtype, written; dgamma [B, T, H] float32, written; dbeta
+ *                  optional [B, T, H] float32 (the gradient at the given beta, or at beta = 1)
+ *   workspace      at least gka_bwd_workspace_bytes(p) = 4 B T H (2 D^2 + 2 D + 1) bytes
+ *                  (rounded up to 256): the forward sweep keeps every H_t and U_t there
+ * One workgroup per head walks the sequence (reference-grade: parallel over heads only).
+ * Errors as for gka_fwd_chunked; outputs must not overlap the inputs or each other
+ * (GKA_ERR_ALIAS). T = 0 is a no-op.
+ */
+size_t gka_bwd_workspace_bytes(const gka_params* p);
+
+gka_status gka_bwd(const gka_params* p, const void* q, const void* k, const void* v,
+                   const float* gamma, const float* beta, const void* dout, void* dq, void* dk,
+                   void* dv, float* dgamma, float* dbeta, void* workspace,
+                   size_t workspace_bytes, void* stream);
+
 /* Static description of a status code. */
 const char* gka_status_str(int status);
 

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgka.so")
-SOURCES = ["gka_api.cpp", "gka_step.hip", "gka_fwd.hip", "gka_walk_tok.hip"]
+SOURCES = ["gka_api.cpp", "gka_step.hip", "gka_fwd.hip", "gka_walk_tok.hip", "gka_bwd.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [

@@ -12,7 +12,7 @@ namespace {
 using gka::ChebConsts;
 using gka::FwdPlan;
 
-constexpr int kAbiVersion = 5;
+constexpr int kAbiVersion = 6;
 constexpr int kCUs = 256;  // MI355X compute units: the segment plan aims at one workgroup per CU
 
 bool dims_supported(int dtype, int D) {
@@ -396,6 +396,64 @@ gka_status gka_step_beta(const gka_params* p, const void* q, const void* k, cons
                          const float* gamma, const float* beta, void* o, float* h_state,
                          float* u_state, float* hnorm2, void* stream) {
   return step_impl(p, q, k, v, gamma, beta, o, h_state, u_state, hnorm2, nullptr, stream);
+}
+
+size_t gka_bwd_workspace_bytes(const gka_params* p) {
+  if (check_common(p) != GKA_OK || p->T < 0) return 0;
+  const size_t n = (size_t)p->B * p->H * p->T;
+  const size_t D = (size_t)p->D;
+  return ((n * (2 * D * D + 2 * D + 1)) * sizeof(float) + 255) & ~(size_t)255;
+}
+
+gka_status gka_bwd(const gka_params* p, const void* q, const void* k, const void* v,
+                   const float* gamma, const float* beta, const void* dout, void* dq, void* dk,
+                   void* dv, float* dgamma, float* dbeta, void* workspace,
+                   size_t workspace_bytes, void* stream) {
+  gka_status st = check_common(p);
+  if (st != GKA_OK) return st;
+  if (p->T < 0) return GKA_ERR_SHAPE;
+  if ((long long)p->B * p->T * p->H * p->D > (1LL << 40)) return GKA_ERR_SHAPE;
+  if (p->T == 0) return GKA_OK;
+  if (!q || !k || !v || !gamma || !dout || !dq || !dk || !dv || !dgamma) return GKA_ERR_NULL;
+  const size_t rows = (size_t)p->B * p->T * p->H;
+  const size_t n_io = rows * p->D * elem_bytes(p->dtype);
+  const void* ins[] = {q, k, v, dout};
+  void* outs[] = {dq, dk, dv};
+  for (void* o : outs) {
+    for (const void* i : ins)
+      if (overlap(o, n_io, i, n_io)) return GKA_ERR_ALIAS;
+    if (overlap(o, n_io, gamma, rows * 4) || (beta && overlap(o, n_io, beta, rows * 4)))
+      return GKA_ERR_ALIAS;
+  }
+  if (overlap(dq, n_io, dk, n_io) || overlap(dq, n_io, dv, n_io) || overlap(dk, n_io, dv, n_io))
+    return GKA_ERR_ALIAS;
+  if ((reinterpret_cast<uintptr_t>(dgamma) & 3u) || (dbeta && (reinterpret_cast<uintptr_t>(dbeta) & 3u)) ||
+      (beta && (reinterpret_cast<uintptr_t>(beta) & 3u)))
+    return GKA_ERR_SHAPE;
+  const size_t need = gka_bwd_workspace_bytes(p);
+  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return GKA_ERR_WORKSPACE;
+  const ChebConsts cc = cheb_consts(p->a, p->iters);
+  const size_t n = rows, D = (size_t)p->D;
+  gka::BwdArgs ba{};
+  ba.q = q;
+  ba.k = k;
+  ba.v = v;
+  ba.gamma = gamma;
+  ba.beta = beta;
+  ba.dout = dout;
+  ba.dq = dq;
+  ba.dk = dk;
+  ba.dv = dv;
+  ba.dgamma = dgamma;
+  ba.dbeta = dbeta;
+  ba.snap = static_cast<float*>(workspace);
+  ba.xs = ba.snap + n * 2 * D * D;
+  ba.ys = ba.xs + n * D;
+  ba.cs = ba.ys + n * D;
+  if (gka::launch_bwd(p->dtype, p->D, p->B * p->H, p->T, p->H, ba, cc,
+                      static_cast<hipStream_t>(stream)) != hipSuccess)
+    return GKA_ERR_HIP;
+  return GKA_OK;
 }
 
 gka_status gka_step_residuals(const gka_params* p, const void* q, const void* k, const void* v,

@@ -1,0 +1,280 @@
+// gka_bwd: backward pass of the Gated KalmaNet layer by implicit differentiation.
+//
+// For L = sum_t <do_t, o_t> (ai.info summary, "Methodology in Plain English" and "Main Findings":
+// the backward re-runs the solver on the upstream gradient; Lemma 2 for the query):
+//   x_t = A_t^-1 q_t, g_t = U_t^T do_t, y_t = A_t^-1 g_t (Chebyshev on the normalised system, as
+//   the forward), dq_t = y_t, c_t = -a (y_t . x_t) / ||H_t||_F,
+//   G_t = -y_t x_t^T + c_t H_t,  W_t = do_t x_t^T,
+//   Gb_t = G_t + gamma_{t+1} Gb_{t+1},  Wb_t = W_t + gamma_{t+1} Wb_{t+1},
+//   dk_t = beta_t ((Gb_t + Gb_t^T) k_t + Wb_t^T v_t),  dv_t = beta_t Wb_t k_t,
+//   dbeta_t = k_t^T Gb_t k_t + v_t^T Wb_t k_t,  dgamma_t = <Gb_t, H_{t-1}> + <Wb_t, U_{t-1}>.
+//
+// Reference-grade design: one workgroup per head walks the whole sequence, the D x D matrices
+// held in registers with the decode step's layout (4D threads; thread tid owns the float4 column
+// group c4 = tid % (D/4) and rows r0 + j RS). The forward sweep writes every H_t and U_t to the
+// workspace (the reverse sweep needs them in reverse order, and the recurrence cannot be run
+// backwards stably: it divides by gamma); the reverse sweep reads them back. Parallel over heads
+// only, and bound by the sequential per-token solves: correct, not fast.
+#include "gka_internal.hpp"
+
+namespace gka {
+
+namespace {
+
+template <int D, int NT>
+struct BwdLayout {
+  static constexpr int C4 = D / 4;    // float4 groups per row
+  static constexpr int RS = NT / C4;  // rows covered by one pass of the workgroup
+  static constexpr int F = D / RS;    // rows per thread
+  static constexpr int NW = NT / kWave;
+  static_assert(NT % C4 == 0 && D % RS == 0 && kWave % C4 == 0, "bad tiling");
+};
+
+// Reductions of the decode-step layout. Every thread of the workgroup calls them (they hold
+// barriers); LDS scratch: part [NW][D], red [NW].
+template <int D, int NT>
+struct BwdReduce {
+  using L = BwdLayout<D, NT>;
+  float (*part)[D];
+  float* red;
+  int tid, lane, wave, c4, r0;
+  // sum over the workgroup of x
+  __device__ float sum(float x) {
+    x = wave_sum(x);
+    __syncthreads();  // earlier readers of red are done
+    if (lane == 0) red[wave] = x;
+    __syncthreads();
+    float s = 0.0f;
+#pragma unroll
+    for (int w = 0; w < L::NW; ++w) s += red[w];
+    return s;
+  }
+  // column sums: thread c < D receives sum_r M[r][c] w[r] (w in LDS, D floats)
+  __device__ float colsum(const f32x4 (&M)[L::F], const float* w) {
+    f32x4 y = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < L::F; ++j) y += M[j] * w[r0 + j * L::RS];
+#pragma unroll
+    for (int m = L::C4; m < kWave; m <<= 1) {
+      y[0] += __shfl_xor(y[0], m, kWave);
+      y[1] += __shfl_xor(y[1], m, kWave);
+      y[2] += __shfl_xor(y[2], m, kWave);
+      y[3] += __shfl_xor(y[3], m, kWave);
+    }
+    __syncthreads();  // earlier readers of part are done
+    if (lane < L::C4) *reinterpret_cast<f32x4*>(&part[wave][4 * c4]) = y;
+    __syncthreads();
+    float s = 0.0f;
+    if (tid < D) {
+#pragma unroll
+      for (int w = 0; w < L::NW; ++w) s += part[w][tid];
+    }
+    return s;
+  }
+  // row sums: out[r] = sum_c M[r][c] w[c] for every row r (w in LDS), written to LDS out
+  __device__ void rowsum(const f32x4 (&M)[L::F], const float* w, float* out) {
+    const f32x4 wc = *reinterpret_cast<const f32x4*>(w + 4 * c4);
+#pragma unroll
+    for (int j = 0; j < L::F; ++j) {
+      float p = M[j][0] * wc[0] + M[j][1] * wc[1] + M[j][2] * wc[2] + M[j][3] * wc[3];
+#pragma unroll
+      for (int m = 1; m < L::C4; m <<= 1) p += __shfl_xor(p, m, kWave);
+      if (c4 == 0) out[r0 + j * L::RS] = p;
+    }
+    __syncthreads();
+  }
+};
+
+template <typename T, int D, int NT>
+__global__ __launch_bounds__(NT) void bwd_forward_kernel(BwdArgs A, int Tlen, int Hn,
+                                                         ChebConsts cc) {
+  using L = BwdLayout<D, NT>;
+  constexpr int F = L::F, RS = L::RS, NW = L::NW;
+  __shared__ float ks[D], vs[D], qv[D], dv_[D], ws[D];
+  __shared__ float part[NW][D];
+  __shared__ float red[NW];
+  const int bh = blockIdx.x;
+  const int b = bh / Hn, h = bh % Hn;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int c4 = tid % L::C4, r0 = tid / L::C4;
+  BwdReduce<D, NT> R{part, red, tid, lane, wave, c4, r0};
+  const T* q = static_cast<const T*>(A.q);
+  const T* k = static_cast<const T*>(A.k);
+  const T* v = static_cast<const T*>(A.v);
+  const T* dout = static_cast<const T*>(A.dout);
+  T* dq = static_cast<T*>(A.dq);
+
+  f32x4 Hr[F], Ur[F];
+#pragma unroll
+  for (int j = 0; j < F; ++j) {
+    Hr[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    Ur[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int t = 0; t < Tlen; ++t) {
+    const long long tok = (b * (long long)Tlen + t) * Hn + h;
+    if (tid < D) {
+      ks[tid] = to_f32(k[tok * D + tid]);
+      vs[tid] = to_f32(v[tok * D + tid]);
+      qv[tid] = to_f32(q[tok * D + tid]);
+      dv_[tid] = to_f32(dout[tok * D + tid]);
+    }
+    const float g = A.gamma[tok];
+    const float bt = A.beta ? A.beta[tok] : 1.0f;
+    __syncthreads();
+    // H_t, U_t, and their snapshot (the reverse sweep reads them back)
+    const f32x4 kc = *reinterpret_cast<const f32x4*>(ks + 4 * c4);
+    float* snap = A.snap + ((size_t)bh * Tlen + t) * 2 * D * D;
+    float sq = 0.0f;
+#pragma unroll
+    for (int j = 0; j < F; ++j) {
+      const int r = r0 + j * RS;
+      Hr[j] = g * Hr[j] + (bt * ks[r]) * kc;
+      Ur[j] = g * Ur[j] + (bt * vs[r]) * kc;
+      *reinterpret_cast<f32x4*>(snap + (size_t)r * D + 4 * c4) = Hr[j];
+      *reinterpret_cast<f32x4*>(snap + (size_t)D * D + (size_t)r * D + 4 * c4) = Ur[j];
+      sq += Hr[j][0] * Hr[j][0] + Hr[j][1] * Hr[j][1] + Hr[j][2] * Hr[j][2] + Hr[j][3] * Hr[j][3];
+    }
+    const float n2 = R.sum(sq);
+    const bool live = n2 > 0.0f;
+    const float n = sqrtf(n2), inv_n = live ? 1.0f / n : 0.0f;
+    // Chebyshev on (H / ||H|| + a I) xh = rhs (thread c < D holds element c); x = xh / ||H||
+    auto solve = [&](float rhs) {
+      float x = cc.c * rhs, xp = 0.0f;
+      for (int i = 1; i < cc.iters; ++i) {
+        if (tid < D) ws[tid] = x;
+        __syncthreads();
+        const float ax = R.colsum(Hr, ws) * inv_n + cc.a * x;
+        if (tid < D) {
+          const float xn = xp + cc.omega[i] * (x - xp + cc.c * (rhs - ax));
+          xp = x;
+          x = xn;
+        }
+      }
+      return x * inv_n;
+    };
+    const float x = solve(tid < D ? qv[tid] : 0.0f);
+    const float gu = R.colsum(Ur, dv_);  // (U^T do)[c]
+    const float y = solve(tid < D ? gu : 0.0f);
+    const float yx = R.sum(tid < D ? y * x : 0.0f);
+    const float c = live ? -cc.a * yx * inv_n : 0.0f;
+    if (tid < D) {
+      const size_t o = ((size_t)bh * Tlen + t) * D + tid;
+      A.xs[o] = live ? x : 0.0f;
+      A.ys[o] = live ? y : 0.0f;
+      dq[tok * D + tid] = from_f32<T>(live ? y : 0.0f);
+    }
+    if (tid == 0) A.cs[(size_t)bh * Tlen + t] = c;
+    __syncthreads();  // the token vectors are read
+  }
+}
+
+template <typename T, int D, int NT>
+__global__ __launch_bounds__(NT) void bwd_reverse_kernel(BwdArgs A, int Tlen, int Hn) {
+  using L = BwdLayout<D, NT>;
+  constexpr int F = L::F, RS = L::RS, NW = L::NW;
+  __shared__ float ks[D], vs[D], xv[D], yv[D], dv_[D], rgk[D], rwk[D];
+  __shared__ float part[NW][D];
+  __shared__ float red[NW];
+  const int bh = blockIdx.x;
+  const int b = bh / Hn, h = bh % Hn;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int c4 = tid % L::C4, r0 = tid / L::C4;
+  BwdReduce<D, NT> R{part, red, tid, lane, wave, c4, r0};
+  const T* k = static_cast<const T*>(A.k);
+  const T* v = static_cast<const T*>(A.v);
+  const T* dout = static_cast<const T*>(A.dout);
+  T* dk = static_cast<T*>(A.dk);
+  T* dvo = static_cast<T*>(A.dv);
+
+  f32x4 Gb[F], Wb[F];
+#pragma unroll
+  for (int j = 0; j < F; ++j) {
+    Gb[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    Wb[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int t = Tlen - 1; t >= 0; --t) {
+    const long long tok = (b * (long long)Tlen + t) * Hn + h;
+    const size_t row = ((size_t)bh * Tlen + t) * D;
+    if (tid < D) {
+      ks[tid] = to_f32(k[tok * D + tid]);
+      vs[tid] = to_f32(v[tok * D + tid]);
+      dv_[tid] = to_f32(dout[tok * D + tid]);
+      xv[tid] = A.xs[row + tid];
+      yv[tid] = A.ys[row + tid];
+    }
+    const float c = A.cs[(size_t)bh * Tlen + t];
+    const float gn = t + 1 < Tlen ? A.gamma[tok + Hn] : 0.0f;  // gamma_{t+1}
+    const float bt = A.beta ? A.beta[tok] : 1.0f;
+    __syncthreads();
+    // Gb_t = -y x^T + c H_t + gamma_{t+1} Gb_{t+1},  Wb_t = do x^T + gamma_{t+1} Wb_{t+1}
+    const f32x4 xc = *reinterpret_cast<const f32x4*>(xv + 4 * c4);
+    const float* snap = A.snap + ((size_t)bh * Tlen + t) * 2 * D * D;
+    const float* prev = t > 0 ? snap - 2 * D * D : nullptr;  // H_{t-1}, U_{t-1} (zero at t = 0)
+    float dg = 0.0f;
+#pragma unroll
+    for (int j = 0; j < F; ++j) {
+      const int r = r0 + j * RS;
+      const f32x4 Ht = *reinterpret_cast<const f32x4*>(snap + (size_t)r * D + 4 * c4);
+      Gb[j] = c * Ht - yv[r] * xc + gn * Gb[j];
+      Wb[j] = dv_[r] * xc + gn * Wb[j];
+      if (prev) {
+        const f32x4 Hp = *reinterpret_cast<const f32x4*>(prev + (size_t)r * D + 4 * c4);
+        const f32x4 Up = *reinterpret_cast<const f32x4*>(prev + (size_t)D * D + (size_t)r * D + 4 * c4);
+        dg += Gb[j][0] * Hp[0] + Gb[j][1] * Hp[1] + Gb[j][2] * Hp[2] + Gb[j][3] * Hp[3];
+        dg += Wb[j][0] * Up[0] + Wb[j][1] * Up[1] + Wb[j][2] * Up[2] + Wb[j][3] * Up[3];
+      }
+    }
+    dg = R.sum(dg);
+    R.rowsum(Gb, ks, rgk);  // (Gb k)[r]
+    R.rowsum(Wb, ks, rwk);  // (Wb k)[r]
+    const float gtk = R.colsum(Gb, ks);  // (Gb^T k)[c]
+    const float wtv = R.colsum(Wb, vs);  // (Wb^T v)[c]
+    float db = 0.0f;
+    if (tid < D) {
+      dk[tok * D + tid] = from_f32<T>(bt * (rgk[tid] + gtk + wtv));
+      dvo[tok * D + tid] = from_f32<T>(bt * rwk[tid]);
+      db = ks[tid] * rgk[tid] + vs[tid] * rwk[tid];
+    }
+    db = R.sum(db);
+    if (tid == 0) {
+      A.dgamma[tok] = dg;
+      if (A.dbeta) A.dbeta[tok] = db;
+    }
+    __syncthreads();  // the token vectors are read
+  }
+}
+
+template <typename T, int D, int NT>
+hipError_t launch_bwd_t(int BH, int Tlen, int Hn, const BwdArgs& a, const ChebConsts& cc,
+                        hipStream_t stream) {
+  hipLaunchKernelGGL((bwd_forward_kernel<T, D, NT>), dim3(BH), dim3(NT), 0, stream, a, Tlen, Hn,
+                     cc);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL((bwd_reverse_kernel<T, D, NT>), dim3(BH), dim3(NT), 0, stream, a, Tlen, Hn);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_bwd(int dtype, int D, int BH, int Tlen, int Hn, const BwdArgs& a,
+                      const ChebConsts& cc, hipStream_t stream) {
+  if (dtype == 0) {
+    switch (D) {
+      case 16: return launch_bwd_t<bf16, 16, 64>(BH, Tlen, Hn, a, cc, stream);
+      case 32: return launch_bwd_t<bf16, 32, 128>(BH, Tlen, Hn, a, cc, stream);
+      case 64: return launch_bwd_t<bf16, 64, 256>(BH, Tlen, Hn, a, cc, stream);
+      case 128: return launch_bwd_t<bf16, 128, 512>(BH, Tlen, Hn, a, cc, stream);
+    }
+  } else {
+    switch (D) {
+      case 16: return launch_bwd_t<float, 16, 64>(BH, Tlen, Hn, a, cc, stream);
+      case 32: return launch_bwd_t<float, 32, 128>(BH, Tlen, Hn, a, cc, stream);
+      case 64: return launch_bwd_t<float, 64, 256>(BH, Tlen, Hn, a, cc, stream);
+      case 128: return launch_bwd_t<float, 128, 512>(BH, Tlen, Hn, a, cc, stream);
+    }
+  }
+  return hipErrorInvalidValue;
+}
+
+}  // namespace gka

@@ -123,4 +123,27 @@ hipError_t launch_scan(const FwdPlan& pl, float* ws_states, const float* ws_log2
                        float* u, const float* hnorm2, float* n2_seg0, const int* cu,
                        hipStream_t stream);
 
+// Backward pass (gka_bwd): arguments of its two kernels. Workspace: snap [BH][T][2][D][D] (H_t, U_t
+// after every token), xs, ys [BH][T][D] (the solves of the forward sweep), cs [BH][T].
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const float* gamma;
+  const float* beta;  // optional write gate (NULL: 1)
+  const void* dout;
+  void* dq;
+  void* dk;
+  void* dv;
+  float* dgamma;
+  float* dbeta;  // optional
+  float* snap;
+  float* xs;
+  float* ys;
+  float* cs;
+};
+
+hipError_t launch_bwd(int dtype, int D, int BH, int Tlen, int Hn, const BwdArgs& a,
+                      const ChebConsts& cc, hipStream_t stream);
+
 }  // namespace gka

@@ -27,8 +27,8 @@ STATUS = {0: "GKA_OK", 1: "GKA_ERR_NULL", 2: "GKA_ERR_SHAPE", 3: "GKA_ERR_VALUE"
           4: "GKA_ERR_DTYPE", 5: "GKA_ERR_WORKSPACE", 6: "GKA_ERR_HIP", 7: "GKA_ERR_ALIAS"}
 EXPORTED = ["gka_fwd_workspace_bytes", "gka_fwd_chunked", "gka_step", "gka_fwd_chunked_beta",
             "gka_step_beta", "gka_fwd_chunked_residuals", "gka_step_residuals",
-            "gka_fwd_varlen", "gka_fwd_varlen_workspace_bytes", "gka_status_str",
-            "gka_abi_version"]
+            "gka_fwd_varlen", "gka_fwd_varlen_workspace_bytes", "gka_bwd",
+            "gka_bwd_workspace_bytes", "gka_status_str", "gka_abi_version"]
 
 
 class GkaParams(ctypes.Structure):
@@ -80,6 +80,11 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gka_fwd_varlen.restype = ctypes.c_int
     lib.gka_fwd_varlen_workspace_bytes.argtypes = [P]
     lib.gka_fwd_varlen_workspace_bytes.restype = ctypes.c_size_t
+    lib.gka_bwd_workspace_bytes.argtypes = [P]
+    lib.gka_bwd_workspace_bytes.restype = ctypes.c_size_t
+    lib.gka_bwd.argtypes = [P, vp, vp, vp, fp, fp, vp, vp, vp, vp, fp, fp, vp, ctypes.c_size_t,
+                            vp]
+    lib.gka_bwd.restype = ctypes.c_int
     lib.gka_status_str.argtypes = [ctypes.c_int]
     lib.gka_status_str.restype = ctypes.c_char_p
     lib.gka_abi_version.argtypes = []
@@ -317,3 +322,35 @@ def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.T
         _stream(stream))
     _check(st)
     return (o, hn) if return_hnorm else o
+
+
+def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor,
+        dout: torch.Tensor, a: float, iters: int, beta: Optional[torch.Tensor] = None,
+        workspace: Optional[torch.Tensor] = None, stream=None):
+    """gka_bwd: gradients of sum <dout, o> for the forward from the zero state.
+    Returns (dq, dk, dv, dgamma, dbeta) -- dq, dk, dv in the dtype of q, the rest float32."""
+    lib = load()
+    B, T, H, D = q.shape
+    p = make_params(B, T, H, D, 64, iters, a, _dtype_code(q))
+    dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
+    _require_io(q, k, v, gamma, dq, None)
+    if dout.shape != q.shape or dout.dtype != q.dtype or not dout.is_contiguous():
+        raise ValueError("dout must match q")
+    _require_beta(beta, (B, T, H))
+    dgamma = torch.empty(B, T, H, device=q.device, dtype=torch.float32)
+    dbeta = torch.empty(B, T, H, device=q.device, dtype=torch.float32)
+    need = int(lib.gka_bwd_workspace_bytes(ctypes.byref(p)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
+    st = lib.gka_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(beta),
+                     _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dgamma), _ptr(dbeta),
+                     _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(stream))
+    _check(st)
+    return dq, dk, dv, dgamma, dbeta
+
+
+def lib_bwd_workspace(w) -> int:
+    """gka_bwd_workspace_bytes for a workload description (B, T, H, D, iters, a, dtype)."""
+    p = make_params(w.B, w.T, w.H, w.D, 64, w.iters, w.a,
+                    GKA_BF16 if w.dtype == "bf16" else GKA_FP32)
+    return int(load().gka_bwd_workspace_bytes(ctypes.byref(p)))

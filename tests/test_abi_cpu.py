@@ -33,7 +33,7 @@ def test_header_declares_the_bound_functions():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.gka_abi_version() == 5
+    assert lib.gka_abi_version() == 6
 
 
 def test_status_strings(lib):
@@ -259,3 +259,24 @@ def test_all_head_sizes_are_accepted(lib):
     for C in (32, 64):  # float32 D = 128 only with chunks of 16
         assert lib.gka_fwd_workspace_bytes(P(params(dtype_code=gka.GKA_FP32, D=128, chunk=C,
                                                     T=4096))) == 0
+
+
+def test_backward_entry_point_checks(lib):
+    P = ctypes.byref
+    p = params(B=1, H=1, T=64, D=32)
+    need = lib.gka_bwd_workspace_bytes(P(p))
+    assert need == ((64 * (2 * 32 * 32 + 2 * 32 + 1)) * 4 + 255) // 256 * 256
+    w = ctypes.c_void_p(ADDR[11] + (1 << 31))
+    bw = lambda p, q=VP[0], dq=VP[5], dk=VP[6], dg=VP[8], ws=w, wsb=need: lib.gka_bwd(
+        P(p) if p is not None else None, q, VP[1], VP[2], VP[3], None, VP[4], dq, dk, VP[7], dg,
+        None, ws, ctypes.c_size_t(wsb), None)
+    assert bw(None) == 1
+    assert bw(params(D=48)) == 2
+    assert bw(params(iters=0)) == 3
+    assert bw(p, q=None) == 1
+    assert bw(p, dg=None) == 1
+    assert bw(p, dq=VP[0]) == 7  # dq == q
+    assert bw(p, dk=VP[5]) == 7  # dk == dq
+    assert bw(p, ws=None) == 5
+    assert bw(p, wsb=need - 1) == 5
+    assert bw(params(T=0), q=None, dq=None) == 0
