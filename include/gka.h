@@ -224,9 +224,12 @@ gka_status gka_fwd_varlen(const gka_params* p, const int32_t* cu_seqlens, int64_
  *   q, k, v, dout  [B, T, H, D] dtype, read; gamma, optional beta (NULL = 1) [B, T, H] float32
  *   dq, dk, dv     [B, T, H, D] dtype, written; dgamma [B, T, H] float32, written; dbeta
  *                  optional [B, T, H] float32 (the gradient at the given beta, or at beta = 1)
- *   workspace      at least gka_bwd_workspace_bytes(p) = 4 B T H (2 D^2 + 2 D + 1) bytes
- *                  (rounded up to 256): the forward sweep keeps every H_t and U_t there
- * One workgroup per head walks the sequence (reference-grade: parallel over heads only).
+ *   workspace      at least gka_bwd_workspace_bytes(p) bytes, about 4 B T H (2 D^2 + 2 D + 1)
+ *                  plus two chunk states per chunk and head: the forward sweep keeps every H_t
+ *                  and U_t there
+ * Chunks of 64 tokens (16 for float32 with D = 128) are swept in parallel, token by token, with
+ * the forward's segment scan giving their starting states and a reverse scan their incoming
+ * gradients.
  * Errors as for gka_fwd_chunked; outputs must not overlap the inputs or each other
  * (GKA_ERR_ALIAS). T = 0 is a no-op.
  */

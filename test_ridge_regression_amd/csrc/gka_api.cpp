@@ -178,6 +178,34 @@ gka_status check_fwd(const gka_params* p) {
   return GKA_OK;
 }
 
+// Backward: chunks of 64 tokens (16 for float32 with D = 128, as the forward), one chunk per
+// segment; workspace regions in floats, each rounded up to 64 floats (256 bytes).
+int bwd_chunk(const gka_params* p) { return p->dtype == GKA_FP32 && p->D == 128 ? 16 : 64; }
+
+struct BwdLayoutHost {
+  size_t snap, xs, ys, cs, fstates, flog2, fn2, rstates, rlog2, rn2, total;  // float offsets; bytes
+};
+
+BwdLayoutHost bwd_layout(const gka_params* p) {
+  auto up = [](size_t x) { return (x + 63) & ~(size_t)63; };
+  const size_t n = (size_t)p->B * p->H * p->T, D = (size_t)p->D, bh = (size_t)p->B * p->H;
+  const size_t N = (size_t)((p->T + bwd_chunk(p) - 1) / bwd_chunk(p));
+  BwdLayoutHost l{};
+  size_t o = 0;
+  l.snap = o; o += up(n * 2 * D * D);
+  l.xs = o; o += up(n * D);
+  l.ys = o; o += up(n * D);
+  l.cs = o; o += up(n);
+  l.fstates = o; o += up(bh * N * 2 * D * D);
+  l.flog2 = o; o += up(bh * N);
+  l.fn2 = o; o += up(bh);
+  l.rstates = o; o += up(bh * N * 2 * D * D);
+  l.rlog2 = o; o += up(bh * N);
+  l.rn2 = o; o += up(bh);
+  l.total = o * sizeof(float);
+  return l;
+}
+
 gka_status fwd_impl(const gka_params* p, const int32_t* cu, int64_t total, const void* q,
                     const void* k, const void* v, const float* gamma, const float* beta, void* o,
                     float* h_state, float* u_state, float* hnorm2, float* hnorm_t, float* resid,
@@ -400,9 +428,7 @@ gka_status gka_step_beta(const gka_params* p, const void* q, const void* k, cons
 
 size_t gka_bwd_workspace_bytes(const gka_params* p) {
   if (check_common(p) != GKA_OK || p->T < 0) return 0;
-  const size_t n = (size_t)p->B * p->H * p->T;
-  const size_t D = (size_t)p->D;
-  return ((n * (2 * D * D + 2 * D + 1)) * sizeof(float) + 255) & ~(size_t)255;
+  return bwd_layout(p).total;
 }
 
 gka_status gka_bwd(const gka_params* p, const void* q, const void* k, const void* v,
@@ -430,10 +456,41 @@ gka_status gka_bwd(const gka_params* p, const void* q, const void* k, const void
   if ((reinterpret_cast<uintptr_t>(dgamma) & 3u) || (dbeta && (reinterpret_cast<uintptr_t>(dbeta) & 3u)) ||
       (beta && (reinterpret_cast<uintptr_t>(beta) & 3u)))
     return GKA_ERR_SHAPE;
-  const size_t need = gka_bwd_workspace_bytes(p);
-  if (!workspace || workspace_bytes < need || !aligned16(workspace)) return GKA_ERR_WORKSPACE;
+  const BwdLayoutHost lay = bwd_layout(p);
+  if (!workspace || workspace_bytes < lay.total || !aligned16(workspace)) return GKA_ERR_WORKSPACE;
   const ChebConsts cc = cheb_consts(p->a, p->iters);
-  const size_t n = rows, D = (size_t)p->D;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  float* ws = static_cast<float*>(workspace);
+  // the plan of one chunk per segment
+  FwdPlan pl{};
+  pl.B = p->B;
+  pl.T = p->T;
+  pl.H = p->H;
+  pl.D = p->D;
+  pl.C = bwd_chunk(p);
+  pl.dtype = p->dtype;
+  pl.N = (p->T + pl.C - 1) / pl.C;
+  pl.S = pl.N;
+  pl.J = 1;
+  const long long DD = (long long)p->D * p->D;
+  // every chunk's starting state from the zero state: the forward's summaries and scan
+  if (pl.S > 1) {
+    gka::WalkArgs sa{};
+    sa.q = q;
+    sa.k = k;
+    sa.v = v;
+    sa.gamma = gamma;
+    sa.beta = beta;
+    sa.sum_h = ws + lay.fstates;
+    sa.sum_u = ws + lay.fstates + DD;
+    sa.sum_bh = (long long)pl.S * 2 * DD;
+    sa.sum_seg = 2 * DD;
+    sa.log2g_out = ws + lay.flog2;
+    if (gka::launch_walk(pl, true, sa, cc, s) != hipSuccess) return GKA_ERR_HIP;
+  }
+  if (gka::launch_scan(pl, ws + lay.fstates, ws + lay.flog2, nullptr, nullptr, nullptr,
+                       ws + lay.fn2, nullptr, s) != hipSuccess)
+    return GKA_ERR_HIP;
   gka::BwdArgs ba{};
   ba.q = q;
   ba.k = k;
@@ -446,13 +503,15 @@ gka_status gka_bwd(const gka_params* p, const void* q, const void* k, const void
   ba.dv = dv;
   ba.dgamma = dgamma;
   ba.dbeta = dbeta;
-  ba.snap = static_cast<float*>(workspace);
-  ba.xs = ba.snap + n * 2 * D * D;
-  ba.ys = ba.xs + n * D;
-  ba.cs = ba.ys + n * D;
-  if (gka::launch_bwd(p->dtype, p->D, p->B * p->H, p->T, p->H, ba, cc,
-                      static_cast<hipStream_t>(stream)) != hipSuccess)
-    return GKA_ERR_HIP;
+  ba.snap = ws + lay.snap;
+  ba.xs = ws + lay.xs;
+  ba.ys = ws + lay.ys;
+  ba.cs = ws + lay.cs;
+  ba.fstates = ws + lay.fstates;
+  ba.rstates = ws + lay.rstates;
+  ba.rlog2 = ws + lay.rlog2;
+  ba.rn2 = ws + lay.rn2;
+  if (gka::launch_bwd(pl, ba, cc, s) != hipSuccess) return GKA_ERR_HIP;
   return GKA_OK;
 }
 

@@ -9,12 +9,23 @@
 //   dk_t = beta_t ((Gb_t + Gb_t^T) k_t + Wb_t^T v_t),  dv_t = beta_t Wb_t k_t,
 //   dbeta_t = k_t^T Gb_t k_t + v_t^T Wb_t k_t,  dgamma_t = <Gb_t, H_{t-1}> + <Wb_t, U_{t-1}>.
 //
-// Reference-grade design: one workgroup per head walks the whole sequence, the D x D matrices
-// held in registers with the decode step's layout (4D threads; thread tid owns the float4 column
-// group c4 = tid % (D/4) and rows r0 + j RS). The forward sweep writes every H_t and U_t to the
-// workspace (the reverse sweep needs them in reverse order, and the recurrence cannot be run
-// backwards stably: it divides by gamma); the reverse sweep reads them back. Parallel over heads
-// only, and bound by the sequential per-token solves: correct, not fast.
+// Chunk-parallel sweeps: the D x D matrices are held in registers with the decode step's layout
+// (4D threads; thread tid owns the float4 column group c4 = tid % (D/4) and rows r0 + j RS), one
+// workgroup per (chunk, head).
+//   1. The forward's segment summaries and scan with one chunk per segment give every chunk's
+//      starting H and U.
+//   2. The forward sweep runs each chunk token by token from its starting state: H_t and U_t
+//      are written to the workspace (the reverse sweep needs them in reverse order, and the
+//      recurrence cannot be run backwards stably: it divides by gamma), the two solves give
+//      x_t, y_t, c_t and dq_t.
+//   3. A local reverse sweep per chunk from zero gives the chunk's part of (Gb, Wb) at its first
+//      token, and the product P_c of the gates that carry the next chunk's gradients into it.
+//   4. The forward's segment scan over the chunks in reverse order combines them into every
+//      chunk's incoming (Gb, Wb): Gb_first(c) = Gb_local(c) + P_c Gb_first(c + 1).
+//   5. The final reverse sweep per chunk starts from its incoming gradients and writes dk, dv,
+//      dgamma, dbeta.
+// Each sweep is sequential over its chunk's tokens (block reductions per token): correct, and
+// parallel over chunks and heads, but far from the matrix cores.
 #include "gka_internal.hpp"
 
 namespace gka {
@@ -86,14 +97,15 @@ struct BwdReduce {
 };
 
 template <typename T, int D, int NT>
-__global__ __launch_bounds__(NT) void bwd_forward_kernel(BwdArgs A, int Tlen, int Hn,
+__global__ __launch_bounds__(NT) void bwd_forward_kernel(BwdArgs A, int Tlen, int Hn, int C,
                                                          ChebConsts cc) {
   using L = BwdLayout<D, NT>;
   constexpr int F = L::F, RS = L::RS, NW = L::NW;
   __shared__ float ks[D], vs[D], qv[D], dv_[D], ws[D];
   __shared__ float part[NW][D];
   __shared__ float red[NW];
-  const int bh = blockIdx.x;
+  const int ch = blockIdx.x, N = gridDim.x;
+  const int bh = blockIdx.y;
   const int b = bh / Hn, h = bh % Hn;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int c4 = tid % L::C4, r0 = tid / L::C4;
@@ -104,13 +116,17 @@ __global__ __launch_bounds__(NT) void bwd_forward_kernel(BwdArgs A, int Tlen, in
   const T* dout = static_cast<const T*>(A.dout);
   T* dq = static_cast<T*>(A.dq);
 
+  // the chunk's starting state (row-major H and U of the forward's segment scan)
   f32x4 Hr[F], Ur[F];
+  const float* st0 = A.fstates + ((size_t)bh * N + ch) * 2 * D * D;
 #pragma unroll
   for (int j = 0; j < F; ++j) {
-    Hr[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    Ur[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int r = r0 + j * RS;
+    Hr[j] = *reinterpret_cast<const f32x4*>(st0 + (size_t)r * D + 4 * c4);
+    Ur[j] = *reinterpret_cast<const f32x4*>(st0 + (size_t)D * D + (size_t)r * D + 4 * c4);
   }
-  for (int t = 0; t < Tlen; ++t) {
+  const int t_end = min(Tlen, (ch + 1) * C);
+  for (int t = ch * C; t < t_end; ++t) {
     const long long tok = (b * (long long)Tlen + t) * Hn + h;
     if (tid < D) {
       ks[tid] = to_f32(k[tok * D + tid]);
@@ -168,14 +184,19 @@ __global__ __launch_bounds__(NT) void bwd_forward_kernel(BwdArgs A, int Tlen, in
   }
 }
 
-template <typename T, int D, int NT>
-__global__ __launch_bounds__(NT) void bwd_reverse_kernel(BwdArgs A, int Tlen, int Hn) {
+// LOCAL: from zero gradients at the chunk's end, writing the chunk's (Gb, Wb) at its first token
+// and log2 of P_c (the gates gamma_{t0+1} .. gamma_{t_end}, the last one the next chunk's first)
+// to slot N - 1 - c of the reverse scan; otherwise from the incoming gradients of that slot (as
+// the scan left them), writing the gradients of the inputs.
+template <typename T, int D, int NT, bool LOCAL>
+__global__ __launch_bounds__(NT) void bwd_reverse_kernel(BwdArgs A, int Tlen, int Hn, int C) {
   using L = BwdLayout<D, NT>;
   constexpr int F = L::F, RS = L::RS, NW = L::NW;
   __shared__ float ks[D], vs[D], xv[D], yv[D], dv_[D], rgk[D], rwk[D];
   __shared__ float part[NW][D];
   __shared__ float red[NW];
-  const int bh = blockIdx.x;
+  const int ch = blockIdx.x, N = gridDim.x;
+  const int bh = blockIdx.y;
   const int b = bh / Hn, h = bh % Hn;
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const int c4 = tid % L::C4, r0 = tid / L::C4;
@@ -186,13 +207,22 @@ __global__ __launch_bounds__(NT) void bwd_reverse_kernel(BwdArgs A, int Tlen, in
   T* dk = static_cast<T*>(A.dk);
   T* dvo = static_cast<T*>(A.dv);
 
+  float* slot = A.rstates + ((size_t)bh * N + (N - 1 - ch)) * 2 * D * D;
   f32x4 Gb[F], Wb[F];
 #pragma unroll
   for (int j = 0; j < F; ++j) {
-    Gb[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    Wb[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int r = r0 + j * RS;
+    if constexpr (LOCAL) {
+      Gb[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+      Wb[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    } else {
+      Gb[j] = *reinterpret_cast<const f32x4*>(slot + (size_t)r * D + 4 * c4);
+      Wb[j] = *reinterpret_cast<const f32x4*>(slot + (size_t)D * D + (size_t)r * D + 4 * c4);
+    }
   }
-  for (int t = Tlen - 1; t >= 0; --t) {
+  const int t0 = ch * C, t_end = min(Tlen, (ch + 1) * C);
+  float l2p = 0.0f;  // LOCAL: log2 of the gates gamma_{t0+1} .. gamma_{t_end}
+  for (int t = t_end - 1; t >= t0; --t) {
     const long long tok = (b * (long long)Tlen + t) * Hn + h;
     const size_t row = ((size_t)bh * Tlen + t) * D;
     if (tid < D) {
@@ -203,7 +233,11 @@ __global__ __launch_bounds__(NT) void bwd_reverse_kernel(BwdArgs A, int Tlen, in
       yv[tid] = A.ys[row + tid];
     }
     const float c = A.cs[(size_t)bh * Tlen + t];
-    const float gn = t + 1 < Tlen ? A.gamma[tok + Hn] : 0.0f;  // gamma_{t+1}
+    // gamma_{t+1}: within the chunk; past its last token only the incoming gradients, which
+    // LOCAL leaves at zero (their factor goes to P_c)
+    const float gnext = t + 1 < Tlen ? A.gamma[tok + Hn] : 0.0f;
+    const float gn = LOCAL && t + 1 == t_end ? 0.0f : gnext;
+    if constexpr (LOCAL) l2p += t + 1 < Tlen ? log2_gate(gnext) : 0.0f;
     const float bt = A.beta ? A.beta[tok] : 1.0f;
     __syncthreads();
     // Gb_t = -y x^T + c H_t + gamma_{t+1} Gb_{t+1},  Wb_t = do x^T + gamma_{t+1} Wb_{t+1}
@@ -217,61 +251,81 @@ __global__ __launch_bounds__(NT) void bwd_reverse_kernel(BwdArgs A, int Tlen, in
       const f32x4 Ht = *reinterpret_cast<const f32x4*>(snap + (size_t)r * D + 4 * c4);
       Gb[j] = c * Ht - yv[r] * xc + gn * Gb[j];
       Wb[j] = dv_[r] * xc + gn * Wb[j];
-      if (prev) {
+      if (!LOCAL && prev) {
         const f32x4 Hp = *reinterpret_cast<const f32x4*>(prev + (size_t)r * D + 4 * c4);
         const f32x4 Up = *reinterpret_cast<const f32x4*>(prev + (size_t)D * D + (size_t)r * D + 4 * c4);
         dg += Gb[j][0] * Hp[0] + Gb[j][1] * Hp[1] + Gb[j][2] * Hp[2] + Gb[j][3] * Hp[3];
         dg += Wb[j][0] * Up[0] + Wb[j][1] * Up[1] + Wb[j][2] * Up[2] + Wb[j][3] * Up[3];
       }
     }
-    dg = R.sum(dg);
-    R.rowsum(Gb, ks, rgk);  // (Gb k)[r]
-    R.rowsum(Wb, ks, rwk);  // (Wb k)[r]
-    const float gtk = R.colsum(Gb, ks);  // (Gb^T k)[c]
-    const float wtv = R.colsum(Wb, vs);  // (Wb^T v)[c]
-    float db = 0.0f;
-    if (tid < D) {
-      dk[tok * D + tid] = from_f32<T>(bt * (rgk[tid] + gtk + wtv));
-      dvo[tok * D + tid] = from_f32<T>(bt * rwk[tid]);
-      db = ks[tid] * rgk[tid] + vs[tid] * rwk[tid];
-    }
-    db = R.sum(db);
-    if (tid == 0) {
-      A.dgamma[tok] = dg;
-      if (A.dbeta) A.dbeta[tok] = db;
+    if constexpr (!LOCAL) {
+      dg = R.sum(dg);
+      R.rowsum(Gb, ks, rgk);  // (Gb k)[r]
+      R.rowsum(Wb, ks, rwk);  // (Wb k)[r]
+      const float gtk = R.colsum(Gb, ks);  // (Gb^T k)[c]
+      const float wtv = R.colsum(Wb, vs);  // (Wb^T v)[c]
+      float db = 0.0f;
+      if (tid < D) {
+        dk[tok * D + tid] = from_f32<T>(bt * (rgk[tid] + gtk + wtv));
+        dvo[tok * D + tid] = from_f32<T>(bt * rwk[tid]);
+        db = ks[tid] * rgk[tid] + vs[tid] * rwk[tid];
+      }
+      db = R.sum(db);
+      if (tid == 0) {
+        A.dgamma[tok] = dg;
+        if (A.dbeta) A.dbeta[tok] = db;
+      }
     }
     __syncthreads();  // the token vectors are read
+  }
+  if constexpr (LOCAL) {
+#pragma unroll
+    for (int j = 0; j < F; ++j) {
+      const int r = r0 + j * RS;
+      *reinterpret_cast<f32x4*>(slot + (size_t)r * D + 4 * c4) = Gb[j];
+      *reinterpret_cast<f32x4*>(slot + (size_t)D * D + (size_t)r * D + 4 * c4) = Wb[j];
+    }
+    if (tid == 0) A.rlog2[(size_t)bh * N + (N - 1 - ch)] = l2p;
   }
 }
 
 template <typename T, int D, int NT>
-hipError_t launch_bwd_t(int BH, int Tlen, int Hn, const BwdArgs& a, const ChebConsts& cc,
+hipError_t launch_bwd_t(const FwdPlan& pl, const BwdArgs& a, const ChebConsts& cc,
                         hipStream_t stream) {
-  hipLaunchKernelGGL((bwd_forward_kernel<T, D, NT>), dim3(BH), dim3(NT), 0, stream, a, Tlen, Hn,
-                     cc);
+  const dim3 grid(pl.N, pl.B * pl.H);
+  hipLaunchKernelGGL((bwd_forward_kernel<T, D, NT>), grid, dim3(NT), 0, stream, a, pl.T, pl.H,
+                     pl.C, cc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_reverse_kernel<T, D, NT>), dim3(BH), dim3(NT), 0, stream, a, Tlen, Hn);
+  hipLaunchKernelGGL((bwd_reverse_kernel<T, D, NT, true>), grid, dim3(NT), 0, stream, a, pl.T,
+                     pl.H, pl.C);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // incoming gradients of every chunk: the segment scan over the chunks in reverse order
+  if ((e = launch_scan(pl, a.rstates, a.rlog2, nullptr, nullptr, nullptr, a.rn2, nullptr,
+                       stream)) != hipSuccess)
+    return e;
+  hipLaunchKernelGGL((bwd_reverse_kernel<T, D, NT, false>), grid, dim3(NT), 0, stream, a, pl.T,
+                     pl.H, pl.C);
   return hipGetLastError();
 }
 
 }  // namespace
 
-hipError_t launch_bwd(int dtype, int D, int BH, int Tlen, int Hn, const BwdArgs& a,
-                      const ChebConsts& cc, hipStream_t stream) {
-  if (dtype == 0) {
-    switch (D) {
-      case 16: return launch_bwd_t<bf16, 16, 64>(BH, Tlen, Hn, a, cc, stream);
-      case 32: return launch_bwd_t<bf16, 32, 128>(BH, Tlen, Hn, a, cc, stream);
-      case 64: return launch_bwd_t<bf16, 64, 256>(BH, Tlen, Hn, a, cc, stream);
-      case 128: return launch_bwd_t<bf16, 128, 512>(BH, Tlen, Hn, a, cc, stream);
+hipError_t launch_bwd(const FwdPlan& pl, const BwdArgs& a, const ChebConsts& cc,
+                      hipStream_t stream) {
+  if (pl.dtype == 0) {
+    switch (pl.D) {
+      case 16: return launch_bwd_t<bf16, 16, 64>(pl, a, cc, stream);
+      case 32: return launch_bwd_t<bf16, 32, 128>(pl, a, cc, stream);
+      case 64: return launch_bwd_t<bf16, 64, 256>(pl, a, cc, stream);
+      case 128: return launch_bwd_t<bf16, 128, 512>(pl, a, cc, stream);
     }
   } else {
-    switch (D) {
-      case 16: return launch_bwd_t<float, 16, 64>(BH, Tlen, Hn, a, cc, stream);
-      case 32: return launch_bwd_t<float, 32, 128>(BH, Tlen, Hn, a, cc, stream);
-      case 64: return launch_bwd_t<float, 64, 256>(BH, Tlen, Hn, a, cc, stream);
-      case 128: return launch_bwd_t<float, 128, 512>(BH, Tlen, Hn, a, cc, stream);
+    switch (pl.D) {
+      case 16: return launch_bwd_t<float, 16, 64>(pl, a, cc, stream);
+      case 32: return launch_bwd_t<float, 32, 128>(pl, a, cc, stream);
+      case 64: return launch_bwd_t<float, 64, 256>(pl, a, cc, stream);
+      case 128: return launch_bwd_t<float, 128, 512>(pl, a, cc, stream);
     }
   }
   return hipErrorInvalidValue;

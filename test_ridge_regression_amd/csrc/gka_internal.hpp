@@ -123,8 +123,9 @@ hipError_t launch_scan(const FwdPlan& pl, float* ws_states, const float* ws_log2
                        float* u, const float* hnorm2, float* n2_seg0, const int* cu,
                        hipStream_t stream);
 
-// Backward pass (gka_bwd): arguments of its two kernels. Workspace: snap [BH][T][2][D][D] (H_t, U_t
-// after every token), xs, ys [BH][T][D] (the solves of the forward sweep), cs [BH][T].
+// Backward pass (gka_bwd): arguments of its kernels. Workspace: snap [BH][T][2][D][D] (H_t, U_t
+// after every token), xs, ys [BH][T][D] (the solves of the forward sweep), cs [BH][T], and the
+// chunk states of the two scans.
 struct BwdArgs {
   const void* q;
   const void* k;
@@ -141,9 +142,14 @@ struct BwdArgs {
   float* xs;
   float* ys;
   float* cs;
+  const float* fstates;  // [BH][N][2][D][D] every chunk's starting H and U (forward scan)
+  float* rstates;        // [BH][N][2][D][D] chunk gradients (Gb, Wb), slot N - 1 - chunk
+  float* rlog2;          // [BH][N] log2 of each chunk's gate product P_c, same slots
+  float* rn2;            // [BH] scratch of the reverse scan
 };
 
-hipError_t launch_bwd(int dtype, int D, int BH, int Tlen, int Hn, const BwdArgs& a,
-                      const ChebConsts& cc, hipStream_t stream);
+// Backward of a dense batch; pl: the plan of one chunk per segment (S = N, J = 1).
+hipError_t launch_bwd(const FwdPlan& pl, const BwdArgs& a, const ChebConsts& cc,
+                      hipStream_t stream);
 
 }  // namespace gka

@@ -265,7 +265,10 @@ def test_backward_entry_point_checks(lib):
     P = ctypes.byref
     p = params(B=1, H=1, T=64, D=32)
     need = lib.gka_bwd_workspace_bytes(P(p))
-    assert need == ((64 * (2 * 32 * 32 + 2 * 32 + 1)) * 4 + 255) // 256 * 256
+    up = lambda x: (x + 63) // 64 * 64
+    n, D, N = 64, 32, 1  # one chunk of 64 tokens
+    assert need == 4 * (up(n * 2 * D * D) + 2 * up(n * D) + up(n)
+                        + 2 * (up(N * 2 * D * D) + up(N) + up(1)))
     w = ctypes.c_void_p(ADDR[11] + (1 << 31))
     bw = lambda p, q=VP[0], dq=VP[5], dk=VP[6], dg=VP[8], ws=w, wsb=need: lib.gka_bwd(
         P(p) if p is not None else None, q, VP[1], VP[2], VP[3], None, VP[4], dq, dk, VP[7], dg,

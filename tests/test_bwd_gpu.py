@@ -82,3 +82,18 @@ def test_backward_at_the_figure_shape_sampled():
         sl = (slice(b, b + 1), slice(None), slice(h, h + 1))
         ref = gka_backward_ref(q[sl], k[sl], v[sl], g[sl], do[sl], w.a, w.iters)
         check({n: got[n][sl] for n in got}, ref, "bf16", f"figure shape head ({b}, {h})")
+
+
+@pytest.mark.parametrize("dtype,D", [("bf16", 64), ("fp32", 64), ("fp32", 128)])
+def test_backward_several_chunks_with_write_gate(dtype, D):
+    # 4 chunks of 64 (16 chunks of 16 for float32 D = 128) and a ragged tail: the chunk-start
+    # states of the forward scan and the incoming gradients of the reverse scan
+    B, T, H = 1, 230, 2
+    q, k, v, g = W.make_prefill(B, T, H, D, 2.0, 1.0, dtype, seed=1130 + D)
+    g[0, 100:110, 0] = 0.0  # gates of 0 inside a chunk and across the reverse scan
+    do = W.make_prefill(B, T, H, D, 0.0, 1.0, dtype, seed=1131)[2]
+    beta = W.make_beta(B, T, H, 1132)
+    ref = gka_backward_ref(q, k, v, g, do, 0.05, 10, beta=beta)
+    log(f"backward several chunks {dtype} D={D}")
+    got = run(q, k, v, g, do, 0.05, 10, dtype, beta=beta)
+    check(got, ref, dtype, f"backward several chunks {dtype} D={D}")
