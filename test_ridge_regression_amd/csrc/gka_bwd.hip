@@ -10,8 +10,9 @@
 //   dbeta_t = k_t^T Gb_t k_t + v_t^T Wb_t k_t,  dgamma_t = <Gb_t, H_{t-1}> + <Wb_t, U_{t-1}>.
 //
 // Chunk-parallel sweeps: the D x D matrices are held in registers with the decode step's layout
-// (4D threads; thread tid owns the float4 column group c4 = tid % (D/4) and rows r0 + j RS), one
-// workgroup per (chunk, head).
+// (thread tid owns the float4 column group c4 = tid % (D/4) and rows r0 + j RS), one workgroup
+// per (chunk, head) of 2D threads (one wave for D <= 32): the per-token block reductions then
+// span fewer waves, and the lower register count lets several workgroups share a compute unit.
 //   1. The forward's segment summaries and scan with one chunk per segment give every chunk's
 //      starting H and U.
 //   2. The forward sweep runs each chunk token by token from its starting state: H_t and U_t
@@ -316,16 +317,16 @@ hipError_t launch_bwd(const FwdPlan& pl, const BwdArgs& a, const ChebConsts& cc,
   if (pl.dtype == 0) {
     switch (pl.D) {
       case 16: return launch_bwd_t<bf16, 16, 64>(pl, a, cc, stream);
-      case 32: return launch_bwd_t<bf16, 32, 128>(pl, a, cc, stream);
-      case 64: return launch_bwd_t<bf16, 64, 256>(pl, a, cc, stream);
-      case 128: return launch_bwd_t<bf16, 128, 512>(pl, a, cc, stream);
+      case 32: return launch_bwd_t<bf16, 32, 64>(pl, a, cc, stream);
+      case 64: return launch_bwd_t<bf16, 64, 128>(pl, a, cc, stream);
+      case 128: return launch_bwd_t<bf16, 128, 256>(pl, a, cc, stream);
     }
   } else {
     switch (pl.D) {
       case 16: return launch_bwd_t<float, 16, 64>(pl, a, cc, stream);
-      case 32: return launch_bwd_t<float, 32, 128>(pl, a, cc, stream);
-      case 64: return launch_bwd_t<float, 64, 256>(pl, a, cc, stream);
-      case 128: return launch_bwd_t<float, 128, 512>(pl, a, cc, stream);
+      case 32: return launch_bwd_t<float, 32, 64>(pl, a, cc, stream);
+      case 64: return launch_bwd_t<float, 64, 128>(pl, a, cc, stream);
+      case 128: return launch_bwd_t<float, 128, 256>(pl, a, cc, stream);
     }
   }
   return hipErrorInvalidValue;
