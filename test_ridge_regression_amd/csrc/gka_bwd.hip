@@ -223,6 +223,14 @@ __global__ __launch_bounds__(NT) void bwd_reverse_kernel(BwdArgs A, int Tlen, in
   }
   const int t0 = ch * C, t_end = min(Tlen, (ch + 1) * C);
   float l2p = 0.0f;  // LOCAL: log2 of the gates gamma_{t0+1} .. gamma_{t_end}
+  // the final sweep reads H_{t-1} for dgamma at step t and keeps it as H_t of step t - 1
+  f32x4 Hc[LOCAL ? 1 : F];
+  if constexpr (!LOCAL) {
+    const float* snap_last = A.snap + ((size_t)bh * Tlen + (t_end - 1)) * 2 * D * D;
+#pragma unroll
+    for (int j = 0; j < F; ++j)
+      Hc[j] = *reinterpret_cast<const f32x4*>(snap_last + (size_t)(r0 + j * RS) * D + 4 * c4);
+  }
   for (int t = t_end - 1; t >= t0; --t) {
     const long long tok = (b * (long long)Tlen + t) * Hn + h;
     const size_t row = ((size_t)bh * Tlen + t) * D;
@@ -249,14 +257,19 @@ __global__ __launch_bounds__(NT) void bwd_reverse_kernel(BwdArgs A, int Tlen, in
 #pragma unroll
     for (int j = 0; j < F; ++j) {
       const int r = r0 + j * RS;
-      const f32x4 Ht = *reinterpret_cast<const f32x4*>(snap + (size_t)r * D + 4 * c4);
+      f32x4 Ht;
+      if constexpr (LOCAL) Ht = *reinterpret_cast<const f32x4*>(snap + (size_t)r * D + 4 * c4);
+      else Ht = Hc[j];
       Gb[j] = c * Ht - yv[r] * xc + gn * Gb[j];
       Wb[j] = dv_[r] * xc + gn * Wb[j];
-      if (!LOCAL && prev) {
-        const f32x4 Hp = *reinterpret_cast<const f32x4*>(prev + (size_t)r * D + 4 * c4);
-        const f32x4 Up = *reinterpret_cast<const f32x4*>(prev + (size_t)D * D + (size_t)r * D + 4 * c4);
-        dg += Gb[j][0] * Hp[0] + Gb[j][1] * Hp[1] + Gb[j][2] * Hp[2] + Gb[j][3] * Hp[3];
-        dg += Wb[j][0] * Up[0] + Wb[j][1] * Up[1] + Wb[j][2] * Up[2] + Wb[j][3] * Up[3];
+      if constexpr (!LOCAL) {
+        if (prev) {
+          const f32x4 Hp = *reinterpret_cast<const f32x4*>(prev + (size_t)r * D + 4 * c4);
+          const f32x4 Up = *reinterpret_cast<const f32x4*>(prev + (size_t)D * D + (size_t)r * D + 4 * c4);
+          dg += Gb[j][0] * Hp[0] + Gb[j][1] * Hp[1] + Gb[j][2] * Hp[2] + Gb[j][3] * Hp[3];
+          dg += Wb[j][0] * Up[0] + Wb[j][1] * Up[1] + Wb[j][2] * Up[2] + Wb[j][3] * Up[3];
+          Hc[j] = Hp;  // H_t of step t - 1
+        }
       }
     }
     if constexpr (!LOCAL) {
