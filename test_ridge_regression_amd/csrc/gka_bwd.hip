@@ -19,8 +19,9 @@
 //      are written to the workspace (the reverse sweep needs them in reverse order, and the
 //      recurrence cannot be run backwards stably: it divides by gamma), the two solves give
 //      x_t, y_t, c_t and dq_t.
-//   3. A local reverse sweep per chunk from zero gives the chunk's part of (Gb, Wb) at its first
-//      token, and the product P_c of the gates that carry the next chunk's gradients into it.
+//   3. The same sweep accumulates the chunk's part of (Gb, Wb) at its first token, a forward
+//      sum: Gb_local(c) = sum_t (gamma_{t0+1} .. gamma_t) G_t, likewise Wb, and the product
+//      P_c of the gates that carry the next chunk's gradients into it.
 //   4. The forward's segment scan over the chunks in reverse order combines them into every
 //      chunk's incoming (Gb, Wb): Gb_first(c) = Gb_local(c) + P_c Gb_first(c + 1).
 //   5. The final reverse sweep per chunk starts from its incoming gradients and writes dk, dv,
@@ -102,7 +103,7 @@ __global__ __launch_bounds__(NT) void bwd_forward_kernel(BwdArgs A, int Tlen, in
                                                          ChebConsts cc) {
   using L = BwdLayout<D, NT>;
   constexpr int F = L::F, RS = L::RS, NW = L::NW;
-  __shared__ float ks[D], vs[D], qv[D], dv_[D], ws[D];
+  __shared__ float ks[D], vs[D], qv[D], dv_[D], ws[D], xl[D], yl[D];
   __shared__ float part[NW][D];
   __shared__ float red[NW];
   const int ch = blockIdx.x, N = gridDim.x;
@@ -126,8 +127,17 @@ __global__ __launch_bounds__(NT) void bwd_forward_kernel(BwdArgs A, int Tlen, in
     Hr[j] = *reinterpret_cast<const f32x4*>(st0 + (size_t)r * D + 4 * c4);
     Ur[j] = *reinterpret_cast<const f32x4*>(st0 + (size_t)D * D + (size_t)r * D + 4 * c4);
   }
-  const int t_end = min(Tlen, (ch + 1) * C);
-  for (int t = ch * C; t < t_end; ++t) {
+  // the chunk's part of the statistics' gradients at its first token, weighted by the gate
+  // products w_t = gamma_{t0+1} .. gamma_t
+  f32x4 Gl[F], Wl[F];
+#pragma unroll
+  for (int j = 0; j < F; ++j) {
+    Gl[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+    Wl[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+  float w = 1.0f, l2p = 0.0f;
+  const int t0 = ch * C, t_end = min(Tlen, (ch + 1) * C);
+  for (int t = t0; t < t_end; ++t) {
     const long long tok = (b * (long long)Tlen + t) * Hn + h;
     if (tid < D) {
       ks[tid] = to_f32(k[tok * D + tid]);
@@ -137,6 +147,10 @@ __global__ __launch_bounds__(NT) void bwd_forward_kernel(BwdArgs A, int Tlen, in
     }
     const float g = A.gamma[tok];
     const float bt = A.beta ? A.beta[tok] : 1.0f;
+    if (t > t0) {
+      w *= g;
+      l2p += log2_gate(g);
+    }
     __syncthreads();
     // H_t, U_t, and their snapshot (the reverse sweep reads them back)
     const f32x4 kc = *reinterpret_cast<const f32x4*>(ks + 4 * c4);
@@ -176,20 +190,42 @@ __global__ __launch_bounds__(NT) void bwd_forward_kernel(BwdArgs A, int Tlen, in
     const float c = live ? -cc.a * yx * inv_n : 0.0f;
     if (tid < D) {
       const size_t o = ((size_t)bh * Tlen + t) * D + tid;
-      A.xs[o] = live ? x : 0.0f;
-      A.ys[o] = live ? y : 0.0f;
+      A.xs[o] = xl[tid] = live ? x : 0.0f;
+      A.ys[o] = yl[tid] = live ? y : 0.0f;
       dq[tok * D + tid] = from_f32<T>(live ? y : 0.0f);
     }
     if (tid == 0) A.cs[(size_t)bh * Tlen + t] = c;
+    __syncthreads();
+    // G_t = -y x^T + c H_t and W_t = do x^T, into the chunk's weighted sums
+    {
+      const f32x4 xc = *reinterpret_cast<const f32x4*>(xl + 4 * c4);
+#pragma unroll
+      for (int j = 0; j < F; ++j) {
+        const int r = r0 + j * RS;
+        Gl[j] += w * (c * Hr[j] - yl[r] * xc);
+        Wl[j] += w * (dv_[r] * xc);
+      }
+    }
     __syncthreads();  // the token vectors are read
+  }
+  // slot N - 1 - c of the reverse scan: the chunk's (Gb, Wb) and log2 P_c, P_c = w_{t_end-1}
+  // gamma_{t_end} (the next chunk's first gate)
+  float* slot = A.rstates + ((size_t)bh * N + (N - 1 - ch)) * 2 * D * D;
+#pragma unroll
+  for (int j = 0; j < F; ++j) {
+    const int r = r0 + j * RS;
+    *reinterpret_cast<f32x4*>(slot + (size_t)r * D + 4 * c4) = Gl[j];
+    *reinterpret_cast<f32x4*>(slot + (size_t)D * D + (size_t)r * D + 4 * c4) = Wl[j];
+  }
+  if (tid == 0) {
+    const long long tnext = (b * (long long)Tlen + t_end) * Hn + h;
+    A.rlog2[(size_t)bh * N + (N - 1 - ch)] = l2p + (t_end < Tlen ? log2_gate(A.gamma[tnext]) : 0.0f);
   }
 }
 
-// LOCAL: from zero gradients at the chunk's end, writing the chunk's (Gb, Wb) at its first token
-// and log2 of P_c (the gates gamma_{t0+1} .. gamma_{t_end}, the last one the next chunk's first)
-// to slot N - 1 - c of the reverse scan; otherwise from the incoming gradients of that slot (as
-// the scan left them), writing the gradients of the inputs.
-template <typename T, int D, int NT, bool LOCAL>
+// From the incoming gradients of slot N - 1 - c (as the reverse scan left them), writing the
+// gradients of the inputs.
+template <typename T, int D, int NT>
 __global__ __launch_bounds__(NT) void bwd_reverse_kernel(BwdArgs A, int Tlen, int Hn, int C) {
   using L = BwdLayout<D, NT>;
   constexpr int F = L::F, RS = L::RS, NW = L::NW;
@@ -208,24 +244,18 @@ __global__ __launch_bounds__(NT) void bwd_reverse_kernel(BwdArgs A, int Tlen, in
   T* dk = static_cast<T*>(A.dk);
   T* dvo = static_cast<T*>(A.dv);
 
-  float* slot = A.rstates + ((size_t)bh * N + (N - 1 - ch)) * 2 * D * D;
+  const float* slot = A.rstates + ((size_t)bh * N + (N - 1 - ch)) * 2 * D * D;
   f32x4 Gb[F], Wb[F];
 #pragma unroll
   for (int j = 0; j < F; ++j) {
     const int r = r0 + j * RS;
-    if constexpr (LOCAL) {
-      Gb[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-      Wb[j] = f32x4{0.f, 0.f, 0.f, 0.f};
-    } else {
-      Gb[j] = *reinterpret_cast<const f32x4*>(slot + (size_t)r * D + 4 * c4);
-      Wb[j] = *reinterpret_cast<const f32x4*>(slot + (size_t)D * D + (size_t)r * D + 4 * c4);
-    }
+    Gb[j] = *reinterpret_cast<const f32x4*>(slot + (size_t)r * D + 4 * c4);
+    Wb[j] = *reinterpret_cast<const f32x4*>(slot + (size_t)D * D + (size_t)r * D + 4 * c4);
   }
   const int t0 = ch * C, t_end = min(Tlen, (ch + 1) * C);
-  float l2p = 0.0f;  // LOCAL: log2 of the gates gamma_{t0+1} .. gamma_{t_end}
-  // the final sweep reads H_{t-1} for dgamma at step t and keeps it as H_t of step t - 1
-  f32x4 Hc[LOCAL ? 1 : F];
-  if constexpr (!LOCAL) {
+  // H_{t-1} is read for dgamma at step t and kept as H_t of step t - 1
+  f32x4 Hc[F];
+  {
     const float* snap_last = A.snap + ((size_t)bh * Tlen + (t_end - 1)) * 2 * D * D;
 #pragma unroll
     for (int j = 0; j < F; ++j)
@@ -242,11 +272,8 @@ __global__ __launch_bounds__(NT) void bwd_reverse_kernel(BwdArgs A, int Tlen, in
       yv[tid] = A.ys[row + tid];
     }
     const float c = A.cs[(size_t)bh * Tlen + t];
-    // gamma_{t+1}: within the chunk; past its last token only the incoming gradients, which
-    // LOCAL leaves at zero (their factor goes to P_c)
-    const float gnext = t + 1 < Tlen ? A.gamma[tok + Hn] : 0.0f;
-    const float gn = LOCAL && t + 1 == t_end ? 0.0f : gnext;
-    if constexpr (LOCAL) l2p += t + 1 < Tlen ? log2_gate(gnext) : 0.0f;
+    // gamma_{t+1} (past the chunk's last token it carries the incoming gradients)
+    const float gn = t + 1 < Tlen ? A.gamma[tok + Hn] : 0.0f;
     const float bt = A.beta ? A.beta[tok] : 1.0f;
     __syncthreads();
     // Gb_t = -y x^T + c H_t + gamma_{t+1} Gb_{t+1},  Wb_t = do x^T + gamma_{t+1} Wb_{t+1}
@@ -257,22 +284,17 @@ __global__ __launch_bounds__(NT) void bwd_reverse_kernel(BwdArgs A, int Tlen, in
 #pragma unroll
     for (int j = 0; j < F; ++j) {
       const int r = r0 + j * RS;
-      f32x4 Ht;
-      if constexpr (LOCAL) Ht = *reinterpret_cast<const f32x4*>(snap + (size_t)r * D + 4 * c4);
-      else Ht = Hc[j];
-      Gb[j] = c * Ht - yv[r] * xc + gn * Gb[j];
+      Gb[j] = c * Hc[j] - yv[r] * xc + gn * Gb[j];
       Wb[j] = dv_[r] * xc + gn * Wb[j];
-      if constexpr (!LOCAL) {
-        if (prev) {
-          const f32x4 Hp = *reinterpret_cast<const f32x4*>(prev + (size_t)r * D + 4 * c4);
-          const f32x4 Up = *reinterpret_cast<const f32x4*>(prev + (size_t)D * D + (size_t)r * D + 4 * c4);
-          dg += Gb[j][0] * Hp[0] + Gb[j][1] * Hp[1] + Gb[j][2] * Hp[2] + Gb[j][3] * Hp[3];
-          dg += Wb[j][0] * Up[0] + Wb[j][1] * Up[1] + Wb[j][2] * Up[2] + Wb[j][3] * Up[3];
-          Hc[j] = Hp;  // H_t of step t - 1
-        }
+      if (prev) {
+        const f32x4 Hp = *reinterpret_cast<const f32x4*>(prev + (size_t)r * D + 4 * c4);
+        const f32x4 Up = *reinterpret_cast<const f32x4*>(prev + (size_t)D * D + (size_t)r * D + 4 * c4);
+        dg += Gb[j][0] * Hp[0] + Gb[j][1] * Hp[1] + Gb[j][2] * Hp[2] + Gb[j][3] * Hp[3];
+        dg += Wb[j][0] * Up[0] + Wb[j][1] * Up[1] + Wb[j][2] * Up[2] + Wb[j][3] * Up[3];
+        Hc[j] = Hp;  // H_t of step t - 1
       }
     }
-    if constexpr (!LOCAL) {
+    {
       dg = R.sum(dg);
       R.rowsum(Gb, ks, rgk);  // (Gb k)[r]
       R.rowsum(Wb, ks, rwk);  // (Wb k)[r]
@@ -292,18 +314,10 @@ __global__ __launch_bounds__(NT) void bwd_reverse_kernel(BwdArgs A, int Tlen, in
     }
     __syncthreads();  // the token vectors are read
   }
-  if constexpr (LOCAL) {
-#pragma unroll
-    for (int j = 0; j < F; ++j) {
-      const int r = r0 + j * RS;
-      *reinterpret_cast<f32x4*>(slot + (size_t)r * D + 4 * c4) = Gb[j];
-      *reinterpret_cast<f32x4*>(slot + (size_t)D * D + (size_t)r * D + 4 * c4) = Wb[j];
-    }
-    if (tid == 0) A.rlog2[(size_t)bh * N + (N - 1 - ch)] = l2p;
-  }
 }
 
-template <typename T, int D, int NT>
+// NT threads for the forward sweep (it holds four D x D matrices), NTR for the reverse (two)
+template <typename T, int D, int NT, int NTR>
 hipError_t launch_bwd_t(const FwdPlan& pl, const BwdArgs& a, const ChebConsts& cc,
                         hipStream_t stream) {
   const dim3 grid(pl.N, pl.B * pl.H);
@@ -311,14 +325,11 @@ hipError_t launch_bwd_t(const FwdPlan& pl, const BwdArgs& a, const ChebConsts& c
                      pl.C, cc);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_reverse_kernel<T, D, NT, true>), grid, dim3(NT), 0, stream, a, pl.T,
-                     pl.H, pl.C);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   // incoming gradients of every chunk: the segment scan over the chunks in reverse order
   if ((e = launch_scan(pl, a.rstates, a.rlog2, nullptr, nullptr, nullptr, a.rn2, nullptr,
                        stream)) != hipSuccess)
     return e;
-  hipLaunchKernelGGL((bwd_reverse_kernel<T, D, NT, false>), grid, dim3(NT), 0, stream, a, pl.T,
+  hipLaunchKernelGGL((bwd_reverse_kernel<T, D, NTR>), grid, dim3(NTR), 0, stream, a, pl.T,
                      pl.H, pl.C);
   return hipGetLastError();
 }
@@ -329,17 +340,17 @@ hipError_t launch_bwd(const FwdPlan& pl, const BwdArgs& a, const ChebConsts& cc,
                       hipStream_t stream) {
   if (pl.dtype == 0) {
     switch (pl.D) {
-      case 16: return launch_bwd_t<bf16, 16, 64>(pl, a, cc, stream);
-      case 32: return launch_bwd_t<bf16, 32, 64>(pl, a, cc, stream);
-      case 64: return launch_bwd_t<bf16, 64, 128>(pl, a, cc, stream);
-      case 128: return launch_bwd_t<bf16, 128, 256>(pl, a, cc, stream);
+      case 16: return launch_bwd_t<bf16, 16, 64, 64>(pl, a, cc, stream);
+      case 32: return launch_bwd_t<bf16, 32, 64, 64>(pl, a, cc, stream);
+      case 64: return launch_bwd_t<bf16, 64, 128, 128>(pl, a, cc, stream);
+      case 128: return launch_bwd_t<bf16, 128, 512, 256>(pl, a, cc, stream);
     }
   } else {
     switch (pl.D) {
-      case 16: return launch_bwd_t<float, 16, 64>(pl, a, cc, stream);
-      case 32: return launch_bwd_t<float, 32, 64>(pl, a, cc, stream);
-      case 64: return launch_bwd_t<float, 64, 128>(pl, a, cc, stream);
-      case 128: return launch_bwd_t<float, 128, 256>(pl, a, cc, stream);
+      case 16: return launch_bwd_t<float, 16, 64, 64>(pl, a, cc, stream);
+      case 32: return launch_bwd_t<float, 32, 64, 64>(pl, a, cc, stream);
+      case 64: return launch_bwd_t<float, 64, 128, 128>(pl, a, cc, stream);
+      case 128: return launch_bwd_t<float, 128, 512, 256>(pl, a, cc, stream);
     }
   }
   return hipErrorInvalidValue;
