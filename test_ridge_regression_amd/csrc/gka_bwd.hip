@@ -84,6 +84,39 @@ struct BwdReduce {
     }
     return s;
   }
+  // two column sums of one matrix at once (one pair of barriers): thread c < D receives
+  // s1 = sum_r M[r][c] w1[r] and s2 = sum_r M[r][c] w2[r]; part2 is a second [NW][D] scratch
+  __device__ void colsum2(const f32x4 (&M)[L::F], const float* w1, const float* w2,
+                          float (*part2)[D], float& s1, float& s2) {
+    f32x4 y1 = {0.0f, 0.0f, 0.0f, 0.0f}, y2 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < L::F; ++j) {
+      y1 += M[j] * w1[r0 + j * L::RS];
+      y2 += M[j] * w2[r0 + j * L::RS];
+    }
+#pragma unroll
+    for (int m = L::C4; m < kWave; m <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        y1[i] += __shfl_xor(y1[i], m, kWave);
+        y2[i] += __shfl_xor(y2[i], m, kWave);
+      }
+    }
+    __syncthreads();  // earlier readers of part and part2 are done
+    if (lane < L::C4) {
+      *reinterpret_cast<f32x4*>(&part[wave][4 * c4]) = y1;
+      *reinterpret_cast<f32x4*>(&part2[wave][4 * c4]) = y2;
+    }
+    __syncthreads();
+    s1 = s2 = 0.0f;
+    if (tid < D) {
+#pragma unroll
+      for (int w = 0; w < L::NW; ++w) {
+        s1 += part[w][tid];
+        s2 += part2[w][tid];
+      }
+    }
+  }
   // row sums: out[r] = sum_c M[r][c] w[c] for every row r (w in LDS), written to LDS out
   __device__ void rowsum(const f32x4 (&M)[L::F], const float* w, float* out) {
     const f32x4 wc = *reinterpret_cast<const f32x4*>(w + 4 * c4);
@@ -103,8 +136,8 @@ __global__ __launch_bounds__(NT) void bwd_forward_kernel(BwdArgs A, int Tlen, in
                                                          ChebConsts cc) {
   using L = BwdLayout<D, NT>;
   constexpr int F = L::F, RS = L::RS, NW = L::NW;
-  __shared__ float ks[D], vs[D], qv[D], dv_[D], ws[D], xl[D], yl[D];
-  __shared__ float part[NW][D];
+  __shared__ float ks[D], vs[D], qv[D], dv_[D], ws[D], ws2[D], xl[D], yl[D];
+  __shared__ float part[NW][D], part2[NW][D];
   __shared__ float red[NW];
   const int ch = blockIdx.x, N = gridDim.x;
   const int bh = blockIdx.y;
@@ -168,24 +201,31 @@ __global__ __launch_bounds__(NT) void bwd_forward_kernel(BwdArgs A, int Tlen, in
     const float n2 = R.sum(sq);
     const bool live = n2 > 0.0f;
     const float n = sqrtf(n2), inv_n = live ? 1.0f / n : 0.0f;
-    // Chebyshev on (H / ||H|| + a I) xh = rhs (thread c < D holds element c); x = xh / ||H||
-    auto solve = [&](float rhs) {
-      float x = cc.c * rhs, xp = 0.0f;
-      for (int i = 1; i < cc.iters; ++i) {
-        if (tid < D) ws[tid] = x;
-        __syncthreads();
-        const float ax = R.colsum(Hr, ws) * inv_n + cc.a * x;
-        if (tid < D) {
-          const float xn = xp + cc.omega[i] * (x - xp + cc.c * (rhs - ax));
-          xp = x;
-          x = xn;
-        }
-      }
-      return x * inv_n;
-    };
-    const float x = solve(tid < D ? qv[tid] : 0.0f);
+    // the two Chebyshev solves on (H / ||H|| + a I) side by side, x for q and y for U^T do
+    // (thread c < D holds element c of both); x = xh / ||H||, y = yh / ||H||
     const float gu = R.colsum(Ur, dv_);  // (U^T do)[c]
-    const float y = solve(tid < D ? gu : 0.0f);
+    const float bq = tid < D ? qv[tid] : 0.0f, bg = tid < D ? gu : 0.0f;
+    float x = cc.c * bq, xp = 0.0f, y = cc.c * bg, yp = 0.0f;
+    for (int i = 1; i < cc.iters; ++i) {
+      if (tid < D) {
+        ws[tid] = x;
+        ws2[tid] = y;
+      }
+      __syncthreads();
+      float hx, hy;
+      R.colsum2(Hr, ws, ws2, part2, hx, hy);
+      if (tid < D) {
+        const float ax = hx * inv_n + cc.a * x, ay = hy * inv_n + cc.a * y;
+        const float xn = xp + cc.omega[i] * (x - xp + cc.c * (bq - ax));
+        const float yn = yp + cc.omega[i] * (y - yp + cc.c * (bg - ay));
+        xp = x;
+        x = xn;
+        yp = y;
+        y = yn;
+      }
+    }
+    x *= inv_n;
+    y *= inv_n;
     const float yx = R.sum(tid < D ? y * x : 0.0f);
     const float c = live ? -cc.a * yx * inv_n : 0.0f;
     if (tid < D) {
