@@ -120,3 +120,30 @@ def test_prefill_in_a_graph(packed):
         assert torch.equal(sg.h, ref_h) and torch.equal(sg.n2, ref_n), rep
         call(gka.GkaState(h0.clone(), u0.clone(), n0.clone()), torch.empty_like(qd), None)
         torch.cuda.synchronize()
+
+
+def test_backward_in_a_graph():
+    B, T, H, D = 1, 150, 2, 64
+    q, k, v, g = W.make_prefill(B, T, H, D, 3.0, 1.0, "bf16", seed=1020)
+    do = W.make_prefill(B, T, H, D, 0.0, 1.0, "bf16", seed=1021)[2]
+    args = (dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), dev(g), dev(do, "bf16"), 0.05, 10)
+    p = gka.make_params(B, T, H, D, 64, 10, 0.05, gka.GKA_BF16)
+    ws = torch.empty(int(gka.load().gka_bwd_workspace_bytes(gka.ctypes.byref(p))), device="cuda",
+                     dtype=torch.uint8)
+    ref = gka.bwd(*args, workspace=ws)
+    torch.cuda.synchronize()
+    ref = [x.clone() for x in ref]
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        outs = gka.bwd(*args, workspace=ws)
+    for rep in range(3):
+        log(f"backward graph replay {rep}")
+        for o in outs:
+            o.zero_()
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        for o, r in zip(outs, ref):
+            assert torch.equal(o, r), rep
+        gka.bwd(*args, workspace=ws)  # eager work between the replays
+        torch.cuda.synchronize()
