@@ -117,6 +117,75 @@ struct BwdReduce {
       }
     }
   }
+  // two sums over the workgroup at once (red2 is a second [NW] scratch)
+  __device__ void sum2(float& a, float& b, float* red2) {
+    a = wave_sum(a);
+    b = wave_sum(b);
+    __syncthreads();
+    if (lane == 0) {
+      red[wave] = a;
+      red2[wave] = b;
+    }
+    __syncthreads();
+    a = b = 0.0f;
+#pragma unroll
+    for (int w = 0; w < L::NW; ++w) {
+      a += red[w];
+      b += red2[w];
+    }
+  }
+  // column sums of two matrices at once: s1 = sum_r M1[r][c] w1[r], s2 = sum_r M2[r][c] w2[r]
+  __device__ void colsum_mm(const f32x4 (&M1)[L::F], const float* w1, const f32x4 (&M2)[L::F],
+                            const float* w2, float (*part2)[D], float& s1, float& s2) {
+    f32x4 y1 = {0.0f, 0.0f, 0.0f, 0.0f}, y2 = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < L::F; ++j) {
+      y1 += M1[j] * w1[r0 + j * L::RS];
+      y2 += M2[j] * w2[r0 + j * L::RS];
+    }
+#pragma unroll
+    for (int m = L::C4; m < kWave; m <<= 1) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        y1[i] += __shfl_xor(y1[i], m, kWave);
+        y2[i] += __shfl_xor(y2[i], m, kWave);
+      }
+    }
+    __syncthreads();
+    if (lane < L::C4) {
+      *reinterpret_cast<f32x4*>(&part[wave][4 * c4]) = y1;
+      *reinterpret_cast<f32x4*>(&part2[wave][4 * c4]) = y2;
+    }
+    __syncthreads();
+    s1 = s2 = 0.0f;
+    if (tid < D) {
+#pragma unroll
+      for (int w = 0; w < L::NW; ++w) {
+        s1 += part[w][tid];
+        s2 += part2[w][tid];
+      }
+    }
+  }
+  // row sums of two matrices with one vector, written to LDS out1, out2 (one barrier)
+  __device__ void rowsum2(const f32x4 (&M1)[L::F], const f32x4 (&M2)[L::F], const float* w,
+                          float* out1, float* out2) {
+    const f32x4 wc = *reinterpret_cast<const f32x4*>(w + 4 * c4);
+#pragma unroll
+    for (int j = 0; j < L::F; ++j) {
+      float p1 = M1[j][0] * wc[0] + M1[j][1] * wc[1] + M1[j][2] * wc[2] + M1[j][3] * wc[3];
+      float p2 = M2[j][0] * wc[0] + M2[j][1] * wc[1] + M2[j][2] * wc[2] + M2[j][3] * wc[3];
+#pragma unroll
+      for (int m = 1; m < L::C4; m <<= 1) {
+        p1 += __shfl_xor(p1, m, kWave);
+        p2 += __shfl_xor(p2, m, kWave);
+      }
+      if (c4 == 0) {
+        out1[r0 + j * L::RS] = p1;
+        out2[r0 + j * L::RS] = p2;
+      }
+    }
+    __syncthreads();
+  }
   // row sums: out[r] = sum_c M[r][c] w[c] for every row r (w in LDS), written to LDS out
   __device__ void rowsum(const f32x4 (&M)[L::F], const float* w, float* out) {
     const f32x4 wc = *reinterpret_cast<const f32x4*>(w + 4 * c4);
@@ -270,8 +339,8 @@ __global__ __launch_bounds__(NT) void bwd_reverse_kernel(BwdArgs A, int Tlen, in
   using L = BwdLayout<D, NT>;
   constexpr int F = L::F, RS = L::RS, NW = L::NW;
   __shared__ float ks[D], vs[D], xv[D], yv[D], dv_[D], rgk[D], rwk[D];
-  __shared__ float part[NW][D];
-  __shared__ float red[NW];
+  __shared__ float part[NW][D], part2[NW][D];
+  __shared__ float red[NW], red2[NW];
   const int ch = blockIdx.x, N = gridDim.x;
   const int bh = blockIdx.y;
   const int b = bh / Hn, h = bh % Hn;
@@ -335,18 +404,16 @@ __global__ __launch_bounds__(NT) void bwd_reverse_kernel(BwdArgs A, int Tlen, in
       }
     }
     {
-      dg = R.sum(dg);
-      R.rowsum(Gb, ks, rgk);  // (Gb k)[r]
-      R.rowsum(Wb, ks, rwk);  // (Wb k)[r]
-      const float gtk = R.colsum(Gb, ks);  // (Gb^T k)[c]
-      const float wtv = R.colsum(Wb, vs);  // (Wb^T v)[c]
+      R.rowsum2(Gb, Wb, ks, rgk, rwk);  // (Gb k)[r], (Wb k)[r]
+      float gtk, wtv;
+      R.colsum_mm(Gb, ks, Wb, vs, part2, gtk, wtv);  // (Gb^T k)[c], (Wb^T v)[c]
       float db = 0.0f;
       if (tid < D) {
         dk[tok * D + tid] = from_f32<T>(bt * (rgk[tid] + gtk + wtv));
         dvo[tok * D + tid] = from_f32<T>(bt * rwk[tid]);
         db = ks[tid] * rgk[tid] + vs[tid] * rwk[tid];
       }
-      db = R.sum(db);
+      R.sum2(dg, db, red2);
       if (tid == 0) {
         A.dgamma[tok] = dg;
         if (A.dbeta) A.dbeta[tok] = db;
