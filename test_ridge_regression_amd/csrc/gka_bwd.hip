@@ -84,8 +84,9 @@ struct BwdReduce {
     }
     return s;
   }
-  // two column sums of one matrix at once (one pair of barriers): thread c < D receives
-  // s1 = sum_r M[r][c] w1[r] and s2 = sum_r M[r][c] w2[r]; part2 is a second [NW][D] scratch
+  // two column sums of one matrix at once: thread c < D receives s1 = sum_r M[r][c] w1[r] and
+  // s2 = sum_r M[r][c] w2[r]; part2 is a second [NW][D] scratch. The caller guarantees a barrier
+  // between the previous reads of part / part2 and this call (the one that publishes w1, w2).
   __device__ void colsum2(const f32x4 (&M)[L::F], const float* w1, const float* w2,
                           float (*part2)[D], float& s1, float& s2) {
     f32x4 y1 = {0.0f, 0.0f, 0.0f, 0.0f}, y2 = {0.0f, 0.0f, 0.0f, 0.0f};
@@ -102,7 +103,6 @@ struct BwdReduce {
         y2[i] += __shfl_xor(y2[i], m, kWave);
       }
     }
-    __syncthreads();  // earlier readers of part and part2 are done
     if (lane < L::C4) {
       *reinterpret_cast<f32x4*>(&part[wave][4 * c4]) = y1;
       *reinterpret_cast<f32x4*>(&part2[wave][4 * c4]) = y2;
