@@ -84,6 +84,33 @@ struct BwdReduce {
     }
     return s;
   }
+  // a column sum (as colsum) and a sum over the workgroup of x at once (one pair of barriers)
+  __device__ void colsum_sum(const f32x4 (&M)[L::F], const float* w, float x, float& cs,
+                             float& s) {
+    f32x4 y = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int j = 0; j < L::F; ++j) y += M[j] * w[r0 + j * L::RS];
+#pragma unroll
+    for (int m = L::C4; m < kWave; m <<= 1) {
+      y[0] += __shfl_xor(y[0], m, kWave);
+      y[1] += __shfl_xor(y[1], m, kWave);
+      y[2] += __shfl_xor(y[2], m, kWave);
+      y[3] += __shfl_xor(y[3], m, kWave);
+    }
+    x = wave_sum(x);
+    __syncthreads();  // earlier readers of part and red are done
+    if (lane < L::C4) *reinterpret_cast<f32x4*>(&part[wave][4 * c4]) = y;
+    if (lane == 0) red[wave] = x;
+    __syncthreads();
+    cs = 0.0f;
+    if (tid < D) {
+#pragma unroll
+      for (int w = 0; w < L::NW; ++w) cs += part[w][tid];
+    }
+    s = 0.0f;
+#pragma unroll
+    for (int w = 0; w < L::NW; ++w) s += red[w];
+  }
   // two column sums of one matrix at once: thread c < D receives s1 = sum_r M[r][c] w1[r] and
   // s2 = sum_r M[r][c] w2[r]; part2 is a second [NW][D] scratch. The caller guarantees a barrier
   // between the previous reads of part / part2 and this call (the one that publishes w1, w2).
@@ -267,12 +294,12 @@ __global__ __launch_bounds__(NT) void bwd_forward_kernel(BwdArgs A, int Tlen, in
       *reinterpret_cast<f32x4*>(snap + (size_t)D * D + (size_t)r * D + 4 * c4) = Ur[j];
       sq += Hr[j][0] * Hr[j][0] + Hr[j][1] * Hr[j][1] + Hr[j][2] * Hr[j][2] + Hr[j][3] * Hr[j][3];
     }
-    const float n2 = R.sum(sq);
+    float n2, gu;  // ||H_t||^2 and (U^T do)[c]
+    R.colsum_sum(Ur, dv_, sq, gu, n2);
     const bool live = n2 > 0.0f;
     const float n = sqrtf(n2), inv_n = live ? 1.0f / n : 0.0f;
     // the two Chebyshev solves on (H / ||H|| + a I) side by side, x for q and y for U^T do
     // (thread c < D holds element c of both); x = xh / ||H||, y = yh / ||H||
-    const float gu = R.colsum(Ur, dv_);  // (U^T do)[c]
     const float bq = tid < D ? qv[tid] : 0.0f, bg = tid < D ? gu : 0.0f;
     float x = cc.c * bq, xp = 0.0f, y = cc.c * bg, yp = 0.0f;
     for (int i = 1; i < cc.iters; ++i) {
