@@ -26,11 +26,23 @@ bool chunk_supported(int dtype, int D, int C) {
 }
 size_t elem_bytes(int dtype) { return dtype == GKA_BF16 ? 2 : 4; }
 
+// The kernels address the rows of one chunk (at most 64 tokens) of one head with 32-bit byte
+// offsets from the chunk's first row, across the H heads of a token: the D-element rows of q, k,
+// v, o and, in the residual mode, the (iters + 1)-float residual rows. Those spans must stay
+// below 2^31 bytes (an offset of 2^31 or more is the kernels' marker for a dropped store).
+bool row_spans_fit(const gka_params* p) {
+  return 64LL * p->H * p->D * (long long)elem_bytes(p->dtype) < (1LL << 31);
+}
+bool resid_rows_fit(const gka_params* p) {
+  return 64LL * p->H * (p->iters + 1) * 4LL < (1LL << 31);
+}
+
 gka_status check_common(const gka_params* p) {
   if (!p) return GKA_ERR_NULL;
   if (p->dtype != GKA_BF16 && p->dtype != GKA_FP32) return GKA_ERR_DTYPE;
   if (p->B < 1 || p->H < 1 || !dims_supported(p->dtype, p->D)) return GKA_ERR_SHAPE;
   if ((long long)p->B * p->H > (1LL << 30)) return GKA_ERR_SHAPE;
+  if (!row_spans_fit(p)) return GKA_ERR_SHAPE;
   if (!(p->a > 0.0f) || !std::isfinite(p->a)) return GKA_ERR_VALUE;
   if (p->iters < 1 || p->iters > GKA_MAX_ITERS) return GKA_ERR_VALUE;
   return GKA_OK;
@@ -269,6 +281,7 @@ gka_status gka_fwd_chunked_residuals(const gka_params* p, const void* q, const v
                                      size_t workspace_bytes, void* stream) {
   gka_status st = check_fwd(p);
   if (st != GKA_OK) return st;
+  if (!resid_rows_fit(p)) return GKA_ERR_SHAPE;
   if (p->T > 0 && !resid) return GKA_ERR_NULL;
   return fwd_impl(p, nullptr, -1, q, k, v, gamma, beta, o, h_state, u_state, hnorm2, hnorm_t,
                   resid, workspace, workspace_bytes, stream, nullptr);
@@ -518,6 +531,7 @@ gka_status gka_bwd(const gka_params* p, const void* q, const void* k, const void
 gka_status gka_step_residuals(const gka_params* p, const void* q, const void* k, const void* v,
                               const float* gamma, const float* beta, void* o, float* h_state,
                               float* u_state, float* hnorm2, float* resid, void* stream) {
+  if (p && check_common(p) == GKA_OK && !resid_rows_fit(p)) return GKA_ERR_SHAPE;
   if (!resid && p) {
     const gka_status st = check_common(p);
     return st != GKA_OK ? st : GKA_ERR_NULL;

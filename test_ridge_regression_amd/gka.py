@@ -110,8 +110,12 @@ def _ptr(t: Optional[torch.Tensor]):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _require_io(q, k, v, gamma, o, state):
-    """Marshalling checks the C side cannot make: dense tensors of matching element types."""
+def _require_io(q, k, v, gamma, o, state, gamma_shape, n_states):
+    """Marshalling checks the C side cannot make, in this order: dense tensors of matching
+    element types, the shapes of gamma (``gamma_shape``) and of the carried state (``n_states``
+    heads' worth: h, u [n_states..., D, D], n2 [n_states...]), and that every tensor lives on
+    q's CUDA device. A host tensor would hand a host pointer to a kernel, and a short gamma or
+    state would be read (the state also written) past its end; neither is visible from C."""
     ts = [q, k, v, gamma, o] + ([state.h, state.u, state.n2] if state is not None else [])
     for t in ts:
         if not t.is_contiguous():
@@ -123,6 +127,24 @@ def _require_io(q, k, v, gamma, o, state):
         raise ValueError("gamma and the state are float32")
     if k.shape != q.shape or v.shape != q.shape or o.shape != q.shape:
         raise ValueError("q, k, v, o must have the same shape")
+    if tuple(gamma.shape) != tuple(gamma_shape):
+        raise ValueError(f"gamma must have shape {tuple(gamma_shape)}, got {tuple(gamma.shape)}")
+    if state is not None:
+        D = q.shape[-1]
+        n = tuple(n_states)
+        if (tuple(state.h.shape) != n + (D, D) or tuple(state.u.shape) != n + (D, D)
+                or tuple(state.n2.shape) != n):
+            raise ValueError(f"state must be h, u {n + (D, D)} and n2 {n}")
+    _require_device(q, ts)
+
+
+def _require_device(q, ts):
+    """Every tensor in ``ts`` (None entries skipped) on q's device, which must be a GPU."""
+    if not q.is_cuda:
+        raise ValueError("libgka takes GPU (device) tensors")
+    for t in ts:
+        if t is not None and (not t.is_cuda or t.device != q.device):
+            raise ValueError(f"every tensor must be on {q.device}; got one on {t.device}")
 
 
 def _require_beta(beta, shape):
@@ -185,12 +207,13 @@ def fwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.
     B, T, H, D = q.shape
     p = make_params(B, T, H, D, chunk, iters, a, _dtype_code(q), segments)
     o = torch.empty_like(q) if out is None else out
-    _require_io(q, k, v, gamma, o, state)
+    _require_io(q, k, v, gamma, o, state, (B, T, H), (B, H))
     _require_beta(beta, (B, T, H))
     hn = torch.empty(B, T, H, device=q.device, dtype=torch.float32) if return_hnorm else None
     need = int(lib.gka_fwd_workspace_bytes(ctypes.byref(p)))
     if workspace is None and need > 0:
         workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    _require_device(q, [beta, workspace])
     rest = (_ptr(o), _ptr(state.h if state else None), _ptr(state.u if state else None),
             _ptr(state.n2 if state else None), _ptr(hn), _ptr(workspace),
             ctypes.c_size_t(workspace.numel() if workspace is not None else 0),
@@ -219,8 +242,9 @@ def step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor,
     B, H, D = q.shape
     p = make_params(B, 1, H, D, 64, iters, a, _dtype_code(q))
     o = torch.empty_like(q) if out is None else out
-    _require_io(q, k, v, gamma, o, state)
+    _require_io(q, k, v, gamma, o, state, (B, H), (B, H))
     _require_beta(beta, (B, H))
+    _require_device(q, [beta])
     rest = (_ptr(o), _ptr(state.h), _ptr(state.u), _ptr(state.n2), _stream(stream))
     if beta is None:
         st = lib.gka_step(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), *rest)
@@ -250,7 +274,7 @@ def fwd_chunked_residuals(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     B, T, H, D = q.shape
     p = make_params(B, T, H, D, chunk, iters, a, _dtype_code(q), segments)
     o = torch.empty_like(q) if out is None else out
-    _require_io(q, k, v, gamma, o, state)
+    _require_io(q, k, v, gamma, o, state, (B, T, H), (B, H))
     _require_beta(beta, (B, T, H))
     if resid is None:
         resid = torch.empty(B, T, H, iters + 1, device=q.device, dtype=torch.float32)
@@ -261,6 +285,7 @@ def fwd_chunked_residuals(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor,
     need = int(lib.gka_fwd_workspace_bytes(ctypes.byref(p)))
     if workspace is None and need > 0:
         workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    _require_device(q, [beta, resid, workspace])
     st = lib.gka_fwd_chunked_residuals(
         ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(beta), _ptr(o),
         _ptr(state.h if state else None), _ptr(state.u if state else None),
@@ -279,8 +304,9 @@ def step_residuals(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: tor
     B, H, D = q.shape
     p = make_params(B, 1, H, D, 64, iters, a, _dtype_code(q))
     o = torch.empty_like(q) if out is None else out
-    _require_io(q, k, v, gamma, o, state)
+    _require_io(q, k, v, gamma, o, state, (B, H), (B, H))
     _require_beta(beta, (B, H))
+    _require_device(q, [beta])
     resid = torch.empty(B, H, iters + 1, device=q.device, dtype=torch.float32)
     st = lib.gka_step_residuals(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma),
                                 _ptr(beta), _ptr(o), _ptr(state.h), _ptr(state.u),
@@ -306,14 +332,13 @@ def fwd_varlen(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.T
     total = rows if total is None else int(total)
     p = make_params(B, max_seqlen, H, D, chunk, iters, a, _dtype_code(q), segments)
     o = torch.empty_like(q) if out is None else out
-    _require_io(q, k, v, gamma, o, state)
+    _require_io(q, k, v, gamma, o, state, (rows, H), (B, H))
     _require_beta(beta, (rows, H))
-    if tuple(gamma.shape) != (rows, H):
-        raise ValueError("gamma must be [total, H]")
     hn = torch.empty(rows, H, device=q.device, dtype=torch.float32) if return_hnorm else None
     need = int(lib.gka_fwd_varlen_workspace_bytes(ctypes.byref(p)))
     if workspace is None and need > 0:
         workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    _require_device(q, [cu_seqlens, beta, workspace])
     st = lib.gka_fwd_varlen(
         ctypes.byref(p), _ptr(cu_seqlens), ctypes.c_int64(total), _ptr(q), _ptr(k), _ptr(v),
         _ptr(gamma), _ptr(beta), _ptr(o), _ptr(state.h if state else None),
@@ -333,7 +358,7 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor,
     B, T, H, D = q.shape
     p = make_params(B, T, H, D, 64, iters, a, _dtype_code(q))
     dq, dk, dv = torch.empty_like(q), torch.empty_like(q), torch.empty_like(q)
-    _require_io(q, k, v, gamma, dq, None)
+    _require_io(q, k, v, gamma, dq, None, (B, T, H), (B, H))
     if dout.shape != q.shape or dout.dtype != q.dtype or not dout.is_contiguous():
         raise ValueError("dout must match q")
     _require_beta(beta, (B, T, H))
@@ -342,6 +367,7 @@ def bwd(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor,
     need = int(lib.gka_bwd_workspace_bytes(ctypes.byref(p)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
+    _require_device(q, [dout, beta, workspace])
     st = lib.gka_bwd(ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(beta),
                      _ptr(dout), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(dgamma), _ptr(dbeta),
                      _ptr(workspace), ctypes.c_size_t(workspace.numel()), _stream(stream))

@@ -283,3 +283,111 @@ def test_backward_entry_point_checks(lib):
     assert bw(p, ws=None) == 5
     assert bw(p, wsb=need - 1) == 5
     assert bw(params(T=0), q=None, dq=None) == 0
+
+
+class _NoGpuLib:
+    """Stands in for libgka.so: the binding must reject the call before any entry point runs.
+    Only the workspace queries (pure host functions) answer."""
+
+    def gka_fwd_workspace_bytes(self, p):
+        return 0
+
+    def gka_fwd_varlen_workspace_bytes(self, p):
+        return 0
+
+    def gka_bwd_workspace_bytes(self, p):
+        return 0
+
+    def __getattr__(self, name):
+        raise AssertionError(f"{name} reached with arguments the binding should have rejected")
+
+
+@pytest.fixture
+def stub_lib():
+    saved = gka._lib
+    gka._lib = _NoGpuLib()
+    try:
+        yield
+    finally:
+        gka._lib = saved
+
+
+def test_binding_rejects_host_tensors_and_bad_shapes(stub_lib):
+    """Host (CPU) tensors would hand host pointers to the kernels; a short gamma or state would
+    be read (and the state written) past its end. The binding raises ValueError for each before
+    any library call (the stub fails the test if one is reached)."""
+    import torch
+    B, T, H, D = 1, 64, 2, 32
+    q = torch.zeros(B, T, H, D, dtype=torch.bfloat16)
+    g = torch.ones(B, T, H)
+    st = gka.GkaState(torch.zeros(B, H, D, D), torch.zeros(B, H, D, D), torch.zeros(B, H))
+    with pytest.raises(ValueError, match="GPU"):  # right shapes, host memory
+        gka.fwd_chunked(q, q, q, g, 0.1, 4, 64, state=st)
+    with pytest.raises(ValueError, match="gamma"):
+        gka.fwd_chunked(q, q, q, torch.ones(B, T, 1), 0.1, 4, 64)
+    with pytest.raises(ValueError, match="state"):
+        bad = gka.GkaState(torch.zeros(B, H, D, D), torch.zeros(B, H, D, D // 2), torch.zeros(B, H))
+        gka.fwd_chunked(q, q, q, g, 0.1, 4, 64, state=bad)
+    with pytest.raises(ValueError, match="state"):
+        bad = gka.GkaState(torch.zeros(B, 1, D, D), torch.zeros(B, 1, D, D), torch.zeros(B, 1))
+        gka.fwd_chunked(q, q, q, g, 0.1, 4, 64, state=bad)
+    with pytest.raises(ValueError, match="state"):
+        bad = gka.GkaState(torch.zeros(B, H, D, D), torch.zeros(B, H, D, D), torch.zeros(B, H, 1))
+        gka.fwd_chunked_residuals(q, q, q, g, 0.1, 4, 64, state=bad)
+    # decode: gamma [B, H] and the state
+    q1 = torch.zeros(B, H, D, dtype=torch.bfloat16)
+    with pytest.raises(ValueError, match="GPU"):
+        gka.step(q1, q1, q1, torch.ones(B, H), 0.1, 4, st)
+    with pytest.raises(ValueError, match="gamma"):
+        gka.step(q1, q1, q1, torch.ones(B, H, 1), 0.1, 4, st)
+    with pytest.raises(ValueError, match="gamma"):
+        gka.step_residuals(q1, q1, q1, torch.ones(B), 0.1, 4, st)
+    # packed batches: gamma [total, H]; one state per sequence
+    qp = torch.zeros(10, H, D, dtype=torch.bfloat16)
+    cu = torch.tensor([0, 4, 10], dtype=torch.int32)
+    with pytest.raises(ValueError, match="gamma"):
+        gka.fwd_varlen(qp, qp, qp, torch.ones(9, H), cu, 6, 0.1, 4)
+    with pytest.raises(ValueError, match="state"):
+        gka.fwd_varlen(qp, qp, qp, torch.ones(10, H), cu, 6, 0.1, 4, state=st)  # B = 2 sequences
+    with pytest.raises(ValueError, match="GPU"):
+        gka.fwd_varlen(qp, qp, qp, torch.ones(10, H), cu, 6, 0.1, 4)
+    # backward
+    with pytest.raises(ValueError, match="gamma"):
+        gka.bwd(q, q, q, torch.ones(B, T), q, 0.1, 4)
+    with pytest.raises(ValueError, match="GPU"):
+        gka.bwd(q, q, q, g, q, 0.1, 4)
+
+
+def test_binding_device_check_names_the_foreign_tensor():
+    import torch
+    q = torch.zeros(2, 3)
+    with pytest.raises(ValueError, match="GPU"):
+        gka._require_device(q, [q])
+
+
+def test_row_spans_past_32_bit_offsets_are_rejected(lib):
+    """The kernels address one chunk's 64 token rows of every head with 32-bit byte offsets:
+    head counts whose row span reaches 2^31 bytes are refused on the host."""
+    P = ctypes.byref
+    # bf16 D = 128: 64 * H * 256 bytes < 2^31  <=>  H < 131072
+    ok, bad = params(B=1, H=131071, D=128, T=64), params(B=1, H=131072, D=128, T=64)
+    assert fwd(lib, bad) == 2
+    assert lib.gka_fwd_workspace_bytes(P(bad)) == 0
+    assert step(lib, bad) == 2
+    # (the accepted one passes the shape checks and stops at the missing gamma)
+    assert fwd(lib, ok, g=None) == 1
+    # float32 D = 128 (chunk 16): 64 * H * 512 bytes
+    assert fwd(lib, params(B=1, H=65536, D=128, T=16, chunk=16, dtype_code=gka.GKA_FP32)) == 2
+    # the residual rows: 64 * H * (iters + 1) * 4 bytes < 2^31; at iters = 64 that is
+    # H <= 129055 (D = 16 keeps the q, k, v rows small)
+    # (gamma NULL: a call that passes the shape checks stops at GKA_ERR_NULL, never launches)
+    res = lambda p: lib.gka_fwd_chunked_residuals(P(p), VP[0], VP[1], VP[2], None, None, VP[4],
+                                                  None, None, None, None, VP[8], None,
+                                                  ctypes.c_size_t(0), None)
+    sres = lambda p: lib.gka_step_residuals(P(p), VP[0], VP[1], VP[2], None, None, VP[4], VP[5],
+                                            VP[6], VP[7], VP[8], None)
+    assert res(params(B=1, H=129056, D=16, T=64, chunk=32, iters=64)) == 2
+    assert sres(params(B=1, H=129056, D=16, iters=64)) == 2
+    assert sres(params(B=1, H=129055, D=16, iters=64)) == 1
+    assert res(params(B=1, H=129055, D=16, T=64, chunk=32, iters=64, segments=1)) == 1  # no gamma
+    assert fwd(lib, params(B=1, H=129056, D=16, T=64, chunk=32, iters=64), g=None) == 1
