@@ -132,8 +132,9 @@ def bench_prefill(W, inputs, steps, warmup, ev, beta=None, what="prefill"):
     need = gka.workspace_bytes(W.B, W.T, W.H, W.D, W.chunk, W.iters, W.a, gka.GKA_BF16)
     ws = torch.empty(max(need, 1), device="cuda", dtype=torch.uint8)
     stream = torch.cuda.current_stream()
-    phase = ev.create(4 * steps)
-    arrs = [(ctypes.c_void_p * 4)(*phase[4 * i:4 * i + 4]) for i in range(steps)]
+    NP = 5  # phase events per call: summaries, scan, walk, output pass, end
+    phase = ev.create(NP * steps)
+    arrs = [(ctypes.c_void_p * NP)(*phase[NP * i:NP * i + NP]) for i in range(steps)]
     t0, t1 = ev.create(2)
     call = lambda **kw: gka.fwd_chunked(qd, kd, vd, gd, W.a, W.iters, W.chunk, out=o,
                                         workspace=ws, beta=beta, **kw)
@@ -155,13 +156,13 @@ def bench_prefill(W, inputs, steps, warmup, ev, beta=None, what="prefill"):
     for i in range(steps):
         call(phase_events=arrs[i])
     torch.cuda.synchronize()
-    walk = [ev.elapsed_ms(phase[4 * i + 2], phase[4 * i + 3]) for i in range(steps)]
-    summ = [ev.elapsed_ms(phase[4 * i + 0], phase[4 * i + 1]) for i in range(steps)]
-    scan = [ev.elapsed_ms(phase[4 * i + 1], phase[4 * i + 2]) for i in range(steps)]
+    span = lambda a, b: float(np.mean([ev.elapsed_ms(phase[NP * i + a], phase[NP * i + b])
+                                        for i in range(steps)]))
+    rec = dict(total_ms=total_ms, ms_per_step=total_ms / steps, summary_ms=span(0, 1),
+               scan_ms=span(1, 2), walk_ms=span(2, 3), output_ms=span(3, 4), segments=_segments(W),
+               o=o)
     ev.destroy(phase + [t0, t1])
-    segs = _segments(W)
-    return dict(total_ms=total_ms, ms_per_step=total_ms / steps, walk_ms=float(np.mean(walk)),
-                summary_ms=float(np.mean(summ)), scan_ms=float(np.mean(scan)), segments=segs, o=o)
+    return rec
 
 
 def bench_residuals(W, inputs, steps, warmup, ev, sweep=(0.1, 0.05, 0.02)):
@@ -300,9 +301,11 @@ def bench_backward(W, inputs, steps, warmup, ev):
 
 def _segments(W):
     from test_ridge_regression_amd import gka
-    # the plan's segment count: workspace = B*H*S*(2 D^2 + 1)*4 + B*H*4 (rounded up to 256)
+    # the plan's segment count: workspace = [B*H*S*(2 D^2 + 1)*4 + B*H*4] (S > 1) + B*T*H*4
+    # (the per-token factors of bf16 with chunks of 64), each rounded up to 256 bytes
     need = gka.workspace_bytes(W.B, W.T, W.H, W.D, W.chunk, W.iters, W.a, gka.GKA_BF16)
-    if need == 0:
+    need -= (W.B * W.T * W.H * 4 + 255) // 256 * 256
+    if need <= 0:
         return 1
     bh = W.B * W.H
     return int((need - bh * 4) // (bh * (2 * W.D * W.D + 1) * 4))

@@ -12,7 +12,7 @@ namespace {
 using gka::ChebConsts;
 using gka::FwdPlan;
 
-constexpr int kAbiVersion = 6;
+constexpr int kAbiVersion = 7;
 constexpr int kCUs = 256;  // MI355X compute units: the segment plan aims at one workgroup per CU
 
 bool dims_supported(int dtype, int D) {
@@ -140,6 +140,8 @@ bool make_plan(const gka_params* p, FwdPlan& pl, bool packed = false) {
   pl.C = p->chunk;
   pl.dtype = p->dtype;
   pl.N = (p->T + p->chunk - 1) / p->chunk;
+  pl.split = false;
+  pl.phi_off = pl.order_off = 0;
   if (pl.N == 0) {
     pl.S = pl.J = 0;
     pl.ws_bytes = 0;
@@ -173,6 +175,13 @@ bool make_plan(const gka_params* p, FwdPlan& pl, bool packed = false) {
                   + bh * pl.S * sizeof(float)          // per-segment log2 gate product
                   + bh * sizeof(float);                // ||H||^2 at the start of segment 0
     pl.ws_bytes = (pl.ws_bytes + 255) & ~(size_t)255;
+  }
+  // token walk + output pass: phi_t of every (row, head), rows = B T (packed: T bounds every
+  // sequence, so B T bounds the rows)
+  pl.split = gka::walk_tok_supported(pl);
+  pl.phi_off = pl.ws_bytes;
+  if (pl.split) {
+    pl.ws_bytes += ((size_t)p->B * p->T * p->H * sizeof(float) + 255) & ~(size_t)255;
   }
   if (packed && p->B <= gka::kMaxOrdered) {  // the dispatch order, after the segment states
     pl.order_off = pl.ws_bytes;
@@ -336,6 +345,8 @@ gka_status fwd_impl(const gka_params* p, const int32_t* cu, int64_t total, const
 
   const ChebConsts cc = cheb_consts(p->a, p->iters);
   hipStream_t s = static_cast<hipStream_t>(stream);
+  float* phi = pl.split ? reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.phi_off)
+                        : nullptr;
   auto mark = [&](int i) {
     if (phase_events && phase_events[i])
       return hipEventRecord(static_cast<hipEvent_t>(phase_events[i]), s) == hipSuccess;
@@ -357,19 +368,28 @@ gka_status fwd_impl(const gka_params* p, const int32_t* cu, int64_t total, const
   }
   wa.o = o;
   wa.hnorm_t = hnorm_t;
-  if (pl.S == 1) {
-    wa.in_h = h_state;
-    wa.in_u = u_state;
-    wa.in_bh = DD;
-    wa.in_seg = 0;
-    wa.n2_in = hnorm2;
+  wa.phi = phi;
+  // the fused walk (or, split, the token walk and then the output pass) from the segment-start
+  // states in (in_h, in_u, n2_in, with strides in_bh, in_seg)
+  auto walk = [&](const float* in_h, const float* in_u, long long in_bh, long long in_seg,
+                  const float* n2_in) -> gka_status {
+    wa.in_h = in_h;
+    wa.in_u = in_u;
+    wa.in_bh = in_bh;
+    wa.in_seg = in_seg;
+    wa.n2_in = n2_in;
     wa.out_h = h_state;
     wa.out_u = u_state;
     wa.n2_out = hnorm2;
-    if (!mark(0) || !mark(1) || !mark(2)) return GKA_ERR_HIP;
     if (gka::launch_walk(pl, false, wa, cc, s) != hipSuccess) return GKA_ERR_HIP;
     if (!mark(3)) return GKA_ERR_HIP;
+    if (pl.split && gka::launch_output(pl, wa, s) != hipSuccess) return GKA_ERR_HIP;
+    if (!mark(4)) return GKA_ERR_HIP;
     return GKA_OK;
+  };
+  if (pl.S == 1) {
+    if (!mark(0) || !mark(1) || !mark(2)) return GKA_ERR_HIP;
+    return walk(h_state, u_state, DD, 0, hnorm2);
   }
   const size_t bh = (size_t)p->B * p->H;
   float* ws_states = static_cast<float*>(workspace);
@@ -388,17 +408,7 @@ gka_status fwd_impl(const gka_params* p, const int32_t* cu, int64_t total, const
       hipSuccess)
     return GKA_ERR_HIP;
   if (!mark(2)) return GKA_ERR_HIP;
-  wa.in_h = ws_states;
-  wa.in_u = ws_states + DD;
-  wa.in_bh = (long long)pl.S * 2 * DD;
-  wa.in_seg = 2 * DD;
-  wa.n2_in = ws_n2;
-  wa.out_h = h_state;
-  wa.out_u = u_state;
-  wa.n2_out = hnorm2;
-  if (gka::launch_walk(pl, false, wa, cc, s) != hipSuccess) return GKA_ERR_HIP;
-  if (!mark(3)) return GKA_ERR_HIP;
-  return GKA_OK;
+  return walk(ws_states, ws_states + DD, (long long)pl.S * 2 * DD, 2 * DD, ws_n2);
 }
 
 gka_status step_impl(const gka_params* p, const void* q, const void* k, const void* v,

@@ -350,6 +350,22 @@ __device__ inline float wave_sum(float x) {
   return x;
 }
 
+__device__ inline float wave_max(float x) {
+#pragma unroll
+  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, kWave));
+  return x;
+}
+
+// ---- exact power-of-two scales (range of the 16-bit matrix operands) ----------------------
+// floor(log2 x) for x > 0, clamped to [-lim, lim] (subnormal x gives -lim, infinity lim); 0 for
+// x = 0 or NaN, where any scale serves
+__device__ inline int pow2_exponent(float x, int lim) {
+  const int e = (int)((__float_as_uint(x) >> 23) & 0xffu) - 127;
+  return x > 0.0f ? min(max(e, -lim), lim) : 0;
+}
+// 2^e as a float, for -126 <= e <= 127
+__device__ inline float exp2_int(int e) { return __uint_as_float((uint32_t)(e + 127) << 23); }
+
 // log2 of a gate with a finite floor for gamma = 0, so that differences of prefix sums stay
 // finite; 2^x for x at or below the floor underflows to exactly 0 in float32.
 constexpr float kLog2GateFloor = -160.0f;

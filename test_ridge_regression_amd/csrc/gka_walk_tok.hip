@@ -1,12 +1,17 @@
-// Chunk walk of gka_fwd_chunked with token-owning waves (bf16 inputs, chunks of 64 tokens).
+// Chunk walk of gka_fwd_chunked with token-owning waves (bf16 inputs, chunks of 64 tokens): the
+// key-side recurrence and the Chebyshev solves. The value side (o_t = U_t x_t and the carry of U)
+// is the output pass of gka_out.hip, which reads the solves this walk leaves in o's rows.
 //
-// The chunk algebra is the one of the feature-split walk in gka_fwd.hip ("Methodology in Plain
-// English" and "Key Contributions" 3 on the ai.info summary of arXiv 2511.21016): per chunk,
+// The chunk algebra follows "Methodology in Plain English" and "Key Contributions" 3 on the
+// ai.info summary of arXiv 2511.21016: per chunk,
 //   Y_t   = s_t H0hat R_t + sum_{s<=t} Mhat_ts (k_s . R_t) k_s    (the system minus a I, on R_t)
-//   n_t^2 = gamma_t^2 n_{t-1}^2 + 2 gamma_t k_t^T H_{t-1} k_t + ||k_t||^4   (affine scan over t)
-//   o_t   = s_t U0hat X_t + sum_{s<=t} Mhat_ts (k_s . X_t) v_s
-//   carry H <- Gam_C H + K^T diag(w) K,  U^T <- Gam_C U^T + K^T diag(w) V
-// with H0hat = H0 / n0, U0hat = U0 / n0, s_t = Gam_t n0 / n_t, Mhat_ts = 2^(cl_t - cl_s) / n_t.
+//   n_t^2 = gamma_t^2 n_{t-1}^2 + 2 gamma_t beta_t k_t^T H_{t-1} k_t + beta_t^2 ||k_t||^4
+//           (an affine scan over t)
+//   carry H <- Gam_C H + K^T diag(w) K
+// with H0hat = H0 / n0, s_t = Gam_t n0 / n_t, Mhat_ts = 2^(cl_t - cl_s) beta_s / n_t and carry
+// weights w_s = 2^(cl_C - cl_s) beta_s. beta_t is the optional write gate ("Main Findings" on the
+// ai.info summary: H_t = gamma_t H_{t-1} + beta_t k_t k_t^T; 1 without it); it enters only
+// through these weights, so the key rows stay exact operands.
 //
 // Every token's Chebyshev iteration is a system of its own: Y_t needs R_t and the chunk's
 // shared matrices (H0hat, K), nothing of the other tokens' iterates. Wave w (one per SIMD)
@@ -19,19 +24,22 @@
 // for index 16 (j / 4) + 4 g + j % 4. The accumulator of a 16x16 output tile holds, in lane
 // (column c, group g), rows 4g..4g+3; with this order the B fragment of block kk of a
 // feature x token matrix is the accumulator rows of tiles 2kk and 2kk+1 of the same lane.
-// The A operands are laid out to match: K and H0hat (U0hat) are staged in LDS with their
-// feature columns permuted the same way (a fragment is one 16-byte read), and K^T / V^T
-// fragments in the permuted token order come from transposing LDS reads.
+// The A operands are laid out to match: K and H0hat are staged in LDS with their feature columns
+// permuted the same way (a fragment is one 16-byte read), and K^T fragments in the permuted token
+// order come from transposing LDS reads.
 //
-// With the optional write gate beta_t ("Main Findings" on the ai.info summary: H_t = gamma_t
-// H_{t-1} + beta_t k_t k_t^T, likewise U_t) everything above holds for the rows sqrt(beta_t) k_t
-// and sqrt(beta_t) v_t, which is what the staging writes.
+// Range of the 16-bit operands: the keys of a chunk are staged times 2^-e (e from the chunk's
+// largest |k|, so the staged rows lie below 2) and the queries of a token times 2^-e_t; both are
+// exact powers of two, undone in float32 where the products are used (norm terms, mask, carry
+// weights) or carried into the solve's own scale. Any bf16 input whose squares stay in float32's
+// range is therefore an fp16 operand of full precision.
 //
-// Per chunk: stage K, V (fp16), gates and H0hat; the norm phase (k_t^T H0hat k_t from the
-// resident H0hat fragments, the Gram tiles of the own tokens) and a scan over the 64 tokens;
-// U0hat is staged; the carry advances the float32 state (held as accumulator tiles, a quarter
-// per wave); the Chebyshev loop; the output products. The next chunk's K, V and gates are
-// loaded into registers during the output phase and staged at the top of the next chunk.
+// Per chunk: stage K (fp16), gates and H0hat; the norm phase (k_t^T H0hat k_t from the resident
+// H0hat fragments, the Gram tiles of the own tokens) and a scan over the 64 tokens; the carry
+// advances the float32 H state (held as accumulator tiles, a quarter per wave); the next chunk's
+// keys and gates are loaded into registers; the Chebyshev loop; the solve of every token is
+// written, scaled to lie below 2 in magnitude, as fp16 to its row of o, with its scale over
+// ||H_t||_F in a per-token float.
 #include "gka_internal.hpp"
 
 #include <type_traits>
@@ -51,7 +59,7 @@ struct TokCfg {
   static constexpr int NST = FT * FT / NW;   // state tiles per wave
   static constexpr int NRT = NST >= FT ? NST / FT : 1;  // state row tiles per wave
   static constexpr int NCT = NST >= FT ? FT : NST;      // state column tiles per wave
-  static constexpr int LDD = D + 8;          // row stride of the [*][D] fp16 / bf16 tiles
+  static constexpr int LDD = D + 8;          // row stride of the [*][D] fp16 tiles
   static constexpr bool PIN = D >= 128;      // resident fragments and state in AGPRs
   static constexpr int VEC = 8;              // bf16 elements per 16-byte unit
   static constexpr int UPR = D / VEC;        // units per token row
@@ -59,13 +67,11 @@ struct TokCfg {
   static constexpr size_t szTok = (size_t)C * LDD * 2;
   static constexpr size_t szHs = (size_t)D * LDD * 2;
   static constexpr size_t oKp = 0;               // K, token-major, permuted features (fp16)
-  static constexpr size_t oVp = oKp + szTok;     // V, token-major (fp16)
-  static constexpr size_t oHs = oVp + szTok;     // H0hat, then U0hat: row-major, permuted columns
-  static constexpr int LDC = C + 8;              // row stride of the [D][C] fp16 tile
-  static constexpr size_t oVT = oHs + szHs;      // V^T: row-major, tokens permuted (fp16)
-  static constexpr size_t oUs = oVT + (size_t)D * LDC * 2;  // float32 U^T state, tile-major
-  static constexpr size_t oVec = oUs + (size_t)D * D * sizeof(float);
-  static constexpr size_t szVec = (size_t)(4 * C + 16 + 4 * 64) * sizeof(float);
+  static constexpr size_t oHs = oKp + szTok;     // H0hat: row-major, permuted columns (fp16)
+  static constexpr size_t oKraw = oHs + szHs;    // the next chunk's key rows as loaded (bf16)
+  static constexpr size_t oGraw = oKraw + (size_t)C * D * 2;  // its gates, write gates [C]
+  static constexpr size_t oVec = oGraw + (size_t)2 * C * sizeof(float);
+  static constexpr size_t szVec = (size_t)(5 * C + 16 + 4 * 64) * sizeof(float);
   static constexpr size_t bytes = oVec + szVec;  // dynamic LDS
   static_assert(D % 32 == 0 && NST >= 1, "unsupported D");
   static_assert(NU % NT == 0, "staging units must fill whole workgroups");
@@ -121,20 +127,20 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
   typedef f16x8 Frag;
   constexpr int C = Cfg::C, NW = Cfg::NW, NT = Cfg::NT, FT = Cfg::FT, KD = Cfg::KD;
   constexpr int KC = Cfg::KC, ST = Cfg::ST, LDD = Cfg::LDD, UPR = Cfg::UPR, NU = Cfg::NU;
-  constexpr int LDC = Cfg::LDC;
-  constexpr int NST = Cfg::NST, NRT = Cfg::NRT, NCT = Cfg::NCT;
+  constexpr int NRT = Cfg::NRT, NCT = Cfg::NCT;
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   f16* Kp = reinterpret_cast<f16*>(smem + Cfg::oKp);
-  f16* Vp = reinterpret_cast<f16*>(smem + Cfg::oVp);
   f16* Hs = reinterpret_cast<f16*>(smem + Cfg::oHs);
-  f16* VT = reinterpret_cast<f16*>(smem + Cfg::oVT);
-  float* Us = reinterpret_cast<float*>(smem + Cfg::oUs);
+  const bf16x8* Kraw = reinterpret_cast<const bf16x8*>(smem + Cfg::oKraw);  // unit u at [u]
+  const float* Graw = reinterpret_cast<const float*>(smem + Cfg::oGraw);    // [C] gates
+  const float* Braw = Graw + C;                                               // [C] write gates
   float* v_cl = reinterpret_cast<float*>(smem + Cfg::oVec);  // [C] in-chunk log2 gate prefix
-  float* v_w = v_cl + C;    // [C] carry weights 2^(cl_C - cl_s)
+  float* v_w = v_cl + C;    // [C] carry weights 2^(cl_C - cl_s) beta_s
   float* v_a = v_w + C;     // [C] n^2 scan: a_t = gamma_t^2
   float* v_b = v_a + C;     // [C] n^2 scan: b_t
-  float* v_sc = v_b + C;    // [16] scratch
+  float* v_bt = v_b + C;    // [C] write gates beta_s (1 without them)
+  float* v_sc = v_bt + C;   // [16] scratch: [0, NW) state norms, [4, 4 + NW) largest |k| per wave
   float* v_coef = v_sc + 16;  // [iters][4] krs, kys, bts of each iteration (rescaled form)
 
   const int seg = blockIdx.x;
@@ -164,40 +170,30 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
   const int c_begin = seg * J;
   const int c_end = min(min(N, c_begin + J), (Tlen + C - 1) / C);
   const long long tok_stride = (long long)Hn * D;
-  const uint32_t tok_bytes = (uint32_t)Hn * D * 2u;  // < 2^25: 64 rows fit a 32-bit offset
+  const uint32_t tok_bytes = (uint32_t)Hn * D * 2u;  // 64 rows span < 2^31 bytes (host check)
   const bf16* qg = static_cast<const bf16*>(A.q);
   const bf16* kg = static_cast<const bf16*>(A.k);
-  const bf16* vg = static_cast<const bf16*>(A.v);
-  bf16* og = static_cast<bf16*>(A.o);
+  f16* yg = static_cast<f16*>(A.o);  // the solves (fp16) go to o's rows; the output pass reads
+                                     // them back and writes o over them
 
-  // ---- float32 state: tiles (a0 + jr, b0 + jc) of H and of U^T (rows = key features). H is
-  // held in registers; U^T in LDS, where each wave only ever touches its own tiles (one f32x4
-  // per lane and tile, tile-major), which frees the registers for resident K^T fragments ------
-  auto us_tile = [&](int jr, int jc) {
-    return reinterpret_cast<f32x4*>(Us) + ((jr * NCT + jc) * NW + wave) * kWave + lane;
-  };
+  // ---- float32 state: tiles (a0 + jr, b0 + jc) of H, held in registers ----------------------
   f32x4 Hst[NRT][NCT];
 #pragma unroll
   for (int jr = 0; jr < NRT; ++jr)
 #pragma unroll
-    for (int jc = 0; jc < NCT; ++jc) {
-      Hst[jr][jc] = f32x4{0.f, 0.f, 0.f, 0.f};
-      *us_tile(jr, jc) = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
+    for (int jc = 0; jc < NCT; ++jc) Hst[jr][jc] = f32x4{0.f, 0.f, 0.f, 0.f};
   float n0sq = 0.0f;
   {
     float sq = 0.0f;
     if (A.in_h) {
       const float* ih = A.in_h + bh * A.in_bh + seg * A.in_seg;
-      const float* iu = A.in_u + bh * A.in_bh + seg * A.in_seg;
 #pragma unroll
       for (int jr = 0; jr < NRT; ++jr)
 #pragma unroll
         for (int jc = 0; jc < NCT; ++jc) {
-          // H[r..r+3][c] is read as H[c][r..r+3] (symmetric); U^T[r..r+3][c] = U[c][r..r+3]
+          // H[r..r+3][c] is read as H[c][r..r+3] (symmetric)
           const size_t o = (size_t)(16 * (b0 + jc) + lr) * D + 16 * (a0 + jr) + 4 * lg;
           Hst[jr][jc] = *reinterpret_cast<const f32x4*>(ih + o);
-          *us_tile(jr, jc) = *reinterpret_cast<const f32x4*>(iu + o);
           const f32x4 x = Hst[jr][jc];
           sq += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
         }
@@ -220,39 +216,52 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
     }
   }
 
-  // The next chunk's K and V (16-byte units, consecutive threads along a token row) and gates
-  // (lane = token) are loaded into registers at the start of the output phase, where few
-  // registers are live, and staged at the top of the next chunk. Rows past the end of the
-  // sequence are zero, with gate 1.
-  bf16x8 kin[NU / NT], vin[NU / NT];
-  float gin = 1.0f, bin = 1.0f;  // gate and write gate of token `lane`
-  // the write gates are read from the gates when there are none (and then not used)
+  // The next chunk's key rows (16-byte units, consecutive threads along a token row) and gates
+  // (lane = token) are prefetched straight into LDS by direct loads, issued after the chunk's
+  // staging and in flight through its loop, so that no registers are held for them. A wave
+  // waits for its own loads (vmcnt) before it reads them (the largest |k| below); the barrier
+  // at the top of the next chunk orders them for the other waves. Lanes of rows past the end of
+  // the sequence load nothing: those rows are zeroed where they are read.
+  // (the write gates are read from the gates when there are none, and then not used)
   const float* bsrc = A.beta ? A.beta : A.gamma;
-  auto load_kv = [&](int chn) {
-    refresh();  // keeps the per-lane addresses from being hoisted out of the chunk loop
-    // Bounds-checked buffer loads: rows past the end of the sequence (or of the segment) read
-    // as 0, with no branch, so the compiler counts these loads and waits for exactly them
-    // where they are used. The values are defined on every path.
-    const int chv = chn < c_end ? chn : c_end - 1;
-    const int t0n = chv * C;
-    const int nvn = chn < c_end ? min(C, Tlen - t0n) : 0;
-    const long long row0 = (seq0 + t0n) * tok_stride + (long long)h * D;
-    const uint32_t valid = nvn > 0 ? (uint32_t)(nvn - 1) * tok_bytes + D * 2u : 0u;
-    const auto rk = buffer_rsrc(kg + row0, valid);
-    const auto rv = buffer_rsrc(vg + row0, valid);
+  typedef __attribute__((address_space(3))) void lds_void;
+  auto prefetch_k = [&](int chn) {
+    refresh();
+    const int t0n = chn * C;
+    const int nvn = min(C, Tlen - t0n);
+    const bf16* src = kg + (seq0 + t0n) * tok_stride + (long long)h * D;
 #pragma unroll
     for (int k = 0; k < NU / NT; ++k) {
       const int u = tid + k * NT;
       const int tt = (uint32_t)u / UPR, cu = (uint32_t)u % UPR;  // u >= 0
-      const uint32_t off = (uint32_t)tt * tok_bytes + (uint32_t)cu * 16u;
-      kin[k] = buffer_load16<bf16x8>(rk, off);
-      vin[k] = buffer_load16<bf16x8>(rv, off);
+      const uint32_t base = __builtin_amdgcn_readfirstlane(
+          (uint32_t)(uintptr_t)(lds_void*)(Kraw + (u - lane)));
+      if (tt < nvn) dma_load16_so(src, (uint32_t)tt * tok_bytes + (uint32_t)cu * 16u, base);
     }
-    const uint32_t gvalid = nvn > 0 ? (uint32_t)(nvn - 1) * Hn * 4u + 4u : 0u;
-    const auto rg = buffer_rsrc(A.gamma + (seq0 + t0n) * Hn + h, gvalid);
-    const auto rb = buffer_rsrc(bsrc + (seq0 + t0n) * Hn + h, gvalid);
-    gin = buffer_load4f(rg, (uint32_t)lane * Hn * 4u);
-    bin = buffer_load4f(rb, (uint32_t)lane * Hn * 4u);
+    if (wave < 2) {
+      const float* gs = (wave == 0 ? A.gamma : bsrc) + (seq0 + t0n) * Hn + h;
+      const uint32_t base = __builtin_amdgcn_readfirstlane(
+          (uint32_t)(uintptr_t)(lds_void*)(wave == 0 ? Graw : Braw));
+      if (lane < nvn) dma_load4_so(gs, (uint32_t)lane * Hn * 4u, base);
+    }
+  };
+  // the largest |k| of the prefetched rows of chunk chn (this wave's units), to v_sc[4 + wave]
+  auto kmax_put = [&](int chn) {
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's direct loads have landed
+    refresh();
+    const int nvn = min(C, Tlen - chn * C);
+    float m = 0.0f;
+#pragma unroll
+    for (int k = 0; k < NU / NT; ++k) {
+      const int u = tid + k * NT;
+      const bf16x8 kv = Kraw[u];
+      float um = 0.0f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) um = fmaxf(um, fabsf((float)kv[i]));
+      if ((int)((uint32_t)u / UPR) < nvn) m = fmaxf(m, um);  // rows past the end hold stale data
+    }
+    m = wave_max(m);
+    if (lane == 0) v_sc[4 + wave] = m;
   };
   // state tiles (times sc) -> Hs as fp16 rows e = column index of the tile, permuted columns
   auto stage_tile = [&](int jr, int jc, f32x4 x) {
@@ -265,35 +274,19 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
 #pragma unroll
       for (int jc = 0; jc < NCT; ++jc) stage_tile(jr, jc, Hst[jr][jc] * sc);
   };
-  auto stage_u = [&](float sc) {
-    f32x4 x[NRT][NCT];  // all reads first: one wait covers them
-#pragma unroll
-    for (int jr = 0; jr < NRT; ++jr)
-#pragma unroll
-      for (int jc = 0; jc < NCT; ++jc) x[jr][jc] = *us_tile(jr, jc);
-#pragma unroll
-    for (int jr = 0; jr < NRT; ++jr)
-#pragma unroll
-      for (int jc = 0; jc < NCT; ++jc) stage_tile(jr, jc, x[jr][jc] * sc);
-  };
   // A fragment of K (rows = tokens 16 sb + lr) over feature block kk
   auto frag_k = [&](int sb, int kk) {
     return *reinterpret_cast<const Frag*>(Kp + (16 * sb + lr) * LDD + 32 * kk + 8 * lg);
   };
-  // A fragment of K^T (V^T) (rows = features 16 ft + lr) over token block kc, permuted token
-  // order (k-slot j of lane group lg: token 32 kc + 16 (j / 4) + 4 lg + j % 4); K^T by two
-  // transposing reads of K, V^T from its tile
+  // A fragment of K^T (rows = features 16 ft + lr) over token block kc, permuted token order
+  // (k-slot j of lane group lg: token 32 kc + 16 (j / 4) + 4 lg + j % 4), by two transposing
+  // reads of K
   auto frag_kt = [&](int ft, int kc) {
     return frag_trans<LDD>(Kp, 32 * kc + 4 * lg, 32 * kc + 16 + 4 * lg, pcol(16 * ft + 4 * (lr & 3)), lr);
   };
-  auto frag_vt = [&](int ft, int kc) {
-    return *reinterpret_cast<const Frag*>(VT + (16 * ft + lr) * LDC + 32 * kc + 8 * lg);
-  };
 
-  load_kv(c_begin);
-  // nothing in flight on entry to the chunk loop, so that the compiler's wait at its top counts
-  // only the loads issued in the output phase of the previous chunk (and not its stores)
-  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
+  prefetch_k(c_begin);
+  kmax_put(c_begin);
 
   for (int ch = c_begin; ch < c_end; ++ch) {
     refresh();
@@ -301,13 +294,21 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
     const int nv = min(C, Tlen - t0);
     const float n0 = sqrtf(n0sq);
     const float n0inv = n0 > 0.0f ? 1.0f / n0 : 0.0f;
-    lds_barrier();  // the last chunk's LDS reads are done
+    lds_barrier();  // the last chunk's LDS reads are done; v_sc holds this chunk's |k| maxima
+
+    // ---- key scale 2^-ke of the chunk: the staged rows lie below 2 in magnitude -------------
+    float km = v_sc[4];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) km = fmaxf(km, v_sc[4 + w]);
+    const int ke = pow2_exponent(km, 30);
+    const float kinv = exp2_int(-ke), ks2 = exp2_int(2 * ke);
 
     // ---- gate prefix (every wave; lane = token) ---------------------------------------------
-    float g_l = 1.0f, l2 = 0.0f;  // tokens past the end: gamma = 1 with k = v = q = 0
+    float g_l = 1.0f, l2 = 0.0f, bt_l = 1.0f;  // tokens past the end: gamma = 1, k = q = 0
     if (lane < nv) {
-      g_l = gin;
+      g_l = Graw[lane];
       l2 = log2_gate(g_l);
+      if (A.beta) bt_l = Braw[lane];
     }
     const float cl = scan_add<kWave>(l2);
     const float clast = lane_value(cl, C - 1);
@@ -315,41 +316,26 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
     const float gC = lane_value(gam, C - 1);
     if (wave == 0) {
       v_cl[lane] = cl;
-      v_w[lane] = fast_exp2(fminf(clast - cl, 0.0f));
+      v_w[lane] = fast_exp2(fminf(clast - cl, 0.0f)) * bt_l;
+      v_bt[lane] = bt_l;
     }
-    // ---- stage K (fp16, permuted features) and V (fp16) ------------------------------------
-    // With the write gate, the rows of token t are scaled by sqrt(beta_t) (lane t holds beta_t):
-    // the base recurrence on the scaled rows is the write-gated one.
-    auto stage_kv = [&](auto gated) {
+    // ---- stage K (fp16, times 2^-ke, permuted features) ------------------------------------
 #pragma unroll
-      for (int k = 0; k < NU / NT; ++k) {
-        const int u = tid + k * NT;
-        const int tt = (uint32_t)u / UPR, cu = (uint32_t)u % UPR;  // u >= 0
-        const bf16x8 kv = kin[k], vv = vin[k];  // rows past the end were read as 0
-        f16x8 ko, vo;
-        if constexpr (decltype(gated)::value) {
-          const float sb = sqrtf(lane_read(bin, tt));
+    for (int k = 0; k < NU / NT; ++k) {
+      const int u = tid + k * NT;
+      const int tt = (uint32_t)u / UPR, cu = (uint32_t)u % UPR;  // u >= 0
+      const bf16x8 kv = Kraw[u];
+      f16x8 ko;
 #pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            ko[i] = (f16)((float)kv[i] * sb);
-            vo[i] = (f16)((float)vv[i] * sb);
-          }
-        } else {
-#pragma unroll
-          for (int i = 0; i < 8; ++i) {
-            ko[i] = (f16)(float)kv[i];
-            vo[i] = (f16)(float)vv[i];
-          }
-        }
-        *reinterpret_cast<f16x8*>(Vp + tt * LDD + 8 * cu) = vo;
-        *reinterpret_cast<f16x4*>(Kp + tt * LDD + pcol(8 * cu)) = f16x4{ko[0], ko[1], ko[2], ko[3]};
-        *reinterpret_cast<f16x4*>(Kp + tt * LDD + pcol(8 * cu + 4)) = f16x4{ko[4], ko[5], ko[6], ko[7]};
-      }
-    };
-    if (A.beta) stage_kv(std::true_type());
-    else stage_kv(std::false_type());
+      for (int i = 0; i < 8; ++i) ko[i] = (f16)((float)kv[i] * kinv);
+      if (tt >= nv) ko = f16x8{};  // rows past the end hold stale data (never loaded): zero them
+      *reinterpret_cast<f16x4*>(Kp + tt * LDD + pcol(8 * cu)) = f16x4{ko[0], ko[1], ko[2], ko[3]};
+      *reinterpret_cast<f16x4*>(Kp + tt * LDD + pcol(8 * cu + 4)) = f16x4{ko[4], ko[5], ko[6], ko[7]};
+    }
     stage_h(n0inv);  // H0hat
     lds_barrier();
+    // the next chunk's keys and gates: in flight through this chunk
+    if (ch + 1 < c_end) prefetch_k(ch + 1);
 
     refresh();
 
@@ -367,8 +353,8 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
         for (int kk = 0; kk < KD; ++kk) keep_in_agpr(Hres[ft][kk]);
     }
 
-    // ---- every K fragment of the chunk (rows = tokens), resident in vector registers until
-    // the output ---------------------------------------------------------------------------------
+    // ---- every K fragment of the chunk (rows = tokens), resident in vector registers through
+    // the loop ----------------------------------------------------------------------------------
     refresh();
     Frag kres[KD][ST];
 #pragma unroll
@@ -376,7 +362,8 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
 #pragma unroll
       for (int sb = 0; sb < ST; ++sb) kres[kk][sb] = frag_k(sb, kk);
 
-    // ---- norm phase: k_t^T H0hat k_t and sum_{s<t} 2^(cl_{t-1} - cl_s) G_st^2 ---------------
+    // ---- norm phase: k_t^T H0hat k_t and sum_{s<t} 2^(cl_{t-1} - cl_s) beta_s G_st^2 --------
+    // (on the staged keys k' = 2^-ke k: the terms are multiplied back by 2^2ke and 2^4ke)
     {
       Frag kb[KD];  // B fragments of the own token's key
 #pragma unroll
@@ -407,10 +394,11 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
       for (int sb = 0; sb < ST; ++sb) {
         const f32x4 gacc = gram[sb];
         const f32x4 cls = *reinterpret_cast<const f32x4*>(v_cl + 16 * sb + 4 * lg);
+        const f32x4 bts = *reinterpret_cast<const f32x4*>(v_bt + 16 * sb + 4 * lg);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int s = 16 * sb + 4 * lg + i;
-          const float e = fast_exp2(fminf(clp - cls[i], 0.0f)) * (gacc[i] * gacc[i]);
+          const float e = fast_exp2(fminf(clp - cls[i], 0.0f)) * bts[i] * (gacc[i] * gacc[i]);
           pv += s < t ? e : 0.0f;
           kd = s == t ? gacc[i] : kd;
         }
@@ -423,26 +411,17 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
       kd += lane_read(kd, lane ^ 32);
       const float gt = lane_read(g_l, t);
       const float gprev = lane_read(gam, t > 0 ? t - 1 : 0);
+      const float btt = lane_read(bt_l, t);
       if (lg == 0) {
+        const float kdt = btt * (kd * ks2);  // beta_t ||k_t||^2
         v_a[t] = gt * gt;
-        v_b[t] = 2.0f * gt * ((t > 0 ? gprev : 1.0f) * n0 * pu + pv) + kd * kd;
+        v_b[t] = 2.0f * gt * btt * ((t > 0 ? gprev : 1.0f) * n0 * (pu * ks2) + (pv * ks2) * ks2) +
+                 kdt * kdt;
       }
     }
-    // ---- V^T with the tokens in the permuted order (fragments from transposing reads of V,
-    // written back as rows: every later operand of it is one 16-byte read), and every K^T
-    // fragment of the chunk, resident in registers until the loop ends (after the norm
-    // phase's products, which do not need them) ----------------------------------------------
+    // ---- every K^T fragment of the chunk, resident in registers until the loop ends (after the
+    // norm phase's products, which do not need them) ------------------------------------------
     refresh();
-#pragma unroll
-    for (int k = 0; k < (FT * KC + NW - 1) / NW; ++k) {
-      const int phi = wave + k * NW;
-      if (FT * KC % NW == 0 || phi < FT * KC) {
-        const int ft = phi / KC, kc = phi % KC;
-        const Frag g = frag_trans<LDD>(Vp, 32 * kc + 4 * lg, 32 * kc + 16 + 4 * lg,
-                                       16 * ft + 4 * (lr & 3), lr);
-        *reinterpret_cast<Frag*>(VT + (16 * ft + lr) * LDC + 32 * kc + 8 * lg) = g;
-      }
-    }
     Frag ktr[KC][FT];
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc)
@@ -465,18 +444,22 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
     const float ninv_t = lane_read(ninv, t);
     const float s_t = lane_read(gam, t) * n0 * ninv_t;
     const float cl_t = lane_read(cl, t);
-    // Mhat^T tiles of the own token: Mh[sb][i] = Mhat_{t, 16 sb + 4 lg + i}
+    // Mhat^T tiles of the own token: Mh[sb][i] = Mhat_{t, 16 sb + 4 lg + i}, for the staged keys
+    // (times 2^2ke)
     f32x4 Mh[ST];
+    {
+      const float mt = ninv_t * ks2;
 #pragma unroll
-    for (int sb = 0; sb < ST; ++sb) {
-      const f32x4 cls = *reinterpret_cast<const f32x4*>(v_cl + 16 * sb + 4 * lg);
+      for (int sb = 0; sb < ST; ++sb) {
+        const f32x4 cls = *reinterpret_cast<const f32x4*>(v_cl + 16 * sb + 4 * lg);
+        const f32x4 bts = *reinterpret_cast<const f32x4*>(v_bt + 16 * sb + 4 * lg);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int s = 16 * sb + 4 * lg + i;
-        Mh[sb][i] = s <= t ? fast_exp2(fminf(cl_t - cls[i], 0.0f)) * ninv_t : 0.0f;
+        for (int i = 0; i < 4; ++i) {
+          const int s = 16 * sb + 4 * lg + i;
+          Mh[sb][i] = s <= t ? fast_exp2(fminf(cl_t - cls[i], 0.0f)) * bts[i] * mt : 0.0f;
+        }
       }
     }
-    stage_u(n0inv);  // U0hat (every wave has read its H0hat fragments)
 
     // ---- queries of the own token, accumulator layout: Q[t][16 ft + 4 lg .. + 3], loaded
     // during the carry's products and consumed at the start of the loop ----------------------
@@ -489,7 +472,9 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
 #pragma unroll
       for (int ft = 0; ft < FT; ++ft) Qraw[ft] = buffer_load8<bf16x4>(rq, qoff + 32u * ft);
     }
-    // ---- state carry: H <- Gam_C H + K^T diag(w) K, U^T <- Gam_C U^T + K^T diag(w) V --------
+    // ---- state carry: H <- Gam_C H + K^T diag(w) K ------------------------------------------
+    // (on the staged keys: the product is accumulated onto Gam_C H / 2^2ke, and the sum is
+    // multiplied by 2^2ke)
     {
       // A operands (w K)^T of the own row tiles, split hi + lo; tokens in the permuted order
       // of the K^T tile (k-slot j of lane group lg: token 32 kc + 16 (j / 4) + 4 lg + j % 4)
@@ -509,78 +494,60 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
           }
         }
       }
-      // column operands in groups of two column tiles, double-buffered: the next group's
-      // reads are in flight during the current group's products. The K operands of column
-      // tile bc are the resident K^T fragments of feature tile bc (K[s][16 bc + lr], the same
-      // token slots) when the wave's column tiles are all of them (b0 = 0), else read again.
-      constexpr int CG = NCT >= 2 ? 2 : 1, NG = NCT / CG;
-      Frag bk[2][CG][KC], bv[2][CG][KC];
-      f32x4 ub[CG][NRT];  // the group's U^T tiles, read as the group starts
-      auto load_group = [&](int g, int buf) {
+      // The K operands of column tile bc are the resident K^T fragments of feature tile bc
+      // (K[s][16 bc + lr], the same token slots) when the wave's column tiles are all of them
+      // (b0 = 0), else read again.
+      const float gsc = gC * exp2_int(-2 * ke);
 #pragma unroll
-        for (int j = 0; j < CG; ++j) {
+      for (int jc = 0; jc < NCT; ++jc) {
+        Frag bk[KC];
 #pragma unroll
-          for (int kc = 0; kc < KC; ++kc) {
-            if constexpr (NCT == FT) {
-              bk[buf][j][kc] = ktr[kc][g * CG + j];
-            } else {
-              bk[buf][j][kc] = frag_kt(b0 + g * CG + j, kc);
-            }
-            bv[buf][j][kc] = frag_vt(b0 + g * CG + j, kc);
+        for (int kc = 0; kc < KC; ++kc) {
+          if constexpr (NCT == FT) {
+            bk[kc] = ktr[kc][jc];
+          } else {
+            bk[kc] = frag_kt(b0 + jc, kc);
           }
         }
-      };
-      load_group(0, 0);
-      __builtin_amdgcn_sched_barrier(0);
+        f32x4 hacc[NRT];
 #pragma unroll
-      for (int g = 0; g < NG; ++g) {
-#pragma unroll
-        for (int j = 0; j < CG; ++j)
-#pragma unroll
-          for (int jr = 0; jr < NRT; ++jr) ub[j][jr] = *us_tile(jr, g * CG + j);
-        if (g + 1 < NG) load_group(g + 1, (g + 1) % 2);
-        // the group's 2 CG NRT accumulators take turns, so that no product waits for the one
-        // before it
-        f32x4 hacc[CG][NRT], uacc[CG][NRT];
-#pragma unroll
-        for (int j = 0; j < CG; ++j)
-#pragma unroll
-          for (int jr = 0; jr < NRT; ++jr) {
-            hacc[j][jr] = Hst[jr][g * CG + j] * gC;
-            uacc[j][jr] = ub[j][jr] * gC;
-          }
+        for (int jr = 0; jr < NRT; ++jr) hacc[jr] = Hst[jr][jc] * gsc;
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
           for (int hl = 0; hl < 2; ++hl)
 #pragma unroll
-            for (int j = 0; j < CG; ++j)
+            for (int jr = 0; jr < NRT; ++jr)
+              hacc[jr] = M::mma(hl == 0 ? awh[jr][kc] : awl[jr][kc], bk[kc], hacc[jr]);
 #pragma unroll
-              for (int jr = 0; jr < NRT; ++jr) {
-                const Frag& aw = hl == 0 ? awh[jr][kc] : awl[jr][kc];
-                hacc[j][jr] = M::mma(aw, bk[g % 2][j][kc], hacc[j][jr]);
-                uacc[j][jr] = M::mma(aw, bv[g % 2][j][kc], uacc[j][jr]);
-              }
-#pragma unroll
-        for (int j = 0; j < CG; ++j)
-#pragma unroll
-          for (int jr = 0; jr < NRT; ++jr) {
-            Hst[jr][g * CG + j] = hacc[j][jr];
-            *us_tile(jr, g * CG + j) = uacc[j][jr];
-            if constexpr (Cfg::PIN) keep_in_agpr(Hst[jr][g * CG + j]);
-          }
-        __builtin_amdgcn_sched_barrier(0);
+        for (int jr = 0; jr < NRT; ++jr) {
+          Hst[jr][jc] = hacc[jr] * ks2;
+          if constexpr (Cfg::PIN) keep_in_agpr(Hst[jr][jc]);
+        }
       }
     }
 
     // ---- Chebyshev loop on the residuals of the own token ----------------------------------
+    // (the query is taken times 2^-qe, so that its largest element lies in [1, 2): the solve
+    // is linear in q, and the scale is carried to the stored solve)
     refresh();
     const bool live = ninv_t > 0.0f;  // ||H_t|| = 0: x_t = 0
+    int qe;
     f32x4 Ra[FT], Rb[FT], X[FT];  // (Rb and X are first written by the first step)
+    {
+      float qm = 0.0f;
 #pragma unroll
-    for (int ft = 0; ft < FT; ++ft)
-      Ra[ft] = live ? f32x4{(float)Qraw[ft][0], (float)Qraw[ft][1], (float)Qraw[ft][2], (float)Qraw[ft][3]} * cc.inv_s0
-                    : f32x4{0.f, 0.f, 0.f, 0.f};
+      for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) qm = fmaxf(qm, fabsf((float)Qraw[ft][j]));
+      qm = fmaxf(qm, lane_read(qm, lane ^ 16));
+      qm = fmaxf(qm, lane_read(qm, lane ^ 32));
+      qe = pow2_exponent(qm, 60);
+      const float qsc = live ? cc.inv_s0 * exp2_int(-qe) : 0.0f;
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft)
+        Ra[ft] = f32x4{(float)Qraw[ft][0], (float)Qraw[ft][1], (float)Qraw[ft][2], (float)Qraw[ft][3]} * qsc;
+    }
     // One iteration it on the current rescaled residual Rc = Rt_it (the residuals divided by
     // host scalars that absorb the R_{it-1} coefficient of the recurrence):
     //   Ro <- Ro + krs Rc + H0hat (kys s_t Rc) + K^T ((K Rc) o kys Mhat)
@@ -637,6 +604,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
     // then over the four lane groups), written by lane group 0; a token with ||H_t|| = 0 has
     // x_i = 0 for every i, so its residuals are all ||q_t||. Rows past the end of the sequence
     // (and the other lane groups) store out of the buffer's range, which drops the store.
+    // (The residual is formed on the query times 2^-qe: its norm is multiplied back.)
     float res_qn = 0.0f;
     const int res_i1 = cc.iters + 1;
     const uint32_t res_row = (uint32_t)Hn * (uint32_t)res_i1 * 4u;  // bytes per token
@@ -649,12 +617,13 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
       return x + lane_read(x, lane ^ 32);
     };
     auto res_put = [&](int i, float val) { buffer_store4f(val, res_rsrc, res_off + 4u * (uint32_t)i); };
+    const float res_sc = exp2_int(qe);
     auto res_step = [&](int i, const f32x4(&R)[FT]) {
       float x = 0.0f;
 #pragma unroll
       for (int ft = 0; ft < FT; ++ft) x += R[ft][0] * R[ft][0] + R[ft][1] * R[ft][1] + R[ft][2] * R[ft][2] + R[ft][3] * R[ft][3];
       x = lane_sum(x);
-      res_put(i, live ? fabsf(cc.sres[i]) * sqrtf(x) : res_qn);
+      res_put(i, live ? fabsf(cc.sres[i]) * sqrtf(x) * res_sc : res_qn);
     };
     if constexpr (RES) {
       float x = 0.0f;
@@ -719,90 +688,47 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
       }
     }
 
-    // ---- output O^T = diag(s) U0hat X^T + V^T ((K X^T) o Mhat), X split into hi + lo -------
-    // Instruction groups: (1) U0hat and K fragment reads, the split of X; (2) the K products
-    // and the V^T fragment reads; (3) the U0hat products; (4) the V^T products and the stores.
-    lds_barrier();  // U0hat is staged
-    load_kv(ch + 1);
+    // ---- the solve of the own token to o's row (fp16), scaled by 2^-xe so that its largest
+    // element lies in [1, 2); phi_t = 2^xe / ||H_t||_F (times the iterate's own scales) to the
+    // per-token array: o_t = phi_t U_t y_t ---------------------------------------------------
     refresh();
+    if (ch + 1 < c_end) kmax_put(ch + 1);
     {
+      float xm = 0.0f;
 #pragma unroll
       for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
-        for (int kk = 0; kk < KD; ++kk) {
-          Hres[ft][kk] = *reinterpret_cast<const Frag*>(Hs + (16 * ft + lr) * LDD + 32 * kk + 8 * lg);
-          if constexpr (Cfg::PIN) keep_in_agpr(Hres[ft][kk]);
-        }
-      Frag vq[KC][FT], xh[KD], xl[KD], pf[KC];
-#pragma unroll
-      for (int kk = 0; kk < KD; ++kk) {
-        xh[kk] = pack8(X[2 * kk], X[2 * kk + 1]);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float x = j < 4 ? X[2 * kk][j] : X[2 * kk + 1][j - 4];
-          xl[kk][j] = (f16)(x - (float)xh[kk][j]);
-        }
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      f32x4 pa[ST];
-#pragma unroll
-      for (int sb = 0; sb < ST; ++sb) pa[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KD; ++kk) {  // (hi and lo products not back to back)
-#pragma unroll
-        for (int sb = 0; sb < ST; ++sb) pa[sb] = M::mma(kres[kk][sb], xh[kk], pa[sb]);
-#pragma unroll
-        for (int sb = 0; sb < ST; ++sb) pa[sb] = M::mma(kres[kk][sb], xl[kk], pa[sb]);
-      }
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc)
-#pragma unroll
-        for (int ft = 0; ft < FT; ++ft) vq[kc][ft] = frag_vt(ft, kc);
-      __builtin_amdgcn_sched_barrier(0);
-      f32x4 y[FT];
-#pragma unroll
-      for (int ft = 0; ft < FT; ++ft) y[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int kk = 0; kk < KD; ++kk) {
-#pragma unroll
-        for (int ft = 0; ft < FT; ++ft) y[ft] = M::mma(Hres[ft][kk], xh[kk], y[ft]);
-#pragma unroll
-        for (int ft = 0; ft < FT; ++ft) y[ft] = M::mma(Hres[ft][kk], xl[kk], y[ft]);
-      }
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc) pf[kc] = pack8(pa[2 * kc] * Mh[2 * kc], pa[2 * kc + 1] * Mh[2 * kc + 1]);
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int ft = 0; ft < FT; ++ft) y[ft] = y[ft] * s_t;
-#pragma unroll
-      for (int kc = 0; kc < KC; ++kc)
-#pragma unroll
-        for (int ft = 0; ft < FT; ++ft) y[ft] = M::mma(vq[kc][ft], pf[kc], y[ft]);
-      // o of the own token straight from the accumulators: 8 bytes per lane, 32 per token row
-      // and tile
+        for (int j = 0; j < 4; ++j) xm = fmaxf(xm, fabsf(X[ft][j]));
+      xm = fmaxf(xm, lane_read(xm, lane ^ 16));
+      xm = fmaxf(xm, lane_read(xm, lane ^ 32));
+      const int xe = pow2_exponent(xm, 100);
+      const float xinv = exp2_int(-xe);
       // (bounds-checked: the stores of tokens past the end are dropped)
-      const auto ro = buffer_rsrc(og + (seq0 + t0) * tok_stride + (long long)h * D,
+      const auto ry = buffer_rsrc(yg + (seq0 + t0) * tok_stride + (long long)h * D,
                                   (uint32_t)(nv - 1) * tok_bytes + D * 2u);
-      const uint32_t ooff = (uint32_t)t * tok_bytes + (uint32_t)lg * 8u;
+      const uint32_t yoff = (uint32_t)t * tok_bytes + (uint32_t)lg * 8u;
 #pragma unroll
       for (int ft = 0; ft < FT; ++ft) {
-        const f32x4 yo = y[ft] * cc.inv_xsc;  // the iterate was formed times a power of two
-        const bf16x4 ov = {(bf16)yo[0], (bf16)yo[1], (bf16)yo[2], (bf16)yo[3]};
-        buffer_store8(ov, ro, ooff + 32u * ft);
+        const f32x4 yv = X[ft] * xinv;
+        const f16x4 y4 = {(f16)yv[0], (f16)yv[1], (f16)yv[2], (f16)yv[3]};
+        buffer_store8(y4, ry, yoff + 32u * ft);
       }
+      // phi_t: 2^xe undoes the solve's scale, inv_xsc the iterate's power of two, 2^qe the
+      // query's, and 1 / ||H_t||_F turns the solve of the normalised system into x_t
+      const float phi = exp2_int(xe) * cc.inv_xsc * exp2_int(qe) * ninv_t;
+      const auto rp = buffer_rsrc(A.phi + (seq0 + t0) * Hn + h, (uint32_t)(nv - 1) * Hn * 4u + 4u);
+      buffer_store4f(phi, rp, lg == 0 ? (uint32_t)t * Hn * 4u : 0x80000000u);
     }
     n0sq = n2last;
   }
   if (A.out_h && seg == last) {
     float* oh = A.out_h + (size_t)bh * D * D;
-    float* ou = A.out_u + (size_t)bh * D * D;
 #pragma unroll
     for (int jr = 0; jr < NRT; ++jr)
 #pragma unroll
       for (int jc = 0; jc < NCT; ++jc) {
         const size_t o = (size_t)(16 * (b0 + jc) + lr) * D + 16 * (a0 + jr) + 4 * lg;
         *reinterpret_cast<f32x4*>(oh + o) = Hst[jr][jc];
-        *reinterpret_cast<f32x4*>(ou + o) = *us_tile(jr, jc);
       }
   }
   if (A.n2_out && seg == last && tid == 0) A.n2_out[bh] = n0sq;
