@@ -132,7 +132,7 @@ def bench_prefill(W, inputs, steps, warmup, ev, beta=None, what="prefill"):
     need = gka.workspace_bytes(W.B, W.T, W.H, W.D, W.chunk, W.iters, W.a, gka.GKA_BF16)
     ws = torch.empty(max(need, 1), device="cuda", dtype=torch.uint8)
     stream = torch.cuda.current_stream()
-    NP = 5  # phase events per call: summaries, scan, walk, output pass, end
+    NP = 4  # phase events per call: summaries, scan, walk, end
     phase = ev.create(NP * steps)
     arrs = [(ctypes.c_void_p * NP)(*phase[NP * i:NP * i + NP]) for i in range(steps)]
     t0, t1 = ev.create(2)
@@ -159,8 +159,7 @@ def bench_prefill(W, inputs, steps, warmup, ev, beta=None, what="prefill"):
     span = lambda a, b: float(np.mean([ev.elapsed_ms(phase[NP * i + a], phase[NP * i + b])
                                         for i in range(steps)]))
     rec = dict(total_ms=total_ms, ms_per_step=total_ms / steps, summary_ms=span(0, 1),
-               scan_ms=span(1, 2), walk_ms=span(2, 3), output_ms=span(3, 4), segments=_segments(W),
-               o=o)
+               scan_ms=span(1, 2), walk_ms=span(2, 3), segments=_segments(W), o=o)
     ev.destroy(phase + [t0, t1])
     return rec
 
@@ -301,10 +300,8 @@ def bench_backward(W, inputs, steps, warmup, ev):
 
 def _segments(W):
     from test_ridge_regression_amd import gka
-    # the plan's segment count: workspace = [B*H*S*(2 D^2 + 1)*4 + B*H*4] (S > 1) + B*T*H*4
-    # (the per-token factors of bf16 with chunks of 64), each rounded up to 256 bytes
+    # the plan's segment count: workspace = B*H*S*(2 D^2 + 1)*4 + B*H*4 (rounded up to 256)
     need = gka.workspace_bytes(W.B, W.T, W.H, W.D, W.chunk, W.iters, W.a, gka.GKA_BF16)
-    need -= (W.B * W.T * W.H * 4 + 255) // 256 * 256
     if need <= 0:
         return 1
     bh = W.B * W.H

@@ -55,7 +55,7 @@ typedef enum {
 typedef enum { GKA_BF16 = 0, GKA_FP32 = 1 } gka_dtype;
 
 #define GKA_MAX_ITERS 64
-#define GKA_PHASE_EVENTS 5
+#define GKA_PHASE_EVENTS 4
 
 /*
  * Problem description shared by both entry points.
@@ -95,18 +95,14 @@ size_t gka_fwd_workspace_bytes(const gka_params* p);
  *             read as the initial state and overwritten with the final state (in place)
  *   hnorm_t   optional [B, T, H] float32: ||H_t||_F of every token, written
  *   workspace device scratch of at least gka_fwd_workspace_bytes(p) bytes (NULL if that is 0):
- *             the segment states of a multi-segment plan and, for bf16 with chunks of 64, one
- *             float per (token, head) that carries each token's solve from the chunk walk to the
- *             output pass. During the call o's rows hold those solves (fp16) before the output
- *             pass writes o over them.
+ *             the per-segment states of a multi-segment plan
  *   phase_events
- *             optional (NULL = none): GKA_PHASE_EVENTS (5) caller-created hipEvent_t recorded on
+ *             optional (NULL = none): GKA_PHASE_EVENTS (4) caller-created hipEvent_t recorded on
  *             `stream` at the phase boundaries -- [0] before the segment summaries, [1] before
- *             the segment scan, [2] before the chunk walk, [3] before the output pass, [4] after
- *             it. With one segment the first three are recorded back to back; where the walk
- *             also forms the output (float32, chunks of 32) the last two are. For per-phase
- *             timing only; nothing else changes. (A timing hook in the signature: it exists so
- *             that the kernels' own times can be measured on the launch stream.)
+ *             the segment scan, [2] before the fused chunk walk, [3] after it. With one segment
+ *             the first three are recorded back to back. For per-phase timing only; nothing else
+ *             changes. (A timing hook in the signature: it exists so that the kernels' own times
+ *             can be measured on the launch stream.)
  */
 gka_status gka_fwd_chunked(const gka_params* p, const void* q, const void* k, const void* v,
                            const float* gamma, void* o, float* h_state, float* u_state,

@@ -140,8 +140,7 @@ bool make_plan(const gka_params* p, FwdPlan& pl, bool packed = false) {
   pl.C = p->chunk;
   pl.dtype = p->dtype;
   pl.N = (p->T + p->chunk - 1) / p->chunk;
-  pl.split = false;
-  pl.phi_off = pl.order_off = 0;
+  pl.order_off = 0;
   if (pl.N == 0) {
     pl.S = pl.J = 0;
     pl.ws_bytes = 0;
@@ -175,13 +174,6 @@ bool make_plan(const gka_params* p, FwdPlan& pl, bool packed = false) {
                   + bh * pl.S * sizeof(float)          // per-segment log2 gate product
                   + bh * sizeof(float);                // ||H||^2 at the start of segment 0
     pl.ws_bytes = (pl.ws_bytes + 255) & ~(size_t)255;
-  }
-  // token walk + output pass: phi_t of every (row, head), rows = B T (packed: T bounds every
-  // sequence, so B T bounds the rows)
-  pl.split = gka::walk_tok_supported(pl);
-  pl.phi_off = pl.ws_bytes;
-  if (pl.split) {
-    pl.ws_bytes += ((size_t)p->B * p->T * p->H * sizeof(float) + 255) & ~(size_t)255;
   }
   if (packed && p->B <= gka::kMaxOrdered) {  // the dispatch order, after the segment states
     pl.order_off = pl.ws_bytes;
@@ -345,8 +337,6 @@ gka_status fwd_impl(const gka_params* p, const int32_t* cu, int64_t total, const
 
   const ChebConsts cc = cheb_consts(p->a, p->iters);
   hipStream_t s = static_cast<hipStream_t>(stream);
-  float* phi = pl.split ? reinterpret_cast<float*>(static_cast<char*>(workspace) + pl.phi_off)
-                        : nullptr;
   auto mark = [&](int i) {
     if (phase_events && phase_events[i])
       return hipEventRecord(static_cast<hipEvent_t>(phase_events[i]), s) == hipSuccess;
@@ -368,9 +358,8 @@ gka_status fwd_impl(const gka_params* p, const int32_t* cu, int64_t total, const
   }
   wa.o = o;
   wa.hnorm_t = hnorm_t;
-  wa.phi = phi;
-  // the fused walk (or, split, the token walk and then the output pass) from the segment-start
-  // states in (in_h, in_u, n2_in, with strides in_bh, in_seg)
+  // the fused chunk walk from the segment-start states in (in_h, in_u, n2_in, with strides
+  // in_bh, in_seg)
   auto walk = [&](const float* in_h, const float* in_u, long long in_bh, long long in_seg,
                   const float* n2_in) -> gka_status {
     wa.in_h = in_h;
@@ -383,8 +372,6 @@ gka_status fwd_impl(const gka_params* p, const int32_t* cu, int64_t total, const
     wa.n2_out = hnorm2;
     if (gka::launch_walk(pl, false, wa, cc, s) != hipSuccess) return GKA_ERR_HIP;
     if (!mark(3)) return GKA_ERR_HIP;
-    if (pl.split && gka::launch_output(pl, wa, s) != hipSuccess) return GKA_ERR_HIP;
-    if (!mark(4)) return GKA_ERR_HIP;
     return GKA_OK;
   };
   if (pl.S == 1) {

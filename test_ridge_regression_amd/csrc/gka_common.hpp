@@ -350,10 +350,17 @@ __device__ inline float wave_sum(float x) {
   return x;
 }
 
+// maximum over the wave, in every lane: a running maximum along the rows of 16 lanes (DPP row
+// shifts; lanes without a source keep their own value), carried across rows by the row
+// broadcasts of lanes 15 and 31 (as in scan_add), then lane 63's value
 __device__ inline float wave_max(float x) {
-#pragma unroll
-  for (int m = 32; m >= 1; m >>= 1) x = fmaxf(x, __shfl_xor(x, m, kWave));
-  return x;
+  x = fmaxf(x, dpp_move<0x111, 0xf>(x, x));
+  x = fmaxf(x, dpp_move<0x112, 0xf>(x, x));
+  x = fmaxf(x, dpp_move<0x114, 0xf>(x, x));
+  x = fmaxf(x, dpp_move<0x118, 0xf>(x, x));
+  x = fmaxf(x, dpp_move<0x142, 0xa>(x, x));
+  x = fmaxf(x, dpp_move<0x143, 0xc>(x, x));
+  return lane_value(x, kWave - 1);
 }
 
 // ---- exact power-of-two scales (range of the 16-bit matrix operands) ----------------------

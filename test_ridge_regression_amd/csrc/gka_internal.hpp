@@ -39,8 +39,6 @@ struct FwdPlan {
   int J;  // chunks per segment
   size_t ws_bytes;
   size_t order_off;  // packed batches: byte offset of the dispatch order in the workspace
-  bool split;        // token walk + output pass (bf16, chunks of 64): phi lives in the workspace
-  size_t phi_off;    // byte offset of phi [rows][H] floats in the workspace (split plans)
 };
 
 // Arguments of the fused chunk walk (one workgroup per (segment, batch row x head)).
@@ -68,11 +66,6 @@ struct WalkArgs {
   float* resid;           // optional residual norms ||q_t - A_t x_i||, [B, T, H, iters + 1]
   const int* cu;          // packed batches: sequence b is rows [cu[b], cu[b+1]) (NULL: dense)
   const int* order;       // packed batches: sequences by decreasing length (NULL: in order)
-  // Token walk and output pass (bf16, chunks of 64): the walk leaves every token's solve
-  // y_t (fp16, largest element in [1, 2)) in o's row and phi_t in phi [rows][H], with
-  // x_t = phi_t y_t the solution of (H_t + a ||H_t||_F I) x_t = q_t; the output pass turns them
-  // into o_t = U_t x_t
-  float* phi;
 };
 
 // The last segment holding tokens of a sequence of len tokens (segments of J chunks of C): -1
@@ -113,16 +106,10 @@ constexpr int kMaxOrdered = 4096;
 hipError_t launch_order(const int* cu, int B, int Tmax, int* order, hipStream_t stream);
 
 // The chunk walk with token-owning waves (bf16 inputs, chunks of 64 tokens, D = 32, 64, 128):
-// the key side of the feature-split walk of launch_walk (H state, ||H_t||_F, the solves); its
-// solves go to a.o and a.phi for launch_output, which produces o and the U state.
+// same arguments and results as the feature-split walk of launch_walk.
 bool walk_tok_supported(const FwdPlan& pl);
 hipError_t launch_walk_tok(const FwdPlan& pl, const WalkArgs& a, const ChebConsts& cc,
                            hipStream_t stream);
-
-// Output pass of the token walk's configurations: o_t = U_t x_t from the solves the walk left
-// (a.o holds y, a.phi the per-token factors), with the U recurrence from the segment start
-// (a.in_u, NULL = zero) and the final U to a.out_u (optional).
-hipError_t launch_output(const FwdPlan& pl, const WalkArgs& a, hipStream_t stream);
 
 // Segment summaries of the token-owning walk's configurations (bf16, chunks of 64, D = 64, 128),
 // for segments 0 .. S-2; same arguments and results as launch_walk with summary = true.

@@ -1,17 +1,17 @@
-// Chunk walk of gka_fwd_chunked with token-owning waves (bf16 inputs, chunks of 64 tokens): the
-// key-side recurrence and the Chebyshev solves. The value side (o_t = U_t x_t and the carry of U)
-// is the output pass of gka_out.hip, which reads the solves this walk leaves in o's rows.
+// Chunk walk of gka_fwd_chunked with token-owning waves (bf16 inputs, chunks of 64 tokens).
 //
 // The chunk algebra follows "Methodology in Plain English" and "Key Contributions" 3 on the
 // ai.info summary of arXiv 2511.21016: per chunk,
 //   Y_t   = s_t H0hat R_t + sum_{s<=t} Mhat_ts (k_s . R_t) k_s    (the system minus a I, on R_t)
 //   n_t^2 = gamma_t^2 n_{t-1}^2 + 2 gamma_t beta_t k_t^T H_{t-1} k_t + beta_t^2 ||k_t||^4
 //           (an affine scan over t)
-//   carry H <- Gam_C H + K^T diag(w) K
-// with H0hat = H0 / n0, s_t = Gam_t n0 / n_t, Mhat_ts = 2^(cl_t - cl_s) beta_s / n_t and carry
-// weights w_s = 2^(cl_C - cl_s) beta_s. beta_t is the optional write gate ("Main Findings" on the
-// ai.info summary: H_t = gamma_t H_{t-1} + beta_t k_t k_t^T; 1 without it); it enters only
-// through these weights, so the key rows stay exact operands.
+//   o_t   = s_t U0hat X_t + sum_{s<=t} Mhat_ts (k_s . X_t) v_s
+//   carry H <- Gam_C H + K^T diag(w) K,  U^T <- Gam_C U^T + K^T diag(w) V
+// with H0hat = H0 / n0, U0hat = U0 / n0, s_t = Gam_t n0 / n_t, Mhat_ts = 2^(cl_t - cl_s) beta_s /
+// n_t and carry weights w_s = 2^(cl_C - cl_s) beta_s. beta_t is the optional write gate ("Main
+// Findings" on the ai.info summary: H_t = gamma_t H_{t-1} + beta_t k_t k_t^T, likewise U_t; 1
+// without it); it enters only through these weights, so the key and value rows stay exact
+// operands.
 //
 // Every token's Chebyshev iteration is a system of its own: Y_t needs R_t and the chunk's
 // shared matrices (H0hat, K), nothing of the other tokens' iterates. Wave w (one per SIMD)
@@ -24,22 +24,22 @@
 // for index 16 (j / 4) + 4 g + j % 4. The accumulator of a 16x16 output tile holds, in lane
 // (column c, group g), rows 4g..4g+3; with this order the B fragment of block kk of a
 // feature x token matrix is the accumulator rows of tiles 2kk and 2kk+1 of the same lane.
-// The A operands are laid out to match: K and H0hat are staged in LDS with their feature columns
-// permuted the same way (a fragment is one 16-byte read), and K^T fragments in the permuted token
-// order come from transposing LDS reads.
+// The A operands are laid out to match: K and H0hat (U0hat) are staged in LDS with their
+// feature columns permuted the same way (a fragment is one 16-byte read), and K^T / V^T
+// fragments in the permuted token order come from transposing LDS reads.
 //
-// Range of the 16-bit operands: the keys of a chunk are staged times 2^-e (e from the chunk's
-// largest |k|, so the staged rows lie below 2) and the queries of a token times 2^-e_t; both are
-// exact powers of two, undone in float32 where the products are used (norm terms, mask, carry
-// weights) or carried into the solve's own scale. Any bf16 input whose squares stay in float32's
-// range is therefore an fp16 operand of full precision.
+// Range of the 16-bit operands: the keys and the values of a chunk are staged times 2^-e (e from
+// the chunk's largest |k|, |v|, so the staged rows lie below 2), U0hat times 2^-e from the
+// largest |U0| entry, the queries and the iterate of a token times 2^-e_t; all are exact powers
+// of two, undone in float32 where the products are used (norm terms, mask, carry, output).
+// Any bf16 input whose products stay in float32's range is therefore an fp16 operand of full
+// precision.
 //
-// Per chunk: stage K (fp16), gates and H0hat; the norm phase (k_t^T H0hat k_t from the resident
-// H0hat fragments, the Gram tiles of the own tokens) and a scan over the 64 tokens; the carry
-// advances the float32 H state (held as accumulator tiles, a quarter per wave); the next chunk's
-// keys and gates are loaded into registers; the Chebyshev loop; the solve of every token is
-// written, scaled to lie below 2 in magnitude, as fp16 to its row of o, with its scale over
-// ||H_t||_F in a per-token float.
+// Per chunk: stage K, V (fp16), gates and H0hat; the norm phase (k_t^T H0hat k_t from the
+// resident H0hat fragments, the Gram tiles of the own tokens) and a scan over the 64 tokens;
+// U0hat is staged; the carry advances the float32 state (H as accumulator tiles in registers,
+// U^T in LDS); the Chebyshev loop; the output products. The next chunk's K, V and gates are
+// loaded into registers during the output phase and staged at the top of the next chunk.
 #include "gka_internal.hpp"
 
 #include <type_traits>
@@ -67,10 +67,12 @@ struct TokCfg {
   static constexpr size_t szTok = (size_t)C * LDD * 2;
   static constexpr size_t szHs = (size_t)D * LDD * 2;
   static constexpr size_t oKp = 0;               // K, token-major, permuted features (fp16)
-  static constexpr size_t oHs = oKp + szTok;     // H0hat: row-major, permuted columns (fp16)
-  static constexpr size_t oKraw = oHs + szHs;    // the next chunk's key rows as loaded (bf16)
-  static constexpr size_t oGraw = oKraw + (size_t)C * D * 2;  // its gates, write gates [C]
-  static constexpr size_t oVec = oGraw + (size_t)2 * C * sizeof(float);
+  static constexpr size_t oVp = oKp + szTok;     // V, token-major (fp16)
+  static constexpr size_t oHs = oVp + szTok;     // H0hat, then U0hat: row-major, permuted columns
+  static constexpr int LDC = C + 8;              // row stride of the [D][C] fp16 tile
+  static constexpr size_t oVT = oHs + szHs;      // V^T: row-major, tokens permuted (fp16)
+  static constexpr size_t oUs = oVT + (size_t)D * LDC * 2;  // float32 U^T state, tile-major
+  static constexpr size_t oVec = oUs + (size_t)D * D * sizeof(float);
   static constexpr size_t szVec = (size_t)(5 * C + 16 + 4 * 64) * sizeof(float);
   static constexpr size_t bytes = oVec + szVec;  // dynamic LDS
   static_assert(D % 32 == 0 && NST >= 1, "unsupported D");
@@ -118,6 +120,18 @@ __device__ inline f16x8 pack8(f32x4 a, f32x4 b) {
                (f16)b[3]};
 }
 
+template <int I>
+using IC = std::integral_constant<int, I>;
+
+// f(IC<I>), ..., f(IC<N - 1>): a loop whose index is a compile-time constant in the body
+template <int I, int N, typename F>
+__device__ inline void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(IC<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
 // RES: residual mode, which also writes ||q_t - A_t x_i|| for i = 0..iters to A.resid
 template <int D, bool RES>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
@@ -127,20 +141,22 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
   typedef f16x8 Frag;
   constexpr int C = Cfg::C, NW = Cfg::NW, NT = Cfg::NT, FT = Cfg::FT, KD = Cfg::KD;
   constexpr int KC = Cfg::KC, ST = Cfg::ST, LDD = Cfg::LDD, UPR = Cfg::UPR, NU = Cfg::NU;
-  constexpr int NRT = Cfg::NRT, NCT = Cfg::NCT;
+  constexpr int NRT = Cfg::NRT, NCT = Cfg::NCT, LDC = Cfg::LDC;
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   f16* Kp = reinterpret_cast<f16*>(smem + Cfg::oKp);
+  f16* Vp = reinterpret_cast<f16*>(smem + Cfg::oVp);
   f16* Hs = reinterpret_cast<f16*>(smem + Cfg::oHs);
-  const bf16x8* Kraw = reinterpret_cast<const bf16x8*>(smem + Cfg::oKraw);  // unit u at [u]
-  const float* Graw = reinterpret_cast<const float*>(smem + Cfg::oGraw);    // [C] gates
-  const float* Braw = Graw + C;                                               // [C] write gates
+  f16* VT = reinterpret_cast<f16*>(smem + Cfg::oVT);
+  float* Us = reinterpret_cast<float*>(smem + Cfg::oUs);
   float* v_cl = reinterpret_cast<float*>(smem + Cfg::oVec);  // [C] in-chunk log2 gate prefix
   float* v_w = v_cl + C;    // [C] carry weights 2^(cl_C - cl_s) beta_s
   float* v_a = v_w + C;     // [C] n^2 scan: a_t = gamma_t^2
   float* v_b = v_a + C;     // [C] n^2 scan: b_t
   float* v_bt = v_b + C;    // [C] write gates beta_s (1 without them)
-  float* v_sc = v_bt + C;   // [16] scratch: [0, NW) state norms, [4, 4 + NW) largest |k| per wave
+  // [16] scratch: [0, NW) state norms; per wave the largest |k| [4 + w], |U| [8 + w] and
+  // |v| [12 + w]
+  float* v_sc = v_bt + C;
   float* v_coef = v_sc + 16;  // [iters][4] krs, kys, bts of each iteration (rescaled form)
 
   const int seg = blockIdx.x;
@@ -173,33 +189,96 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
   const uint32_t tok_bytes = (uint32_t)Hn * D * 2u;  // 64 rows span < 2^31 bytes (host check)
   const bf16* qg = static_cast<const bf16*>(A.q);
   const bf16* kg = static_cast<const bf16*>(A.k);
-  f16* yg = static_cast<f16*>(A.o);  // the solves (fp16) go to o's rows; the output pass reads
-                                     // them back and writes o over them
+  const bf16* vg = static_cast<const bf16*>(A.v);
+  bf16* og = static_cast<bf16*>(A.o);
 
-  // ---- float32 state: tiles (a0 + jr, b0 + jc) of H, held in registers ----------------------
-  f32x4 Hst[NRT][NCT];
+  // ---- float32 state: the wave's tiles of H, held in registers. H is symmetric: at D = 128
+  // (TRI) the waves hold only the 36 tiles on and above the diagonal, wave w the nine of row
+  // tiles w and 7 - w (from the diagonal to the last column); the mirror tiles are written from
+  // them where H is staged or stored. Otherwise the wave holds the block (a0 + jr, b0 + jc),
+  // jr < NRT, jc < NCT, of the full grid. The tiles are kept times 2^-2E (E: the key scale of
+  // the last carry), so that the carry needs no second rescaling ------------------------------
+  constexpr bool TRI = D == 128;
+  constexpr int NTL = TRI ? 9 : NRT * NCT;  // tiles per wave
+  const int wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  // f(j, a, b, r) for the wave's tiles j = 0 .. NTL - 1: tile (a, b) holds H[16a + 4lg + i]
+  // [16b + lr] (i = 0..3) in a lane; r selects the A operand of its row tile in the carry. With
+  // TRI, j, a, b and r are compile-time constants (one instantiation per wave).
+  auto for_tiles = [&](auto f) {
+    if constexpr (TRI) {
+      auto run = [&](auto W) {
+        constexpr int w = decltype(W)::value, n0 = FT - w;
+        static_for<0, NTL>([&](auto J) {
+          constexpr int j = decltype(J)::value;
+          f(J, IC<(j < n0 ? w : FT - 1 - w)>{}, IC<(j < n0 ? w + j : FT - 1 - w + (j - n0))>{},
+            IC<(j < n0 ? 0 : 1)>{});
+        });
+      };
+      switch (wave_u) {
+        case 0: run(IC<0>{}); break;
+        case 1: run(IC<1>{}); break;
+        case 2: run(IC<2>{}); break;
+        default: run(IC<3>{}); break;
+      }
+    } else {
+      static_for<0, NTL>([&](auto J) {
+        constexpr int j = decltype(J)::value;
+        f(J, a0 + j / NCT, b0 + j % NCT, IC<j / NCT>{});
+      });
+    }
+  };
+  f32x4 Hst[NTL];
 #pragma unroll
-  for (int jr = 0; jr < NRT; ++jr)
-#pragma unroll
-    for (int jc = 0; jc < NCT; ++jc) Hst[jr][jc] = f32x4{0.f, 0.f, 0.f, 0.f};
+  for (int j = 0; j < NTL; ++j) Hst[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+  int Ek = 0;  // H = Hst 2^2Ek
+  // ---- U^T (rows = key features) in LDS, the wave's tiles only: the row tiles of its H tiles
+  // (w and 7 - w with TRI, else a0 + jr) across every column, one f32x4 per lane and tile,
+  // tile-major. Kept times 2^-Eu (Eu: key plus value scale of the last carry) -----------------
+  constexpr int NUTL = TRI ? 2 * FT : NRT * NCT;  // U tiles per wave
+  auto urow = [&](int r) { return TRI ? (r == 0 ? wave_u : FT - 1 - wave_u) : a0 + r; };
+  // f(j, a, b, r) for the wave's U tiles j = 0 .. NUTL - 1 (row tile a = urow(r), column b)
+  auto for_utiles = [&](auto f) {
+    static_for<0, NUTL>([&](auto J) {
+      constexpr int j = decltype(J)::value;
+      constexpr int r = TRI ? j / FT : j / NCT;
+      f(J, urow(r), TRI ? j % FT : b0 + j % NCT, IC<r>{});
+    });
+  };
+  auto us_tile = [&](int j) {
+    return reinterpret_cast<f32x4*>(Us) + ((j * NW + wave_u) * kWave + lane);
+  };
+  int Eu = 0;  // U = Us 2^Eu
   float n0sq = 0.0f;
   {
     float sq = 0.0f;
     if (A.in_h) {
       const float* ih = A.in_h + bh * A.in_bh + seg * A.in_seg;
-#pragma unroll
-      for (int jr = 0; jr < NRT; ++jr)
-#pragma unroll
-        for (int jc = 0; jc < NCT; ++jc) {
-          // H[r..r+3][c] is read as H[c][r..r+3] (symmetric)
-          const size_t o = (size_t)(16 * (b0 + jc) + lr) * D + 16 * (a0 + jr) + 4 * lg;
-          Hst[jr][jc] = *reinterpret_cast<const f32x4*>(ih + o);
-          const f32x4 x = Hst[jr][jc];
-          sq += x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3];
-        }
+      for_tiles([&](auto J, auto a, auto b, auto) {
+        constexpr int j = decltype(J)::value;
+        // H[r..r+3][c] is read as H[c][r..r+3] (symmetric)
+        const size_t o = (size_t)(16 * (int)b + lr) * D + 16 * (int)a + 4 * lg;
+        Hst[j] = *reinterpret_cast<const f32x4*>(ih + o);
+        const f32x4 x = Hst[j];
+        const float m = TRI && (int)a != (int)b ? 2.0f : 1.0f;  // an upper tile stands for two
+        sq += m * (x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3]);
+      });
     }
     sq = wave_sum(sq);
     if (lane == 0) v_sc[wave] = sq;
+    // U^T[r..r+3][c] = U[c][r..r+3]
+    float um = 0.0f;
+    for_utiles([&](auto J, int a, int b, auto) {
+      constexpr int j = decltype(J)::value;
+      f32x4 x = {0.f, 0.f, 0.f, 0.f};
+      if (A.in_u) {
+        const float* iu = A.in_u + bh * A.in_bh + seg * A.in_seg;
+        x = *reinterpret_cast<const f32x4*>(iu + (size_t)(16 * b + lr) * D + 16 * a + 4 * lg);
+      }
+      *us_tile(j) = x;
+      um = fmaxf(um, fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))));
+    });
+    um = wave_max(um);
+    if (lane == 0) v_sc[8 + wave_u] = um;
     // Chebyshev coefficients, read from LDS in the loop (scalar loads in flight would make
     // every wait for an LDS fragment a wait for all of them)
     if (tid < cc.iters_rs) {
@@ -216,77 +295,107 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
     }
   }
 
-  // The next chunk's key rows (16-byte units, consecutive threads along a token row) and gates
-  // (lane = token) are prefetched straight into LDS by direct loads, issued after the chunk's
-  // staging and in flight through its loop, so that no registers are held for them. A wave
-  // waits for its own loads (vmcnt) before it reads them (the largest |k| below); the barrier
-  // at the top of the next chunk orders them for the other waves. Lanes of rows past the end of
-  // the sequence load nothing: those rows are zeroed where they are read.
-  // (the write gates are read from the gates when there are none, and then not used)
+  // The next chunk's K and V (16-byte units, consecutive threads along a token row) and gates
+  // (lane = token) are loaded into registers at the start of the output phase, where few
+  // registers are live, and staged at the top of the next chunk. Rows past the end of the
+  // sequence are zero, with gate 1.
+  bf16x8 kin[NU / NT], vin[NU / NT];
+  float gin = 1.0f, bin = 1.0f;  // gate and write gate of token `lane`
+  // the write gates are read from the gates when there are none (and then not used)
   const float* bsrc = A.beta ? A.beta : A.gamma;
-  typedef __attribute__((address_space(3))) void lds_void;
-  auto prefetch_k = [&](int chn) {
-    refresh();
-    const int t0n = chn * C;
-    const int nvn = min(C, Tlen - t0n);
-    const bf16* src = kg + (seq0 + t0n) * tok_stride + (long long)h * D;
+  auto load_kv = [&](int chn) {
+    refresh();  // keeps the per-lane addresses from being hoisted out of the chunk loop
+    // Bounds-checked buffer loads: rows past the end of the sequence (or of the segment) read
+    // as 0, with no branch, so the compiler counts these loads and waits for exactly them
+    // where they are used. The values are defined on every path.
+    const int chv = chn < c_end ? chn : c_end - 1;
+    const int t0n = chv * C;
+    const int nvn = chn < c_end ? min(C, Tlen - t0n) : 0;
+    const long long row0 = (seq0 + t0n) * tok_stride + (long long)h * D;
+    const uint32_t valid = nvn > 0 ? (uint32_t)(nvn - 1) * tok_bytes + D * 2u : 0u;
+    const auto rk = buffer_rsrc(kg + row0, valid);
+    const auto rv = buffer_rsrc(vg + row0, valid);
 #pragma unroll
     for (int k = 0; k < NU / NT; ++k) {
       const int u = tid + k * NT;
       const int tt = (uint32_t)u / UPR, cu = (uint32_t)u % UPR;  // u >= 0
-      const uint32_t base = __builtin_amdgcn_readfirstlane(
-          (uint32_t)(uintptr_t)(lds_void*)(Kraw + (u - lane)));
-      if (tt < nvn) dma_load16_so(src, (uint32_t)tt * tok_bytes + (uint32_t)cu * 16u, base);
+      const uint32_t off = (uint32_t)tt * tok_bytes + (uint32_t)cu * 16u;
+      kin[k] = buffer_load16<bf16x8>(rk, off);
+      vin[k] = buffer_load16<bf16x8>(rv, off);
     }
-    if (wave < 2) {
-      const float* gs = (wave == 0 ? A.gamma : bsrc) + (seq0 + t0n) * Hn + h;
-      const uint32_t base = __builtin_amdgcn_readfirstlane(
-          (uint32_t)(uintptr_t)(lds_void*)(wave == 0 ? Graw : Braw));
-      if (lane < nvn) dma_load4_so(gs, (uint32_t)lane * Hn * 4u, base);
-    }
+    const uint32_t gvalid = nvn > 0 ? (uint32_t)(nvn - 1) * Hn * 4u + 4u : 0u;
+    const auto rg = buffer_rsrc(A.gamma + (seq0 + t0n) * Hn + h, gvalid);
+    const auto rb = buffer_rsrc(bsrc + (seq0 + t0n) * Hn + h, gvalid);
+    gin = buffer_load4f(rg, (uint32_t)lane * Hn * 4u);
+    bin = buffer_load4f(rb, (uint32_t)lane * Hn * 4u);
   };
-  // the largest |k| of the prefetched rows of chunk chn (this wave's units), to v_sc[4 + wave]
-  auto kmax_put = [&](int chn) {
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // this wave's direct loads have landed
-    refresh();
-    const int nvn = min(C, Tlen - chn * C);
-    float m = 0.0f;
+  // the largest |k| and |v| of the loaded rows (this wave's units), to v_sc[4 + wave] and
+  // v_sc[12 + wave]: read by every wave after the barrier at the top of the chunk
+  auto kvmax_put = [&]() {
+    float mk = 0.0f, mv = 0.0f;
 #pragma unroll
-    for (int k = 0; k < NU / NT; ++k) {
-      const int u = tid + k * NT;
-      const bf16x8 kv = Kraw[u];
-      float um = 0.0f;
+    for (int k = 0; k < NU / NT; ++k)
 #pragma unroll
-      for (int i = 0; i < 8; ++i) um = fmaxf(um, fabsf((float)kv[i]));
-      if ((int)((uint32_t)u / UPR) < nvn) m = fmaxf(m, um);  // rows past the end hold stale data
+      for (int i = 0; i < 8; ++i) {
+        mk = fmaxf(mk, fabsf((float)kin[k][i]));
+        mv = fmaxf(mv, fabsf((float)vin[k][i]));
+      }
+    mk = wave_max(mk);
+    mv = wave_max(mv);
+    if (lane == 0) {
+      v_sc[4 + wave_u] = mk;
+      v_sc[12 + wave_u] = mv;
     }
-    m = wave_max(m);
-    if (lane == 0) v_sc[4 + wave] = m;
   };
-  // state tiles (times sc) -> Hs as fp16 rows e = column index of the tile, permuted columns
-  auto stage_tile = [&](int jr, int jc, f32x4 x) {
-    f16x4 y = {(f16)x[0], (f16)x[1], (f16)x[2], (f16)x[3]};
-    *reinterpret_cast<f16x4*>(Hs + (16 * (b0 + jc) + lr) * LDD + pcol(16 * (a0 + jr) + 4 * lg)) = y;
-  };
+  // state tiles (times sc) -> Hs as fp16: row e of Hs holds H[e][*] (permuted columns); tile
+  // (a, b) gives rows 16b + lr (H[16b + lr][16a + 4lg ..] = H[16a + 4lg ..][16b + lr]) and, for
+  // an upper tile of the symmetric scheme, its mirror rows 16a + 4lg + i
   auto stage_h = [&](float sc) {
+    for_tiles([&](auto J, auto a, auto b, auto) {
+      constexpr int j = decltype(J)::value;
+      const f32x4 x = Hst[j] * sc;
+      const f16x4 y = {(f16)x[0], (f16)x[1], (f16)x[2], (f16)x[3]};
+      *reinterpret_cast<f16x4*>(Hs + (16 * (int)b + lr) * LDD + pcol(16 * (int)a + 4 * lg)) = y;
+      if constexpr (TRI) {
+        if constexpr (decltype(a)::value != decltype(b)::value) {
 #pragma unroll
-    for (int jr = 0; jr < NRT; ++jr)
+          for (int i = 0; i < 4; ++i) Hs[(16 * (int)a + 4 * lg + i) * LDD + pcol(16 * (int)b + lr)] = y[i];
+        }
+      }
+    });
+  };
+  // U^T tiles (times sc) -> Hs as fp16: row v of Hs holds U[v][*] (permuted columns); tile
+  // (a, b) holds U[16b + lr][16a + 4lg ..]
+  auto stage_u = [&](float sc) {
+    f32x4 x[NUTL];  // all reads first: one wait covers them
 #pragma unroll
-      for (int jc = 0; jc < NCT; ++jc) stage_tile(jr, jc, Hst[jr][jc] * sc);
+    for (int j = 0; j < NUTL; ++j) x[j] = *us_tile(j);
+    for_utiles([&](auto J, int a, int b, auto) {
+      constexpr int j = decltype(J)::value;
+      const f32x4 y = x[j] * sc;
+      *reinterpret_cast<f16x4*>(Hs + (16 * b + lr) * LDD + pcol(16 * a + 4 * lg)) =
+          f16x4{(f16)y[0], (f16)y[1], (f16)y[2], (f16)y[3]};
+    });
   };
   // A fragment of K (rows = tokens 16 sb + lr) over feature block kk
   auto frag_k = [&](int sb, int kk) {
     return *reinterpret_cast<const Frag*>(Kp + (16 * sb + lr) * LDD + 32 * kk + 8 * lg);
   };
-  // A fragment of K^T (rows = features 16 ft + lr) over token block kc, permuted token order
-  // (k-slot j of lane group lg: token 32 kc + 16 (j / 4) + 4 lg + j % 4), by two transposing
-  // reads of K
+  // A fragment of K^T (V^T) (rows = features 16 ft + lr) over token block kc, permuted token
+  // order (k-slot j of lane group lg: token 32 kc + 16 (j / 4) + 4 lg + j % 4); K^T by two
+  // transposing reads of K, V^T from its tile
   auto frag_kt = [&](int ft, int kc) {
     return frag_trans<LDD>(Kp, 32 * kc + 4 * lg, 32 * kc + 16 + 4 * lg, pcol(16 * ft + 4 * (lr & 3)), lr);
   };
+  auto frag_vt = [&](int ft, int kc) {
+    return *reinterpret_cast<const Frag*>(VT + (16 * ft + lr) * LDC + 32 * kc + 8 * lg);
+  };
 
-  prefetch_k(c_begin);
-  kmax_put(c_begin);
+  load_kv(c_begin);
+  kvmax_put();
+  // nothing in flight on entry to the chunk loop, so that the compiler's wait at its top counts
+  // only the loads issued in the output phase of the previous chunk (and not its stores)
+  __builtin_amdgcn_s_waitcnt((7 << 4) | (15 << 8));  // vmcnt(0)
 
   for (int ch = c_begin; ch < c_end; ++ch) {
     refresh();
@@ -294,21 +403,28 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
     const int nv = min(C, Tlen - t0);
     const float n0 = sqrtf(n0sq);
     const float n0inv = n0 > 0.0f ? 1.0f / n0 : 0.0f;
-    lds_barrier();  // the last chunk's LDS reads are done; v_sc holds this chunk's |k| maxima
+    lds_barrier();  // the last chunk's LDS reads are done; v_sc holds this chunk's maxima
 
-    // ---- key scale 2^-ke of the chunk: the staged rows lie below 2 in magnitude -------------
-    float km = v_sc[4];
+    // ---- scales of the chunk: keys 2^-ke and values 2^-ve (the staged rows lie below 2 in
+    // magnitude), U0hat 2^-ue (its largest element lies below 2) -----------------------------
+    float km = v_sc[4], vm = v_sc[12], umx = v_sc[8];
 #pragma unroll
-    for (int w = 1; w < NW; ++w) km = fmaxf(km, v_sc[4 + w]);
-    const int ke = pow2_exponent(km, 30);
-    const float kinv = exp2_int(-ke), ks2 = exp2_int(2 * ke);
+    for (int w = 1; w < NW; ++w) {
+      km = fmaxf(km, v_sc[4 + w]);
+      vm = fmaxf(vm, v_sc[12 + w]);
+      umx = fmaxf(umx, v_sc[8 + w]);
+    }
+    const int ke = pow2_exponent(km, 30), ve = pow2_exponent(vm, 60);
+    const float kinv = exp2_int(-ke), ks2 = exp2_int(2 * ke), vinv = exp2_int(-ve);
+    // U0 / n0 = Us 2^Eu / n0: its largest element is umx 2^Eu n0inv
+    const int ue = pow2_exponent(umx * exp2_int(Eu) * n0inv, 100);
 
     // ---- gate prefix (every wave; lane = token) ---------------------------------------------
     float g_l = 1.0f, l2 = 0.0f, bt_l = 1.0f;  // tokens past the end: gamma = 1, k = q = 0
     if (lane < nv) {
-      g_l = Graw[lane];
+      g_l = gin;
       l2 = log2_gate(g_l);
-      if (A.beta) bt_l = Braw[lane];
+      if (A.beta) bt_l = bin;
     }
     const float cl = scan_add<kWave>(l2);
     const float clast = lane_value(cl, C - 1);
@@ -319,23 +435,24 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
       v_w[lane] = fast_exp2(fminf(clast - cl, 0.0f)) * bt_l;
       v_bt[lane] = bt_l;
     }
-    // ---- stage K (fp16, times 2^-ke, permuted features) ------------------------------------
+    // ---- stage K (fp16, times 2^-ke, permuted features) and V (fp16, times 2^-ve) --------
 #pragma unroll
     for (int k = 0; k < NU / NT; ++k) {
       const int u = tid + k * NT;
       const int tt = (uint32_t)u / UPR, cu = (uint32_t)u % UPR;  // u >= 0
-      const bf16x8 kv = Kraw[u];
-      f16x8 ko;
+      const bf16x8 kv = kin[k], vv = vin[k];  // rows past the end were read as 0
+      f16x8 ko, vo;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) ko[i] = (f16)((float)kv[i] * kinv);
-      if (tt >= nv) ko = f16x8{};  // rows past the end hold stale data (never loaded): zero them
+      for (int i = 0; i < 8; ++i) {
+        ko[i] = (f16)((float)kv[i] * kinv);
+        vo[i] = (f16)((float)vv[i] * vinv);
+      }
+      *reinterpret_cast<f16x8*>(Vp + tt * LDD + 8 * cu) = vo;
       *reinterpret_cast<f16x4*>(Kp + tt * LDD + pcol(8 * cu)) = f16x4{ko[0], ko[1], ko[2], ko[3]};
       *reinterpret_cast<f16x4*>(Kp + tt * LDD + pcol(8 * cu + 4)) = f16x4{ko[4], ko[5], ko[6], ko[7]};
     }
-    stage_h(n0inv);  // H0hat
+    stage_h(n0inv * exp2_int(2 * Ek));  // H0hat
     lds_barrier();
-    // the next chunk's keys and gates: in flight through this chunk
-    if (ch + 1 < c_end) prefetch_k(ch + 1);
 
     refresh();
 
@@ -419,9 +536,21 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
                  kdt * kdt;
       }
     }
-    // ---- every K^T fragment of the chunk, resident in registers until the loop ends (after the
-    // norm phase's products, which do not need them) ------------------------------------------
+    // ---- V^T with the tokens in the permuted order (fragments from transposing reads of V,
+    // written back as rows: every later operand of it is one 16-byte read), and every K^T
+    // fragment of the chunk, resident in registers until the loop ends (after the norm
+    // phase's products, which do not need them) ----------------------------------------------
     refresh();
+#pragma unroll
+    for (int k = 0; k < (FT * KC + NW - 1) / NW; ++k) {
+      const int phi = wave + k * NW;
+      if (FT * KC % NW == 0 || phi < FT * KC) {
+        const int ft = phi / KC, kc = phi % KC;
+        const Frag g = frag_trans<LDD>(Vp, 32 * kc + 4 * lg, 32 * kc + 16 + 4 * lg,
+                                       16 * ft + 4 * (lr & 3), lr);
+        *reinterpret_cast<Frag*>(VT + (16 * ft + lr) * LDC + 32 * kc + 8 * lg) = g;
+      }
+    }
     Frag ktr[KC][FT];
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc)
@@ -460,6 +589,8 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
         }
       }
     }
+    // U0hat times 2^-ue (every wave has read its H0hat fragments)
+    stage_u(exp2_int(Eu - ue) * n0inv);
 
     // ---- queries of the own token, accumulator layout: Q[t][16 ft + 4 lg .. + 3], loaded
     // during the carry's products and consumed at the start of the loop ----------------------
@@ -473,19 +604,21 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
       for (int ft = 0; ft < FT; ++ft) Qraw[ft] = buffer_load8<bf16x4>(rq, qoff + 32u * ft);
     }
     // ---- state carry: H <- Gam_C H + K^T diag(w) K ------------------------------------------
-    // (on the staged keys: the product is accumulated onto Gam_C H / 2^2ke, and the sum is
-    // multiplied by 2^2ke)
+    // (on the staged keys k' = 2^-ke k: the tiles, kept times 2^-2E, are rescaled to 2^-2ke and
+    // the product on k' added; E becomes ke)
     {
-      // A operands (w K)^T of the own row tiles, split hi + lo; tokens in the permuted order
+      // A operands (w K)^T of the wave's row tiles, split hi + lo; tokens in the permuted order
       // of the K^T tile (k-slot j of lane group lg: token 32 kc + 16 (j / 4) + 4 lg + j % 4)
-      Frag awh[NRT][KC], awl[NRT][KC];
+      constexpr int NR = TRI ? 2 : NRT;
+      Frag awh[NR][KC], awl[NR][KC];
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
         const f32x4 w0 = *reinterpret_cast<const f32x4*>(v_w + 32 * kc + 4 * lg);
         const f32x4 w1 = *reinterpret_cast<const f32x4*>(v_w + 32 * kc + 16 + 4 * lg);
 #pragma unroll
-        for (int jr = 0; jr < NRT; ++jr) {
-          const Frag kf = frag_kt(a0 + jr, kc);
+        for (int jr = 0; jr < NR; ++jr) {
+          const int ar = TRI ? (jr == 0 ? wave_u : FT - 1 - wave_u) : a0 + jr;
+          const Frag kf = frag_kt(ar, kc);
 #pragma unroll
           for (int j = 0; j < 8; ++j) {
             const float x = (float)kf[j] * (j < 4 ? w0[j] : w1[j - 4]);
@@ -494,37 +627,73 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
           }
         }
       }
-      // The K operands of column tile bc are the resident K^T fragments of feature tile bc
-      // (K[s][16 bc + lr], the same token slots) when the wave's column tiles are all of them
-      // (b0 = 0), else read again.
-      const float gsc = gC * exp2_int(-2 * ke);
-#pragma unroll
-      for (int jc = 0; jc < NCT; ++jc) {
+      // The K operands of column tile b are the resident K^T fragments of feature tile b
+      // (K[s][16 b + lr], the same token slots) where b is a compile-time constant, else read
+      // again.
+      const float gsc = gC * exp2_int(2 * (Ek - ke));
+      for_tiles([&](auto J, auto a, auto b, auto R) {
+        constexpr int j = decltype(J)::value, r = decltype(R)::value;
         Frag bk[KC];
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) {
-          if constexpr (NCT == FT) {
-            bk[kc] = ktr[kc][jc];
+          if constexpr (TRI) {
+            bk[kc] = ktr[kc][decltype(b)::value];
+          } else if constexpr (NCT == FT) {
+            bk[kc] = ktr[kc][j % NCT];
           } else {
-            bk[kc] = frag_kt(b0 + jc, kc);
+            bk[kc] = frag_kt((int)b, kc);
           }
         }
-        f32x4 hacc[NRT];
+        f32x4 hacc = Hst[j] * gsc;
 #pragma unroll
-        for (int jr = 0; jr < NRT; ++jr) hacc[jr] = Hst[jr][jc] * gsc;
+        for (int kc = 0; kc < KC; ++kc) {
+          hacc = M::mma(awh[r][kc], bk[kc], hacc);
+          hacc = M::mma(awl[r][kc], bk[kc], hacc);
+        }
+        Hst[j] = hacc;
+        if constexpr (Cfg::PIN) keep_in_agpr(Hst[j]);
+      });
+      Ek = ke;
+      // U^T tiles: the same A operands against the V^T fragments of their column tiles, on
+      // Gam_C U^T rescaled to the frame 2^(ke + ve) of the product; the largest |U| of the
+      // wave's tiles to v_sc[8 + wave] for the next chunk's U0hat. Column by column: the V^T
+      // fragments and U^T tiles of the next column are read while the current one's products
+      // run (double-buffered), and the rows of a column share them.
+      const float usc = gC * exp2_int(Eu - ke - ve);
+      constexpr int NUR = TRI ? 2 : NRT, NUC = TRI ? FT : NCT;  // U row, column tiles per wave
+      float um = 0.0f;
+      Frag bv[2][KC];
+      f32x4 ub[2][NUR];
+      auto load_col = [&](int c, int buf) {
+#pragma unroll
+        for (int kc = 0; kc < KC; ++kc) bv[buf][kc] = frag_vt(TRI ? c : b0 + c, kc);
+#pragma unroll
+        for (int r = 0; r < NUR; ++r) ub[buf][r] = *us_tile(r * NUC + c);
+      };
+      load_col(0, 0);
+#pragma unroll
+      for (int c = 0; c < NUC; ++c) {
+        if (c + 1 < NUC) load_col(c + 1, (c + 1) % 2);
+        f32x4 uacc[NUR];
+#pragma unroll
+        for (int r = 0; r < NUR; ++r) uacc[r] = ub[c % 2][r] * usc;
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
           for (int hl = 0; hl < 2; ++hl)
 #pragma unroll
-            for (int jr = 0; jr < NRT; ++jr)
-              hacc[jr] = M::mma(hl == 0 ? awh[jr][kc] : awl[jr][kc], bk[kc], hacc[jr]);
+            for (int r = 0; r < NUR; ++r)
+              uacc[r] = M::mma(hl == 0 ? awh[r][kc] : awl[r][kc], bv[c % 2][kc], uacc[r]);
 #pragma unroll
-        for (int jr = 0; jr < NRT; ++jr) {
-          Hst[jr][jc] = hacc[jr] * ks2;
-          if constexpr (Cfg::PIN) keep_in_agpr(Hst[jr][jc]);
+        for (int r = 0; r < NUR; ++r) {
+          *us_tile(r * NUC + c) = uacc[r];
+          const f32x4 x = uacc[r];
+          um = fmaxf(um, fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))));
         }
       }
+      Eu = ke + ve;
+      um = wave_max(um);
+      if (lane == 0) v_sc[8 + wave_u] = um;
     }
 
     // ---- Chebyshev loop on the residuals of the own token ----------------------------------
@@ -688,12 +857,22 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
       }
     }
 
-    // ---- the solve of the own token to o's row (fp16), scaled by 2^-xe so that its largest
-    // element lies in [1, 2); phi_t = 2^xe / ||H_t||_F (times the iterate's own scales) to the
-    // per-token array: o_t = phi_t U_t y_t ---------------------------------------------------
+    // ---- output O^T = diag(s) U0hat X^T + V^T ((K X^T) o Mhat), X split into hi + lo -------
+    // (X is taken times 2^-xe, so that its largest element lies in [1, 2), and U0hat, K and V
+    // are the staged, scaled operands: their powers of two are undone at the store)
+    // Instruction groups: (1) U0hat and K fragment reads, the split of X; (2) the K products
+    // and the V^T fragment reads; (3) the U0hat products; (4) the V^T products and the stores.
+    lds_barrier();  // U0hat is staged
+    load_kv(ch + 1);
     refresh();
-    if (ch + 1 < c_end) kmax_put(ch + 1);
     {
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+        for (int kk = 0; kk < KD; ++kk) {
+          Hres[ft][kk] = *reinterpret_cast<const Frag*>(Hs + (16 * ft + lr) * LDD + 32 * kk + 8 * lg);
+          if constexpr (Cfg::PIN) keep_in_agpr(Hres[ft][kk]);
+        }
       float xm = 0.0f;
 #pragma unroll
       for (int ft = 0; ft < FT; ++ft)
@@ -703,33 +882,95 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
       xm = fmaxf(xm, lane_read(xm, lane ^ 32));
       const int xe = pow2_exponent(xm, 100);
       const float xinv = exp2_int(-xe);
-      // (bounds-checked: the stores of tokens past the end are dropped)
-      const auto ry = buffer_rsrc(yg + (seq0 + t0) * tok_stride + (long long)h * D,
+      Frag vq[KC][FT], xh[KD], xl[KD], pf[KC];
+#pragma unroll
+      for (int kk = 0; kk < KD; ++kk) {
+        const f32x4 x0 = X[2 * kk] * xinv, x1 = X[2 * kk + 1] * xinv;
+        xh[kk] = pack8(x0, x1);
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float x = j < 4 ? x0[j] : x1[j - 4];
+          xl[kk][j] = (f16)(x - (float)xh[kk][j]);
+        }
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 pa[ST];
+#pragma unroll
+      for (int sb = 0; sb < ST; ++sb) pa[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KD; ++kk) {  // (hi and lo products not back to back)
+#pragma unroll
+        for (int sb = 0; sb < ST; ++sb) pa[sb] = M::mma(kres[kk][sb], xh[kk], pa[sb]);
+#pragma unroll
+        for (int sb = 0; sb < ST; ++sb) pa[sb] = M::mma(kres[kk][sb], xl[kk], pa[sb]);
+      }
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft) vq[kc][ft] = frag_vt(ft, kc);
+      __builtin_amdgcn_sched_barrier(0);
+      f32x4 y[FT];
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft) y[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kk = 0; kk < KD; ++kk) {
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft) y[ft] = M::mma(Hres[ft][kk], xh[kk], y[ft]);
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft) y[ft] = M::mma(Hres[ft][kk], xl[kk], y[ft]);
+      }
+      // (the loop's mask Mh carries 2^2ke, the K product 2^-ke: their product is the masked
+      // K X^T times 2^ke)
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) pf[kc] = pack8(pa[2 * kc] * Mh[2 * kc], pa[2 * kc + 1] * Mh[2 * kc + 1]);
+      __builtin_amdgcn_sched_barrier(0);
+      // o = inv_xsc 2^(qe + xe + ve - ke) (s_t 2^(ue - ve + ke) U0hat' X'' + V'^T pf)
+      const float ysc = s_t * exp2_int(ue - ve + ke);
+#pragma unroll
+      for (int ft = 0; ft < FT; ++ft) y[ft] = y[ft] * ysc;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft) y[ft] = M::mma(vq[kc][ft], pf[kc], y[ft]);
+      // o of the own token straight from the accumulators: 8 bytes per lane, 32 per token row
+      // and tile (bounds-checked: the stores of tokens past the end are dropped)
+      const float osc = cc.inv_xsc * exp2_int(qe + xe) * exp2_int(ve - ke);
+      const auto ro = buffer_rsrc(og + (seq0 + t0) * tok_stride + (long long)h * D,
                                   (uint32_t)(nv - 1) * tok_bytes + D * 2u);
-      const uint32_t yoff = (uint32_t)t * tok_bytes + (uint32_t)lg * 8u;
+      const uint32_t ooff = (uint32_t)t * tok_bytes + (uint32_t)lg * 8u;
 #pragma unroll
       for (int ft = 0; ft < FT; ++ft) {
-        const f32x4 yv = X[ft] * xinv;
-        const f16x4 y4 = {(f16)yv[0], (f16)yv[1], (f16)yv[2], (f16)yv[3]};
-        buffer_store8(y4, ry, yoff + 32u * ft);
+        const f32x4 yo = y[ft] * osc;
+        const bf16x4 ov = {(bf16)yo[0], (bf16)yo[1], (bf16)yo[2], (bf16)yo[3]};
+        buffer_store8(ov, ro, ooff + 32u * ft);
       }
-      // phi_t: 2^xe undoes the solve's scale, inv_xsc the iterate's power of two, 2^qe the
-      // query's, and 1 / ||H_t||_F turns the solve of the normalised system into x_t
-      const float phi = exp2_int(xe) * cc.inv_xsc * exp2_int(qe) * ninv_t;
-      const auto rp = buffer_rsrc(A.phi + (seq0 + t0) * Hn + h, (uint32_t)(nv - 1) * Hn * 4u + 4u);
-      buffer_store4f(phi, rp, lg == 0 ? (uint32_t)t * Hn * 4u : 0x80000000u);
     }
+    kvmax_put();  // the next chunk's rows: their largest |k|, |v| for its scales
     n0sq = n2last;
   }
   if (A.out_h && seg == last) {
     float* oh = A.out_h + (size_t)bh * D * D;
+    const float sc = exp2_int(2 * Ek);
+    for_tiles([&](auto J, auto a, auto b, auto) {
+      constexpr int j = decltype(J)::value;
+      const f32x4 x = Hst[j] * sc;
+      *reinterpret_cast<f32x4*>(oh + (size_t)(16 * (int)b + lr) * D + 16 * (int)a + 4 * lg) = x;
+      if constexpr (TRI) {
+        if constexpr (decltype(a)::value != decltype(b)::value) {
 #pragma unroll
-    for (int jr = 0; jr < NRT; ++jr)
-#pragma unroll
-      for (int jc = 0; jc < NCT; ++jc) {
-        const size_t o = (size_t)(16 * (b0 + jc) + lr) * D + 16 * (a0 + jr) + 4 * lg;
-        *reinterpret_cast<f32x4*>(oh + o) = Hst[jr][jc];
+          for (int i = 0; i < 4; ++i) oh[(size_t)(16 * (int)a + 4 * lg + i) * D + 16 * (int)b + lr] = x[i];
+        }
       }
+    });
+  }
+  if (A.out_u && seg == last) {
+    float* ou = A.out_u + (size_t)bh * D * D;
+    const float sc = exp2_int(Eu);
+    for_utiles([&](auto J, int a, int b, auto) {
+      constexpr int j = decltype(J)::value;
+      // U^T[r..r+3][c] is written as U[c][r..r+3]
+      *reinterpret_cast<f32x4*>(ou + (size_t)(16 * b + lr) * D + 16 * a + 4 * lg) = *us_tile(j) * sc;
+    });
   }
   if (A.n2_out && seg == last && tid == 0) A.n2_out[bh] = n0sq;
 }

@@ -106,11 +106,6 @@ def test_fwd_empty_sequence_is_a_noop(lib):
     assert fwd(lib, params(T=0), q=None, k=None, v=None, g=None, o=None) == 0
 
 
-def phi_bytes(B, T, H):
-    """The token walk's per-token factors (bf16 with chunks of 64): B T H floats, 256-aligned."""
-    return (B * T * H * 4 + 255) // 256 * 256
-
-
 def seg_bytes(B, H, S, D):
     """Per-segment states, log2 gates and the start norm of an S-segment plan (0 for S = 1)."""
     return 0 if S == 1 else ((B * H * S * (2 * D * D + 1) + B * H) * 4 + 255) // 256 * 256
@@ -120,19 +115,15 @@ def test_workspace_plan(lib):
     D = 128
     P = ctypes.byref
     one = lib.gka_fwd_workspace_bytes(P(params(D=D, B=1, H=1, T=64, segments=0)))
-    assert one == phi_bytes(1, 64, 1)  # a single chunk: one segment, the per-token factors only
-    # float32 (and bf16 with chunks of 32) run the fused walk: no per-token factors
-    assert lib.gka_fwd_workspace_bytes(P(params(D=64, B=1, H=1, T=64, dtype_code=gka.GKA_FP32))) == 0
-    assert lib.gka_fwd_workspace_bytes(P(params(D=64, B=1, H=1, T=64, chunk=32, segments=1))) == 0
+    assert one == 0  # a single chunk: one segment, no workspace
     p = params(B=8, H=8, T=2048, D=D)  # 32 chunks per head -> four segments (one per CU)
     ws = lib.gka_fwd_workspace_bytes(P(p))
-    assert ws == seg_bytes(8, 8, 4, D) + phi_bytes(8, 2048, 8)
+    assert ws == seg_bytes(8, 8, 4, D)
     # explicit segment counts are clamped to the number of chunks
     big = lib.gka_fwd_workspace_bytes(P(params(B=1, H=1, T=128, D=D, segments=50)))
     two = lib.gka_fwd_workspace_bytes(P(params(B=1, H=1, T=128, D=D, segments=2)))
-    assert big == two == seg_bytes(1, 1, 2, D) + phi_bytes(1, 128, 1)
-    assert lib.gka_fwd_workspace_bytes(P(params(B=1, H=1, T=128, D=D, segments=1))) == \
-        phi_bytes(1, 128, 1)
+    assert big == two == seg_bytes(1, 1, 2, D)
+    assert lib.gka_fwd_workspace_bytes(P(params(B=1, H=1, T=128, D=D, segments=1))) == 0
 
 
 def test_step_rejects_bad_arguments(lib):
@@ -248,7 +239,7 @@ def test_varlen_plan_and_workspace(lib):
     D, B, H = 128, 64, 8
     for T, S in ((64, 1), (768, 1), (832, 2), (2048, 3)):
         ws = lib.gka_fwd_varlen_workspace_bytes(P(params(B=B, H=H, T=T, D=D)))
-        assert ws == seg_bytes(B, H, S, D) + phi_bytes(B, T, H) + 256, (T, S, ws)
+        assert ws == seg_bytes(B, H, S, D) + 256, (T, S, ws)
     # more sequences than the order kernel takes: no order, no extra bytes
     big = params(B=5000, H=1, T=64, D=32)
     assert lib.gka_fwd_varlen_workspace_bytes(P(big)) == lib.gka_fwd_workspace_bytes(P(big))
