@@ -13,9 +13,11 @@
  * schedule of Lemma 3/4 on the pith.science page) and emits o_t = U_t x_t.
  *
  * Conventions shared by both entry points
- *   - Every data pointer is a DEVICE pointer owned by the caller; the library keeps no global
- *     state and allocates nothing. `stream` is a hipStream_t (NULL = the default stream); all
- *     work is enqueued on it and the call returns without synchronising.
+ *   - Every data pointer is a DEVICE pointer owned by the caller, and the library allocates no
+ *     memory. Its only global state: per device, which kernels have had their LDS limit raised
+ *     (a kernel attribute, set once per device), and the static scratch array of
+ *     gka_fwd_chunked_static with its device address. `stream` is a hipStream_t (NULL = the
+ *     default stream); all work is enqueued on it and the call returns without synchronising.
  *   - Tensors are dense, contiguous, row-major: q, k, v, o are [B, T, H, D] (prefill) or
  *     [B, H, D] (decode) in `dtype`; gamma is float32 [B, T, H] / [B, H] with values in [0, 1];
  *     h_state and u_state are float32 [B, H, D, D]; hnorm2 is float32 [B, H] holding
@@ -49,13 +51,15 @@ typedef enum {
   GKA_ERR_DTYPE = 4,     /* dtype not one of gka_dtype                                       */
   GKA_ERR_WORKSPACE = 5, /* workspace missing or smaller than gka_fwd_workspace_bytes()      */
   GKA_ERR_HIP = 6,       /* a kernel launch failed                                           */
-  GKA_ERR_ALIAS = 7      /* o overlaps an input tensor                                       */
+  GKA_ERR_ALIAS = 7,     /* o overlaps an input tensor                                       */
+  GKA_ERR_SCRATCH = 8    /* gka_fwd_chunked_static: plan needs more than the static scratch   */
 } gka_status;
 
 typedef enum { GKA_BF16 = 0, GKA_FP32 = 1 } gka_dtype;
 
 #define GKA_MAX_ITERS 64
 #define GKA_PHASE_EVENTS 4
+#define GKA_STATIC_SCRATCH_BYTES (64u << 20) /* per GPU, held by gka_fwd_chunked_static */
 
 /*
  * Problem description shared by both entry points.
@@ -242,6 +246,28 @@ gka_status gka_bwd(const gka_params* p, const void* q, const void* k, const void
                    const float* gamma, const float* beta, const void* dout, void* dq, void* dk,
                    void* dv, float* dgamma, float* dbeta, void* workspace,
                    size_t workspace_bytes, void* stream);
+
+/*
+ * Allocation-free prefill, for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc). It is gka_fwd_chunked_beta
+ * (beta may be NULL) with the segment workspace in a static device array of the library,
+ * GKA_STATIC_SCRATCH_BYTES (64 MiB) on every GPU the library runs on, held until the process
+ * ends; it calls no allocating routine. Arguments, layouts and results are those of
+ * gka_fwd_chunked_beta (the same kernels: identical output for the same parameters), without
+ * the workspace and the phase events.
+ *   Errors: those of gka_fwd_chunked_beta; GKA_ERR_SCRATCH when the segment plan of *p needs
+ *   more than GKA_STATIC_SCRATCH_BYTES (gka_fwd_workspace_bytes(p) says how much: 2 D^2 floats
+ *   per segment and head; set p->segments lower, 1 needs none); GKA_ERR_HIP when the array's
+ *   address cannot be obtained on the current device (looked up once per device, on the first
+ *   call there that needs it).
+ *   Concurrency: all calls on one GPU share its array, which keeps the last call's contents.
+ *   Calls on one stream are ordered and safe; calls that overlap in time on one GPU (several
+ *   streams or host threads without ordering between them) race and give wrong results.
+ */
+gka_status gka_fwd_chunked_static(const gka_params* p, const void* q, const void* k,
+                                  const void* v, const float* gamma, const float* beta, void* o,
+                                  float* h_state, float* u_state, float* hnorm2, float* hnorm_t,
+                                  void* stream);
 
 /* Static description of a status code. */
 const char* gka_status_str(int status);

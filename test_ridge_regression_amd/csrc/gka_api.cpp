@@ -12,7 +12,7 @@ namespace {
 using gka::ChebConsts;
 using gka::FwdPlan;
 
-constexpr int kAbiVersion = 7;
+constexpr int kAbiVersion = 8;
 constexpr int kCUs = 256;  // MI355X compute units: the segment plan aims at one workgroup per CU
 
 bool dims_supported(int dtype, int D) {
@@ -223,7 +223,7 @@ gka_status fwd_impl(const gka_params* p, const int32_t* cu, int64_t total, const
                     const void* k, const void* v, const float* gamma, const float* beta, void* o,
                     float* h_state, float* u_state, float* hnorm2, float* hnorm_t, float* resid,
                     void* workspace, size_t workspace_bytes, void* stream,
-                    void* const* phase_events);
+                    void* const* phase_events, bool static_ws = false);
 
 }  // namespace
 
@@ -241,6 +241,8 @@ const char* gka_status_str(int s) {
     case GKA_ERR_WORKSPACE: return "workspace missing or too small";
     case GKA_ERR_HIP: return "HIP launch failed";
     case GKA_ERR_ALIAS: return "output overlaps an input";
+    case GKA_ERR_SCRATCH:
+      return "segment plan needs more workspace than the static scratch (GKA_STATIC_SCRATCH_BYTES)";
   }
   return "unknown status";
 }
@@ -288,6 +290,14 @@ gka_status gka_fwd_chunked_residuals(const gka_params* p, const void* q, const v
                   resid, workspace, workspace_bytes, stream, nullptr);
 }
 
+gka_status gka_fwd_chunked_static(const gka_params* p, const void* q, const void* k,
+                                  const void* v, const float* gamma, const float* beta, void* o,
+                                  float* h_state, float* u_state, float* hnorm2, float* hnorm_t,
+                                  void* stream) {
+  return fwd_impl(p, nullptr, -1, q, k, v, gamma, beta, o, h_state, u_state, hnorm2, hnorm_t,
+                  nullptr, nullptr, 0, stream, nullptr, /*static_ws=*/true);
+}
+
 gka_status gka_fwd_varlen(const gka_params* p, const int32_t* cu_seqlens, int64_t total,
                           const void* q, const void* k, const void* v, const float* gamma,
                           const float* beta, void* o, float* h_state, float* u_state,
@@ -310,7 +320,7 @@ gka_status fwd_impl(const gka_params* p, const int32_t* cu, int64_t total, const
                     const void* k, const void* v, const float* gamma, const float* beta, void* o,
                     float* h_state, float* u_state, float* hnorm2, float* hnorm_t, float* resid,
                     void* workspace, size_t workspace_bytes, void* stream,
-                    void* const* phase_events) {
+                    void* const* phase_events, bool static_ws) {
   gka_status st = check_fwd(p);
   if (st != GKA_OK) return st;
   const bool any_state = h_state || u_state || hnorm2;
@@ -332,6 +342,11 @@ gka_status fwd_impl(const gka_params* p, const int32_t* cu, int64_t total, const
     return GKA_ERR_ALIAS;
   FwdPlan pl;
   make_plan(p, pl, cu != nullptr);
+  if (static_ws && pl.ws_bytes > 0) {  // the library's static scratch replaces the workspace
+    if (pl.ws_bytes > (size_t)GKA_STATIC_SCRATCH_BYTES) return GKA_ERR_SCRATCH;
+    if (gka::static_scratch(&workspace) != hipSuccess) return GKA_ERR_HIP;
+    workspace_bytes = GKA_STATIC_SCRATCH_BYTES;
+  }
   if (pl.ws_bytes > 0 && (!workspace || workspace_bytes < pl.ws_bytes || !aligned16(workspace)))
     return GKA_ERR_WORKSPACE;
 

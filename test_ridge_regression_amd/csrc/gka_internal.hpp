@@ -123,6 +123,10 @@ hipError_t launch_scan(const FwdPlan& pl, float* ws_states, const float* ws_log2
                        float* u, const float* hnorm2, float* n2_seg0, const int* cu,
                        hipStream_t stream);
 
+// Device address of the static scratch array (GKA_STATIC_SCRATCH_BYTES) on the current device,
+// looked up on the first call there and kept.
+hipError_t static_scratch(void** out);
+
 // Backward pass (gka_bwd): arguments of its kernels. Workspace: snap [BH][T][2][D][D] (H_t, U_t
 // after every token), xs, ys [BH][T][D] (the solves of the forward sweep), cs [BH][T], and the
 // chunk states of the two scans.

@@ -24,11 +24,14 @@ GKA_BF16 = 0
 GKA_FP32 = 1
 GKA_MAX_ITERS = 64
 STATUS = {0: "GKA_OK", 1: "GKA_ERR_NULL", 2: "GKA_ERR_SHAPE", 3: "GKA_ERR_VALUE",
-          4: "GKA_ERR_DTYPE", 5: "GKA_ERR_WORKSPACE", 6: "GKA_ERR_HIP", 7: "GKA_ERR_ALIAS"}
+          4: "GKA_ERR_DTYPE", 5: "GKA_ERR_WORKSPACE", 6: "GKA_ERR_HIP", 7: "GKA_ERR_ALIAS",
+          8: "GKA_ERR_SCRATCH"}
+GKA_STATIC_SCRATCH_BYTES = 64 << 20
 EXPORTED = ["gka_fwd_workspace_bytes", "gka_fwd_chunked", "gka_step", "gka_fwd_chunked_beta",
             "gka_step_beta", "gka_fwd_chunked_residuals", "gka_step_residuals",
             "gka_fwd_varlen", "gka_fwd_varlen_workspace_bytes", "gka_bwd",
-            "gka_bwd_workspace_bytes", "gka_status_str", "gka_abi_version"]
+            "gka_bwd_workspace_bytes", "gka_fwd_chunked_static", "gka_status_str",
+            "gka_abi_version"]
 
 
 class GkaParams(ctypes.Structure):
@@ -85,6 +88,8 @@ def load(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.gka_bwd.argtypes = [P, vp, vp, vp, fp, fp, vp, vp, vp, vp, fp, fp, vp, ctypes.c_size_t,
                             vp]
     lib.gka_bwd.restype = ctypes.c_int
+    lib.gka_fwd_chunked_static.argtypes = [P, vp, vp, vp, fp, fp, vp, fp, fp, fp, fp, vp]
+    lib.gka_fwd_chunked_static.restype = ctypes.c_int
     lib.gka_status_str.argtypes = [ctypes.c_int]
     lib.gka_status_str.restype = ctypes.c_char_p
     lib.gka_abi_version.argtypes = []
@@ -230,6 +235,32 @@ def fwd_chunked(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.
 def fwd_chunked_beta(q, k, v, gamma, beta, a, iters, **kw):
     """gka_fwd_chunked_beta: fwd_chunked with the per-token write gate beta [B, T, H]."""
     return fwd_chunked(q, k, v, gamma, a, iters, beta=beta, **kw)
+
+
+def fwd_chunked_static(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor,
+                       a: float, iters: int, chunk: int = 64, state: Optional[GkaState] = None,
+                       beta: Optional[torch.Tensor] = None, segments: int = 0,
+                       out: Optional[torch.Tensor] = None, hnorm: Optional[torch.Tensor] = None,
+                       stream=None):
+    """gka_fwd_chunked_static: fwd_chunked without a workspace (the library's static scratch
+    holds the segment states). The call allocates nothing when ``out`` (and ``hnorm``, the
+    optional per-token ||H_t||_F [B, T, H] output) are given; returns o."""
+    lib = load()
+    B, T, H, D = q.shape
+    p = make_params(B, T, H, D, chunk, iters, a, _dtype_code(q), segments)
+    o = torch.empty_like(q) if out is None else out
+    _require_io(q, k, v, gamma, o, state, (B, T, H), (B, H))
+    _require_beta(beta, (B, T, H))
+    if hnorm is not None and (hnorm.dtype != torch.float32 or not hnorm.is_contiguous()
+                              or tuple(hnorm.shape) != (B, T, H)):
+        raise ValueError(f"hnorm must be a dense float32 tensor of shape {(B, T, H)}")
+    _require_device(q, [beta, hnorm])
+    st = lib.gka_fwd_chunked_static(
+        ctypes.byref(p), _ptr(q), _ptr(k), _ptr(v), _ptr(gamma), _ptr(beta), _ptr(o),
+        _ptr(state.h if state else None), _ptr(state.u if state else None),
+        _ptr(state.n2 if state else None), _ptr(hnorm), _stream(stream))
+    _check(st)
+    return o
 
 
 def step(q: torch.Tensor, k: torch.Tensor, v: torch.Tensor, gamma: torch.Tensor, a: float,

@@ -33,11 +33,11 @@ def test_header_declares_the_bound_functions():
 def test_library_exports_every_declared_symbol(lib):
     for name in declared_functions():
         assert hasattr(lib, name), name
-    assert lib.gka_abi_version() == 7
+    assert lib.gka_abi_version() == 8
 
 
 def test_status_strings(lib):
-    for code in range(8):
+    for code in range(9):
         assert lib.gka_status_str(code)
     assert lib.gka_status_str(99) == b"unknown status"
 
@@ -396,3 +396,35 @@ def test_row_spans_past_32_bit_offsets_are_rejected(lib):
     assert sres(params(B=1, H=129055, D=16, iters=64)) == 1
     assert res(params(B=1, H=129055, D=16, T=64, chunk=32, iters=64, segments=1)) == 1  # no gamma
     assert fwd(lib, params(B=1, H=129056, D=16, T=64, chunk=32, iters=64), g=None) == 1
+
+
+def test_static_entry_point_checks_before_any_device_call(lib):
+    """gka_fwd_chunked_static validates like gka_fwd_chunked_beta, and a plan whose segment
+    states exceed the static scratch is GKA_ERR_SCRATCH -- all on the host, before the scratch
+    address is looked up (no GPU here)."""
+    def call(p, **kw):
+        a = dict(q=VP[0], k=VP[1], v=VP[2], g=VP[3], b=None, o=VP[4], h=None, u=None, n2=None,
+                 hn=None)
+        a.update(kw)
+        return lib.gka_fwd_chunked_static(ctypes.byref(p) if p is not None else None, a["q"],
+                                          a["k"], a["v"], a["g"], a["b"], a["o"], a["h"], a["u"],
+                                          a["n2"], a["hn"], None)
+    assert call(None) == 1
+    assert call(params(D=48)) == 2
+    assert call(params(a=0.0)) == 3
+    assert call(params(), q=None) == 1
+    assert call(params(), o=VP[0]) == 7
+    assert call(params(), h=VP[5]) == 1            # state pointers mixed NULL / non-NULL
+    # T = 0: a no-op that needs no scratch
+    assert call(params(T=0)) == 0
+    # B 64 x H 8 heads of D = 128 in 32 segments: 64 * 8 * 32 * 2 * 64 KiB = 2 GiB of states
+    big = params(B=64, T=4096, H=8, D=128, segments=32)
+    assert lib.gka_fwd_workspace_bytes(ctypes.byref(big)) > gka.GKA_STATIC_SCRATCH_BYTES
+    assert call(big) == 8
+    # multi-segment plans that fit still fail their argument checks first
+    mid = params(B=2, T=1024, H=2, D=128)
+    assert 0 < lib.gka_fwd_workspace_bytes(ctypes.byref(mid)) <= gka.GKA_STATIC_SCRATCH_BYTES
+    assert call(mid, g=None) == 1
+    assert call(mid, o=VP[1]) == 7
+    assert call(mid, q=ctypes.c_void_p(ADDR[0] + 8)) == 2
+    assert b"static scratch" in lib.gka_status_str(8)
