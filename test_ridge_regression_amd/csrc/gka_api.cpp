@@ -14,6 +14,10 @@ using gka::FwdPlan;
 
 constexpr int kAbiVersion = 8;
 constexpr int kCUs = 256;  // MI355X compute units: the segment plan aims at one workgroup per CU
+// A call from the zero state with at most this many segments skips the segment scan: the token
+// walk of segment s composes its start state from the s summaries before it (s x 2 D^2 floats
+// read by that workgroup, against a separate scan over every segment state)
+constexpr int kComposeMaxSegments = 4;
 
 bool dims_supported(int dtype, int D) {
   (void)dtype;
@@ -376,7 +380,8 @@ gka_status fwd_impl(const gka_params* p, const int32_t* cu, int64_t total, const
   // the fused chunk walk from the segment-start states in (in_h, in_u, n2_in, with strides
   // in_bh, in_seg)
   auto walk = [&](const float* in_h, const float* in_u, long long in_bh, long long in_seg,
-                  const float* n2_in) -> gka_status {
+                  const float* n2_in, const float* in_log2g) -> gka_status {
+    wa.in_log2g = in_log2g;
     wa.in_h = in_h;
     wa.in_u = in_u;
     wa.in_bh = in_bh;
@@ -391,7 +396,7 @@ gka_status fwd_impl(const gka_params* p, const int32_t* cu, int64_t total, const
   };
   if (pl.S == 1) {
     if (!mark(0) || !mark(1) || !mark(2)) return GKA_ERR_HIP;
-    return walk(h_state, u_state, DD, 0, hnorm2);
+    return walk(h_state, u_state, DD, 0, hnorm2, nullptr);
   }
   const size_t bh = (size_t)p->B * p->H;
   float* ws_states = static_cast<float*>(workspace);
@@ -406,11 +411,15 @@ gka_status fwd_impl(const gka_params* p, const int32_t* cu, int64_t total, const
   if (!mark(0)) return GKA_ERR_HIP;
   if (gka::launch_walk(pl, true, sa, cc, s) != hipSuccess) return GKA_ERR_HIP;
   if (!mark(1)) return GKA_ERR_HIP;
+  if (!cu && !h_state && pl.S <= kComposeMaxSegments && gka::walk_tok_supported(pl)) {
+    if (!mark(2)) return GKA_ERR_HIP;
+    return walk(ws_states, ws_states + DD, (long long)pl.S * 2 * DD, 2 * DD, nullptr, ws_log2g);
+  }
   if (gka::launch_scan(pl, ws_states, ws_log2g, h_state, u_state, hnorm2, ws_n2, cu, s) !=
       hipSuccess)
     return GKA_ERR_HIP;
   if (!mark(2)) return GKA_ERR_HIP;
-  return walk(ws_states, ws_states + DD, (long long)pl.S * 2 * DD, 2 * DD, ws_n2);
+  return walk(ws_states, ws_states + DD, (long long)pl.S * 2 * DD, 2 * DD, ws_n2, nullptr);
 }
 
 gka_status step_impl(const gka_params* p, const void* q, const void* k, const void* v,

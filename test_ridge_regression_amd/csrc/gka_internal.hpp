@@ -56,6 +56,9 @@ struct WalkArgs {
   const float* in_u;      // segment-start U
   long long in_bh, in_seg;
   const float* n2_in;     // [BH] ||H||_F^2 at the start of segment 0 (NULL: from in_h / zero)
+  const float* in_log2g;  // token walk, a call from the zero state: the segment summaries'
+                          // log2 gate products [BH][S]; in_h / in_u then hold the summaries of
+                          // segments 0 .. S-2 and every segment composes its own start state
   float* out_h;           // optional final state, [BH][D][D], written by the last segment
   float* out_u;
   float* n2_out;          // optional final ||H||_F^2, written by the last segment

@@ -250,31 +250,51 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
   int Eu = 0;  // U = Us 2^Eu
   float n0sq = 0.0f;
   {
-    float sq = 0.0f;
-    if (A.in_h) {
-      const float* ih = A.in_h + bh * A.in_bh + seg * A.in_seg;
+    // The segment-start state: slot seg of in_h / in_u, or, with in_log2g (a call from the
+    // zero state), composed here from the summaries d_j of the segments before this one --
+    // the affine scan over segments: start = sum_{j < seg} 2^(log2 gates of segments
+    // j+1 .. seg-1) d_j, taken from j = seg - 1 down (the first source has weight 1 exactly)
+    const int nsrc = A.in_log2g ? seg : (A.in_h ? 1 : 0);
+    float lam = 0.0f;
+    for (int i = 0; i < nsrc; ++i) {
+      const int sl = A.in_log2g ? seg - 1 - i : seg;
+      const float wj = exp2f(lam);
+      const float* ih = A.in_h + bh * A.in_bh + sl * A.in_seg;
+      const float* iu = A.in_u + bh * A.in_bh + sl * A.in_seg;
       for_tiles([&](auto J, auto a, auto b, auto) {
         constexpr int j = decltype(J)::value;
         // H[r..r+3][c] is read as H[c][r..r+3] (symmetric)
         const size_t o = (size_t)(16 * (int)b + lr) * D + 16 * (int)a + 4 * lg;
-        Hst[j] = *reinterpret_cast<const f32x4*>(ih + o);
-        const f32x4 x = Hst[j];
-        const float m = TRI && (int)a != (int)b ? 2.0f : 1.0f;  // an upper tile stands for two
-        sq += m * (x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3]);
+        const f32x4 x = *reinterpret_cast<const f32x4*>(ih + o);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Hst[j][e] = fmaf(wj, x[e], Hst[j][e]);
       });
+      // U^T[r..r+3][c] = U[c][r..r+3], accumulated in the lane's own LDS slots
+      for_utiles([&](auto J, int a, int b, auto) {
+        constexpr int j = decltype(J)::value;
+        const f32x4 x =
+            *reinterpret_cast<const f32x4*>(iu + (size_t)(16 * b + lr) * D + 16 * a + 4 * lg);
+        f32x4 y = i == 0 ? f32x4{0.f, 0.f, 0.f, 0.f} : *us_tile(j);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) y[e] = fmaf(wj, x[e], y[e]);
+        *us_tile(j) = y;
+      });
+      if (A.in_log2g) lam += A.in_log2g[(long long)bh * S + sl];
     }
+    float sq = 0.0f;
+    for_tiles([&](auto J, auto a, auto b, auto) {
+      const f32x4 x = Hst[decltype(J)::value];
+      const float m = TRI && (int)a != (int)b ? 2.0f : 1.0f;  // an upper tile stands for two
+      sq += m * (x[0] * x[0] + x[1] * x[1] + x[2] * x[2] + x[3] * x[3]);
+    });
     sq = wave_sum(sq);
     if (lane == 0) v_sc[wave] = sq;
-    // U^T[r..r+3][c] = U[c][r..r+3]
     float um = 0.0f;
-    for_utiles([&](auto J, int a, int b, auto) {
+    for_utiles([&](auto J, int, int, auto) {
       constexpr int j = decltype(J)::value;
       f32x4 x = {0.f, 0.f, 0.f, 0.f};
-      if (A.in_u) {
-        const float* iu = A.in_u + bh * A.in_bh + seg * A.in_seg;
-        x = *reinterpret_cast<const f32x4*>(iu + (size_t)(16 * b + lr) * D + 16 * a + 4 * lg);
-      }
-      *us_tile(j) = x;
+      if (nsrc > 0) x = *us_tile(j);
+      else *us_tile(j) = x;
       um = fmaxf(um, fmaxf(fmaxf(fabsf(x[0]), fabsf(x[1])), fmaxf(fabsf(x[2]), fabsf(x[3]))));
     });
     um = wave_max(um);
@@ -984,15 +1004,16 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
 // so the tokens are taken in blocks of 64 from the last block to the first, with the gate sum
 // of the blocks already taken as the suffix of every weight, and no rescaling of the state.
 // Matrix-core operands are bf16: K and V exactly, the weighted keys w k as a hi + lo pair
-// (about 2^-17 relative). Eight waves, two per SIMD; wave w holds the float32 tiles (row tiles
-// RT*(w % 2).., column tiles CT*(w / 2)..) of dH and of dU (rows = value features), computed as
-// dH = K^T diag(w) K and dU = V^T diag(w) K, so that both take the weighted keys of the wave's
-// column tiles as their second operand (weighted by the two waves that share those tiles).
-// Per block every wave reads its own operand fragments with transposing reads of the block's
-// K and V rows in LDS (bf16, padded rows), in the walk's permuted token order; the block's
-// weights were computed one block earlier, from its gates in registers. The rows of
-// the next block go to the other of two LDS slots, from registers loaded two blocks ahead with
-// bounds-checked buffer loads (rows past the end read as 0): one barrier per block.
+// (about 2^-17 relative), formed once per block when its rows are staged to LDS. Eight waves,
+// two per SIMD; wave w holds the float32 tiles (row tiles RT*(w % 2).., column tiles
+// CT*(w / 2)..) of dH and of dU (rows = value features), computed as dH = K^T diag(w) K and
+// dU = V^T diag(w) K, so that both take the weighted keys of the wave's column tiles as their
+// second operand. Per block every wave reads its operand fragments with transposing reads of
+// the block's K, V and weighted-key rows in LDS (bf16, padded rows), in the walk's permuted
+// token order; the block's weights are computed from its gates in registers just before its
+// rows are staged. The rows of the next block go to the other of two LDS slots, from registers
+// loaded two blocks ahead with bounds-checked buffer loads (rows past the end read as 0): one
+// barrier per block.
 template <int D>
 struct SumCfg {
   static constexpr int CB = 64;                // tokens per block (a chunk)
@@ -1002,11 +1023,12 @@ struct SumCfg {
   static constexpr int FT = D / 16;
   static constexpr int RT = FT / 2;            // state row tiles per wave (more rows than
   static constexpr int CT = FT / 4;            // columns: fewer operand fragments per product)
-  static constexpr int LDR = D + 8;            // row stride of a block's K or V rows (bf16)
+  static constexpr int LDR = D + 16;  // row stride of the rows (bf16): 8 banks apart, so the
+                                      // 16 rows of a transposing read share no bank
   static constexpr int VEC = 8, UPR = D / VEC, NU = CB * UPR;
   static constexpr int NUT = (NU + NT - 1) / NT;  // 16-byte units per thread and matrix
   static constexpr size_t szRows = (size_t)CB * LDR * 2;
-  static constexpr size_t szSlot = 2 * szRows;  // K rows, V rows
+  static constexpr size_t szSlot = 4 * szRows;  // rows of K, V, (w k) hi and (w k) lo
   static constexpr size_t bytes = 2 * szSlot + 2 * (size_t)NW * CB * sizeof(float);  // + weights
   static_assert(D == 64 || D == 128, "summary tiling");
   static_assert(bytes <= 160 * 1024, "LDS budget of one CU exceeded");
@@ -1039,6 +1061,8 @@ void summary_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   auto krows = [&](int slot) { return reinterpret_cast<bf16*>(smem + slot * Cfg::szSlot); };
   auto vrows = [&](int slot) { return krows(slot) + CB * LDR; };
+  auto hirows = [&](int slot) { return krows(slot) + 2 * CB * LDR; };  // (w k) hi
+  auto lorows = [&](int slot) { return krows(slot) + 3 * CB * LDR; };  // (w k) lo
 
   const int seg = blockIdx.x;
   int b, h;
@@ -1093,15 +1117,27 @@ void summary_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J
     gr[q] = buffer_load4f(rg, (uint32_t)lane * Hn * 4u);
     br[q] = buffer_load4f(rb, (uint32_t)lane * Hn * 4u);
   };
-  auto write_block = [&](int slot, int q) {
+  // rows of register set q to slot `slot`, with the weighted keys (weights wl, token-indexed)
+  auto write_block = [&](int slot, int q, const float* wl) {
     refresh();
 #pragma unroll
     for (int k = 0; k < NUT; ++k) {
       const int u = tid + k * NT;
       if (NU % NT == 0 || u < NU) {
         const int tt = (uint32_t)u / UPR, cu = (uint32_t)u % UPR;  // u >= 0
-        *reinterpret_cast<bf16x8*>(krows(slot) + tt * LDR + cu * 8) = kr[q][k];
-        *reinterpret_cast<bf16x8*>(vrows(slot) + tt * LDR + cu * 8) = vr[q][k];
+        const int o = tt * LDR + cu * 8;
+        *reinterpret_cast<bf16x8*>(krows(slot) + o) = kr[q][k];
+        *reinterpret_cast<bf16x8*>(vrows(slot) + o) = vr[q][k];
+        const float w = wl[tt];
+        bf16x8 hi, lo;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float x = (float)kr[q][k][j] * w;
+          hi[j] = (bf16)x;
+          lo[j] = (bf16)(x - (float)hi[j]);
+        }
+        *reinterpret_cast<bf16x8*>(hirows(slot) + o) = hi;
+        *reinterpret_cast<bf16x8*>(lorows(slot) + o) = lo;
       }
     }
   };
@@ -1127,63 +1163,74 @@ void summary_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J
     v_wl[(p & 1) * CB + lane] = fast_exp2(fminf(clast - cl + suffix, 0.0f)) * bw;
     suffix += clast;
   };
-  // block p from slot p % 2 into the state
+  // block p from slot p % 2 into the state: every fragment of the block first, then the
+  // products, the hi halves of all tiles before the lo halves (dependent products far apart)
   auto accumulate = [&](int p) {
     refresh();
     const int slot = p & 1;
-    const float* wl = v_wl + (p & 1) * CB;
     const bf16* kb = krows(slot);
     const bf16* vb = vrows(slot);
+    const bf16* hb = hirows(slot);
+    const bf16* lb = lorows(slot);
     const int cq = 4 * (lr & 3);
+    constexpr int KB = Cfg::KB;
+    // A operands: K^T and V^T row fragments; B operands: the weighted keys of the column tiles,
+    // hi and lo (shared by the two products: dH = K^T diag(w) K, dU = V^T diag(w) K)
+    Frag ak[KB][RT], av[KB][RT], bh[KB][CT], bl[KB][CT];
 #pragma unroll
-    for (int kc = 0; kc < Cfg::KB; ++kc) {
+    for (int kc = 0; kc < KB; ++kc) {
       const int s0 = 32 * kc + 4 * lg, s1 = s0 + 16;
-      // A operands: K^T and V^T row fragments; B operands: the weighted keys of the column
-      // tiles, hi + lo (shared by the two products: dH = K^T diag(w) K, dU = V^T diag(w) K)
-      Frag ak[RT], av[RT], bh[CT], bl[CT];
 #pragma unroll
       for (int jr = 0; jr < RT; ++jr) {
-        ak[jr] = frag_trans_bf16<LDR>(kb, s0, s1, 16 * (a0 + jr) + cq, lr);
-        av[jr] = frag_trans_bf16<LDR>(vb, s0, s1, 16 * (a0 + jr) + cq, lr);
+        ak[kc][jr] = frag_trans_bf16<LDR>(kb, s0, s1, 16 * (a0 + jr) + cq, lr);
+        av[kc][jr] = frag_trans_bf16<LDR>(vb, s0, s1, 16 * (a0 + jr) + cq, lr);
       }
-      const f32x4 w0 = *reinterpret_cast<const f32x4*>(wl + s0);
-      const f32x4 w1 = *reinterpret_cast<const f32x4*>(wl + s1);
 #pragma unroll
       for (int jc = 0; jc < CT; ++jc) {
-        const Frag f = frag_trans_bf16<LDR>(kb, s0, s1, 16 * (b0 + jc) + cq, lr);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float x = (float)f[j] * (j < 4 ? w0[j] : w1[j - 4]);
-          bh[jc][j] = (bf16)x;
-          bl[jc][j] = (bf16)(x - (float)bh[jc][j]);
-        }
+        bh[kc][jc] = frag_trans_bf16<LDR>(hb, s0, s1, 16 * (b0 + jc) + cq, lr);
+        bl[kc][jc] = frag_trans_bf16<LDR>(lb, s0, s1, 16 * (b0 + jc) + cq, lr);
       }
+    }
+#pragma unroll
+    for (int kc = 0; kc < KB; ++kc) {
 #pragma unroll
       for (int jc = 0; jc < CT; ++jc)
 #pragma unroll
         for (int jr = 0; jr < RT; ++jr) {
-          Hst[jr][jc] = M::mma(ak[jr], bh[jc], Hst[jr][jc]);
-          Ust[jr][jc] = M::mma(av[jr], bh[jc], Ust[jr][jc]);
-          Hst[jr][jc] = M::mma(ak[jr], bl[jc], Hst[jr][jc]);
-          Ust[jr][jc] = M::mma(av[jr], bl[jc], Ust[jr][jc]);
+          Hst[jr][jc] = M::mma(ak[kc][jr], bh[kc][jc], Hst[jr][jc]);
+          Ust[jr][jc] = M::mma(av[kc][jr], bh[kc][jc], Ust[jr][jc]);
+        }
+#pragma unroll
+      for (int jc = 0; jc < CT; ++jc)
+#pragma unroll
+        for (int jr = 0; jr < RT; ++jr) {
+          Hst[jr][jc] = M::mma(ak[kc][jr], bl[kc][jc], Hst[jr][jc]);
+          Ust[jr][jc] = M::mma(av[kc][jr], bl[kc][jc], Ust[jr][jc]);
         }
     }
   };
   // phase p: the rows of block p + 1 (register set (p + 1) % 2) go to slot (p + 1) % 2, that set
-  // is reloaded with block p + 3, and block p is accumulated from slot p % 2
-  auto phase = [&](int p, int q) {
+  // is reloaded with block p + 3, and block p is accumulated from slot p % 2. The two waves of a
+  // SIMD (w and w + 4) take the two halves in opposite orders: while one issues its products,
+  // the other stages, so the matrix pipe stays busy through the staging.
+  const bool stage_first = wave >= Cfg::NW / 2;
+  auto stage = [&](int p, int q) {
     if (p + 1 < NB) {
-      write_block(q, q);
       weigh(p + 1, q);
+      write_block(q, q, v_wl + ((p + 1) & 1) * CB);
       load_block(p + 3, q);
     }
+  };
+  auto phase = [&](int p, int q) {
+    if (stage_first) stage(p, q);
     accumulate(p);
+    if (!stage_first) stage(p, q);
     lds_barrier();  // slot (p + 1) % 2 is written; slot p % 2 is read
   };
   load_block(0, 0);
   load_block(1, 1);
-  write_block(0, 0);
   weigh(0, 0);
+  write_block(0, 0, v_wl);
   load_block(2, 0);
   lds_barrier();
   for (int p = 0; p < NB; p += 2) {
