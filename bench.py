@@ -15,8 +15,14 @@ step on a packed batch of prompts and decode rows (gka_fwd_varlen) under "varlen
 pass (gka_bwd) on the prefill workload under "backward". The oracle leg also compares its outputs of
 the prefix with the timed device run's.
 
+The wide-head (B4 T8192 H32 D64) and long-context (B1 T131072 H8 D128) prefill workloads are
+timed the same way under "prefill_configs". Every prefill record gives the MFMA-peak fraction
+on the chunked form's flops and on the sequential per-token form's D^2 (2 r + 6), for the walk
+kernel and for the whole call.
+
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps S] [--no-cpu]
                        [--no-decode] [--no-beta] [--no-resid] [--no-varlen] [--no-bwd]
+                       [--no-configs]
 """
 from __future__ import annotations
 
@@ -84,6 +90,25 @@ def prefill_flops_per_token_head(D, C, r):
     """Algorithmic flops of the chunk-wise forward per (token, head):
     Chebyshev loop (r-1)(2D^2 + 4CD), output 2D^2 + 4CD, norms 2D^2 + 2CD + 2C^2, carry 4D^2."""
     return D * D * (2 * r + 6) + C * D * (4 * r + 2) + 2 * C * C
+
+
+def sequential_flops_per_token_head(D, r):
+    """Flops per (token, head) of the sequential per-token form the chunked walk replaces:
+    H and U updates 2 D^2 each, ||H_t||_F^2 2 D^2, r - 1 products with H_t 2 D^2 each, and
+    o_t = U_t x_t 2 D^2 -- D^2 (2 r + 6), the work any implementation must do."""
+    return D * D * (2 * r + 6)
+
+
+def prefill_fractions(W, ms_step, ms_walk):
+    """MFMA-peak fractions of a prefill timing: on the chunked form's flops F and on the
+    sequential form's, for the walk kernel alone and for the whole call."""
+    n = W.B * W.T * W.H
+    F = prefill_flops_per_token_head(W.D, W.chunk, W.iters) * n
+    Fs = sequential_flops_per_token_head(W.D, W.iters) * n
+    frac = lambda f, ms: f / (ms * 1e-3) / PEAK_BF16_MFMA
+    return {"walk_frac": frac(F, ms_walk), "step_frac": frac(F, ms_step),
+            "walk_frac_sequential": frac(Fs, ms_walk), "step_frac_sequential": frac(Fs, ms_step),
+            "flops_per_call": F, "sequential_flops_per_call": Fs}
 
 
 def decode_bytes_per_head(D, in_bytes=2):
@@ -415,6 +440,8 @@ def main():
     ap.add_argument("--no-resid", action="store_true", help="skip the solver-convergence mode")
     ap.add_argument("--no-varlen", action="store_true", help="skip the packed serving step")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward pass")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the wide-head and long-context prefill workloads")
     ap.add_argument("--copy-probe", action="store_true",
                     help="also run a plain 512 MiB device copy (calibrates HBM byte counters)")
     args = ap.parse_args()
@@ -464,11 +491,16 @@ def main():
         "config": {"workload": W.name, "B": W.B, "T": W.T, "H": W.H, "D": W.D, "chunk": W.chunk,
                    "a": W.a, "iters": W.iters, "segments": pre["segments"]},
         "roofline": {"bound": "mfma", "kernel": "walk_tok_kernel (token-owning chunk walk)",
+                     "scope": "the walk kernel alone; whole_step_mfma_frac covers the whole call",
                      "achieved": achieved / 1e12, "peak": PEAK_BF16_MFMA / 1e12,
                      "unit": "TFLOP/s", "frac": achieved / PEAK_BF16_MFMA,
                      "traffic": measured_traffic("walk_tok_kernel"),
                      "flops_per_launch": F, "avg_launch_ms": pre["walk_ms"]},
         "whole_step_mfma_frac": F / (pre["ms_per_step"] * 1e-3) / PEAK_BF16_MFMA,
+        "sequential_form": {
+            "flops_per_token_head": sequential_flops_per_token_head(W.D, W.iters),
+            **{k: v for k, v in prefill_fractions(W, pre["ms_per_step"], pre["walk_ms"]).items()
+               if k in ("walk_frac_sequential", "step_frac_sequential")}},
         "phases_ms": {"summary": pre["summary_ms"], "scan": pre["scan_ms"],
                       "walk": pre["walk_ms"]},
     }
@@ -496,6 +528,27 @@ def main():
                                                     args.warmup, ev)
     del pre, inputs
     torch.cuda.empty_cache()
+    if not args.no_configs:
+        # the wide-head (B4 T8192 H32 D64) and long-context (B1 T131072 H8 D128) prefill
+        # workloads, timed like the headline one
+        rec["prefill_configs"] = []
+        for name in ("prefill_b4_t8192_h32_d64", "prefill_b1_t131072_h8_d128"):
+            Wc = Wl.WORKLOADS[name]
+            inp = prefill_inputs(Wc)
+            pc = bench_prefill(Wc, inp, args.steps, args.warmup, ev, what=name)
+            pc.pop("o")
+            rec["prefill_configs"].append({
+                "workload": Wc.name, "B": Wc.B, "T": Wc.T, "H": Wc.H, "D": Wc.D,
+                "chunk": Wc.chunk, "a": Wc.a, "iters": Wc.iters, "segments": pc["segments"],
+                "tokens_per_s": Wc.B * Wc.T / (pc["ms_per_step"] * 1e-3),
+                "ms_per_step": pc["ms_per_step"],
+                "phases_ms": {"summary": pc["summary_ms"], "scan": pc["scan_ms"],
+                              "walk": pc["walk_ms"]},
+                **prefill_fractions(Wc, pc["ms_per_step"], pc["walk_ms"])})
+            log(f"{name}: {pc['ms_per_step']:.3f} ms/step (summary {pc['summary_ms']:.3f}, scan "
+                f"{pc['scan_ms']:.3f}, walk {pc['walk_ms']:.3f})")
+            del inp, pc
+            torch.cuda.empty_cache()
     if not args.no_varlen:
         rec["varlen"] = bench_varlen(Wl.WORKLOADS["varlen_b64_h8_d128"], args.steps, args.warmup,
                                      ev)

@@ -159,9 +159,10 @@ bool make_plan(const gka_params* p, FwdPlan& pl, bool packed = false) {
     S = std::max(1, (pl.N + 11) / 12);
   } else if (S <= 0) {
     const long long bh = (long long)p->B * p->H;
-    // one fused-walk workgroup fits a compute unit (its LDS): aim at one workgroup per CU;
-    // more segments only lengthen the segment scan
-    const long long want = (kCUs + bh - 1) / bh;
+    // aim at one fused-walk workgroup per CU (its LDS, and for D = 128 its registers, fill
+    // one), two for the token walk of D <= 64; more segments only add summary and scan work
+    const long long per_cu = p->dtype == GKA_BF16 && p->chunk == 64 && p->D <= 64 ? 2 : 1;
+    const long long want = (kCUs * per_cu + bh - 1) / bh;
     S = (int)std::min<long long>(want, pl.N);
     if (pl.N / S < 2 && pl.N >= 2) S = std::max(1, pl.N / 2);  // keep >= 2 chunks per segment
   }

@@ -132,9 +132,12 @@ __device__ inline void static_for(F&& f) {
   }
 }
 
-// RES: residual mode, which also writes ||q_t - A_t x_i|| for i = 0..iters to A.resid
+// RES: residual mode, which also writes ||q_t - A_t x_i|| for i = 0..iters to A.resid.
+// D = 128 takes a whole SIMD per wave (its resident operands fill the register file); D <= 64
+// fits in half of it, so two workgroups share a CU (their LDS fits too) and hide each other's
+// latencies.
 template <int D, bool RES>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, D >= 128 ? 1 : 2)))
 void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, ChebConsts cc) {
   using Cfg = TokCfg<D>;
   using M = Mma<f16>;
@@ -1094,7 +1097,7 @@ void summary_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J
   float gr[2], br[2];  // gates and write gates (lane = token)
   // the write gates are read from the gates when there are none (and then not used)
   const float* bsrc = A.beta ? A.beta : A.gamma;
-  auto load_block = [&](int p, int q) {
+  auto load_block = [&](int p, int q) __attribute__((always_inline)) {
     refresh();
     const int pv = p < NB ? p : NB - 1;
     const int t0n = block_t0(pv);
@@ -1118,7 +1121,7 @@ void summary_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J
     br[q] = buffer_load4f(rb, (uint32_t)lane * Hn * 4u);
   };
   // rows of register set q to slot `slot`, with the weighted keys (weights wl, token-indexed)
-  auto write_block = [&](int slot, int q, const float* wl) {
+  auto write_block = [&](int slot, int q, const float* wl) __attribute__((always_inline)) {
     refresh();
 #pragma unroll
     for (int k = 0; k < NUT; ++k) {
@@ -1154,7 +1157,7 @@ void summary_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J
 
   // weights of block p (lane = token), from its gates in register set q, one phase before
   // its products: 2^(log2 of the gates after the token), times the token's write gate
-  auto weigh = [&](int p, int q) {
+  auto weigh = [&](int p, int q) __attribute__((always_inline)) {
     const int nv = p < NB ? min(CB, t_end - block_t0(p)) : 0;
     const float l2 = lane < nv ? log2_gate(gr[q]) : 0.0f;
     const float cl = scan_add<kWave>(l2);
@@ -1165,7 +1168,7 @@ void summary_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J
   };
   // block p from slot p % 2 into the state: every fragment of the block first, then the
   // products, the hi halves of all tiles before the lo halves (dependent products far apart)
-  auto accumulate = [&](int p) {
+  auto accumulate = [&](int p) __attribute__((always_inline)) {
     refresh();
     const int slot = p & 1;
     const bf16* kb = krows(slot);
@@ -1214,18 +1217,12 @@ void summary_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J
   // SIMD (w and w + 4) take the two halves in opposite orders: while one issues its products,
   // the other stages, so the matrix pipe stays busy through the staging.
   const bool stage_first = wave >= Cfg::NW / 2;
-  auto stage = [&](int p, int q) {
-    if (p + 1 < NB) {
-      weigh(p + 1, q);
-      write_block(q, q, v_wl + ((p + 1) & 1) * CB);
-      load_block(p + 3, q);
-    }
-  };
-  auto phase = [&](int p, int q) {
-    if (stage_first) stage(p, q);
-    accumulate(p);
-    if (!stage_first) stage(p, q);
-    lds_barrier();  // slot (p + 1) % 2 is written; slot p % 2 is read
+  // (every phase stages and loads, also past the last block -- zero rows from loads with an
+  // empty range -- so that every path through the loop has the same loads in flight)
+  auto stage = [&](int p, int q) __attribute__((always_inline)) {
+    weigh(p + 1, q);
+    write_block(q, q, v_wl + ((p + 1) & 1) * CB);
+    load_block(p + 3, q);
   };
   load_block(0, 0);
   load_block(1, 1);
@@ -1233,9 +1230,26 @@ void summary_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J
   write_block(0, 0, v_wl);
   load_block(2, 0);
   lds_barrier();
-  for (int p = 0; p < NB; p += 2) {
-    phase(p, 1);
-    if (p + 1 < NB) phase(p + 1, 0);
+  // (one loop per order: with the order fixed inside a loop the compiler tracks which loads
+  // are still in flight, and waits for the older register set only)
+  if (stage_first) {
+    for (int p = 0; p < NB; p += 2) {
+      stage(p, 1);
+      accumulate(p);
+      lds_barrier();  // slot (p + 1) % 2 is written; slot p % 2 is read
+      stage(p + 1, 0);
+      if (p + 1 < NB) accumulate(p + 1);
+      lds_barrier();
+    }
+  } else {
+    for (int p = 0; p < NB; p += 2) {
+      accumulate(p);
+      stage(p, 1);
+      lds_barrier();
+      if (p + 1 < NB) accumulate(p + 1);
+      stage(p + 1, 0);
+      lds_barrier();
+    }
   }
 
   if (wave == 0 && lane == 0) A.log2g_out[(long long)bh * S + seg] = suffix;
