@@ -12,6 +12,21 @@ TORCH_DTYPE = {"bf16": torch.bfloat16, "fp32": torch.float32}
 # parity bars: relative L2 of o against the oracle's Chebyshev output, and ||H_t||_F per token
 TOL_O = {"bf16": 2e-2, "fp32": 1e-5}
 TOL_HNORM = 1e-3
+# Tripwires beside those bars: about three times the largest error the kernels show on cases of
+# at least TRIP_MIN_TOKENS tokens (bf16 o 1.8e-3, float32 o 6.2e-7; ||H_t||_F 2.1e-4 on the
+# write-gated C = 32 path, 2e-5 elsewhere). With fewer tokens a handful of bf16 roundings of o
+# decide the figure (6.1e-3 for one token of D = 32), so only the bars apply there. A change
+# that makes the kernels several times less accurate fails here, far inside the bars.
+TRIP_O = {"bf16": 6e-3, "fp32": 2e-6}
+TRIP_HNORM = 6e-4
+TRIP_MIN_TOKENS = 64
+
+
+def tripwire(e_o: float, e_hnorm: float, dtype: str, tokens: int, what: str = ""):
+    """Assert the tripwire bars on a parity case's relative L2 of o and ||H_t||_F error."""
+    if tokens >= TRIP_MIN_TOKENS:
+        assert e_o <= TRIP_O[dtype], f"{what}: rel_l2(o) {e_o:.3e} above the tripwire"
+    assert e_hnorm <= TRIP_HNORM, f"{what}: ||H_t||_F error {e_hnorm:.3e} above the tripwire"
 
 
 def log(msg: str):

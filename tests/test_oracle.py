@@ -545,6 +545,36 @@ def test_solver_residuals_use_the_layer_systems():
         assert r.shape == (6,) and abs(r[0] - np.linalg.norm(qt)) < 1e-14
 
 
+def test_solver_residuals_on_a_rank_one_state_follow_closed_forms():
+    """The gd / agd / cg branches of solver_residuals pinned on the one state whose system has
+    its extreme eigenvalues exactly at the layer's interval ends: H = diag(n, 0, ..., 0), so
+    ||H||_F = n and A = H + a n I has eigenvalue L = (1 + a) n on e_0 and mu = a n on the rest.
+    Textbook facts then fix every residual (kappa = L / mu = (1 + a) / a):
+      * GD with step 2 / (L + mu): the residual along any eigenvector shrinks by
+        |1 - 2 lambda / (L + mu)| per step, rho = (L - mu) / (L + mu) = 1 / (1 + 2 a) at both ends;
+      * Nesterov AGD with step 1 / L: along lambda = L one step solves exactly (x_1 = q / L),
+        along lambda = mu the momentum m = (sqrt(kappa) - 1) / (sqrt(kappa) + 1) makes the error
+        recurrence critically damped, r_i = (1 + i / sqrt(kappa)) (1 - 1 / sqrt(kappa))^i;
+      * CG: two distinct eigenvalues, so the residual vanishes after two steps.
+    Swapping mu and L in the AGD call, or a wrong interval, breaks these."""
+    a, n, D, iters = 0.1, 2.5, 5, 6
+    H = np.zeros((D, D))
+    H[0, 0] = n
+    e0, e1 = np.eye(D)[0], np.eye(D)[1]
+    i = np.arange(iters + 1)
+    rho = 1.0 / (1.0 + 2.0 * a)
+    for q in (e0, e1, 3.0 * e1):
+        np.testing.assert_allclose(solver_residuals(H, q, a, iters, "gd"),
+                                   np.linalg.norm(q) * rho ** i, rtol=1e-12)
+    r = solver_residuals(H, 2.0 * e0, a, iters, "agd")
+    assert r[0] == 2.0 and np.all(r[1:] < 1e-14)
+    sk = np.sqrt((1.0 + a) / a)
+    np.testing.assert_allclose(solver_residuals(H, e1, a, iters, "agd"),
+                               (1.0 + i / sk) * (1.0 - 1.0 / sk) ** i, rtol=1e-10)
+    r = solver_residuals(H, e0 + e1, a, 3, "cg")
+    assert abs(r[0] - np.sqrt(2.0)) < 1e-14 and r[1] > 1e-3 and r[2] < 1e-13 and r[3] < 1e-13
+
+
 def test_residuals_of_a_token_with_zero_state_are_q():
     # ||H_t|| = 0 (no key written yet): x_t = 0 is every iterate, so every residual is ||q_t||
     rng = np.random.default_rng(46)

@@ -7,12 +7,14 @@ Bars as for the base entry points: relative L2 of o <= 2e-2 (bf16) / 1e-5 (fp32)
 within 1e-3 relative per token. Gates are drawn by workloads.make_beta (sigmoid of N(0, 2),
 spread over (0, 1)); some cases set whole stretches to 0 or 1.
 
-Bar for the carried state of the bf16 path: the library applies the gate as sqrt(beta_t) on the
-key and value rows where they become fp16 matrix operands. bf16 inputs are exact in fp16, the
-scaled rows are not: each element picks up a relative rounding error of at most 2^-12, so H and U
-(sums of products of two such rows) carry a relative error of up to about 2 * 2^-11 ~ 1e-3
-(||H||_F^2 twice that), instead of the ~1e-5 of float32 accumulation alone. The state bars below
-are those; the output and ||H_t||_F bars are unchanged.
+Bars for the carried state of the bf16 paths. The token-owning walk (chunks of 64) applies the
+gate through float32 weights (carry weights, the intra-chunk mask, the norm terms), so its state
+is as accurate as without a gate: bars 1e-4 (measured below 1e-5). The feature-split walk
+(chunks of 32) applies it as sqrt(beta_t) on the key and value rows where they become fp16
+matrix operands; bf16 inputs are exact in fp16, the scaled rows are not: each element picks up a
+relative rounding error of at most 2^-12, so H and U (sums of products of two such rows) carry a
+relative error of up to about 2 * 2^-11 ~ 1e-3 (||H||_F^2 twice that): bars 1e-3 and 2e-3
+(measured 3e-4). The output and ||H_t||_F bars are unchanged.
 """
 import numpy as np
 import pytest
@@ -22,7 +24,8 @@ from oracle import gka_forward_ref, gka_step_ref
 from test_ridge_regression_amd import gka
 from test_ridge_regression_amd import workloads as W
 
-from gka_testutil import TOL_HNORM, TOL_O, dev, host, log, max_rel, rel_l2, run_prefill
+from gka_testutil import (TOL_HNORM, TOL_O, dev, host, log, max_rel, rel_l2, run_prefill,
+                          tripwire)
 
 pytestmark = pytest.mark.gpu
 
@@ -43,12 +46,15 @@ def gated_inputs(B, T, H, D, dtype, seed, mu=3.0, sd=1.0):
     return q, k, v, g, W.make_beta(B, T, H, seed)
 
 
-# relative bars of the carried state (H, U) and of ||H||_F^2 (see the module docstring)
-TOL_STATE = {"fp32": 1e-6, "bf16": 1e-3}
-TOL_N2 = {"fp32": 1e-5, "bf16": 2e-3}
+# relative bars of the carried state (H, U) and of ||H||_F^2 by dtype and chunk (see the module
+# docstring)
+TOL_STATE = {("fp32", 16): 1e-6, ("fp32", 32): 1e-6, ("fp32", 64): 1e-6,
+             ("bf16", 64): 1e-4, ("bf16", 32): 1e-3}
+TOL_N2 = {("fp32", 16): 1e-5, ("fp32", 32): 1e-5, ("fp32", 64): 1e-5,
+          ("bf16", 64): 1e-4, ("bf16", 32): 2e-3}
 
 
-def check(got, ref, dtype, what, state=False):
+def check(got, ref, dtype, what, state=False, chunk=64):
     e = rel_l2(got["o"], ref["o"])
     eh = max_rel(got["hnorm"], ref["hnorm"])
     msg = f"{what}: rel_l2(o)={e:.3e} max_rel(hnorm)={eh:.3e}"
@@ -60,9 +66,10 @@ def check(got, ref, dtype, what, state=False):
     assert np.all(np.isfinite(got["o"]))
     assert e <= TOL_O[dtype], what
     assert eh <= TOL_HNORM, what
+    tripwire(e, eh, dtype, got["o"].shape[1], what)
     if state:
-        assert eH < TOL_STATE[dtype] and eU < TOL_STATE[dtype], what
-        assert en < TOL_N2[dtype], what
+        assert eH < TOL_STATE[dtype, chunk] and eU < TOL_STATE[dtype, chunk], what
+        assert en < TOL_N2[dtype, chunk], what
 
 
 # the token-owning walk (bf16, chunks of 64) with its summaries, ragged lengths, segment counts
@@ -89,7 +96,7 @@ def test_beta_feature_split(dtype, D, C):
         log(f"beta {dtype} D={D} C={C} segments={seg}")
         got = run_prefill(q, k, v, g, 0.1, 8, C, dtype, state=zero_state(2, 2, D), segments=seg,
                           beta=bt)
-        check(got, ref, dtype, f"beta {dtype} D={D} C={C} S={seg}", state=True)
+        check(got, ref, dtype, f"beta {dtype} D={D} C={C} S={seg}", state=True, chunk=C)
 
 
 @pytest.mark.parametrize("dtype,D,C", [("bf16", 128, 64), ("bf16", 64, 32), ("fp32", 32, 16)])
@@ -144,7 +151,8 @@ def test_beta_nonzero_initial_state(dtype, D, C):
         log(f"beta initial state {dtype} D={D} segments={seg}")
         got = run_prefill(q, k, v, g, 0.05, 10, C, dtype, state=(h0, u0, n20), segments=seg,
                           beta=bt)
-        check(got, ref, dtype, f"beta initial state {dtype} D={D} S={seg}", state=True)
+        check(got, ref, dtype, f"beta initial state {dtype} D={D} S={seg}", state=True,
+              chunk=C)
 
 
 @pytest.mark.parametrize("dtype,D,C", [("fp32", 64, 16), ("bf16", 128, 64), ("bf16", 32, 64)])
@@ -166,9 +174,9 @@ def test_beta_prefill_then_steps(dtype, D, C):
     e = rel_l2(o, ref["o"][:, T:])
     log(f"beta prefill -> step {dtype} D={D}: rel_l2(o)={e:.3e}")
     assert e <= TOL_O[dtype]
-    assert max_rel(host(st.n2), ref["n2"]) < TOL_N2[dtype]
-    assert rel_l2(host(st.h), ref["h"]) < TOL_STATE[dtype]
-    assert rel_l2(host(st.u), ref["u"]) < TOL_STATE[dtype]
+    assert max_rel(host(st.n2), ref["n2"]) < TOL_N2[dtype, C]
+    assert rel_l2(host(st.h), ref["h"]) < TOL_STATE[dtype, C]
+    assert rel_l2(host(st.u), ref["u"]) < TOL_STATE[dtype, C]
 
 
 @pytest.mark.parametrize("dtype,D", [("bf16", 128), ("fp32", 16)])

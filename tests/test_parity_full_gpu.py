@@ -7,10 +7,12 @@ relative at every token.
 
   * prefill B8 T2048 H8 D128: 8 of 64 heads over the whole sequence;
   * prefill B4 T8192 H32 D64: 16 of 128 heads over the whole sequence;
-  * prefill B1 T131072 H8 D128 (2048 chunks, 64 segments): 2 of 8 heads. The oracle carries
-    the exact state through all tokens (state-only mode, which still yields ||H_t||_F at every
-    token) and runs the solve on the first and the last 1024 tokens, whose outputs depend on
-    the first segment only and on the whole segment scan respectively;
+  * prefill B1 T131072 H8 D128 (2048 chunks in 32 segments of 4096 tokens): 2 of 8 heads. The
+    oracle carries the exact state through all tokens (state-only mode, which still yields
+    ||H_t||_F at every token) and runs the solve on four windows of 1024 tokens: the first
+    (segment 0 alone), two that straddle inner segment boundaries (tokens 4096 and 65536: the
+    ends of segments 0 and 15 and the starts of segments 1 and 16, whose start states come from
+    the segment scan), and the last (segment 31, after the whole scan);
   * decode B256 H8 D128: 16 of 256 sequences, all 8 heads, over all 1000 steps, from a carried
     state that the oracle builds from 512 warm-up tokens (the same float32 state on both sides).
 """
@@ -22,7 +24,7 @@ from oracle import gka_forward_ref, gka_step_ref
 from test_ridge_regression_amd import gka
 from test_ridge_regression_amd import workloads as W
 
-from gka_testutil import TOL_HNORM, TOL_O, dev, host, log, max_rel, rel_l2
+from gka_testutil import TOL_HNORM, TOL_O, dev, host, log, max_rel, rel_l2, tripwire
 
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
@@ -62,6 +64,7 @@ def check_sampled(w, o, hn, pairs):
     assert e <= TOL_O[w.dtype]
     assert worst <= TOL_O[w.dtype]
     assert eh <= TOL_HNORM
+    tripwire(worst, eh, w.dtype, w.T, w.name)
 
 
 @pytest.mark.timeout(300)
@@ -97,21 +100,38 @@ def test_prefill_b1_t131072_h8_d128_full():
     got_h = host(hn[0][:, [h for _, h in pairs]])[None]
     del o, hn
     T, win = w.T, 1024
-    head = gka_forward_ref(qs[:, :win], ks[:, :win], vs[:, :win], gs[:, :win], w.a, w.iters)
-    log(f"{w.name}: oracle state through {T - win} tokens")
-    mid = gka_forward_ref(qs[:, win:T - win], ks[:, win:T - win], vs[:, win:T - win],
-                          gs[:, win:T - win], w.a, w.iters, mode="state", h0=head["h"],
-                          u0=head["u"], n2_0=head["n2"])
-    tail = gka_forward_ref(qs[:, T - win:], ks[:, T - win:], vs[:, T - win:], gs[:, T - win:],
-                           w.a, w.iters, h0=mid["h"], u0=mid["u"], n2_0=mid["n2"])
-    ref_h = np.concatenate([head["hnorm"], mid["hnorm"], tail["hnorm"]], axis=1)
-    e0 = rel_l2(got_o[:, :win], head["o"])
-    e1 = rel_l2(got_o[:, T - win:], tail["o"])
-    eh = max_rel(got_h, ref_h)
-    log(f"{w.name}: rel_l2(o) first {win}={e0:.3e} last {win}={e1:.3e} hnorm={eh:.3e}")
+    seg_tokens = 64 * w.chunk  # the plan: 2048 chunks in 32 segments of 64
+    assert gka.workspace_bytes(w.B, w.T, w.H, w.D, w.chunk, w.iters, w.a, gka.GKA_BF16) > 0
+    windows = [(0, win), (seg_tokens - win // 2, seg_tokens + win // 2),
+               (16 * seg_tokens - win // 2, 16 * seg_tokens + win // 2), (T - win, T)]
+    st = None  # (h, u, n2) after the tokens handled so far
+    pos, ref_h, errs = 0, [], []
+    for a, b in windows:
+        if a > pos:  # carry the state to the window in state-only mode
+            log(f"{w.name}: oracle state through tokens {pos}..{a}")
+            mid = gka_forward_ref(qs[:, pos:a], ks[:, pos:a], vs[:, pos:a], gs[:, pos:a], w.a,
+                                  w.iters, mode="state", **_state_kw(st))
+            ref_h.append(mid["hnorm"])
+            st = (mid["h"], mid["u"], mid["n2"])
+        log(f"{w.name}: oracle solve on tokens {a}..{b}")
+        r = gka_forward_ref(qs[:, a:b], ks[:, a:b], vs[:, a:b], gs[:, a:b], w.a, w.iters,
+                            **_state_kw(st))
+        ref_h.append(r["hnorm"])
+        st = (r["h"], r["u"], r["n2"])
+        errs.append(rel_l2(got_o[:, a:b], r["o"]))
+        pos = b
+    eh = max_rel(got_h, np.concatenate(ref_h, axis=1))
+    log(f"{w.name}: rel_l2(o) per window " + " ".join(f"{a}..{b}: {e:.3e}"
+                                                       for (a, b), e in zip(windows, errs))
+        + f"; hnorm={eh:.3e}")
     assert np.all(np.isfinite(got_o))
-    assert e0 <= TOL_O[w.dtype] and e1 <= TOL_O[w.dtype]
+    assert all(e <= TOL_O[w.dtype] for e in errs)
     assert eh <= TOL_HNORM
+    tripwire(max(errs), eh, w.dtype, win, w.name)
+
+
+def _state_kw(st):
+    return {} if st is None else dict(h0=st[0], u0=st[1], n2_0=st[2])
 
 
 @pytest.mark.timeout(400)

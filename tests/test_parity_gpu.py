@@ -12,7 +12,7 @@ from test_ridge_regression_amd import gka
 from test_ridge_regression_amd import workloads as W
 
 from gka_testutil import (TOL_HNORM, TOL_O, dev, host, log, max_rel, rel_l2, run_prefill,
-                          worst_head_rel_l2)
+                          tripwire, worst_head_rel_l2)
 
 pytestmark = pytest.mark.gpu
 
@@ -39,6 +39,7 @@ def check_prefill(got, ref, dtype, what=""):
     assert np.all(np.isfinite(got["o"]))
     assert e <= TOL_O[dtype], what
     assert eh <= TOL_HNORM, what
+    tripwire(e, eh, dtype, got["o"].shape[1], what)
 
 
 # ------------------------------------------------------------------------------------------
