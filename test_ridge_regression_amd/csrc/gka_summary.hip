@@ -5,6 +5,8 @@
 // the chunk-initial states are carried sequentially).
 #include "gka_internal.hpp"
 
+#include <type_traits>
+
 namespace gka {
 namespace {
 
@@ -17,33 +19,39 @@ namespace {
 // so the tokens are taken in blocks of 64 from the last block to the first, with the gate sum
 // of the blocks already taken as the suffix of every weight, and no rescaling of the state.
 // Matrix-core operands are bf16: K and V exactly, the weighted keys w k as a hi + lo pair
-// (about 2^-17 relative), formed once per block when its rows are staged to LDS. Eight waves,
-// two per SIMD; wave w holds the float32 tiles (row tiles RT*(w % 2).., column tiles
-// CT*(w / 2)..) of dH and of dU (rows = value features), computed as dH = K^T diag(w) K and
-// dU = V^T diag(w) K, so that both take the weighted keys of the wave's column tiles as their
-// second operand. Per block every wave reads its operand fragments with transposing reads of
-// the block's K, V and weighted-key rows in LDS (bf16, padded rows), in the walk's permuted
-// token order; the block's weights are computed from its gates in registers just before its
-// rows are staged. The rows of the next block go to the other of two LDS slots, from registers
-// loaded two blocks ahead with bounds-checked buffer loads (rows past the end read as 0): one
-// barrier per block.
+// (about 2^-17 relative), formed once per block when its rows are staged to LDS.
+//
+// Two kinds of wave share each SIMD. A product wave (waves 0..3, one per SIMD) holds the float32
+// tiles of dH = K^T diag(w) K and dU = V^T diag(w) K for its row tiles (two at D = 128, w and
+// 7 - w, which pair the longer and the shorter row of dH's upper triangle, so that each wave
+// has 9 tiles of dH and 16 of dU; one at D = 64, all columns) and only issues products, with
+// operands from transposing LDS reads of the block's rows (the walk's permuted token order).
+// A staging wave (waves 4..7) only moves data: it loads the rows of the block after next into
+// registers (bounds-checked buffer loads: rows past the end read as 0), computes the next
+// block's weights from its gates, and writes the next block's K, V and weighted-key rows to the
+// other of two LDS slots. One barrier per block separates the slots' uses, so the matrix pipe of
+// a SIMD runs its product wave while its staging wave works.
 template <int D>
 struct SumCfg {
   static constexpr int CB = 64;                // tokens per block (a chunk)
   static constexpr int KB = CB / 32;           // 32-deep token blocks per block
-  static constexpr int NW = 8;                 // waves, two per SIMD
+  static constexpr int NWC = 4;                // product waves, one per SIMD
+  static constexpr int NWS = 4;                // staging waves, one per SIMD
+  static constexpr int NW = NWC + NWS;
   static constexpr int NT = NW * kWave;
-  static constexpr int FT = D / 16;
-  static constexpr int RT = FT / 2;            // state row tiles per wave (more rows than
-  static constexpr int CT = FT / 4;            // columns: fewer operand fragments per product)
+  static constexpr int NTS = NWS * kWave;      // staging threads
+  static constexpr int FT = D / 16;            // feature tiles
+  static constexpr bool TRI = D == 128;        // dH from its upper-triangle tiles
+  static constexpr int NR = FT / NWC;          // row tiles per product wave
   static constexpr int LDR = D + 16;  // row stride of the rows (bf16): 8 banks apart, so the
                                       // 16 rows of a transposing read share no bank
   static constexpr int VEC = 8, UPR = D / VEC, NU = CB * UPR;
-  static constexpr int NUT = (NU + NT - 1) / NT;  // 16-byte units per thread and matrix
+  static constexpr int NUS = NU / NTS;         // 16-byte units per staging thread and matrix
   static constexpr size_t szRows = (size_t)CB * LDR * 2;
   static constexpr size_t szSlot = 4 * szRows;  // rows of K, V, (w k) hi and (w k) lo
-  static constexpr size_t bytes = 2 * szSlot + 2 * (size_t)NW * CB * sizeof(float);  // + weights
+  static constexpr size_t bytes = 2 * szSlot + (size_t)NWS * CB * sizeof(float);  // + weights
   static_assert(D == 64 || D == 128, "summary tiling");
+  static_assert(NU % NTS == 0 && NR * NWC == FT, "summary work split");
   static_assert(bytes <= 160 * 1024, "LDS budget of one CU exceeded");
 };
 
@@ -63,14 +71,17 @@ __device__ inline bf16x8 frag_trans_bf16(const bf16* base, int s0, int s1, int c
 #endif
 }
 
+template <int V>
+using IC = std::integral_constant<int, V>;
+
 template <int D>
 __global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void summary_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J) {
   using Cfg = SumCfg<D>;
   using M = Mma<bf16>;
   typedef bf16x8 Frag;
-  constexpr int CB = Cfg::CB, NT = Cfg::NT, RT = Cfg::RT, CT = Cfg::CT, LDR = Cfg::LDR;
-  constexpr int UPR = Cfg::UPR, NU = Cfg::NU, NUT = Cfg::NUT;
+  constexpr int CB = Cfg::CB, LDR = Cfg::LDR, FT = Cfg::FT, NR = Cfg::NR;
+  constexpr int UPR = Cfg::UPR, NUS = Cfg::NUS, NTS = Cfg::NTS, NWC = Cfg::NWC;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   auto krows = [&](int slot) { return reinterpret_cast<bf16*>(smem + slot * Cfg::szSlot); };
   auto vrows = [&](int slot) { return krows(slot) + CB * LDR; };
@@ -85,9 +96,6 @@ void summary_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J
   int tid = threadIdx.x, lane = tid % kWave;
   int lr = lane % 16, lg = lane / 16;
   auto refresh = [&]() { asm volatile("" : "+v"(tid), "+v"(lane), "+v"(lr), "+v"(lg)); };
-  // the wave's weights of two blocks (block p in half p % 2)
-  float* v_wl = reinterpret_cast<float*>(smem + 2 * Cfg::szSlot) + wave * 2 * CB;
-  const int a0 = RT * (wave % 2), b0 = CT * (wave / 2);
   // the segment's tokens [t_begin, t_end) in blocks of CB (= the chunk), block 0 the last one
   const int t_begin = seg * J * CB;
   long long seq0;  // first row of sequence b
@@ -98,50 +106,71 @@ void summary_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J
   if (seg >= last_segment(Tlen, J, CB)) return;
   const int t_end = min(Tlen, t_begin + J * CB);
   const int NB = (t_end - t_begin + CB - 1) / CB;
-  const long long tok_stride = (long long)Hn * D;
-  const uint32_t tok_bytes = (uint32_t)Hn * D * 2u;
   auto block_t0 = [&](int p) { return t_begin + (NB - 1 - p) * CB; };
 
-  // rows of two blocks in registers (register set q holds block p with p % 2 == q)
-  bf16x8 kr[2][NUT], vr[2][NUT];
-  float gr[2], br[2];  // gates and write gates (lane = token)
-  // the write gates are read from the gates when there are none (and then not used)
-  const float* bsrc = A.beta ? A.beta : A.gamma;
-  auto load_block = [&](int p, int q) __attribute__((always_inline)) {
-    refresh();
-    const int pv = p < NB ? p : NB - 1;
-    const int t0n = block_t0(pv);
-    const int nvn = p < NB ? min(CB, t_end - t0n) : 0;
-    const long long row0 = (seq0 + t0n) * tok_stride + (long long)h * D;
-    const uint32_t valid = nvn > 0 ? (uint32_t)(nvn - 1) * tok_bytes + D * 2u : 0u;
-    const auto rk = buffer_rsrc(static_cast<const bf16*>(A.k) + row0, valid);
-    const auto rv = buffer_rsrc(static_cast<const bf16*>(A.v) + row0, valid);
+  if (wave >= NWC) {
+    // ======== staging wave ========
+    const int ts = tid - NWC * kWave;  // 0 .. NTS - 1
+    float* v_wl = reinterpret_cast<float*>(smem + 2 * Cfg::szSlot) + (wave - NWC) * CB;
+    const long long tok_stride = (long long)Hn * D;
+    const uint32_t tok_bytes = (uint32_t)Hn * D * 2u;
+    // rows of two blocks in registers (register set q holds block p with p % 2 == q)
+    bf16x8 kr[2][NUS], vr[2][NUS];
+    float gr[2], br[2];  // gates and write gates (lane = token)
+    // the write gates are read from the gates when there are none (and then not used)
+    const float* bsrc = A.beta ? A.beta : A.gamma;
+    float suffix = 0.0f;  // log2 gate sum of the blocks already weighted (the later ones)
+    auto load_block = [&](int p, int q) __attribute__((always_inline)) {
+      refresh();
+      const int pv = p < NB ? p : NB - 1;
+      const int t0n = block_t0(pv);
+      const int nvn = p < NB ? min(CB, t_end - t0n) : 0;
+      const long long row0 = (seq0 + t0n) * tok_stride + (long long)h * D;
+      const uint32_t valid = nvn > 0 ? (uint32_t)(nvn - 1) * tok_bytes + D * 2u : 0u;
+      const auto rk = buffer_rsrc(static_cast<const bf16*>(A.k) + row0, valid);
+      const auto rv = buffer_rsrc(static_cast<const bf16*>(A.v) + row0, valid);
 #pragma unroll
-    for (int k = 0; k < NUT; ++k) {
-      const int u = (tid + k * NT) % NU;  // (threads past NU repeat a unit; never written)
-      const int tt = (uint32_t)u / UPR, cu = (uint32_t)u % UPR;  // u >= 0
-      const uint32_t off = (uint32_t)tt * tok_bytes + (uint32_t)cu * 16u;
-      kr[q][k] = buffer_load16<bf16x8>(rk, off);
-      vr[q][k] = buffer_load16<bf16x8>(rv, off);
-    }
-    const uint32_t gvalid = nvn > 0 ? (uint32_t)(nvn - 1) * Hn * 4u + 4u : 0u;
-    const auto rg = buffer_rsrc(A.gamma + (seq0 + t0n) * Hn + h, gvalid);
-    const auto rb = buffer_rsrc(bsrc + (seq0 + t0n) * Hn + h, gvalid);
-    gr[q] = buffer_load4f(rg, (uint32_t)lane * Hn * 4u);
-    br[q] = buffer_load4f(rb, (uint32_t)lane * Hn * 4u);
-  };
-  // rows of register set q to slot `slot`, with the weighted keys (weights wl, token-indexed)
-  auto write_block = [&](int slot, int q, const float* wl) __attribute__((always_inline)) {
-    refresh();
+      for (int k = 0; k < NUS; ++k) {
+        const int u = ts + k * NTS;
+        const int tt = (uint32_t)u / UPR, cu = (uint32_t)u % UPR;  // u >= 0
+        const uint32_t off = (uint32_t)tt * tok_bytes + (uint32_t)cu * 16u;
+        kr[q][k] = buffer_load16<bf16x8>(rk, off);
+        vr[q][k] = buffer_load16<bf16x8>(rv, off);
+      }
+      const uint32_t gvalid = nvn > 0 ? (uint32_t)(nvn - 1) * Hn * 4u + 4u : 0u;
+      const auto rg = buffer_rsrc(A.gamma + (seq0 + t0n) * Hn + h, gvalid);
+      const auto rb = buffer_rsrc(bsrc + (seq0 + t0n) * Hn + h, gvalid);
+      gr[q] = buffer_load4f(rg, (uint32_t)lane * Hn * 4u);
+      br[q] = buffer_load4f(rb, (uint32_t)lane * Hn * 4u);
+    };
+    // weights of block p (lane = token) from its gates in register set q, into this wave's
+    // v_wl: 2^(log2 of the gates after the token), times the token's write gate
+    // (the asm statements below tie the register sets to the phase that consumes them: without
+    // them the compiler hoists their arithmetic above the previous barrier, and with it the wait
+    // for loads issued one phase ago instead of two)
+    auto weigh = [&](int p, int q) __attribute__((always_inline)) {
+      asm volatile("" : "+v"(gr[q]), "+v"(br[q]));
+      const int nv = p < NB ? min(CB, t_end - block_t0(p)) : 0;
+      const float l2 = lane < nv ? log2_gate(gr[q]) : 0.0f;
+      const float cl = scan_add<kWave>(l2);
+      const float clast = lane_value(cl, CB - 1);
+      const float bw = A.beta ? br[q] : 1.0f;
+      v_wl[lane] = fast_exp2(fminf(clast - cl + suffix, 0.0f)) * bw;
+      suffix += clast;
+    };
+    // rows of register set q to slot `slot`, with the weighted keys (weights from v_wl)
+    auto write_block = [&](int slot, int q) __attribute__((always_inline)) {
+      refresh();
 #pragma unroll
-    for (int k = 0; k < NUT; ++k) {
-      const int u = tid + k * NT;
-      if (NU % NT == 0 || u < NU) {
+      for (int k = 0; k < NUS; ++k) asm volatile("" : "+v"(kr[q][k]), "+v"(vr[q][k]));
+#pragma unroll
+      for (int k = 0; k < NUS; ++k) {
+        const int u = ts + k * NTS;
         const int tt = (uint32_t)u / UPR, cu = (uint32_t)u % UPR;  // u >= 0
         const int o = tt * LDR + cu * 8;
         *reinterpret_cast<bf16x8*>(krows(slot) + o) = kr[q][k];
         *reinterpret_cast<bf16x8*>(vrows(slot) + o) = vr[q][k];
-        const float w = wl[tt];
+        const float w = v_wl[tt];
         bf16x8 hi, lo;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
@@ -152,131 +181,120 @@ void summary_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J
         *reinterpret_cast<bf16x8*>(hirows(slot) + o) = hi;
         *reinterpret_cast<bf16x8*>(lorows(slot) + o) = lo;
       }
-    }
-  };
-
-  f32x4 Hst[RT][CT], Ust[RT][CT];
-#pragma unroll
-  for (int jr = 0; jr < RT; ++jr)
-#pragma unroll
-    for (int jc = 0; jc < CT; ++jc) {
-      Hst[jr][jc] = f32x4{0.f, 0.f, 0.f, 0.f};
-      Ust[jr][jc] = f32x4{0.f, 0.f, 0.f, 0.f};
-    }
-  float suffix = 0.0f;  // log2 gate sum of the blocks already weighted (the later ones)
-
-  // weights of block p (lane = token), from its gates in register set q, one phase before
-  // its products: 2^(log2 of the gates after the token), times the token's write gate
-  auto weigh = [&](int p, int q) __attribute__((always_inline)) {
-    const int nv = p < NB ? min(CB, t_end - block_t0(p)) : 0;
-    const float l2 = lane < nv ? log2_gate(gr[q]) : 0.0f;
-    const float cl = scan_add<kWave>(l2);
-    const float clast = lane_value(cl, CB - 1);
-    const float bw = A.beta ? br[q] : 1.0f;
-    v_wl[(p & 1) * CB + lane] = fast_exp2(fminf(clast - cl + suffix, 0.0f)) * bw;
-    suffix += clast;
-  };
-  // block p from slot p % 2 into the state: every fragment of the block first, then the
-  // products, the hi halves of all tiles before the lo halves (dependent products far apart)
-  auto accumulate = [&](int p) __attribute__((always_inline)) {
-    refresh();
-    const int slot = p & 1;
-    const bf16* kb = krows(slot);
-    const bf16* vb = vrows(slot);
-    const bf16* hb = hirows(slot);
-    const bf16* lb = lorows(slot);
-    const int cq = 4 * (lr & 3);
-    constexpr int KB = Cfg::KB;
-    // A operands: K^T and V^T row fragments; B operands: the weighted keys of the column tiles,
-    // hi and lo (shared by the two products: dH = K^T diag(w) K, dU = V^T diag(w) K)
-    Frag ak[KB][RT], av[KB][RT], bh[KB][CT], bl[KB][CT];
-#pragma unroll
-    for (int kc = 0; kc < KB; ++kc) {
-      const int s0 = 32 * kc + 4 * lg, s1 = s0 + 16;
-#pragma unroll
-      for (int jr = 0; jr < RT; ++jr) {
-        ak[kc][jr] = frag_trans_bf16<LDR>(kb, s0, s1, 16 * (a0 + jr) + cq, lr);
-        av[kc][jr] = frag_trans_bf16<LDR>(vb, s0, s1, 16 * (a0 + jr) + cq, lr);
-      }
-#pragma unroll
-      for (int jc = 0; jc < CT; ++jc) {
-        bh[kc][jc] = frag_trans_bf16<LDR>(hb, s0, s1, 16 * (b0 + jc) + cq, lr);
-        bl[kc][jc] = frag_trans_bf16<LDR>(lb, s0, s1, 16 * (b0 + jc) + cq, lr);
-      }
-    }
-#pragma unroll
-    for (int kc = 0; kc < KB; ++kc) {
-#pragma unroll
-      for (int jc = 0; jc < CT; ++jc)
-#pragma unroll
-        for (int jr = 0; jr < RT; ++jr) {
-          Hst[jr][jc] = M::mma(ak[kc][jr], bh[kc][jc], Hst[jr][jc]);
-          Ust[jr][jc] = M::mma(av[kc][jr], bh[kc][jc], Ust[jr][jc]);
-        }
-#pragma unroll
-      for (int jc = 0; jc < CT; ++jc)
-#pragma unroll
-        for (int jr = 0; jr < RT; ++jr) {
-          Hst[jr][jc] = M::mma(ak[kc][jr], bl[kc][jc], Hst[jr][jc]);
-          Ust[jr][jc] = M::mma(av[kc][jr], bl[kc][jc], Ust[jr][jc]);
-        }
-    }
-  };
-  // phase p: the rows of block p + 1 (register set (p + 1) % 2) go to slot (p + 1) % 2, that set
-  // is reloaded with block p + 3, and block p is accumulated from slot p % 2. The two waves of a
-  // SIMD (w and w + 4) take the two halves in opposite orders: while one issues its products,
-  // the other stages, so the matrix pipe stays busy through the staging.
-  const bool stage_first = wave >= Cfg::NW / 2;
-  // (every phase stages and loads, also past the last block -- zero rows from loads with an
-  // empty range -- so that every path through the loop has the same loads in flight)
-  auto stage = [&](int p, int q) __attribute__((always_inline)) {
-    weigh(p + 1, q);
-    write_block(q, q, v_wl + ((p + 1) & 1) * CB);
-    load_block(p + 3, q);
-  };
-  load_block(0, 0);
-  load_block(1, 1);
-  weigh(0, 0);
-  write_block(0, 0, v_wl);
-  load_block(2, 0);
-  lds_barrier();
-  // (one loop per order: with the order fixed inside a loop the compiler tracks which loads
-  // are still in flight, and waits for the older register set only)
-  if (stage_first) {
+    };
+    // block p + 1 (register set q) to slot q, and set q reloaded with block p + 3 (every phase
+    // stages and loads, also past the last block -- zero rows from loads with an empty range --
+    // so that every path through the loop has the same loads in flight)
+    auto stage = [&](int p, int q) __attribute__((always_inline)) {
+      weigh(p + 1, q);
+      write_block(q, q);
+      load_block(p + 3, q);
+    };
+    load_block(0, 0);
+    load_block(1, 1);
+    weigh(0, 0);
+    write_block(0, 0);
+    load_block(2, 0);
+    lds_barrier();
     for (int p = 0; p < NB; p += 2) {
       stage(p, 1);
-      accumulate(p);
-      lds_barrier();  // slot (p + 1) % 2 is written; slot p % 2 is read
-      stage(p + 1, 0);
-      if (p + 1 < NB) accumulate(p + 1);
-      lds_barrier();
-    }
-  } else {
-    for (int p = 0; p < NB; p += 2) {
-      accumulate(p);
-      stage(p, 1);
-      lds_barrier();
-      if (p + 1 < NB) accumulate(p + 1);
+      lds_barrier();  // slot (p + 1) % 2 is written; slot p % 2 has been read
       stage(p + 1, 0);
       lds_barrier();
     }
+    if (wave == NWC && lane == 0) A.log2g_out[(long long)bh * S + seg] = suffix;
+    return;
   }
 
-  if (wave == 0 && lane == 0) A.log2g_out[(long long)bh * S + seg] = suffix;
-  float* oh = A.sum_h + bh * A.sum_bh + seg * A.sum_seg;
-  float* ou = A.sum_u + bh * A.sum_bh + seg * A.sum_seg;
+  // ======== product wave ========
+  // (one instantiation per wave: its row tiles, and with TRI which tiles of dH it holds, are
+  // compile-time constants)
+  auto run = [&](auto W) __attribute__((always_inline)) {
+    constexpr int w = decltype(W)::value;
+    auto row = [](int r) { return Cfg::TRI ? (r == 0 ? w : FT - 1 - w) : w * NR + r; };
+    // tile (r, c) of dH is held when it lies on or above the diagonal (with TRI)
+    auto held = [&](int r, int c) { return !Cfg::TRI || c >= row(r); };
+    f32x4 Hacc[NR][FT], Uacc[NR][FT];
 #pragma unroll
-  for (int jr = 0; jr < RT; ++jr)
+    for (int r = 0; r < NR; ++r)
 #pragma unroll
-    for (int jc = 0; jc < CT; ++jc) {
-      // H[r..r+3][c] is written as H[c][r..r+3] (symmetric); the tile of U holds
-      // U[r..r+3][c] (rows = value features), four scattered stores
-      const size_t o = (size_t)(16 * (b0 + jc) + lr) * D + 16 * (a0 + jr) + 4 * lg;
-      *reinterpret_cast<f32x4*>(oh + o) = Hst[jr][jc];
+      for (int c = 0; c < FT; ++c) {
+        Hacc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+        Uacc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
+      }
+    // block p from slot p % 2: per 32-token block the A operands (K^T and V^T of the own row
+    // tiles), then column by column the B operands (weighted keys hi and lo) and the products,
+    // the hi halves of a column's tiles before its lo halves
+    auto accumulate = [&](int p) __attribute__((always_inline)) {
+      refresh();
+      const int slot = p & 1;
+      const bf16* kb = krows(slot);
+      const bf16* vb = vrows(slot);
+      const bf16* hb = hirows(slot);
+      const bf16* lb = lorows(slot);
+      const int cq = 4 * (lr & 3);
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-        ou[(size_t)(16 * (a0 + jr) + 4 * lg + i) * D + 16 * (b0 + jc) + lr] = Ust[jr][jc][i];
+      for (int kc = 0; kc < Cfg::KB; ++kc) {
+        const int s0 = 32 * kc + 4 * lg, s1 = s0 + 16;
+        Frag ak[NR], av[NR];
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          ak[r] = frag_trans_bf16<LDR>(kb, s0, s1, 16 * row(r) + cq, lr);
+          av[r] = frag_trans_bf16<LDR>(vb, s0, s1, 16 * row(r) + cq, lr);
+        }
+#pragma unroll
+        for (int c = 0; c < FT; ++c) {
+          const Frag bhf = frag_trans_bf16<LDR>(hb, s0, s1, 16 * c + cq, lr);
+          const Frag blf = frag_trans_bf16<LDR>(lb, s0, s1, 16 * c + cq, lr);
+#pragma unroll
+          for (int r = 0; r < NR; ++r) {
+            if (held(r, c)) Hacc[r][c] = M::mma(ak[r], bhf, Hacc[r][c]);
+            Uacc[r][c] = M::mma(av[r], bhf, Uacc[r][c]);
+          }
+#pragma unroll
+          for (int r = 0; r < NR; ++r) {
+            if (held(r, c)) Hacc[r][c] = M::mma(ak[r], blf, Hacc[r][c]);
+            Uacc[r][c] = M::mma(av[r], blf, Uacc[r][c]);
+          }
+        }
+      }
+    };
+    lds_barrier();  // block 0 is staged
+    for (int p = 0; p < NB; p += 2) {
+      accumulate(p);
+      lds_barrier();
+      if (p + 1 < NB) accumulate(p + 1);
+      lds_barrier();
     }
+    float* oh = A.sum_h + bh * A.sum_bh + seg * A.sum_seg;
+    float* ou = A.sum_u + bh * A.sum_bh + seg * A.sum_seg;
+#pragma unroll
+    for (int r = 0; r < NR; ++r)
+#pragma unroll
+      for (int c = 0; c < FT; ++c) {
+        // a tile (a, c) holds X[16 a + 4 lg + i][16 c + lr], i = 0..3. dH (symmetric) is written
+        // transposed as the rows 16 c + lr (one 16-byte store), and for an upper tile also as
+        // the mirror rows 16 a + 4 lg + i; dU (rows = value features) as four scattered stores
+        const int a = row(r);
+        if (held(r, c)) {
+          const f32x4 x = Hacc[r][c];
+          *reinterpret_cast<f32x4*>(oh + (size_t)(16 * c + lr) * D + 16 * a + 4 * lg) = x;
+          if (Cfg::TRI && c != a) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) oh[(size_t)(16 * a + 4 * lg + i) * D + 16 * c + lr] = x[i];
+          }
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          ou[(size_t)(16 * a + 4 * lg + i) * D + 16 * c + lr] = Uacc[r][c][i];
+      }
+  };
+  switch (wave) {
+    case 0: run(IC<0>{}); break;
+    case 1: run(IC<1>{}); break;
+    case 2: run(IC<2>{}); break;
+    default: run(IC<3>{}); break;
+  }
 }
 
 template <int D>
