@@ -563,25 +563,41 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
     // written back as rows: every later operand of it is one 16-byte read), and every K^T
     // fragment of the chunk, resident in registers until the loop ends (after the norm
     // phase's products, which do not need them) ----------------------------------------------
+    // (every read is issued before the first write and before the register-class hints, so
+    // that one wait covers them: a write between reads orders the later reads behind it)
     refresh();
+    {
+      constexpr int NVT = (FT * KC + NW - 1) / NW;
+      Frag g[NVT];
 #pragma unroll
-    for (int k = 0; k < (FT * KC + NW - 1) / NW; ++k) {
-      const int phi = wave + k * NW;
-      if (FT * KC % NW == 0 || phi < FT * KC) {
-        const int ft = phi / KC, kc = phi % KC;
-        const Frag g = frag_trans<LDD>(Vp, 32 * kc + 4 * lg, 32 * kc + 16 + 4 * lg,
-                                       16 * ft + 4 * (lr & 3), lr);
-        *reinterpret_cast<Frag*>(VT + (16 * ft + lr) * LDC + 32 * kc + 8 * lg) = g;
+      for (int k = 0; k < NVT; ++k) {
+        const int phi = wave + k * NW;
+        if (FT * KC % NW == 0 || phi < FT * KC) {
+          const int ft = phi / KC, kc = phi % KC;
+          g[k] = frag_trans<LDD>(Vp, 32 * kc + 4 * lg, 32 * kc + 16 + 4 * lg,
+                                 16 * ft + 4 * (lr & 3), lr);
+        }
+      }
+#pragma unroll
+      for (int k = 0; k < NVT; ++k) {
+        const int phi = wave + k * NW;
+        if (FT * KC % NW == 0 || phi < FT * KC) {
+          const int ft = phi / KC, kc = phi % KC;
+          *reinterpret_cast<Frag*>(VT + (16 * ft + lr) * LDC + 32 * kc + 8 * lg) = g[k];
+        }
       }
     }
     Frag ktr[KC][FT];
 #pragma unroll
     for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
-      for (int ft = 0; ft < FT; ++ft) {
-        ktr[kc][ft] = frag_kt(ft, kc);
-        if constexpr (Cfg::PIN) keep_in_agpr(ktr[kc][ft]);
-      }
+      for (int ft = 0; ft < FT; ++ft) ktr[kc][ft] = frag_kt(ft, kc);
+    if constexpr (Cfg::PIN) {
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc)
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft) keep_in_agpr(ktr[kc][ft]);
+    }
     lds_barrier();
 
     // ---- n_t^2 by an affine scan over the chunk (every wave; lane = token) -------------------
@@ -608,7 +624,9 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
           const int s = 16 * sb + 4 * lg + i;
-          Mh[sb][i] = s <= t ? fast_exp2(fminf(cl_t - cls[i], 0.0f)) * bts[i] * mt : 0.0f;
+          // (computed for every s and then selected: a conditional exp2 becomes a branch)
+          const float e = fast_exp2(fminf(cl_t - cls[i], 0.0f)) * bts[i] * mt;
+          Mh[sb][i] = s <= t ? e : 0.0f;
         }
       }
     }
@@ -892,10 +910,14 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
 #pragma unroll
       for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
-        for (int kk = 0; kk < KD; ++kk) {
+        for (int kk = 0; kk < KD; ++kk)
           Hres[ft][kk] = *reinterpret_cast<const Frag*>(Hs + (16 * ft + lr) * LDD + 32 * kk + 8 * lg);
-          if constexpr (Cfg::PIN) keep_in_agpr(Hres[ft][kk]);
-        }
+      if constexpr (Cfg::PIN) {
+#pragma unroll
+        for (int ft = 0; ft < FT; ++ft)
+#pragma unroll
+          for (int kk = 0; kk < KD; ++kk) keep_in_agpr(Hres[ft][kk]);
+      }
       float xm = 0.0f;
 #pragma unroll
       for (int ft = 0; ft < FT; ++ft)
