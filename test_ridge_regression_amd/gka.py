@@ -18,7 +18,8 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libgka.so")
+# GKA_LIBRARY names another build of the library (a sanitizer build of the host code, say)
+LIB_PATH = os.environ.get("GKA_LIBRARY") or os.path.join(_HERE, "libgka.so")
 
 GKA_BF16 = 0
 GKA_FP32 = 1
