@@ -32,6 +32,22 @@
  *   - Errors: every argument is checked on the host before anything is enqueued; on an error
  *     the call returns its status and writes nothing. GKA_ERR_HIP reports a failed launch;
  *     faults inside a kernel surface at the caller's next synchronisation of `stream`.
+ *   - Accepted range. The bf16 prefill with chunks of 64 (the token-owning walk) rescales its
+ *     16-bit matrix operands by exact powers of two: the keys and values per chunk, the queries
+ *     and the iterate per token, the value state per wave. At its largest each operand then lies
+ *     in [1, 2), and the scales are undone in float32. Any bf16 inputs are therefore accepted
+ *     whose float32 intermediates stay finite and normal: in practice |q| and |v| within 2^+-60
+ *     of unit scale and |k| within 2^+-25 (||H_t||_F^2 grows like |k|^4). Tested with q scaled by
+ *     2^-12 .. 2^10, k by 2^-12 .. 2^8 and v by 2^-20 .. 2^17 at D = 64 and 128.
+ *     Elsewhere the operands are used as they are. The bf16 prefill with chunks of 32 (D >= 32),
+ *     and the segment summaries of a multi-segment plan at D = 32, convert k and v (and q) to
+ *     fp16 operands, so there they must lie within fp16's range (|x| < 65504, and above 2^-14 for
+ *     full precision). bf16 at D = 16, the float32 prefill and the decode step compute on
+ *     float32 throughout.
+ *   - Interface choices: `stream` is a void* (a hipStream_t) so that this header needs no HIP
+ *     include; gka_params.segments lets a caller fix the segment plan (results depend on it only
+ *     through rounding order); gka_fwd_chunked's phase_events is a timing hook;
+ *     GKA_ERR_ALIAS rejects outputs that overlap inputs.
  */
 #ifndef GKA_H
 #define GKA_H
@@ -140,9 +156,12 @@ gka_status gka_step(const gka_params* p, const void* q, const void* k, const voi
  * Other arguments, layouts, ownership and errors are those of the base entry point; in addition
  * a beta that is not 4-byte aligned gives GKA_ERR_SHAPE and one that overlaps o GKA_ERR_ALIAS.
  * Internally
- * the prefill applies beta as sqrt(beta_t) on the token's key and value rows where they are
- * converted to the 16-bit matrix operands, and as a factor of the token's weight in the
- * per-segment summaries; in exact arithmetic both give the recurrence above.
+ * the bf16 prefill with chunks of 64 applies beta through float32 weights (the carry weights,
+ * the intra-chunk mask and the norm terms), so its carried state is as accurate as without a
+ * gate. The other prefill paths apply sqrt(beta_t) on the token's key and value rows where they
+ * become matrix operands (bf16 with chunks of 32: fp16 operands, so the state is accurate to
+ * about 1e-3 relative). The per-segment summaries take beta_t as a factor of the token's
+ * weight. In exact arithmetic all of these give the recurrence above.
  */
 gka_status gka_fwd_chunked_beta(const gka_params* p, const void* q, const void* k, const void* v,
                                 const float* gamma, const float* beta, void* o, float* h_state,
