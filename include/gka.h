@@ -84,8 +84,9 @@ typedef enum { GKA_BF16 = 0, GKA_FP32 = 1 } gka_dtype;
  *            last partial chunk is handled exactly
  *   D        head dimension (key dim = value dim): {16, 32, 64, 128}
  *   chunk    tokens per chunk for the chunk-wise form (prefill; ignored by gka_step):
- *            bf16 {32, 64}; fp32 {16, 32, 64} for D <= 64 and {16} for D = 128. The result
- *            does not depend on it beyond rounding (N = ceil(T / chunk) chunks).
+ *            bf16 {32, 64}, and 16 for D >= 32 (float32 matrix operands); fp32 {16, 32, 64}
+ *            for D <= 64 and {16} for D = 128. The result does not depend on it beyond
+ *            rounding (N = ceil(T / chunk) chunks).
  *   iters    Chebyshev iterations r, 1 <= r <= GKA_MAX_ITERS
  *   a        ridge scale, a > 0 and finite
  *   dtype    element type of q, k, v, o (gka_dtype)

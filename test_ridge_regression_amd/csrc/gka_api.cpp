@@ -24,7 +24,9 @@ bool dims_supported(int dtype, int D) {
   return D == 16 || D == 32 || D == 64 || D == 128;
 }
 bool chunk_supported(int dtype, int D, int C) {
-  if (dtype == GKA_BF16) return C == 32 || C == 64;
+  // bf16 with chunks of 16 (D >= 32: a chunk's rows must fill whole waves of 16-byte loads)
+  // takes float32 operands, as float32 inputs do (fp16 products need blocks of 32 tokens)
+  if (dtype == GKA_BF16) return C == 32 || C == 64 || (C == 16 && D >= 32);
   if (D == 128) return C == 16;  // float32 operands of D = 128 fit the LDS of a CU at C = 16
   return C == 16 || C == 32 || C == 64;
 }

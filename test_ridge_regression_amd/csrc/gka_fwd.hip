@@ -57,9 +57,10 @@ namespace gka {
 // the summary walk, which holds only the state and so spreads it over four waves per SIMD.
 template <typename T, int D, int C, int NWaves = 8>
 struct WalkCfg {
-  // matrix-core operand type: fp16 for bf16 inputs, whose products take blocks of 32 features;
-  // float32 for float32 inputs and for bf16 inputs with D = 16 (exact for bf16 values)
-  typedef typename std::conditional<(D < 32), float, typename OperandOf<T>::type>::type O;
+  // matrix-core operand type: fp16 for bf16 inputs, whose products take blocks of 32 features
+  // and 32 tokens; float32 for float32 inputs, and for bf16 inputs with D = 16 or C = 16 (exact
+  // for bf16 values)
+  typedef typename std::conditional<(D < 32 || C < 32), float, typename OperandOf<T>::type>::type O;
   static constexpr int NW = NWaves;
   static constexpr int NT = NW * kWave;
   static constexpr int FT = D / 16;  // feature tiles
@@ -1118,7 +1119,13 @@ hipError_t launch_walk(const FwdPlan& pl, bool summary, const WalkArgs& a, const
   if (!summary && walk_tok_supported(pl)) return launch_walk_tok(pl, a, cc, stream);
   if (summary && summary_tok_supported(pl)) return launch_summary_tok(pl, a, stream);
   if (pl.dtype == 0) {
-    if (pl.C == 64) {
+    if (pl.C == 16) {
+      switch (pl.D) {
+        case 32: return launch_walk_t<bf16, 32, 16>(pl, summary, a, cc, stream);
+        case 64: return launch_walk_t<bf16, 64, 16>(pl, summary, a, cc, stream);
+        case 128: return launch_walk_t<bf16, 128, 16>(pl, summary, a, cc, stream);
+      }
+    } else if (pl.C == 64) {
       switch (pl.D) {
         case 16: return launch_walk_t<bf16, 16, 64>(pl, summary, a, cc, stream);
         case 32: return launch_walk_t<bf16, 32, 64>(pl, summary, a, cc, stream);

@@ -69,7 +69,7 @@ def step(lib, p, q=VP[0], k=VP[1], v=VP[2], g=VP[3], o=VP[4], h=VP[5], u=VP[6], 
 @pytest.mark.parametrize("kw,code", [
     (dict(dtype_code=7), 4),
     (dict(D=48), 2), (dict(D=256), 2), (dict(dtype_code=gka.GKA_FP32, D=128), 2),
-    (dict(chunk=48), 2), (dict(chunk=16), 2), (dict(chunk=128), 2),
+    (dict(chunk=48), 2), (dict(chunk=8), 2), (dict(chunk=128), 2), (dict(D=16, chunk=16), 2),
     (dict(B=0), 2), (dict(H=0), 2), (dict(T=-1), 2), (dict(segments=-3), 2),
     (dict(a=0.0), 3), (dict(a=-0.1), 3), (dict(a=float("nan")), 3), (dict(a=float("inf")), 3),
     (dict(iters=0), 3), (dict(iters=65), 3),
@@ -259,7 +259,8 @@ def test_missing_library_fails_loudly(tmp_path):
 def test_all_head_sizes_are_accepted(lib):
     P = ctypes.byref
     # multi-segment plans need a workspace: a nonzero size means the shape passed the checks
-    for dt, D, C in ((gka.GKA_BF16, 16, 32), (gka.GKA_BF16, 16, 64), (gka.GKA_FP32, 128, 16)):
+    for dt, D, C in ((gka.GKA_BF16, 16, 32), (gka.GKA_BF16, 16, 64), (gka.GKA_FP32, 128, 16),
+                     (gka.GKA_BF16, 32, 16), (gka.GKA_BF16, 128, 16)):
         assert lib.gka_fwd_workspace_bytes(P(params(dtype_code=dt, D=D, chunk=C, T=4096))) > 0
     for C in (32, 64):  # float32 D = 128 only with chunks of 16
         assert lib.gka_fwd_workspace_bytes(P(params(dtype_code=gka.GKA_FP32, D=128, chunk=C,

@@ -93,7 +93,8 @@ def test_fp32_chunk_and_head_sizes(D, C):
     check_prefill(got, ref, "fp32", f"fp32 D={D} C={C}")
 
 
-@pytest.mark.parametrize("D,C", [(32, 32), (32, 64), (64, 32), (64, 64), (128, 32), (128, 64)])
+@pytest.mark.parametrize("D,C", [(32, 16), (32, 32), (32, 64), (64, 16), (64, 32), (64, 64),
+                                 (128, 16), (128, 32), (128, 64)])
 def test_bf16_chunk_and_head_sizes(D, C):
     T = 448
     q, k, v, g = inputs(2, T, 3, D, "bf16", seed=30 + D + C)
@@ -101,6 +102,33 @@ def test_bf16_chunk_and_head_sizes(D, C):
     log(f"bf16 D={D} C={C} T={T}")
     got = run_prefill(q, k, v, g, 0.05, 10, C, "bf16")
     check_prefill(got, ref, "bf16", f"bf16 D={D} C={C}")
+
+
+@pytest.mark.parametrize("D", [64, 128])
+def test_bf16_chunk_size_invariance(D):
+    """C in {16, 32, 64} (float32 operands, the feature-split walk, the token walk) on the same
+    inputs, from a carried state and in 3 segments: each against the oracle, and the final
+    states against each other."""
+    B, T, H = 1, 5 * 64 + 19, 2
+    q, k, v, g = inputs(B, 2 * T, H, D, "bf16", seed=71 + D)
+    ref = gka_forward_ref(q, k, v, g, 0.05, 10)
+    warm = gka_forward_ref(q[:, :T], k[:, :T], v[:, :T], g[:, :T], 0.05, 10, mode="state")
+    st = (warm["h"].astype(np.float32).astype(np.float64),
+          warm["u"].astype(np.float32).astype(np.float64),
+          warm["n2"].astype(np.float32).astype(np.float64))
+    ref2 = gka_forward_ref(q[:, T:], k[:, T:], v[:, T:], g[:, T:], 0.05, 10, h0=st[0], u0=st[1],
+                           n2_0=st[2])
+    finals = []
+    for C in (16, 32, 64):
+        log(f"bf16 chunk invariance D={D} C={C}")
+        got = run_prefill(q[:, T:], k[:, T:], v[:, T:], g[:, T:], 0.05, 10, C, "bf16", state=st,
+                          segments=3)
+        check_prefill(got, ref2, "bf16", f"bf16 D={D} C={C} (carried state, 3 segments)")
+        finals.append(got)
+        assert rel_l2(got["h"], ref["h"]) < 1e-4 and rel_l2(got["u"], ref["u"]) < 1e-4
+    for other in finals[1:]:
+        assert rel_l2(other["h"], finals[0]["h"]) < 1e-4
+        assert rel_l2(other["u"], finals[0]["u"]) < 1e-4
 
 
 @pytest.mark.parametrize("segments", [1, 2, 3, 5, 16])
