@@ -9,7 +9,8 @@ each path (measured with HIP events on the library's stream), and the float64 CP
 on a bounded sample of the prefill workload on this host.
 
 The write-gated prefill (gka_fwd_chunked_beta, same workload plus per-token write gates) is
-timed the same way and reported under "write_gate"; the solver-convergence mode
+timed the same way and reported under "write_gate"; the same workload at chunks of 32 and 16 (the
+feature-split walk) under "chunk_sizes"; the solver-convergence mode
 (gka_fwd_chunked_residuals) under "solver_convergence", with its residual curve; a serving
 step on a packed batch of prompts and decode rows (gka_fwd_varlen) under "varlen"; the backward
 pass (gka_bwd) on the prefill workload under "backward". The oracle leg also compares its outputs of
@@ -24,12 +25,13 @@ kernel and for the whole call.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W] [--decode-steps S] [--no-cpu]
                        [--no-decode] [--no-beta] [--no-resid] [--no-varlen] [--no-bwd]
-                       [--no-configs]
+                       [--no-configs] [--no-chunks]
 """
 from __future__ import annotations
 
 import argparse
 import ctypes
+import dataclasses
 import hashlib
 import json
 import os
@@ -442,6 +444,8 @@ def main():
     ap.add_argument("--no-resid", action="store_true", help="skip the solver-convergence mode")
     ap.add_argument("--no-varlen", action="store_true", help="skip the packed serving step")
     ap.add_argument("--no-bwd", action="store_true", help="skip the backward pass")
+    ap.add_argument("--no-chunks", action="store_true",
+                    help="skip the headline workload at chunks of 32 and 16")
     ap.add_argument("--no-configs", action="store_true",
                     help="skip the wide-head and long-context prefill workloads")
     ap.add_argument("--copy-probe", action="store_true",
@@ -547,6 +551,23 @@ def main():
         }
         log(f"beta prefill: {pb['ms_per_step']:.3f} ms/step (walk {pb['walk_ms']:.3f})")
         del pb, bd
+    if not args.no_chunks:
+        # the other chunk sizes of the bf16 path on the same inputs: C = 32 takes the
+        # feature-split walk (fp16 operands), C = 16 the same walk on float32 operands
+        rec["chunk_sizes"] = []
+        for C in (32, 16):
+            Wc = dataclasses.replace(W, chunk=C)
+            pc = bench_prefill(Wc, inputs, args.steps, args.warmup, ev, what=f"prefill C={C}")
+            pc.pop("o")
+            rec["chunk_sizes"].append({
+                "workload": W.name, "chunk": C, "segments": pc["segments"],
+                "tokens_per_s": tokens / (pc["ms_per_step"] * 1e-3),
+                "ms_per_step": pc["ms_per_step"],
+                "phases_ms": {"summary": pc["summary_ms"], "scan": pc["scan_ms"],
+                              "walk": pc["walk_ms"]},
+                **prefill_fractions(Wc, pc["ms_per_step"], pc["walk_ms"])})
+            log(f"prefill C={C}: {pc['ms_per_step']:.3f} ms/step (walk {pc['walk_ms']:.3f})")
+            del pc
     if not args.no_bwd:
         rec["backward"] = bench_backward(W, inputs, max(1, args.steps // 10), 1, ev)
         log(f"backward: {rec['backward']['ms_per_step']:.2f} ms/step")
