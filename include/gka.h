@@ -37,13 +37,12 @@
  *     and the iterate per token, the value state per wave. At its largest each operand then lies
  *     in [1, 2), and the scales are undone in float32. Any bf16 inputs are therefore accepted
  *     whose float32 intermediates stay finite and normal: in practice |q| and |v| within 2^+-60
- *     of unit scale and |k| within 2^+-25 (||H_t||_F^2 grows like |k|^4). Tested with q scaled by
- *     2^-12 .. 2^10, k by 2^-12 .. 2^8 and v by 2^-20 .. 2^17 at D = 64 and 128.
- *     Elsewhere the operands are used as they are. The bf16 prefill with chunks of 32 (D >= 32),
- *     and the segment summaries of a multi-segment plan at D = 32, convert k and v (and q) to
- *     fp16 operands, so there they must lie within fp16's range (|x| < 65504, and above 2^-14 for
- *     full precision). bf16 at D = 16, the float32 prefill and the decode step compute on
- *     float32 throughout.
+ *     of unit scale and |k| within 2^+-25 (||H_t||_F^2 grows like |k|^4).
+ *     Tested with q scaled by 2^-12 .. 2^10, k by 2^-12 .. 2^8 and v by 2^-20 .. 2^17 at D = 32,
+ *     64 and 128. Elsewhere the operands are used as they are. The bf16 prefill with chunks of 32
+ *     converts q, k and v to fp16 operands, so there they must lie within fp16's range
+ *     (|x| < 65504, and above 2^-14 for full precision). bf16 with chunks of 16 or D = 16, the
+ *     float32 prefill and the decode step compute on float32 throughout.
  *   - Interface choices: `stream` is a void* (a hipStream_t) so that this header needs no HIP
  *     include; gka_params.segments lets a caller fix the segment plan (results depend on it only
  *     through rounding order); gka_fwd_chunked's phase_events is a timing hook;

@@ -42,7 +42,10 @@ struct SumCfg {
   static constexpr int NTS = NWS * kWave;      // staging threads
   static constexpr int FT = D / 16;            // feature tiles
   static constexpr bool TRI = D == 128;        // dH from its upper-triangle tiles
-  static constexpr int NR = FT / NWC;          // row tiles per product wave
+  // tiles of a product wave: NR row tiles by NC column tiles (D = 128: rows w and 7 - w, all
+  // columns; D = 64: row w, all columns; D = 32: row w / 2, column w % 2)
+  static constexpr int NR = FT >= NWC ? FT / NWC : 1;
+  static constexpr int NC = FT >= NWC ? FT : FT * FT / NWC;
   static constexpr int LDR = D + 16;  // row stride of the rows (bf16): 8 banks apart, so the
                                       // 16 rows of a transposing read share no bank
   static constexpr int VEC = 8, UPR = D / VEC, NU = CB * UPR;
@@ -50,8 +53,8 @@ struct SumCfg {
   static constexpr size_t szRows = (size_t)CB * LDR * 2;
   static constexpr size_t szSlot = 4 * szRows;  // rows of K, V, (w k) hi and (w k) lo
   static constexpr size_t bytes = 2 * szSlot + (size_t)NWS * CB * sizeof(float);  // + weights
-  static_assert(D == 64 || D == 128, "summary tiling");
-  static_assert(NU % NTS == 0 && NR * NWC == FT, "summary work split");
+  static_assert(D == 32 || D == 64 || D == 128, "summary tiling");
+  static_assert(NU % NTS == 0 && NR * NC * NWC == FT * FT, "summary work split");
   static_assert(bytes <= 160 * 1024, "LDS budget of one CU exceeded");
 };
 
@@ -80,7 +83,7 @@ void summary_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J
   using Cfg = SumCfg<D>;
   using M = Mma<bf16>;
   typedef bf16x8 Frag;
-  constexpr int CB = Cfg::CB, LDR = Cfg::LDR, FT = Cfg::FT, NR = Cfg::NR;
+  constexpr int CB = Cfg::CB, LDR = Cfg::LDR, FT = Cfg::FT, NR = Cfg::NR, NC = Cfg::NC;
   constexpr int UPR = Cfg::UPR, NUS = Cfg::NUS, NTS = Cfg::NTS, NWC = Cfg::NWC;
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
   auto krows = [&](int slot) { return reinterpret_cast<bf16*>(smem + slot * Cfg::szSlot); };
@@ -211,14 +214,18 @@ void summary_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J
   // compile-time constants)
   auto run = [&](auto W) __attribute__((always_inline)) {
     constexpr int w = decltype(W)::value;
-    auto row = [](int r) { return Cfg::TRI ? (r == 0 ? w : FT - 1 - w) : w * NR + r; };
-    // tile (r, c) of dH is held when it lies on or above the diagonal (with TRI)
-    auto held = [&](int r, int c) { return !Cfg::TRI || c >= row(r); };
-    f32x4 Hacc[NR][FT], Uacc[NR][FT];
+    auto row = [](int r) {
+      return Cfg::TRI ? (r == 0 ? w : FT - 1 - w) : NC == FT ? w * NR + r : w / (FT / NC);
+    };
+    auto col = [](int c) { return NC == FT ? c : (w % (FT / NC)) * NC + c; };
+    // tile (r, c) of dH is held when it lies on or above the diagonal (with TRI; at D = 32 the
+    // wave below it holds dU only)
+    auto held = [&](int r, int c) { return Cfg::TRI || NC < FT ? col(c) >= row(r) : true; };
+    f32x4 Hacc[NR][NC], Uacc[NR][NC];
 #pragma unroll
     for (int r = 0; r < NR; ++r)
 #pragma unroll
-      for (int c = 0; c < FT; ++c) {
+      for (int c = 0; c < NC; ++c) {
         Hacc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
         Uacc[r][c] = f32x4{0.f, 0.f, 0.f, 0.f};
       }
@@ -243,9 +250,9 @@ void summary_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J
           av[r] = frag_trans_bf16<LDR>(vb, s0, s1, 16 * row(r) + cq, lr);
         }
 #pragma unroll
-        for (int c = 0; c < FT; ++c) {
-          const Frag bhf = frag_trans_bf16<LDR>(hb, s0, s1, 16 * c + cq, lr);
-          const Frag blf = frag_trans_bf16<LDR>(lb, s0, s1, 16 * c + cq, lr);
+        for (int c = 0; c < NC; ++c) {
+          const Frag bhf = frag_trans_bf16<LDR>(hb, s0, s1, 16 * col(c) + cq, lr);
+          const Frag blf = frag_trans_bf16<LDR>(lb, s0, s1, 16 * col(c) + cq, lr);
 #pragma unroll
           for (int r = 0; r < NR; ++r) {
             if (held(r, c)) Hacc[r][c] = M::mma(ak[r], bhf, Hacc[r][c]);
@@ -271,22 +278,22 @@ void summary_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J
 #pragma unroll
     for (int r = 0; r < NR; ++r)
 #pragma unroll
-      for (int c = 0; c < FT; ++c) {
-        // a tile (a, c) holds X[16 a + 4 lg + i][16 c + lr], i = 0..3. dH (symmetric) is written
-        // transposed as the rows 16 c + lr (one 16-byte store), and for an upper tile also as
+      for (int c = 0; c < NC; ++c) {
+        // a tile (a, b) holds X[16 a + 4 lg + i][16 b + lr], i = 0..3. dH (symmetric) is written
+        // transposed as the rows 16 b + lr (one 16-byte store), and for an upper tile also as
         // the mirror rows 16 a + 4 lg + i; dU (rows = value features) as four scattered stores
-        const int a = row(r);
+        const int a = row(r), bc = col(c);
         if (held(r, c)) {
           const f32x4 x = Hacc[r][c];
-          *reinterpret_cast<f32x4*>(oh + (size_t)(16 * c + lr) * D + 16 * a + 4 * lg) = x;
-          if (Cfg::TRI && c != a) {
+          *reinterpret_cast<f32x4*>(oh + (size_t)(16 * bc + lr) * D + 16 * a + 4 * lg) = x;
+          if ((Cfg::TRI || NC < FT) && bc != a) {  // (with every tile held, no mirrors)
 #pragma unroll
-            for (int i = 0; i < 4; ++i) oh[(size_t)(16 * a + 4 * lg + i) * D + 16 * c + lr] = x[i];
+            for (int i = 0; i < 4; ++i) oh[(size_t)(16 * a + 4 * lg + i) * D + 16 * bc + lr] = x[i];
           }
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-          ou[(size_t)(16 * a + 4 * lg + i) * D + 16 * c + lr] = Uacc[r][c][i];
+          ou[(size_t)(16 * a + 4 * lg + i) * D + 16 * bc + lr] = Uacc[r][c][i];
       }
   };
   switch (wave) {
@@ -315,11 +322,13 @@ hipError_t launch_sum(const FwdPlan& pl, const WalkArgs& a, hipStream_t stream) 
 bool summary_tok_supported(const FwdPlan& pl) {
   // the buffer loads address a block of 64 tokens with 32-bit byte offsets per lane
   const long long block_bytes = 64LL * pl.H * pl.D * 2;
-  return pl.dtype == 0 && pl.C == 64 && (pl.D == 64 || pl.D == 128) && block_bytes < (1LL << 31);
+  return pl.dtype == 0 && pl.C == 64 && (pl.D == 32 || pl.D == 64 || pl.D == 128) &&
+         block_bytes < (1LL << 31);
 }
 
 hipError_t launch_summary_tok(const FwdPlan& pl, const WalkArgs& a, hipStream_t stream) {
   switch (pl.D) {
+    case 32: return launch_sum<32>(pl, a, stream);
     case 64: return launch_sum<64>(pl, a, stream);
     case 128: return launch_sum<128>(pl, a, stream);
   }

@@ -85,6 +85,20 @@ def test_beta_bf16_chunk64(D, T):
         check(got, ref, "bf16", f"beta bf16 C=64 D={D} T={T} S={seg}", state=True)
 
 
+# calls from the zero state with 2..4 segments: each walk workgroup composes its segment-start
+# state from the summaries before it (no scan); D = 32 takes its summaries from the
+# feature-split summary kernel
+@pytest.mark.parametrize("D", [32, 128])
+def test_beta_bf16_composed_segment_starts(D):
+    T = 4 * 64 + 23
+    q, k, v, g, bt = gated_inputs(2, T, 2, D, "bf16", seed=560 + D)
+    ref = gka_forward_ref(q, k, v, g, 0.05, 10, beta=bt)
+    for seg in (2, 3, 4):
+        log(f"beta bf16 composed starts D={D} segments={seg}")
+        got = run_prefill(q, k, v, g, 0.05, 10, 64, "bf16", segments=seg, beta=bt)
+        check(got, ref, "bf16", f"beta bf16 composed starts D={D} S={seg}")
+
+
 # the feature-split walk and summary: float32 inputs, and bf16 with chunks of 32
 @pytest.mark.parametrize("dtype,D,C", [("fp32", 16, 16), ("fp32", 32, 32), ("fp32", 64, 64),
                                        ("bf16", 64, 32), ("bf16", 128, 32)])

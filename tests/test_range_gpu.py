@@ -26,7 +26,7 @@ def _gpu():
     gka.load()
 
 
-@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("D", [32, 64, 128])
 @pytest.mark.parametrize("sq,sk,sv", [
     (0, 0, -20), (0, 0, 17), (0, -12, 0), (0, 8, 0), (-12, 0, 0), (10, 0, 0), (-6, -12, 17),
 ])
