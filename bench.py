@@ -285,11 +285,23 @@ def bench_varlen(Wv, steps, warmup, ev):
 
 
 def backward_flops_per_token_head(D, r):
-    """Algorithmic flops of one token-head of the backward (gka_bwd), multiply-add = 2: forward
-    sweep -- H and U updates 6 D^2, ||H||^2 2 D^2, two Chebyshev solves 2 (r - 1) 2 D^2,
-    U^T do 2 D^2; reverse sweep -- the two gradient recurrences 8 D^2, dgamma 4 D^2, dk and dv
-    products 8 D^2."""
+    """Sequential-form flops of one token-head of the backward (gka_bwd), multiply-add = 2: the
+    recurrences' own per-token work -- H and U updates 6 D^2, ||H||^2 2 D^2, two Chebyshev
+    solves 2 (r - 1) 2 D^2, U^T do 2 D^2, the two gradient recurrences 8 D^2, dgamma 4 D^2, dk
+    and dv products 8 D^2."""
     return (6 + 2 + 4 * (r - 1) + 2 + 8 + 4 + 8) * D * D
+
+
+def backward_chunk_flops_per_token_head(D, C, r):
+    """Flops of one token-head of the matrix-core backward (bf16, chunks of C), multiply-add = 2,
+    from its products per chunk divided by C. D x D x C products: H0hat k, U0^T do, two solves
+    of r - 1 steps, H0 y, H0 k, the chunk gradient's three, the later chunks' three (Gn k, Wn k,
+    Wn^T v); C x C x D products: the Gram and V DO^T columns, the in-chunk terms of g and of the
+    two solves, the seven token-pair products and the four dk / dv products; C x C x C: the two
+    interaction sums of dgamma."""
+    dd = 2 + 2 + 4 * (r - 1) + 4 + 6 + 6
+    cc = 2 + 4 + 8 * (r - 1) + 14 + 8
+    return dd * D * D + cc * C * D + 4 * C * C
 
 
 def bench_backward(W, inputs, steps, warmup, ev):
@@ -317,13 +329,19 @@ def bench_backward(W, inputs, steps, warmup, ev):
     ev.sync(t1)
     ms = ev.elapsed_ms(t0, t1) / steps
     ev.destroy([t0, t1])
-    F = backward_flops_per_token_head(W.D, W.iters) * W.B * W.T * W.H
+    n = W.B * W.T * W.H
+    F = backward_chunk_flops_per_token_head(W.D, W.chunk, W.iters) * n
+    Fs = backward_flops_per_token_head(W.D, W.iters) * n
     return {"entry_point": "gka_bwd", "workload": W.name, "ms_per_step": ms,
             "tokens_per_s": W.B * W.T / (ms * 1e-3),
-            "roofline": {"bound": "alu", "kernel": "bwd_forward_kernel + bwd_reverse_kernel",
-                         "achieved": F / (ms * 1e-3) / 1e12, "peak": PEAK_FP32_VALU / 1e12,
-                         "unit": "TFLOP/s", "frac": F / (ms * 1e-3) / PEAK_FP32_VALU,
+            "roofline": {"bound": "mfma", "scope": "the whole backward call",
+                         "kernel": "bwd_solve_kernel + bwd_grad_kernel (with the forward's "
+                                   "summaries and the two segment scans)",
+                         "achieved": F / (ms * 1e-3) / 1e12, "peak": PEAK_BF16_MFMA / 1e12,
+                         "unit": "TFLOP/s", "frac": F / (ms * 1e-3) / PEAK_BF16_MFMA,
                          "traffic": None, "flops_per_launch": F, "avg_launch_ms": ms},
+            "sequential_form": {"flops_per_token_head": backward_flops_per_token_head(W.D, W.iters),
+                                "frac": Fs / (ms * 1e-3) / PEAK_BF16_MFMA},
             "workspace_bytes": need}
 
 
@@ -569,7 +587,7 @@ def main():
             log(f"prefill C={C}: {pc['ms_per_step']:.3f} ms/step (walk {pc['walk_ms']:.3f})")
             del pc
     if not args.no_bwd:
-        rec["backward"] = bench_backward(W, inputs, max(1, args.steps // 10), 1, ev)
+        rec["backward"] = bench_backward(W, inputs, max(2, args.steps // 2), 2, ev)
         log(f"backward: {rec['backward']['ms_per_step']:.2f} ms/step")
         torch.cuda.empty_cache()
     if not args.no_resid:

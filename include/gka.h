@@ -250,12 +250,21 @@ gka_status gka_fwd_varlen(const gka_params* p, const int32_t* cu_seqlens, int64_
  *   q, k, v, dout  [B, T, H, D] dtype, read; gamma, optional beta (NULL = 1) [B, T, H] float32
  *   dq, dk, dv     [B, T, H, D] dtype, written; dgamma [B, T, H] float32, written; dbeta
  *                  optional [B, T, H] float32 (the gradient at the given beta, or at beta = 1)
- *   workspace      at least gka_bwd_workspace_bytes(p) bytes, about 4 B T H (2 D^2 + 2 D + 1)
- *                  plus two chunk states per chunk and head: the forward sweep keeps every H_t
- *                  and U_t there
- * Chunks of 64 tokens (16 for float32 with D = 128) are swept in parallel, token by token, with
- * the forward's segment scan giving their starting states and a reverse scan their incoming
- * gradients.
+ *   workspace      at least gka_bwd_workspace_bytes(p) bytes: two D x D float32 pairs per chunk
+ *                  of 64 tokens and head (the chunk's start state and incoming gradient), plus
+ *                  per token 4 (3 D + 4) bytes for bf16 with D = 32, 64, 128, or 4 (2 D^2 + 2 D
+ *                  + 1) bytes (every H_t and U_t) otherwise
+ * Two paths, both from the forward's segment summaries and scan with one chunk per segment (every
+ * chunk's start state) and the same scan over the chunks in reverse order (every chunk's incoming
+ * gradient):
+ *   bf16 with D = 32, 64, 128: the chunk form on the matrix cores (chunks of 64). Per chunk, the
+ *     two Chebyshev solves (x for q, y for U^T do) on the forward walk's scheme, then every
+ *     gradient from C x C token-pair products with the decay mask and the dense interaction mask
+ *     M diag(c Gam^2) M^T (ai.info summary, "Main Findings", the backward's full interaction
+ *     mask). fp16 operands with exact power-of-two scales and float32 accumulation, as the
+ *     forward: every gradient within the forward's bf16 tolerance.
+ *   float32, and bf16 with D = 16: chunks of 64 tokens (16 for float32 with D = 128) swept in
+ *     parallel, token by token, in float32 on the vector units.
  * Errors as for gka_fwd_chunked; outputs must not overlap the inputs or each other
  * (GKA_ERR_ALIAS). T = 0 is a no-op.
  */

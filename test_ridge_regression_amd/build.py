@@ -17,7 +17,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libgka.so")
 SOURCES = ["gka_api.cpp", "gka_step.hip", "gka_fwd.hip", "gka_walk_tok.hip", "gka_summary.hip",
-           "gka_bwd.hip", "gka_noalloc.hip"]
+           "gka_bwd.hip", "gka_bwd_tok.hip", "gka_noalloc.hip"]
 
 HIPCC = os.environ.get("HIPCC", shutil.which("hipcc") or "/opt/rocm/bin/hipcc")
 FLAGS = [
@@ -28,11 +28,12 @@ FLAGS = [
 ]
 
 
-# Per-source flags. The token-owning walk keeps matrix-core results in vector registers (its
+# Per-source flags. The token-owning kernels (the walk, the summaries, the backward) keep matrix-core results in vector registers (its
 # products feed vector arithmetic directly); its resident operands are placed in the accumulator
 # registers by the kernel itself.
 EXTRA = {"gka_walk_tok.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
-         "gka_summary.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
+         "gka_summary.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
+         "gka_bwd_tok.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"]}
 
 
 def _compile(src: str, verbose: bool) -> str:

@@ -202,8 +202,23 @@ gka_status check_fwd(const gka_params* p) {
 // segment; workspace regions in floats, each rounded up to 64 floats (256 bytes).
 int bwd_chunk(const gka_params* p) { return p->dtype == GKA_FP32 && p->D == 128 ? 16 : 64; }
 
+FwdPlan bwd_plan(const gka_params* p) {
+  FwdPlan pl{};
+  pl.B = p->B;
+  pl.T = p->T;
+  pl.H = p->H;
+  pl.D = p->D;
+  pl.C = bwd_chunk(p);
+  pl.dtype = p->dtype;
+  pl.N = (p->T + pl.C - 1) / pl.C;
+  pl.S = pl.N;
+  pl.J = 1;
+  return pl;
+}
+
 struct BwdLayoutHost {
-  size_t snap, xs, ys, cs, fstates, flog2, fn2, rstates, rlog2, rn2, total;  // float offsets; bytes
+  bool tok;  // the matrix-core path: no snapshots, per-token results of the solve kernel
+  size_t snap, xs, ys, cs, dkh, tokv, fstates, flog2, fn2, rstates, rlog2, rn2, total;
 };
 
 BwdLayoutHost bwd_layout(const gka_params* p) {
@@ -211,11 +226,20 @@ BwdLayoutHost bwd_layout(const gka_params* p) {
   const size_t n = (size_t)p->B * p->H * p->T, D = (size_t)p->D, bh = (size_t)p->B * p->H;
   const size_t N = (size_t)((p->T + bwd_chunk(p) - 1) / bwd_chunk(p));
   BwdLayoutHost l{};
+  l.tok = gka::bwd_tok_supported(bwd_plan(p));
   size_t o = 0;
-  l.snap = o; o += up(n * 2 * D * D);
+  if (!l.tok) {
+    l.snap = o;
+    o += up(n * 2 * D * D);
+  }
   l.xs = o; o += up(n * D);
   l.ys = o; o += up(n * D);
-  l.cs = o; o += up(n);
+  if (l.tok) {
+    l.dkh = o; o += up(n * D);
+    l.tokv = o; o += up(n * 4);
+  } else {
+    l.cs = o; o += up(n);
+  }
   l.fstates = o; o += up(bh * N * 2 * D * D);
   l.flog2 = o; o += up(bh * N);
   l.fn2 = o; o += up(bh);
@@ -499,16 +523,7 @@ gka_status gka_bwd(const gka_params* p, const void* q, const void* k, const void
   hipStream_t s = static_cast<hipStream_t>(stream);
   float* ws = static_cast<float*>(workspace);
   // the plan of one chunk per segment
-  FwdPlan pl{};
-  pl.B = p->B;
-  pl.T = p->T;
-  pl.H = p->H;
-  pl.D = p->D;
-  pl.C = bwd_chunk(p);
-  pl.dtype = p->dtype;
-  pl.N = (p->T + pl.C - 1) / pl.C;
-  pl.S = pl.N;
-  pl.J = 1;
+  const FwdPlan pl = bwd_plan(p);
   const long long DD = (long long)p->D * p->D;
   // every chunk's starting state from the zero state: the forward's summaries and scan
   if (pl.S > 1) {
@@ -540,15 +555,21 @@ gka_status gka_bwd(const gka_params* p, const void* q, const void* k, const void
   ba.dv = dv;
   ba.dgamma = dgamma;
   ba.dbeta = dbeta;
-  ba.snap = ws + lay.snap;
   ba.xs = ws + lay.xs;
   ba.ys = ws + lay.ys;
-  ba.cs = ws + lay.cs;
   ba.fstates = ws + lay.fstates;
   ba.rstates = ws + lay.rstates;
   ba.rlog2 = ws + lay.rlog2;
   ba.rn2 = ws + lay.rn2;
-  if (gka::launch_bwd(pl, ba, cc, s) != hipSuccess) return GKA_ERR_HIP;
+  if (lay.tok) {
+    ba.dkh = ws + lay.dkh;
+    ba.tokv = ws + lay.tokv;
+    if (gka::launch_bwd_tok(pl, ba, cc, s) != hipSuccess) return GKA_ERR_HIP;
+  } else {
+    ba.snap = ws + lay.snap;
+    ba.cs = ws + lay.cs;
+    if (gka::launch_bwd(pl, ba, cc, s) != hipSuccess) return GKA_ERR_HIP;
+  }
   return GKA_OK;
 }
 

@@ -130,9 +130,11 @@ hipError_t launch_scan(const FwdPlan& pl, float* ws_states, const float* ws_log2
 // looked up on the first call there and kept.
 hipError_t static_scratch(void** out);
 
-// Backward pass (gka_bwd): arguments of its kernels. Workspace: snap [BH][T][2][D][D] (H_t, U_t
-// after every token), xs, ys [BH][T][D] (the solves of the forward sweep), cs [BH][T], and the
-// chunk states of the two scans.
+// Backward pass (gka_bwd): arguments of its kernels. Workspace of the vector sweeps: snap
+// [BH][T][2][D][D] (H_t, U_t after every token), xs, ys [BH][T][D] (the solves of the forward
+// sweep), cs [BH][T], and the chunk states of the two scans. The matrix-core path (bf16, chunks
+// of 64) has no snapshots: xs, ys, dkh [BH][T][D] and tokv [BH][T][4] carry the solve kernel's
+// per-token results to the gradient kernel.
 struct BwdArgs {
   const void* q;
   const void* k;
@@ -149,6 +151,8 @@ struct BwdArgs {
   float* xs;
   float* ys;
   float* cs;
+  float* dkh;   // [BH][T][D] 2 Gam_t E_t H0 k_t (matrix-core path)
+  float* tokv;  // [BH][T][4] (c_t, sigma_t, k_t^T H0 k_t, -) (matrix-core path)
   const float* fstates;  // [BH][N][2][D][D] every chunk's starting H and U (forward scan)
   float* rstates;        // [BH][N][2][D][D] chunk gradients (Gb, Wb), slot N - 1 - chunk
   float* rlog2;          // [BH][N] log2 of each chunk's gate product P_c, same slots
@@ -158,5 +162,11 @@ struct BwdArgs {
 // Backward of a dense batch; pl: the plan of one chunk per segment (S = N, J = 1).
 hipError_t launch_bwd(const FwdPlan& pl, const BwdArgs& a, const ChebConsts& cc,
                       hipStream_t stream);
+
+// The backward on the matrix cores (bf16, chunks of 64, D = 32, 64, 128): the solve kernel, the
+// reverse scan and the gradient kernel, after the forward's scan has filled fstates.
+bool bwd_tok_supported(const FwdPlan& pl);
+hipError_t launch_bwd_tok(const FwdPlan& pl, const BwdArgs& a, const ChebConsts& cc,
+                          hipStream_t stream);
 
 }  // namespace gka

@@ -1,0 +1,67 @@
+// Layout helpers of the token-owning kernels (the fused chunk walk and the backward pass):
+// permuted feature columns, transposing fragment reads, register-class hints, compile-time
+// loops. The reduction index of a product is taken in a permuted order within each block of
+// 32: k-slot j of lane group g stands for index 16 (j / 4) + 4 g + j % 4, so that the
+// accumulator rows of two 16x16 output tiles, as a lane holds them, are the B operand fragment
+// of the next product.
+#pragma once
+
+#include <type_traits>
+
+#include "gka_common.hpp"
+
+namespace gka {
+
+// column of logical feature d in a permuted row: within each block of 32, the four-element
+// group 4g + 16h (g = 0..3, h = 0, 1) sits at 8g + 4h
+__device__ constexpr int pcol(int d) {
+  return (d & ~31) + 8 * ((d >> 2) & 3) + 4 * ((d >> 4) & 1) + (d & 3);
+}
+
+// Operand fragment of M^T for a token-major matrix M[s][*] in LDS (row stride LDD): rows
+// (output index) col0 + lr, where the four columns col0 + 4q .. + 3 of a row start at element
+// off(q) of that row; the eight k-slots of lane group lg are tokens s0 + m (first read) and
+// s1 + m (second read), m = 0..3. Two transposing 8-byte reads (ds_read_b64_tr_b16): within a
+// group of 16 lanes, lane i receives element i % 4 of the chunks addressed by lanes i / 4 + 4m,
+// so lane q addresses row s + q / 4 at the four columns of lane group q % 4.
+template <int LDD>
+__device__ inline f16x8 frag_trans(const f16* base, int s0, int s1, int coff, int lr) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(3))) fp16x4_t lds_fp16x4;
+  const int r = lr >> 2;
+  const fp16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)(base + (s0 + r) * LDD + coff));
+  const fp16x4_t y = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)(base + (s1 + r) * LDD + coff));
+  return f16x8{(f16)x[0], (f16)x[1], (f16)x[2], (f16)x[3],
+               (f16)y[0], (f16)y[1], (f16)y[2], (f16)y[3]};
+#else
+  return f16x8{};
+#endif
+}
+
+// Register-class hints for values that only matrix-core instructions read between chunk
+// boundaries: the resident operand fragments and the float32 state live in the accumulator
+// registers (AGPRs), leaving the vector registers to the iterate and the products. An empty
+// asm statement with an AGPR operand makes the allocator keep the value there.
+template <typename V>
+__device__ inline void keep_in_agpr(V& x) {
+  asm volatile("" : "+a"(x));
+}
+
+__device__ inline f16x8 pack8(f32x4 a, f32x4 b) {
+  return f16x8{(f16)a[0], (f16)a[1], (f16)a[2], (f16)a[3], (f16)b[0], (f16)b[1], (f16)b[2],
+               (f16)b[3]};
+}
+
+template <int I>
+using IC = std::integral_constant<int, I>;
+
+// f(IC<I>), ..., f(IC<N - 1>): a loop whose index is a compile-time constant in the body
+template <int I, int N, typename F>
+__device__ inline void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(IC<I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+}  // namespace gka
