@@ -252,11 +252,12 @@ gka_status gka_fwd_varlen(const gka_params* p, const int32_t* cu_seqlens, int64_
  *                  optional [B, T, H] float32 (the gradient at the given beta, or at beta = 1)
  *   workspace      at least gka_bwd_workspace_bytes(p) bytes: two D x D float32 pairs per chunk
  *                  of 64 tokens and head (the chunk's start state and incoming gradient), plus
- *                  per token 4 (3 D + 4) bytes for bf16 with D = 32, 64, 128, or 4 (2 D^2 + 2 D
- *                  + 1) bytes (every H_t and U_t) otherwise
- * Two paths, both from the forward's segment summaries and scan with one chunk per segment (every
- * chunk's start state) and the same scan over the chunks in reverse order (every chunk's incoming
- * gradient):
+ *                  per token 4 (3 D + 4) bytes and one D x D pair per segment of the forward's
+ *                  plan for bf16 with D = 32, 64, 128, or 4 (2 D^2 + 2 D + 1) bytes per token
+ *                  (every H_t and U_t) otherwise
+ * Two paths. Every chunk's start state comes from the forward's segment summaries and scan (then,
+ * on the matrix-core path, a walk over each segment's chunks), every chunk's incoming gradient
+ * from the same scan run over the chunks in reverse order:
  *   bf16 with D = 32, 64, 128: the chunk form on the matrix cores (chunks of 64). Per chunk, the
  *     two Chebyshev solves (x for q, y for U^T do) on the forward walk's scheme, then every
  *     gradient from C x C token-pair products with the decay mask and the dense interaction mask

@@ -216,9 +216,22 @@ FwdPlan bwd_plan(const gka_params* p) {
   return pl;
 }
 
+// The matrix-core path's segment plan for the chunk-state walk: the forward's plan of the same
+// shape with chunks of 64.
+FwdPlan bwd_seg_plan(const gka_params* p) {
+  gka_params q = *p;
+  q.chunk = 64;
+  q.segments = 0;
+  FwdPlan ps{};
+  make_plan(&q, ps);
+  return ps;
+}
+
 struct BwdLayoutHost {
   bool tok;  // the matrix-core path: no snapshots, per-token results of the solve kernel
-  size_t snap, xs, ys, cs, dkh, tokv, fstates, flog2, fn2, rstates, rlog2, rn2, total;
+  size_t snap, xs, ys, cs, dkh, tokv, fstates, flog2, fn2, rstates, rlog2, rn2;
+  size_t sstates, slog2, sn2;  // matrix-core path: the segment summaries and start states
+  size_t total;
 };
 
 BwdLayoutHost bwd_layout(const gka_params* p) {
@@ -237,6 +250,10 @@ BwdLayoutHost bwd_layout(const gka_params* p) {
   if (l.tok) {
     l.dkh = o; o += up(n * D);
     l.tokv = o; o += up(n * 4);
+    const size_t S = (size_t)bwd_seg_plan(p).S;
+    l.sstates = o; o += up(bh * S * 2 * D * D);
+    l.slog2 = o; o += up(bh * S);
+    l.sn2 = o; o += up(bh);
   } else {
     l.cs = o; o += up(n);
   }
@@ -525,8 +542,36 @@ gka_status gka_bwd(const gka_params* p, const void* q, const void* k, const void
   // the plan of one chunk per segment
   const FwdPlan pl = bwd_plan(p);
   const long long DD = (long long)p->D * p->D;
-  // every chunk's starting state from the zero state: the forward's summaries and scan
-  if (pl.S > 1) {
+  // every chunk's starting state from the zero state. Matrix-core path: the forward's segment
+  // summaries and scan, then a walk over each segment's chunks. Vector sweeps: the summaries and
+  // scan with one chunk per segment.
+  if (lay.tok) {
+    const FwdPlan ps = bwd_seg_plan(p);
+    if (ps.S > 1) {
+      gka::WalkArgs sa{};
+      sa.q = q;
+      sa.k = k;
+      sa.v = v;
+      sa.gamma = gamma;
+      sa.beta = beta;
+      sa.sum_h = ws + lay.sstates;
+      sa.sum_u = ws + lay.sstates + DD;
+      sa.sum_bh = (long long)ps.S * 2 * DD;
+      sa.sum_seg = 2 * DD;
+      sa.log2g_out = ws + lay.slog2;
+      if (gka::launch_walk(ps, true, sa, cc, s) != hipSuccess) return GKA_ERR_HIP;
+    }
+    if (gka::launch_scan(ps, ws + lay.sstates, ws + lay.slog2, nullptr, nullptr, nullptr,
+                         ws + lay.sn2, nullptr, s) != hipSuccess)
+      return GKA_ERR_HIP;
+    gka::BwdArgs sb{};
+    sb.k = k;
+    sb.v = v;
+    sb.gamma = gamma;
+    sb.beta = beta;
+    sb.fstates = ws + lay.fstates;
+    if (gka::launch_bwd_states(ps, sb, ws + lay.sstates, s) != hipSuccess) return GKA_ERR_HIP;
+  } else if (pl.S > 1) {
     gka::WalkArgs sa{};
     sa.q = q;
     sa.k = k;
@@ -540,8 +585,8 @@ gka_status gka_bwd(const gka_params* p, const void* q, const void* k, const void
     sa.log2g_out = ws + lay.flog2;
     if (gka::launch_walk(pl, true, sa, cc, s) != hipSuccess) return GKA_ERR_HIP;
   }
-  if (gka::launch_scan(pl, ws + lay.fstates, ws + lay.flog2, nullptr, nullptr, nullptr,
-                       ws + lay.fn2, nullptr, s) != hipSuccess)
+  if (!lay.tok && gka::launch_scan(pl, ws + lay.fstates, ws + lay.flog2, nullptr, nullptr,
+                                   nullptr, ws + lay.fn2, nullptr, s) != hipSuccess)
     return GKA_ERR_HIP;
   gka::BwdArgs ba{};
   ba.q = q;

@@ -578,13 +578,6 @@ void bwd_solve_kernel(BwdArgs A, int Tlen, int Hn, int N, ChebConsts cc) {
   refresh();
 #pragma unroll
   for (int ft = 0; ft < FT; ++ft) xv[ft] = Xs[(ft * NW + wave) * kWave + lane];
-  // the start state's values at the wave's dG tiles (read here, used at the end)
-  f32x4 h0t[Cfg::TPW];
-#pragma unroll
-  for (int q = 0; q < Cfg::TPW; ++q) {
-    const int tile = wave * Cfg::TPW + q, a = tile / FT, bq = tile % FT;
-    h0t[q] = *reinterpret_cast<const f32x4*>(H0g + (size_t)(16 * bq + lr) * D + 16 * a + 4 * lg);
-  }
   float xy = 0.0f, ymax = 0.0f, gxmax = 0.0f;
 #pragma unroll
   for (int ft = 0; ft < FT; ++ft) {
@@ -650,6 +643,15 @@ void bwd_solve_kernel(BwdArgs A, int Tlen, int Hn, int N, ChebConsts cc) {
   const float hh_t = lane_read(ha * n0sq + hb, t);
   const float sig_t = -yHx + c_t * hh_t + sigU;
 
+  // the start state's values at the wave's dG tiles (read here, used at the end)
+  const int wave_u = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);
+  f32x4 h0t[Cfg::TPW];
+#pragma unroll
+  for (int q = 0; q < Cfg::TPW; ++q) {
+    const int tile = wave_u * Cfg::TPW + q, a = tile / FT, bq = tile % FT;
+    h0t[q] = *reinterpret_cast<const f32x4*>(H0g + (size_t)(16 * bq + lr) * D + 16 * a + 4 * lg);
+  }
+
   // ---- outputs of the token: dq = y, the workspaces x (written above), y, 2 Gam E H0 k, and
   // (c, sigma, k^T H0 k) ------------------------------------------------------------------------
   {
@@ -698,41 +700,48 @@ void bwd_solve_kernel(BwdArgs A, int Tlen, int Hn, int N, ChebConsts cc) {
   if (tid == 0) A.rlog2[(size_t)bh * N + (N - 1 - ch)] = cl_last;
   const float hsc0 = fast_exp2(2.0f * cl_first) * E_0;
   const float sxy = -pow2f(xe2 + ye2), sw = pow2f(2 * ke + we), sxd = pow2f(xe2 + de);
+  // (one instance per wave: the tile indices, and with them the resident K^T fragments of the
+  // tile's rows and columns, are compile-time constants)
+  auto dg_tiles = [&](auto W) {
+    constexpr int w = decltype(W)::value;
+    static_for<0, Cfg::TPW>([&](auto Q) {
+      constexpr int q = decltype(Q)::value, tile = w * Cfg::TPW + q;
+      constexpr int a = tile / FT, bq = tile % FT;
+      f32x4 acc1 = {0.f, 0.f, 0.f, 0.f}, acc2 = acc1, acc3 = acc1;
 #pragma unroll
-  for (int q = 0; q < Cfg::TPW; ++q) {
-    const int tile = wave * Cfg::TPW + q, a = tile / FT, bq = tile % FT;
-    f32x4 acc1 = {0.f, 0.f, 0.f, 0.f}, acc2 = acc1, acc3 = acc1;
+      for (int kc = 0; kc < KC; ++kc) {
+        const int s0 = 32 * kc + 4 * lg, s1 = s0 + 16;
+        const int ca = pcol(16 * a + 4 * (lr & 3)), cb = pcol(16 * bq + 4 * (lr & 3));
+        const Frag xa = frag_trans<LDD>(Vp, s0, s1, ca, lr);
+        const Frag yb = frag_trans<LDD>(Kp, s0, s1, cb, lr);
+        const Frag ya = frag_trans<LDD>(Kp, s0, s1, ca, lr);
+        const Frag xb = frag_trans<LDD>(Vp, s0, s1, cb, lr);
+        const Frag dbf = frag_trans<LDD>(Dp, s0, s1, cb, lr);
+        // (w K)^T over the permuted tokens of ktr, and K as B
+        const f32x4 w0 = *reinterpret_cast<const f32x4*>(v_w + s0);
+        const f32x4 w1 = *reinterpret_cast<const f32x4*>(v_w + s1);
+        const Frag ka = ktr[kc][a];
+        Frag wa;
 #pragma unroll
-    for (int kc = 0; kc < KC; ++kc) {
-      const int s0 = 32 * kc + 4 * lg, s1 = s0 + 16;
-      const int ca = pcol(16 * a + 4 * (lr & 3)), cb = pcol(16 * bq + 4 * (lr & 3));
-      const Frag xa = frag_trans<LDD>(Vp, s0, s1, ca, lr);
-      const Frag yb = frag_trans<LDD>(Kp, s0, s1, cb, lr);
-      const Frag ya = frag_trans<LDD>(Kp, s0, s1, ca, lr);
-      const Frag xb = frag_trans<LDD>(Vp, s0, s1, cb, lr);
-      const Frag dbf = frag_trans<LDD>(Dp, s0, s1, cb, lr);
-      // (w K)^T over the permuted tokens of ktr, and K as B
-      const f32x4 w0 = *reinterpret_cast<const f32x4*>(v_w + s0);
-      const f32x4 w1 = *reinterpret_cast<const f32x4*>(v_w + s1);
-      Frag ka, kbq;
-#pragma unroll
-      for (int ft = 0; ft < FT; ++ft) {
-        if (ft == a) ka = ktr[kc][ft];
-        if (ft == bq) kbq = ktr[kc][ft];
+        for (int j = 0; j < 8; ++j) wa[j] = (f16)((float)ka[j] * (j < 4 ? w0[j] : w1[j - 4]));
+        acc1 = M::mma(xa, yb, acc1);
+        acc1 = M::mma(ya, xb, acc1);
+        acc2 = M::mma(wa, ktr[kc][bq], acc2);
+        acc3 = M::mma(xa, dbf, acc3);
       }
-      Frag wa;
-#pragma unroll
-      for (int j = 0; j < 8; ++j) wa[j] = (f16)((float)ka[j] * (j < 4 ? w0[j] : w1[j - 4]));
-      acc1 = M::mma(xa, yb, acc1);
-      acc1 = M::mma(ya, xb, acc1);
-      acc2 = M::mma(wa, kbq, acc2);
-      acc3 = M::mma(xa, dbf, acc3);
-    }
-    // lane: element [16a + 4lg + i][16bq + lr] of the products, stored at [16bq + lr][16a + 4lg
-    // + i]: the transpose for dW, the same matrix for the symmetric dG + dG^T (H0 symmetric)
-    const size_t o = (size_t)(16 * bq + lr) * D + 16 * a + 4 * lg;
-    *reinterpret_cast<f32x4*>(rs + o) = acc1 * sxy + acc2 * (2.0f * sw) + h0t[q] * (2.0f * hsc0);
-    *reinterpret_cast<f32x4*>(rs + D * D + o) = acc3 * sxd;
+      // lane: element [16a + 4lg + i][16bq + lr] of the products, stored at [16bq + lr][16a +
+      // 4lg + i]: the transpose for dW, the same matrix for the symmetric dG + dG^T (H0
+      // symmetric)
+      const size_t o = (size_t)(16 * bq + lr) * D + 16 * a + 4 * lg;
+      *reinterpret_cast<f32x4*>(rs + o) = acc1 * sxy + acc2 * (2.0f * sw) + h0t[q] * (2.0f * hsc0);
+      *reinterpret_cast<f32x4*>(rs + D * D + o) = acc3 * sxd;
+    });
+  };
+  switch (wave_u) {
+    case 0: dg_tiles(IC<0>{}); break;
+    case 1: dg_tiles(IC<1>{}); break;
+    case 2: dg_tiles(IC<2>{}); break;
+    default: dg_tiles(IC<3>{}); break;
   }
 }
 
@@ -1206,6 +1215,154 @@ void bwd_grad_kernel(BwdArgs A, int Tlen, int Hn, int N) {
   }
 }
 
+// ============================================================================================
+// Every chunk's start state: a walk over the chunks of each (segment, head) of the forward's
+// segment plan, from the segment's start state, writing the state at every chunk start. Per
+// chunk H <- Gam_C H + K^T diag(w) K and U^T <- Gam_C U^T + K^T diag(w) V, w_s = 2^(l_{C-1} -
+// l_s) beta_s, with (w K)^T split into fp16 hi + lo (float32-accurate products). Wave w holds
+// the float32 tiles q = w TPW .. of H and U^T in registers (tile (a, b): H[16a + 4lg + i][16b +
+// lr] in a lane; U^T likewise, so that the lane's four values are a row segment of U).
+// ============================================================================================
+template <int D>
+__global__ __launch_bounds__(256) void bwd_states_kernel(BwdArgs A, int Tlen, int Hn, int N,
+                                                         int J, const float* seg_states, int S) {
+  using Cfg = BwdCfg<D>;
+  using M = Mma<f16>;
+  typedef f16x8 Frag;
+  constexpr int C = Cfg::C, NW = Cfg::NW, NT = Cfg::NT, FT = Cfg::FT, KC = Cfg::KC;
+  constexpr int LDD = Cfg::LDD, NU = Cfg::NU, TPW = Cfg::TPW;
+  __shared__ __attribute__((aligned(16))) f16 Kp[C * LDD];
+  __shared__ __attribute__((aligned(16))) f16 Vp[C * LDD];
+  __shared__ __attribute__((aligned(16))) float v_w[C];
+  __shared__ float v_sc[2 * NW];
+
+  const int seg = blockIdx.x, bh = blockIdx.y;
+  const int b = bh / Hn, h = bh % Hn;
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const int lr = lane % 16, lg = lane / 16;
+  const int c_begin = seg * J, c_end = min(N, c_begin + J);
+  if (c_begin >= c_end) return;
+
+  f32x4 Ht[TPW], Ut[TPW];
+  {
+    const float* st = seg_states + ((size_t)bh * S + seg) * 2 * D * D;
+#pragma unroll
+    for (int q = 0; q < TPW; ++q) {
+      const int tile = wave * TPW + q, a = tile / FT, bq = tile % FT;
+      const size_t o = (size_t)(16 * bq + lr) * D + 16 * a + 4 * lg;
+      Ht[q] = *reinterpret_cast<const f32x4*>(st + o);          // H symmetric
+      Ut[q] = *reinterpret_cast<const f32x4*>(st + D * D + o);  // U[16bq + lr][16a + 4lg ..]
+    }
+  }
+  bf16x8 kin[NU / NT], vin[NU / NT];
+  float g_l = 1.0f, bt_l = 1.0f;  // as loaded: past the end of the sequence they read as 0
+  int nv_l = 0;                   // valid rows of the loaded chunk
+  auto load = [&](int c) {
+    const int t0 = c * C, nv = min(C, Tlen - t0);
+    const long long row0 = ((long long)b * Tlen + t0) * Hn * D + (long long)h * D;
+    const ChunkRows<D> rk(A.k, row0, nv, Hn), rv(A.v, row0, nv, Hn);
+#pragma unroll
+    for (int j = 0; j < NU / NT; ++j) {
+      kin[j] = rk.unit(tid + j * NT);
+      vin[j] = rv.unit(tid + j * NT);
+    }
+    const long long gb = ((long long)b * Tlen + t0) * Hn + h;
+    const uint32_t gvalid = (uint32_t)(nv - 1) * Hn * 4u + 4u;
+    // (the write gates are read from the gates when there are none: an unconditional load, so
+    // that the compiler counts the loads in flight exactly; rows past the end get gate 1 where
+    // the values are used, so that nothing waits for these loads here)
+    g_l = buffer_load4f(buffer_rsrc(A.gamma + gb, gvalid), (uint32_t)lane * Hn * 4u);
+    bt_l = buffer_load4f(buffer_rsrc((A.beta ? A.beta : A.gamma) + gb, gvalid),
+                         (uint32_t)lane * Hn * 4u);
+    nv_l = nv;
+  };
+  // the start state of chunk c, from the tiles
+  auto store_state = [&](int c) {
+    float* out = A.fstates + ((size_t)bh * N + c) * 2 * D * D;
+#pragma unroll
+    for (int q = 0; q < TPW; ++q) {
+      const int tile = wave * TPW + q, a = tile / FT, bq = tile % FT;
+      const size_t o = (size_t)(16 * bq + lr) * D + 16 * a + 4 * lg;
+      *reinterpret_cast<f32x4*>(out + o) = Ht[q];
+      *reinterpret_cast<f32x4*>(out + D * D + o) = Ut[q];
+    }
+  };
+  // Per chunk with a successor in the segment: stage the rows loaded before, issue the next
+  // chunk's loads, then the state stores (after the loads, so that waiting for the loads does not
+  // wait for the stores), then the products. The segment's last chunk only stores its start
+  // state (the next segment starts from the scan).
+  load(c_begin);
+  for (int c = c_begin; c + 1 < c_end; ++c) {
+    // scales of the chunk, gate prefix and carry weights
+    float mk = 0.0f, mv = 0.0f;
+#pragma unroll
+    for (int j = 0; j < NU / NT; ++j)
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        mk = fmaxf(mk, fabsf((float)kin[j][i]));
+        mv = fmaxf(mv, fabsf((float)vin[j][i]));
+      }
+    mk = wave_max(mk);
+    mv = wave_max(mv);
+    const bool valid = lane < nv_l;
+    const float gv = valid ? g_l : 1.0f, bv = valid && A.beta ? bt_l : 1.0f;
+    const float cl = scan_add<kWave>(log2_gate(gv));
+    const float clast = lane_value(cl, C - 1);
+    __syncthreads();  // the previous chunk's products have read Kp, Vp, v_w
+    if (lane == 0) {
+      v_sc[wave] = mk;
+      v_sc[NW + wave] = mv;
+    }
+    if (wave == 0) v_w[lane] = fast_exp2(fminf(clast - cl, 0.0f)) * bv;
+    __syncthreads();
+    float km = v_sc[0], vm = v_sc[NW];
+#pragma unroll
+    for (int w = 1; w < NW; ++w) {
+      km = fmaxf(km, v_sc[w]);
+      vm = fmaxf(vm, v_sc[NW + w]);
+    }
+    const int ke = pow2_exponent(km, 30), ve = pow2_exponent(vm, 60);
+#pragma unroll
+    for (int j = 0; j < NU / NT; ++j) {
+      stage_unit<D, LDD>(Kp, tid + j * NT, kin[j], exp2_int(-ke));
+      stage_unit<D, LDD>(Vp, tid + j * NT, vin[j], exp2_int(-ve));
+    }
+    lds_barrier();
+    load(c + 1);  // the next chunk's rows, in flight during the stores and products
+    store_state(c);
+    const float gC = fast_exp2(clast);
+    const float sh = exp2_int(2 * ke), su = exp2_int(ke + ve);
+#pragma unroll
+    for (int q = 0; q < TPW; ++q) {
+      const int tile = wave * TPW + q, a = tile / FT, bq = tile % FT;
+      f32x4 ah = {0.f, 0.f, 0.f, 0.f}, au = ah;
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const int s0 = 32 * kc + 4 * lg, s1 = s0 + 16;
+        const Frag ka = frag_trans<LDD>(Kp, s0, s1, pcol(16 * a + 4 * (lr & 3)), lr);
+        const Frag kbf = frag_trans<LDD>(Kp, s0, s1, pcol(16 * bq + 4 * (lr & 3)), lr);
+        const Frag vbf = frag_trans<LDD>(Vp, s0, s1, pcol(16 * bq + 4 * (lr & 3)), lr);
+        const f32x4 w0 = *reinterpret_cast<const f32x4*>(v_w + s0);
+        const f32x4 w1 = *reinterpret_cast<const f32x4*>(v_w + s1);
+        Frag hi, lo;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float x = (float)ka[j] * (j < 4 ? w0[j] : w1[j - 4]);
+          hi[j] = (f16)x;
+          lo[j] = (f16)(x - (float)hi[j]);
+        }
+        ah = M::mma(hi, kbf, ah);
+        ah = M::mma(lo, kbf, ah);
+        au = M::mma(hi, vbf, au);
+        au = M::mma(lo, vbf, au);
+      }
+      Ht[q] = Ht[q] * gC + ah * sh;
+      Ut[q] = Ut[q] * gC + au * su;
+    }
+  }
+  store_state(c_end - 1);
+}
+
 template <int D>
 hipError_t launch_bwd_tok_t(const FwdPlan& pl, const BwdArgs& a, const ChebConsts& cc,
                             hipStream_t stream) {
@@ -1231,6 +1388,27 @@ hipError_t launch_bwd_tok_t(const FwdPlan& pl, const BwdArgs& a, const ChebConst
 }
 
 }  // namespace
+
+hipError_t launch_bwd_states(const FwdPlan& ps, const BwdArgs& a, const float* seg_states,
+                             hipStream_t stream) {
+  const dim3 grid(ps.S, ps.B * ps.H);
+  const int N = ps.N;
+  switch (ps.D) {
+    case 32:
+      hipLaunchKernelGGL(bwd_states_kernel<32>, grid, dim3(256), 0, stream, a, ps.T, ps.H, N,
+                         ps.J, seg_states, ps.S);
+      return hipGetLastError();
+    case 64:
+      hipLaunchKernelGGL(bwd_states_kernel<64>, grid, dim3(256), 0, stream, a, ps.T, ps.H, N,
+                         ps.J, seg_states, ps.S);
+      return hipGetLastError();
+    case 128:
+      hipLaunchKernelGGL(bwd_states_kernel<128>, grid, dim3(256), 0, stream, a, ps.T, ps.H, N,
+                         ps.J, seg_states, ps.S);
+      return hipGetLastError();
+  }
+  return hipErrorInvalidValue;
+}
 
 bool bwd_tok_supported(const FwdPlan& pl) {
   const long long chunk_bytes = 64LL * pl.H * pl.D * 2;

@@ -153,7 +153,8 @@ struct BwdArgs {
   float* cs;
   float* dkh;   // [BH][T][D] 2 Gam_t E_t H0 k_t (matrix-core path)
   float* tokv;  // [BH][T][4] (c_t, sigma_t, k_t^T H0 k_t, -) (matrix-core path)
-  const float* fstates;  // [BH][N][2][D][D] every chunk's starting H and U (forward scan)
+  float* fstates;  // [BH][N][2][D][D] every chunk's starting H and U (forward scan or the
+                   // matrix-core path's state walk)
   float* rstates;        // [BH][N][2][D][D] chunk gradients (Gb, Wb), slot N - 1 - chunk
   float* rlog2;          // [BH][N] log2 of each chunk's gate product P_c, same slots
   float* rn2;            // [BH] scratch of the reverse scan
@@ -166,6 +167,11 @@ hipError_t launch_bwd(const FwdPlan& pl, const BwdArgs& a, const ChebConsts& cc,
 // The backward on the matrix cores (bf16, chunks of 64, D = 32, 64, 128): the solve kernel, the
 // reverse scan and the gradient kernel, after the forward's scan has filled fstates.
 bool bwd_tok_supported(const FwdPlan& pl);
+// Every chunk's start state into a.fstates [BH][N][2][D][D] for the matrix-core backward: a walk
+// over the chunks of each segment of the plan ps (chunks of 64) from seg_states [BH][S][2][D][D],
+// the segment scan's start states.
+hipError_t launch_bwd_states(const FwdPlan& ps, const BwdArgs& a, const float* seg_states,
+                             hipStream_t stream);
 hipError_t launch_bwd_tok(const FwdPlan& pl, const BwdArgs& a, const ChebConsts& cc,
                           hipStream_t stream);
 
