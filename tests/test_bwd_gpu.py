@@ -118,3 +118,37 @@ def test_backward_several_chunks_with_write_gate(dtype, D):
     log(f"backward several chunks {dtype} D={D}")
     got = run(q, k, v, g, do, 0.05, 10, dtype, beta=beta)
     check(got, ref, dtype, f"backward several chunks {dtype} D={D}", D)
+
+
+def test_backward_many_segments_long_sequence():
+    """B1 T2565 H1 D64 (bf16): 41 chunks in 14 segments of the forward's plan, so the chunk
+    states come from the segment scan and the walk over each segment's chunks; zero gates at a
+    segment boundary and inside a chunk, write gates."""
+    B, T, H, D = 1, 64 * 40 + 5, 1, 64
+    q, k, v, g = W.make_prefill(B, T, H, D, 3.0, 1.0, "bf16", seed=1140)
+    g[0, [192, 193, 700], 0] = 0.0
+    do = W.make_prefill(B, T, H, D, 0.0, 1.0, "bf16", seed=1141)[2]
+    beta = W.make_beta(B, T, H, 1142)
+    ref = gka_backward_ref(q, k, v, g, do, 0.05, 10, beta=beta)
+    log("backward B1 T2565 H1 D64, many segments")
+    got = run(q, k, v, g, do, 0.05, 10, "bf16", beta=beta)
+    check(got, ref, "bf16", "backward many segments", D)
+
+
+@pytest.mark.parametrize("D", [64, 128])
+@pytest.mark.parametrize("sq,sk,sv,sd", [
+    (0, 0, -20, 0), (0, 0, 17, 0), (0, -12, 0, 0), (0, 8, 0, 0), (-12, 0, 0, 0), (10, 0, 0, 0),
+    (0, 0, 0, -20), (0, 0, 0, 17), (-6, -12, 17, 5),
+])
+def test_backward_power_of_two_scaled_inputs(D, sq, sk, sv, sd):
+    """q, k, v and do scaled by exact powers of two across the bf16 range (the matrix-core
+    path's operands carry power-of-two scales): every gradient at the bar and the tripwires."""
+    B, T, H = 1, 3 * 64 + 17, 2
+    q, k, v, g = W.make_prefill(B, T, H, D, 3.0, 1.0, "bf16", seed=1150 + D)
+    do = W.make_prefill(B, T, H, D, 0.0, 1.0, "bf16", seed=1151 + D)[2]
+    q, k, v, do = q * 2.0 ** sq, k * 2.0 ** sk, v * 2.0 ** sv, do * 2.0 ** sd
+    ref = gka_backward_ref(q, k, v, g, do, 0.05, 10)
+    what = f"backward D={D} scales 2^({sq}, {sk}, {sv}, {sd})"
+    log(what)
+    got = run(q, k, v, g, do, 0.05, 10, "bf16")
+    check(got, ref, "bf16", what, D)
