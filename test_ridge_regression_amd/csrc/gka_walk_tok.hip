@@ -847,10 +847,10 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
       }
     }
 
-    // ---- output O^T = diag(s) U0hat X^T + V^T ((K X^T) o Mhat), X split into hi + lo -------
+    // ---- output O^T = diag(s) U0hat X^T + V^T ((K X^T) o Mhat) ------------------------------
     // (X is taken times 2^-xe, so that its largest element lies in [1, 2), and U0hat, K and V
     // are the staged, scaled operands: their powers of two are undone at the store)
-    // Instruction groups: (1) U0hat and K fragment reads, the split of X; (2) the K products
+    // Instruction groups: (1) U0hat and K fragment reads, X as fp16; (2) the K products
     // and the V^T fragment reads; (3) the U0hat products; (4) the V^T products and the stores.
     lds_barrier();  // U0hat is staged
     load_kv(ch + 1);
@@ -876,28 +876,20 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
       xm = fmaxf(xm, lane_read(xm, lane ^ 32));
       const int xe = pow2_exponent(xm, 100);
       const float xinv = exp2_int(-xe);
-      Frag vq[KC][FT], xh[KD], xl[KD], pf[KC];
+      // (one fp16 rounding of X: o is stored in bf16, whose rounding is 4x coarser; a lo part of
+      // X measured 1.8e-3 against 1.9e-3 relative error of o at B8 T2048 H8 D128 and cost 3.5%
+      // of the call)
+      Frag vq[KC][FT], xh[KD], pf[KC];
 #pragma unroll
-      for (int kk = 0; kk < KD; ++kk) {
-        const f32x4 x0 = X[2 * kk] * xinv, x1 = X[2 * kk + 1] * xinv;
-        xh[kk] = pack8(x0, x1);
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float x = j < 4 ? x0[j] : x1[j - 4];
-          xl[kk][j] = (f16)(x - (float)xh[kk][j]);
-        }
-      }
+      for (int kk = 0; kk < KD; ++kk) xh[kk] = pack8(X[2 * kk] * xinv, X[2 * kk + 1] * xinv);
       __builtin_amdgcn_sched_barrier(0);
       f32x4 pa[ST];
 #pragma unroll
       for (int sb = 0; sb < ST; ++sb) pa[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < KD; ++kk) {  // (hi and lo products not back to back)
+      for (int kk = 0; kk < KD; ++kk)
 #pragma unroll
         for (int sb = 0; sb < ST; ++sb) pa[sb] = M::mma(kres[kk][sb], xh[kk], pa[sb]);
-#pragma unroll
-        for (int sb = 0; sb < ST; ++sb) pa[sb] = M::mma(kres[kk][sb], xl[kk], pa[sb]);
-      }
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
@@ -907,12 +899,9 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
 #pragma unroll
       for (int ft = 0; ft < FT; ++ft) y[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int kk = 0; kk < KD; ++kk) {
+      for (int kk = 0; kk < KD; ++kk)
 #pragma unroll
         for (int ft = 0; ft < FT; ++ft) y[ft] = M::mma(Hres[ft][kk], xh[kk], y[ft]);
-#pragma unroll
-        for (int ft = 0; ft < FT; ++ft) y[ft] = M::mma(Hres[ft][kk], xl[kk], y[ft]);
-      }
       // (the loop's mask Mh carries 2^2ke, the K product 2^-ke: their product is the masked
       // K X^T times 2^ke)
 #pragma unroll
