@@ -130,7 +130,8 @@ def measured_traffic(kernel):
         rec = json.load(open(path))[kernel]
     except (OSError, KeyError, ValueError):
         return None
-    files = {"walk_tok_kernel": ("gka_walk_tok.hip", "gka_common.hpp", "gka_internal.hpp"),
+    files = {"walk_tok_kernel": ("gka_walk_tok.hip", "gka_tok.hpp", "gka_common.hpp",
+                                 "gka_internal.hpp"),
              "step_kernel": ("gka_step.hip", "gka_common.hpp", "gka_internal.hpp")}[kernel]
     h = hashlib.sha256()
     for f in files:
