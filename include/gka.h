@@ -250,11 +250,12 @@ gka_status gka_fwd_varlen(const gka_params* p, const int32_t* cu_seqlens, int64_
  *   q, k, v, dout  [B, T, H, D] dtype, read; gamma, optional beta (NULL = 1) [B, T, H] float32
  *   dq, dk, dv     [B, T, H, D] dtype, written; dgamma [B, T, H] float32, written; dbeta
  *                  optional [B, T, H] float32 (the gradient at the given beta, or at beta = 1)
- *   workspace      at least gka_bwd_workspace_bytes(p) bytes: two D x D float32 pairs per chunk
- *                  of 64 tokens and head (the chunk's start state and incoming gradient), plus
- *                  per token 4 (3 D + 4) bytes and one D x D pair per segment of the forward's
- *                  plan for bf16 with D = 32, 64, 128, or 4 (2 D^2 + 2 D + 1) bytes per token
- *                  (every H_t and U_t) otherwise
+ *   workspace      at least gka_bwd_workspace_bytes(p) bytes. bf16 with D = 32, 64, 128: per
+ *                  chunk of 64 tokens and head, the start state in fp16 (4 D^2 bytes) and the
+ *                  incoming gradient in float32 and fp16 (12 D^2 bytes); per token 4 (3 D + 4)
+ *                  bytes; one float32 D x D pair per segment of the forward's plan. Otherwise:
+ *                  two float32 D x D pairs per chunk and 4 (2 D^2 + 2 D + 1) bytes per token
+ *                  (every H_t and U_t)
  * Two paths. Every chunk's start state comes from the forward's segment summaries and scan (then,
  * on the matrix-core path, a walk over each segment's chunks), every chunk's incoming gradient
  * from the same scan run over the chunks in reverse order:

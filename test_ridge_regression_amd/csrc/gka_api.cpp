@@ -231,6 +231,8 @@ struct BwdLayoutHost {
   bool tok;  // the matrix-core path: no snapshots, per-token results of the solve kernel
   size_t snap, xs, ys, cs, dkh, tokv, fstates, flog2, fn2, rstates, rlog2, rn2;
   size_t sstates, slog2, sn2;  // matrix-core path: the segment summaries and start states
+  size_t rs16, rexp;           // matrix-core path: the reverse scan's fp16 outputs
+  size_t fs16, fexp;           // matrix-core path: every chunk's start state (fp16)
   size_t total;
 };
 
@@ -254,12 +256,19 @@ BwdLayoutHost bwd_layout(const gka_params* p) {
     l.sstates = o; o += up(bh * S * 2 * D * D);
     l.slog2 = o; o += up(bh * S);
     l.sn2 = o; o += up(bh);
+    l.rs16 = o; o += up(bh * N * D * D);  // (2 D^2 fp16 per slot)
+    l.rexp = o; o += up(bh * N * 2 * D);
   } else {
     l.cs = o; o += up(n);
   }
-  l.fstates = o; o += up(bh * N * 2 * D * D);
-  l.flog2 = o; o += up(bh * N);
-  l.fn2 = o; o += up(bh);
+  if (l.tok) {
+    l.fs16 = o; o += up(bh * N * D * D);  // (2 D^2 fp16 per chunk)
+    l.fexp = o; o += up(bh * N * 2);
+  } else {
+    l.fstates = o; o += up(bh * N * 2 * D * D);
+    l.flog2 = o; o += up(bh * N);
+    l.fn2 = o; o += up(bh);
+  }
   l.rstates = o; o += up(bh * N * 2 * D * D);
   l.rlog2 = o; o += up(bh * N);
   l.rn2 = o; o += up(bh);
@@ -569,7 +578,8 @@ gka_status gka_bwd(const gka_params* p, const void* q, const void* k, const void
     sb.v = v;
     sb.gamma = gamma;
     sb.beta = beta;
-    sb.fstates = ws + lay.fstates;
+    sb.fs16 = ws + lay.fs16;
+    sb.fexp = ws + lay.fexp;
     if (gka::launch_bwd_states(ps, sb, ws + lay.sstates, s) != hipSuccess) return GKA_ERR_HIP;
   } else if (pl.S > 1) {
     gka::WalkArgs sa{};
@@ -602,13 +612,17 @@ gka_status gka_bwd(const gka_params* p, const void* q, const void* k, const void
   ba.dbeta = dbeta;
   ba.xs = ws + lay.xs;
   ba.ys = ws + lay.ys;
-  ba.fstates = ws + lay.fstates;
+  ba.fstates = lay.tok ? nullptr : ws + lay.fstates;
+  ba.fs16 = lay.tok ? ws + lay.fs16 : nullptr;
+  ba.fexp = lay.tok ? ws + lay.fexp : nullptr;
   ba.rstates = ws + lay.rstates;
   ba.rlog2 = ws + lay.rlog2;
   ba.rn2 = ws + lay.rn2;
   if (lay.tok) {
     ba.dkh = ws + lay.dkh;
     ba.tokv = ws + lay.tokv;
+    ba.rs16 = ws + lay.rs16;
+    ba.rexp = ws + lay.rexp;
     if (gka::launch_bwd_tok(pl, ba, cc, s) != hipSuccess) return GKA_ERR_HIP;
   } else {
     ba.snap = ws + lay.snap;

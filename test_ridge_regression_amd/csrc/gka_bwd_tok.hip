@@ -216,14 +216,17 @@ void bwd_solve_kernel(BwdArgs A, int Tlen, int Hn, int N, ChebConsts cc) {
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) Qraw[ft] = buffer_load8<bf16x4>(rq, qoff + 32u * ft);
   }
-  const float* H0g = A.fstates + ((size_t)bh * N + ch) * 2 * D * D;
-  const float* U0g = H0g + D * D;
+  // the chunk's start state (fp16, each matrix times a power of two)
+  const size_t fslot = (size_t)bh * N + ch;
+  const f16* H0g = static_cast<const f16*>(A.fs16) + fslot * 2 * D * D;
+  const f16* U0g = H0g + D * D;
+  const float h0sc = pow2f((int)A.fexp[2 * fslot]), u0sc = pow2f((int)A.fexp[2 * fslot + 1]);
   f32x4 hreg[NH4], ureg[NH4];
   float sq = 0.0f, um = 0.0f;
 #pragma unroll
   for (int j = 0; j < NH4; ++j) {
-    hreg[j] = reinterpret_cast<const f32x4*>(H0g)[tid + j * NT];
-    ureg[j] = reinterpret_cast<const f32x4*>(U0g)[tid + j * NT];
+    hreg[j] = load4(H0g + 4 * (tid + j * NT)) * h0sc;
+    ureg[j] = load4(U0g + 4 * (tid + j * NT)) * u0sc;
     sq += dot4(hreg[j], hreg[j]);
     um = fmaxf(um, absmax4(ureg[j]));
   }
@@ -649,7 +652,7 @@ void bwd_solve_kernel(BwdArgs A, int Tlen, int Hn, int N, ChebConsts cc) {
 #pragma unroll
   for (int q = 0; q < Cfg::TPW; ++q) {
     const int tile = wave_u * Cfg::TPW + q, a = tile / FT, bq = tile % FT;
-    h0t[q] = *reinterpret_cast<const f32x4*>(H0g + (size_t)(16 * bq + lr) * D + 16 * a + 4 * lg);
+    h0t[q] = load4(H0g + (size_t)(16 * bq + lr) * D + 16 * a + 4 * lg) * h0sc;
   }
 
   // ---- outputs of the token: dq = y, the workspaces x (written above), y, 2 Gam E H0 k, and
@@ -824,21 +827,26 @@ void bwd_grad_kernel(BwdArgs A, int Tlen, int Hn, int N) {
   // (c, sigma, k^T H0 k) of token `lane` (zero past the end)
   const auto rt = buffer_rsrc(A.tokv + ((size_t)bh * Tlen + t0) * 4, (uint32_t)nv * 16u);
   const f32x4 tv = buffer_load16<f32x4>(rt, (uint32_t)lane * 16u);
-  // the later chunks' gradients (Gs = Gn + Gn^T and Wn: reverse-scan slot N - 1 - ch) and the
-  // start state
-  const float* Gsg = A.rstates + ((size_t)bh * N + (N - 1 - ch)) * 2 * D * D;
-  const float* Wn = Gsg + D * D;
-  const float* H0g = A.fstates + ((size_t)bh * N + ch) * 2 * D * D;
-  const float* U0g = H0g + D * D;
+  // the later chunks' gradients (Gs = Gn + Gn^T and Wn: reverse-scan slot N - 1 - ch, fp16 rows
+  // with an exponent each) and the start state
+  const size_t rslot = (size_t)bh * N + (N - 1 - ch);
+  const f16* Gs16 = static_cast<const f16*>(A.rs16) + rslot * 2 * D * D;
+  const f16* Wn16 = Gs16 + D * D;
+  const float* Gsx = A.rexp + rslot * 2 * D;
+  const float* Wnx = Gsx + D;
+  const size_t fslot = (size_t)bh * N + ch;
+  const f16* H0g = static_cast<const f16*>(A.fs16) + fslot * 2 * D * D;
+  const f16* U0g = H0g + D * D;
+  const float h0sc = pow2f((int)A.fexp[2 * fslot]), u0sc = pow2f((int)A.fexp[2 * fslot + 1]);
   f32x4 gs[NH4], wn[NH4];
   float sdot = 0.0f, wmx = 0.0f, gmx = 0.0f;  // sdot: <Gn, H0> + <Wn, U0>
 #pragma unroll
   for (int j = 0; j < NH4; ++j) {
-    const int e4 = tid + j * NT;
-    gs[j] = reinterpret_cast<const f32x4*>(Gsg)[e4];
-    wn[j] = reinterpret_cast<const f32x4*>(Wn)[e4];
-    sdot += 0.5f * dot4(gs[j], reinterpret_cast<const f32x4*>(H0g)[e4]) +
-            dot4(wn[j], reinterpret_cast<const f32x4*>(U0g)[e4]);
+    const int e4 = tid + j * NT, r = e4 / (D / 4);
+    gs[j] = load4(Gs16 + 4 * e4) * pow2f((int)Gsx[r]);
+    wn[j] = load4(Wn16 + 4 * e4) * pow2f((int)Wnx[r]);
+    sdot += 0.5f * h0sc * dot4(gs[j], load4(H0g + 4 * e4)) +
+            u0sc * dot4(wn[j], load4(U0g + 4 * e4));
     wmx = fmaxf(wmx, absmax4(wn[j]));
     gmx = fmaxf(gmx, absmax4(gs[j]));
   }
@@ -1216,6 +1224,48 @@ void bwd_grad_kernel(BwdArgs A, int Tlen, int Hn, int N) {
 }
 
 // ============================================================================================
+// The chunks' incoming gradients: the segment scan over the chunks in reverse order (slot N - 1 -
+// c holds chunk c's dG + dG^T and dW, float32; log2g its gate product), the running sum in
+// float32 per thread, each start state written as fp16 rows, row r times 2^-e_r (e_r from the
+// row's largest element, in oexp). Thread e4 holds elements 4 e4 .. 4 e4 + 3 of both matrices;
+// the D / 4 lanes of a row share its exponent.
+// ============================================================================================
+template <int D>
+__global__ __launch_bounds__(256) void bwd_rscan_kernel(const float* __restrict__ st,
+                                                        const float* __restrict__ log2g,
+                                                        f16* __restrict__ out,
+                                                        float* __restrict__ oexp, int N) {
+  constexpr int DD = D * D, G = D / 4;
+  static_assert((DD / 4) % 256 == 0 && kWave % G == 0, "rows within waves");
+  const int bh = blockIdx.y;
+  const int e4 = blockIdx.x * 256 + threadIdx.x;
+  const int lane = threadIdx.x % kWave, r = e4 / G;
+  f32x4 sh = {0.f, 0.f, 0.f, 0.f}, su = sh;
+  auto put = [&](f32x4 x, size_t slot, int mat) {
+    float m = absmax4(x);
+#pragma unroll
+    for (int k = 1; k < G; k <<= 1) m = fmaxf(m, lane_read(m, lane ^ k));
+    const int e = pow2_exponent(m, 126);
+    const f32x4 y = x * pow2f(-e);
+    *reinterpret_cast<f16x4*>(out + slot * 2 * DD + (size_t)mat * DD + 4 * e4) =
+        f16x4{(f16)y[0], (f16)y[1], (f16)y[2], (f16)y[3]};
+    if (lane % G == 0) oexp[slot * 2 * D + (size_t)mat * D + r] = (float)e;
+  };
+  for (int s = 0; s < N; ++s) {
+    const size_t slot = (size_t)bh * N + s;
+    put(sh, slot, 0);
+    put(su, slot, 1);
+    if (s + 1 < N) {  // the last slot has no summary
+      const f32x4 dh = reinterpret_cast<const f32x4*>(st + slot * 2 * DD)[e4];
+      const f32x4 du = reinterpret_cast<const f32x4*>(st + slot * 2 * DD + DD)[e4];
+      const float g = exp2f(log2g[slot]);
+      sh = g * sh + dh;
+      su = g * su + du;
+    }
+  }
+}
+
+// ============================================================================================
 // Every chunk's start state: a walk over the chunks of each (segment, head) of the forward's
 // segment plan, from the segment's start state, writing the state at every chunk start. Per
 // chunk H <- Gam_C H + K^T diag(w) K and U^T <- Gam_C U^T + K^T diag(w) V, w_s = 2^(l_{C-1} -
@@ -1235,6 +1285,7 @@ __global__ __launch_bounds__(256) void bwd_states_kernel(BwdArgs A, int Tlen, in
   __shared__ __attribute__((aligned(16))) f16 Vp[C * LDD];
   __shared__ __attribute__((aligned(16))) float v_w[C];
   __shared__ float v_sc[2 * NW];
+  __shared__ float v_sm[2 * NW];  // the state's maxima per wave
 
   const int seg = blockIdx.x, bh = blockIdx.y;
   const int b = bh / Hn, h = bh % Hn;
@@ -1276,15 +1327,43 @@ __global__ __launch_bounds__(256) void bwd_states_kernel(BwdArgs A, int Tlen, in
                          (uint32_t)lane * Hn * 4u);
     nv_l = nv;
   };
-  // the start state of chunk c, from the tiles
+  // the start state of chunk c, from the tiles: fp16, each matrix times 2^-e (e from its
+  // largest element, over the four waves)
   auto store_state = [&](int c) {
-    float* out = A.fstates + ((size_t)bh * N + c) * 2 * D * D;
+    float mh = 0.0f, mu = 0.0f;
+#pragma unroll
+    for (int q = 0; q < TPW; ++q) {
+      mh = fmaxf(mh, absmax4(Ht[q]));
+      mu = fmaxf(mu, absmax4(Ut[q]));
+    }
+    mh = wave_max(mh);
+    mu = wave_max(mu);
+    if (lane == 0) {
+      v_sm[wave] = mh;
+      v_sm[NW + wave] = mu;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int w = 0; w < NW; ++w) {
+      mh = fmaxf(mh, v_sm[w]);
+      mu = fmaxf(mu, v_sm[NW + w]);
+    }
+    __syncthreads();  // v_sm is read before the next state's maxima are written
+    const int eh = pow2_exponent(mh, 126), eu = pow2_exponent(mu, 126);
+    const float ih = pow2f(-eh), iu = pow2f(-eu);
+    const size_t slot = (size_t)bh * N + c;
+    f16* out = static_cast<f16*>(A.fs16) + slot * 2 * D * D;
 #pragma unroll
     for (int q = 0; q < TPW; ++q) {
       const int tile = wave * TPW + q, a = tile / FT, bq = tile % FT;
       const size_t o = (size_t)(16 * bq + lr) * D + 16 * a + 4 * lg;
-      *reinterpret_cast<f32x4*>(out + o) = Ht[q];
-      *reinterpret_cast<f32x4*>(out + D * D + o) = Ut[q];
+      const f32x4 x = Ht[q] * ih, y = Ut[q] * iu;
+      *reinterpret_cast<f16x4*>(out + o) = f16x4{(f16)x[0], (f16)x[1], (f16)x[2], (f16)x[3]};
+      *reinterpret_cast<f16x4*>(out + D * D + o) = f16x4{(f16)y[0], (f16)y[1], (f16)y[2], (f16)y[3]};
+    }
+    if (tid == 0) {
+      A.fexp[2 * slot] = (float)eh;
+      A.fexp[2 * slot + 1] = (float)eu;
     }
   };
   // Per chunk with a successor in the segment: stage the rows loaded before, issue the next
@@ -1375,9 +1454,9 @@ hipError_t launch_bwd_tok_t(const FwdPlan& pl, const BwdArgs& a, const ChebConst
   hipLaunchKernelGGL(ks, grid, dim3(Cfg::NT), Cfg::aBytes, stream, a, pl.T, pl.H, pl.N, cc);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // every chunk's incoming gradients: the segment scan over the chunks in reverse order
-  if ((e = launch_scan(pl, a.rstates, a.rlog2, nullptr, nullptr, nullptr, a.rn2, nullptr,
-                       stream)) != hipSuccess)
-    return e;
+  hipLaunchKernelGGL(bwd_rscan_kernel<D>, dim3(D * D / 4 / 256, pl.B * pl.H), dim3(256), 0,
+                     stream, a.rstates, a.rlog2, static_cast<f16*>(a.rs16), a.rexp, pl.N);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   auto kg = bwd_grad_kernel<D>;
   static std::atomic<uint64_t> lds_g{0};
   if ((e = ensure_dynamic_lds(reinterpret_cast<const void*>(kg), (int)Cfg::gBytes, lds_g)) !=

@@ -157,6 +157,10 @@ struct BwdArgs {
                    // matrix-core path's state walk)
   float* rstates;        // [BH][N][2][D][D] chunk gradients (Gb, Wb), slot N - 1 - chunk
   float* rlog2;          // [BH][N] log2 of each chunk's gate product P_c, same slots
+  void* rs16;            // matrix-core path: the scan's outputs, fp16 [BH][N][2][D][D], each
+  float* rexp;           // row times 2^-rexp[BH][N][2][D]
+  void* fs16;            // matrix-core path: every chunk's start state, fp16 [BH][N][2][D][D],
+  float* fexp;           // each matrix times 2^-fexp[BH][N][2]
   float* rn2;            // [BH] scratch of the reverse scan
 };
 

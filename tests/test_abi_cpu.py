@@ -275,9 +275,13 @@ def test_backward_entry_point_checks(lib):
     n, D, N = 64, 32, 1  # one chunk of 64 tokens
     scans = 2 * (up(N * 2 * D * D) + up(N) + up(1))  # the forward and the reverse scan
     # bf16 (chunks of 64, matrix cores): x, y, 2 Gam E H0 k per token and 4 scalars, the segment
-    # states of the chunk-state walk (one segment here); no snapshots
+    # states of the chunk-state walk (one segment here), every chunk's start state in fp16 with
+    # two exponents, the reverse scan (float32 inputs, fp16 outputs with row exponents); no
+    # snapshots
     seg = up(2 * D * D) + up(1) + up(1)
-    assert need == 4 * (3 * up(n * D) + up(n * 4) + seg + scans)
+    fs16 = up(N * D * D) + up(N * 2)
+    rscan = up(N * 2 * D * D) + up(N) + up(1) + up(N * D * D) + up(N * 2 * D)
+    assert need == 4 * (3 * up(n * D) + up(n * 4) + seg + fs16 + rscan)
     # float32 (vector sweeps): every H_t, U_t, then x, y, c
     need32 = lib.gka_bwd_workspace_bytes(P(params(B=1, H=1, T=64, D=32, dtype_code=gka.GKA_FP32)))
     assert need32 == 4 * (up(n * 2 * D * D) + 2 * up(n * D) + up(n) + scans)
