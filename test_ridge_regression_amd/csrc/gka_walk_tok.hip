@@ -37,8 +37,8 @@
 //
 // Per chunk: stage K, V (fp16), gates and H0hat; the norm phase (k_t^T H0hat k_t from the
 // resident H0hat fragments, the Gram tiles of the own tokens) and a scan over the 64 tokens;
-// U0hat is staged; the carry advances the float32 state (H as accumulator tiles in registers,
-// U^T in LDS); the Chebyshev loop; the output products. The next chunk's K, V and gates are
+// the carry advances the float32 state (H as accumulator tiles in registers, U^T in LDS) and
+// stages U0hat from the U^T tiles it reads; the Chebyshev loop; the output products. The next chunk's K, V and gates are
 // loaded into registers during the output phase and staged at the top of the next chunk.
 #include "gka_internal.hpp"
 #include "gka_tok.hpp"
@@ -336,19 +336,6 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
       }
     });
   };
-  // U^T tiles (times sc) -> Hs as fp16: row v of Hs holds U[v][*] (permuted columns); tile
-  // (a, b) holds U[16b + lr][16a + 4lg ..]
-  auto stage_u = [&](float sc) {
-    f32x4 x[NUTL];  // all reads first: one wait covers them
-#pragma unroll
-    for (int j = 0; j < NUTL; ++j) x[j] = *us_tile(j);
-    for_utiles([&](auto J, int a, int b, auto) {
-      constexpr int j = decltype(J)::value;
-      const f32x4 y = x[j] * sc;
-      *reinterpret_cast<f16x4*>(Hs + (16 * b + lr) * LDD + pcol(16 * a + 4 * lg)) =
-          f16x4{(f16)y[0], (f16)y[1], (f16)y[2], (f16)y[3]};
-    });
-  };
   // A fragment of K (rows = tokens 16 sb + lr) over feature block kk
   auto frag_k = [&](int sb, int kk) {
     return *reinterpret_cast<const Frag*>(Kp + (16 * sb + lr) * LDD + 32 * kk + 8 * lg);
@@ -579,8 +566,6 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
         }
       }
     }
-    // U0hat times 2^-ue (every wave has read its H0hat fragments)
-    stage_u(exp2_int(Eu - ue) * n0inv);
 
     // ---- queries of the own token, accumulator layout: Q[t][16 ft + 4 lg .. + 3], loaded
     // during the carry's products and consumed at the start of the loop ----------------------
@@ -648,7 +633,11 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
       // Gam_C U^T rescaled to the frame 2^(ke + ve) of the product; the largest |U| of the
       // wave's tiles to v_sc[8 + wave] for the next chunk's U0hat. Column by column: the V^T
       // fragments and U^T tiles of the next column are read while the current one's products
-      // run (double-buffered), and the rows of a column share them.
+      // run (double-buffered), and the rows of a column share them. The tiles as read are
+      // this chunk's U0: each is also staged to Hs as U0hat times 2^-ue (fp16; row v of Hs
+      // holds U[v][*], permuted columns), which the output reads after its barrier (every wave
+      // has read its H0hat fragments from Hs before the barrier ahead of the norm scan).
+      const float u0sc = exp2_int(Eu - ue) * n0inv;
       const float usc = gC * exp2_int(Eu - ke - ve);
       constexpr int NUR = TRI ? 2 : NRT, NUC = TRI ? FT : NCT;  // U row, column tiles per wave
       float um = 0.0f;
@@ -666,7 +655,13 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
         if (c + 1 < NUC) load_col(c + 1, (c + 1) % 2);
         f32x4 uacc[NUR];
 #pragma unroll
-        for (int r = 0; r < NUR; ++r) uacc[r] = ub[c % 2][r] * usc;
+        for (int r = 0; r < NUR; ++r) {
+          // U^T tile (urow(r), column b) holds U[16 b + lr][16 urow(r) + 4 lg ..]
+          const f32x4 y = ub[c % 2][r] * u0sc;
+          *reinterpret_cast<f16x4*>(Hs + (16 * (TRI ? c : b0 + c) + lr) * LDD + pcol(16 * urow(r) + 4 * lg)) =
+              f16x4{(f16)y[0], (f16)y[1], (f16)y[2], (f16)y[3]};
+          uacc[r] = ub[c % 2][r] * usc;
+        }
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc)
 #pragma unroll
