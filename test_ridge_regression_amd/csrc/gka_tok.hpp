@@ -38,6 +38,19 @@ __device__ inline f16x8 frag_trans(const f16* base, int s0, int s1, int coff, in
 #endif
 }
 
+// The first half of frag_trans: the k-slots of tokens s + m, m = 0..3, only (one transposing
+// read)
+template <int LDD>
+__device__ inline f16x4 frag_trans_half(const f16* base, int s, int coff, int lr) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  typedef __attribute__((address_space(3))) fp16x4_t lds_fp16x4;
+  const fp16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)(base + (s + (lr >> 2)) * LDD + coff));
+  return f16x4{(f16)x[0], (f16)x[1], (f16)x[2], (f16)x[3]};
+#else
+  return f16x4{};
+#endif
+}
+
 // Register-class hints for values that only matrix-core instructions read between chunk
 // boundaries: the resident operand fragments and the float32 state live in the accumulator
 // registers (AGPRs), leaving the vector registers to the iterate and the products. An empty
@@ -50,6 +63,25 @@ __device__ inline void keep_in_agpr(V& x) {
 __device__ inline f16x8 pack8(f32x4 a, f32x4 b) {
   return f16x8{(f16)a[0], (f16)a[1], (f16)a[2], (f16)a[3], (f16)b[0], (f16)b[1], (f16)b[2],
                (f16)b[3]};
+}
+
+// The largest |x| over N units of eight bf16 values, as a float. The bit pattern of a bf16
+// without its sign orders like its magnitude, so the maxima are taken on the integers, two
+// halves to a register (v_pk_max_u16), and the result is the bf16 pattern widened to float.
+template <int N>
+__device__ inline float absmax_bf16(const bf16x8* x) {
+  typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+  typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+  u16x2 acc = {0, 0};
+#pragma unroll
+  for (int k = 0; k < N; ++k) {
+    const u32x4 w = __builtin_bit_cast(u32x4, x[k]);
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      acc = __builtin_elementwise_max(acc, __builtin_bit_cast(u16x2, w[j] & 0x7fff7fffu));
+  }
+  const uint32_t m = acc[0] > acc[1] ? acc[0] : acc[1];
+  return __uint_as_float(m << 16);
 }
 
 template <int I>

@@ -304,14 +304,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
   // the largest |k| and |v| of the loaded rows (this wave's units), to v_sc[4 + wave] and
   // v_sc[12 + wave]: read by every wave after the barrier at the top of the chunk
   auto kvmax_put = [&]() {
-    float mk = 0.0f, mv = 0.0f;
-#pragma unroll
-    for (int k = 0; k < NU / NT; ++k)
-#pragma unroll
-      for (int i = 0; i < 8; ++i) {
-        mk = fmaxf(mk, fabsf((float)kin[k][i]));
-        mv = fmaxf(mv, fabsf((float)vin[k][i]));
-      }
+    float mk = absmax_bf16<NU / NT>(kin), mv = absmax_bf16<NU / NT>(vin);
     mk = wave_max(mk);
     mv = wave_max(mv);
     if (lane == 0) {
@@ -320,21 +313,35 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
     }
   };
   // state tiles (times sc) -> Hs as fp16: row e of Hs holds H[e][*] (permuted columns); tile
-  // (a, b) gives rows 16b + lr (H[16b + lr][16a + 4lg ..] = H[16a + 4lg ..][16b + lr]) and, for
-  // an upper tile of the symmetric scheme, its mirror rows 16a + 4lg + i
+  // (a, b) gives rows 16b + lr (H[16b + lr][16a + 4lg ..] = H[16a + 4lg ..][16b + lr]). In the
+  // symmetric scheme (b >= a) these are the blocks on and below the diagonal of Hs only: the
+  // fragments of the blocks above it are read transposed from their mirrors (h0_frag).
   auto stage_h = [&](float sc) {
     for_tiles([&](auto J, auto a, auto b, auto) {
       constexpr int j = decltype(J)::value;
       const f32x4 x = Hst[j] * sc;
       const f16x4 y = {(f16)x[0], (f16)x[1], (f16)x[2], (f16)x[3]};
       *reinterpret_cast<f16x4*>(Hs + (16 * (int)b + lr) * LDD + pcol(16 * (int)a + 4 * lg)) = y;
-      if constexpr (TRI) {
-        if constexpr (decltype(a)::value != decltype(b)::value) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) Hs[(16 * (int)a + 4 * lg + i) * LDD + pcol(16 * (int)b + lr)] = y[i];
-        }
-      }
     });
+  };
+  // A fragment of H0hat (rows 16 ft + lr) over feature block kk, i.e. the column tiles 2 kk and
+  // 2 kk + 1. With the symmetric scheme only the blocks of Hs on and below the diagonal are
+  // staged: a column tile right of the diagonal (c > ft) is read as the transpose of block
+  // (c, ft) (H0hat[16 ft + lr][16 c + m] = Hs[16 c + m][16 ft + lr]), by a transposing read of the
+  // rows of that block, in the permuted k order of the direct read.
+  auto h0_frag = [&](auto FTc, auto KKc) -> Frag {
+    constexpr int ft = decltype(FTc)::value, kk = decltype(KKc)::value;
+    const f16* row = Hs + (16 * ft + lr) * LDD + 32 * kk + 8 * lg;
+    const int coff = pcol(16 * ft + 4 * (lr & 3));
+    if constexpr (!TRI || ft > 2 * kk) {
+      return *reinterpret_cast<const Frag*>(row);
+    } else if constexpr (ft < 2 * kk) {
+      return frag_trans<LDD>(Hs, 32 * kk + 4 * lg, 32 * kk + 16 + 4 * lg, coff, lr);
+    } else {  // ft == 2 kk: the diagonal block, then the block right of it
+      const f16x4 lo = *reinterpret_cast<const f16x4*>(row);
+      const f16x4 hi = frag_trans_half<LDD>(Hs, 32 * kk + 16 + 4 * lg, coff, lr);
+      return Frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    }
   };
   // A fragment of K (rows = tokens 16 sb + lr) over feature block kk
   auto frag_k = [&](int sb, int kk) {
@@ -417,11 +424,9 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
 
     // ---- resident H0hat fragments ------------------------------------------------------------
     Frag Hres[FT][KD];
-#pragma unroll
-    for (int ft = 0; ft < FT; ++ft)
-#pragma unroll
-      for (int kk = 0; kk < KD; ++kk)
-        Hres[ft][kk] = *reinterpret_cast<const Frag*>(Hs + (16 * ft + lr) * LDD + 32 * kk + 8 * lg);
+    static_for<0, FT>([&](auto F) {
+      static_for<0, KD>([&](auto K) { Hres[decltype(F)::value][decltype(K)::value] = h0_frag(F, K); });
+    });
     if constexpr (Cfg::PIN) {
 #pragma unroll
       for (int ft = 0; ft < FT; ++ft)
