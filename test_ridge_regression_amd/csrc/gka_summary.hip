@@ -162,25 +162,29 @@ void summary_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J
       suffix += clast;
     };
     // rows of register set q to slot `slot`, with the weighted keys (weights from v_wl)
+    // (the weights of the thread's tokens are read before any row is written: a read after a
+    // write would wait for the write)
     auto write_block = [&](int slot, int q) __attribute__((always_inline)) {
       refresh();
 #pragma unroll
       for (int k = 0; k < NUS; ++k) asm volatile("" : "+v"(kr[q][k]), "+v"(vr[q][k]));
+      float w[NUS];
+#pragma unroll
+      for (int k = 0; k < NUS; ++k) w[k] = v_wl[(uint32_t)(ts + k * NTS) / UPR];
 #pragma unroll
       for (int k = 0; k < NUS; ++k) {
         const int u = ts + k * NTS;
         const int tt = (uint32_t)u / UPR, cu = (uint32_t)u % UPR;  // u >= 0
         const int o = tt * LDR + cu * 8;
-        *reinterpret_cast<bf16x8*>(krows(slot) + o) = kr[q][k];
-        *reinterpret_cast<bf16x8*>(vrows(slot) + o) = vr[q][k];
-        const float w = v_wl[tt];
         bf16x8 hi, lo;
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-          const float x = (float)kr[q][k][j] * w;
+          const float x = (float)kr[q][k][j] * w[k];
           hi[j] = (bf16)x;
           lo[j] = (bf16)(x - (float)hi[j]);
         }
+        *reinterpret_cast<bf16x8*>(krows(slot) + o) = kr[q][k];
+        *reinterpret_cast<bf16x8*>(vrows(slot) + o) = vr[q][k];
         *reinterpret_cast<bf16x8*>(hirows(slot) + o) = hi;
         *reinterpret_cast<bf16x8*>(lorows(slot) + o) = lo;
       }

@@ -23,16 +23,18 @@ __device__ constexpr int pcol(int d) {
 // off(q) of that row; the eight k-slots of lane group lg are tokens s0 + m (first read) and
 // s1 + m (second read), m = 0..3. Two transposing 8-byte reads (ds_read_b64_tr_b16): within a
 // group of 16 lanes, lane i receives element i % 4 of the chunks addressed by lanes i / 4 + 4m,
-// so lane q addresses row s + q / 4 at the four columns of lane group q % 4.
+// so lane q addresses row s + q / 4 at the four columns of lane group q % 4. x: the lane's XOR
+// of the element offset in the rows it addresses (a row-dependent unit permutation of the
+// layout, the same for both reads; 0 for plain rows).
 template <int LDD>
-__device__ inline f16x8 frag_trans(const f16* base, int s0, int s1, int coff, int lr) {
+__device__ inline f16x8 frag_trans(const f16* base, int s0, int s1, int coff, int lr, int x = 0) {
 #if defined(__HIP_DEVICE_COMPILE__)
   typedef __attribute__((address_space(3))) fp16x4_t lds_fp16x4;
   const int r = lr >> 2;
-  const fp16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)(base + (s0 + r) * LDD + coff));
-  const fp16x4_t y = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)(base + (s1 + r) * LDD + coff));
-  return f16x8{(f16)x[0], (f16)x[1], (f16)x[2], (f16)x[3],
-               (f16)y[0], (f16)y[1], (f16)y[2], (f16)y[3]};
+  const fp16x4_t x0 = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)(base + (s0 + r) * LDD + (coff ^ x)));
+  const fp16x4_t y0 = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)(base + (s1 + r) * LDD + (coff ^ x)));
+  return f16x8{(f16)x0[0], (f16)x0[1], (f16)x0[2], (f16)x0[3],
+               (f16)y0[0], (f16)y0[1], (f16)y0[2], (f16)y0[3]};
 #else
   return f16x8{};
 #endif
@@ -41,10 +43,10 @@ __device__ inline f16x8 frag_trans(const f16* base, int s0, int s1, int coff, in
 // The first half of frag_trans: the k-slots of tokens s + m, m = 0..3, only (one transposing
 // read)
 template <int LDD>
-__device__ inline f16x4 frag_trans_half(const f16* base, int s, int coff, int lr) {
+__device__ inline f16x4 frag_trans_half(const f16* base, int s, int coff, int lr, int xo = 0) {
 #if defined(__HIP_DEVICE_COMPILE__)
   typedef __attribute__((address_space(3))) fp16x4_t lds_fp16x4;
-  const fp16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)(base + (s + (lr >> 2)) * LDD + coff));
+  const fp16x4_t x = __builtin_amdgcn_ds_read_tr16_b64_v4f16((lds_fp16x4*)(base + (s + (lr >> 2)) * LDD + (coff ^ xo)));
   return f16x4{(f16)x[0], (f16)x[1], (f16)x[2], (f16)x[3]};
 #else
   return f16x4{};

@@ -60,7 +60,13 @@ struct TokCfg {
   static constexpr int NST = FT * FT / NW;   // state tiles per wave
   static constexpr int NRT = NST >= FT ? NST / FT : 1;  // state row tiles per wave
   static constexpr int NCT = NST >= FT ? FT : NST;      // state column tiles per wave
-  static constexpr int LDD = D + 8;          // row stride of the [*][D] fp16 tiles
+  // Row stride of the [*][D] fp16 tiles (K, V, H0hat / U0hat). At D = 128 the rows are
+  // unpadded and the 16-byte units of row r are permuted by XOR with (5 r) & 15 (swz): the
+  // transposing reads (eight rows by four column groups per 32 lanes) then meet each LDS bank
+  // at most twice, against four times with a 16-byte pad, while the 16-byte row reads stay
+  // conflict-free. At D <= 64 a 16-byte pad does better.
+  static constexpr bool SWZ = D == 128;
+  static constexpr int LDD = SWZ ? D : D + 8;
   static constexpr bool PIN = D >= 128;      // resident fragments and state in AGPRs
   static constexpr int VEC = 8;              // bf16 elements per 16-byte unit
   static constexpr int UPR = D / VEC;        // units per token row
@@ -93,6 +99,11 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
   typedef f16x8 Frag;
   constexpr int C = Cfg::C, NW = Cfg::NW, NT = Cfg::NT, FT = Cfg::FT, KD = Cfg::KD;
   constexpr int KC = Cfg::KC, ST = Cfg::ST, LDD = Cfg::LDD, UPR = Cfg::UPR, NU = Cfg::NU;
+  // element offset of column position e in row `row` of a [*][D] tile (the units permuted)
+  auto sw = [](int row, int e) { return Cfg::SWZ ? e ^ (8 * ((5 * row) & 15)) : e; };
+  // the XOR of a transposing read's rows s + (lr >> 2), s a multiple of 4: the same for every
+  // s that differs by a multiple of 16
+  auto swt = [](int s, int lr_) { return Cfg::SWZ ? 8 * ((5 * (s + (lr_ >> 2))) & 15) : 0; };
   constexpr int NRT = Cfg::NRT, NCT = Cfg::NCT, LDC = Cfg::LDC;
 
   extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -321,7 +332,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
       constexpr int j = decltype(J)::value;
       const f32x4 x = Hst[j] * sc;
       const f16x4 y = {(f16)x[0], (f16)x[1], (f16)x[2], (f16)x[3]};
-      *reinterpret_cast<f16x4*>(Hs + (16 * (int)b + lr) * LDD + pcol(16 * (int)a + 4 * lg)) = y;
+      *reinterpret_cast<f16x4*>(Hs + (16 * (int)b + lr) * LDD + sw(16 * (int)b + lr, pcol(16 * (int)a + 4 * lg))) = y;
     });
   };
   // A fragment of H0hat (rows 16 ft + lr) over feature block kk, i.e. the column tiles 2 kk and
@@ -331,27 +342,28 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
   // rows of that block, in the permuted k order of the direct read.
   auto h0_frag = [&](auto FTc, auto KKc) -> Frag {
     constexpr int ft = decltype(FTc)::value, kk = decltype(KKc)::value;
-    const f16* row = Hs + (16 * ft + lr) * LDD + 32 * kk + 8 * lg;
+    const f16* row = Hs + (16 * ft + lr) * LDD + sw(16 * ft + lr, 32 * kk + 8 * lg);
     const int coff = pcol(16 * ft + 4 * (lr & 3));
     if constexpr (!TRI || ft > 2 * kk) {
       return *reinterpret_cast<const Frag*>(row);
     } else if constexpr (ft < 2 * kk) {
-      return frag_trans<LDD>(Hs, 32 * kk + 4 * lg, 32 * kk + 16 + 4 * lg, coff, lr);
+      return frag_trans<LDD>(Hs, 32 * kk + 4 * lg, 32 * kk + 16 + 4 * lg, coff, lr, swt(4 * lg, lr));
     } else {  // ft == 2 kk: the diagonal block, then the block right of it
       const f16x4 lo = *reinterpret_cast<const f16x4*>(row);
-      const f16x4 hi = frag_trans_half<LDD>(Hs, 32 * kk + 16 + 4 * lg, coff, lr);
+      const f16x4 hi = frag_trans_half<LDD>(Hs, 32 * kk + 16 + 4 * lg, coff, lr, swt(4 * lg, lr));
       return Frag{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
     }
   };
   // A fragment of K (rows = tokens 16 sb + lr) over feature block kk
   auto frag_k = [&](int sb, int kk) {
-    return *reinterpret_cast<const Frag*>(Kp + (16 * sb + lr) * LDD + 32 * kk + 8 * lg);
+    return *reinterpret_cast<const Frag*>(Kp + (16 * sb + lr) * LDD + sw(16 * sb + lr, 32 * kk + 8 * lg));
   };
   // A fragment of K^T (V^T) (rows = features 16 ft + lr) over token block kc, permuted token
   // order (k-slot j of lane group lg: token 32 kc + 16 (j / 4) + 4 lg + j % 4); K^T by two
   // transposing reads of K, V^T from its tile
   auto frag_kt = [&](int ft, int kc) {
-    return frag_trans<LDD>(Kp, 32 * kc + 4 * lg, 32 * kc + 16 + 4 * lg, pcol(16 * ft + 4 * (lr & 3)), lr);
+    return frag_trans<LDD>(Kp, 32 * kc + 4 * lg, 32 * kc + 16 + 4 * lg, pcol(16 * ft + 4 * (lr & 3)), lr,
+                           swt(4 * lg, lr));
   };
   auto frag_vt = [&](int ft, int kc) {
     return *reinterpret_cast<const Frag*>(VT + (16 * ft + lr) * LDC + 32 * kc + 8 * lg);
@@ -413,9 +425,9 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
         ko[i] = (f16)((float)kv[i] * kinv);
         vo[i] = (f16)((float)vv[i] * vinv);
       }
-      *reinterpret_cast<f16x8*>(Vp + tt * LDD + 8 * cu) = vo;
-      *reinterpret_cast<f16x4*>(Kp + tt * LDD + pcol(8 * cu)) = f16x4{ko[0], ko[1], ko[2], ko[3]};
-      *reinterpret_cast<f16x4*>(Kp + tt * LDD + pcol(8 * cu + 4)) = f16x4{ko[4], ko[5], ko[6], ko[7]};
+      *reinterpret_cast<f16x8*>(Vp + tt * LDD + sw(tt, 8 * cu)) = vo;
+      *reinterpret_cast<f16x4*>(Kp + tt * LDD + sw(tt, pcol(8 * cu))) = f16x4{ko[0], ko[1], ko[2], ko[3]};
+      *reinterpret_cast<f16x4*>(Kp + tt * LDD + sw(tt, pcol(8 * cu + 4))) = f16x4{ko[4], ko[5], ko[6], ko[7]};
     }
     stage_h(n0inv * exp2_int(2 * Ek));  // H0hat
     lds_barrier();
@@ -449,7 +461,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
       Frag kb[KD];  // B fragments of the own token's key
 #pragma unroll
       for (int kk = 0; kk < KD; ++kk)
-        kb[kk] = *reinterpret_cast<const Frag*>(Kp + t * LDD + 32 * kk + 8 * lg);
+        kb[kk] = *reinterpret_cast<const Frag*>(Kp + t * LDD + sw(t, 32 * kk + 8 * lg));
       float pu = 0.0f;
       f32x4 z[FT];  // H0hat k of the own token, the FT accumulators taking turns
 #pragma unroll
@@ -516,7 +528,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
         if (FT * KC % NW == 0 || phi < FT * KC) {
           const int ft = phi / KC, kc = phi % KC;
           g[k] = frag_trans<LDD>(Vp, 32 * kc + 4 * lg, 32 * kc + 16 + 4 * lg,
-                                 16 * ft + 4 * (lr & 3), lr);
+                                 16 * ft + 4 * (lr & 3), lr, swt(4 * lg, lr));
         }
       }
 #pragma unroll
@@ -663,7 +675,8 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
         for (int r = 0; r < NUR; ++r) {
           // U^T tile (urow(r), column b) holds U[16 b + lr][16 urow(r) + 4 lg ..]
           const f32x4 y = ub[c % 2][r] * u0sc;
-          *reinterpret_cast<f16x4*>(Hs + (16 * (TRI ? c : b0 + c) + lr) * LDD + pcol(16 * urow(r) + 4 * lg)) =
+          const int hrow = 16 * (TRI ? c : b0 + c) + lr;
+          *reinterpret_cast<f16x4*>(Hs + hrow * LDD + sw(hrow, pcol(16 * urow(r) + 4 * lg))) =
               f16x4{(f16)y[0], (f16)y[1], (f16)y[2], (f16)y[3]};
           uacc[r] = ub[c % 2][r] * usc;
         }
@@ -860,7 +873,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
       for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
         for (int kk = 0; kk < KD; ++kk)
-          Hres[ft][kk] = *reinterpret_cast<const Frag*>(Hs + (16 * ft + lr) * LDD + 32 * kk + 8 * lg);
+          Hres[ft][kk] = *reinterpret_cast<const Frag*>(Hs + (16 * ft + lr) * LDD + sw(16 * ft + lr, 32 * kk + 8 * lg));
       if constexpr (Cfg::PIN) {
 #pragma unroll
         for (int ft = 0; ft < FT; ++ft)
