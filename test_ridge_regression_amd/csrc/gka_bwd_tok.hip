@@ -58,7 +58,11 @@ struct BwdCfg {
   static constexpr int KD = D / 32;    // 32-deep blocks over the features
   static constexpr int KC = C / 32;    // 32-deep blocks over the tokens
   static constexpr int ST = C / 16;    // token tiles
-  static constexpr int LDD = D + 8;    // row stride of the [*][D] fp16 tiles
+  // Row stride of the [*][D] fp16 tiles. At D = 128 the rows are unpadded and the 16-byte
+  // units of row r are permuted by XOR with (5 r) & 15 (tix), which halves the LDS bank
+  // conflicts of the transposing fragment reads; at D <= 64 a 16-byte pad does better.
+  static constexpr bool SWZ = D == 128;
+  static constexpr int LDD = SWZ ? D : D + 8;
   static constexpr int LDP = C + 8;    // row stride of the [C][C] fp16 tiles
   static constexpr int UPR = D / 8;    // 16-byte units per bf16 token row
   static constexpr int NU = C * UPR;   // units per token-major chunk matrix
@@ -105,13 +109,26 @@ __device__ inline void buffer_store16f(f32x4 x, __amdgpu_buffer_rsrc_t r, uint32
 }
 // 2^e for any integer e (exp2_int needs -126 <= e <= 127)
 __device__ inline float pow2f(int e) { return ldexpf(1.0f, e); }
+// element offset of column position e (permuted features) in row `row` of a [*][D] tile
+template <int D>
+__device__ inline int tix(int row, int e) {
+  return row * BwdCfg<D>::LDD + (BwdCfg<D>::SWZ ? e ^ (8 * ((5 * row) & 15)) : e);
+}
+// the XOR of the element offsets of a transposing read of rows s + (lr >> 2), s = 4 lg modulo
+// 16 (the same for both reads of frag_trans, whose rows differ by 16)
+template <int D>
+__device__ inline int tix_trans(int lg, int lr) {
+  return BwdCfg<D>::SWZ ? 8 * ((5 * (4 * lg + (lr >> 2))) & 15) : 0;
+}
 // the four fp16 values of a token-major permuted row at logical features d..d+3 (d % 4 == 0)
-__device__ inline f32x4 row4(const f16* row, int d) {
-  const f16x4 h = *reinterpret_cast<const f16x4*>(row + pcol(d));
+template <int D>
+__device__ inline f32x4 row4(const f16* tile, int row, int d) {
+  const f16x4 h = *reinterpret_cast<const f16x4*>(tile + tix<D>(row, pcol(d)));
   return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]};
 }
-__device__ inline void put_row4(f16* row, int d, f32x4 x) {
-  *reinterpret_cast<f16x4*>(row + pcol(d)) = f16x4{(f16)x[0], (f16)x[1], (f16)x[2], (f16)x[3]};
+template <int D>
+__device__ inline void put_row4(f16* tile, int row, int d, f32x4 x) {
+  *reinterpret_cast<f16x4*>(tile + tix<D>(row, pcol(d))) = f16x4{(f16)x[0], (f16)x[1], (f16)x[2], (f16)x[3]};
 }
 
 // bf16 16-byte units of a chunk's token rows (bounds-checked: rows past the end read as 0)
@@ -131,7 +148,7 @@ struct ChunkRows {
 };
 
 // stage 16-byte bf16 units into a token-major permuted fp16 tile, times sc
-template <int D, int LDD>
+template <int D>
 __device__ inline void stage_unit(f16* dst, int u, bf16x8 x, float sc) {
   const int tt = (uint32_t)u / (D / 8), cu = (uint32_t)u % (D / 8);
   f16x4 a, b;
@@ -140,8 +157,8 @@ __device__ inline void stage_unit(f16* dst, int u, bf16x8 x, float sc) {
     a[i] = (f16)((float)x[i] * sc);
     b[i] = (f16)((float)x[4 + i] * sc);
   }
-  *reinterpret_cast<f16x4*>(dst + tt * LDD + pcol(8 * cu)) = a;
-  *reinterpret_cast<f16x4*>(dst + tt * LDD + pcol(8 * cu + 4)) = b;
+  *reinterpret_cast<f16x4*>(dst + tix<D>(tt, pcol(8 * cu))) = a;
+  *reinterpret_cast<f16x4*>(dst + tix<D>(tt, pcol(8 * cu + 4))) = b;
 }
 
 // ============================================================================================
@@ -288,17 +305,17 @@ void bwd_solve_kernel(BwdArgs A, int Tlen, int Hn, int N, ChebConsts cc) {
 #pragma unroll
   for (int j = 0; j < NU / NT; ++j) {
     const int u = tid + j * NT;
-    stage_unit<D, LDD>(Kp, u, kin[j], exp2_int(-ke));
-    stage_unit<D, LDD>(Vp, u, vin[j], exp2_int(-ve));
-    stage_unit<D, LDD>(Dp, u, din[j], exp2_int(-de));
+    stage_unit<D>(Kp, u, kin[j], exp2_int(-ke));
+    stage_unit<D>(Vp, u, vin[j], exp2_int(-ve));
+    stage_unit<D>(Dp, u, din[j], exp2_int(-de));
   }
   {
     const float usc = pow2f(-ue);
 #pragma unroll
     for (int j = 0; j < NH4; ++j) {
       const int e4 = tid + j * NT, r = e4 / (D / 4), c4 = e4 % (D / 4);
-      put_row4(Hs + r * LDD, 4 * c4, hreg[j] * n0inv);
-      put_row4(Us + r * LDD, 4 * c4, ureg[j] * usc);
+      put_row4<D>(Hs, r, 4 * c4, hreg[j] * n0inv);
+      put_row4<D>(Us, r, 4 * c4, ureg[j] * usc);
     }
   }
   lds_barrier();
@@ -309,11 +326,11 @@ void bwd_solve_kernel(BwdArgs A, int Tlen, int Hn, int N, ChebConsts cc) {
   for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
     for (int kk = 0; kk < KD; ++kk)
-      Hres[ft][kk] = *reinterpret_cast<const Frag*>(Hs + (16 * ft + lr) * LDD + 32 * kk + 8 * lg);
+      Hres[ft][kk] = *reinterpret_cast<const Frag*>(Hs + tix<D>(16 * ft + lr, 32 * kk + 8 * lg));
   // K fragments (rows = tokens) are read from LDS where they are used (K stays staged until
   // both solves are done): resident, they would push the solves past the register file
   auto kfrag = [&](int kk, int sb) {
-    return *reinterpret_cast<const Frag*>(Kp + (16 * sb + lr) * LDD + 32 * kk + 8 * lg);
+    return *reinterpret_cast<const Frag*>(Kp + tix<D>(16 * sb + lr, 32 * kk + 8 * lg));
   };
   Frag ktr[KC][FT];
 #pragma unroll
@@ -321,7 +338,7 @@ void bwd_solve_kernel(BwdArgs A, int Tlen, int Hn, int N, ChebConsts cc) {
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft)
       ktr[kc][ft] = frag_trans<LDD>(Kp, 32 * kc + 4 * lg, 32 * kc + 16 + 4 * lg,
-                                    pcol(16 * ft + 4 * (lr & 3)), lr);
+                                    pcol(16 * ft + 4 * (lr & 3)), lr, tix_trans<D>(lg, lr));
   if constexpr (Cfg::PIN) {
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft)
@@ -337,7 +354,7 @@ void bwd_solve_kernel(BwdArgs A, int Tlen, int Hn, int N, ChebConsts cc) {
   Frag kb[KD];  // B fragments of the own token's key
 #pragma unroll
   for (int kk = 0; kk < KD; ++kk)
-    kb[kk] = *reinterpret_cast<const Frag*>(Kp + t * LDD + 32 * kk + 8 * lg);
+    kb[kk] = *reinterpret_cast<const Frag*>(Kp + tix<D>(t, 32 * kk + 8 * lg));
   {
     f32x4 z[FT];
 #pragma unroll
@@ -512,7 +529,7 @@ void bwd_solve_kernel(BwdArgs A, int Tlen, int Hn, int N, ChebConsts cc) {
     Frag db[KD];
 #pragma unroll
     for (int kk = 0; kk < KD; ++kk)
-      db[kk] = *reinterpret_cast<const Frag*>(Dp + t * LDD + 32 * kk + 8 * lg);
+      db[kk] = *reinterpret_cast<const Frag*>(Dp + tix<D>(t, 32 * kk + 8 * lg));
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) gacc[ft] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -520,7 +537,7 @@ void bwd_solve_kernel(BwdArgs A, int Tlen, int Hn, int N, ChebConsts cc) {
 #pragma unroll
       for (int ft = 0; ft < FT; ++ft)
         gacc[ft] = M::mma(frag_trans<LDD>(Us, 32 * kk + 4 * lg, 32 * kk + 16 + 4 * lg,
-                                          pcol(16 * ft + 4 * (lr & 3)), lr),
+                                          pcol(16 * ft + 4 * (lr & 3)), lr, tix_trans<D>(lg, lr)),
                           db[kk], gacc[ft]);
     f32x4 pa[ST];
 #pragma unroll
@@ -529,7 +546,7 @@ void bwd_solve_kernel(BwdArgs A, int Tlen, int Hn, int N, ChebConsts cc) {
     for (int kk = 0; kk < KD; ++kk)
 #pragma unroll
       for (int sb = 0; sb < ST; ++sb)
-        pa[sb] = M::mma(*reinterpret_cast<const Frag*>(Vp + (16 * sb + lr) * LDD + 32 * kk + 8 * lg),
+        pa[sb] = M::mma(*reinterpret_cast<const Frag*>(Vp + tix<D>(16 * sb + lr, 32 * kk + 8 * lg)),
                         db[kk], pa[sb]);
     float su = 0.0f;
 #pragma unroll
@@ -597,7 +614,7 @@ void bwd_solve_kernel(BwdArgs A, int Tlen, int Hn, int N, ChebConsts cc) {
   {
 #pragma unroll
     for (int kk = 0; kk < KD; ++kk)
-      kb[kk] = *reinterpret_cast<const Frag*>(Kp + t * LDD + 32 * kk + 8 * lg);
+      kb[kk] = *reinterpret_cast<const Frag*>(Kp + tix<D>(t, 32 * kk + 8 * lg));
     const int ye = pow2_exponent(ymax, 126);
     const float yi = pow2f(-ye);
     Frag yf[KD];
@@ -694,8 +711,8 @@ void bwd_solve_kernel(BwdArgs A, int Tlen, int Hn, int N, ChebConsts cc) {
     const float xi = gam_t * pow2f(-xe2), yi = pow2f(-ye2);
 #pragma unroll
     for (int ft = 0; ft < FT; ++ft) {
-      put_row4(Vp + t * LDD, 16 * ft + 4 * lg, xv[ft] * xi);
-      put_row4(Kp + t * LDD, 16 * ft + 4 * lg, yv[ft] * yi);
+      put_row4<D>(Vp, t, 16 * ft + 4 * lg, xv[ft] * xi);
+      put_row4<D>(Kp, t, 16 * ft + 4 * lg, yv[ft] * yi);
     }
   }
   lds_barrier();
@@ -715,11 +732,11 @@ void bwd_solve_kernel(BwdArgs A, int Tlen, int Hn, int N, ChebConsts cc) {
       for (int kc = 0; kc < KC; ++kc) {
         const int s0 = 32 * kc + 4 * lg, s1 = s0 + 16;
         const int ca = pcol(16 * a + 4 * (lr & 3)), cb = pcol(16 * bq + 4 * (lr & 3));
-        const Frag xa = frag_trans<LDD>(Vp, s0, s1, ca, lr);
-        const Frag yb = frag_trans<LDD>(Kp, s0, s1, cb, lr);
-        const Frag ya = frag_trans<LDD>(Kp, s0, s1, ca, lr);
-        const Frag xb = frag_trans<LDD>(Vp, s0, s1, cb, lr);
-        const Frag dbf = frag_trans<LDD>(Dp, s0, s1, cb, lr);
+        const Frag xa = frag_trans<LDD>(Vp, s0, s1, ca, lr, tix_trans<D>(lg, lr));
+        const Frag yb = frag_trans<LDD>(Kp, s0, s1, cb, lr, tix_trans<D>(lg, lr));
+        const Frag ya = frag_trans<LDD>(Kp, s0, s1, ca, lr, tix_trans<D>(lg, lr));
+        const Frag xb = frag_trans<LDD>(Vp, s0, s1, cb, lr, tix_trans<D>(lg, lr));
+        const Frag dbf = frag_trans<LDD>(Dp, s0, s1, cb, lr, tix_trans<D>(lg, lr));
         // (w K)^T over the permuted tokens of ktr, and K as B
         const f32x4 w0 = *reinterpret_cast<const f32x4*>(v_w + s0);
         const f32x4 w1 = *reinterpret_cast<const f32x4*>(v_w + s1);
@@ -917,23 +934,23 @@ void bwd_grad_kernel(BwdArgs A, int Tlen, int Hn, int N) {
 #pragma unroll
   for (int j = 0; j < NU / NT; ++j) {
     const int u = tid + j * NT;
-    stage_unit<D, LDD>(Kp, u, kin[j], exp2_int(-ke));
-    stage_unit<D, LDD>(Vp, u, vin[j], exp2_int(-ve));
-    stage_unit<D, LDD>(Dp, u, din[j], exp2_int(-de));
+    stage_unit<D>(Kp, u, kin[j], exp2_int(-ke));
+    stage_unit<D>(Vp, u, vin[j], exp2_int(-ve));
+    stage_unit<D>(Dp, u, din[j], exp2_int(-de));
   }
   {
     const float xi = pow2f(-xe), yi = pow2f(-ye);
 #pragma unroll
     for (int j = 0; j < NX4; ++j) {
       const int u = tid + j * NT, tt = u / (D / 4), c4 = u % (D / 4);
-      put_row4(Xp + tt * LDD, 4 * c4, xin[j] * xi);
-      put_row4(Yp + tt * LDD, 4 * c4, yin[j] * yi);
+      put_row4<D>(Xp, tt, 4 * c4, xin[j] * xi);
+      put_row4<D>(Yp, tt, 4 * c4, yin[j] * yi);
     }
     const float gi = pow2f(-gse);
 #pragma unroll
     for (int j = 0; j < NH4; ++j) {
       const int e4 = tid + j * NT, r = e4 / (D / 4), c4 = e4 % (D / 4);
-      put_row4(Hs + r * LDD, 4 * c4, gs[j] * gi);
+      put_row4<D>(Hs, r, 4 * c4, gs[j] * gi);
     }
   }
   lds_barrier();
@@ -942,14 +959,14 @@ void bwd_grad_kernel(BwdArgs A, int Tlen, int Hn, int N) {
   Frag kb[KD], vbf[KD];
 #pragma unroll
   for (int kk = 0; kk < KD; ++kk) {
-    kb[kk] = *reinterpret_cast<const Frag*>(Kp + t * LDD + 32 * kk + 8 * lg);
-    vbf[kk] = *reinterpret_cast<const Frag*>(Vp + t * LDD + 32 * kk + 8 * lg);
+    kb[kk] = *reinterpret_cast<const Frag*>(Kp + tix<D>(t, 32 * kk + 8 * lg));
+    vbf[kk] = *reinterpret_cast<const Frag*>(Vp + tix<D>(t, 32 * kk + 8 * lg));
   }
   f32x4 kv[FT], vv[FT];  // k_t, v_t [16 ft + 4 lg + i]
 #pragma unroll
   for (int ft = 0; ft < FT; ++ft) {
-    kv[ft] = row4(Kp + t * LDD, 16 * ft + 4 * lg) * exp2_int(ke);
-    vv[ft] = row4(Vp + t * LDD, 16 * ft + 4 * lg) * exp2_int(ve);
+    kv[ft] = row4<D>(Kp, t, 16 * ft + 4 * lg) * exp2_int(ke);
+    vv[ft] = row4<D>(Vp, t, 16 * ft + 4 * lg) * exp2_int(ve);
   }
   const float cl_t = v_cl[t], clp = t > 0 ? v_cl[t - 1] : 0.0f;
   const float e_t = fast_exp2(fminf(clast - cl_t, 0.0f));
@@ -966,7 +983,7 @@ void bwd_grad_kernel(BwdArgs A, int Tlen, int Hn, int N) {
     for (int kk = 0; kk < KD; ++kk)
 #pragma unroll
       for (int ft = 0; ft < FT; ++ft)
-        acc[ft] = M::mma(*reinterpret_cast<const Frag*>(Hs + (16 * ft + lr) * LDD + 32 * kk + 8 * lg),
+        acc[ft] = M::mma(*reinterpret_cast<const Frag*>(Hs + tix<D>(16 * ft + lr, 32 * kk + 8 * lg)),
                          bf[kk], acc[ft]);
   };
   {
@@ -985,7 +1002,7 @@ void bwd_grad_kernel(BwdArgs A, int Tlen, int Hn, int N) {
 #pragma unroll
     for (int j = 0; j < NH4; ++j) {  // Wn, row-major (from the registers of the first load)
       const int e4 = tid + j * NT, r = e4 / (D / 4), c4 = e4 % (D / 4);
-      put_row4(Hs + r * LDD, 4 * c4, wn[j] * wi);
+      put_row4<D>(Hs, r, 4 * c4, wn[j] * wi);
     }
   }
   lds_barrier();
@@ -1000,7 +1017,7 @@ void bwd_grad_kernel(BwdArgs A, int Tlen, int Hn, int N) {
 #pragma unroll
       for (int ft = 0; ft < FT; ++ft)
         pt[ft] = M::mma(frag_trans<LDD>(Hs, 32 * kk + 4 * lg, 32 * kk + 16 + 4 * lg,
-                                        pcol(16 * ft + 4 * (lr & 3)), lr),
+                                        pcol(16 * ft + 4 * (lr & 3)), lr, tix_trans<D>(lg, lr)),
                         vbf[kk], pt[ft]);
     const float sc = pow2f(wne + ke), sct = pow2f(wne + ve);
 #pragma unroll
@@ -1031,7 +1048,7 @@ void bwd_grad_kernel(BwdArgs A, int Tlen, int Hn, int N) {
     for (int kk = 0; kk < KD; ++kk)
 #pragma unroll
       for (int sb = 0; sb < ST; ++sb) {
-        const int ro = (16 * sb + lr) * LDD + 32 * kk + 8 * lg;
+        const int ro = tix<D>(16 * sb + lr, 32 * kk + 8 * lg);
         pKX[sb] = M::mma(*reinterpret_cast<const Frag*>(Xp + ro), kb[kk], pKX[sb]);
         pKY[sb] = M::mma(*reinterpret_cast<const Frag*>(Yp + ro), kb[kk], pKY[sb]);
         pVD[sb] = M::mma(*reinterpret_cast<const Frag*>(Dp + ro), vbf[kk], pVD[sb]);
@@ -1090,10 +1107,10 @@ void bwd_grad_kernel(BwdArgs A, int Tlen, int Hn, int N) {
 #pragma unroll
       for (int ft = 0; ft < FT; ++ft) {
         const int co = pcol(16 * ft + 4 * (lr & 3));
-        ak[ft] = M::mma(frag_trans<LDD>(Yp, s0, s1, co, lr), pf1[kc], ak[ft]);
-        ak[ft] = M::mma(frag_trans<LDD>(Xp, s0, s1, co, lr), pf2[kc], ak[ft]);
-        ak[ft] = M::mma(frag_trans<LDD>(Kp, s0, s1, co, lr), pf3[kc], ak[ft]);
-        av[ft] = M::mma(frag_trans<LDD>(Dp, s0, s1, co, lr), pf4[kc], av[ft]);
+        ak[ft] = M::mma(frag_trans<LDD>(Yp, s0, s1, co, lr, tix_trans<D>(lg, lr)), pf1[kc], ak[ft]);
+        ak[ft] = M::mma(frag_trans<LDD>(Xp, s0, s1, co, lr, tix_trans<D>(lg, lr)), pf2[kc], ak[ft]);
+        ak[ft] = M::mma(frag_trans<LDD>(Kp, s0, s1, co, lr, tix_trans<D>(lg, lr)), pf3[kc], ak[ft]);
+        av[ft] = M::mma(frag_trans<LDD>(Dp, s0, s1, co, lr, tix_trans<D>(lg, lr)), pf4[kc], av[ft]);
       }
     }
     const float sk = pow2f(fk), sv = pow2f(fv);
@@ -1125,9 +1142,9 @@ void bwd_grad_kernel(BwdArgs A, int Tlen, int Hn, int N) {
     Frag dbf[KD], xbf[KD], ybf[KD];
 #pragma unroll
     for (int kk = 0; kk < KD; ++kk) {
-      dbf[kk] = *reinterpret_cast<const Frag*>(Dp + t * LDD + 32 * kk + 8 * lg);
-      xbf[kk] = *reinterpret_cast<const Frag*>(Xp + t * LDD + 32 * kk + 8 * lg);
-      ybf[kk] = *reinterpret_cast<const Frag*>(Yp + t * LDD + 32 * kk + 8 * lg);
+      dbf[kk] = *reinterpret_cast<const Frag*>(Dp + tix<D>(t, 32 * kk + 8 * lg));
+      xbf[kk] = *reinterpret_cast<const Frag*>(Xp + tix<D>(t, 32 * kk + 8 * lg));
+      ybf[kk] = *reinterpret_cast<const Frag*>(Yp + tix<D>(t, 32 * kk + 8 * lg));
     }
     f32x4 a1[ST], a2[ST];
 #pragma unroll
@@ -1140,7 +1157,7 @@ void bwd_grad_kernel(BwdArgs A, int Tlen, int Hn, int N) {
     for (int kk = 0; kk < KD; ++kk)
 #pragma unroll
       for (int sb = 0; sb < ST; ++sb) {
-        const int ro = (16 * sb + lr) * LDD + 32 * kk + 8 * lg;
+        const int ro = tix<D>(16 * sb + lr, 32 * kk + 8 * lg);
         const Frag kf = *reinterpret_cast<const Frag*>(Kp + ro);
         a1[sb] = M::mma(*reinterpret_cast<const Frag*>(Vp + ro), dbf[kk], a1[sb]);
         a2[sb] = M::mma(kf, ybf[kk], a2[sb]);
@@ -1403,8 +1420,8 @@ __global__ __launch_bounds__(256) void bwd_states_kernel(BwdArgs A, int Tlen, in
     const int ke = pow2_exponent(km, 30), ve = pow2_exponent(vm, 60);
 #pragma unroll
     for (int j = 0; j < NU / NT; ++j) {
-      stage_unit<D, LDD>(Kp, tid + j * NT, kin[j], exp2_int(-ke));
-      stage_unit<D, LDD>(Vp, tid + j * NT, vin[j], exp2_int(-ve));
+      stage_unit<D>(Kp, tid + j * NT, kin[j], exp2_int(-ke));
+      stage_unit<D>(Vp, tid + j * NT, vin[j], exp2_int(-ve));
     }
     lds_barrier();
     load(c + 1);  // the next chunk's rows, in flight during the stores and products
@@ -1418,9 +1435,9 @@ __global__ __launch_bounds__(256) void bwd_states_kernel(BwdArgs A, int Tlen, in
 #pragma unroll
       for (int kc = 0; kc < KC; ++kc) {
         const int s0 = 32 * kc + 4 * lg, s1 = s0 + 16;
-        const Frag ka = frag_trans<LDD>(Kp, s0, s1, pcol(16 * a + 4 * (lr & 3)), lr);
-        const Frag kbf = frag_trans<LDD>(Kp, s0, s1, pcol(16 * bq + 4 * (lr & 3)), lr);
-        const Frag vbf = frag_trans<LDD>(Vp, s0, s1, pcol(16 * bq + 4 * (lr & 3)), lr);
+        const Frag ka = frag_trans<LDD>(Kp, s0, s1, pcol(16 * a + 4 * (lr & 3)), lr, tix_trans<D>(lg, lr));
+        const Frag kbf = frag_trans<LDD>(Kp, s0, s1, pcol(16 * bq + 4 * (lr & 3)), lr, tix_trans<D>(lg, lr));
+        const Frag vbf = frag_trans<LDD>(Vp, s0, s1, pcol(16 * bq + 4 * (lr & 3)), lr, tix_trans<D>(lg, lr));
         const f32x4 w0 = *reinterpret_cast<const f32x4*>(v_w + s0);
         const f32x4 w1 = *reinterpret_cast<const f32x4*>(v_w + s1);
         Frag hi, lo;
