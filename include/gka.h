@@ -251,11 +251,11 @@ gka_status gka_fwd_varlen(const gka_params* p, const int32_t* cu_seqlens, int64_
  *   dq, dk, dv     [B, T, H, D] dtype, written; dgamma [B, T, H] float32, written; dbeta
  *                  optional [B, T, H] float32 (the gradient at the given beta, or at beta = 1)
  *   workspace      at least gka_bwd_workspace_bytes(p) bytes. bf16 with D = 32, 64, 128: per
- *                  chunk of 64 tokens and head, the start state in fp16 (4 D^2 bytes) and the
- *                  incoming gradient in float32 and fp16 (12 D^2 bytes); per token 4 (3 D + 4)
- *                  bytes; one float32 D x D pair per segment of the forward's plan. Otherwise:
- *                  two float32 D x D pairs per chunk and 4 (2 D^2 + 2 D + 1) bytes per token
- *                  (every H_t and U_t)
+ *                  chunk of 64 tokens and head, the start state, the chunk's own gradient and
+ *                  the incoming gradient, each in fp16 (12 D^2 bytes and their exponents); per
+ *                  token 4 (3 D + 4) bytes; one float32 D x D pair per segment of the forward's
+ *                  plan. Otherwise: two float32 D x D pairs per chunk and 4 (2 D^2 + 2 D + 1)
+ *                  bytes per token (every H_t and U_t)
  * Two paths. Every chunk's start state comes from the forward's segment summaries and scan (then,
  * on the matrix-core path, a walk over each segment's chunks), every chunk's incoming gradient
  * from the same scan run over the chunks in reverse order:

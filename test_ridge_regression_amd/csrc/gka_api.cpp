@@ -232,6 +232,7 @@ struct BwdLayoutHost {
   size_t snap, xs, ys, cs, dkh, tokv, fstates, flog2, fn2, rstates, rlog2, rn2;
   size_t sstates, slog2, sn2;  // matrix-core path: the segment summaries and start states
   size_t rs16, rexp;           // matrix-core path: the reverse scan's fp16 outputs
+  size_t rd16, rdx;            // matrix-core path: the chunk gradients it scans (fp16)
   size_t fs16, fexp;           // matrix-core path: every chunk's start state (fp16)
   size_t total;
 };
@@ -269,7 +270,12 @@ BwdLayoutHost bwd_layout(const gka_params* p) {
     l.flog2 = o; o += up(bh * N);
     l.fn2 = o; o += up(bh);
   }
-  l.rstates = o; o += up(bh * N * 2 * D * D);
+  if (l.tok) {
+    l.rd16 = o; o += up(bh * N * D * D);      // (2 D^2 fp16 per slot)
+    l.rdx = o; o += up(bh * N * D * D / 32);  // (2 D (D / 16) bytes per slot)
+  } else {
+    l.rstates = o; o += up(bh * N * 2 * D * D);
+  }
   l.rlog2 = o; o += up(bh * N);
   l.rn2 = o; o += up(bh);
   l.total = o * sizeof(float);
@@ -615,7 +621,9 @@ gka_status gka_bwd(const gka_params* p, const void* q, const void* k, const void
   ba.fstates = lay.tok ? nullptr : ws + lay.fstates;
   ba.fs16 = lay.tok ? ws + lay.fs16 : nullptr;
   ba.fexp = lay.tok ? ws + lay.fexp : nullptr;
-  ba.rstates = ws + lay.rstates;
+  ba.rstates = lay.tok ? nullptr : ws + lay.rstates;
+  ba.rd16 = lay.tok ? ws + lay.rd16 : nullptr;
+  ba.rdx = lay.tok ? reinterpret_cast<signed char*>(ws + lay.rdx) : nullptr;
   ba.rlog2 = ws + lay.rlog2;
   ba.rn2 = ws + lay.rn2;
   if (lay.tok) {

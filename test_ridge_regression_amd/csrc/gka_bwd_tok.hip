@@ -716,8 +716,19 @@ void bwd_solve_kernel(BwdArgs A, int Tlen, int Hn, int N, ChebConsts cc) {
     }
   }
   lds_barrier();
-  float* rs = A.rstates + ((size_t)bh * N + (N - 1 - ch)) * 2 * D * D;
-  if (tid == 0) A.rlog2[(size_t)bh * N + (N - 1 - ch)] = cl_last;
+  const size_t rslot = (size_t)bh * N + (N - 1 - ch);
+  f16* rs = static_cast<f16*>(A.rd16) + rslot * 2 * D * D;
+  signed char* rx = A.rdx + rslot * 2 * D * (D / 16);
+  if (tid == 0) A.rlog2[rslot] = cl_last;
+  // a lane's four values (a row segment) to slot matrix `mat`, fp16, the 16 columns of the row
+  // segment's tile times the power of two of their largest magnitude (the lane groups of the
+  // column share it; lane group 0 stores it)
+  auto put16 = [&](f32x4 x, size_t o, int row, int blk, int mat) {
+    const int e = pow2_exponent(group_max(absmax4(x), lane), 126);
+    const f32x4 y = x * pow2f(-e);
+    *reinterpret_cast<f16x4*>(rs + (size_t)mat * D * D + o) = f16x4{(f16)y[0], (f16)y[1], (f16)y[2], (f16)y[3]};
+    if (lg == 0) rx[(size_t)mat * D * (D / 16) + row * (D / 16) + blk] = (signed char)e;
+  };
   const float hsc0 = fast_exp2(2.0f * cl_first) * E_0;
   const float sxy = -pow2f(xe2 + ye2), sw = pow2f(2 * ke + we), sxd = pow2f(xe2 + de);
   // (one instance per wave: the tile indices, and with them the resident K^T fragments of the
@@ -753,8 +764,8 @@ void bwd_solve_kernel(BwdArgs A, int Tlen, int Hn, int N, ChebConsts cc) {
       // 4lg + i]: the transpose for dW, the same matrix for the symmetric dG + dG^T (H0
       // symmetric)
       const size_t o = (size_t)(16 * bq + lr) * D + 16 * a + 4 * lg;
-      *reinterpret_cast<f32x4*>(rs + o) = acc1 * sxy + acc2 * (2.0f * sw) + h0t[q] * (2.0f * hsc0);
-      *reinterpret_cast<f32x4*>(rs + D * D + o) = acc3 * sxd;
+      put16(acc1 * sxy + acc2 * (2.0f * sw) + h0t[q] * (2.0f * hsc0), o, 16 * bq + lr, a, 0);
+      put16(acc3 * sxd, o, 16 * bq + lr, a, 1);
     });
   };
   switch (wave_u) {
@@ -1248,15 +1259,16 @@ void bwd_grad_kernel(BwdArgs A, int Tlen, int Hn, int N) {
 // the D / 4 lanes of a row share its exponent.
 // ============================================================================================
 template <int D>
-__global__ __launch_bounds__(256) void bwd_rscan_kernel(const float* __restrict__ st,
+__global__ __launch_bounds__(256) void bwd_rscan_kernel(const f16* __restrict__ st,
+                                                        const signed char* __restrict__ stx,
                                                         const float* __restrict__ log2g,
                                                         f16* __restrict__ out,
                                                         float* __restrict__ oexp, int N) {
-  constexpr int DD = D * D, G = D / 4;
+  constexpr int DD = D * D, G = D / 4, NB = D / 16;
   static_assert((DD / 4) % 256 == 0 && kWave % G == 0, "rows within waves");
   const int bh = blockIdx.y;
   const int e4 = blockIdx.x * 256 + threadIdx.x;
-  const int lane = threadIdx.x % kWave, r = e4 / G;
+  const int lane = threadIdx.x % kWave, r = e4 / G, blk = (e4 % G) / 4;
   f32x4 sh = {0.f, 0.f, 0.f, 0.f}, su = sh;
   auto put = [&](f32x4 x, size_t slot, int mat) {
     float m = absmax4(x);
@@ -1268,17 +1280,40 @@ __global__ __launch_bounds__(256) void bwd_rscan_kernel(const float* __restrict_
         f16x4{(f16)y[0], (f16)y[1], (f16)y[2], (f16)y[3]};
     if (lane % G == 0) oexp[slot * 2 * D + (size_t)mat * D + r] = (float)e;
   };
+  // a slot's two chunk gradients (fp16 with a power of two per 16 columns of a row) and gate;
+  // loaded one slot ahead of their use. The last slot has none (chunk 0): its index is clamped
+  // to the one before (to slot 0 with a single chunk), whose values are loaded and not used.
+  struct Src {
+    f16x4 h, u;
+    signed char xh, xu;
+    float lg2;
+  };
+  auto load = [&](int s) {
+    const size_t slot = (size_t)bh * N + max(min(s, N - 2), 0);
+    Src v;
+    v.h = reinterpret_cast<const f16x4*>(st + slot * 2 * DD)[e4];
+    v.u = reinterpret_cast<const f16x4*>(st + slot * 2 * DD + DD)[e4];
+    v.xh = stx[slot * 2 * D * NB + r * NB + blk];
+    v.xu = stx[slot * 2 * D * NB + D * NB + r * NB + blk];
+    v.lg2 = log2g[slot];
+    return v;
+  };
+  auto widen = [](f16x4 x, signed char e) {
+    const float sc = pow2f((int)e);
+    return f32x4{(float)x[0] * sc, (float)x[1] * sc, (float)x[2] * sc, (float)x[3] * sc};
+  };
+  Src cur = load(0);
   for (int s = 0; s < N; ++s) {
     const size_t slot = (size_t)bh * N + s;
+    const Src nxt = load(s + 1);
     put(sh, slot, 0);
     put(su, slot, 1);
     if (s + 1 < N) {  // the last slot has no summary
-      const f32x4 dh = reinterpret_cast<const f32x4*>(st + slot * 2 * DD)[e4];
-      const f32x4 du = reinterpret_cast<const f32x4*>(st + slot * 2 * DD + DD)[e4];
-      const float g = exp2f(log2g[slot]);
-      sh = g * sh + dh;
-      su = g * su + du;
+      const float g = exp2f(cur.lg2);
+      sh = g * sh + widen(cur.h, cur.xh);
+      su = g * su + widen(cur.u, cur.xu);
     }
+    cur = nxt;
   }
 }
 
@@ -1472,7 +1507,8 @@ hipError_t launch_bwd_tok_t(const FwdPlan& pl, const BwdArgs& a, const ChebConst
   if ((e = hipGetLastError()) != hipSuccess) return e;
   // every chunk's incoming gradients: the segment scan over the chunks in reverse order
   hipLaunchKernelGGL(bwd_rscan_kernel<D>, dim3(D * D / 4 / 256, pl.B * pl.H), dim3(256), 0,
-                     stream, a.rstates, a.rlog2, static_cast<f16*>(a.rs16), a.rexp, pl.N);
+                     stream, static_cast<const f16*>(a.rd16), a.rdx, a.rlog2,
+                     static_cast<f16*>(a.rs16), a.rexp, pl.N);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   auto kg = bwd_grad_kernel<D>;
   static std::atomic<uint64_t> lds_g{0};

@@ -156,6 +156,8 @@ struct BwdArgs {
   float* fstates;  // [BH][N][2][D][D] every chunk's starting H and U (forward scan or the
                    // matrix-core path's state walk)
   float* rstates;        // [BH][N][2][D][D] chunk gradients (Gb, Wb), slot N - 1 - chunk
+  void* rd16;            // matrix-core path: the same in fp16, [BH][N][2][D][D], each run of 16
+  signed char* rdx;      // columns of a row times 2^-rdx[BH][N][2][D][D / 16]
   float* rlog2;          // [BH][N] log2 of each chunk's gate product P_c, same slots
   void* rs16;            // matrix-core path: the scan's outputs, fp16 [BH][N][2][D][D], each
   float* rexp;           // row times 2^-rexp[BH][N][2][D]

@@ -280,7 +280,7 @@ def test_backward_entry_point_checks(lib):
     # snapshots
     seg = up(2 * D * D) + up(1) + up(1)
     fs16 = up(N * D * D) + up(N * 2)
-    rscan = up(N * 2 * D * D) + up(N) + up(1) + up(N * D * D) + up(N * 2 * D)
+    rscan = up(N * D * D) + up(N * D * D // 32) + up(N) + up(1) + up(N * D * D) + up(N * 2 * D)
     assert need == 4 * (3 * up(n * D) + up(n * 4) + seg + fs16 + rscan)
     # float32 (vector sweeps): every H_t, U_t, then x, y, c
     need32 = lib.gka_bwd_workspace_bytes(P(params(B=1, H=1, T=64, D=32, dtype_code=gka.GKA_FP32)))
