@@ -649,8 +649,8 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
       // U^T tiles: the same A operands against the V^T fragments of their column tiles, on
       // Gam_C U^T rescaled to the frame 2^(ke + ve) of the product; the largest |U| of the
       // wave's tiles to v_sc[8 + wave] for the next chunk's U0hat. Column by column: the V^T
-      // fragments and U^T tiles of the next column are read while the current one's products
-      // run (double-buffered), and the rows of a column share them. The tiles as read are
+      // fragments and U^T tiles of the next two columns are read while the current one's
+      // products run, and the rows of a column share them. The tiles as read are
       // this chunk's U0: each is also staged to Hs as U0hat times 2^-ue (fp16; row v of Hs
       // holds U[v][*], permuted columns), which the output reads after its barrier (every wave
       // has read its H0hat fragments from Hs before the barrier ahead of the norm scan).
@@ -658,27 +658,29 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
       const float usc = gC * exp2_int(Eu - ke - ve);
       constexpr int NUR = TRI ? 2 : NRT, NUC = TRI ? FT : NCT;  // U row, column tiles per wave
       float um = 0.0f;
-      Frag bv[2][KC];
-      f32x4 ub[2][NUR];
+      constexpr int NB = NUC > 2 ? 3 : 2;  // column buffers: the reads run two columns ahead
+      Frag bv[NB][KC];
+      f32x4 ub[NB][NUR];
       auto load_col = [&](int c, int buf) {
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc) bv[buf][kc] = frag_vt(TRI ? c : b0 + c, kc);
 #pragma unroll
         for (int r = 0; r < NUR; ++r) ub[buf][r] = *us_tile(r * NUC + c);
       };
-      load_col(0, 0);
+#pragma unroll
+      for (int c = 0; c < NB - 1 && c < NUC; ++c) load_col(c, c);
 #pragma unroll
       for (int c = 0; c < NUC; ++c) {
-        if (c + 1 < NUC) load_col(c + 1, (c + 1) % 2);
+        if (c + NB - 1 < NUC) load_col(c + NB - 1, (c + NB - 1) % NB);
         f32x4 uacc[NUR];
 #pragma unroll
         for (int r = 0; r < NUR; ++r) {
           // U^T tile (urow(r), column b) holds U[16 b + lr][16 urow(r) + 4 lg ..]
-          const f32x4 y = ub[c % 2][r] * u0sc;
+          const f32x4 y = ub[c % NB][r] * u0sc;
           const int hrow = 16 * (TRI ? c : b0 + c) + lr;
           *reinterpret_cast<f16x4*>(Hs + hrow * LDD + sw(hrow, pcol(16 * urow(r) + 4 * lg))) =
               f16x4{(f16)y[0], (f16)y[1], (f16)y[2], (f16)y[3]};
-          uacc[r] = ub[c % 2][r] * usc;
+          uacc[r] = ub[c % NB][r] * usc;
         }
 #pragma unroll
         for (int kc = 0; kc < KC; ++kc)
@@ -686,7 +688,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
           for (int hl = 0; hl < 2; ++hl)
 #pragma unroll
             for (int r = 0; r < NUR; ++r)
-              uacc[r] = M::mma(hl == 0 ? awh[r][kc] : awl[r][kc], bv[c % 2][kc], uacc[r]);
+              uacc[r] = M::mma(hl == 0 ? awh[r][kc] : awl[r][kc], bv[c % NB][kc], uacc[r]);
 #pragma unroll
         for (int r = 0; r < NUR; ++r) {
           *us_tile(r * NUC + c) = uacc[r];
