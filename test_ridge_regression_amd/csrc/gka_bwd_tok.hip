@@ -131,6 +131,28 @@ __device__ inline void put_row4(f16* tile, int row, int d, f32x4 x) {
   *reinterpret_cast<f16x4*>(tile + tix<D>(row, pcol(d))) = f16x4{(f16)x[0], (f16)x[1], (f16)x[2], (f16)x[3]};
 }
 
+// A thread's groups of four elements of a row-major D x D fp16 matrix: group j is element
+// 4 e4(j). At D >= 64 they come in pairs, one 16-byte load of eight elements per pair (the
+// loads of these matrices are latency-bound: fewer, wider loads are faster).
+template <int D>
+struct DDGroups {
+  static constexpr int NT = 256;
+  static constexpr int N4 = D * D / 4 / NT;  // groups per thread
+  static constexpr bool PAIRS = N4 % 2 == 0;
+  __device__ static int e4(int tid, int j) {
+    return PAIRS ? 2 * (tid + (j >> 1) * NT) + (j & 1) : tid + j * NT;
+  }
+};
+__device__ inline void widen8(const f16* p, float sc, f32x4& lo, f32x4& hi) {
+  const f16x8 h = *reinterpret_cast<const f16x8*>(p);
+  lo = f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]} * sc;
+  hi = f32x4{(float)h[4], (float)h[5], (float)h[6], (float)h[7]} * sc;
+}
+__device__ inline f32x4 widen4(const f16* p, float sc) {
+  const f16x4 h = *reinterpret_cast<const f16x4*>(p);
+  return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]} * sc;
+}
+
 // bf16 16-byte units of a chunk's token rows (bounds-checked: rows past the end read as 0)
 template <int D>
 struct ChunkRows {
@@ -238,12 +260,22 @@ void bwd_solve_kernel(BwdArgs A, int Tlen, int Hn, int N, ChebConsts cc) {
   const f16* H0g = static_cast<const f16*>(A.fs16) + fslot * 2 * D * D;
   const f16* U0g = H0g + D * D;
   const float h0sc = pow2f((int)A.fexp[2 * fslot]), u0sc = pow2f((int)A.fexp[2 * fslot + 1]);
+  using DG = DDGroups<D>;
   f32x4 hreg[NH4], ureg[NH4];
   float sq = 0.0f, um = 0.0f;
 #pragma unroll
+  for (int j = 0; j < NH4; j += DG::PAIRS ? 2 : 1) {
+    const int e4 = DG::e4(tid, j);
+    if constexpr (DG::PAIRS) {
+      widen8(H0g + 4 * e4, h0sc, hreg[j], hreg[j + 1]);
+      widen8(U0g + 4 * e4, u0sc, ureg[j], ureg[j + 1]);
+    } else {
+      hreg[j] = widen4(H0g + 4 * e4, h0sc);
+      ureg[j] = widen4(U0g + 4 * e4, u0sc);
+    }
+  }
+#pragma unroll
   for (int j = 0; j < NH4; ++j) {
-    hreg[j] = load4(H0g + 4 * (tid + j * NT)) * h0sc;
-    ureg[j] = load4(U0g + 4 * (tid + j * NT)) * u0sc;
     sq += dot4(hreg[j], hreg[j]);
     um = fmaxf(um, absmax4(ureg[j]));
   }
@@ -313,7 +345,7 @@ void bwd_solve_kernel(BwdArgs A, int Tlen, int Hn, int N, ChebConsts cc) {
     const float usc = pow2f(-ue);
 #pragma unroll
     for (int j = 0; j < NH4; ++j) {
-      const int e4 = tid + j * NT, r = e4 / (D / 4), c4 = e4 % (D / 4);
+      const int e4 = DG::e4(tid, j), r = e4 / (D / 4), c4 = e4 % (D / 4);
       put_row4<D>(Hs, r, 4 * c4, hreg[j] * n0inv);
       put_row4<D>(Us, r, 4 * c4, ureg[j] * usc);
     }
@@ -868,15 +900,29 @@ void bwd_grad_kernel(BwdArgs A, int Tlen, int Hn, int N) {
   const float h0sc = pow2f((int)A.fexp[2 * fslot]), u0sc = pow2f((int)A.fexp[2 * fslot + 1]);
   f32x4 gs[NH4], wn[NH4];
   float sdot = 0.0f, wmx = 0.0f, gmx = 0.0f;  // sdot: <Gn, H0> + <Wn, U0>
+  using DG = DDGroups<D>;
 #pragma unroll
-  for (int j = 0; j < NH4; ++j) {
-    const int e4 = tid + j * NT, r = e4 / (D / 4);
-    gs[j] = load4(Gs16 + 4 * e4) * pow2f((int)Gsx[r]);
-    wn[j] = load4(Wn16 + 4 * e4) * pow2f((int)Wnx[r]);
-    sdot += 0.5f * h0sc * dot4(gs[j], load4(H0g + 4 * e4)) +
-            u0sc * dot4(wn[j], load4(U0g + 4 * e4));
-    wmx = fmaxf(wmx, absmax4(wn[j]));
-    gmx = fmaxf(gmx, absmax4(gs[j]));
+  for (int j = 0; j < NH4; j += DG::PAIRS ? 2 : 1) {
+    const int e4 = DG::e4(tid, j), r = e4 / (D / 4);  // (a pair shares its row)
+    const float gsc = pow2f((int)Gsx[r]), wsc = pow2f((int)Wnx[r]);
+    f32x4 h0[2], u0[2];
+    if constexpr (DG::PAIRS) {
+      widen8(Gs16 + 4 * e4, gsc, gs[j], gs[j + 1]);
+      widen8(Wn16 + 4 * e4, wsc, wn[j], wn[j + 1]);
+      widen8(H0g + 4 * e4, 1.0f, h0[0], h0[1]);
+      widen8(U0g + 4 * e4, 1.0f, u0[0], u0[1]);
+    } else {
+      gs[j] = widen4(Gs16 + 4 * e4, gsc);
+      wn[j] = widen4(Wn16 + 4 * e4, wsc);
+      h0[0] = widen4(H0g + 4 * e4, 1.0f);
+      u0[0] = widen4(U0g + 4 * e4, 1.0f);
+    }
+#pragma unroll
+    for (int h = 0; h < (DG::PAIRS ? 2 : 1); ++h) {
+      sdot += 0.5f * h0sc * dot4(gs[j + h], h0[h]) + u0sc * dot4(wn[j + h], u0[h]);
+      wmx = fmaxf(wmx, absmax4(wn[j + h]));
+      gmx = fmaxf(gmx, absmax4(gs[j + h]));
+    }
   }
   {
     float mk = 0.0f, mv = 0.0f, md = 0.0f, mx = 0.0f, my = 0.0f;
@@ -960,7 +1006,7 @@ void bwd_grad_kernel(BwdArgs A, int Tlen, int Hn, int N) {
     const float gi = pow2f(-gse);
 #pragma unroll
     for (int j = 0; j < NH4; ++j) {
-      const int e4 = tid + j * NT, r = e4 / (D / 4), c4 = e4 % (D / 4);
+      const int e4 = DG::e4(tid, j), r = e4 / (D / 4), c4 = e4 % (D / 4);
       put_row4<D>(Hs, r, 4 * c4, gs[j] * gi);
     }
   }
@@ -1012,7 +1058,7 @@ void bwd_grad_kernel(BwdArgs A, int Tlen, int Hn, int N) {
     const float wi = pow2f(-wne);
 #pragma unroll
     for (int j = 0; j < NH4; ++j) {  // Wn, row-major (from the registers of the first load)
-      const int e4 = tid + j * NT, r = e4 / (D / 4), c4 = e4 % (D / 4);
+      const int e4 = DG::e4(tid, j), r = e4 / (D / 4), c4 = e4 % (D / 4);
       put_row4<D>(Hs, r, 4 * c4, wn[j] * wi);
     }
   }
