@@ -1509,32 +1509,53 @@ __global__ __launch_bounds__(256) void bwd_states_kernel(BwdArgs A, int Tlen, in
     store_state(c);
     const float gC = fast_exp2(clast);
     const float sh = exp2_int(2 * ke), su = exp2_int(ke + ve);
+    // The wave's tiles q = r NC + c: NR row tiles (the A operands (w K)^T, split hi + lo once
+    // per chunk) by NC column tiles (the K and V fragments of a column read once for its rows)
+    constexpr int NR = TPW >= FT ? TPW / FT : 1, NC = TPW / NR;
+    const int xt = tix_trans<D>(lg, lr);
+    Frag awh[NR][KC], awl[NR][KC];
 #pragma unroll
-    for (int q = 0; q < TPW; ++q) {
-      const int tile = wave * TPW + q, a = tile / FT, bq = tile % FT;
-      f32x4 ah = {0.f, 0.f, 0.f, 0.f}, au = ah;
+    for (int kc = 0; kc < KC; ++kc) {
+      const int s0 = 32 * kc + 4 * lg, s1 = s0 + 16;
+      const f32x4 w0 = *reinterpret_cast<const f32x4*>(v_w + s0);
+      const f32x4 w1 = *reinterpret_cast<const f32x4*>(v_w + s1);
 #pragma unroll
-      for (int kc = 0; kc < KC; ++kc) {
-        const int s0 = 32 * kc + 4 * lg, s1 = s0 + 16;
-        const Frag ka = frag_trans<LDD>(Kp, s0, s1, pcol(16 * a + 4 * (lr & 3)), lr, tix_trans<D>(lg, lr));
-        const Frag kbf = frag_trans<LDD>(Kp, s0, s1, pcol(16 * bq + 4 * (lr & 3)), lr, tix_trans<D>(lg, lr));
-        const Frag vbf = frag_trans<LDD>(Vp, s0, s1, pcol(16 * bq + 4 * (lr & 3)), lr, tix_trans<D>(lg, lr));
-        const f32x4 w0 = *reinterpret_cast<const f32x4*>(v_w + s0);
-        const f32x4 w1 = *reinterpret_cast<const f32x4*>(v_w + s1);
-        Frag hi, lo;
+      for (int r = 0; r < NR; ++r) {
+        const int a = (wave * TPW + r * NC) / FT;
+        const Frag ka = frag_trans<LDD>(Kp, s0, s1, pcol(16 * a + 4 * (lr & 3)), lr, xt);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
           const float x = (float)ka[j] * (j < 4 ? w0[j] : w1[j - 4]);
-          hi[j] = (f16)x;
-          lo[j] = (f16)(x - (float)hi[j]);
+          awh[r][kc][j] = (f16)x;
+          awl[r][kc][j] = (f16)(x - (float)awh[r][kc][j]);
         }
-        ah = M::mma(hi, kbf, ah);
-        ah = M::mma(lo, kbf, ah);
-        au = M::mma(hi, vbf, au);
-        au = M::mma(lo, vbf, au);
       }
-      Ht[q] = Ht[q] * gC + ah * sh;
-      Ut[q] = Ut[q] * gC + au * su;
+    }
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const int bq = (wave * TPW + c) % FT;
+      f32x4 ah[NR], au[NR];
+#pragma unroll
+      for (int r = 0; r < NR; ++r) ah[r] = au[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int kc = 0; kc < KC; ++kc) {
+        const int s0 = 32 * kc + 4 * lg, s1 = s0 + 16;
+        const Frag kbf = frag_trans<LDD>(Kp, s0, s1, pcol(16 * bq + 4 * (lr & 3)), lr, xt);
+        const Frag vbf = frag_trans<LDD>(Vp, s0, s1, pcol(16 * bq + 4 * (lr & 3)), lr, xt);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) {
+          ah[r] = M::mma(awh[r][kc], kbf, ah[r]);
+          ah[r] = M::mma(awl[r][kc], kbf, ah[r]);
+          au[r] = M::mma(awh[r][kc], vbf, au[r]);
+          au[r] = M::mma(awl[r][kc], vbf, au[r]);
+        }
+      }
+#pragma unroll
+      for (int r = 0; r < NR; ++r) {
+        const int q = r * NC + c;
+        Ht[q] = Ht[q] * gC + ah[r] * sh;
+        Ut[q] = Ut[q] * gC + au[r] * su;
+      }
     }
   }
   store_state(c_end - 1);
