@@ -153,7 +153,8 @@ __device__ inline f32x4 widen4(const f16* p, float sc) {
   return f32x4{(float)h[0], (float)h[1], (float)h[2], (float)h[3]} * sc;
 }
 
-// bf16 16-byte units of a chunk's token rows (bounds-checked: rows past the end read as 0)
+// bf16 16-byte units of a chunk's token rows (bounds-checked: rows past the end read as 0;
+// nv <= 0, a chunk past the sequence, is an empty range)
 template <int D>
 struct ChunkRows {
   __amdgpu_buffer_rsrc_t r;
@@ -161,7 +162,7 @@ struct ChunkRows {
   __device__ ChunkRows(const void* base, long long row0, int nv, int Hn) {
     tok_bytes = (uint32_t)Hn * D * 2u;
     r = buffer_rsrc(static_cast<const bf16*>(base) + row0,
-                    (uint32_t)(nv - 1) * tok_bytes + D * 2u);
+                    nv > 0 ? (uint32_t)(nv - 1) * tok_bytes + D * 2u : 0u);
   }
   __device__ bf16x8 unit(int u) const {
     const int tt = (uint32_t)u / (D / 8), cu = (uint32_t)u % (D / 8);
@@ -1403,31 +1404,35 @@ __global__ __launch_bounds__(256) void bwd_states_kernel(BwdArgs A, int Tlen, in
       Ut[q] = *reinterpret_cast<const f32x4*>(st + D * D + o);  // U[16bq + lr][16a + 4lg ..]
     }
   }
-  bf16x8 kin[NU / NT], vin[NU / NT];
-  float g_l = 1.0f, bt_l = 1.0f;  // as loaded: past the end of the sequence they read as 0
-  int nv_l = 0;                   // valid rows of the loaded chunk
-  auto load = [&](int c) {
-    const int t0 = c * C, nv = min(C, Tlen - t0);
+  // Rows and gates of two chunks in flight: set q holds chunk c_begin + q + 2 i. A chunk's loads
+  // are issued right after the chunk two before it is staged, so that a whole chunk's work
+  // covers their latency. Chunks past the segment's last one load empty ranges.
+  bf16x8 kin[2][NU / NT], vin[2][NU / NT];
+  float g_l[2] = {1.0f, 1.0f}, bt_l[2] = {1.0f, 1.0f};  // past the end of the sequence: 0 as loaded
+  int nv_l[2] = {0, 0};                                   // valid rows of the loaded chunk
+  auto load = [&](int c, auto Q) __attribute__((always_inline)) {
+    constexpr int q = decltype(Q)::value;
+    const int t0 = c * C, nv = c < c_end ? min(C, Tlen - t0) : 0;
     const long long row0 = ((long long)b * Tlen + t0) * Hn * D + (long long)h * D;
     const ChunkRows<D> rk(A.k, row0, nv, Hn), rv(A.v, row0, nv, Hn);
 #pragma unroll
     for (int j = 0; j < NU / NT; ++j) {
-      kin[j] = rk.unit(tid + j * NT);
-      vin[j] = rv.unit(tid + j * NT);
+      kin[q][j] = rk.unit(tid + j * NT);
+      vin[q][j] = rv.unit(tid + j * NT);
     }
     const long long gb = ((long long)b * Tlen + t0) * Hn + h;
-    const uint32_t gvalid = (uint32_t)(nv - 1) * Hn * 4u + 4u;
+    const uint32_t gvalid = nv > 0 ? (uint32_t)(nv - 1) * Hn * 4u + 4u : 0u;
     // (the write gates are read from the gates when there are none: an unconditional load, so
     // that the compiler counts the loads in flight exactly; rows past the end get gate 1 where
     // the values are used, so that nothing waits for these loads here)
-    g_l = buffer_load4f(buffer_rsrc(A.gamma + gb, gvalid), (uint32_t)lane * Hn * 4u);
-    bt_l = buffer_load4f(buffer_rsrc((A.beta ? A.beta : A.gamma) + gb, gvalid),
-                         (uint32_t)lane * Hn * 4u);
-    nv_l = nv;
+    g_l[q] = buffer_load4f(buffer_rsrc(A.gamma + gb, gvalid), (uint32_t)lane * Hn * 4u);
+    bt_l[q] = buffer_load4f(buffer_rsrc((A.beta ? A.beta : A.gamma) + gb, gvalid),
+                            (uint32_t)lane * Hn * 4u);
+    nv_l[q] = nv;
   };
   // the start state of chunk c, from the tiles: fp16, each matrix times 2^-e (e from its
   // largest element, over the four waves)
-  auto store_state = [&](int c) {
+  auto store_state = [&](int c) __attribute__((always_inline)) {
     float mh = 0.0f, mu = 0.0f;
 #pragma unroll
     for (int q = 0; q < TPW; ++q) {
@@ -1464,25 +1469,25 @@ __global__ __launch_bounds__(256) void bwd_states_kernel(BwdArgs A, int Tlen, in
       A.fexp[2 * slot + 1] = (float)eu;
     }
   };
-  // Per chunk with a successor in the segment: stage the rows loaded before, issue the next
-  // chunk's loads, then the state stores (after the loads, so that waiting for the loads does not
-  // wait for the stores), then the products. The segment's last chunk only stores its start
-  // state (the next segment starts from the scan).
-  load(c_begin);
-  for (int c = c_begin; c + 1 < c_end; ++c) {
+  // Per chunk with a successor in the segment: stage the rows loaded before, issue the loads of
+  // the chunk two ahead into the freed register set, then the state stores (after the loads, so
+  // that waiting for the loads does not wait for the stores), then the products. The segment's
+  // last chunk only stores its start state (the next segment starts from the scan).
+  auto step = [&](int c, auto Q) __attribute__((always_inline)) {
+    constexpr int set = decltype(Q)::value;
     // scales of the chunk, gate prefix and carry weights
     float mk = 0.0f, mv = 0.0f;
 #pragma unroll
     for (int j = 0; j < NU / NT; ++j)
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
-        mk = fmaxf(mk, fabsf((float)kin[j][i]));
-        mv = fmaxf(mv, fabsf((float)vin[j][i]));
+        mk = fmaxf(mk, fabsf((float)kin[set][j][i]));
+        mv = fmaxf(mv, fabsf((float)vin[set][j][i]));
       }
     mk = wave_max(mk);
     mv = wave_max(mv);
-    const bool valid = lane < nv_l;
-    const float gv = valid ? g_l : 1.0f, bv = valid && A.beta ? bt_l : 1.0f;
+    const bool valid = lane < nv_l[set];
+    const float gv = valid ? g_l[set] : 1.0f, bv = valid && A.beta ? bt_l[set] : 1.0f;
     const float cl = scan_add<kWave>(log2_gate(gv));
     const float clast = lane_value(cl, C - 1);
     __syncthreads();  // the previous chunk's products have read Kp, Vp, v_w
@@ -1501,11 +1506,11 @@ __global__ __launch_bounds__(256) void bwd_states_kernel(BwdArgs A, int Tlen, in
     const int ke = pow2_exponent(km, 30), ve = pow2_exponent(vm, 60);
 #pragma unroll
     for (int j = 0; j < NU / NT; ++j) {
-      stage_unit<D>(Kp, tid + j * NT, kin[j], exp2_int(-ke));
-      stage_unit<D>(Vp, tid + j * NT, vin[j], exp2_int(-ve));
+      stage_unit<D>(Kp, tid + j * NT, kin[set][j], exp2_int(-ke));
+      stage_unit<D>(Vp, tid + j * NT, vin[set][j], exp2_int(-ve));
     }
     lds_barrier();
-    load(c + 1);  // the next chunk's rows, in flight during the stores and products
+    load(c + 2, Q);  // the rows of the chunk two ahead, in flight during the next two chunks
     store_state(c);
     const float gC = fast_exp2(clast);
     const float sh = exp2_int(2 * ke), su = exp2_int(ke + ve);
@@ -1532,8 +1537,8 @@ __global__ __launch_bounds__(256) void bwd_states_kernel(BwdArgs A, int Tlen, in
       }
     }
 #pragma unroll
-    for (int c = 0; c < NC; ++c) {
-      const int bq = (wave * TPW + c) % FT;
+    for (int cq = 0; cq < NC; ++cq) {
+      const int bq = (wave * TPW + cq) % FT;
       f32x4 ah[NR], au[NR];
 #pragma unroll
       for (int r = 0; r < NR; ++r) ah[r] = au[r] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -1552,11 +1557,22 @@ __global__ __launch_bounds__(256) void bwd_states_kernel(BwdArgs A, int Tlen, in
       }
 #pragma unroll
       for (int r = 0; r < NR; ++r) {
-        const int q = r * NC + c;
+        const int q = r * NC + cq;
         Ht[q] = Ht[q] * gC + ah[r] * sh;
         Ut[q] = Ut[q] * gC + au[r] * su;
       }
     }
+  };
+  load(c_begin, IC<0>{});
+  load(c_begin + 1, IC<1>{});
+  int c = c_begin;
+  for (; c + 2 < c_end; c += 2) {
+    step(c, IC<0>{});
+    step(c + 1, IC<1>{});
+  }
+  if (c + 1 < c_end) {
+    step(c, IC<0>{});
+    ++c;
   }
   store_state(c_end - 1);
 }
