@@ -120,7 +120,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
   // [16] scratch: [0, NW) state norms; per wave the largest |k| [4 + w], |U| [8 + w] and
   // |v| [12 + w]
   float* v_sc = v_bt + C;
-  float* v_coef = v_sc + 16;  // [iters][4] krs, kys, bts of each iteration (rescaled form)
+  float* v_coef = v_sc + 16;  // [iters][4] krs, kys, bts, |s| of each iteration (rescaled form)
 
   const int seg = blockIdx.x;
   int b, h;
@@ -268,7 +268,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
       v_coef[4 * tid] = cc.krs[tid];
       v_coef[4 * tid + 1] = cc.kys[tid];
       v_coef[4 * tid + 2] = cc.bts[tid];
-      v_coef[4 * tid + 3] = 0.0f;
+      v_coef[4 * tid + 3] = RES ? fabsf(cc.sres[tid]) : 0.0f;  // residual mode: |s_i|
     }
     __syncthreads();
     if (seg == 0 && A.n2_in) {
@@ -722,6 +722,46 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
       for (int ft = 0; ft < FT; ++ft)
         Ra[ft] = f32x4{(float)Qraw[ft][0], (float)Qraw[ft][1], (float)Qraw[ft][2], (float)Qraw[ft][3]} * qsc;
     }
+    // Residual mode: ||R_i|| = |s_i| ||Rt_i|| of the own token (a sum over the lane's features,
+    // then over the four lane groups), written by lane group 0; a token with ||H_t|| = 0 has
+    // x_i = 0 for every i, so its residuals are all ||q_t||. Rows past the end of the sequence
+    // (and the other lane groups) store out of the buffer's range, which drops the store.
+    // (The residual is formed on the query times 2^-qe: its norm is multiplied back.)
+    float res_qn = 0.0f;
+    const int res_i1 = cc.iters + 1;
+    const uint32_t res_row = (uint32_t)Hn * (uint32_t)res_i1 * 4u;  // bytes per token
+    const auto res_rsrc =
+        buffer_rsrc(RES ? A.resid + ((seq0 + t0) * Hn + h) * res_i1 : nullptr,
+                    RES ? (uint32_t)(nv - 1) * res_row + (uint32_t)res_i1 * 4u : 0u);
+    const uint32_t res_off = lg == 0 ? (uint32_t)t * res_row : 0x80000000u;
+    // a lane's sum of squares of a residual, taken on its fp16 operand copy (the values the
+    // products use): two elements per dot-product instruction, float32 accumulation
+    auto sumsq = [&](const Frag(&rf)[KD]) {
+      float x = 0.0f;
+#pragma unroll
+      for (int kk = 0; kk < KD; ++kk) {
+        x = __builtin_amdgcn_fdot2(__builtin_shufflevector(rf[kk], rf[kk], 0, 1), __builtin_shufflevector(rf[kk], rf[kk], 0, 1), x, false);
+        x = __builtin_amdgcn_fdot2(__builtin_shufflevector(rf[kk], rf[kk], 2, 3), __builtin_shufflevector(rf[kk], rf[kk], 2, 3), x, false);
+        x = __builtin_amdgcn_fdot2(__builtin_shufflevector(rf[kk], rf[kk], 4, 5), __builtin_shufflevector(rf[kk], rf[kk], 4, 5), x, false);
+        x = __builtin_amdgcn_fdot2(__builtin_shufflevector(rf[kk], rf[kk], 6, 7), __builtin_shufflevector(rf[kk], rf[kk], 6, 7), x, false);
+      }
+      return x;
+    };
+    auto res_put = [&](int i, float val) { buffer_store4f(val, res_rsrc, res_off + 4u * (uint32_t)i); };
+    const float res_sc = exp2_int(qe);
+    // the residual from a lane's sum of squares x summed over the lane groups, and |s_i|
+    auto res_val = [&](float x, float s_abs) {
+      return live ? s_abs * __builtin_amdgcn_sqrtf(x) * res_sc : res_qn;
+    };
+    auto res_step = [&](int i, const f32x4(&R)[FT]) {
+      Frag rf[KD];
+#pragma unroll
+      for (int kk = 0; kk < KD; ++kk) rf[kk] = pack8(R[2 * kk], R[2 * kk + 1]);
+      float x = sumsq(rf);
+      x += lane_read(x, lane ^ 16);
+      x += lane_read(x, lane ^ 32);
+      res_put(i, res_val(x, fabsf(cc.sres[i])));
+    };
     // One iteration it on the current rescaled residual Rc = Rt_it (the residuals divided by
     // host scalars that absorb the R_{it-1} coefficient of the recurrence):
     //   Ro <- Ro + krs Rc + H0hat (kys s_t Rc) + K^T ((K Rc) o kys Mhat)
@@ -732,15 +772,24 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
     // the scaled operands and the P' operands; (C) the K^T products, the X update and the
     // next step's first K fragments. With one wave per SIMD nothing else hides latency.
     // (the first step, FIRST = true, has Rt_{-1} = 0 and X = 0: it writes Ro and X outright)
-    auto step = [&](auto first, f32x4(&Ro)[FT], f32x4(&Rc)[FT], int it, auto... no_x) {
+    // In the residual mode a step with RESC = true also writes ||R_it|| of its operand: the
+    // lane's sum of squares in (A), the sums over the lane groups (two cross-lane reads, whose
+    // LDS round trips pass under the products) in (B) and (C), the store in (C).
+    auto step = [&](auto first, auto resc, f32x4(&Ro)[FT], f32x4(&Rc)[FT], int it, auto... no_x) {
       constexpr bool FIRST = decltype(first)::value;
+      constexpr bool RESC = RES && decltype(resc)::value;
       constexpr bool UPDX = sizeof...(no_x) == 0;  // the residual mode's last step leaves X
-      const f32x4 cf = *reinterpret_cast<const f32x4*>(v_coef + 4 * it);  // krs, kys, bts
+      const f32x4 cf = *reinterpret_cast<const f32x4*>(v_coef + 4 * it);  // krs, kys, bts, |s|
       Frag rf[KD], rs[KD], pf[KC];
       f32x4 pa[ST];
+      float rsq = 0.0f, rsx = 0.0f;
       // (A)
 #pragma unroll
       for (int kk = 0; kk < KD; ++kk) rf[kk] = pack8(Rc[2 * kk], Rc[2 * kk + 1]);
+      if constexpr (RESC) {
+        rsq = sumsq(rf);
+        rsx = lane_read(rsq, lane ^ 16);
+      }
 #pragma unroll
       for (int sb = 0; sb < ST; ++sb) pa[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -753,6 +802,10 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
       for (int ft = 0; ft < FT; ++ft) Ro[ft] = FIRST ? cf[0] * Rc[ft] : Ro[ft] + cf[0] * Rc[ft];
       __builtin_amdgcn_sched_barrier(0);
       // (B)
+      if constexpr (RESC) {
+        rsq += rsx;
+        rsx = lane_read(rsq, lane ^ 32);
+      }
 #pragma unroll
       for (int kk = 1; kk < KD; ++kk) rs[kk] = pack8(Rc[2 * kk] * kys, Rc[2 * kk + 1] * kys);
 #pragma unroll
@@ -772,32 +825,8 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
 #pragma unroll
         for (int ft = 0; ft < FT; ++ft) X[ft] = FIRST ? cf[2] * Rc[ft] : X[ft] + cf[2] * Rc[ft];
       }
+      if constexpr (RESC) res_put(it, res_val(rsq + rsx, cf[3]));
       __builtin_amdgcn_sched_barrier(0);
-    };
-    // Residual mode: ||R_i|| = |s_i| ||Rt_i|| of the own token (a sum over the lane's features,
-    // then over the four lane groups), written by lane group 0; a token with ||H_t|| = 0 has
-    // x_i = 0 for every i, so its residuals are all ||q_t||. Rows past the end of the sequence
-    // (and the other lane groups) store out of the buffer's range, which drops the store.
-    // (The residual is formed on the query times 2^-qe: its norm is multiplied back.)
-    float res_qn = 0.0f;
-    const int res_i1 = cc.iters + 1;
-    const uint32_t res_row = (uint32_t)Hn * (uint32_t)res_i1 * 4u;  // bytes per token
-    const auto res_rsrc =
-        buffer_rsrc(RES ? A.resid + ((seq0 + t0) * Hn + h) * res_i1 : nullptr,
-                    RES ? (uint32_t)(nv - 1) * res_row + (uint32_t)res_i1 * 4u : 0u);
-    const uint32_t res_off = lg == 0 ? (uint32_t)t * res_row : 0x80000000u;
-    auto lane_sum = [&](float x) {
-      x += lane_read(x, lane ^ 16);
-      return x + lane_read(x, lane ^ 32);
-    };
-    auto res_put = [&](int i, float val) { buffer_store4f(val, res_rsrc, res_off + 4u * (uint32_t)i); };
-    const float res_sc = exp2_int(qe);
-    auto res_step = [&](int i, const f32x4(&R)[FT]) {
-      float x = 0.0f;
-#pragma unroll
-      for (int ft = 0; ft < FT; ++ft) x += R[ft][0] * R[ft][0] + R[ft][1] * R[ft][1] + R[ft][2] * R[ft][2] + R[ft][3] * R[ft][3];
-      x = lane_sum(x);
-      res_put(i, live ? fabsf(cc.sres[i]) * sqrtf(x) * res_sc : res_qn);
     };
     if constexpr (RES) {
       float x = 0.0f;
@@ -805,7 +834,9 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
       for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
         for (int j = 0; j < 4; ++j) x += (float)Qraw[ft][j] * (float)Qraw[ft][j];
-      res_qn = sqrtf(lane_sum(x));
+      x += lane_read(x, lane ^ 16);
+      x += lane_read(x, lane ^ 32);
+      res_qn = sqrtf(x);
       res_put(0, res_qn);  // x_0 = 0
     }
     {
@@ -815,43 +846,45 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
       const float bl = v_coef[4 * (iters - 1) + 2];  // X += bts_{r-1} Rt_{r-1}
       // residual mode: one more step on Rt_{r-1} without the X update gives Rt_r
       const bool extra = RES && cc.res_extra;
+      // (residual mode: step it also writes ||R_it|| for it >= 1; the last one or two residuals
+      // come from res_step)
       if (iters == 1) {
 #pragma unroll
         for (int ft = 0; ft < FT; ++ft) X[ft] = bl * Ra[ft];
         if constexpr (RES) {
           if (extra) {
-            step(T1{}, Rb, Ra, 0, 0);
+            step(T1{}, T0{}, Rb, Ra, 0, 0);
             res_step(1, Rb);
           }
         }
       } else {
-        step(T1{}, Rb, Ra, 0);  // Rb = Rt_1
-        if constexpr (RES) res_step(1, Rb);
+        step(T1{}, T0{}, Rb, Ra, 0);  // Rb = Rt_1
         int it = 1;
         for (; it + 2 < iters; it += 2) {
-          step(T0{}, Ra, Rb, it);      // Ra = Rt_{it+1}
-          if constexpr (RES) res_step(it + 1, Ra);
-          step(T0{}, Rb, Ra, it + 1);  // Rb = Rt_{it+2}
-          if constexpr (RES) res_step(it + 2, Rb);
+          step(T0{}, T1{}, Ra, Rb, it);      // Ra = Rt_{it+1}
+          step(T0{}, T1{}, Rb, Ra, it + 1);  // Rb = Rt_{it+2}
         }
         if (it + 1 < iters) {
-          step(T0{}, Ra, Rb, it);
-          if constexpr (RES) res_step(it + 1, Ra);
+          step(T0{}, T1{}, Ra, Rb, it);  // Ra = Rt_{iters-1}
 #pragma unroll
           for (int ft = 0; ft < FT; ++ft) X[ft] += bl * Ra[ft];
           if constexpr (RES) {
             if (extra) {
-              step(T0{}, Rb, Ra, iters - 1, 0);
+              step(T0{}, T1{}, Rb, Ra, iters - 1, 0);
               res_step(iters, Rb);
+            } else {
+              res_step(iters - 1, Ra);
             }
           }
-        } else {
+        } else {  // Rb = Rt_{iters-1}
 #pragma unroll
           for (int ft = 0; ft < FT; ++ft) X[ft] += bl * Rb[ft];
           if constexpr (RES) {
             if (extra) {
-              step(T0{}, Ra, Rb, iters - 1, 0);
+              step(T0{}, T1{}, Ra, Rb, iters - 1, 0);
               res_step(iters, Ra);
+            } else {
+              res_step(iters - 1, Rb);
             }
           }
         }
