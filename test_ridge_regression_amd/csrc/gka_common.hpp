@@ -343,6 +343,38 @@ __device__ inline float lane_read(float x, int src) {
   return __builtin_bit_cast(float, __builtin_amdgcn_ds_bpermute(src << 2, __builtin_bit_cast(int, x)));
 }
 
+// x combined with x of lane ^ 16 and lane ^ 32 (the four lanes l % 16 + 16 j) by the CDNA4 row
+// swaps, without an LDS round trip. With both registers holding x, v_permlane16_swap exchanges
+// the odd 16-lane rows of the first with the even rows of the second, so in every lane one of
+// them holds x of the lane and the other x of lane ^ 16; v_permlane32_swap does the same for
+// the two 32-lane halves. (Written as asm with two read-write operands: the matching compiler
+// builtin's second result came out as a copy of its first in this toolchain's code.) The nop
+// gives the swap the wait states it needs after a vector write of its operands.
+__device__ inline void swap_rows16(float& a, float& b) {
+  asm("s_nop 1\n\tv_permlane16_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ inline void swap_rows32(float& a, float& b) {
+  asm("s_nop 1\n\tv_permlane32_swap_b32 %0, %1" : "+v"(a), "+v"(b));
+}
+__device__ inline float group_sum(float x) {
+  float a = x, b = x;
+  swap_rows16(a, b);
+  x = a + b;
+  a = x;
+  b = x;
+  swap_rows32(a, b);
+  return a + b;
+}
+__device__ inline float group_max(float x) {
+  float a = x, b = x;
+  swap_rows16(a, b);
+  x = fmaxf(a, b);
+  a = x;
+  b = x;
+  swap_rows32(a, b);
+  return fmaxf(a, b);
+}
+
 // ---- wave reductions (wave64) -------------------------------------------------------------
 __device__ inline float wave_sum(float x) {
 #pragma unroll

@@ -139,6 +139,26 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
     asm volatile("" : "+v"(tid), "+v"(lane), "+v"(lr), "+v"(lg), "+v"(t), "+v"(wave));
     asm volatile("" : "+v"(a0), "+v"(b0));
   };
+  // sum and max over the four lanes of a token (lane % 16 + 16 j): at D = 128, with one wave per
+  // SIMD, by the row swaps (no LDS round trip to wait for); at D <= 64 the other wave on the
+  // SIMD hides the round trip of the crossbar reads, which take fewer instructions. The two
+  // give the same sums (the same pairs are added in the same order).
+  auto gsum = [&](float x) {
+    if constexpr (D >= 128) {
+      return group_sum(x);
+    } else {
+      x += lane_read(x, lane ^ 16);
+      return x + lane_read(x, lane ^ 32);
+    }
+  };
+  auto gmax = [&](float x) {
+    if constexpr (D >= 128) {
+      return group_max(x);
+    } else {
+      x = fmaxf(x, lane_read(x, lane ^ 16));
+      return fmaxf(x, lane_read(x, lane ^ 32));
+    }
+  };
   long long seq0;  // first row of sequence b
   int Tlen;        // its length
   seq_range(A, b, Tmax, seq0, Tlen);
@@ -496,12 +516,9 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
           kd = s == t ? gacc[i] : kd;
         }
       }
-      pu += lane_read(pu, lane ^ 16);
-      pu += lane_read(pu, lane ^ 32);
-      pv += lane_read(pv, lane ^ 16);
-      pv += lane_read(pv, lane ^ 32);
-      kd += lane_read(kd, lane ^ 16);
-      kd += lane_read(kd, lane ^ 32);
+      pu = gsum(pu);
+      pv = gsum(pv);
+      kd = gsum(kd);
       const float gt = lane_read(g_l, t);
       const float gprev = lane_read(gam, t > 0 ? t - 1 : 0);
       const float btt = lane_read(bt_l, t);
@@ -714,8 +731,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
       for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
         for (int j = 0; j < 4; ++j) qm = fmaxf(qm, fabsf((float)Qraw[ft][j]));
-      qm = fmaxf(qm, lane_read(qm, lane ^ 16));
-      qm = fmaxf(qm, lane_read(qm, lane ^ 32));
+      qm = gmax(qm);
       qe = pow2_exponent(qm, 60);
       const float qsc = live ? cc.inv_s0 * exp2_int(-qe) : 0.0f;
 #pragma unroll
@@ -758,8 +774,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
 #pragma unroll
       for (int kk = 0; kk < KD; ++kk) rf[kk] = pack8(R[2 * kk], R[2 * kk + 1]);
       float x = sumsq(rf);
-      x += lane_read(x, lane ^ 16);
-      x += lane_read(x, lane ^ 32);
+      x = gsum(x);
       res_put(i, res_val(x, fabsf(cc.sres[i])));
     };
     // One iteration it on the current rescaled residual Rc = Rt_it (the residuals divided by
@@ -834,8 +849,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
       for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
         for (int j = 0; j < 4; ++j) x += (float)Qraw[ft][j] * (float)Qraw[ft][j];
-      x += lane_read(x, lane ^ 16);
-      x += lane_read(x, lane ^ 32);
+      x = gsum(x);
       res_qn = sqrtf(x);
       res_put(0, res_qn);  // x_0 = 0
     }
@@ -920,8 +934,7 @@ void walk_tok_kernel(WalkArgs A, int B, int Tmax, int Hn, int N, int S, int J, C
       for (int ft = 0; ft < FT; ++ft)
 #pragma unroll
         for (int j = 0; j < 4; ++j) xm = fmaxf(xm, fabsf(X[ft][j]));
-      xm = fmaxf(xm, lane_read(xm, lane ^ 16));
-      xm = fmaxf(xm, lane_read(xm, lane ^ 32));
+      xm = gmax(xm);
       const int xe = pow2_exponent(xm, 100);
       const float xinv = exp2_int(-xe);
       // (one fp16 rounding of X: o is stored in bf16, whose rounding is 4x coarser; a lo part of
